@@ -1,0 +1,538 @@
+"""Plain float64 NumPy oracle of Mixture-of-Gaussians (Iceberg) decode attention.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module. It shares
+no code with the HIP library and imports nothing from it.
+
+What the pages fix
+------------------
+* "Iceberg Attention: Sublinear Long-Context Decoding with Mixture-of-Gaussians"
+  (page 1, abstract): after prefill the keys of each head are partitioned
+  hierarchically into O(sqrt N) clusters and O(log N) subclusters per
+  cluster; each group is represented by a Gaussian; at decode the query is
+  scored against these summaries, the most relevant clusters and
+  subclusters are attended exactly, and the rest of the cache is estimated
+  from the groups' means and variances.
+* Retrieval-completion attention page (page 4, abstract and summary): exact
+  attention also covers fixed sink/tail anchor tokens; the exact part and
+  the estimated remainder are added as unnormalised numerator and
+  denominator, and a single normalisation follows.
+* DuoAttention review (page 2, "Method"): 64 sink plus 256 recent tokens is
+  the anchor size used on long-context workloads.
+
+Readings taken where the pages leave a step open (each one is also listed
+in the design notes of the repository):
+  R1  C = ceil(sqrt(N)) clusters and S = ceil(log2(N)) subclusters per
+      cluster, N the total sequence length; C is capped at the number of
+      middle-region keys.
+  R2  Only the middle region [n_sink, N - n_recent) is clustered; anchors are
+      always exact.
+  R3  The partitioner is Lloyd k-means with squared Euclidean distance,
+      Forgy initialisation by a partial Fisher-Yates shuffle driven by
+      SplitMix64, T iterations of (assign, update), then one final assign.
+      Ties go to the lower centroid id; an empty cluster keeps its centroid.
+  R4  A cluster is split by a second k-means over its members with
+      k = min(S, n_members), same rules, its own PRNG stream.
+  R5  Group Gaussian = diagonal: mean mu and population variance s (divide
+      by n), plus count n and mean value vbar.
+  R6  Group score = log of the estimated unnormalised attention mass of the
+      group: ln n + tau q.mu + tau^2/2 sum_i q_i^2 s_i, which is
+      ln(n E[exp(tau q.k)]) for k ~ N(mu, diag s) (Gaussian moment
+      generating function).  The residual uses the same quantity:
+      denominator term exp(score), numerator term exp(score) * vbar.
+  R7  Top-c clusters per query head, then top-s subclusters inside each
+      chosen cluster; a chosen cluster is represented by its subclusters
+      (chosen ones exact, the others by their own Gaussian).  Ties go to the
+      lower id; empty groups are never chosen; with fewer nonempty groups
+      than the budget all nonempty ones are chosen.
+  R8  Every query head makes its own selection (GQA heads sharing a KV head
+      are independent instances).
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# SplitMix64 (Steele, Lea & Flood, "Fast splittable pseudorandom number
+# generators", OOPSLA 2014; the stand-alone 64-bit generator as published by
+# Vigna).  Written from its definition: add the golden gamma to the state,
+# then a three-step xor-shift-multiply finaliser.
+# ---------------------------------------------------------------------------
+
+MASK64 = (1 << 64) - 1
+GOLDEN_GAMMA = 0x9E3779B97F4A7C15
+_MIX1 = 0xBF58476D1CE4E5B9
+_MIX2 = 0x94D049BB133111EB
+# Multiplier that separates the per-cluster subcluster streams (an odd
+# 64-bit constant; any odd constant would do, this one is fixed so the two
+# implementations agree).
+SUB_STREAM_MUL = 0xD1B54A32D192ED03
+
+
+def splitmix64(state: int) -> tuple[int, int]:
+    """Advance a SplitMix64 state once; return (new_state, 64-bit output)."""
+    state = (state + GOLDEN_GAMMA) & MASK64
+    z = state
+    z = ((z ^ (z >> 30)) * _MIX1) & MASK64
+    z = ((z ^ (z >> 27)) * _MIX2) & MASK64
+    return state, z ^ (z >> 31)
+
+
+def unit_state(seed: int, seq: int, kv_head: int, n_kv_heads: int) -> int:
+    """PRNG state of one (sequence, KV head) unit (reading R3)."""
+    return (seed ^ ((GOLDEN_GAMMA * (1 + seq * n_kv_heads + kv_head)) & MASK64)) & MASK64
+
+
+def sub_state(ustate: int, cluster: int) -> int:
+    """PRNG state of the subcluster k-means of one cluster (reading R4)."""
+    return (ustate ^ ((SUB_STREAM_MUL * (cluster + 1)) & MASK64)) & MASK64
+
+
+def forgy_ids(n: int, k: int, state: int) -> list[int]:
+    """First k entries of a Fisher-Yates shuffle of [0, n) (Forgy init, R3).
+
+    Step i draws r from SplitMix64, picks j = i + (r mod (n - i)) and swaps
+    positions i and j; the value that lands in position i is the i-th id.
+    """
+    if not 0 <= k <= n:
+        raise ValueError("need 0 <= k <= n")
+    moved: dict[int, int] = {}
+    out = []
+    for i in range(k):
+        state, r = splitmix64(state)
+        j = i + r % (n - i)
+        vi = moved.get(i, i)
+        vj = moved.get(j, j)
+        moved[i] = vj
+        moved[j] = vi
+        out.append(vj)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Sizes (reading R1)
+# ---------------------------------------------------------------------------
+
+
+def ceil_sqrt(n: int) -> int:
+    """Smallest integer r with r*r >= n."""
+    r = math.isqrt(n)
+    return r if r * r == n else r + 1
+
+
+def ceil_log2(n: int) -> int:
+    """Smallest integer e with 2**e >= n."""
+    return (n - 1).bit_length() if n > 1 else 0
+
+
+def unit_dims(N: int, n_sink: int, n_recent: int) -> tuple[int, int, int]:
+    """(N_mid, C, S) for one sequence of total length N."""
+    n_mid = N - n_sink - n_recent
+    if n_mid < 1:
+        raise ValueError("the middle region must hold at least one key")
+    C = min(ceil_sqrt(N), n_mid)
+    S = max(1, ceil_log2(N))
+    return n_mid, C, S
+
+
+# ---------------------------------------------------------------------------
+# Lloyd k-means (readings R3, R4)
+# ---------------------------------------------------------------------------
+
+
+def nearest_centroid(X: np.ndarray, mu: np.ndarray, chunk: int = 32768) -> np.ndarray:
+    """argmin_j ||x - mu_j||^2 per row; the lowest j wins a tie.
+
+    ||x - mu_j||^2 = ||x||^2 - 2 x.mu_j + ||mu_j||^2 and the first term does
+    not depend on j, so the argmin is taken over ||mu_j||^2 - 2 x.mu_j.
+    np.argmin returns the first minimum, i.e. the lowest j.
+    """
+    mu2 = np.einsum("jd,jd->j", mu, mu)
+    out = np.empty(X.shape[0], dtype=np.int64)
+    for r0 in range(0, X.shape[0], chunk):
+        d = mu2[None, :] - 2.0 * (X[r0:r0 + chunk] @ mu.T)
+        out[r0:r0 + chunk] = np.argmin(d, axis=1)
+    return out
+
+
+def centroid_sse(X: np.ndarray, mu: np.ndarray, a: np.ndarray) -> float:
+    """sum_x ||x - mu_{a(x)}||^2."""
+    diff = X - mu[a]
+    return float(np.einsum("nd,nd->", diff, diff))
+
+
+def partition_sse(X: np.ndarray, labels: np.ndarray) -> float:
+    """k-means objective of a partition: sum over groups of the squared
+    distances of the members to their group mean."""
+    total = 0.0
+    for g in np.unique(labels):
+        Xg = X[labels == g]
+        dev = Xg - Xg.mean(axis=0)
+        total += float(np.einsum("nd,nd->", dev, dev))
+    return total
+
+
+def _recenter(X: np.ndarray, a: np.ndarray, mu_old: np.ndarray) -> np.ndarray:
+    """New centroid = mean of its members; an empty cluster keeps its old one."""
+    k, d = mu_old.shape
+    counts = np.bincount(a, minlength=k)
+    sums = np.empty((k, d))
+    for i in range(d):
+        sums[:, i] = np.bincount(a, weights=X[:, i], minlength=k)
+    mu = mu_old.copy()
+    nz = counts > 0
+    mu[nz] = sums[nz] / counts[nz, None]
+    return mu
+
+
+def lloyd(X: np.ndarray, mu0: np.ndarray, iters: int):
+    """T rounds of (assign, update), then one final assign.
+
+    Returns (final assignment, centroids used by the final assign, objective
+    trace).  The trace holds, per round, J(a_t, mu_t) and J(a_t, mu_{t+1}),
+    then J(a_final, mu_T); for Lloyd's method it never increases.
+    """
+    mu = np.array(mu0, dtype=np.float64, copy=True)
+    trace = []
+    for _ in range(iters):
+        a = nearest_centroid(X, mu)
+        trace.append(centroid_sse(X, mu, a))
+        mu = _recenter(X, a, mu)
+        trace.append(centroid_sse(X, mu, a))
+    a = nearest_centroid(X, mu)
+    trace.append(centroid_sse(X, mu, a))
+    return a, mu, trace
+
+
+# ---------------------------------------------------------------------------
+# Gaussian summaries (reading R5) and the layout
+# ---------------------------------------------------------------------------
+
+
+def group_stats(Kg: np.ndarray, Vg: np.ndarray):
+    """(n, mu, s, vbar) of one group: mean key, population diagonal variance
+    (two passes: mean first, then mean squared deviation), mean value."""
+    n = Kg.shape[0]
+    mu = Kg.mean(axis=0)
+    s = ((Kg - mu) ** 2).mean(axis=0)
+    vbar = Vg.mean(axis=0)
+    return n, mu, s, vbar
+
+
+@dataclass
+class UnitLayout:
+    """Cluster layout of one (sequence, KV head).
+
+    Rows of the middle region are ordered by (cluster, subcluster, original
+    position).  ``perm[r]`` is the original token position of row r;
+    subcluster i of cluster j owns rows [sub_off[j*S+i], sub_off[j*S+i+1]).
+    Statistics are stored in float32, as the device keeps them.
+    """
+
+    N: int
+    n_sink: int
+    n_recent: int
+    C: int
+    S: int
+    perm: np.ndarray
+    sub_off: np.ndarray
+    cl_mu: np.ndarray
+    cl_var: np.ndarray
+    cl_vbar: np.ndarray
+    sub_mu: np.ndarray
+    sub_var: np.ndarray
+    sub_vbar: np.ndarray
+    init_ids: list = field(default_factory=list)
+    sub_init_ids: dict = field(default_factory=dict)
+    sse_trace: list = field(default_factory=list)
+
+    @property
+    def n_mid(self) -> int:
+        return self.N - self.n_sink - self.n_recent
+
+    @property
+    def sub_count(self) -> np.ndarray:
+        return np.diff(self.sub_off)
+
+    @property
+    def cl_count(self) -> np.ndarray:
+        return self.sub_off[self.S::self.S] - self.sub_off[:-1:self.S]
+
+    def cluster_labels(self) -> np.ndarray:
+        """Cluster id of each middle-region key, indexed by position - n_sink."""
+        lab = np.empty(self.n_mid, dtype=np.int64)
+        for j in range(self.C):
+            rows = self.perm[self.sub_off[j * self.S]:self.sub_off[(j + 1) * self.S]]
+            lab[rows - self.n_sink] = j
+        return lab
+
+    def subcluster_labels(self) -> np.ndarray:
+        """Global subcluster id (j*S+i) of each middle-region key."""
+        lab = np.empty(self.n_mid, dtype=np.int64)
+        for g in range(self.C * self.S):
+            rows = self.perm[self.sub_off[g]:self.sub_off[g + 1]]
+            lab[rows - self.n_sink] = g
+        return lab
+
+
+def layout_from_assignment(K, V, n_sink, n_recent, C, S, cl_assign, sub_assign):
+    """Order the middle region by (cluster, subcluster, position) and compute
+    the Gaussian summaries of every cluster and subcluster (reading R5).
+
+    ``cl_assign`` / ``sub_assign`` are indexed by middle-local position
+    (token position minus n_sink); ``sub_assign`` holds ids in [0, S).
+    """
+    N, d = K.shape
+    n_mid = N - n_sink - n_recent
+    cl_assign = np.asarray(cl_assign, dtype=np.int64)
+    sub_assign = np.asarray(sub_assign, dtype=np.int64)
+    assert cl_assign.shape == (n_mid,) and sub_assign.shape == (n_mid,)
+    assert cl_assign.min(initial=0) >= 0 and cl_assign.max(initial=0) < C
+    assert sub_assign.min(initial=0) >= 0 and sub_assign.max(initial=0) < S
+    local = np.arange(n_mid)
+    order = np.lexsort((local, sub_assign, cl_assign))
+    perm = (order + n_sink).astype(np.int64)
+    group = cl_assign * S + sub_assign
+    counts = np.bincount(group, minlength=C * S)
+    sub_off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+
+    Km = K[n_sink:N - n_recent]
+    Vm = V[n_sink:N - n_recent]
+    cl = [np.zeros((C, d), np.float32) for _ in range(3)]
+    sb = [np.zeros((C * S, d), np.float32) for _ in range(3)]
+    for j in range(C):
+        idx = cl_assign == j
+        if idx.any():
+            _, mu, s, vb = group_stats(Km[idx], Vm[idx])
+            cl[0][j], cl[1][j], cl[2][j] = mu, s, vb
+    for g in range(C * S):
+        if counts[g]:
+            rows = order[sub_off[g]:sub_off[g + 1]]
+            _, mu, s, vb = group_stats(Km[rows], Vm[rows])
+            sb[0][g], sb[1][g], sb[2][g] = mu, s, vb
+    return UnitLayout(N=N, n_sink=n_sink, n_recent=n_recent, C=C, S=S,
+                      perm=perm, sub_off=sub_off,
+                      cl_mu=cl[0], cl_var=cl[1], cl_vbar=cl[2],
+                      sub_mu=sb[0], sub_var=sb[1], sub_vbar=sb[2])
+
+
+def build_unit(K, V, n_sink, n_recent, iters, state, init_ids=None, sub_init_ids=None):
+    """Prefill-side build of one (sequence, KV head) (page 1, abstract:
+    hierarchical partition of the keys, one Gaussian per group).
+
+    K, V: float64 [N][d], the whole sequence.  ``init_ids`` (middle-local
+    positions) and ``sub_init_ids`` ({cluster: middle-local positions})
+    override the seeded Forgy draws; the ones actually used are returned in
+    the layout so a test can replay them.
+    """
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    N = K.shape[0]
+    n_mid, C, S = unit_dims(N, n_sink, n_recent)
+    X = K[n_sink:N - n_recent]
+    if init_ids is None:
+        init_ids = forgy_ids(n_mid, C, state)
+    init_ids = [int(i) for i in init_ids]
+    cl_assign, _, trace = lloyd(X, X[init_ids], iters)
+
+    sub_assign = np.zeros(n_mid, dtype=np.int64)
+    used_sub_init = {}
+    for j in range(C):
+        members = np.nonzero(cl_assign == j)[0]  # ascending position
+        n_j = members.size
+        if n_j == 0:
+            continue
+        k_j = min(S, n_j)
+        if sub_init_ids is not None and j in sub_init_ids:
+            where = {int(m): p for p, m in enumerate(members)}
+            local = [where[int(m)] for m in sub_init_ids[j]]
+        else:
+            local = forgy_ids(n_j, k_j, sub_state(state, j))
+        used_sub_init[j] = [int(members[p]) for p in local]
+        Xj = X[members]
+        sa, _, _ = lloyd(Xj, Xj[local], iters)
+        sub_assign[members] = sa
+    lay = layout_from_assignment(K, V, n_sink, n_recent, C, S, cl_assign, sub_assign)
+    lay.init_ids = init_ids
+    lay.sub_init_ids = used_sub_init
+    lay.sse_trace = trace
+    return lay
+
+
+# ---------------------------------------------------------------------------
+# Decode (readings R6-R8; merge rule from page 4's abstract)
+# ---------------------------------------------------------------------------
+
+
+def group_log_mass(q, count, mu, var, scale):
+    """Score of each group: ln n + scale q.mu + scale^2/2 sum_i q_i^2 var_i.
+
+    exp(score) = n * E[exp(scale q.k)] for k ~ N(mu, diag var): the estimated
+    unnormalised softmax mass of the group (reading R6).  Empty groups score
+    -inf.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    count = np.asarray(count)
+    mu = np.asarray(mu, dtype=np.float64)
+    var = np.asarray(var, dtype=np.float64)
+    with np.errstate(divide="ignore"):
+        lnn = np.where(count > 0, np.log(np.maximum(count, 1)), -np.inf)
+    return lnn + scale * (mu @ q) + 0.5 * scale * scale * (var @ (q * q))
+
+
+def top_by_score(scores, k, valid):
+    """The k highest-scoring valid entries, ties to the lower index, returned
+    in ascending index order (reading R7)."""
+    idx = np.nonzero(valid)[0]
+    if k <= 0 or idx.size == 0:
+        return np.zeros(0, dtype=np.int64)
+    order = idx[np.lexsort((idx, -np.asarray(scores)[idx]))]
+    return np.sort(order[:k])
+
+
+def _softmax_merge(logw, vals):
+    """Single normalisation of unnormalised terms exp(logw_i) * vals_i, with a
+    max shift (mathematically the same as the plain quotient)."""
+    m = np.max(logw)
+    w = np.exp(logw - m)
+    den = w.sum()
+    return (w @ vals) / den, m + np.log(den)
+
+
+def decode_unit(L: UnitLayout, K, V, Q, top_c, top_s, scale=None, residual=True,
+                sel_override=None):
+    """One decode step for the query heads that share one KV head.
+
+    K, V: float64 [N][d] of the sequence (anchors are read from here, the
+    middle rows through ``L.perm``).  Q: [G][d].  Returns a dict with
+    ``out``/``lse`` (exact + residual, one normalisation), ``out_top`` /
+    ``lse_top`` (exact part only, renormalised), ``sel_c`` (per head, chosen
+    cluster ids ascending), ``sel_s`` (per head, per chosen cluster, chosen
+    subcluster ids ascending) and ``n_exact`` (rows attended exactly per head).
+    ``sel_override`` = (sel_c, sel_s) replaces the selection.
+    """
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    Q = np.atleast_2d(np.asarray(Q, dtype=np.float64))
+    G, d = Q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    N, C, S = L.N, L.C, L.S
+    anchors = np.concatenate([np.arange(L.n_sink), np.arange(N - L.n_recent, N)])
+    cl_cnt = L.cl_count
+    sub_cnt = L.sub_count
+
+    res = dict(out=np.zeros((G, d)), lse=np.zeros(G), out_top=np.zeros((G, d)),
+               lse_top=np.zeros(G), sel_c=[], sel_s=[], n_exact=np.zeros(G, np.int64))
+    for h in range(G):
+        q = Q[h]
+        sc = group_log_mass(q, cl_cnt, L.cl_mu, L.cl_var, scale)
+        if sel_override is not None:
+            chosen = np.asarray(sel_override[0][h], dtype=np.int64)
+        else:
+            chosen = top_by_score(sc, top_c, cl_cnt > 0)
+        exact_rows = [anchors]
+        r_logw, r_vals = [], []
+        chosen_set = set(int(j) for j in chosen)
+        for j in range(C):
+            if cl_cnt[j] > 0 and j not in chosen_set:
+                r_logw.append(sc[j])
+                r_vals.append(L.cl_vbar[j].astype(np.float64))
+        sel_s_h = []
+        for jj, j in enumerate(chosen):
+            g0 = j * S
+            ss = group_log_mass(q, sub_cnt[g0:g0 + S], L.sub_mu[g0:g0 + S],
+                                L.sub_var[g0:g0 + S], scale)
+            if sel_override is not None:
+                picks = np.asarray(sel_override[1][h][jj], dtype=np.int64)
+            else:
+                picks = top_by_score(ss, top_s, sub_cnt[g0:g0 + S] > 0)
+            sel_s_h.append(picks)
+            pick_set = set(int(i) for i in picks)
+            for i in range(S):
+                g = g0 + i
+                if sub_cnt[g] == 0:
+                    continue
+                if i in pick_set:
+                    exact_rows.append(L.perm[L.sub_off[g]:L.sub_off[g + 1]])
+                else:
+                    r_logw.append(ss[i])
+                    r_vals.append(L.sub_vbar[g].astype(np.float64))
+        rows = np.concatenate(exact_rows)
+        e_logw = scale * (K[rows] @ q)
+        e_vals = V[rows]
+        res["out_top"][h], res["lse_top"][h] = _softmax_merge(e_logw, e_vals)
+        if residual and r_logw:
+            logw = np.concatenate([e_logw, np.asarray(r_logw)])
+            vals = np.concatenate([e_vals, np.asarray(r_vals)])
+            res["out"][h], res["lse"][h] = _softmax_merge(logw, vals)
+        else:
+            res["out"][h], res["lse"][h] = res["out_top"][h], res["lse_top"][h]
+        res["sel_c"].append(np.asarray(chosen, dtype=np.int64))
+        res["sel_s"].append(sel_s_h)
+        res["n_exact"][h] = rows.size
+    return res
+
+
+def dense_attention(K, V, Q, scale=None):
+    """Exact softmax attention of each query row over all N keys:
+    out = softmax(scale K q)^T V.  Returns (out [G][d], lse [G])."""
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    Q = np.atleast_2d(np.asarray(Q, dtype=np.float64))
+    if scale is None:
+        scale = 1.0 / math.sqrt(Q.shape[1])
+    logits = scale * (Q @ K.T)
+    m = logits.max(axis=1, keepdims=True)
+    w = np.exp(logits - m)
+    den = w.sum(axis=1)
+    return (w @ V) / den[:, None], m[:, 0] + np.log(den)
+
+
+# ---------------------------------------------------------------------------
+# Batched drivers: [n_seq][H][N][d] arrays, one layout per (seq, KV head)
+# ---------------------------------------------------------------------------
+
+
+def decode_batch(layouts, K, V, Q, n_kv_heads, top_c, top_s, scale=None,
+                 residual=True, units=None):
+    """Decode every (or the listed) (seq, KV head) unit.
+
+    ``layouts[u]`` with u = seq * n_kv_heads + kv_head; ``K[seq][kvh]`` and
+    ``V[seq][kvh]`` are [N_seq][d]; ``Q[seq]`` is [Hq][d]; ``top_c`` /
+    ``top_s`` are per-sequence sequences of ints.  Query head h reads KV head
+    h // G.  Returns {u: decode_unit result}.
+    """
+    out = {}
+    n_seq = len(Q)
+    for seq in range(n_seq):
+        Hq = Q[seq].shape[0]
+        G = Hq // n_kv_heads
+        for kvh in range(n_kv_heads):
+            u = seq * n_kv_heads + kvh
+            if units is not None and u not in units:
+                continue
+            out[u] = decode_unit(layouts[u], K[seq][kvh], V[seq][kvh],
+                                 Q[seq][kvh * G:(kvh + 1) * G], top_c[seq], top_s[seq],
+                                 scale=scale, residual=residual)
+    return out
+
+
+def dense_batch(K, V, Q, n_kv_heads, scale=None):
+    """Dense attention for every sequence and query head; returns lists of
+    (out [Hq][d], lse [Hq]) per sequence."""
+    res = []
+    for seq in range(len(Q)):
+        Hq = Q[seq].shape[0]
+        G = Hq // n_kv_heads
+        outs, lses = [], []
+        for kvh in range(n_kv_heads):
+            o, l = dense_attention(K[seq][kvh], V[seq][kvh], Q[seq][kvh * G:(kvh + 1) * G], scale)
+            outs.append(o)
+            lses.append(l)
+        res.append((np.concatenate(outs), np.concatenate(lses)))
+    return res

@@ -1,0 +1,484 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a published
+test vector, a closed form, an invariant the method must have, a textbook
+special case, or brute force on a tiny input.  None of them needs a GPU.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.special import logsumexp
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rel(a, b):
+    return float(np.linalg.norm(np.asarray(a) - np.asarray(b)) / np.linalg.norm(np.asarray(b)))
+
+
+def mixture_keys(rng, n, d, m, spread=0.5, sep=1.0):
+    cent = rng.normal(0, sep, (m, d))
+    comp = rng.integers(0, m, n)
+    return cent[comp] + spread * rng.normal(0, 1, (n, d))
+
+
+# ---------------------------------------------------------------------------
+# PRNG and Forgy draws
+# ---------------------------------------------------------------------------
+
+
+def test_splitmix64_published_vector():
+    g = json.load(open(os.path.join(GOLDEN, "splitmix64.json")))
+    s = g["state"]
+    for want in g["outputs_hex"]:
+        s, out = O.splitmix64(s)
+        assert out == int(want, 16)
+
+
+def _fisher_yates_array(n, k, state):
+    # textbook in-place Fisher-Yates on an explicit array, stopped after k steps
+    a = list(range(n))
+    for i in range(k):
+        state, r = O.splitmix64(state)
+        j = i + r % (n - i)
+        a[i], a[j] = a[j], a[i]
+    return a[:k]
+
+
+@pytest.mark.parametrize("n,k,seed", [(10, 10, 1), (1000, 37, 7), (5, 0, 3), (4028, 64, 99)])
+def test_forgy_ids_match_explicit_shuffle(n, k, seed):
+    st = O.unit_state(seed, 0, 0, 1)
+    ids = O.forgy_ids(n, k, st)
+    assert ids == _fisher_yates_array(n, k, st)
+    assert len(set(ids)) == k and all(0 <= i < n for i in ids)
+
+
+def test_forgy_full_shuffle_is_uniform():
+    # every permutation of 3 items appears with frequency near 1/6
+    counts = {}
+    for seed in range(6000):
+        p = tuple(O.forgy_ids(3, 3, O.unit_state(seed, 0, 0, 1)))
+        counts[p] = counts.get(p, 0) + 1
+    assert len(counts) == 6
+    for c in counts.values():
+        assert abs(c - 1000) < 5 * math.sqrt(1000 * 5 / 6)
+
+
+def test_streams_differ():
+    a = O.unit_state(5, 0, 0, 8)
+    assert len({a, O.unit_state(5, 0, 1, 8), O.unit_state(5, 1, 0, 8)}) == 3
+    assert len({O.sub_state(a, j) for j in range(100)}) == 100
+
+
+# ---------------------------------------------------------------------------
+# Sizes
+# ---------------------------------------------------------------------------
+
+
+def test_partition_sizes_of_the_workloads():
+    # sqrt / log2 partition sizes quoted for the five workloads
+    assert O.unit_dims(4096, 4, 64)[1:] == (64, 12)
+    assert O.unit_dims(32768, 64, 256)[1:] == (182, 15)
+    assert O.unit_dims(131072, 64, 256)[1:] == (363, 17)
+    assert O.unit_dims(1048576, 64, 256)[1:] == (1024, 20)
+
+
+def test_ceil_sqrt_log2_brute():
+    for n in range(1, 5000):
+        assert O.ceil_sqrt(n) == min(r for r in range(n + 2) if r * r >= n)
+        assert O.ceil_log2(n) == min(e for e in range(64) if 2 ** e >= n)
+    with pytest.raises(ValueError):
+        O.unit_dims(10, 5, 5)
+    # C never exceeds the middle region
+    assert O.unit_dims(12, 4, 4) == (4, 4, 4)
+
+
+# ---------------------------------------------------------------------------
+# Score / residual: the Gaussian moment generating function
+# ---------------------------------------------------------------------------
+
+
+def test_group_log_mass_is_gaussian_mgf_montecarlo():
+    rng = np.random.default_rng(0)
+    d, n_draw, tau = 8, 1_000_000, 0.7
+    mu = rng.normal(0, 0.5, d)
+    var = rng.uniform(0.2, 1.5, d)
+    q = rng.normal(0, 1.0, d)
+    k = mu + np.sqrt(var) * rng.normal(0, 1, (n_draw, d))
+    x = np.exp(tau * (k @ q))
+    n_group = 37
+    est = math.log(n_group * x.mean())
+    se = x.std() / math.sqrt(n_draw) / x.mean()  # std error of the log estimate
+    got = O.group_log_mass(q, np.array([n_group]), mu[None], var[None], tau)[0]
+    assert abs(got - est) < 6 * se
+    # the variance term is large compared with the MC error, so a dropped
+    # 1/2, a missing tau^2 or a dropped q_i^2 would all fail the bound above
+    var_term = 0.5 * tau * tau * float(var @ (q * q))
+    assert var_term > 100 * se
+    assert abs(var_term * 2 - var_term) > 6 * se
+    assert abs(0.5 * tau * float(var @ (q * q)) - var_term) > 6 * se
+
+
+def test_group_log_mass_two_point_closed_form():
+    # two keys mu +/- a: true mass 2 e^{tau q.mu} cosh(tau q.a); the Gaussian
+    # estimate 2 e^{tau q.mu + tau^2 (q.a)^2/2} differs only at 4th order.
+    tau = 0.125
+    mu = np.array([0.3, -0.2, 0.1])
+    a = np.array([0.4, 0.0, 0.0])
+    q = np.array([2.0, 1.0, -1.0])
+    K = np.stack([mu + a, mu - a])
+    n, m, s, _ = O.group_stats(K, K)
+    assert np.allclose(s, a * a) and np.allclose(m, mu)
+    got = O.group_log_mass(q, np.array([n]), m[None], s[None], tau)[0]
+    x = tau * float(q @ a)
+    true = math.log(2 * math.exp(tau * float(q @ mu)) * math.cosh(x))
+    assert abs(got - true) == pytest.approx(x ** 4 / 12, rel=0.05)
+
+
+def test_group_log_mass_empty_is_minus_inf():
+    sc = O.group_log_mass(np.ones(2), np.array([0, 3]), np.zeros((2, 2)), np.zeros((2, 2)), 1.0)
+    assert sc[0] == -np.inf and sc[1] == pytest.approx(math.log(3))
+
+
+# ---------------------------------------------------------------------------
+# Selection
+# ---------------------------------------------------------------------------
+
+
+def test_top_by_score_ties_and_empties():
+    s = np.array([1.0, 3.0, 3.0, 2.0, 3.0, -np.inf])
+    valid = np.array([True, True, True, True, True, False])
+    assert list(O.top_by_score(s, 2, valid)) == [1, 2]
+    assert list(O.top_by_score(s, 3, valid)) == [1, 2, 4]
+    assert list(O.top_by_score(s, 10, valid)) == [0, 1, 2, 3, 4]
+    assert list(O.top_by_score(s, 0, valid)) == []
+    v2 = valid.copy()
+    v2[1] = False
+    assert list(O.top_by_score(s, 2, v2)) == [2, 4]
+
+
+# ---------------------------------------------------------------------------
+# k-means
+# ---------------------------------------------------------------------------
+
+
+def test_lloyd_monotone_and_fixed_point():
+    rng = np.random.default_rng(1)
+    X = mixture_keys(rng, 600, 6, 5)
+    st = O.unit_state(11, 0, 0, 1)
+    init = O.forgy_ids(600, 7, st)
+    a, mu, trace = O.lloyd(X, X[init], 10)
+    assert all(trace[i + 1] <= trace[i] * (1 + 1e-12) for i in range(len(trace) - 1))
+    # the final assignment is nearest-centroid by direct distances
+    d2 = ((X[:, None, :] - mu[None, :, :]) ** 2).sum(-1)
+    assert np.array_equal(a, np.argmin(d2, axis=1))
+
+
+def test_nearest_centroid_ties_to_lower_id():
+    X = np.array([[0.0, 0.0], [1.0, 1.0]])
+    mu = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, 0.0]])
+    assert list(O.nearest_centroid(X, mu)) == [0, 0]
+
+
+def _all_partitions(n, k):
+    # assignments with labels in [0,k) up to relabelling, every label used
+    for lab in itertools.product(range(k), repeat=n):
+        if lab[0] != 0 or len(set(lab)) != k:
+            continue
+        seen = []
+        ok = True
+        for x in lab:
+            if x not in seen:
+                if x != len(seen):
+                    ok = False
+                    break
+                seen.append(x)
+        if ok:
+            yield np.array(lab)
+
+
+def test_kmeans_brute_force_optimum_tiny():
+    rng = np.random.default_rng(2)
+    # three well separated blobs of three points: Lloyd from any Forgy init
+    # that hits each blob reaches the global optimum of the enumeration
+    cent = np.array([[0.0, 0.0], [10.0, 0.0], [0.0, 10.0]])
+    X = np.concatenate([c + 0.3 * rng.normal(0, 1, (3, 2)) for c in cent])
+    best = min(O.partition_sse(X, lab) for lab in _all_partitions(9, 3))
+    a, _, _ = O.lloyd(X, X[[0, 3, 6]], 10)
+    assert O.partition_sse(X, a) == pytest.approx(best, rel=1e-12)
+    # from any Forgy init Lloyd's objective is at least the optimum
+    for seed in range(20):
+        ids = O.forgy_ids(9, 3, O.unit_state(seed, 0, 0, 1))
+        a, _, _ = O.lloyd(X, X[ids], 10)
+        assert O.partition_sse(X, a) >= best * (1 - 1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Build: stats and layout
+# ---------------------------------------------------------------------------
+
+
+def _small_unit(seed=3, N=700, d=8, m=12, fp=np.float64):
+    rng = np.random.default_rng(seed)
+    K = mixture_keys(rng, N, d, m)
+    V = rng.normal(0, 1, (N, d))
+    return K, V
+
+
+def test_stats_match_direct_numpy():
+    K, V = _small_unit()
+    L = O.build_unit(K, V, 4, 16, 10, O.unit_state(5, 0, 0, 1))
+    lab_c = L.cluster_labels()
+    lab_s = L.subcluster_labels()
+    Km, Vm = K[4:-16], V[4:-16]
+    for j in range(L.C):
+        m = lab_c == j
+        if m.any():
+            np.testing.assert_allclose(L.cl_mu[j], Km[m].mean(0), rtol=1e-6, atol=1e-6)
+            np.testing.assert_allclose(L.cl_var[j], Km[m].var(0), rtol=1e-5, atol=1e-6)
+            np.testing.assert_allclose(L.cl_vbar[j], Vm[m].mean(0), rtol=1e-6, atol=1e-6)
+    for g in range(L.C * L.S):
+        m = lab_s == g
+        assert m.sum() == L.sub_count[g]
+        if m.any():
+            np.testing.assert_allclose(L.sub_mu[g], Km[m].mean(0), rtol=1e-6, atol=1e-6)
+            np.testing.assert_allclose(L.sub_var[g], Km[m].var(0), rtol=1e-5, atol=1e-6)
+            np.testing.assert_allclose(L.sub_vbar[g], Vm[m].mean(0), rtol=1e-6, atol=1e-6)
+    # rows ordered by (cluster, subcluster, position); perm is a permutation
+    assert sorted(L.perm.tolist()) == list(range(4, 700 - 16))
+    key = [(lab_s[p - 4], p) for p in L.perm]
+    assert key == sorted(key)
+    # subclusters stay inside their cluster
+    assert np.array_equal(lab_s // L.S, lab_c)
+    # sub-k-means used at most min(S, n_j) subclusters per cluster
+    for j in range(L.C):
+        used = np.count_nonzero(L.sub_count[j * L.S:(j + 1) * L.S])
+        assert used <= min(L.S, L.cl_count[j])
+
+
+def test_build_reaches_a_lloyd_partition():
+    K, V = _small_unit(seed=4)
+    L = O.build_unit(K, V, 4, 16, 10, O.unit_state(6, 0, 0, 1))
+    tr = L.sse_trace
+    assert all(tr[i + 1] <= tr[i] * (1 + 1e-12) for i in range(len(tr) - 1))
+    # init centroids were the seeded Forgy draw
+    assert L.init_ids == O.forgy_ids(L.n_mid, L.C, O.unit_state(6, 0, 0, 1))
+
+
+# ---------------------------------------------------------------------------
+# Decode: invariants the method must have
+# ---------------------------------------------------------------------------
+
+
+def test_all_selected_is_dense():
+    K, V = _small_unit(seed=5)
+    L = O.build_unit(K, V, 4, 16, 10, O.unit_state(7, 0, 0, 1))
+    rng = np.random.default_rng(9)
+    Q = rng.normal(0, 1, (3, K.shape[1])) * 1.5
+    r = O.decode_unit(L, K, V, Q, L.C, L.S)
+    o, lse = O.dense_attention(K, V, Q)
+    assert rel(r["out"], o) < 1e-12
+    assert rel(r["out_top"], o) < 1e-12
+    np.testing.assert_allclose(r["lse"], lse, rtol=1e-12)
+    assert (r["n_exact"] == K.shape[0]).all()
+
+
+@pytest.mark.parametrize("c,s", [(0, 0), (1, 1), (3, 2), (2, 5), (40, 1)])
+def test_singleton_groups_make_residual_exact(c, s):
+    rng = np.random.default_rng(10)
+    N, d, ns, nr = 40, 5, 2, 3
+    K = rng.normal(0, 1, (N, d))
+    V = rng.normal(0, 1, (N, d))
+    n_mid = N - ns - nr
+    Q = rng.normal(0, 1, (2, d))
+    o, lse = O.dense_attention(K, V, Q)
+    # (a) every cluster and every subcluster a single key: exact for any c, s
+    C, S = n_mid, 3
+    L = O.layout_from_assignment(K, V, ns, nr, C, S, np.arange(n_mid), np.zeros(n_mid, int))
+    assert (L.cl_count == 1).all() and (L.cl_var == 0).all()
+    r = O.decode_unit(L, K, V, Q, c, s)
+    assert rel(r["out"], o) < 1e-6       # stats are stored in float32
+    np.testing.assert_allclose(r["lse"], lse, atol=1e-6)
+    if c < C:
+        assert rel(r["out_top"], o) > 1e-3
+    # (b) multi-key clusters, single-key subclusters, every cluster chosen:
+    # the estimated part is made of singletons only, so exact for any s
+    C, S = 5, 7
+    L = O.layout_from_assignment(K, V, ns, nr, C, S, np.arange(n_mid) % C, np.arange(n_mid) // C)
+    assert (L.sub_count <= 1).all() and (L.sub_var == 0).all() and (L.cl_count > 1).all()
+    r = O.decode_unit(L, K, V, Q, C, s)
+    assert rel(r["out"], o) < 1e-6
+
+
+def test_singletons_from_kmeans_tiny():
+    # N_mid <= S: every cluster has at most S members, so each sub-k-means
+    # has k = n and every subcluster is a single key
+    rng = np.random.default_rng(11)
+    N, d = 10, 4
+    K = rng.normal(0, 1, (N, d))
+    V = rng.normal(0, 1, (N, d))
+    L = O.build_unit(K, V, 3, 3, 10, O.unit_state(1, 0, 0, 1))
+    assert L.n_mid == 4 and (L.sub_count <= 1).all()
+    Q = rng.normal(0, 1, (2, d))
+    o, _ = O.dense_attention(K, V, Q)
+    for c, s in [(0, 0), (1, 1), (2, 4)]:
+        assert rel(O.decode_unit(L, K, V, Q, c, s)["out"], o) < 1e-6
+
+
+def test_key_permutation_invariance():
+    rng = np.random.default_rng(12)
+    N, d, ns, nr = 500, 6, 4, 12
+    K = mixture_keys(rng, N, d, 9, spread=0.3, sep=2.0)
+    V = rng.normal(0, 1, (N, d))
+    L1 = O.build_unit(K, V, ns, nr, 10, O.unit_state(3, 0, 0, 1))
+    n_mid = L1.n_mid
+    pi = rng.permutation(n_mid)          # new middle slot m holds old slot pi[m]
+    inv = np.empty_like(pi)
+    inv[pi] = np.arange(n_mid)
+    K2, V2 = K.copy(), V.copy()
+    K2[ns:N - nr] = K[ns:N - nr][pi]
+    V2[ns:N - nr] = V[ns:N - nr][pi]
+    init2 = [int(inv[i]) for i in L1.init_ids]
+    sub2 = {j: [int(inv[i]) for i in ids] for j, ids in L1.sub_init_ids.items()}
+    L2 = O.build_unit(K2, V2, ns, nr, 10, O.unit_state(3, 0, 0, 1), init_ids=init2,
+                      sub_init_ids=sub2)
+    # identical partitions as sets of (key, value) pairs
+    c1, c2 = L1.subcluster_labels(), L2.subcluster_labels()
+    assert np.array_equal(c2, c1[pi])
+    Q = rng.normal(0, 1, (3, d)) * 2
+    for c, s in [(2, 2), (4, 3), (1, 6)]:
+        r1 = O.decode_unit(L1, K, V, Q, c, s)
+        r2 = O.decode_unit(L2, K2, V2, Q, c, s)
+        assert rel(r2["out"], r1["out"]) < 1e-12
+        assert rel(r2["out_top"], r1["out_top"]) < 1e-12
+
+
+def _brute_force(L, K, V, q, c, s, scale):
+    """Selection by sorting every group, output by the literal unshifted
+    quotient of sums over every token and every estimated group."""
+    N, C, S = L.N, L.C, L.S
+    cnt_c = L.cl_count
+    cnt_s = L.sub_count
+    lab_s = L.subcluster_labels()
+    f64 = lambda a: np.asarray(a, dtype=np.float64)
+
+    def score(n, mu, var):
+        return math.log(n) + scale * float(q @ mu) + 0.5 * scale ** 2 * float((q * q) @ var)
+
+    cl_scores = [(score(cnt_c[j], L.cl_mu[j], L.cl_var[j]), j) for j in range(C) if cnt_c[j]]
+    chosen = sorted(cl_scores, key=lambda t: (-t[0], t[1]))[:c]
+    chosen = {j for _, j in chosen}
+    chosen_sub = set()
+    for j in chosen:
+        subs = [(score(cnt_s[g], L.sub_mu[g], L.sub_var[g]), g) for g in range(j * S, j * S + S) if cnt_s[g]]
+        chosen_sub |= {g for _, g in sorted(subs, key=lambda t: (-t[0], t[1]))[:s]}
+    num = np.zeros(K.shape[1])
+    den = 0.0
+    for t in range(N):
+        mid = L.n_sink <= t < N - L.n_recent
+        if not mid or lab_s[t - L.n_sink] in chosen_sub:
+            w = math.exp(scale * float(q @ K[t]))
+            num += w * V[t]
+            den += w
+    for j in range(C):
+        if cnt_c[j] and j not in chosen:
+            w = math.exp(score(cnt_c[j], L.cl_mu[j], L.cl_var[j]))
+            num += w * f64(L.cl_vbar[j])
+            den += w
+    for g in range(C * S):
+        if cnt_s[g] and g // S in chosen and g not in chosen_sub:
+            w = math.exp(score(cnt_s[g], L.sub_mu[g], L.sub_var[g]))
+            num += w * f64(L.sub_vbar[g])
+            den += w
+    return num / den, sorted(chosen), sorted(chosen_sub)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_matches_brute_force_tiny(seed):
+    rng = np.random.default_rng(100 + seed)
+    N, d = 90, 4
+    K = mixture_keys(rng, N, d, 6)
+    V = rng.normal(0, 1, (N, d))
+    L = O.build_unit(K, V, 3, 5, 10, O.unit_state(seed, 0, 0, 1))
+    Q = rng.normal(0, 1, (2, d)) * 1.5
+    scale = 0.5
+    for c, s in [(0, 0), (1, 1), (2, 3), (5, 2), (L.C, L.S)]:
+        r = O.decode_unit(L, K, V, Q, c, s, scale=scale)
+        for h in range(2):
+            out, ch, chs = _brute_force(L, K, V, Q[h], c, s, scale)
+            assert rel(r["out"][h], out) < 1e-12
+            assert list(r["sel_c"][h]) == ch
+            got_subs = sorted(int(j) * L.S + int(i) for j, picks in zip(r["sel_c"][h], r["sel_s"][h]) for i in picks)
+            assert got_subs == chs
+
+
+def test_translation_invariance():
+    rng = np.random.default_rng(13)
+    N, d = 400, 6
+    K = mixture_keys(rng, N, d, 8, spread=0.3, sep=2.0)
+    V = rng.normal(0, 1, (N, d))
+    Q = rng.normal(0, 1, (2, d))
+    st = O.unit_state(4, 0, 0, 1)
+    L = O.build_unit(K, V, 4, 8, 10, st)
+    r = O.decode_unit(L, K, V, Q, 3, 2)
+    b_k = rng.normal(0, 1, d)
+    Lk = O.build_unit(K + b_k, V, 4, 8, 10, st)
+    assert np.array_equal(Lk.subcluster_labels(), L.subcluster_labels())
+    rk = O.decode_unit(Lk, K + b_k, V, Q, 3, 2)
+    assert rel(rk["out"], r["out"]) < 1e-6  # float32-stored means shift
+    b_v = rng.normal(0, 1, d)
+    Lv = O.build_unit(K, V + b_v, 4, 8, 10, st)
+    rv = O.decode_unit(Lv, K, V + b_v, Q, 3, 2)
+    assert rel(rv["out"], r["out"] + b_v) < 1e-6
+
+
+def test_selection_override_and_top_only():
+    K, V = _small_unit(seed=6)
+    L = O.build_unit(K, V, 4, 16, 10, O.unit_state(8, 0, 0, 1))
+    Q = np.random.default_rng(1).normal(0, 1, (2, K.shape[1]))
+    r = O.decode_unit(L, K, V, Q, 3, 2)
+    r2 = O.decode_unit(L, K, V, Q, 3, 2, sel_override=(r["sel_c"], r["sel_s"]))
+    assert rel(r2["out"], r["out"]) == 0.0
+    # top-only = softmax restricted to the exact rows (textbook)
+    for h in range(2):
+        rows = list(range(4)) + list(range(K.shape[0] - 16, K.shape[0]))
+        for j, picks in zip(r["sel_c"][h], r["sel_s"][h]):
+            for i in picks:
+                g = j * L.S + i
+                rows += list(L.perm[L.sub_off[g]:L.sub_off[g + 1]])
+        o, _ = O.dense_attention(K[rows], V[rows], Q[h])
+        assert rel(r["out_top"][h], o[0]) < 1e-12
+    # residual off returns the top-only output
+    r3 = O.decode_unit(L, K, V, Q, 3, 2, residual=False)
+    assert rel(r3["out"], r["out_top"]) == 0.0
+
+
+# ---------------------------------------------------------------------------
+# Dense attention: textbook special cases
+# ---------------------------------------------------------------------------
+
+
+def test_dense_special_cases():
+    rng = np.random.default_rng(14)
+    V = rng.normal(0, 1, (7, 3))
+    # equal keys: plain mean of the values
+    K = np.ones((7, 3))
+    o, lse = O.dense_attention(K, V, np.array([0.3, 0.1, -2.0]), scale=1.0)
+    np.testing.assert_allclose(o[0], V.mean(0), rtol=1e-13)
+    assert lse[0] == pytest.approx(math.log(7) + (0.3 + 0.1 - 2.0), rel=1e-13)
+    # one key far ahead: its value
+    K = rng.normal(0, 1, (7, 3))
+    K[4] = [100.0, 0, 0]
+    o, _ = O.dense_attention(K, V, np.array([1.0, 0, 0]), scale=1.0)
+    np.testing.assert_allclose(o[0], V[4], atol=1e-30 + 1e-12)
+    # lse against a library logsumexp
+    q = rng.normal(0, 1, 3)
+    _, lse = O.dense_attention(K, V, q, scale=0.7)
+    assert lse[0] == pytest.approx(logsumexp(0.7 * K @ q), rel=1e-13)
