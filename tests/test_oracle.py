@@ -187,6 +187,16 @@ def test_nearest_centroid_ties_to_lower_id():
     assert list(O.nearest_centroid(X, mu)) == [0, 0]
 
 
+def test_empty_cluster_keeps_its_centroid():
+    # duplicate init centroids: the tie goes to the lower id, the other one
+    # gets no member and must keep its position through the update
+    X = np.array([[10.0, 0.0], [10.0, 0.0], [10.3, 0.0], [1.0, 1.0], [1.2, 1.0]])
+    a, mu, _ = O.lloyd(X, X[[0, 1, 3]], 1)
+    np.testing.assert_array_equal(mu[1], [10.0, 0.0])
+    np.testing.assert_allclose(mu[0], X[:3].mean(0))
+    np.testing.assert_allclose(mu[2], X[3:].mean(0))
+
+
 def _all_partitions(n, k):
     # assignments with labels in [0,k) up to relabelling, every label used
     for lab in itertools.product(range(k), repeat=n):
