@@ -1,0 +1,244 @@
+/*
+ * mog.h -- C ABI of libmog, Mixture-of-Gaussians (Iceberg) decode attention
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one of "Iceberg Attention: Sublinear Long-Context
+ * Decoding with Mixture-of-Gaussians" (abstract): after prefill the keys of
+ * every attention head are partitioned into about sqrt(N) clusters, each
+ * split into about log2(N) subclusters, and every group is summarised by a
+ * Gaussian; at each decode step the query is scored against the summaries,
+ * the best clusters and subclusters are attended exactly and the rest of the
+ * cache is estimated from the groups' means and variances.  Following the
+ * retrieval-completion attention page (abstract), sink and tail anchor
+ * tokens are always attended exactly, and the exact and estimated parts are
+ * added as unnormalised numerator and denominator before one normalisation.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer marked DEVICE is caller-owned device memory; the library
+ *    never allocates, frees or synchronises.  HOST pointers are read during
+ *    the call only.
+ *  - All GPU work is enqueued on the caller's stream; the call returns as
+ *    soon as it is enqueued.  A fault inside a kernel shows up at the
+ *    caller's next synchronisation, not as a return code.
+ *  - Arguments are validated before anything is enqueued; a call that
+ *    returns an error has enqueued nothing.  mog_last_error() then returns a
+ *    description (per thread).
+ *  - Layouts: keys/values are row-major with head_dim contiguous elements per
+ *    token.  Queries and outputs are float32 [n_seq][n_q_heads][head_dim];
+ *    query head h reads KV head h / (n_q_heads / n_kv_heads).
+ *  - NaN or Inf in inputs propagate; they are not checked.
+ *
+ * Limits: head_dim 64 or 128; 1 <= n_q_heads / n_kv_heads <= 8;
+ * n_seq <= MOG_MAX_SEQ; per-sequence length N with n_sink + n_recent < N and
+ * N <= MOG_MAX_LEN; keys within |k| < 65536 (the build sums them in 64-bit
+ * fixed point).
+ */
+#ifndef MOG_H
+#define MOG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOG_MAX_SEQ 256
+#define MOG_MAX_LEN (1 << 22)
+
+typedef enum {
+  MOG_OK = 0,
+  MOG_ERR_INVALID_ARG = 1, /* null pointer, bad size, inconsistent shapes   */
+  MOG_ERR_UNSUPPORTED = 2, /* a valid request this build does not cover    */
+  MOG_ERR_WORKSPACE = 3,   /* workspace or layout buffer too small          */
+  MOG_ERR_HIP = 4          /* a HIP launch or runtime call failed           */
+} mog_status;
+
+typedef enum { MOG_F32 = 0, MOG_BF16 = 1 } mog_dtype;
+
+typedef enum { MOG_KV_CONTIGUOUS = 0, MOG_KV_PAGED = 1 } mog_kv_format;
+
+/* The KV cache of a batch of sequences.
+ *
+ * CONTIGUOUS: k and v are DEVICE arrays [n_seq][n_kv_heads][max_len][head_dim]
+ *   of `dtype`; sequence s uses its first seq_lens[s] rows.
+ * PAGED: k and v are DEVICE page pools [n_pages][n_kv_heads][page_size][head_dim];
+ *   block_table is a DEVICE int32 array [n_seq][max_blocks]; token t of
+ *   sequence s lives in page block_table[s][t / page_size], slot
+ *   t % page_size.  The table must hold valid page ids for every used block.
+ * seq_lens is a HOST int32 array [n_seq]. */
+typedef struct {
+  int32_t format;     /* mog_kv_format */
+  int32_t dtype;      /* mog_dtype     */
+  int32_t n_seq;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t max_len;    /* CONTIGUOUS: rows per (seq, head); PAGED: unused   */
+  int32_t page_size;  /* PAGED only (any power of two, 1..256)             */
+  int32_t n_pages;    /* PAGED only: pages in the pool                     */
+  int32_t max_blocks; /* PAGED only: columns of block_table                */
+  const int32_t* seq_lens;    /* HOST   [n_seq]                  */
+  const void* k;              /* DEVICE                          */
+  const void* v;              /* DEVICE                          */
+  const int32_t* block_table; /* DEVICE [n_seq][max_blocks], PAGED only */
+} mog_kv;
+
+/* Shape of a layout (what mog_layout_size needs). */
+typedef struct {
+  int32_t n_seq;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;            /* dtype of the reordered K/V copy (= the cache's) */
+  int32_t n_sink;           /* anchors at the start of every sequence */
+  int32_t n_recent;         /* anchors at the end of every sequence   */
+  const int32_t* seq_lens;  /* HOST [n_seq] */
+} mog_dims;
+
+/* Per-unit geometry, one unit = one (sequence, KV head); unit id
+ * u = seq * n_kv_heads + kv_head.  C = min(ceil(sqrt(N)), N_mid) clusters,
+ * S = ceil(log2(N)) subclusters per cluster, N_mid = N - n_sink - n_recent
+ * middle-region tokens (the clustered part). */
+typedef struct {
+  int32_t seq, kv_head;
+  int32_t N, n_mid;
+  int32_t C, S;
+  int32_t reserved0, reserved1;
+  int64_t row_base; /* first row of this unit in k_mid / v_mid / perm        */
+  int64_t cl_base;  /* first cluster of this unit in cl_ms / cl_vbar         */
+  int64_t sub_base; /* first subcluster of this unit in sub_ms / sub_vbar    */
+  int64_t off_base; /* first entry of this unit's C*S+1 offsets in sub_off   */
+} mog_unit;
+
+/* A built (or imported) cluster layout.  Plain descriptor: every pointer
+ * points into the caller's layout buffer.
+ *  k_mid, v_mid  [total_mid][head_dim] dtype: the middle region of every unit,
+ *                rows ordered by (cluster, subcluster, token position).
+ *  perm          [total_mid] int32: token position of every reordered row.
+ *  sub_off       per unit C*S+1 int32 row offsets relative to row_base;
+ *                subcluster i of cluster j owns rows [sub_off[j*S+i],
+ *                sub_off[j*S+i+1]); cluster j owns [sub_off[j*S], sub_off[(j+1)*S]).
+ *  cl_ms, sub_ms [groups][2*head_dim] float32: mean key (first head_dim
+ *                entries) then diagonal population variance of the keys.
+ *  cl_vbar, sub_vbar [groups][head_dim] float32: mean value.
+ *  units         DEVICE copy of the mog_unit table (n_units entries). */
+typedef struct {
+  int32_t n_seq, n_kv_heads, head_dim, dtype, n_sink, n_recent;
+  int32_t n_units;
+  int32_t max_C, max_S;
+  int32_t seq_lens[MOG_MAX_SEQ];
+  int64_t total_mid, total_cl, total_sub, total_off;
+  mog_unit* units;
+  void* k_mid;
+  void* v_mid;
+  int32_t* perm;
+  int32_t* sub_off;
+  float* cl_ms;
+  float* cl_vbar;
+  float* sub_ms;
+  float* sub_vbar;
+} mog_layout;
+
+typedef struct {
+  int32_t kmeans_iters; /* Lloyd rounds before the final assignment (10)   */
+  int32_t n_sink;
+  int32_t n_recent;
+  int32_t reserved;
+  uint64_t seed;        /* seeds the Forgy initialisation of every unit    */
+} mog_build_params;
+
+typedef struct {
+  int32_t n_q_heads;            /* Hq; Hq / n_kv_heads query heads per KV head */
+  int32_t top_c;                /* clusters attended exactly per query head     */
+  int32_t top_s;                /* subclusters per chosen cluster               */
+  int32_t residual;             /* 1: add the Gaussian estimate of the rest;
+                                   0: exact part only, renormalised            */
+  float scale;                  /* logit scale; 0 selects 1/sqrt(head_dim)      */
+  int32_t splits;               /* 0: automatic; else exact-attention splits per unit */
+  const int32_t* top_c_per_seq; /* HOST [n_seq] or NULL (then top_c)           */
+  const int32_t* top_s_per_seq; /* HOST [n_seq] or NULL (then top_s)           */
+} mog_decode_params;
+
+typedef enum { MOG_OP_BUILD = 0, MOG_OP_DECODE = 1, MOG_OP_DENSE = 2 } mog_op;
+
+/* ---------------------------------------------------------------------- */
+
+/* Bytes of the layout buffer for `dims`.  Pure host computation. */
+mog_status mog_layout_size(const mog_dims* dims, size_t* bytes);
+
+/* Carve `layout_mem` (DEVICE, >= mog_layout_size bytes, 256-byte aligned)
+ * into a layout for `dims`, fill `out` (host) and enqueue the write of the
+ * device unit table.  mog_build calls this itself; it is exported so a
+ * caller can import a layout computed elsewhere by writing the arrays. */
+mog_status mog_layout_init(const mog_dims* dims, void* layout_mem, size_t layout_bytes,
+                           mog_layout* out, hipStream_t stream);
+
+/* Host copy of the geometry of unit `unit` of a layout. */
+mog_status mog_layout_unit(const mog_layout* layout, int32_t unit, mog_unit* out);
+
+/* Workspace bytes for an operation.
+ *  MOG_OP_BUILD : `kv` and `bp` used (layout geometry follows from them).
+ *  MOG_OP_DECODE: `layout` and `dp` used.
+ *  MOG_OP_DENSE : `kv` and `dp` used (n_q_heads, splits).
+ * Unused arguments may be NULL. */
+mog_status mog_workspace_size(mog_op op, const mog_kv* kv, const mog_layout* layout,
+                              const mog_build_params* bp, const mog_decode_params* dp,
+                              size_t* bytes);
+
+/* Prefill-side build (Iceberg Attention abstract: hierarchical partition of
+ * each head's keys, one Gaussian per group): for every unit, seeded Forgy
+ * k-means of the middle-region keys into C clusters (kmeans_iters rounds,
+ * then a final assignment), k-means of every cluster into min(S, n)
+ * subclusters, reordering of K/V into cluster-contiguous rows, and the
+ * per-group statistics.  Fills `out`.  `ws`: DEVICE scratch of
+ * mog_workspace_size(MOG_OP_BUILD) bytes. */
+mog_status mog_build(const mog_kv* kv, const mog_build_params* params, void* layout_mem,
+                     size_t layout_bytes, void* ws, size_t ws_bytes, mog_layout* out,
+                     hipStream_t stream);
+
+/* One decode step (Iceberg Attention abstract; merge rule of the
+ * retrieval-completion page's abstract).  Per query head: score every
+ * cluster by ln n + scale q.mu + scale^2/2 sum q_i^2 var_i, take the top_c
+ * clusters, score their subclusters the same way, take top_s in each;
+ * attend exactly over the anchors (read from `kv`) and the chosen
+ * subclusters' rows (read from the layout); add exp(score) and
+ * exp(score) * vbar of every group left out; normalise once.
+ *  q    DEVICE float32 [n_seq][n_q_heads][head_dim]
+ *  out  DEVICE float32 [n_seq][n_q_heads][head_dim]
+ *  lse  DEVICE float32 [n_seq][n_q_heads] natural-log normaliser, or NULL
+ *  sel_c DEVICE int32 [n_seq][n_q_heads][cmax] chosen cluster ids, ascending,
+ *        padded with -1 (cmax = max over sequences of top_c), or NULL
+ *  sel_s DEVICE int32 [n_seq][n_q_heads][cmax][smax] chosen subcluster ids
+ *        (0..S-1) of the k-th chosen cluster, ascending, padded with -1
+ *        (smax = max top_s), or NULL.  Selection outputs are left
+ *        untouched when the corresponding maximum budget is 0.
+ *  ws   DEVICE scratch of mog_workspace_size(MOG_OP_DECODE) bytes.  Its first
+ *        256 bytes must be zero before the first call; the library leaves
+ *        them zero.
+ * Calls that share a workspace must not overlap. */
+mog_status mog_decode(const mog_layout* layout, const mog_kv* kv, const float* q,
+                      const mog_decode_params* params, float* out, float* lse,
+                      int32_t* sel_c, int32_t* sel_s, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
+
+/* Exact dense decode attention over all tokens of every sequence (the
+ * in-library baseline): out = softmax(scale K q)^T V.  Same q/out/lse/ws
+ * conventions as mog_decode; only n_q_heads, scale and splits of `params`
+ * are used. */
+mog_status mog_dense_decode(const mog_kv* kv, const float* q, const mog_decode_params* params,
+                            float* out, float* lse, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/* Static text of a status code. */
+const char* mog_status_string(mog_status status);
+
+/* Description of the last error raised on the calling thread ("" if none). */
+const char* mog_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOG_H */

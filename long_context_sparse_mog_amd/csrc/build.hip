@@ -1,0 +1,672 @@
+// Prefill-side build of libmog ("Iceberg Attention" abstract: after prefill,
+// partition the keys of each head into about sqrt(N) clusters and about
+// log2(N) subclusters per cluster and represent every group by a Gaussian).
+//
+// Per unit (sequence, KV head), over the middle-region keys:
+//   1. Forgy init: C distinct keys drawn by a partial Fisher-Yates shuffle
+//      driven by SplitMix64 (Steele, Lea & Flood, OOPSLA 2014).
+//   2. Lloyd rounds: nearest centroid by ||mu||^2 - 2 x.mu (lowest id wins a
+//      tie), new centroid = mean of its keys (an empty cluster keeps its
+//      centroid).  Sums are accumulated in 64-bit fixed point (keys scaled by
+//      2^24), so the result does not depend on the order of the atomics.
+//   3. Final assignment, stable grouping of the keys by cluster.
+//   4. Per cluster, the same k-means with k = min(S, n) on its members,
+//      then stable grouping by subcluster: rows ordered by (cluster,
+//      subcluster, token position).
+//   5. Copy of the K/V rows into that order, and per-group statistics: count
+//      (offsets), mean key, population variance of the keys, mean value.
+#include "mog_internal.h"
+
+namespace mog {
+
+constexpr unsigned long long kGamma = 0x9E3779B97F4A7C15ull;
+constexpr unsigned long long kMix1 = 0xBF58476D1CE4E5B9ull;
+constexpr unsigned long long kMix2 = 0x94D049BB133111EBull;
+constexpr unsigned long long kSubStreamMul = 0xD1B54A32D192ED03ull;
+constexpr float kFixScale = 16777216.0f;  // 2^24
+
+__device__ inline unsigned long long splitmix_next(unsigned long long& state) {
+  state += kGamma;
+  unsigned long long z = state;
+  z = (z ^ (z >> 30)) * kMix1;
+  z = (z ^ (z >> 27)) * kMix2;
+  return z ^ (z >> 31);
+}
+
+__device__ inline unsigned long long unit_prng_state(unsigned long long seed, int unit) {
+  return seed ^ (kGamma * (unsigned long long)(1 + unit));
+}
+
+struct BArgs {
+  const mog_unit* units;
+  KVRef kv;
+  int n_sink, D;
+  float* cent;
+  float* cent_norm;
+  unsigned long long* sums;
+  int32_t* counts;
+  int32_t* labels;
+  int32_t* cl_start;
+  int32_t* members;
+  int32_t* sublab;
+  int32_t* perm;
+  int32_t* sub_off;
+  void* k_mid;
+  void* v_mid;
+  float* cl_ms;
+  float* cl_vbar;
+  float* sub_ms;
+  float* sub_vbar;
+  unsigned long long seed;
+};
+
+template <typename T>
+__device__ inline float elem(const T* p, int64_t i);
+template <>
+__device__ inline float elem<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ inline float elem<uint16_t>(const uint16_t* p, int64_t i) {
+  return __uint_as_float((uint32_t)p[i] << 16);
+}
+
+// ---------------------------------------------------------------------------
+// 1a. Forgy draw of one unit: one thread runs the partial Fisher-Yates
+//     shuffle of [0, n_mid) with an open-addressing map (in LDS) of the
+//     positions already swapped.  The C drawn ids go to labels[row_base + i].
+// ---------------------------------------------------------------------------
+constexpr int kHashSize = 8192;  // >= 2 * (2 * kMaxC) entries: load <= 1/2
+
+__device__ inline int hash_slot(int key) { return (int)(((uint32_t)key * 2654435761u) >> 19); }
+
+__device__ inline int map_get(const int* hk, const int* hv, int key) {
+  int s = hash_slot(key);
+  while (true) {
+    const int k = hk[s];
+    if (k == key) return hv[s];
+    if (k < 0) return key;
+    s = (s + 1) & (kHashSize - 1);
+  }
+}
+
+__device__ inline void map_put(int* hk, int* hv, int key, int val) {
+  int s = hash_slot(key);
+  while (hk[s] >= 0 && hk[s] != key) s = (s + 1) & (kHashSize - 1);
+  hk[s] = key;
+  hv[s] = val;
+}
+
+__global__ __launch_bounds__(256) void k_forgy(BArgs a) {
+  __shared__ int hk[kHashSize];
+  __shared__ int hv[kHashSize];
+  const int u = blockIdx.x;
+  const mog_unit U = a.units[u];
+  for (int i = threadIdx.x; i < kHashSize; i += 256) hk[i] = -1;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long st = unit_prng_state(a.seed, u);
+    const int n = U.n_mid;
+    for (int i = 0; i < U.C; ++i) {
+      const unsigned long long r = splitmix_next(st);
+      const int j = i + (int)(r % (unsigned long long)(n - i));
+      const int vi = map_get(hk, hv, i);
+      const int vj = map_get(hk, hv, j);
+      map_put(hk, hv, i, vj);
+      map_put(hk, hv, j, vi);
+      a.labels[U.row_base + i] = vj;
+    }
+  }
+}
+
+// 1b. Centroid i of unit u = key of middle position labels[row_base + i];
+//     also zero the fixed-point sums and counts.  One wave per centroid.
+template <int D, typename T>
+__global__ __launch_bounds__(256) void k_init_centroids(BArgs a) {
+  const int u = blockIdx.y;
+  const mog_unit U = a.units[u];
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (i >= U.C) return;
+  const int id = a.labels[U.row_base + i];
+  const T* kb = static_cast<const T*>(a.kv.k) + kv_row_offset(a.kv, U.seq, U.kv_head, a.n_sink + id, D);
+  const int64_t cg = U.cl_base + i;
+  float nrm = 0.f;
+  for (int d = lane; d < D; d += 64) {
+    const float x = elem<T>(kb, d);
+    a.cent[cg * D + d] = x;
+    nrm += x * x;
+    a.sums[cg * D + d] = 0ull;
+  }
+  nrm = wave_sum(nrm);
+  if (lane == 0) {
+    a.cent_norm[cg] = nrm;
+    a.counts[cg] = 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. Assignment of 64 keys per block against all centroids of the unit:
+//    register-blocked 4x4 dot products from LDS tiles, running argmin of
+//    ||mu||^2 - 2 x.mu; then (optionally) fixed-point sums of the key into
+//    its cluster, and the cluster count.
+// ---------------------------------------------------------------------------
+template <int D, typename T>
+__global__ __launch_bounds__(256) void k_assign(BArgs a, int accumulate) {
+  __shared__ float xs[D * 64];   // [d][key]
+  __shared__ float cs[D * 64];   // [d][centroid]
+  __shared__ float cn[64];
+  const int u = blockIdx.y;
+  const mog_unit U = a.units[u];
+  const int k0 = blockIdx.x * 64;
+  if (k0 >= U.n_mid) return;
+  const int tid = threadIdx.x;
+  const int nk = min(64, U.n_mid - k0);
+  const T* kbase = static_cast<const T*>(a.kv.k);
+  // stage keys, transposed
+  for (int idx = tid; idx < 64 * D; idx += 256) {
+    const int kk = idx / D, d = idx % D;
+    float x = 0.f;
+    if (kk < nk) x = elem<T>(kbase, kv_row_offset(a.kv, U.seq, U.kv_head, a.n_sink + k0 + kk, D) + d);
+    xs[d * 64 + kk] = x;
+  }
+  const int tk = tid & 15, tc = tid >> 4;   // keys tk*4.., centroids tc*4..
+  float best[4];
+  int bid[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    best[i] = INFINITY;
+    bid[i] = 0x7fffffff;
+  }
+  for (int c0 = 0; c0 < U.C; c0 += 64) {
+    __syncthreads();
+    const int nc = min(64, U.C - c0);
+    for (int idx = tid; idx < 64 * D; idx += 256) {
+      const int cc = idx / D, d = idx % D;
+      cs[d * 64 + cc] = cc < nc ? a.cent[(U.cl_base + c0 + cc) * D + d] : 0.f;
+    }
+    if (tid < 64) cn[tid] = tid < nc ? a.cent_norm[U.cl_base + c0 + tid] : INFINITY;
+    __syncthreads();
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+#pragma unroll 8
+    for (int d = 0; d < D; ++d) {
+      const float4 xv = *reinterpret_cast<const float4*>(&xs[d * 64 + tk * 4]);
+      const float4 cv = *reinterpret_cast<const float4*>(&cs[d * 64 + tc * 4]);
+      const float xa[4] = {xv.x, xv.y, xv.z, xv.w};
+      const float ca[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] += xa[i] * ca[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int cid = c0 + tc * 4 + j;
+      const float nrm = cn[tc * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float dist = nrm - 2.f * acc[i][j];
+        if (dist < best[i]) {  // centroids visited in increasing id: ties keep the lower id
+          best[i] = dist;
+          bid[i] = cid;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // reduce over the 16 centroid groups of each key
+  float* rb = cs;                                   // [16][64] distances
+  int* ri = reinterpret_cast<int*>(cs + 16 * 64);   // [16][64] ids
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    rb[tc * 64 + tk * 4 + i] = best[i];
+    ri[tc * 64 + tk * 4 + i] = bid[i];
+  }
+  __syncthreads();
+  __shared__ int lab[64];
+  if (tid < 64) {
+    float b = rb[tid];
+    int id = ri[tid];
+    for (int g = 1; g < 16; ++g) {
+      const float v = rb[g * 64 + tid];
+      const int vid = ri[g * 64 + tid];
+      if (v < b || (v == b && vid < id)) {
+        b = v;
+        id = vid;
+      }
+    }
+    if (id < 0 || id >= U.C) id = 0;  // only reachable for non-finite keys
+    lab[tid] = id;
+    if (tid < nk) {
+      a.labels[U.row_base + k0 + tid] = id;
+      atomicAdd(&a.counts[U.cl_base + id], 1);
+    }
+  }
+  if (!accumulate) return;
+  __syncthreads();
+  for (int idx = tid; idx < nk * D; idx += 256) {
+    const int kk = idx / D, d = idx % D;
+    const long long fx = __float2ll_rn(xs[d * 64 + kk] * kFixScale);
+    atomicAdd(&a.sums[(U.cl_base + lab[kk]) * D + d], (unsigned long long)fx);
+  }
+}
+
+// 2b. New centroid = fixed-point sum / count (empty keeps); zero the sums.
+template <int D>
+__global__ __launch_bounds__(256) void k_update(BArgs a) {
+  const int u = blockIdx.y;
+  const mog_unit U = a.units[u];
+  const int lane = threadIdx.x & 63;
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (j >= U.C) return;
+  const int64_t cg = U.cl_base + j;
+  const int n = a.counts[cg];
+  float nrm = 0.f;
+  for (int d = lane; d < D; d += 64) {
+    float c = a.cent[cg * D + d];
+    if (n > 0) {
+      const long long s = (long long)a.sums[cg * D + d];
+      c = (float)((double)s / (double)kFixScale / (double)n);
+      a.cent[cg * D + d] = c;
+    }
+    nrm += c * c;
+    a.sums[cg * D + d] = 0ull;
+  }
+  nrm = wave_sum(nrm);
+  if (lane == 0) {
+    a.cent_norm[cg] = nrm;
+    a.counts[cg] = 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3a. Exclusive prefix of the final cluster counts -> first member slot.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_cluster_starts(BArgs a) {
+  __shared__ int sh[16];
+  __shared__ int carry;
+  const int u = blockIdx.x, tid = threadIdx.x;
+  const mog_unit U = a.units[u];
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < U.C; base += 1024) {
+    const int j = base + tid;
+    const int v = j < U.C ? a.counts[U.cl_base + j] : 0;
+    int x = v;
+    const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) sh[wave] = x;
+    __syncthreads();
+    int off = carry, tot = 0;
+    for (int w = 0; w < 16; ++w) {
+      off += (w < wave) ? sh[w] : 0;
+      tot += sh[w];
+    }
+    if (j < U.C) a.cl_start[U.cl_base + j] = off + x - v;
+    __syncthreads();
+    if (tid == 0) carry += tot;
+    __syncthreads();
+  }
+}
+
+// 3b. Stable grouping: block (b, u) scans all middle keys of unit u in order
+//     and appends those of clusters [8b, 8b+8) to their member lists.
+__global__ __launch_bounds__(1024) void k_group_members(BArgs a) {
+  __shared__ int cnt[16][8];
+  __shared__ int run[8];
+  __shared__ int start[8];
+  const int u = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const mog_unit U = a.units[u];
+  const int j0 = blockIdx.x * 8;
+  if (j0 >= U.C) return;
+  if (tid < 8) {
+    run[tid] = 0;
+    start[tid] = (j0 + tid < U.C) ? a.cl_start[U.cl_base + j0 + tid] : 0;
+  }
+  __syncthreads();
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  for (int base = 0; base < U.n_mid; base += 1024) {
+    const int i = base + tid;
+    int slot = -1;
+    if (i < U.n_mid) {
+      const int lab = a.labels[U.row_base + i];
+      if (lab >= j0 && lab < j0 + 8) slot = lab - j0;
+    }
+    int myrank = 0;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const unsigned long long b = __ballot(slot == s);
+      if (slot == s) myrank = __popcll(b & lt);
+      if (lane == 0) cnt[wave][s] = __popcll(b);
+    }
+    __syncthreads();
+    if (slot >= 0) {
+      int pos = run[slot] + myrank;
+      for (int w = 0; w < wave; ++w) pos += cnt[w][slot];
+      a.members[U.row_base + start[slot] + pos] = i;
+    }
+    __syncthreads();
+    if (tid < 8) {
+      int t = 0;
+      for (int w = 0; w < 16; ++w) t += cnt[w][tid];
+      run[tid] += t;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 4. Subcluster k-means of one cluster per block, then the stable order of
+//    its members by subcluster: writes perm and the cluster's S offsets.
+// ---------------------------------------------------------------------------
+template <int D, typename T>
+__global__ __launch_bounds__(256) void k_subkmeans(BArgs a, int iters) {
+  __shared__ float cen[kMaxS][D];
+  __shared__ float cnorm[kMaxS];
+  __shared__ float acc[2][kMaxS][D];
+  __shared__ int scount[kMaxS];
+  __shared__ int sstart[kMaxS + 1];
+  __shared__ int ids[kMaxS];
+  __shared__ int wcnt[4][kMaxS];
+  __shared__ int run[kMaxS];
+  const int u = blockIdx.y, j = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const mog_unit U = a.units[u];
+  if (j >= U.C) return;
+  const int S = U.S;
+  const int64_t cg = U.cl_base + j;
+  const int cl0 = a.cl_start[cg];
+  const int n = (j + 1 < U.C ? a.cl_start[cg + 1] : U.n_mid) - cl0;
+  int32_t* off = a.sub_off + U.off_base;
+  if (j == U.C - 1 && tid == 0) off[U.C * S] = U.n_mid;
+  if (n == 0) {
+    for (int i = tid; i < S; i += 256) off[j * S + i] = cl0;
+    return;
+  }
+  const int k = n < S ? n : S;
+  const int32_t* mem = a.members + U.row_base + cl0;
+  int32_t* sl = a.sublab + U.row_base + cl0;
+  const T* kb = static_cast<const T*>(a.kv.k);
+  // Forgy draw over [0, n): k <= 32 steps, the swapped positions kept in a
+  // short list (at most 2k entries)
+  if (tid == 0) {
+    unsigned long long st = unit_prng_state(a.seed, u) ^ (kSubStreamMul * (unsigned long long)(j + 1));
+    int pk[2 * kMaxS], pv[2 * kMaxS], np = 0;
+    auto get = [&](int key) {
+      for (int e = 0; e < np; ++e)
+        if (pk[e] == key) return pv[e];
+      return key;
+    };
+    auto put = [&](int key, int val) {
+      for (int e = 0; e < np; ++e)
+        if (pk[e] == key) {
+          pv[e] = val;
+          return;
+        }
+      pk[np] = key;
+      pv[np] = val;
+      ++np;
+    };
+    for (int i = 0; i < k; ++i) {
+      const unsigned long long r = splitmix_next(st);
+      const int jj = i + (int)(r % (unsigned long long)(n - i));
+      const int vi = get(i), vj = get(jj);
+      put(i, vj);
+      put(jj, vi);
+      ids[i] = vj;
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < k * D; idx += 256) {
+    const int c = idx / D, d = idx % D;
+    const int m = mem[ids[c]];
+    cen[c][d] = elem<T>(kb, kv_row_offset(a.kv, U.seq, U.kv_head, a.n_sink + m, D) + d);
+  }
+  __syncthreads();
+  for (int round = 0; round <= iters; ++round) {
+    // norms of the current centroids
+    if (tid < k) {
+      float s = 0.f;
+      for (int d = 0; d < D; ++d) s += cen[tid][d] * cen[tid][d];
+      cnorm[tid] = s;
+    }
+    if (tid < kMaxS) scount[tid] = 0;
+    __syncthreads();
+    // assignment: one member per thread
+    for (int m = tid; m < n; m += 256) {
+      const int64_t ro = kv_row_offset(a.kv, U.seq, U.kv_head, a.n_sink + mem[m], D);
+      float dot[kMaxS];
+#pragma unroll
+      for (int c = 0; c < kMaxS; ++c) dot[c] = 0.f;
+      for (int d0 = 0; d0 < D; d0 += 8) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = elem<T>(kb, ro + d0 + e);
+#pragma unroll
+        for (int c = 0; c < kMaxS; ++c) {
+          if (c < k) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dot[c] += x[e] * cen[c][d0 + e];
+          }
+        }
+      }
+      float best = INFINITY;
+      int bid = 0;
+#pragma unroll
+      for (int c = 0; c < kMaxS; ++c) {
+        if (c < k) {
+          const float dist = cnorm[c] - 2.f * dot[c];
+          if (dist < best) {
+            best = dist;
+            bid = c;
+          }
+        }
+      }
+      sl[m] = bid;
+      atomicAdd(&scount[bid], 1);
+    }
+    __syncthreads();
+    if (round == iters) break;
+    // update: thread (d, phase) sums its dimension over its half of the members
+    const int d = tid % D, ph = tid / D;          // D=128: 2 phases, D=64: 4 phases (use first 2)
+    if (ph < 2) {
+      for (int c = 0; c < k; ++c) acc[ph][c][d] = 0.f;
+      for (int m = ph; m < n; m += 2) {
+        const int c = sl[m];
+        acc[ph][c][d] += elem<T>(kb, kv_row_offset(a.kv, U.seq, U.kv_head, a.n_sink + mem[m], D) + d);
+      }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < k * D; idx += 256) {
+      const int c = idx / D, dd = idx % D;
+      if (scount[c] > 0) cen[c][dd] = (acc[0][c][dd] + acc[1][c][dd]) / (float)scount[c];
+    }
+    __syncthreads();
+  }
+  // offsets of the subclusters inside the cluster
+  if (tid == 0) {
+    int s = 0;
+    for (int c = 0; c < S; ++c) {
+      sstart[c] = s;
+      run[c] = 0;
+      s += c < k ? scount[c] : 0;
+    }
+    sstart[S] = s;
+  }
+  __syncthreads();
+  for (int i = tid; i < S; i += 256) off[j * S + i] = cl0 + sstart[i];
+  // stable scatter of the members by subcluster
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  for (int base = 0; base < n; base += 256) {
+    const int m = base + tid;
+    const int lab = m < n ? sl[m] : -1;
+    int myrank = 0;
+    for (int c = 0; c < k; ++c) {
+      const unsigned long long b = __ballot(lab == c);
+      if (lab == c) myrank = __popcll(b & lt);
+      if (lane == 0) wcnt[wave][c] = __popcll(b);
+    }
+    __syncthreads();
+    if (lab >= 0) {
+      int pos = sstart[lab] + run[lab] + myrank;
+      for (int w = 0; w < wave; ++w) pos += wcnt[w][lab];
+      a.perm[U.row_base + cl0 + pos] = a.n_sink + mem[m];
+    }
+    __syncthreads();
+    if (tid < k) run[tid] += wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 5a. Copy K/V rows into (cluster, subcluster, position) order: 16-byte
+//     pieces, rows spread over the wave.
+// ---------------------------------------------------------------------------
+template <int D, typename T>
+__global__ __launch_bounds__(256) void k_gather_rows(BArgs a) {
+  constexpr int EL = 16 / sizeof(T);      // elements per 16-byte piece
+  constexpr int LPR = D / EL;             // lanes per row
+  constexpr int RPW = 64 / LPR;           // rows per wave step
+  const int u = blockIdx.y;
+  const mog_unit U = a.units[u];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = (blockIdx.x * 4 + wave) * RPW + lane / LPR;
+  if (r >= U.n_mid) return;
+  const int t = a.perm[U.row_base + r];
+  const int64_t src = kv_row_offset(a.kv, U.seq, U.kv_head, t, D) + (lane % LPR) * EL;
+  const int64_t dst = (U.row_base + r) * D + (lane % LPR) * EL;
+  const uint4* ks = reinterpret_cast<const uint4*>(static_cast<const T*>(a.kv.k) + src);
+  const uint4* vs = reinterpret_cast<const uint4*>(static_cast<const T*>(a.kv.v) + src);
+  *reinterpret_cast<uint4*>(static_cast<T*>(a.k_mid) + dst) = *ks;
+  *reinterpret_cast<uint4*>(static_cast<T*>(a.v_mid) + dst) = *vs;
+}
+
+// 5b. Statistics of one cluster and its subclusters: two passes over the
+//     reordered keys (means, then centred squares), one over the values,
+//     accumulated in float64, stored in float32.  Thread (d, phase) owns
+//     dimension d of every NPH-th row.
+template <int D, typename T>
+__global__ __launch_bounds__(256) void k_group_stats(BArgs a) {
+  constexpr int NPH = 256 / D;
+  __shared__ double rk[NPH][D];
+  __shared__ double rv[NPH][D];
+  const int u = blockIdx.y, j = blockIdx.x, tid = threadIdx.x;
+  const mog_unit U = a.units[u];
+  if (j >= U.C) return;
+  const int S = U.S;
+  const int32_t* off = a.sub_off + U.off_base;
+  const int64_t cg = U.cl_base + j;
+  const T* km = static_cast<const T*>(a.k_mid);
+  const T* vm = static_cast<const T*>(a.v_mid);
+  const int d = tid % D, ph = tid / D;
+  // g = -1 is the cluster itself, g >= 0 its subclusters
+  for (int g = -1; g < S; ++g) {
+    const int r0 = g < 0 ? off[j * S] : off[j * S + g];
+    const int r1 = g < 0 ? off[(j + 1) * S] : off[j * S + g + 1];
+    const int n = r1 - r0;
+    float* ms = g < 0 ? a.cl_ms + cg * 2 * D : a.sub_ms + (U.sub_base + (int64_t)j * S + g) * 2 * D;
+    float* vb = g < 0 ? a.cl_vbar + cg * D : a.sub_vbar + (U.sub_base + (int64_t)j * S + g) * D;
+    if (n == 0) {
+      if (ph == 0) {
+        ms[d] = 0.f;
+        ms[D + d] = 0.f;
+        vb[d] = 0.f;
+      }
+      continue;
+    }
+    double sk = 0.0, sv = 0.0;
+    for (int r = r0 + ph; r < r1; r += NPH) {
+      sk += (double)elem<T>(km, (U.row_base + r) * D + d);
+      sv += (double)elem<T>(vm, (U.row_base + r) * D + d);
+    }
+    rk[ph][d] = sk;
+    rv[ph][d] = sv;
+    __syncthreads();
+    double tk = 0.0, tv = 0.0;
+#pragma unroll
+    for (int p = 0; p < NPH; ++p) {
+      tk += rk[p][d];
+      tv += rv[p][d];
+    }
+    const double mean = tk / n, vmean = tv / n;
+    __syncthreads();
+    double sq = 0.0;
+    for (int r = r0 + ph; r < r1; r += NPH) {
+      const double x = (double)elem<T>(km, (U.row_base + r) * D + d) - mean;
+      sq += x * x;
+    }
+    rk[ph][d] = sq;
+    __syncthreads();
+    if (ph == 0) {
+      double t = 0.0;
+#pragma unroll
+      for (int p = 0; p < NPH; ++p) t += rk[p][d];
+      ms[d] = (float)mean;
+      ms[D + d] = (float)(t / n);
+      vb[d] = (float)vmean;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launcher
+// ---------------------------------------------------------------------------
+template <int D, typename T>
+static hipError_t build_impl(const BuildLaunch& x, hipStream_t s) {
+  BArgs a;
+  a.units = x.L.units;
+  a.kv = x.kv;
+  a.n_sink = x.L.n_sink;
+  a.D = D;
+  a.cent = x.ws.cent;
+  a.cent_norm = x.ws.cent_norm;
+  a.sums = x.ws.sums;
+  a.counts = x.ws.counts;
+  a.labels = x.ws.labels;
+  a.cl_start = x.ws.cl_start;
+  a.members = x.ws.members;
+  a.sublab = x.ws.sublab;
+  a.perm = x.L.perm;
+  a.sub_off = x.L.sub_off;
+  a.k_mid = x.L.k_mid;
+  a.v_mid = x.L.v_mid;
+  a.cl_ms = x.L.cl_ms;
+  a.cl_vbar = x.L.cl_vbar;
+  a.sub_ms = x.L.sub_ms;
+  a.sub_vbar = x.L.sub_vbar;
+  a.seed = x.seed;
+  const int nu = x.L.n_units;
+  int max_mid = 0;
+  for (int si = 0; si < x.seq.n_seq; ++si) {
+    const UnitSizes z = unit_sizes(x.seq.len[si], x.L.n_sink, x.L.n_recent);
+    max_mid = z.n_mid > max_mid ? z.n_mid : max_mid;
+  }
+  const int maxC = x.L.max_C;
+  hipLaunchKernelGGL(k_forgy, dim3(nu), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_init_centroids<D, T>), dim3((maxC + 3) / 4, nu), dim3(256), 0, s, a);
+  for (int it = 0; it < x.iters; ++it) {
+    hipLaunchKernelGGL((k_assign<D, T>), dim3((max_mid + 63) / 64, nu), dim3(256), 0, s, a, 1);
+    hipLaunchKernelGGL((k_update<D>), dim3((maxC + 3) / 4, nu), dim3(256), 0, s, a);
+  }
+  hipLaunchKernelGGL((k_assign<D, T>), dim3((max_mid + 63) / 64, nu), dim3(256), 0, s, a, 0);
+  hipLaunchKernelGGL(k_cluster_starts, dim3(nu), dim3(1024), 0, s, a);
+  hipLaunchKernelGGL(k_group_members, dim3((maxC + 7) / 8, nu), dim3(1024), 0, s, a);
+  hipLaunchKernelGGL((k_subkmeans<D, T>), dim3(maxC, nu), dim3(256), 0, s, a, x.iters);
+  constexpr int RPB = 4 * (64 / (D / (16 / (int)sizeof(T))));
+  hipLaunchKernelGGL((k_gather_rows<D, T>), dim3((max_mid + RPB - 1) / RPB, nu), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_group_stats<D, T>), dim3(maxC, nu), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_build(const BuildLaunch& x, hipStream_t s) {
+  if (x.D == 128) return x.dtype == MOG_BF16 ? build_impl<128, uint16_t>(x, s) : build_impl<128, float>(x, s);
+  return x.dtype == MOG_BF16 ? build_impl<64, uint16_t>(x, s) : build_impl<64, float>(x, s);
+}
+
+}  // namespace mog

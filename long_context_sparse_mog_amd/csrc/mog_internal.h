@@ -1,0 +1,221 @@
+// Internal declarations of libmog: geometry shared by the host API and the
+// kernels, the argument blocks handed to the launchers, and small device
+// helpers.  gfx950 only (64-wide wavefronts).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mog.h"
+
+namespace mog {
+
+constexpr int kWave = 64;
+constexpr int kMaxG = 8;        // query heads per KV head
+constexpr int kMaxS = 32;       // subclusters per cluster (N <= 2^22 gives S <= 22)
+constexpr int kMaxC = 2048;     // clusters per unit (N <= 2^22 gives C <= 2048)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// Geometry: one unit = one (sequence, KV head).  The same arithmetic runs on
+// the host (sizes, carving) and in the layout-table kernel.
+// ---------------------------------------------------------------------------
+
+__host__ __device__ inline int ceil_sqrt_i(int64_t n) {
+  if (n <= 0) return 0;
+  int64_t r = (int64_t)sqrt((double)n);
+  while (r * r > n) --r;
+  while (r * r < n) ++r;
+  return (int)r;
+}
+
+__host__ __device__ inline int ceil_log2_i(int64_t n) {
+  int e = 0;
+  while (((int64_t)1 << e) < n) ++e;
+  return e;
+}
+
+struct UnitSizes {
+  int n_mid, C, S;
+};
+
+__host__ __device__ inline UnitSizes unit_sizes(int N, int n_sink, int n_recent) {
+  UnitSizes s;
+  s.n_mid = N - n_sink - n_recent;
+  int c = ceil_sqrt_i(N);
+  s.C = c < s.n_mid ? c : s.n_mid;
+  int S = ceil_log2_i(N);
+  s.S = S < 1 ? 1 : S;
+  return s;
+}
+
+// Per-sequence numbers passed by value to kernels.
+struct SeqArgs {
+  int32_t n_seq;
+  int32_t len[MOG_MAX_SEQ];
+  int16_t top_c[MOG_MAX_SEQ];
+  int8_t top_s[MOG_MAX_SEQ];
+};
+
+// ---------------------------------------------------------------------------
+// KV cache addressing (contiguous or paged) for kernels.
+// ---------------------------------------------------------------------------
+struct KVRef {
+  const void* k;
+  const void* v;
+  const int32_t* block_table;
+  int32_t paged;
+  int32_t n_kv_heads;
+  int32_t max_len;      // contiguous
+  int32_t page_shift;   // paged: log2(page_size)
+  int32_t max_blocks;   // paged
+};
+
+// Element offset of token t of (seq, kvh) in the K (or V) array.
+__device__ inline int64_t kv_row_offset(const KVRef& kv, int seq, int kvh, int t, int D) {
+  if (!kv.paged) {
+    return ((int64_t)(seq * kv.n_kv_heads + kvh) * kv.max_len + t) * D;
+  }
+  const int blk = t >> kv.page_shift;
+  const int slot = t & ((1 << kv.page_shift) - 1);
+  const int page = kv.block_table[(int64_t)seq * kv.max_blocks + blk];
+  const int64_t row = (((int64_t)page * kv.n_kv_heads + kvh) << kv.page_shift) + slot;
+  return row * D;
+}
+
+// ---------------------------------------------------------------------------
+// Decode launch block.
+// ---------------------------------------------------------------------------
+struct DecodeWS {
+  float* cl_score;      // [total_cl][G]      log2-domain scores
+  uint32_t* cl_mask;    // [total_cl]         heads that chose the cluster
+  int32_t* cl_rank;     // [total_cl][G]      rank among a head's chosen clusters, or -1
+  uint32_t* sub_mask;   // [total_sub]        heads that chose the subcluster
+  float* res_part;      // [n_units][nb_res][G][D+4] residual partials
+  int32_t* run_start;   // [total_sub + 2*n_units]
+  int32_t* run_len;
+  uint32_t* run_mask;
+  int32_t* run_vstart;
+  int32_t* unit_tot;    // [n_units][2]  runs, rows
+  int32_t* wstart;      // [n_units][splits*4][2]
+  float* ex_part;       // [n_units][splits][G][D+4] exact partials
+};
+
+struct DecodeLaunch {
+  mog_layout L;
+  KVRef kv;
+  SeqArgs seq;
+  const float* q;
+  float* out;
+  float* lse;
+  int32_t* sel_c;
+  int32_t* sel_s;
+  int32_t c_stride, s_stride;
+  int32_t Hq, G, D, dtype;
+  int32_t residual;
+  int32_t splits;
+  int32_t nb_res;       // residual blocks per unit (max over units)
+  float scale;
+  DecodeWS ws;
+};
+
+struct DenseLaunch {
+  KVRef kv;
+  SeqArgs seq;
+  const float* q;
+  float* out;
+  float* lse;
+  int32_t Hq, G, D, dtype, n_kv_heads;
+  int32_t splits;
+  float scale;
+  float* ex_part;       // [n_units][splits][G][D+4]
+};
+
+constexpr int kResClustersPerBlock = 16;
+constexpr int kPartPad = 4;   // partial record = o[D], m, l, pad
+
+hipError_t launch_layout_table(const mog_layout& L, const SeqArgs& seq, hipStream_t s);
+hipError_t launch_decode(const DecodeLaunch& a, hipStream_t s);
+hipError_t launch_dense(const DenseLaunch& a, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Build launch block.
+// ---------------------------------------------------------------------------
+struct BuildWS {
+  float* cent;          // [total_cl][D]  centroids
+  float* cent_norm;     // [total_cl]     ||mu||^2
+  unsigned long long* sums;  // [total_cl][D] fixed-point sums
+  int32_t* counts;      // [total_cl]
+  int32_t* labels;      // [total_mid]    cluster of every middle key
+  int32_t* cl_start;    // [total_cl]     first member slot of each cluster
+  int32_t* members;     // [total_mid]    middle-local ids grouped by cluster, ascending
+  int32_t* sublab;      // [total_mid]    subcluster of every member slot
+};
+
+struct BuildLaunch {
+  mog_layout L;
+  KVRef kv;
+  SeqArgs seq;
+  int32_t D, dtype, iters;
+  uint64_t seed;
+  BuildWS ws;
+};
+
+hipError_t launch_build(const BuildLaunch& a, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+#if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// 8 consecutive elements starting at element offset `off` as float32.
+template <typename T>
+__device__ inline void load8(const T* base, int64_t off, float (&x)[8]);
+
+template <>
+__device__ inline void load8<float>(const float* base, int64_t off, float (&x)[8]) {
+  const float4* p = reinterpret_cast<const float4*>(base + off);
+  float4 a = p[0], b = p[1];
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+template <>
+__device__ inline void load8<uint16_t>(const uint16_t* base, int64_t off, float (&x)[8]) {
+  uint4 w = *reinterpret_cast<const uint4*>(base + off);
+  x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x);
+  x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+  x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z);
+  x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+}
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+// Merge partial softmax state (m2, l2, o2) into (m1, l1, o1); log2 domain.
+__device__ inline void merge_scale(float m1, float m2, float& a1, float& a2, float& mnew) {
+  mnew = fmaxf(m1, m2);
+  a1 = (m1 == -INFINITY) ? 0.f : exp2f(m1 - mnew);
+  a2 = (m2 == -INFINITY) ? 0.f : exp2f(m2 - mnew);
+}
+
+// Order-preserving map of a float to uint32 (larger float -> larger key).
+__device__ inline uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+#endif
+
+}  // namespace mog

@@ -1,0 +1,323 @@
+"""Torch-facing wrappers of the libmog C ABI.
+
+Tensors supply device memory and the stream; every computation runs in the
+library's HIP kernels.  Nothing here falls back to a CPU path: without a GPU
+or without the built library every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import math
+
+import numpy as np
+import torch
+
+from . import capi
+from .capi import check, lib
+
+_DTYPES = {torch.float32: capi.MOG_F32, torch.bfloat16: capi.MOG_BF16}
+
+
+def _vp(t):
+    return C.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libmog works on device tensors only")
+
+
+class KVCache:
+    """A batch of KV caches as the library sees it.
+
+    Contiguous: ``k``/``v`` are [n_seq][Hkv][max_len][D].  Paged: ``k``/``v``
+    are page pools [n_pages][Hkv][page][D] and ``block_table`` is
+    [n_seq][max_blocks] int32.  ``seq_lens`` is a host list.
+    """
+
+    def __init__(self, k, v, seq_lens, block_table=None):
+        _require_cuda(k, v, block_table)
+        if k.dtype not in _DTYPES or v.dtype != k.dtype:
+            raise ValueError("k/v must both be float32 or bfloat16")
+        if not (k.is_contiguous() and v.is_contiguous()):
+            raise ValueError("k/v must be contiguous")
+        self.k, self.v, self.block_table = k, v, block_table
+        self.seq_lens = [int(x) for x in seq_lens]
+        self._lens = capi.int_array(self.seq_lens)
+        c = capi.mog_kv()
+        c.dtype = _DTYPES[k.dtype]
+        c.n_seq = len(self.seq_lens)
+        c.n_kv_heads = k.shape[1]
+        c.head_dim = k.shape[3]
+        c.seq_lens = C.cast(self._lens, C.POINTER(capi.i32))
+        c.k = k.data_ptr()
+        c.v = v.data_ptr()
+        if block_table is None:
+            c.format = capi.MOG_KV_CONTIGUOUS
+            c.max_len = k.shape[2]
+        else:
+            if block_table.dtype != torch.int32 or not block_table.is_contiguous():
+                raise ValueError("block_table must be contiguous int32")
+            c.format = capi.MOG_KV_PAGED
+            c.page_size = k.shape[2]
+            c.n_pages = k.shape[0]
+            c.max_blocks = block_table.shape[1]
+            c.block_table = block_table.data_ptr()
+        self.c = c
+
+    @property
+    def n_kv_heads(self):
+        return self.c.n_kv_heads
+
+    @property
+    def head_dim(self):
+        return self.c.head_dim
+
+    @classmethod
+    def from_batch(cls, b, paged=None):
+        """From a ``synth.Batch``; paged follows the workload unless given."""
+        paged = b.wl.paged if paged is None else paged
+        if paged:
+            return cls(b.pool_K, b.pool_V, b.wl.seq_lens, b.block_table)
+        return cls(b.K, b.V, b.wl.seq_lens)
+
+
+class Layout:
+    """A cluster layout living in ``mem`` (a uint8 device tensor)."""
+
+    def __init__(self, c_layout, mem):
+        self.c = c_layout
+        self.mem = mem
+
+    @property
+    def n_units(self):
+        return self.c.n_units
+
+    def unit(self, u: int) -> capi.mog_unit:
+        out = capi.mog_unit()
+        check(lib().mog_layout_unit(C.byref(self.c), u, C.byref(out)), "mog_layout_unit")
+        return out
+
+    def _view(self, ptr, count, dtype):
+        off = ptr - self.mem.data_ptr()
+        nbytes = count * torch.empty((), dtype=dtype).element_size()
+        return self.mem[off:off + nbytes].view(dtype)
+
+    def arrays(self):
+        """Typed device views of every layout array (all units)."""
+        c, D = self.c, self.c.head_dim
+        kd = torch.bfloat16 if c.dtype == capi.MOG_BF16 else torch.float32
+        return dict(
+            k_mid=self._view(c.k_mid, c.total_mid * D, kd).view(-1, D),
+            v_mid=self._view(c.v_mid, c.total_mid * D, kd).view(-1, D),
+            perm=self._view(c.perm, c.total_mid, torch.int32),
+            sub_off=self._view(c.sub_off, c.total_off, torch.int32),
+            cl_ms=self._view(c.cl_ms, c.total_cl * 2 * D, torch.float32).view(-1, 2 * D),
+            cl_vbar=self._view(c.cl_vbar, c.total_cl * D, torch.float32).view(-1, D),
+            sub_ms=self._view(c.sub_ms, c.total_sub * 2 * D, torch.float32).view(-1, 2 * D),
+            sub_vbar=self._view(c.sub_vbar, c.total_sub * D, torch.float32).view(-1, D),
+        )
+
+    def export_unit(self, u: int) -> dict:
+        """Host (NumPy) copy of one unit's layout."""
+        U = self.unit(u)
+        a = self.arrays()
+        D = self.c.head_dim
+        C_, S = U.C, U.S
+        rows = slice(U.row_base, U.row_base + U.n_mid)
+        cl = slice(U.cl_base, U.cl_base + C_)
+        sb = slice(U.sub_base, U.sub_base + C_ * S)
+        ms_c = a["cl_ms"][cl].cpu().numpy()
+        ms_s = a["sub_ms"][sb].cpu().numpy()
+        return dict(
+            N=U.N, C=C_, S=S, n_mid=U.n_mid, seq=U.seq, kv_head=U.kv_head,
+            perm=a["perm"][rows].cpu().numpy().astype(np.int64),
+            sub_off=a["sub_off"][U.off_base:U.off_base + C_ * S + 1].cpu().numpy().astype(np.int64),
+            cl_mu=ms_c[:, :D], cl_var=ms_c[:, D:], cl_vbar=a["cl_vbar"][cl].cpu().numpy(),
+            sub_mu=ms_s[:, :D], sub_var=ms_s[:, D:], sub_vbar=a["sub_vbar"][sb].cpu().numpy(),
+        )
+
+
+def _dims(n_seq, n_kv_heads, head_dim, dtype, n_sink, n_recent, seq_lens):
+    lens = capi.int_array(seq_lens)
+    d = capi.mog_dims(n_seq, n_kv_heads, head_dim, dtype, n_sink, n_recent,
+                      C.cast(lens, C.POINTER(capi.i32)))
+    return d, lens
+
+
+def mog_layout_size(n_kv_heads, head_dim, dtype, n_sink, n_recent, seq_lens) -> int:
+    d, _keep = _dims(len(seq_lens), n_kv_heads, head_dim, dtype, n_sink, n_recent, seq_lens)
+    out = C.c_size_t()
+    check(lib().mog_layout_size(C.byref(d), C.byref(out)), "mog_layout_size")
+    return out.value
+
+
+def mog_layout_init(kv: KVCache, n_sink, n_recent, device="cuda", stream=None) -> Layout:
+    """Allocate and carve an empty layout for ``kv`` (for importing arrays)."""
+    d, _keep = _dims(kv.c.n_seq, kv.c.n_kv_heads, kv.c.head_dim, kv.c.dtype, n_sink, n_recent,
+                     kv.seq_lens)
+    nbytes = C.c_size_t()
+    check(lib().mog_layout_size(C.byref(d), C.byref(nbytes)), "mog_layout_size")
+    mem = torch.zeros(nbytes.value, dtype=torch.uint8, device=device)
+    L = capi.mog_layout()
+    check(lib().mog_layout_init(C.byref(d), _vp(mem), nbytes.value, C.byref(L), _stream(stream)),
+          "mog_layout_init")
+    return Layout(L, mem)
+
+
+def decode_params(n_q_heads, top_c, top_s, residual=True, scale=0.0, splits=0):
+    """mog_decode_params; ``top_c``/``top_s`` are ints or per-sequence lists."""
+    p = capi.mog_decode_params()
+    p.n_q_heads = n_q_heads
+    p.residual = 1 if residual else 0
+    p.scale = float(scale)
+    p.splits = int(splits)
+    keep = []
+    if isinstance(top_c, (list, tuple)):
+        arr = capi.int_array(top_c)
+        keep.append(arr)
+        p.top_c_per_seq = C.cast(arr, C.POINTER(capi.i32))
+        p.top_c = int(top_c[0])
+    else:
+        p.top_c = int(top_c)
+    if isinstance(top_s, (list, tuple)):
+        arr = capi.int_array(top_s)
+        keep.append(arr)
+        p.top_s_per_seq = C.cast(arr, C.POINTER(capi.i32))
+        p.top_s = int(top_s[0])
+    else:
+        p.top_s = int(top_s)
+    p._keep = keep
+    return p
+
+
+def mog_workspace_size(op, kv: KVCache = None, layout: Layout = None, build_params=None,
+                       params=None) -> int:
+    out = C.c_size_t()
+    check(lib().mog_workspace_size(
+        op, C.byref(kv.c) if kv is not None else None,
+        C.byref(layout.c) if layout is not None else None,
+        C.byref(build_params) if build_params is not None else None,
+        C.byref(params) if params is not None else None, C.byref(out)), "mog_workspace_size")
+    return out.value
+
+
+def workspace(nbytes, device="cuda"):
+    """A zero-filled workspace (mog_decode needs its first 256 bytes zero)."""
+    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def mog_build(kv: KVCache, n_sink, n_recent, kmeans_iters=10, seed=0, ws=None, stream=None) -> Layout:
+    """Prefill-side build; allocates the layout (and the workspace unless given)."""
+    bp = capi.mog_build_params(kmeans_iters, n_sink, n_recent, 0, seed)
+    d, _keep = _dims(kv.c.n_seq, kv.c.n_kv_heads, kv.c.head_dim, kv.c.dtype, n_sink, n_recent,
+                     kv.seq_lens)
+    nbytes = C.c_size_t()
+    check(lib().mog_layout_size(C.byref(d), C.byref(nbytes)), "mog_layout_size")
+    mem = torch.empty(nbytes.value, dtype=torch.uint8, device=kv.k.device)
+    need = mog_workspace_size(capi.MOG_OP_BUILD, kv=kv, build_params=bp)
+    if ws is None or ws.numel() < need:
+        ws = workspace(need, kv.k.device)
+    L = capi.mog_layout()
+    check(lib().mog_build(C.byref(kv.c), C.byref(bp), _vp(mem), nbytes.value, _vp(ws), ws.numel(),
+                          C.byref(L), _stream(stream)), "mog_build")
+    lay = Layout(L, mem)
+    lay._build_ws = ws
+    return lay
+
+
+def mog_decode(layout: Layout, kv: KVCache, q, params, out=None, lse=None, want_sel=False,
+               ws=None, stream=None):
+    """One decode step.  Returns (out, lse, sel_c, sel_s)."""
+    _require_cuda(q)
+    if q.dtype != torch.float32 or not q.is_contiguous():
+        raise ValueError("q must be contiguous float32 [n_seq][Hq][D]")
+    n_seq, Hq, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(n_seq, Hq, dtype=torch.float32, device=q.device)
+    sel_c = sel_s = None
+    if want_sel:
+        cs = [params.top_c_per_seq[i] for i in range(n_seq)] if params.top_c_per_seq else [params.top_c]
+        ss = [params.top_s_per_seq[i] for i in range(n_seq)] if params.top_s_per_seq else [params.top_s]
+        cmax, smax = max(cs), max(ss)
+        sel_c = torch.full((n_seq, Hq, max(cmax, 1)), -1, dtype=torch.int32, device=q.device)
+        sel_s = torch.full((n_seq, Hq, max(cmax, 1), max(smax, 1)), -1, dtype=torch.int32,
+                           device=q.device)
+    need = mog_workspace_size(capi.MOG_OP_DECODE, layout=layout, params=params)
+    if ws is None or ws.numel() < need:
+        ws = workspace(need, q.device)
+    check(lib().mog_decode(C.byref(layout.c), C.byref(kv.c), _vp(q), C.byref(params), _vp(out),
+                           _vp(lse), _vp(sel_c), _vp(sel_s), _vp(ws), ws.numel(), _stream(stream)),
+          "mog_decode")
+    return out, lse, sel_c, sel_s
+
+
+def mog_dense_decode(kv: KVCache, q, params, out=None, lse=None, ws=None, stream=None):
+    """Dense exact decode attention (the in-library baseline).  Returns (out, lse)."""
+    _require_cuda(q)
+    if q.dtype != torch.float32 or not q.is_contiguous():
+        raise ValueError("q must be contiguous float32 [n_seq][Hq][D]")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
+    need = mog_workspace_size(capi.MOG_OP_DENSE, kv=kv, params=params)
+    if ws is None or ws.numel() < need:
+        ws = workspace(need, q.device)
+    check(lib().mog_dense_decode(C.byref(kv.c), _vp(q), C.byref(params), _vp(out), _vp(lse),
+                                 _vp(ws), ws.numel(), _stream(stream)), "mog_dense_decode")
+    return out, lse
+
+
+def import_layout(kv: KVCache, n_sink, n_recent, units, k_rows=None, v_rows=None,
+                  stream=None) -> Layout:
+    """Place a layout computed elsewhere into a fresh library layout.
+
+    ``units[u]`` is a dict with ``perm`` (token position of every reordered
+    row), ``sub_off`` (C*S+1 row offsets) and float32 ``cl_mu``, ``cl_var``,
+    ``cl_vbar``, ``sub_mu``, ``sub_var``, ``sub_vbar``.  The reordered K/V
+    rows are gathered from ``kv`` on the device.
+    """
+    lay = mog_layout_init(kv, n_sink, n_recent, device=kv.k.device, stream=stream)
+    a = lay.arrays()
+    dev = kv.k.device
+    D = kv.head_dim
+    Hkv = kv.n_kv_heads
+    for u, src in enumerate(units):
+        U = lay.unit(u)
+        C_, S = U.C, U.S
+        perm = torch.as_tensor(np.asarray(src["perm"], dtype=np.int64), device=dev)
+        sub_off = np.asarray(src["sub_off"], dtype=np.int64)
+        if perm.numel() != U.n_mid or sub_off.size != C_ * S + 1:
+            raise ValueError(f"unit {u}: layout arrays do not match the unit geometry")
+        seq, kvh = U.seq, U.kv_head
+        rows = slice(U.row_base, U.row_base + U.n_mid)
+        if kv.block_table is None:
+            a["k_mid"][rows] = kv.k[seq, kvh, perm]
+            a["v_mid"][rows] = kv.v[seq, kvh, perm]
+        else:
+            P = kv.k.shape[2]
+            page = kv.block_table[seq].long()[perm // P]
+            a["k_mid"][rows] = kv.k[page, kvh, perm % P]
+            a["v_mid"][rows] = kv.v[page, kvh, perm % P]
+        a["perm"][rows] = perm.to(torch.int32)
+        a["sub_off"][U.off_base:U.off_base + C_ * S + 1] = torch.as_tensor(sub_off, dtype=torch.int32, device=dev)
+        cl = slice(U.cl_base, U.cl_base + C_)
+        sb = slice(U.sub_base, U.sub_base + C_ * S)
+        f32 = lambda x: torch.as_tensor(np.asarray(x, dtype=np.float32), device=dev)
+        a["cl_ms"][cl, :D] = f32(src["cl_mu"])
+        a["cl_ms"][cl, D:] = f32(src["cl_var"])
+        a["cl_vbar"][cl] = f32(src["cl_vbar"])
+        a["sub_ms"][sb, :D] = f32(src["sub_mu"])
+        a["sub_ms"][sb, D:] = f32(src["sub_var"])
+        a["sub_vbar"][sb] = f32(src["sub_vbar"])
+    return lay

@@ -1,0 +1,101 @@
+"""Helpers shared by the GPU parity tests: conversion of oracle layouts to the
+arrays the library imports, oracle runs on downloaded layouts, and the
+selection comparison with its near-tie rule."""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+import oracle as O
+
+NEAR_TIE = 1e-5  # absolute, on float64 oracle scores (natural log)
+
+
+def unit_layout_arrays(L: "O.UnitLayout") -> dict:
+    return dict(perm=L.perm, sub_off=L.sub_off, cl_mu=L.cl_mu, cl_var=L.cl_var, cl_vbar=L.cl_vbar,
+                sub_mu=L.sub_mu, sub_var=L.sub_var, sub_vbar=L.sub_vbar)
+
+
+def oracle_layout_from_export(ex: dict, n_sink: int, n_recent: int) -> "O.UnitLayout":
+    """An oracle UnitLayout holding a layout downloaded from the device."""
+    return O.UnitLayout(N=ex["N"], n_sink=n_sink, n_recent=n_recent, C=ex["C"], S=ex["S"],
+                        perm=ex["perm"], sub_off=ex["sub_off"], cl_mu=ex["cl_mu"],
+                        cl_var=ex["cl_var"], cl_vbar=ex["cl_vbar"], sub_mu=ex["sub_mu"],
+                        sub_var=ex["sub_var"], sub_vbar=ex["sub_vbar"])
+
+
+def build_oracle_layouts(batch, iters=10, seed=0, units=None):
+    wl = batch.wl
+    out = {}
+    for s in range(wl.n_seq):
+        for h in range(wl.n_kv_heads):
+            u = s * wl.n_kv_heads + h
+            if units is not None and u not in units:
+                continue
+            k, v = batch.unit_kv(s, h)
+            out[u] = O.build_unit(k, v, wl.n_sink, wl.n_recent, iters,
+                                  O.unit_state(seed, s, h, wl.n_kv_heads))
+    return out
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def _cutoff_ok(scores, valid, chosen_gpu, chosen_ora, k):
+    """Selections may differ only where oracle scores are within NEAR_TIE of
+    the k-th best score."""
+    if set(chosen_gpu) == set(chosen_ora):
+        return True
+    idx = np.nonzero(valid)[0]
+    kk = min(k, idx.size)
+    if kk == 0:
+        return False
+    cut = np.sort(scores[idx])[::-1][kk - 1]
+    diff = set(chosen_gpu) ^ set(chosen_ora)
+    return all(abs(scores[i] - cut) <= NEAR_TIE for i in diff) and len(chosen_gpu) == len(chosen_ora)
+
+
+def compare_unit(L, K, V, Q, c, s, gpu_out, gpu_lse, gpu_sel_c, gpu_sel_s, tol, residual=True,
+                 scale=None):
+    """Compare one unit's GPU results with the oracle's.  Returns a dict of
+    the errors; raises AssertionError on a selection mismatch that is not a
+    near tie."""
+    G, d = Q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    ref = O.decode_unit(L, K, V, Q, c, s, scale=scale, residual=residual)
+    sel_c_gpu, sel_s_gpu = [], []
+    ties = 0
+    for h in range(G):
+        gc = [int(x) for x in gpu_sel_c[h] if x >= 0]
+        sel_c_gpu.append(np.asarray(gc, np.int64))
+        subs = []
+        for r, j in enumerate(gc):
+            subs.append(np.asarray([int(x) for x in gpu_sel_s[h][r] if x >= 0], np.int64))
+        sel_s_gpu.append(subs)
+        oc = [int(x) for x in ref["sel_c"][h]]
+        if gc != oc:
+            sc = O.group_log_mass(Q[h], L.cl_count, L.cl_mu, L.cl_var, scale)
+            assert _cutoff_ok(sc, L.cl_count > 0, gc, oc, c), (h, gc, oc)
+            ties += 1
+        for r, j in enumerate(gc):
+            if j in oc:
+                osub = [int(x) for x in ref["sel_s"][h][oc.index(j)]]
+                gsub = [int(x) for x in subs[r]]
+                if gsub != osub:
+                    g0 = j * L.S
+                    ss = O.group_log_mass(Q[h], L.sub_count[g0:g0 + L.S], L.sub_mu[g0:g0 + L.S],
+                                          L.sub_var[g0:g0 + L.S], scale)
+                    assert _cutoff_ok(ss, L.sub_count[g0:g0 + L.S] > 0, gsub, osub, s), (h, j, gsub, osub)
+                    ties += 1
+    if ties:
+        ref = O.decode_unit(L, K, V, Q, c, s, scale=scale, residual=residual,
+                            sel_override=(sel_c_gpu, sel_s_gpu))
+    errs = [rel_l2(gpu_out[h], ref["out"][h]) for h in range(G)]
+    lse_err = float(np.max(np.abs(np.asarray(gpu_lse, np.float64) - ref["lse"])))
+    assert max(errs) <= tol, (errs, tol)
+    return dict(max_rel=max(errs), lse_err=lse_err, ties=ties, ref=ref)

@@ -1,0 +1,192 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/mog.h declares, the ctypes structs match the C layout, sizes are
+computed on the host, and invalid arguments are rejected before anything
+is enqueued."""
+
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+from long_context_sparse_mog_amd import build_lib, capi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mog.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(capi.LIB_PATH):
+        build_lib.build(force=False)
+    return capi.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mog_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert len(names) == 9, names
+    out = subprocess.run(["nm", "-D", "--defined-only", capi.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (mog_\w+)", out))
+    assert set(names) == exported, (set(names) ^ exported)
+    for n in names:
+        assert hasattr(L, n)
+    assert set(names) == set(capi.SIGNATURES)
+
+
+def test_struct_layout_matches_c(tmp_path):
+    fields = {
+        "mog_kv": capi.mog_kv, "mog_dims": capi.mog_dims, "mog_unit": capi.mog_unit,
+        "mog_layout": capi.mog_layout, "mog_build_params": capi.mog_build_params,
+        "mog_decode_params": capi.mog_decode_params,
+    }
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "mog.h"', 'int main(void){']
+    for name, cls in fields.items():
+        lines.append(f'printf("{name} %zu\\n", sizeof({name}));')
+        for f, _ in cls._fields_:
+            lines.append(f'printf("{name}.{f} %zu\\n", offsetof({name}, {f}));')
+    lines.append("return 0;}")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", str(src), "-o", str(exe)], check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                       check=True).stdout.splitlines())
+    for name, cls in fields.items():
+        assert int(got[name]) == C.sizeof(cls), name
+        for f, _ in cls._fields_:
+            assert int(got[f"{name}.{f}"]) == getattr(cls, f).offset, f"{name}.{f}"
+
+
+def _dims(lens, n_sink=64, n_recent=256, hkv=8, d=128, dtype=capi.MOG_BF16):
+    arr = capi.int_array(lens)
+    return capi.mog_dims(len(lens), hkv, d, dtype, n_sink, n_recent, C.cast(arr, C.POINTER(capi.i32))), arr
+
+
+def test_layout_size_matches_geometry(L):
+    d, keep = _dims([1048576])
+    out = C.c_size_t()
+    assert L.mog_layout_size(C.byref(d), C.byref(out)) == capi.MOG_OK
+    n_mid, Cc, S, D = 1048576 - 320, 1024, 20, 128
+    expect = 8 * (2 * n_mid * D * 2 + n_mid * 4 + (Cc * S + 1) * 4 + Cc * 3 * D * 4 + Cc * S * 3 * D * 4)
+    assert expect <= out.value <= expect + 16 * 256
+
+
+def test_layout_unit_geometry(L):
+    lens = [4096, 20000, 777]
+    d, keep = _dims(lens, n_sink=4, n_recent=64, hkv=2, d=64, dtype=capi.MOG_F32)
+    lay = capi.mog_layout()
+    lay.n_seq, lay.n_kv_heads, lay.head_dim, lay.n_sink, lay.n_recent = 3, 2, 64, 4, 64
+    lay.n_units = 6
+    for i, x in enumerate(lens):
+        lay.seq_lens[i] = x
+    row = cl = sub = off = 0
+    import oracle as O
+    for u in range(6):
+        U = capi.mog_unit()
+        assert L.mog_layout_unit(C.byref(lay), u, C.byref(U)) == capi.MOG_OK
+        n_mid, Cc, S = O.unit_dims(lens[u // 2], 4, 64)
+        assert (U.seq, U.kv_head, U.N, U.n_mid, U.C, U.S) == (u // 2, u % 2, lens[u // 2], n_mid, Cc, S)
+        assert (U.row_base, U.cl_base, U.sub_base, U.off_base) == (row, cl, sub, off)
+        row += n_mid
+        cl += Cc
+        sub += Cc * S
+        off += Cc * S + 1
+    assert L.mog_layout_unit(C.byref(lay), 6, C.byref(U)) == capi.MOG_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad, status", [
+    (dict(lens=[300]), capi.MOG_ERR_INVALID_ARG),              # no middle region after 64+256
+    (dict(lens=[5000], d=96), capi.MOG_ERR_UNSUPPORTED),
+    (dict(lens=[(1 << 22) + 1]), capi.MOG_ERR_UNSUPPORTED),
+    (dict(lens=[5000], n_sink=-1), capi.MOG_ERR_INVALID_ARG),
+    (dict(lens=[5000], dtype=7), capi.MOG_ERR_UNSUPPORTED),
+    (dict(lens=[]), capi.MOG_ERR_INVALID_ARG),
+])
+def test_layout_size_rejects(L, bad, status):
+    lens = bad.pop("lens")
+    d, keep = _dims(lens if lens else [1], **bad)
+    if not lens:
+        d.n_seq = 0
+    out = C.c_size_t()
+    assert L.mog_layout_size(C.byref(d), C.byref(out)) == status
+    assert L.mog_last_error().decode() != ""
+
+
+def _kv(lens, **kw):
+    arr = capi.int_array(lens)
+    kv = capi.mog_kv()
+    kv.format, kv.dtype, kv.n_seq, kv.n_kv_heads, kv.head_dim = 0, capi.MOG_BF16, len(lens), 8, 128
+    kv.max_len = max(lens)
+    kv.seq_lens = C.cast(arr, C.POINTER(capi.i32))
+    kv.k, kv.v = 0x100000, 0x200000   # never dereferenced: validation fails first or no launch
+    for k, v in kw.items():
+        setattr(kv, k, v)
+    return kv, arr
+
+
+def test_decode_and_dense_validation(L):
+    kv, keep = _kv([5000])
+    p = capi.mog_decode_params(n_q_heads=12, top_c=4, top_s=2, residual=1, scale=0.0, splits=0)
+    out = C.c_size_t()
+    # 12 query heads on 8 KV heads
+    assert L.mog_workspace_size(capi.MOG_OP_DENSE, C.byref(kv), None, None, C.byref(p), C.byref(out)) == capi.MOG_ERR_INVALID_ARG
+    p.n_q_heads = 8 * 9   # G = 9 > 8
+    assert L.mog_workspace_size(capi.MOG_OP_DENSE, C.byref(kv), None, None, C.byref(p), C.byref(out)) == capi.MOG_ERR_UNSUPPORTED
+    p.n_q_heads = 32
+    assert L.mog_workspace_size(capi.MOG_OP_DENSE, C.byref(kv), None, None, C.byref(p), C.byref(out)) == capi.MOG_OK
+    assert out.value > 0
+    p.top_c = -1
+    assert L.mog_workspace_size(capi.MOG_OP_DENSE, C.byref(kv), None, None, C.byref(p), C.byref(out)) == capi.MOG_ERR_INVALID_ARG
+    p.top_c = 4
+    # dense with a NULL q / NULL workspace
+    assert L.mog_dense_decode(C.byref(kv), None, C.byref(p), C.c_void_p(0x1000), None, C.c_void_p(0x1000), 1 << 30, None) == capi.MOG_ERR_INVALID_ARG
+    assert L.mog_dense_decode(C.byref(kv), C.c_void_p(0x1000), C.byref(p), C.c_void_p(0x1000), None, None, 1 << 30, None) == capi.MOG_ERR_INVALID_ARG
+    # workspace too small
+    assert L.mog_dense_decode(C.byref(kv), C.c_void_p(0x1000), C.byref(p), C.c_void_p(0x1000), None, C.c_void_p(0x1000), 16, None) == capi.MOG_ERR_WORKSPACE
+    # misaligned k
+    kv2, keep2 = _kv([5000], k=0x100004)
+    assert L.mog_dense_decode(C.byref(kv2), C.c_void_p(0x1000), C.byref(p), C.c_void_p(0x1000), None, C.c_void_p(0x1000), 1 << 30, None) == capi.MOG_ERR_INVALID_ARG
+    # paged without a block table
+    kv3, keep3 = _kv([5000], format=1, page_size=16, n_pages=400, max_blocks=313)
+    assert L.mog_workspace_size(capi.MOG_OP_DENSE, C.byref(kv3), None, None, C.byref(p), C.byref(out)) == capi.MOG_ERR_INVALID_ARG
+    kv4, keep4 = _kv([5000], format=1, page_size=12, n_pages=400, max_blocks=313, block_table=0x3000)
+    assert L.mog_workspace_size(capi.MOG_OP_DENSE, C.byref(kv4), None, None, C.byref(p), C.byref(out)) == capi.MOG_ERR_INVALID_ARG
+    # decode with no layout
+    assert L.mog_decode(None, C.byref(kv), C.c_void_p(0x1000), C.byref(p), C.c_void_p(0x1000), None, None, None, C.c_void_p(0x1000), 1 << 30, None) == capi.MOG_ERR_INVALID_ARG
+    # layout that does not match the cache
+    lay = capi.mog_layout()
+    lay.n_seq, lay.n_kv_heads, lay.head_dim, lay.dtype = 1, 4, 128, capi.MOG_BF16
+    assert L.mog_decode(C.byref(lay), C.byref(kv), C.c_void_p(0x1000), C.byref(p), C.c_void_p(0x1000), None, None, None, C.c_void_p(0x1000), 1 << 30, None) == capi.MOG_ERR_INVALID_ARG
+    assert "does not match" in L.mog_last_error().decode()
+
+
+def test_build_validation(L):
+    kv, keep = _kv([5000])
+    bp = capi.mog_build_params(10, 64, 256, 0, 7)
+    out = C.c_size_t()
+    assert L.mog_workspace_size(capi.MOG_OP_BUILD, C.byref(kv), None, C.byref(bp), None, C.byref(out)) == capi.MOG_OK
+    bp.kmeans_iters = -1
+    assert L.mog_workspace_size(capi.MOG_OP_BUILD, C.byref(kv), None, C.byref(bp), None, C.byref(out)) == capi.MOG_ERR_INVALID_ARG
+    bp.kmeans_iters = 10
+    bp.n_recent = 5000
+    assert L.mog_workspace_size(capi.MOG_OP_BUILD, C.byref(kv), None, C.byref(bp), None, C.byref(out)) == capi.MOG_ERR_INVALID_ARG
+    bp.n_recent = 256
+    lay = capi.mog_layout()
+    # misaligned layout memory
+    assert L.mog_build(C.byref(kv), C.byref(bp), C.c_void_p(0x1001), 1 << 40, C.c_void_p(0x1000), 1 << 40, C.byref(lay), None) == capi.MOG_ERR_INVALID_ARG
+    # layout memory too small
+    assert L.mog_build(C.byref(kv), C.byref(bp), C.c_void_p(0x1000), 64, C.c_void_p(0x1000), 1 << 40, C.byref(lay), None) == capi.MOG_ERR_WORKSPACE
+
+
+def test_status_strings(L):
+    for s in range(5):
+        assert L.mog_status_string(s).decode()
+    assert L.mog_status_string(99).decode() == "unknown status"

@@ -1,0 +1,175 @@
+"""GPU parity of mog_decode and mog_dense_decode against the CPU oracle.
+
+mog_decode runs on a layout built by the oracle and imported into the
+library, so both sides see the same partition; selections must agree except
+at near ties, outputs within the stated tolerance (per-head relative L2:
+1e-5 for float32 K/V, 2e-3 for bf16 K/V).
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from long_context_sparse_mog_amd import ops, synth
+from parity import build_oracle_layouts, compare_unit, rel_l2, unit_layout_arrays
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def tol_of(wl):
+    return 1e-5 if wl.dtype == "fp32" else 2e-3
+
+
+def run_decode_case(wl, residual=True, top_c=None, top_s=None, qset=0, n_qsets=1, splits=0):
+    say(f"[case] {wl.name} lens={wl.seq_lens} Hq={wl.n_q_heads} Hkv={wl.n_kv_heads} "
+        f"D={wl.head_dim} {wl.dtype} c={top_c or wl.top_c} s={top_s or wl.top_s} res={residual}")
+    b = synth.generate(wl, device="cuda", n_qsets=n_qsets)
+    kv = ops.KVCache.from_batch(b)
+    lays = build_oracle_layouts(b)
+    lay = ops.import_layout(kv, wl.n_sink, wl.n_recent,
+                            [unit_layout_arrays(lays[u]) for u in range(wl.n_seq * wl.n_kv_heads)])
+    tc = top_c if top_c is not None else wl.top_c
+    ts = top_s if top_s is not None else wl.top_s
+    params = ops.decode_params(wl.n_q_heads, list(tc), list(ts), residual=residual, splits=splits)
+    q = b.Q[qset].contiguous()
+    out, lse, sel_c, sel_s = ops.mog_decode(lay, kv, q, params, want_sel=True)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    sel_c, sel_s = sel_c.cpu().numpy(), sel_s.cpu().numpy()
+    G = wl.group
+    worst = 0.0
+    for s in range(wl.n_seq):
+        for h in range(wl.n_kv_heads):
+            u = s * wl.n_kv_heads + h
+            K, V = b.unit_kv(s, h)
+            Q = q[s, h * G:(h + 1) * G].cpu().numpy().astype(np.float64)
+            hs = slice(h * G, (h + 1) * G)
+            r = compare_unit(lays[u], K, V, Q, tc[s], ts[s], out[s, hs], lse[s, hs], sel_c[s, hs],
+                             sel_s[s, hs], tol_of(wl), residual=residual)
+            assert r["lse_err"] < (1e-5 if wl.dtype == "fp32" else 1e-3) * max(1.0, float(np.abs(lse[s, hs]).max()))
+            worst = max(worst, r["max_rel"])
+    say(f"  worst per-head rel L2 = {worst:.3e}")
+    return b, kv, lays, out
+
+
+def test_config0_full():
+    run_decode_case(synth.config(0))
+
+
+def test_config0_top_only():
+    run_decode_case(synth.config(0), residual=False)
+
+
+def test_config0_all_clusters_is_dense():
+    wl = synth.config(0)
+    b, kv, lays, out = run_decode_case(wl, top_c=[64], top_s=[12])
+    K, V = b.unit_kv(0, 0)
+    o, _ = O.dense_attention(K, V, b.Q[0, 0].cpu().numpy())
+    assert rel_l2(out[0], o) < 1e-5
+
+
+def test_config0_no_clusters():
+    run_decode_case(synth.config(0), top_c=[0], top_s=[3])
+
+
+def test_config1_gqa_reduced():
+    run_decode_case(synth.config(1, seq_lens=[8192], n_kv_heads=2, n_q_heads=8, n_components=64))
+
+
+def test_config2_mha_needles_reduced():
+    run_decode_case(synth.config(2, seq_lens=[6000, 6000], n_kv_heads=2, n_q_heads=2,
+                                 n_components=64))
+
+
+def test_config3_gqa5_reduced():
+    run_decode_case(synth.config(3, seq_lens=[12000], n_kv_heads=2, n_q_heads=10, n_components=128))
+
+
+def test_config4_ragged_paged_reduced():
+    run_decode_case(synth.config(4, seq_lens=[3000, 9000, 1000], n_kv_heads=2, n_q_heads=8,
+                                 high_entropy_heads=(1,), n_components=64))
+
+
+@pytest.mark.parametrize("G", [3, 8])
+def test_other_group_sizes(G):
+    run_decode_case(synth.config(1, seq_lens=[3000], n_kv_heads=1, n_q_heads=G, n_components=32))
+
+
+def test_fp32_d128_and_splits():
+    wl = synth.config(1, seq_lens=[5000], n_kv_heads=1, n_q_heads=4, n_components=32, dtype="fp32")
+    run_decode_case(wl, splits=1)
+    run_decode_case(wl, splits=37)
+
+
+def test_bf16_d64():
+    run_decode_case(synth.config(1, seq_lens=[4000], n_kv_heads=2, n_q_heads=4, head_dim=64,
+                                 n_components=32))
+
+
+@pytest.mark.parametrize("ns,nr,L", [(0, 16, 700), (16, 0, 700), (0, 0, 500), (2, 3, 6), (4, 4, 9)])
+def test_anchor_edges(ns, nr, L):
+    wl = synth.config(1, seq_lens=[L], n_kv_heads=1, n_q_heads=2, n_components=8, n_sink=ns,
+                      n_recent=nr, top_c=[2], top_s=[2])
+    run_decode_case(wl)
+
+
+def test_budget_larger_than_partition():
+    wl = synth.config(1, seq_lens=[1500], n_kv_heads=1, n_q_heads=2, n_components=16,
+                      top_c=[500], top_s=[100])
+    b, kv, lays, out = run_decode_case(wl)
+    K, V = b.unit_kv(0, 0)
+    o, _ = O.dense_attention(K, V, b.Q[0, 0].cpu().numpy())
+    assert rel_l2(out[0], o) < 2e-3
+
+
+# ---------------------------------------------------------------------------
+# dense baseline
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("wl", [
+    synth.config(0),
+    synth.config(1, seq_lens=[8192], n_kv_heads=2, n_q_heads=8, n_components=64),
+    synth.config(4, seq_lens=[3000, 9000, 1000], n_kv_heads=2, n_q_heads=8,
+                 high_entropy_heads=(1,), n_components=64),
+    synth.config(3, seq_lens=[7001], n_kv_heads=1, n_q_heads=5, n_components=64),
+], ids=["cfg0", "cfg1r", "cfg4r-paged", "cfg3r"])
+def test_dense_matches_oracle(wl):
+    say(f"[dense] {wl.name} {wl.seq_lens}")
+    b = synth.generate(wl, device="cuda")
+    kv = ops.KVCache.from_batch(b)
+    q = b.Q[0].contiguous()
+    params = ops.decode_params(wl.n_q_heads, 1, 1)
+    out, lse = ops.mog_dense_decode(kv, q, params)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    G = wl.group
+    for s in range(wl.n_seq):
+        for h in range(wl.n_kv_heads):
+            K, V = b.unit_kv(s, h)
+            o, l = O.dense_attention(K, V, q[s, h * G:(h + 1) * G].cpu().numpy())
+            for g in range(G):
+                assert rel_l2(out[s, h * G + g], o[g]) < (1e-5 if wl.dtype == "fp32" else 1e-4)
+            np.testing.assert_allclose(lse[s, h * G:(h + 1) * G], l, rtol=1e-5, atol=1e-4)
+
+
+def test_decode_is_deterministic():
+    wl = synth.config(1, seq_lens=[8192], n_kv_heads=2, n_q_heads=8, n_components=64)
+    b = synth.generate(wl, device="cuda")
+    kv = ops.KVCache.from_batch(b)
+    lays = build_oracle_layouts(b)
+    lay = ops.import_layout(kv, wl.n_sink, wl.n_recent, [unit_layout_arrays(lays[u]) for u in range(2)])
+    params = ops.decode_params(wl.n_q_heads, wl.top_c, wl.top_s)
+    q = b.Q[0].contiguous()
+    o1 = ops.mog_decode(lay, kv, q, params)[0].clone()
+    o2 = ops.mog_decode(lay, kv, q, params)[0].clone()
+    assert torch.equal(o1, o2)
