@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""MoG decode-attention throughput on one MI355X.
+
+Prints ONE JSON line: MoG (Iceberg) decode-attention steps/s at N=1M (the
+`value`, GQA 40q/8kv, d=128, bf16) and at N=128K (batch 4, 32 MHA heads),
+achieved HBM GB/s, the fraction of the KV cache read, the speedup over the
+in-library dense decode, approximation errors against dense attention, the
+roofline of the exact-attention kernel (timed live with HIP events recorded
+around it on its stream), and the CPU oracle timed on a bounded sample.
+
+A step is one full decode pass (cluster scoring, top-c, subcluster scoring
+and top-s, exact attention, residual, merge) over one batch of queries; the
+KV cache and its cluster layout are resident in HBM when timing starts and
+queries rotate through pre-generated sets so selections change every step.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoG decode-attention steps/s at N=128K and 1M + achieved HBM GB/s"
+HBM_PEAK_GBPS = 8000.0
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the library records them on its stream)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.owned = []
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        self.owned.append(ev)
+        return ev
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def close(self):
+        for ev in self.owned:
+            self.hip.hipEventDestroy(ev)
+        self.owned.clear()
+
+
+def selection_volume(wl, lay, sel_c, sel_s, offs):
+    """Rows and bytes a step must move, from the selections (per step)."""
+    G, d = wl.group, wl.head_dim
+    e = 2 if wl.dtype == "bf16" else 4
+    rows_union = rows_head = 0
+    stat_bytes = 0
+    n_tokens = 0
+    for s in range(wl.n_seq):
+        N = wl.seq_lens[s]
+        for h in range(wl.n_kv_heads):
+            u = s * wl.n_kv_heads + h
+            U = lay.unit(u)
+            C, S = U.C, U.S
+            off = offs[u]
+            n_tokens += N
+            chosen_sets = []
+            subs_union = set()
+            sub_vbar_needed = set()
+            for g in range(G):
+                hq = h * G + g
+                cs = set()
+                for r, j in enumerate(sel_c[s, hq]):
+                    if j < 0:
+                        continue
+                    cs.add(int(j))
+                    picks = {int(i) for i in sel_s[s, hq, r] if i >= 0}
+                    for i in range(S):
+                        gg = int(j) * S + i
+                        if off[gg + 1] == off[gg]:
+                            continue
+                        if i in picks:
+                            subs_union.add(gg)
+                            rows_head += off[gg + 1] - off[gg]
+                        else:
+                            sub_vbar_needed.add(gg)
+                chosen_sets.append(cs)
+            union_c = set().union(*chosen_sets) if chosen_sets else set()
+            inter_c = set.intersection(*chosen_sets) if chosen_sets else set()
+            rows_u = sum(off[g + 1] - off[g] for g in subs_union) + wl.n_sink + wl.n_recent
+            rows_union += rows_u
+            rows_head += G * (wl.n_sink + wl.n_recent)
+            stat_bytes += C * (2 * d + 1) * 4              # cluster mean, variance, count
+            stat_bytes += (C - len(inter_c)) * d * 4       # cluster mean values left out
+            stat_bytes += len(union_c) * S * (2 * d + 1) * 4
+            stat_bytes += len(sub_vbar_needed) * d * 4
+            stat_bytes += G * d * 4 * 2                    # queries in, outputs out
+    kv_rows_bytes = rows_union * d * 2 * e
+    return dict(rows_union=rows_union, rows_per_head=rows_head / G, n_tokens=n_tokens,
+                kv_row_bytes=kv_rows_bytes, step_bytes=kv_rows_bytes + stat_bytes)
+
+
+def bench_workload(idx, steps, warmup, n_qsets, ev, with_errors=True):
+    import numpy as np
+    import torch
+
+    from long_context_sparse_mog_amd import capi, ops, synth
+
+    wl = synth.config(idx)
+    t0 = time.time()
+    b = synth.generate(wl, device="cuda", n_qsets=n_qsets, keep_contiguous=not wl.paged)
+    kv = ops.KVCache.from_batch(b)
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    torch.cuda.synchronize()
+    t0 = time.time()
+    lay = ops.mog_build(kv, wl.n_sink, wl.n_recent, kmeans_iters=wl.kmeans_iters, seed=1)
+    torch.cuda.synchronize()
+    build_s = time.time() - t0
+    qs = [b.Q[i].contiguous() for i in range(n_qsets)]
+    out = torch.empty_like(qs[0])
+    lse = torch.empty(qs[0].shape[:2], device="cuda")
+
+    def params_with_events(n, residual=True):
+        ps, pairs = [], []
+        for _ in range(n):
+            p = ops.decode_params(wl.n_q_heads, list(wl.top_c), list(wl.top_s), residual=residual)
+            a, z = ev.create(), ev.create()
+            p.exact_begin, p.exact_end = a, z
+            ps.append(p)
+            pairs.append((a, z))
+        return ps, pairs
+
+    p0 = ops.decode_params(wl.n_q_heads, list(wl.top_c), list(wl.top_s))
+    ws = ops.workspace(ops.mog_workspace_size(capi.MOG_OP_DECODE, layout=lay, params=p0))
+    pd0 = ops.decode_params(wl.n_q_heads, 1, 1)
+    wsd = ops.workspace(ops.mog_workspace_size(capi.MOG_OP_DENSE, kv=kv, params=pd0))
+
+    def timed(fn, plist, pairs, k, w):
+        for i in range(w):
+            fn(qs[i % n_qsets], p0 if plist is None else plist[0])
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(k):
+            fn(qs[i % n_qsets], plist[i])
+        e1.record()
+        torch.cuda.synchronize()
+        total_ms = e0.elapsed_time(e1)
+        kern = [ev.elapsed_ms(a, z) for a, z in pairs]
+        return total_ms / k, sum(kern) / len(kern)
+
+    pm, pairs_m = params_with_events(steps)
+    mog_ms, exact_ms = timed(lambda q, p: ops.mog_decode(lay, kv, q, p, out=out, lse=lse, ws=ws), pm, pairs_m,
+                             steps, warmup)
+    dsteps = max(10, steps // 4)
+    pdl = []
+    pairs_d = []
+    for _ in range(dsteps):
+        p = ops.decode_params(wl.n_q_heads, 1, 1)
+        a, z = ev.create(), ev.create()
+        p.exact_begin, p.exact_end = a, z
+        pdl.append(p)
+        pairs_d.append((a, z))
+    dense_ms, dense_kern_ms = timed(lambda q, p: ops.mog_dense_decode(kv, q, p, out=out, lse=lse, ws=wsd), pdl,
+                                    pairs_d, dsteps, max(2, warmup // 2))
+
+    # selections and errors (outside the timed region)
+    offs = [lay.export_unit(u)["sub_off"] for u in range(lay.n_units)]
+    vols = []
+    err_res, err_top = [], []
+    pt = ops.decode_params(wl.n_q_heads, list(wl.top_c), list(wl.top_s), residual=False)
+    for t in range(min(n_qsets, 4)):
+        o, _, sc, ss = ops.mog_decode(lay, kv, qs[t], p0, want_sel=True)
+        vols.append(selection_volume(wl, lay, sc.cpu().numpy(), ss.cpu().numpy(), offs))
+        if with_errors:
+            od, _ = ops.mog_dense_decode(kv, qs[t], pd0)
+            ot = ops.mog_decode(lay, kv, qs[t], pt)[0]
+            err_res.append((torch.linalg.norm(o - od, dim=-1) / torch.linalg.norm(od, dim=-1)).flatten())
+            err_top.append((torch.linalg.norm(ot - od, dim=-1) / torch.linalg.norm(od, dim=-1)).flatten())
+    mean = lambda k: float(np.mean([v[k] for v in vols]))
+    e = 2 if wl.dtype == "bf16" else 4
+    dense_bytes = wl.kv_bytes()
+    res = dict(
+        workload=wl.name, n_seq=wl.n_seq, seq_lens=wl.seq_lens if wl.n_seq <= 4 else "ragged",
+        n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads, head_dim=wl.head_dim, dtype=wl.dtype,
+        top_c=wl.top_c[0] if len(set(wl.top_c)) == 1 else "per-seq", top_s=wl.top_s[0] if len(set(wl.top_s)) == 1 else "per-seq",
+        steps_per_s=1000.0 / mog_ms, ms_per_step=mog_ms,
+        exact_kernel_ms=exact_ms,
+        step_bytes=mean("step_bytes"), exact_kernel_bytes=mean("kv_row_bytes"),
+        hbm_GBps=mean("step_bytes") / (mog_ms * 1e-3) / 1e9,
+        exact_kernel_GBps=mean("kv_row_bytes") / (exact_ms * 1e-3) / 1e9,
+        frac_kv_read_union=mean("rows_union") / mean("n_tokens"),
+        frac_kv_read_per_head=mean("rows_per_head") / mean("n_tokens"),
+        dense_ms_per_step=dense_ms, dense_kernel_ms=dense_kern_ms,
+        dense_GBps=dense_bytes / (dense_kern_ms * 1e-3) / 1e9,
+        speedup_vs_dense=dense_ms / mog_ms,
+        build_s=build_s, gen_s=gen_s,
+    )
+    if with_errors:
+        er, et = torch.cat(err_res), torch.cat(err_top)
+        res.update(err_vs_dense_residual_mean=float(er.mean()), err_vs_dense_residual_max=float(er.max()),
+                   err_vs_dense_toponly_mean=float(et.mean()), err_vs_dense_toponly_max=float(et.max()))
+    state = dict(wl=wl, b=b, lay=lay, qs=qs, e=e)
+    return res, state
+
+
+def cpu_baseline(state, budget_s):
+    """The CPU oracle (as it stands) decoding units of the same step on the
+    host cores, given the GPU-built layout; extrapolated to a whole step."""
+    import numpy as np
+
+    import oracle as O
+
+    wl, b, lay, qs = state["wl"], state["b"], state["lay"], state["qs"]
+    G = wl.group
+    times = []
+    units_done = 0
+    t_start = time.time()
+    for u in range(lay.n_units):
+        s, h = divmod(u, wl.n_kv_heads)
+        ex = lay.export_unit(u)
+        L = O.UnitLayout(N=ex["N"], n_sink=wl.n_sink, n_recent=wl.n_recent, C=ex["C"], S=ex["S"],
+                         perm=ex["perm"], sub_off=ex["sub_off"], cl_mu=ex["cl_mu"], cl_var=ex["cl_var"],
+                         cl_vbar=ex["cl_vbar"], sub_mu=ex["sub_mu"], sub_var=ex["sub_var"],
+                         sub_vbar=ex["sub_vbar"])
+        K, V = b.unit_kv(s, h)
+        Q = qs[0][s, h * G:(h + 1) * G].cpu().numpy().astype(np.float64)
+        t0 = time.time()
+        O.decode_unit(L, K, V, Q, wl.top_c[s], wl.top_s[s])
+        times.append(time.time() - t0)
+        units_done += 1
+        del K, V
+        if time.time() - t_start > budget_s:
+            break
+    per_unit = float(np.mean(times))
+    step_s = per_unit * lay.n_units
+    try:
+        import threadpoolctl
+        blas = [p.get("num_threads") for p in threadpoolctl.threadpool_info()]
+        threads = max([t for t in blas if t] or [1])
+    except Exception:  # pragma: no cover
+        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    return dict(value=1.0 / step_s, unit="steps/s", cores=threads, kind="oracle",
+                sample=f"oracle.decode_unit on {units_done} of {lay.n_units} (seq, KV head) units of "
+                       f"'{wl.name}' (query set 0, GPU-built layout), {sum(times):.1f} s of CPU work, "
+                       f"scaled to one step; host cores available {len(os.sched_getaffinity(0))}")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--qsets", type=int, default=16)
+    ap.add_argument("--no-128k", action="store_true", help="skip the N=128K workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    from long_context_sparse_mog_amd import capi
+
+    capi.lib()  # fail loudly when the HIP library is missing
+    ev = HipEvents()
+    r1m, st1m = bench_workload(3, args.steps, args.warmup, args.qsets, ev)
+    r128 = None
+    if not args.no_128k:
+        r128, _ = bench_workload(2, args.steps, args.warmup, args.qsets, ev)
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(st1m, args.cpu_seconds)
+    ev.close()
+    ach = r1m["exact_kernel_GBps"]
+    line = {
+        "metric": METRIC,
+        "value": r1m["steps_per_s"],
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r1m["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian-mixture keys, N(0,1) values, planted queries)",
+        "config": {"workload": r1m["workload"], "batch": r1m["n_seq"], "seq_len": 1048576,
+                   "q_heads": r1m["n_q_heads"], "kv_heads": r1m["n_kv_heads"], "head_dim": r1m["head_dim"],
+                   "top_c": r1m["top_c"], "top_s": r1m["top_s"]},
+        "hbm_GBps": r1m["hbm_GBps"],
+        "roofline": {"bound": "hbm", "kernel": "k_exact (exact split-K attention, MFMA bf16)",
+                     "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
+                     "traffic": None},
+        "cpu_baseline": cpu,
+        "at_1m": r1m,
+        "at_128k": r128,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

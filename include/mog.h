@@ -159,6 +159,9 @@ typedef struct {
   int32_t splits;               /* 0: automatic; else exact-attention splits per unit */
   const int32_t* top_c_per_seq; /* HOST [n_seq] or NULL (then top_c)           */
   const int32_t* top_s_per_seq; /* HOST [n_seq] or NULL (then top_s)           */
+  hipEvent_t exact_begin;       /* optional (NULL: unused): recorded on the    */
+  hipEvent_t exact_end;         /* stream right before / after the exact-      */
+                                /* attention kernel, for timing it alone       */
 } mog_decode_params;
 
 typedef enum { MOG_OP_BUILD = 0, MOG_OP_DECODE = 1, MOG_OP_DENSE = 2 } mog_op;

@@ -23,6 +23,7 @@ OUT_DIR = os.path.join(PKG, "_lib")
 OBJ_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(OUT_DIR, "libmog.so")
 SOURCES = ["api.cpp", "decode.hip", "build.hip"]
+HEADERS = ["mog_internal.h", "attn_tile.h"]
 ARCH = "gfx950"
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

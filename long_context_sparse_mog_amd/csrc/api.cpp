@@ -166,9 +166,8 @@ KVRef make_kvref(const mog_kv* kv) {
 // Decode geometry
 // ------------------------------------------------------------------------
 struct DecodePlan {
-  int G, c_stride, s_stride, splits, nb_res;
-  size_t o_clscore, o_clmask, o_clrank, o_submask, o_res, o_rstart, o_rlen, o_rmask, o_rvs, o_utot,
-      o_wstart, o_ex, bytes;
+  int G, c_stride, s_stride, splits, nb_res, nb_chosen;
+  size_t o_clscore, o_clmask, o_clrank, o_clrows, o_submask, o_res, o_ex, bytes;
 };
 
 int seq_top(const int32_t* per, int dflt, int s) { return per ? per[s] : dflt; }
@@ -197,6 +196,7 @@ DecodePlan plan_decode(const mog_layout* L, const mog_decode_params* p) {
   d.c_stride = 0;
   d.s_stride = 0;
   int64_t est = 1;
+  d.nb_chosen = 0;
   for (int s = 0; s < L->n_seq; ++s) {
     const int c = seq_top(p->top_c_per_seq, p->top_c, s);
     const int sk = seq_top(p->top_s_per_seq, p->top_s, s);
@@ -204,32 +204,32 @@ DecodePlan plan_decode(const mog_layout* L, const mog_decode_params* p) {
     d.s_stride = std::max(d.s_stride, sk);
     const UnitSizes z = unit_sizes(L->seq_lens[s], L->n_sink, L->n_recent);
     const int64_t per_sub = ceil_div(z.n_mid, (int64_t)z.C * z.S);
-    const int64_t sel = std::min<int64_t>(z.n_mid, (int64_t)d.G * std::min(c, z.C) * std::min(sk, z.S) * per_sub);
+    // chosen groups run larger than average (their score carries ln n), and
+    // the heads of a group choose partly different ones: allow 3x
+    const int64_t sel =
+        std::min<int64_t>(z.n_mid, 3 * (int64_t)d.G * std::min(c, z.C) * std::min(sk, z.S) * per_sub);
     est = std::max<int64_t>(est, L->n_sink + L->n_recent + sel);
+    d.nb_chosen = std::max<int>(d.nb_chosen, std::min(z.C, d.G * std::min(c, z.C)));
   }
   if (p->splits > 0) {
     d.splits = p->splits;
   } else {
-    int sp = (int)std::min<int64_t>(256, ceil_div(est, 512));
-    sp = std::max<int>(sp, (int)std::min<int64_t>(64, ceil_div(512, L->n_units)));
-    d.splits = std::max(1, std::min(sp, 256));
+    // one round of 2 blocks of 4 waves per compute unit (512 blocks), at
+    // least ~64 rows per wave
+    int64_t sp = std::max<int64_t>(1, 512 / L->n_units);
+    sp = std::min<int64_t>(sp, ceil_div(est, 256));
+    d.splits = (int)std::max<int64_t>(1, std::min<int64_t>(sp, 256));
   }
-  d.nb_res = (int)ceil_div(L->max_C, kResClustersPerBlock);
+  d.nb_res = d.nb_chosen + (int)ceil_div(L->max_C, kRestClustersPerBlock);
   const int D = L->head_dim, G = d.G, RS = D + kPartPad;
   const int64_t nu = L->n_units;
-  const int64_t runs = L->total_sub + 2 * nu;
   size_t o = kAlign;  // first 256 bytes: reserved, kept zero
   d.o_clscore = o; o = align_up(o + (size_t)L->total_cl * G * 4);
   d.o_clmask = o; o = align_up(o + (size_t)L->total_cl * 4);
   d.o_clrank = o; o = align_up(o + (size_t)L->total_cl * G * 4);
+  d.o_clrows = o; o = align_up(o + (size_t)L->total_cl * 4);
   d.o_submask = o; o = align_up(o + (size_t)L->total_sub * 4);
   d.o_res = o; o = align_up(o + (size_t)nu * d.nb_res * G * RS * 4);
-  d.o_rstart = o; o = align_up(o + (size_t)runs * 4);
-  d.o_rlen = o; o = align_up(o + (size_t)runs * 4);
-  d.o_rmask = o; o = align_up(o + (size_t)runs * 4);
-  d.o_rvs = o; o = align_up(o + (size_t)runs * 4);
-  d.o_utot = o; o = align_up(o + (size_t)nu * 2 * 4);
-  d.o_wstart = o; o = align_up(o + (size_t)nu * d.splits * 4 * 2 * 4);
   d.o_ex = o; o = align_up(o + (size_t)nu * d.splits * G * RS * 4);
   d.bytes = o;
   return d;
@@ -503,19 +503,17 @@ mog_status mog_decode(const mog_layout* layout, const mog_kv* kv, const float* q
   x.residual = params->residual ? 1 : 0;
   x.splits = d.splits;
   x.nb_res = d.nb_res;
+  x.nb_chosen = d.nb_chosen;
   x.scale = params->scale > 0.f ? params->scale : 1.0f / sqrtf((float)kv->head_dim);
+  x.ev_begin = params->exact_begin;
+  x.ev_end = params->exact_end;
   char* w = static_cast<char*>(ws);
   x.ws.cl_score = reinterpret_cast<float*>(w + d.o_clscore);
   x.ws.cl_mask = reinterpret_cast<uint32_t*>(w + d.o_clmask);
   x.ws.cl_rank = reinterpret_cast<int32_t*>(w + d.o_clrank);
+  x.ws.cl_rows = reinterpret_cast<int32_t*>(w + d.o_clrows);
   x.ws.sub_mask = reinterpret_cast<uint32_t*>(w + d.o_submask);
   x.ws.res_part = reinterpret_cast<float*>(w + d.o_res);
-  x.ws.run_start = reinterpret_cast<int32_t*>(w + d.o_rstart);
-  x.ws.run_len = reinterpret_cast<int32_t*>(w + d.o_rlen);
-  x.ws.run_mask = reinterpret_cast<uint32_t*>(w + d.o_rmask);
-  x.ws.run_vstart = reinterpret_cast<int32_t*>(w + d.o_rvs);
-  x.ws.unit_tot = reinterpret_cast<int32_t*>(w + d.o_utot);
-  x.ws.wstart = reinterpret_cast<int32_t*>(w + d.o_wstart);
   x.ws.ex_part = reinterpret_cast<float*>(w + d.o_ex);
   hipError_t e = launch_decode(x, stream);
   if (e != hipSuccess) return fail(MOG_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
@@ -546,6 +544,8 @@ mog_status mog_dense_decode(const mog_kv* kv, const float* q, const mog_decode_p
   x.n_kv_heads = kv->n_kv_heads;
   x.splits = d.splits;
   x.scale = params->scale > 0.f ? params->scale : 1.0f / sqrtf((float)kv->head_dim);
+  x.ev_begin = params->exact_begin;
+  x.ev_end = params->exact_end;
   x.ex_part = reinterpret_cast<float*>(static_cast<char*>(ws) + d.o_ex);
   hipError_t e = launch_dense(x, stream);
   if (e != hipSuccess) return fail(MOG_ERR_HIP, "dense launch: %s", hipGetErrorString(e));

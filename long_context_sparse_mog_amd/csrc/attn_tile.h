@@ -1,0 +1,370 @@
+// Exact online-softmax accumulation over rows of K/V, shared by the MoG exact
+// pass and the dense baseline.  One wave accumulates, for the G query heads
+// of one KV head, the running (m, l, o) of softmax attention in the base-2
+// log domain (logits carry a factor log2(e), folded into the query).
+//
+//  * MfmaTile (bf16 K/V): 32-row tiles.  Rows are read with coalesced 16-byte
+//    loads and staged row-major in a wave-private LDS buffer whose rows are
+//    padded by 16 bytes, so the writes and the 16-row fragment reads are
+//    bank-conflict free and every LDS access is one base plus an immediate.  Scores are S^T = K Q^T on the 16x16x32 bf16
+//    matrix cores, with Q split into bf16 high and low parts placed in
+//    columns h and h+8 (so scores carry ~16 mantissa bits of the fp32
+//    query).  The probabilities of a lane's 8 tokens come out of the score
+//    accumulator in exactly the layout the P^T operand needs, split into
+//    high/low parts the same way, and O^T += V^T P^T takes V^T fragments
+//    from LDS with transpose reads.
+//  * RowAcc (fp32 K/V): plain VALU, 16 (D=128) or 8 (D=64) lanes per row.
+#pragma once
+
+#include "mog_internal.h"
+
+namespace mog {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+template <int CTRL>
+__device__ inline float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// sum over the 16 lanes of each row (every lane gets the row sum)
+__device__ inline float row16_sum(float x) {
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);  // row_half_mirror
+  x += dpp<0x140>(x);  // row_mirror
+  return x;
+}
+
+__device__ inline float wave_sum_dpp(float x) {
+  x = row16_sum(x);
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
+// value of lane (lane ^ 8) inside each row of 16 lanes
+__device__ inline float swap8(float x) { return dpp<0x128>(x); }  // row_ror:8
+
+// ---------------------------------------------------------------------------
+// MFMA tile engine (bf16)
+// ---------------------------------------------------------------------------
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int D, int G>
+struct MfmaTile {
+  static constexpr int PPR = D / 8;      // 16-byte pieces per row
+  static constexpr int RPI = 64 / PPR;   // rows per wave-wide 16-byte load
+  static constexpr int NLI = 32 / RPI;   // loads per 32-row tile (per K or V)
+  static constexpr int NC = D / 32;      // k-chunks of the score product
+  static constexpr int NB = D / 16;      // 16-wide d blocks of the output
+  static constexpr int RSB = D * 2 + 16; // LDS row stride in bytes (one 16-byte pad)
+  static constexpr int BUF = 32 * RSB / 16;  // u32x4 per wave buffer
+
+  f32x4 o[NB];
+  float m, l;
+  bf16x8 qf[NC];
+
+  __device__ void init(const float* qb, float scale_l2) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15, h = n & 7;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float qv = h < G ? qb[h * D + 32 * c + 8 * g + j] * scale_l2 : 0.f;
+        const __bf16 hi = (__bf16)qv;
+        qf[c][j] = n < 8 ? hi : (__bf16)(qv - (float)hi);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m = -INFINITY;
+    l = 0.f;
+  }
+
+  // 16-byte piece of this lane for load i of a tile of rows r0 + RPI*i:
+  // lane = (row r0 = lane / PPR, piece p = lane % PPR).  Rows at or past
+  // nrows re-read the last row: their probability is exactly zero.
+  __device__ static int load_row(int i, int nrows) {
+    const int r = (threadIdx.x & 63) / PPR + RPI * i;
+    return r < nrows ? r : nrows - 1;
+  }
+
+  // Contiguous rows: row i of the tile at kp + i*D (elements).
+  __device__ void tile(u32x4* buf, const uint16_t* kp, const uint16_t* vp, int nrows, uint32_t mask) {
+    const int p = (threadIdx.x & 63) % PPR;
+    u32x4 kr[NLI], vr[NLI];
+#pragma unroll
+    for (int i = 0; i < NLI; ++i) {
+      const int64_t off = (int64_t)load_row(i, nrows) * D + p * 8;
+      kr[i] = *reinterpret_cast<const u32x4*>(kp + off);
+      vr[i] = *reinterpret_cast<const u32x4*>(vp + off);
+    }
+    compute(buf, kr, vr, nrows, mask);
+  }
+
+  // Rows anywhere: row i of the tile at element offset rowoff(i).
+  template <typename RowOff>
+  __device__ void tile_gather(u32x4* buf, const uint16_t* kb, const uint16_t* vb, int nrows, uint32_t mask,
+                              RowOff rowoff) {
+    const int p = (threadIdx.x & 63) % PPR;
+    u32x4 kr[NLI], vr[NLI];
+#pragma unroll
+    for (int i = 0; i < NLI; ++i) {
+      const int64_t off = rowoff(load_row(i, nrows)) + p * 8;
+      kr[i] = *reinterpret_cast<const u32x4*>(kb + off);
+      vr[i] = *reinterpret_cast<const u32x4*>(vb + off);
+    }
+    compute(buf, kr, vr, nrows, mask);
+  }
+
+  __device__ void compute(u32x4* buf, const u32x4 (&kr)[NLI], const u32x4 (&vr)[NLI], int nrows,
+                          uint32_t mask) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15, h = n & 7;
+    char* lds = reinterpret_cast<char*>(buf);
+    // row-major staging address of this lane's pieces
+    char* wr = lds + (lane / PPR) * RSB + (lane % PPR) * 16;
+    // the previous tile's reads of this buffer were issued before these
+    // writes, and LDS executes a wave's operations in order
+    __asm__ volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < NLI; ++i) *reinterpret_cast<u32x4*>(wr + i * RPI * RSB) = kr[i];
+    // S^T = K Q^T for the two 16-token halves
+    const char* kf_base = lds + n * RSB + g * 16;
+    f32x4 s[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(kf_base + t * 16 * RSB + c * 64);
+        s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf), qf[c], s[t], 0, 0, 0);
+      }
+    }
+    const bool hv = h < G && ((mask >> h) & 1u);
+    float mt = -INFINITY;
+    float sv[8];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float x = s[t][j] + swap8(s[t][j]);
+        const bool ok = hv && (16 * t + 4 * g + j) < nrows;
+        x = ok ? x : -INFINITY;
+        sv[4 * t + j] = x;
+        mt = fmaxf(mt, x);
+      }
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float mn = fmaxf(m, mt);
+    const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mn);
+    bf16x8 pf;
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float pj = sv[j] == -INFINITY ? 0.f : fast_exp2(sv[j] - mn);
+      ps += pj;
+      const __bf16 hi = (__bf16)pj;
+      pf[j] = n < 8 ? hi : (__bf16)(pj - (float)hi);
+    }
+    l = l * alpha + ps;
+    m = mn;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) o[b] *= alpha;
+    // values: same buffer, row-major, then V^T fragments by transpose reads:
+    // src lane (g, s) of each 16-lane group points at row 4g + s/4 (+16),
+    // columns 16b + 4(s%4) .. +3
+    __asm__ volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < NLI; ++i) *reinterpret_cast<u32x4*>(wr + i * RPI * RSB) = vr[i];
+    auto* tr = (__attribute__((address_space(3))) char*)(lds) + (4 * g + (n >> 2)) * RSB + (n & 3) * 8;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tr + 32 * b));
+      const bf16x4 vc = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tr + 32 * b + 16 * RSB));
+      const bf16x8 vf = {va[0], va[1], va[2], va[3], vc[0], vc[1], vc[2], vc[3]};
+      o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[b], 0, 0, 0);
+    }
+  }
+
+  // Combine the lanes of the wave and store its state (o[D], m, l) per head
+  // in st[wave][h][0..D+1].
+  __device__ void to_lds(float* st) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, n = lane & 15;
+    float lt = l;
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[b][j] += swap8(o[b][j]);
+    }
+    if (n < G) {
+      float* w = st + (wave * G + n) * (D + 2);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[16 * b + 4 * g + j] = o[b][j];
+      }
+      if (g == 0) {
+        w[D] = m;
+        w[D + 1] = lt;
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// VALU row engine (fp32 K/V): LPR = D/8 lanes per row, 8 elements per lane.
+// ---------------------------------------------------------------------------
+template <int D, int G>
+struct RowAcc {
+  static constexpr int LPR = D / 8;
+  static constexpr int RPI = 64 / LPR;
+  float m[G], l[G], o[G][8];
+  float qv[G][8];
+
+  __device__ void init(const float* qb, float scale_l2) {
+    const int sub = (threadIdx.x & 63) % LPR;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m[h] = -INFINITY;
+      l[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        o[h][e] = 0.f;
+        qv[h][e] = qb[h * D + sub * 8 + e] * scale_l2;
+      }
+    }
+  }
+
+  static constexpr int BUF = 1;
+
+  __device__ void tile(u32x4*, const float* kp, const float* vp, int nrows, uint32_t mask) {
+    rows(kp, vp, nrows, mask, [](int i) { return (int64_t)i * D; });
+  }
+
+  template <typename RowOff>
+  __device__ void tile_gather(u32x4*, const float* kb, const float* vb, int nrows, uint32_t mask, RowOff rowoff) {
+    rows(kb, vb, nrows, mask, rowoff);
+  }
+
+  template <typename RowOff>
+  __device__ void rows(const float* kb, const float* vb, int n, uint32_t mask, RowOff rowoff) {
+    const int lane = threadIdx.x & 63;
+    const int sub = lane % LPR, slot = lane / LPR;
+    for (int r = 0; r < n; r += RPI) {
+      const int my = r + slot;
+      const bool valid = my < n;
+      float k8[8], v8[8];
+      if (valid) {
+        const int64_t ro = rowoff(my) + sub * 8;
+        load8<float>(kb, ro, k8);
+        load8<float>(vb, ro, v8);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) k8[e] = v8[e] = 0.f;
+      }
+      float s[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float t = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t += qv[h][e] * k8[e];
+#pragma unroll
+        for (int o2 = 1; o2 < LPR; o2 <<= 1) t += __shfl_xor(t, o2, 64);
+        s[h] = t;
+      }
+      if (valid) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          if (!((mask >> h) & 1u)) continue;
+          const float mn = fmaxf(m[h], s[h]);
+          const float al = exp2f(m[h] - mn);
+          const float p = exp2f(s[h] - mn);
+          l[h] = l[h] * al + p;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[h][e] = o[h][e] * al + p * v8[e];
+          m[h] = mn;
+        }
+      }
+    }
+  }
+
+  __device__ void to_lds(float* st) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int x = LPR; x < 64; x <<= 1) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float m2 = __shfl_xor(m[h], x, 64);
+        const float l2 = __shfl_xor(l[h], x, 64);
+        float a1, a2, mn;
+        merge_scale(m[h], m2, a1, a2, mn);
+        l[h] = a1 * l[h] + a2 * l2;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float o2 = __shfl_xor(o[h][e], x, 64);
+          o[h][e] = a1 * o[h][e] + a2 * o2;
+        }
+        m[h] = mn;
+      }
+    }
+    if (lane < LPR) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float* w = st + (wave * G + h) * (D + 2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[lane * 8 + e] = o[h][e];
+        if (lane == 0) {
+          w[D] = m[h];
+          w[D + 1] = l[h];
+        }
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Block epilogue: merge the 4 wave states in st ([4][G][D+2]) and n_extra
+// further records (extra(j) points at record j's head-0 entry, heads RS
+// floats apart), then write one record (o[D], m, l) per head to dst.
+// Must be called by all 256 threads after to_lds() and a barrier.
+// ---------------------------------------------------------------------------
+template <int D, int G, typename Extra>
+__device__ inline void write_block_record(const float* st, int n_extra, Extra extra, float* dst) {
+  constexpr int RS = D + kPartPad;
+  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    const int h = idx / D, e = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, st[(w * G + h) * (D + 2) + D]);
+    for (int j = 0; j < n_extra; ++j) M = fmaxf(M, extra(j)[h * RS + D]);
+    float l2 = 0.f, o2 = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float* r = st + (w * G + h) * (D + 2);
+      const float f = (r[D] == -INFINITY) ? 0.f : exp2f(r[D] - M);
+      l2 += f * r[D + 1];
+      o2 += f * r[e];
+    }
+    for (int j = 0; j < n_extra; ++j) {
+      const float* r = extra(j) + h * RS;
+      const float f = (r[D] == -INFINITY) ? 0.f : exp2f(r[D] - M);
+      l2 += f * r[D + 1];
+      o2 += f * r[e];
+    }
+    dst[h * RS + e] = o2;
+    if (e == 0) {
+      dst[h * RS + D] = M;
+      dst[h * RS + D + 1] = l2;
+    }
+  }
+}
+
+}  // namespace mog

@@ -13,6 +13,7 @@
 //
 // All softmax bookkeeping is in the base-2 log domain: a logit x is carried
 // as x*log2(e) so every exponential is an exp2.
+#include "attn_tile.h"
 #include "mog_internal.h"
 
 namespace mog {
@@ -48,7 +49,7 @@ struct BudgetArgs {
 };
 
 // ---------------------------------------------------------------------------
-// Block-wide exclusive prefix sum over NT threads (NT a multiple of 64).
+// Block-wide helpers (NT threads, a multiple of 64)
 // ---------------------------------------------------------------------------
 template <int NT>
 __device__ inline int block_excl_scan(int v, int* sh, int& total) {
@@ -71,6 +72,30 @@ __device__ inline int block_excl_scan(int v, int* sh, int& total) {
   __syncthreads();
   total = tot;
   return off + x - v;
+}
+
+template <int NT>
+__device__ inline float block_max(float v, float* sh) {
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) r = fmaxf(r, sh[w]);
+  __syncthreads();
+  return r;
+}
+
+template <int NT>
+__device__ inline float block_sum(float v, float* sh) {
+  v = wave_sum_dpp(v);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = 0.f;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) r += sh[w];
+  __syncthreads();
+  return r;
 }
 
 // exp-weighted accumulation of one estimated group (log2 weight w, mean
@@ -120,51 +145,61 @@ __device__ inline void score_coefs(const DArgs& a, const float* qb, float (&coef
   }
 }
 
-template <int D, int G>
-__device__ inline void score_row(const float* row, const float (&coef)[G][D / 32], float (&s)[G]) {
+// Scores of R group rows (already loaded, x[r][EPL] per lane): lane r ends
+// up holding the G scores of row r (without the count term).
+template <int D, int G, int R>
+__device__ inline void score_rows(const float (&x)[R][D / 32], const float (&coef)[G][D / 32], int lane,
+                                  float (&mine)[G]) {
   constexpr int EPL = D / 32;
-  const int lane = threadIdx.x & 63;
-  float x[EPL];
-  load_floats<EPL>(row + lane * EPL, x);
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float t = 0.f;
+  for (int r = 0; r < R; ++r) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) t += coef[h][e] * x[e];
-    s[h] = wave_sum(t);
+    for (int h = 0; h < G; ++h) {
+      float t = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) t += coef[h][e] * x[r][e];
+      t = wave_sum_dpp(t);
+      if (lane == r) mine[h] = t;
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // 1. Cluster scores: score[g][h] = log2 n_g + log2e (scale q_h.mu_g +
 //    scale^2/2 sum_i q_{h,i}^2 var_{g,i}); -inf for an empty cluster.
-//    Grid (ceil(maxC/64), units), 4 waves, each wave 16 clusters.
+//    Grid (ceil(maxC/16), units); each wave loads 4 cluster rows at once.
 // ---------------------------------------------------------------------------
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_score_clusters(DArgs a) {
+  constexpr int EPL = D / 32;
   const int u = blockIdx.y;
   const mog_unit U = a.L.units[u];
-  const int g_begin = blockIdx.x * 64;
-  if (g_begin >= U.C) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g0 = blockIdx.x * 16 + wave * 4;
+  if (g0 >= U.C) return;
   const float* qb = a.q + ((int64_t)U.seq * a.Hq + (int64_t)U.kv_head * G) * D;
-  float coef[G][D / 32];
+  float coef[G][EPL];
   score_coefs<D, G>(a, qb, coef);
   const int32_t* off = a.L.sub_off + U.off_base;
-  for (int k = 0; k < 16; ++k) {
-    const int g = g_begin + wave + 4 * k;
-    if (g >= U.C) break;
+  float x[4][EPL];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int g = min(g0 + k, U.C - 1);
+    load_floats<EPL>(a.L.cl_ms + (U.cl_base + g) * (2 * D) + lane * EPL, x[k]);
+  }
+  float mine[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) mine[h] = 0.f;
+  score_rows<D, G, 4>(x, coef, lane, mine);
+  // lane k (< 4) now holds the scores of cluster g0 + k
+  const int g = g0 + lane;
+  if (lane < 4 && g < U.C) {
     const int64_t cg = U.cl_base + g;
-    float s[G];
-    score_row<D, G>(a.L.cl_ms + cg * (2 * D), coef, s);
     const int n = off[(g + 1) * U.S] - off[g * U.S];
     const float lg = n > 0 ? log2f((float)n) : -INFINITY;
-    float mine = 0.f;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-      if (lane == h) mine = s[h];
-    if (lane < G) a.ws.cl_score[cg * G + lane] = n > 0 ? mine + lg : -INFINITY;
-    if (lane == 0) a.ws.cl_mask[cg] = 0u;
+    for (int h = 0; h < G; ++h) a.ws.cl_score[cg * G + h] = n > 0 ? mine[h] + lg : -INFINITY;
+    a.ws.cl_mask[cg] = 0u;
   }
 }
 
@@ -269,130 +304,21 @@ __global__ __launch_bounds__(256) void k_select_topc(DArgs a, BudgetArgs b, int 
 }
 
 // ---------------------------------------------------------------------------
-// 3. Per cluster: the residual term of every head that left the cluster out;
-//    for the heads that chose it, subcluster scores, top-s per head, and the
-//    residual terms of the subclusters a head left out.  Writes the head
-//    mask of every subcluster and one residual partial per (block, head).
-//    Grid (ceil(maxC/16), units), 4 waves x 4 clusters.
+// 3. Subclusters and residual.  Grid (nb_chosen + nb_rest, units):
+//    * block x < nb_chosen takes the x-th chosen cluster of its unit (in
+//      cluster order; found by a block scan of the head masks): scores its S
+//      subclusters for every head (one batch of row loads per wave), picks
+//      the top-s of each head that chose the cluster, writes the subcluster
+//      head masks and the cluster's exactly-read row count, and accumulates
+//      the residual terms of the subclusters a choosing head left out;
+//    * block nb_chosen + y covers clusters [16y, 16y+16) (4 per wave): the
+//      residual terms of every head that left a cluster out, and a zero row
+//      count for clusters no head chose.
+//    Every block writes one residual record per head (slot = block index).
 // ---------------------------------------------------------------------------
 template <int D, int G>
-__global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b) {
-  constexpr int VPL = D / 64;
+__device__ inline void write_residual_record(float (*st)[G][D + 2], float* dst) {
   constexpr int RS = D + kPartPad;
-  const int u = blockIdx.y;
-  const mog_unit U = a.L.units[u];
-  const int g_begin = blockIdx.x * kResClustersPerBlock;
-  if (g_begin >= U.C) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const float* qb = a.q + ((int64_t)U.seq * a.Hq + (int64_t)U.kv_head * G) * D;
-  float coef[G][D / 32];
-  score_coefs<D, G>(a, qb, coef);
-  float rm[G], rl[G], ro[G][VPL];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    rm[h] = -INFINITY;
-    rl[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < VPL; ++e) ro[h][e] = 0.f;
-  }
-  const int S = U.S;
-  int s_keep = b.top_s[U.seq];
-  s_keep = s_keep < 0 ? 0 : s_keep;
-  const int32_t* off = a.L.sub_off + U.off_base;
-  const uint32_t all = (1u << G) - 1u;
-
-  for (int k = 0; k < kResClustersPerBlock / 4; ++k) {
-    const int g = g_begin + wave * (kResClustersPerBlock / 4) + k;
-    if (g >= U.C) break;
-    const int64_t cg = U.cl_base + g;
-    const int64_t sg0 = U.sub_base + (int64_t)g * S;
-    const int n_g = off[(g + 1) * S] - off[g * S];
-    if (n_g == 0) {
-      if (lane < S) a.ws.sub_mask[sg0 + lane] = 0u;
-      continue;
-    }
-    const uint32_t mask = a.ws.cl_mask[cg];
-    const uint32_t unchosen = all & ~mask;
-    if (unchosen && a.residual) {
-      float vb[VPL];
-      load_floats<VPL>(a.L.cl_vbar + cg * D + lane * VPL, vb);
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-        if ((unchosen >> h) & 1u) add_group<VPL>(rm[h], rl[h], ro[h], a.ws.cl_score[cg * G + h], vb);
-    }
-    uint32_t my_sm = 0u;
-    if (mask) {
-      int my_cnt = 0;
-      if (lane < S) my_cnt = off[g * S + lane + 1] - off[g * S + lane];
-      float my_ss[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) my_ss[h] = -INFINITY;
-      for (int i = 0; i < S; ++i) {
-        const int cnt_i = __shfl(my_cnt, i, 64);
-        if (cnt_i == 0) continue;
-        float s[G];
-        score_row<D, G>(a.L.sub_ms + (sg0 + i) * (2 * D), coef, s);
-        const float lg = log2f((float)cnt_i);
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-          if (lane == i) my_ss[h] = s[h] + lg;
-      }
-      const bool valid = lane < S && my_cnt > 0;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        if (!((mask >> h) & 1u)) continue;
-        const float my = my_ss[h];
-        int rank = 0;
-        for (int j = 0; j < S; ++j) {
-          const float o = __shfl(my, j, 64);
-          const int vj = __shfl((int)valid, j, 64);
-          if (vj && (o > my || (o == my && j < lane))) ++rank;
-        }
-        const bool sel = valid && rank < s_keep;
-        if (sel) my_sm |= 1u << h;
-        if (a.sel_s) {
-          const unsigned long long bal = __ballot(sel);
-          const int rc = a.ws.cl_rank[cg * G + h];
-          const int hq = U.kv_head * G + h;
-          const int64_t base = (((int64_t)U.seq * a.Hq + hq) * a.c_stride + rc) * a.s_stride;
-          if (sel) a.sel_s[base + __popcll(bal & ((1ull << lane) - 1ull))] = lane;
-          for (int j = __popcll(bal) + lane; j < a.s_stride; j += 64) a.sel_s[base + j] = -1;
-        }
-      }
-      if (lane < S) a.ws.sub_mask[sg0 + lane] = my_sm;
-      if (a.residual) {
-        for (int i = 0; i < S; ++i) {
-          const int cnt_i = __shfl(my_cnt, i, 64);
-          const uint32_t sm_i = (uint32_t)__shfl((int)my_sm, i, 64);
-          const uint32_t need = cnt_i > 0 ? (mask & ~sm_i) : 0u;
-          if (!need) continue;
-          float vb[VPL];
-          load_floats<VPL>(a.L.sub_vbar + (sg0 + i) * D + lane * VPL, vb);
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const float w = __shfl(my_ss[h], i, 64);
-            if ((need >> h) & 1u) add_group<VPL>(rm[h], rl[h], ro[h], w, vb);
-          }
-        }
-      }
-    } else {
-      if (lane < S) a.ws.sub_mask[sg0 + lane] = 0u;
-    }
-  }
-
-  // combine the four waves and write this block's residual partial per head
-  __shared__ float st[4][G][D + 2];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-#pragma unroll
-    for (int e = 0; e < VPL; ++e) st[wave][h][lane * VPL + e] = ro[h][e];
-    if (lane == 0) {
-      st[wave][h][D] = rm[h];
-      st[wave][h][D + 1] = rl[h];
-    }
-  }
-  __syncthreads();
-  float* dst = a.ws.res_part + ((int64_t)u * a.nb_res + blockIdx.x) * G * RS;
   for (int idx = threadIdx.x; idx < G * D; idx += 256) {
     const int h = idx / D, e = idx % D;
     float M = -INFINITY;
@@ -414,315 +340,385 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// 4. Plan of the exact pass of one unit: the run list (two anchor runs read
-//    from the KV cache, then every chosen subcluster as a run of layout rows
-//    with the mask of the heads that chose it), its virtual row prefix, and
-//    the first (run, offset) of each of the splits*4 wave ranges that divide
-//    the rows evenly.  One block of 1024 threads per unit.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k_plan(DArgs a, int G) {
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int nb_chosen) {
+  constexpr int EPL = D / 32;
+  constexpr int VPL = D / 64;
+  constexpr int RS = D + kPartPad;
+  constexpr int RPW = kMaxS / 4;   // subcluster rows per wave
+  __shared__ float st[4][G][D + 2];
+  __shared__ float lds_sc[kMaxS][G];
+  __shared__ uint32_t lds_sm[kMaxS];
   __shared__ int sh[16];
-  const int u = blockIdx.x, tid = threadIdx.x;
+  __shared__ int found;
+  const int u = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const mog_unit U = a.L.units[u];
-  const int CS = U.C * U.S;
-  const int64_t rb = U.sub_base + 2 * (int64_t)u;
+  const int S = U.S, C = U.C;
   const uint32_t all = (1u << G) - 1u;
   const int32_t* off = a.L.sub_off + U.off_base;
-  if (tid == 0) {
-    a.ws.run_start[rb] = 0;
-    a.ws.run_len[rb] = a.n_sink;
-    a.ws.run_mask[rb] = all;
-    a.ws.run_vstart[rb] = 0;
-    a.ws.run_start[rb + 1] = U.N - a.n_recent;
-    a.ws.run_len[rb + 1] = a.n_recent;
-    a.ws.run_mask[rb + 1] = all;
-    a.ws.run_vstart[rb + 1] = a.n_sink;
+  float rm[G], rl[G], ro[G][VPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    rm[h] = -INFINITY;
+    rl[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) ro[h][e] = 0.f;
   }
-  int cr = 2, crow = a.n_sink + a.n_recent;
-  for (int base = 0; base < CS; base += 1024) {
-    const int g = base + tid;
-    uint32_t m = 0u;
-    int st = 0, len = 0;
-    if (g < CS) {
-      m = a.ws.sub_mask[U.sub_base + g];
-      if (m) {
-        st = off[g];
-        len = off[g + 1] - st;
+  float* dst = a.ws.res_part + ((int64_t)u * a.nb_res + blockIdx.x) * G * RS;
+
+  if ((int)blockIdx.x < nb_chosen) {
+    // -------- the x-th chosen cluster ---------------------------------------
+    const int x = blockIdx.x;
+    {
+      constexpr int EM = kMaxC / 256;
+      const int E = (C + 255) / 256;
+      int cnt = 0;
+#pragma unroll
+      for (int k = 0; k < EM; ++k) {
+        const int g = tid * E + k;
+        if (k < E && g < C) cnt += a.ws.cl_mask[U.cl_base + g] != 0u;
+      }
+      if (tid == 0) found = -1;
+      int total;
+      int base = block_excl_scan<256>(cnt, sh, total);
+      if (x >= base && x < base + cnt) {
+        for (int k = 0; k < EM; ++k) {
+          const int g = tid * E + k;
+          if (k < E && g < C && a.ws.cl_mask[U.cl_base + g] != 0u) {
+            if (base == x) found = g;
+            ++base;
+          }
+        }
+      }
+      __syncthreads();
+    }
+    const int g = found;
+    if (g >= 0) {
+      const int64_t cg = U.cl_base + g;
+      const int64_t sg0 = U.sub_base + (int64_t)g * S;
+      const uint32_t mask = a.ws.cl_mask[cg];
+      const float* qb = a.q + ((int64_t)U.seq * a.Hq + (int64_t)U.kv_head * G) * D;
+      float coef[G][EPL];
+      score_coefs<D, G>(a, qb, coef);
+      // scores: wave w takes rows w, w+4, ...
+      float xr[RPW][EPL];
+#pragma unroll
+      for (int k = 0; k < RPW; ++k) {
+        const int i = min(wave + 4 * k, S - 1);
+        load_floats<EPL>(a.L.sub_ms + (sg0 + i) * (2 * D) + lane * EPL, xr[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < RPW; ++k) {
+        const int i = wave + 4 * k;
+        if (i >= S) break;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float t = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) t += coef[h][e] * xr[k][e];
+          t = wave_sum_dpp(t);
+          if (lane == 0) lds_sc[i][h] = t;
+        }
+      }
+      if (tid < kMaxS) lds_sm[tid] = 0u;
+      __syncthreads();
+      // full scores (count term added; -inf for an empty subcluster)
+      if (tid < S * G) {
+        const int i = tid / G, h = tid % G;
+        const int cnt = off[g * S + i + 1] - off[g * S + i];
+        lds_sc[i][h] = cnt > 0 ? lds_sc[i][h] + log2f((float)cnt) : -INFINITY;
+      }
+      __syncthreads();
+      // top-s of each choosing head: wave w handles heads w, w+4
+      int my_cnt = 0;
+      if (lane < S) my_cnt = off[g * S + lane + 1] - off[g * S + lane];
+      const bool valid = lane < S && my_cnt > 0;
+      int s_keep = b.top_s[U.seq];
+      s_keep = s_keep < 0 ? 0 : s_keep;
+      for (int h = wave; h < G; h += 4) {
+        if (!((mask >> h) & 1u)) continue;
+        const float my = valid ? lds_sc[lane][h] : -INFINITY;
+        int rank = 0;
+#pragma unroll
+        for (int j = 0; j < kMaxS; ++j) {
+          if (j >= S) break;
+          const float o = lds_sc[j][h];
+          if (o != -INFINITY && (o > my || (o == my && j < lane))) ++rank;
+        }
+        const bool sel = valid && rank < s_keep;
+        if (sel) atomicOr(&lds_sm[lane], 1u << h);
+        if (a.sel_s) {
+          const unsigned long long bal = __ballot(sel);
+          const int rc = a.ws.cl_rank[cg * G + h];
+          const int hq = U.kv_head * G + h;
+          const int64_t base = (((int64_t)U.seq * a.Hq + hq) * a.c_stride + rc) * a.s_stride;
+          if (sel) a.sel_s[base + __popcll(bal & ((1ull << lane) - 1ull))] = lane;
+          for (int j = __popcll(bal) + lane; j < a.s_stride; j += 64) a.sel_s[base + j] = -1;
+        }
+      }
+      __syncthreads();
+      if (tid < S) a.ws.sub_mask[sg0 + tid] = lds_sm[tid];
+      if (wave == 0) {
+        int rows = (lane < S && lds_sm[lane]) ? my_cnt : 0;
+#pragma unroll
+        for (int o2 = 1; o2 < 64; o2 <<= 1) rows += __shfl_xor(rows, o2, 64);
+        if (lane == 0) a.ws.cl_rows[cg] = rows;
+      }
+      // residual of the subclusters a choosing head left out: wave w takes
+      // subclusters w, w+4, ...
+      if (a.residual) {
+        float vb[RPW][VPL];
+        uint32_t need[RPW];
+#pragma unroll
+        for (int k = 0; k < RPW; ++k) {
+          const int i = wave + 4 * k;
+          need[k] = 0u;
+          if (i < S && off[g * S + i + 1] > off[g * S + i]) need[k] = mask & ~lds_sm[i];
+          if (need[k]) load_floats<VPL>(a.L.sub_vbar + (sg0 + i) * D + lane * VPL, vb[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < RPW; ++k) {
+          if (!need[k]) continue;
+          const int i = wave + 4 * k;
+#pragma unroll
+          for (int h = 0; h < G; ++h)
+            if ((need[k] >> h) & 1u) add_group<VPL>(rm[h], rl[h], ro[h], lds_sc[i][h], vb[k]);
+        }
       }
     }
-    const int flag = (m != 0u && len > 0) ? 1 : 0;
-    int tf, tl;
-    const int ri = block_excl_scan<1024>(flag, sh, tf);
-    const int vo = block_excl_scan<1024>(flag * len, sh, tl);
-    if (flag) {
-      const int64_t idx = rb + cr + ri;
-      a.ws.run_start[idx] = st;
-      a.ws.run_len[idx] = len;
-      a.ws.run_mask[idx] = m;
-      a.ws.run_vstart[idx] = crow + vo;
+  } else {
+    // -------- residual of clusters left out, 4 clusters per wave ------------
+    const int y = blockIdx.x - nb_chosen;
+    for (int k = 0; k < 4; ++k) {
+      const int g = y * 16 + wave * 4 + k;
+      if (g >= C) break;
+      const int64_t cg = U.cl_base + g;
+      const uint32_t mask = a.ws.cl_mask[cg];
+      if (mask == 0u && lane == 0) a.ws.cl_rows[cg] = 0;
+      const int n_g = off[(g + 1) * S] - off[g * S];
+      const uint32_t unchosen = n_g > 0 ? (all & ~mask) : 0u;
+      if (unchosen && a.residual) {
+        float vb[VPL];
+        load_floats<VPL>(a.L.cl_vbar + cg * D + lane * VPL, vb);
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+          if ((unchosen >> h) & 1u) add_group<VPL>(rm[h], rl[h], ro[h], a.ws.cl_score[cg * G + h], vb);
+      }
     }
-    cr += tf;
-    crow += tl;
   }
-  const int R = cr, T = crow;
-  if (tid == 0) {
-    a.ws.unit_tot[2 * u] = R;
-    a.ws.unit_tot[2 * u + 1] = T;
-  }
-  const int NW = a.splits * 4;
-  int32_t* wst = a.ws.wstart + (int64_t)u * NW * 2;
-  for (int w = tid; w < NW; w += 1024) {
-    wst[2 * w] = R;
-    wst[2 * w + 1] = 0;
+
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) st[wave][h][lane * VPL + e] = ro[h][e];
+    if (lane == 0) {
+      st[wave][h][D] = rm[h];
+      st[wave][h][D + 1] = rl[h];
+    }
   }
   __syncthreads();
-  if (T > 0) {
-    for (int r = tid; r < R; r += 1024) {
-      const int64_t vs = a.ws.run_vstart[rb + r];
-      const int64_t ve = vs + a.ws.run_len[rb + r];
-      int64_t wlo = (vs * NW + T - 1) / T;
-      const int64_t whi = (ve * NW + T - 1) / T;
-      for (int64_t w = wlo; w < whi && w < NW; ++w) {
-        wst[2 * w] = r;
-        wst[2 * w + 1] = (int)(w * T / NW - vs);
-      }
-    }
-  }
+  write_residual_record<D, G>(st, dst);
 }
 
 // ---------------------------------------------------------------------------
-// Exact online-softmax accumulation shared by the MoG exact pass and the
-// dense baseline.  A wave reads LPR = D/8 lanes per row (8 elements per lane,
-// one 16-byte load per lane for bf16), RPI = 64/LPR rows per step; each lane
-// keeps a (m, l, o[8]) state per head for its row slot.
+// 4. Exact split-K pass.  The rows a unit reads exactly are laid out
+//    virtually as [sink anchors | recent anchors | rows of every cluster's
+//    chosen subclusters, clusters in order]; wave w of the unit covers
+//    virtual rows [w*T/NW, (w+1)*T/NW).  Every block first scans the
+//    per-cluster row counts into LDS, then each wave locates its first
+//    cluster by binary search and walks the chosen subclusters (adjacent
+//    subclusters chosen by the same heads form one contiguous run).  The
+//    block also folds the residual partials p, p+splits, ... of its unit
+//    into its record.  Grid (splits, units).
 // ---------------------------------------------------------------------------
-template <int D, int G>
-struct RowAcc {
-  static constexpr int LPR = D / 8;
-  static constexpr int RPI = 64 / LPR;
-  float m[G], l[G], o[G][8];
-  float qv[G][8];
-
-  __device__ void init(const float* qb, float scale_l2) {
-    const int sub = (threadIdx.x & 63) % LPR;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      m[h] = -INFINITY;
-      l[h] = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        o[h][e] = 0.f;
-        qv[h][e] = qb[h * D + sub * 8 + e] * scale_l2;
-      }
-    }
-  }
-
-  // rows given by a functor rowoff(i) -> element offset of row i, i < n
-  template <typename T, typename RowOff>
-  __device__ void rows(const T* kb, const T* vb, int n, uint32_t mask, RowOff rowoff) {
-    const int lane = threadIdx.x & 63;
-    const int sub = lane % LPR, slot = lane / LPR;
-    for (int r = 0; r < n; r += RPI) {
-      const int my = r + slot;
-      const bool valid = my < n;
-      float k8[8], v8[8];
-      if (valid) {
-        const int64_t ro = rowoff(my) + sub * 8;
-        load8<T>(kb, ro, k8);
-        load8<T>(vb, ro, v8);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) k8[e] = v8[e] = 0.f;
-      }
-      float s[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float t = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) t += qv[h][e] * k8[e];
-#pragma unroll
-        for (int o2 = 1; o2 < LPR; o2 <<= 1) t += __shfl_xor(t, o2, 64);
-        s[h] = t;
-      }
-      if (valid) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          if (!((mask >> h) & 1u)) continue;
-          const float mn = fmaxf(m[h], s[h]);
-          const float al = exp2f(m[h] - mn);
-          const float p = exp2f(s[h] - mn);
-          l[h] = l[h] * al + p;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[h][e] = o[h][e] * al + p * v8[e];
-          m[h] = mn;
-        }
-      }
-    }
-  }
-
-  // merge the RPI row slots of the wave, then the 4 waves of the block, and
-  // write one partial record (o[D], m, l) per head to dst[h*RS].
-  __device__ void finish(float* dst) {
-    constexpr int RS = D + kPartPad;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int x = LPR; x < 64; x <<= 1) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float m2 = __shfl_xor(m[h], x, 64);
-        const float l2 = __shfl_xor(l[h], x, 64);
-        float a1, a2, mn;
-        merge_scale(m[h], m2, a1, a2, mn);
-        l[h] = a1 * l[h] + a2 * l2;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float o2 = __shfl_xor(o[h][e], x, 64);
-          o[h][e] = a1 * o[h][e] + a2 * o2;
-        }
-        m[h] = mn;
-      }
-    }
-    __shared__ float st[4][G][D + 2];
-    if (lane < LPR) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) st[wave][h][lane * 8 + e] = o[h][e];
-        if (lane == 0) {
-          st[wave][h][D] = m[h];
-          st[wave][h][D + 1] = l[h];
-        }
-      }
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-      const int h = idx / D, e = idx % D;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, st[w][h][D]);
-      float l2 = 0.f, o2 = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float mw = st[w][h][D];
-        const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-        l2 += f * st[w][h][D + 1];
-        o2 += f * st[w][h][e];
-      }
-      dst[h * RS + e] = o2;
-      if (e == 0) {
-        dst[h * RS + D] = M;
-        dst[h * RS + D + 1] = l2;
-      }
-    }
-  }
-};
-
-// ---------------------------------------------------------------------------
-// 5. Exact split-K pass: wave w of unit u covers virtual rows
-//    [w*T/NW, (w+1)*T/NW) of the unit's run list.  Grid (splits, units).
-// ---------------------------------------------------------------------------
-template <int D, int G, typename T>
+template <int D, int G, typename Engine, typename T>
 __global__ __launch_bounds__(256) void k_exact(DArgs a) {
   constexpr int RS = D + kPartPad;
-  const int u = blockIdx.y, p = blockIdx.x;
-  const int wave = threadIdx.x >> 6;
+  __shared__ u32x4 kvbuf[4][Engine::BUF];
+  __shared__ float st[4 * G * (D + 2)];
+  __shared__ int vpre[kMaxC + 1];
+  __shared__ int sh[16];
+  const int u = blockIdx.y, p = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const mog_unit U = a.L.units[u];
-  const int R = a.ws.unit_tot[2 * u];
-  const int64_t Tt = a.ws.unit_tot[2 * u + 1];
+  const int C = U.C, S = U.S;
+  const int A = a.n_sink + a.n_recent;
+  {
+    constexpr int EM = kMaxC / 256;
+    const int E = (C + 255) / 256;
+    int loc[EM];
+    int sum = 0;
+#pragma unroll
+    for (int k = 0; k < EM; ++k) {
+      const int g = tid * E + k;
+      const int v = (k < E && g < C) ? a.ws.cl_rows[U.cl_base + g] : 0;
+      loc[k] = v;
+      sum += v;
+    }
+    int total;
+    int base = block_excl_scan<256>(sum, sh, total);
+#pragma unroll
+    for (int k = 0; k < EM; ++k) {
+      const int g = tid * E + k;
+      if (k < E && g < C) vpre[g] = base;
+      base += loc[k];
+    }
+    if (tid == 0) vpre[C] = total;
+    __syncthreads();
+  }
+  const int64_t Tt = A + vpre[C];
   const int NW = a.splits * 4;
   const int w = p * 4 + wave;
   const int64_t r0 = (int64_t)w * Tt / NW;
   const int64_t r1 = (int64_t)(w + 1) * Tt / NW;
-  RowAcc<D, G> acc;
+  Engine acc;
   acc.init(a.q + ((int64_t)U.seq * a.Hq + (int64_t)U.kv_head * G) * D, a.scale_l2);
-  if (r0 < r1) {
-    const int64_t rb = U.sub_base + 2 * (int64_t)u;
-    const int32_t* wst = a.ws.wstart + ((int64_t)u * NW + w) * 2;
-    int r = wst[0];
-    int offr = wst[1];
-    int64_t row = r0;
-    const T* kc = static_cast<const T*>(a.kv.k);
-    const T* vc = static_cast<const T*>(a.kv.v);
-    const T* km = static_cast<const T*>(a.L.k_mid);
-    const T* vm = static_cast<const T*>(a.L.v_mid);
-    while (row < r1 && r < R) {
-      const int st = a.ws.run_start[rb + r];
-      const int ln = a.ws.run_len[rb + r];
-      const uint32_t msk = a.ws.run_mask[rb + r];
-      int take = ln - offr;
-      if ((int64_t)take > r1 - row) take = (int)(r1 - row);
-      if (take > 0) {
-        if (r < 2) {
-          const KVRef kv = a.kv;
-          const int t0 = st + offr, seq = U.seq, kvh = U.kv_head;
-          acc.template rows<T>(kc, vc, take, msk,
-                               [&](int i) { return kv_row_offset(kv, seq, kvh, t0 + i, D); });
-        } else {
-          const int64_t base = (U.row_base + st + offr) * D;
-          acc.template rows<T>(km, vm, take, msk, [&](int i) { return base + (int64_t)i * D; });
-        }
+  u32x4* buf = kvbuf[wave];
+  const T* kc = static_cast<const T*>(a.kv.k);
+  const T* vc = static_cast<const T*>(a.kv.v);
+  const uint32_t all = (1u << G) - 1u;
+  int64_t x = r0;
+  if (x < r1 && x < A) {
+    // anchors from the KV cache: virtual row x < n_sink is token x, else
+    // token N - n_recent + (x - n_sink)
+    const KVRef kv = a.kv;
+    const int seq = U.seq, kvh = U.kv_head;
+    const int64_t xe = r1 < A ? r1 : A;
+    while (x < xe) {
+      const bool sink = x < a.n_sink;
+      const int tok = sink ? (int)x : U.N - a.n_recent + (int)(x - a.n_sink);
+      const int64_t seg_end = sink ? (a.n_sink < xe ? a.n_sink : xe) : xe;
+      const int nr = (int)((seg_end - x) < 32 ? (seg_end - x) : 32);
+      if (!kv.paged) {
+        const int64_t base = kv_row_offset(kv, seq, kvh, tok, D);
+        acc.tile(buf, kc + base, vc + base, nr, all);
+      } else {
+        acc.tile_gather(buf, kc, vc, nr, all, [&](int i) { return kv_row_offset(kv, seq, kvh, tok + i, D); });
       }
-      row += take;
-      ++r;
-      offr = 0;
+      x += nr;
     }
   }
-  acc.finish(a.ws.ex_part + ((int64_t)u * a.splits + p) * G * RS);
+  if (x < r1) {
+    const T* km = static_cast<const T*>(a.L.k_mid);
+    const T* vm = static_cast<const T*>(a.L.v_mid);
+    const int32_t* off = a.L.sub_off + U.off_base;
+    int64_t y = x - A;
+    const int64_t y1 = r1 - A;
+    int lo = 0, hi = C;  // last cluster g with vpre[g] <= y
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (vpre[mid] <= y) lo = mid; else hi = mid;
+    }
+    int g = lo;
+    while (y < y1 && g < C) {
+      if (vpre[g + 1] == vpre[g]) {
+        ++g;
+        continue;
+      }
+      int skip = (int)(y - vpre[g]);
+      // the S subclusters of cluster g, one per lane
+      const int64_t sg0 = U.sub_base + (int64_t)g * S;
+      uint32_t my_m = 0u;
+      int my_st = 0, my_en = 0;
+      if (lane < S) {
+        my_m = a.ws.sub_mask[sg0 + lane];
+        my_st = off[g * S + lane];
+        my_en = off[g * S + lane + 1];
+      }
+      unsigned long long chosen = __ballot(my_m != 0u && my_en > my_st);
+      while (chosen && y < y1) {
+        const int i = __ffsll((long long)chosen) - 1;
+        const uint32_t m = (uint32_t)__shfl((int)my_m, i, 64);
+        const int st0 = __shfl(my_st, i, 64);
+        int en = __shfl(my_en, i, 64);
+        chosen &= chosen - 1ull;
+        // absorb following subclusters chosen by the same heads
+        while (chosen) {
+          const int j = __ffsll((long long)chosen) - 1;
+          if ((uint32_t)__shfl((int)my_m, j, 64) != m || __shfl(my_st, j, 64) != en) break;
+          en = __shfl(my_en, j, 64);
+          chosen &= chosen - 1ull;
+        }
+        const int len = en - st0;
+        if (skip >= len) {
+          skip -= len;
+          continue;
+        }
+        const int take = (int)((int64_t)(len - skip) < y1 - y ? (len - skip) : (y1 - y));
+        const int64_t base = (U.row_base + st0 + skip) * D;
+        for (int t0 = 0; t0 < take; t0 += 32)
+          acc.tile(buf, km + base + (int64_t)t0 * D, vm + base + (int64_t)t0 * D, min(32, take - t0), m);
+        y += take;
+        skip = 0;
+      }
+      ++g;
+    }
+  }
+  acc.to_lds(st);
+  __syncthreads();
+  const int nres = a.residual ? a.nb_res : 0;
+  const int n_extra = nres > p ? (nres - p + a.splits - 1) / a.splits : 0;
+  const float* rp = a.ws.res_part + (int64_t)u * a.nb_res * G * RS;
+  write_block_record<D, G>(st, n_extra, [&](int j) { return rp + (int64_t)(p + j * a.splits) * G * RS; },
+                           a.ws.ex_part + ((int64_t)u * a.splits + p) * G * RS);
 }
 
 // ---------------------------------------------------------------------------
-// 6. Merge: per query head, max over every partial (exact splits, then the
-//    residual blocks), one normalisation.  Grid (Hq, n_seq), D threads.
+// 5. Merge: per query head, the records of the unit's splits: one max, one
+//    weighted sum, one normalisation.  Grid (Hq, n_seq), 256 threads.
 // ---------------------------------------------------------------------------
+constexpr int kMaxParts = 1024;
+
 template <int D>
-__global__ __launch_bounds__(128) void k_merge(const float* ex_part, int n_ex, const float* res_part,
-                                               int nb_res_stride, const mog_unit* units,
-                                               int use_res, int G, int Hq, int Hkv, float* out,
+__global__ __launch_bounds__(256) void k_merge(const float* part, int n_part, int G, int Hq, int Hkv, float* out,
                                                float* lse) {
   constexpr int RS = D + kPartPad;
-  const int hq = blockIdx.x, seq = blockIdx.y, t = threadIdx.x;
+  constexpr int NG = 256 / D;
+  __shared__ float wts[kMaxParts];
+  __shared__ float sh[8];
+  __shared__ float acc[NG][D];
+  const int hq = blockIdx.x, seq = blockIdx.y, tid = threadIdx.x;
   const int kvh = hq / G, h = hq % G;
   const int u = seq * Hkv + kvh;
-  int n_res = 0;
-  if (use_res) {
-    const int C = units[u].C;
-    n_res = (C + kResClustersPerBlock - 1) / kResClustersPerBlock;
-  }
-  const float* ex = ex_part + ((int64_t)u * n_ex * G + h) * RS;
-  const float* rs = use_res ? res_part + ((int64_t)u * nb_res_stride * G + h) * RS : nullptr;
+  const float* base = part + ((int64_t)u * n_part * G + h) * RS;
+  const int64_t stride = (int64_t)G * RS;
   float M = -INFINITY;
-  for (int i = 0; i < n_ex; ++i) M = fmaxf(M, ex[(int64_t)i * G * RS + D]);
-  for (int i = 0; i < n_res; ++i) M = fmaxf(M, rs[(int64_t)i * G * RS + D]);
-  float den = 0.f, num = 0.f;
-  for (int i = 0; i < n_ex; ++i) {
-    const float* r = ex + (int64_t)i * G * RS;
-    const float m = r[D];
-    if (m == -INFINITY) continue;
-    const float f = exp2f(m - M);
-    den += f * r[D + 1];
-    num += f * r[t];
+  for (int i = tid; i < n_part; i += 256) M = fmaxf(M, base[i * stride + D]);
+  M = block_max<256>(M, sh);
+  float den = 0.f;
+  for (int i = tid; i < n_part; i += 256) {
+    const float m = base[i * stride + D];
+    const float f = (m == -INFINITY) ? 0.f : exp2f(m - M);
+    wts[i] = f;
+    den += f * base[i * stride + D + 1];
   }
-  for (int i = 0; i < n_res; ++i) {
-    const float* r = rs + (int64_t)i * G * RS;
-    const float m = r[D];
-    if (m == -INFINITY) continue;
-    const float f = exp2f(m - M);
-    den += f * r[D + 1];
-    num += f * r[t];
+  den = block_sum<256>(den, sh);
+  const int d = tid % D, grp = tid / D;
+  float num = 0.f;
+#pragma unroll 8
+  for (int i = grp; i < n_part; i += NG) num += wts[i] * base[i * stride + d];
+  acc[grp][d] = num;
+  __syncthreads();
+  if (grp == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < NG; ++k) t += acc[k][d];
+    const int64_t orow = (int64_t)seq * Hq + hq;
+    out[orow * D + d] = den > 0.f ? t / den : 0.f;
+    if (lse && d == 0) lse[orow] = den > 0.f ? (M + log2f(den)) * kLn2 : -INFINITY;
   }
-  const int64_t orow = (int64_t)seq * Hq + hq;
-  out[orow * D + t] = den > 0.f ? num / den : 0.f;
-  if (lse && t == 0) lse[orow] = den > 0.f ? (M + log2f(den)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
 // Dense baseline: wave w of unit u covers tokens [w*N/NW, (w+1)*N/NW).
 // ---------------------------------------------------------------------------
-template <int D, int G, typename T>
+template <int D, int G, typename Engine, typename T>
 __global__ __launch_bounds__(256) void k_dense(KVRef kv, const float* q, int Hq, int Hkv, int splits,
                                                float scale_l2, SeqArgs seq_args, float* ex_part) {
   constexpr int RS = D + kPartPad;
+  __shared__ u32x4 kvbuf[4][Engine::BUF];
+  __shared__ float st[4 * G * (D + 2)];
   const int u = blockIdx.y, p = blockIdx.x;
   const int wave = threadIdx.x >> 6;
   const int seq = u / Hkv, kvh = u % Hkv;
@@ -731,20 +727,24 @@ __global__ __launch_bounds__(256) void k_dense(KVRef kv, const float* q, int Hq,
   const int w = p * 4 + wave;
   const int t0 = (int)((int64_t)w * N / NW);
   const int t1 = (int)((int64_t)(w + 1) * N / NW);
-  RowAcc<D, G> acc;
+  Engine acc;
   acc.init(q + ((int64_t)seq * Hq + (int64_t)kvh * G) * D, scale_l2);
-  if (t1 > t0) {
-    const T* kc = static_cast<const T*>(kv.k);
-    const T* vc = static_cast<const T*>(kv.v);
-    if (!kv.paged) {
-      const int64_t base = kv_row_offset(kv, seq, kvh, t0, D);
-      acc.template rows<T>(kc, vc, t1 - t0, 0xffffffffu, [&](int i) { return base + (int64_t)i * D; });
-    } else {
-      acc.template rows<T>(kc, vc, t1 - t0, 0xffffffffu,
-                           [&](int i) { return kv_row_offset(kv, seq, kvh, t0 + i, D); });
-    }
+  const T* kc = static_cast<const T*>(kv.k);
+  const T* vc = static_cast<const T*>(kv.v);
+  u32x4* buf = kvbuf[wave];
+  if (!kv.paged) {
+    const int64_t base = kv_row_offset(kv, seq, kvh, 0, D);
+    for (int t = t0; t < t1; t += 32)
+      acc.tile(buf, kc + base + (int64_t)t * D, vc + base + (int64_t)t * D, min(32, t1 - t), 0xffffffffu);
+  } else {
+    for (int t = t0; t < t1; t += 32)
+      acc.tile_gather(buf, kc, vc, min(32, t1 - t), 0xffffffffu,
+                      [&](int i) { return kv_row_offset(kv, seq, kvh, t + i, D); });
   }
-  acc.finish(ex_part + ((int64_t)u * splits + p) * G * RS);
+  acc.to_lds(st);
+  __syncthreads();
+  write_block_record<D, G>(st, 0, [](int) { return (const float*)nullptr; },
+                           ex_part + ((int64_t)u * splits + p) * G * RS);
 }
 
 // ---------------------------------------------------------------------------
@@ -788,31 +788,35 @@ hipError_t launch_layout_table(const mog_layout& L, const SeqArgs& seq, hipStrea
   return hipGetLastError();
 }
 
-template <int D, int G, typename T>
+template <int D, int G>
 static hipError_t decode_impl(const DecodeLaunch& x, const DArgs& a, const BudgetArgs& b, hipStream_t s) {
   const int nu = x.L.n_units;
-  hipLaunchKernelGGL((k_score_clusters<D, G>), dim3((x.L.max_C + 63) / 64, nu), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_score_clusters<D, G>), dim3((x.L.max_C + 15) / 16, nu), dim3(256), 0, s, a);
   hipLaunchKernelGGL(k_select_topc, dim3(G, nu), dim3(256), 0, s, a, b, G);
-  hipLaunchKernelGGL((k_subclusters<D, G>), dim3(x.nb_res, nu), dim3(256), 0, s, a, b);
-  hipLaunchKernelGGL(k_plan, dim3(nu), dim3(1024), 0, s, a, G);
-  hipLaunchKernelGGL((k_exact<D, G, T>), dim3(x.splits, nu), dim3(256), 0, s, a);
-  hipLaunchKernelGGL((k_merge<D>), dim3(x.Hq, x.L.n_seq), dim3(D), 0, s, a.ws.ex_part, x.splits,
-                     a.ws.res_part, x.nb_res, a.L.units, x.residual, G, x.Hq, x.L.n_kv_heads, x.out,
-                     x.lse);
+  hipLaunchKernelGGL((k_subclusters<D, G>), dim3(x.nb_res, nu), dim3(256), 0, s, a, b, x.nb_chosen);
+  if (x.ev_begin) hipEventRecord(x.ev_begin, s);
+  if (x.dtype == MOG_BF16) {
+    hipLaunchKernelGGL((k_exact<D, G, MfmaTile<D, G>, uint16_t>), dim3(x.splits, nu), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((k_exact<D, G, RowAcc<D, G>, float>), dim3(x.splits, nu), dim3(256), 0, s, a);
+  }
+  if (x.ev_end) hipEventRecord(x.ev_end, s);
+  hipLaunchKernelGGL((k_merge<D>), dim3(x.Hq, x.L.n_seq), dim3(256), 0, s, a.ws.ex_part, x.splits, G, x.Hq,
+                     x.L.n_kv_heads, x.out, x.lse);
   return hipGetLastError();
 }
 
-template <int D, typename T>
+template <int D>
 static hipError_t decode_g(const DecodeLaunch& x, const DArgs& a, const BudgetArgs& b, hipStream_t s) {
   switch (x.G) {
-    case 1: return decode_impl<D, 1, T>(x, a, b, s);
-    case 2: return decode_impl<D, 2, T>(x, a, b, s);
-    case 3: return decode_impl<D, 3, T>(x, a, b, s);
-    case 4: return decode_impl<D, 4, T>(x, a, b, s);
-    case 5: return decode_impl<D, 5, T>(x, a, b, s);
-    case 6: return decode_impl<D, 6, T>(x, a, b, s);
-    case 7: return decode_impl<D, 7, T>(x, a, b, s);
-    case 8: return decode_impl<D, 8, T>(x, a, b, s);
+    case 1: return decode_impl<D, 1>(x, a, b, s);
+    case 2: return decode_impl<D, 2>(x, a, b, s);
+    case 3: return decode_impl<D, 3>(x, a, b, s);
+    case 4: return decode_impl<D, 4>(x, a, b, s);
+    case 5: return decode_impl<D, 5>(x, a, b, s);
+    case 6: return decode_impl<D, 6>(x, a, b, s);
+    case 7: return decode_impl<D, 7>(x, a, b, s);
+    case 8: return decode_impl<D, 8>(x, a, b, s);
   }
   return hipErrorInvalidValue;
 }
@@ -850,41 +854,43 @@ hipError_t launch_decode(const DecodeLaunch& x, hipStream_t s) {
     b.top_c[i] = x.seq.top_c[i];
     b.top_s[i] = x.seq.top_s[i];
   }
-  if (x.D == 128) {
-    return x.dtype == MOG_BF16 ? decode_g<128, uint16_t>(x, a, b, s) : decode_g<128, float>(x, a, b, s);
-  }
-  return x.dtype == MOG_BF16 ? decode_g<64, uint16_t>(x, a, b, s) : decode_g<64, float>(x, a, b, s);
+  return x.D == 128 ? decode_g<128>(x, a, b, s) : decode_g<64>(x, a, b, s);
 }
 
-template <int D, int G, typename T>
+template <int D, int G>
 static hipError_t dense_impl(const DenseLaunch& x, hipStream_t s) {
   const int nu = x.seq.n_seq * x.n_kv_heads;
-  hipLaunchKernelGGL((k_dense<D, G, T>), dim3(x.splits, nu), dim3(256), 0, s, x.kv, x.q, x.Hq,
-                     x.n_kv_heads, x.splits, x.scale * kLog2e, x.seq, x.ex_part);
-  hipLaunchKernelGGL((k_merge<D>), dim3(x.Hq, x.seq.n_seq), dim3(D), 0, s, x.ex_part, x.splits,
-                     (const float*)nullptr, 0, (const mog_unit*)nullptr, 0, G, x.Hq, x.n_kv_heads,
-                     x.out, x.lse);
+  if (x.ev_begin) hipEventRecord(x.ev_begin, s);
+  if (x.dtype == MOG_BF16) {
+    hipLaunchKernelGGL((k_dense<D, G, MfmaTile<D, G>, uint16_t>), dim3(x.splits, nu), dim3(256), 0, s, x.kv, x.q,
+                       x.Hq, x.n_kv_heads, x.splits, x.scale * kLog2e, x.seq, x.ex_part);
+  } else {
+    hipLaunchKernelGGL((k_dense<D, G, RowAcc<D, G>, float>), dim3(x.splits, nu), dim3(256), 0, s, x.kv, x.q,
+                       x.Hq, x.n_kv_heads, x.splits, x.scale * kLog2e, x.seq, x.ex_part);
+  }
+  if (x.ev_end) hipEventRecord(x.ev_end, s);
+  hipLaunchKernelGGL((k_merge<D>), dim3(x.Hq, x.seq.n_seq), dim3(256), 0, s, x.ex_part, x.splits, G, x.Hq,
+                     x.n_kv_heads, x.out, x.lse);
   return hipGetLastError();
 }
 
-template <int D, typename T>
+template <int D>
 static hipError_t dense_g(const DenseLaunch& x, hipStream_t s) {
   switch (x.G) {
-    case 1: return dense_impl<D, 1, T>(x, s);
-    case 2: return dense_impl<D, 2, T>(x, s);
-    case 3: return dense_impl<D, 3, T>(x, s);
-    case 4: return dense_impl<D, 4, T>(x, s);
-    case 5: return dense_impl<D, 5, T>(x, s);
-    case 6: return dense_impl<D, 6, T>(x, s);
-    case 7: return dense_impl<D, 7, T>(x, s);
-    case 8: return dense_impl<D, 8, T>(x, s);
+    case 1: return dense_impl<D, 1>(x, s);
+    case 2: return dense_impl<D, 2>(x, s);
+    case 3: return dense_impl<D, 3>(x, s);
+    case 4: return dense_impl<D, 4>(x, s);
+    case 5: return dense_impl<D, 5>(x, s);
+    case 6: return dense_impl<D, 6>(x, s);
+    case 7: return dense_impl<D, 7>(x, s);
+    case 8: return dense_impl<D, 8>(x, s);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_dense(const DenseLaunch& x, hipStream_t s) {
-  if (x.D == 128) return x.dtype == MOG_BF16 ? dense_g<128, uint16_t>(x, s) : dense_g<128, float>(x, s);
-  return x.dtype == MOG_BF16 ? dense_g<64, uint16_t>(x, s) : dense_g<64, float>(x, s);
+  return x.D == 128 ? dense_g<128>(x, s) : dense_g<64>(x, s);
 }
 
 }  // namespace mog

@@ -91,15 +91,10 @@ struct DecodeWS {
   float* cl_score;      // [total_cl][G]      log2-domain scores
   uint32_t* cl_mask;    // [total_cl]         heads that chose the cluster
   int32_t* cl_rank;     // [total_cl][G]      rank among a head's chosen clusters, or -1
+  int32_t* cl_rows;     // [total_cl]         rows of the cluster read exactly (any head)
   uint32_t* sub_mask;   // [total_sub]        heads that chose the subcluster
   float* res_part;      // [n_units][nb_res][G][D+4] residual partials
-  int32_t* run_start;   // [total_sub + 2*n_units]
-  int32_t* run_len;
-  uint32_t* run_mask;
-  int32_t* run_vstart;
-  int32_t* unit_tot;    // [n_units][2]  runs, rows
-  int32_t* wstart;      // [n_units][splits*4][2]
-  float* ex_part;       // [n_units][splits][G][D+4] exact partials
+  float* ex_part;       // [n_units][splits][G][D+4] exact (+ residual) partials
 };
 
 struct DecodeLaunch {
@@ -115,8 +110,10 @@ struct DecodeLaunch {
   int32_t Hq, G, D, dtype;
   int32_t residual;
   int32_t splits;
-  int32_t nb_res;       // residual blocks per unit (max over units)
+  int32_t nb_res;       // residual records per unit: nb_chosen + clusters/16
+  int32_t nb_chosen;    // chosen-cluster blocks per unit (max G * top_c)
   float scale;
+  hipEvent_t ev_begin, ev_end;  // optional, around the exact kernel
   DecodeWS ws;
 };
 
@@ -129,10 +126,11 @@ struct DenseLaunch {
   int32_t Hq, G, D, dtype, n_kv_heads;
   int32_t splits;
   float scale;
+  hipEvent_t ev_begin, ev_end;  // optional, around the dense kernel
   float* ex_part;       // [n_units][splits][G][D+4]
 };
 
-constexpr int kResClustersPerBlock = 16;
+constexpr int kRestClustersPerBlock = 16;  // residual-only blocks: 4 clusters per wave
 constexpr int kPartPad = 4;   // partial record = o[D], m, l, pad
 
 hipError_t launch_layout_table(const mog_layout& L, const SeqArgs& seq, hipStream_t s);

@@ -29,18 +29,22 @@ def _isqrt_ceil(n: int) -> int:
     return r if r * r == n else r + 1
 
 
-def budget_for_length(L: int, n_sink: int, n_recent: int, frac: float = 0.05):
-    """Per-query-head exact budget (top_c, top_s) that reads about ``frac``
-    of a length-L sequence: s = ceil(S/4) and c is the largest count whose
+def budget_for_length(L: int, n_sink: int, n_recent: int, frac: float = 0.05, kappa: float = 1.0):
+    """Per-query-head exact budget (top_c, top_s) for a length-L sequence.
+
+    Average-size rule: s = ceil(S/4) and c is the largest count whose
     expected exact rows (anchors plus c*s average-sized subclusters) stay
-    within frac*L.  C and S are the workload's nominal partition sizes."""
+    within frac*L.  The groups the log-mass score picks are larger than
+    average (their score carries ln n), so a workload scales c by ``kappa``,
+    measured so that the mean share of the sequence a query head actually
+    reads stays within frac (see ``calibrate.py``)."""
     C = _isqrt_ceil(L)
     S = max(1, (L - 1).bit_length())
     s = -(-S // 4)
     n_mid = L - n_sink - n_recent
     per_sub = n_mid / (C * S)
     c = int(math.floor((frac * L - (n_sink + n_recent)) / (s * per_sub)))
-    return max(c, 1), s
+    return max(int(math.floor(kappa * max(c, 1))), 1), s
 
 
 @dataclass
@@ -66,6 +70,7 @@ class Workload:
     plant_uniform: bool = False     # plant on a uniform middle token, not a component
     seed: int = BASE_SEED
     kmeans_iters: int = 10
+    budget_kappa: float = 1.0       # scale of the average-size budget rule
     notes: str = ""
 
     @property
@@ -95,35 +100,36 @@ def config(i: int, **override) -> Workload:
     elif i == 1:
         wl = Workload(name="gqa-32q8kv-d128-32K-bf16", n_seq=1, n_q_heads=32, n_kv_heads=8,
                       head_dim=128, seq_lens=[32768], dtype="bf16", n_sink=64, n_recent=256,
-                      top_c=[27], top_s=[4], n_components=512, outlier_dims=2,
-                      seed=BASE_SEED + 1)
+                      top_c=[8], top_s=[4], n_components=512, outlier_dims=2,
+                      budget_kappa=8 / 27, seed=BASE_SEED + 1)
     elif i == 2:
         wl = Workload(name="mha-4x32h-d128-128K-bf16", n_seq=4, n_q_heads=32, n_kv_heads=32,
                       head_dim=128, seq_lens=[131072] * 4, dtype="bf16", n_sink=64,
-                      n_recent=256, top_c=[58] * 4, top_s=[5] * 4, n_components=512,
-                      outlier_dims=2, needles=16, seed=BASE_SEED + 2)
+                      n_recent=256, top_c=[18] * 4, top_s=[5] * 4, n_components=512,
+                      outlier_dims=2, needles=16, budget_kappa=18 / 58, seed=BASE_SEED + 2)
     elif i == 3:
         wl = Workload(name="gqa-40q8kv-d128-1M-bf16", n_seq=1, n_q_heads=40, n_kv_heads=8,
                       head_dim=128, seq_lens=[1048576], dtype="bf16", n_sink=64, n_recent=256,
-                      top_c=[203], top_s=[5], n_components=2048, outlier_dims=2,
-                      seed=BASE_SEED + 3)
+                      top_c=[34], top_s=[5], n_components=2048, outlier_dims=2,
+                      budget_kappa=34 / 203, seed=BASE_SEED + 3)
     elif i == 4:
         rng = np.random.default_rng(BASE_SEED + 4)
         lens = [int(math.floor(math.exp(rng.uniform(math.log(8192), math.log(262144)))))
                 for _ in range(16)]
-        bud = [budget_for_length(L, 64, 256) for L in lens]
+        bud = [budget_for_length(L, 64, 256, kappa=0.35) for L in lens]
         wl = Workload(name="ragged-16seq-8K-256K-paged-bf16", n_seq=16, n_q_heads=32,
                       n_kv_heads=8, head_dim=128, seq_lens=lens, dtype="bf16", n_sink=64,
                       n_recent=256, top_c=[b[0] for b in bud], top_s=[b[1] for b in bud],
                       n_components=512, outlier_dims=2, high_entropy_heads=(4, 5, 6, 7),
-                      paged=True, page_size=16, seed=BASE_SEED + 4)
+                      paged=True, page_size=16, budget_kappa=0.35, seed=BASE_SEED + 4)
     else:
         raise ValueError(f"no workload {i}")
     if "seq_lens" in override:
         override.setdefault("n_seq", len(override["seq_lens"]))
         if "top_c" not in override:
             bud = [budget_for_length(L, override.get("n_sink", wl.n_sink),
-                                     override.get("n_recent", wl.n_recent))
+                                     override.get("n_recent", wl.n_recent),
+                                     kappa=override.get("budget_kappa", wl.budget_kappa))
                    for L in override["seq_lens"]]
             override["top_c"] = [b[0] for b in bud]
             override["top_s"] = [b[1] for b in bud]
@@ -133,7 +139,7 @@ def config(i: int, **override) -> Workload:
 def build_workload():
     """The 128K-key single-head partition whose build time is reported:
     mixture keys as in the 32K GQA workload, d=128, bf16, 10 iterations."""
-    return config(1, n_q_heads=1, n_kv_heads=1, seq_lens=[131072], top_c=[58], top_s=[5],
+    return config(1, n_q_heads=1, n_kv_heads=1, seq_lens=[131072], top_c=[18], top_s=[5],
                   name="build-1head-128K-bf16", seed=BASE_SEED + 40)
 
 
