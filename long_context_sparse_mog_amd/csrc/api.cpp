@@ -166,8 +166,8 @@ KVRef make_kvref(const mog_kv* kv) {
 // Decode geometry
 // ------------------------------------------------------------------------
 struct DecodePlan {
-  int G, c_stride, s_stride, splits, nb_res, nb_chosen;
-  size_t o_clscore, o_clmask, o_clrank, o_clrows, o_submask, o_res, o_ex, bytes;
+  int G, c_stride, s_stride, splits, nblk, nb_res, nb_chosen;
+  size_t o_clscore, o_clmask, o_clrank, o_clrows, o_submask, o_urows, o_btab, o_uinfo, o_res, o_ex, bytes;
 };
 
 int seq_top(const int32_t* per, int dflt, int s) { return per ? per[s] : dflt; }
@@ -195,7 +195,6 @@ DecodePlan plan_decode(const mog_layout* L, const mog_decode_params* p) {
   d.G = p->n_q_heads / L->n_kv_heads;
   d.c_stride = 0;
   d.s_stride = 0;
-  int64_t est = 1;
   d.nb_chosen = 0;
   for (int s = 0; s < L->n_seq; ++s) {
     const int c = seq_top(p->top_c_per_seq, p->top_c, s);
@@ -203,23 +202,17 @@ DecodePlan plan_decode(const mog_layout* L, const mog_decode_params* p) {
     d.c_stride = std::max(d.c_stride, c);
     d.s_stride = std::max(d.s_stride, sk);
     const UnitSizes z = unit_sizes(L->seq_lens[s], L->n_sink, L->n_recent);
-    const int64_t per_sub = ceil_div(z.n_mid, (int64_t)z.C * z.S);
-    // chosen groups run larger than average (their score carries ln n), and
-    // the heads of a group choose partly different ones: allow 3x
-    const int64_t sel =
-        std::min<int64_t>(z.n_mid, 3 * (int64_t)d.G * std::min(c, z.C) * std::min(sk, z.S) * per_sub);
-    est = std::max<int64_t>(est, L->n_sink + L->n_recent + sel);
     d.nb_chosen = std::max<int>(d.nb_chosen, std::min(z.C, d.G * std::min(c, z.C)));
   }
   if (p->splits > 0) {
     d.splits = p->splits;
   } else {
-    // one round of 2 blocks of 4 waves per compute unit (512 blocks), at
-    // least ~64 rows per wave
-    int64_t sp = std::max<int64_t>(1, 512 / L->n_units);
-    sp = std::min<int64_t>(sp, ceil_div(est, 256));
-    d.splits = (int)std::max<int64_t>(1, std::min<int64_t>(sp, 256));
+    // one round of blocks: the exact kernel holds 2 blocks of 4 waves per
+    // compute unit, 512 on the chip; launching more leaves a second round
+    // that runs behind the first
+    d.splits = std::max(1, kExactResidentBlocks - L->n_units);
   }
+  d.nblk = d.splits + L->n_units;
   d.nb_res = d.nb_chosen + (int)ceil_div(L->max_C, kRestClustersPerBlock);
   const int D = L->head_dim, G = d.G, RS = D + kPartPad;
   const int64_t nu = L->n_units;
@@ -229,8 +222,11 @@ DecodePlan plan_decode(const mog_layout* L, const mog_decode_params* p) {
   d.o_clrank = o; o = align_up(o + (size_t)L->total_cl * G * 4);
   d.o_clrows = o; o = align_up(o + (size_t)L->total_cl * 4);
   d.o_submask = o; o = align_up(o + (size_t)L->total_sub * 4);
+  d.o_urows = o; o = align_up(o + (size_t)nu * 4);
+  d.o_btab = o; o = align_up(o + (size_t)d.nblk * 4 * 4);
+  d.o_uinfo = o; o = align_up(o + (size_t)nu * 2 * 4);
   d.o_res = o; o = align_up(o + (size_t)nu * d.nb_res * G * RS * 4);
-  d.o_ex = o; o = align_up(o + (size_t)nu * d.splits * G * RS * 4);
+  d.o_ex = o; o = align_up(o + (size_t)d.nblk * G * RS * 4);
   d.bytes = o;
   return d;
 }
@@ -502,6 +498,7 @@ mog_status mog_decode(const mog_layout* layout, const mog_kv* kv, const float* q
   x.dtype = kv->dtype;
   x.residual = params->residual ? 1 : 0;
   x.splits = d.splits;
+  x.nblk = d.nblk;
   x.nb_res = d.nb_res;
   x.nb_chosen = d.nb_chosen;
   x.scale = params->scale > 0.f ? params->scale : 1.0f / sqrtf((float)kv->head_dim);
@@ -513,6 +510,9 @@ mog_status mog_decode(const mog_layout* layout, const mog_kv* kv, const float* q
   x.ws.cl_rank = reinterpret_cast<int32_t*>(w + d.o_clrank);
   x.ws.cl_rows = reinterpret_cast<int32_t*>(w + d.o_clrows);
   x.ws.sub_mask = reinterpret_cast<uint32_t*>(w + d.o_submask);
+  x.ws.unit_rows = reinterpret_cast<int32_t*>(w + d.o_urows);
+  x.ws.btab = reinterpret_cast<int32_t*>(w + d.o_btab);
+  x.ws.uinfo = reinterpret_cast<int32_t*>(w + d.o_uinfo);
   x.ws.res_part = reinterpret_cast<float*>(w + d.o_res);
   x.ws.ex_part = reinterpret_cast<float*>(w + d.o_ex);
   hipError_t e = launch_decode(x, stream);

@@ -55,6 +55,10 @@ __device__ inline float swap8(float x) { return dpp<0x128>(x); }  // row_ror:8
 // ---------------------------------------------------------------------------
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Third word of a raw buffer resource on gfx9-family chips: 32-bit data
+// format (a zero format makes untyped loads return zero), no swizzle.
+constexpr int kBufferWord3 = 0x00020000;
+
 template <int D, int G>
 struct MfmaTile {
   static constexpr int PPR = D / 8;      // 16-byte pieces per row
@@ -63,23 +67,46 @@ struct MfmaTile {
   static constexpr int NC = D / 32;      // k-chunks of the score product
   static constexpr int NB = D / 16;      // 16-wide d blocks of the output
   static constexpr int RSB = D * 2 + 16; // LDS row stride in bytes (one 16-byte pad)
-  static constexpr int BUF = 32 * RSB / 16;  // u32x4 per wave buffer
+  static constexpr int VBUF = 32 * RSB / 16;  // u32x4 of the V staging rows
+  static constexpr int BUF = VBUF + NC * 64;   // + the query fragments
+
+  static constexpr bool PIPELINED = true;
+  struct Regs {
+    u32x4 k[NLI], v[NLI];
+  };
 
   f32x4 o[NB];
   float m, l;
-  bf16x8 qf[NC];
+  const u32x4* qf;  // LDS: query fragment c of lane l at qf[64 c + l]
 
-  __device__ void init(const float* qb, float scale_l2) {
+  // The query fragments live in the wave's LDS buffer (after the V rows),
+  // read back once per tile: registers go to the tile pipeline instead.
+  __device__ void init(const float* qb, float scale_l2, u32x4* buf) {
     const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15, h = n & 7;
+    // every lane loads (heads past G read head 0 and are zeroed): no
+    // divergent loads, all 2 * NC vector loads in flight together
+    const float4* src = reinterpret_cast<const float4*>(qb + (h < G ? h : 0) * D + 8 * g);
+    float4 raw[NC][2];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
+      raw[c][0] = src[8 * c];
+      raw[c][1] = src[8 * c + 1];
+    }
+    const float sc = h < G ? scale_l2 : 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const float v8[8] = {raw[c][0].x, raw[c][0].y, raw[c][0].z, raw[c][0].w,
+                           raw[c][1].x, raw[c][1].y, raw[c][1].z, raw[c][1].w};
+      bf16x8 f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float qv = h < G ? qb[h * D + 32 * c + 8 * g + j] * scale_l2 : 0.f;
+        const float qv = v8[j] * sc;
         const __bf16 hi = (__bf16)qv;
-        qf[c][j] = n < 8 ? hi : (__bf16)(qv - (float)hi);
+        f[j] = n < 8 ? hi : (__bf16)(qv - (float)hi);
       }
+      buf[VBUF + 64 * c + lane] = __builtin_bit_cast(u32x4, f);
     }
+    qf = buf + VBUF + lane;
 #pragma unroll
     for (int b = 0; b < NB; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     m = -INFINITY;
@@ -94,29 +121,66 @@ struct MfmaTile {
     return r < nrows ? r : nrows - 1;
   }
 
+  // Raw buffer resource over `bytes` bytes at p: a lane whose offset is at
+  // or past `bytes` reads zeros and touches no memory.
+  __device__ static __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kBufferWord3);
+  }
+
+  // Register layouts of a 32-row tile (lane = 16 g + n):
+  //  K: kr[NC t + c] holds row 16t + n, elements 32c + 8g .. +7: exactly the
+  //     A fragment of the score product, so K never passes through LDS;
+  //  V: vr[i] holds row lane / PPR + RPI i, elements 8 (lane % PPR) .. +7
+  //     (whole rows per load), staged row-major in LDS for transpose reads.
+  static_assert(2 * NC == NLI, "K and V tiles take the same registers");
+
+  // Load a tile of contiguous rows (row i at kp + i*D elements) with buffer
+  // loads over exactly nrows rows: one offset register each for K and V,
+  // row steps in the immediate/scalar offset (both count in the hardware
+  // range check).  Rows at or past nrows read zeros and touch no memory;
+  // their probability is zero.
+  __device__ static void load(const uint16_t* kp, const uint16_t* vp, int nrows, u32x4 (&kr)[NLI],
+                              u32x4 (&vr)[NLI]) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t bytes = (uint32_t)nrows * (D * 2);
+    const __amdgpu_buffer_rsrc_t rk = rsrc(kp, bytes), rv = rsrc(vp, bytes);
+    const int kb = (lane & 15) * (D * 2) + (lane >> 4) * 16;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        kr[NC * t + c] = __builtin_amdgcn_raw_buffer_load_b128(rk, kb, t * 16 * (D * 2) + c * 64, 0);
+    }
+    const int vb = (lane / PPR) * (D * 2) + (lane % PPR) * 16;
+#pragma unroll
+    for (int i = 0; i < NLI; ++i) vr[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vb, i * RPI * (D * 2), 0);
+  }
+
   // Contiguous rows: row i of the tile at kp + i*D (elements).
   __device__ void tile(u32x4* buf, const uint16_t* kp, const uint16_t* vp, int nrows, uint32_t mask) {
-    const int p = (threadIdx.x & 63) % PPR;
     u32x4 kr[NLI], vr[NLI];
-#pragma unroll
-    for (int i = 0; i < NLI; ++i) {
-      const int64_t off = (int64_t)load_row(i, nrows) * D + p * 8;
-      kr[i] = *reinterpret_cast<const u32x4*>(kp + off);
-      vr[i] = *reinterpret_cast<const u32x4*>(vp + off);
-    }
+    load(kp, vp, nrows, kr, vr);
     compute(buf, kr, vr, nrows, mask);
   }
 
-  // Rows anywhere: row i of the tile at element offset rowoff(i).
+  // Rows anywhere: row i of the tile at element offset rowoff(i); rows at or
+  // past nrows re-read row nrows - 1 (their probability is zero).
   template <typename RowOff>
   __device__ void tile_gather(u32x4* buf, const uint16_t* kb, const uint16_t* vb, int nrows, uint32_t mask,
                               RowOff rowoff) {
-    const int p = (threadIdx.x & 63) % PPR;
+    const int lane = threadIdx.x & 63;
     u32x4 kr[NLI], vr[NLI];
 #pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int r = 16 * t + (lane & 15);
+      const int64_t off = rowoff(r < nrows ? r : nrows - 1) + (lane >> 4) * 8;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) kr[NC * t + c] = *reinterpret_cast<const u32x4*>(kb + off + 32 * c);
+    }
+#pragma unroll
     for (int i = 0; i < NLI; ++i) {
-      const int64_t off = rowoff(load_row(i, nrows)) + p * 8;
-      kr[i] = *reinterpret_cast<const u32x4*>(kb + off);
+      const int r = lane / PPR + RPI * i;
+      const int64_t off = rowoff(r < nrows ? r : nrows - 1) + (lane % PPR) * 8;
       vr[i] = *reinterpret_cast<const u32x4*>(vb + off);
     }
     compute(buf, kr, vr, nrows, mask);
@@ -126,26 +190,20 @@ struct MfmaTile {
                           uint32_t mask) {
     const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15, h = n & 7;
     char* lds = reinterpret_cast<char*>(buf);
-    // row-major staging address of this lane's pieces
-    char* wr = lds + (lane / PPR) * RSB + (lane % PPR) * 16;
-    // the previous tile's reads of this buffer were issued before these
-    // writes, and LDS executes a wave's operations in order
-    __asm__ volatile("" ::: "memory");
-#pragma unroll
-    for (int i = 0; i < NLI; ++i) *reinterpret_cast<u32x4*>(wr + i * RPI * RSB) = kr[i];
-    // S^T = K Q^T for the two 16-token halves
-    const char* kf_base = lds + n * RSB + g * 16;
+    // S^T = K Q^T for the two 16-token halves, K straight from registers
     f32x4 s[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(kf_base + t * 16 * RSB + c * 64);
-        s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf), qf[c], s[t], 0, 0, 0);
-      }
+      for (int c = 0; c < NC; ++c)
+        s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[NC * t + c]),
+                                                       __builtin_bit_cast(bf16x8, qf[64 * c]), s[t], 0, 0, 0);
     }
     const bool hv = h < G && ((mask >> h) & 1u);
+    // token 16t + 4g + j of the tile exists when 16t + j < nrows - 4g (one
+    // per-lane register instead of eight row constants)
+    const int lim = nrows - 4 * g;
     float mt = -INFINITY;
     float sv[8];
 #pragma unroll
@@ -153,7 +211,7 @@ struct MfmaTile {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float x = s[t][j] + swap8(s[t][j]);
-        const bool ok = hv && (16 * t + 4 * g + j) < nrows;
+        const bool ok = hv && (16 * t + j) < lim;
         x = ok ? x : -INFINITY;
         sv[4 * t + j] = x;
         mt = fmaxf(mt, x);
@@ -176,9 +234,12 @@ struct MfmaTile {
     m = mn;
 #pragma unroll
     for (int b = 0; b < NB; ++b) o[b] *= alpha;
-    // values: same buffer, row-major, then V^T fragments by transpose reads:
-    // src lane (g, s) of each 16-lane group points at row 4g + s/4 (+16),
-    // columns 16b + 4(s%4) .. +3
+    // values: row-major in the wave's LDS buffer, then V^T fragments by
+    // transpose reads: src lane (g, s) of each 16-lane group points at row
+    // 4g + s/4 (+16), columns 16b + 4(s%4) .. +3.  The previous tile's reads
+    // of this buffer were issued before these writes, and LDS executes a
+    // wave's operations in order.
+    char* wr = lds + (lane / PPR) * RSB + (lane % PPR) * 16;
     __asm__ volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < NLI; ++i) *reinterpret_cast<u32x4*>(wr + i * RPI * RSB) = vr[i];
@@ -229,7 +290,7 @@ struct RowAcc {
   float m[G], l[G], o[G][8];
   float qv[G][8];
 
-  __device__ void init(const float* qb, float scale_l2) {
+  __device__ void init(const float* qb, float scale_l2, u32x4*) {
     const int sub = (threadIdx.x & 63) % LPR;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -244,6 +305,12 @@ struct RowAcc {
   }
 
   static constexpr int BUF = 1;
+  static constexpr bool PIPELINED = false;
+  struct Regs {
+    u32x4 k[1], v[1];
+  };
+  __device__ static void load(const float*, const float*, int, u32x4 (&)[1], u32x4 (&)[1]) {}
+  __device__ void compute(u32x4*, const u32x4 (&)[1], const u32x4 (&)[1], int, uint32_t) {}
 
   __device__ void tile(u32x4*, const float* kp, const float* vp, int nrows, uint32_t mask) {
     rows(kp, vp, nrows, mask, [](int i) { return (int64_t)i * D; });
@@ -331,38 +398,34 @@ struct RowAcc {
 };
 
 // ---------------------------------------------------------------------------
-// Block epilogue: merge the 4 wave states in st ([4][G][D+2]) and n_extra
-// further records (extra(j) points at record j's head-0 entry, heads RS
-// floats apart), then write one record (o[D], m, l) per head to dst.
-// Must be called by all 256 threads after to_lds() and a barrier.
-// ---------------------------------------------------------------------------
-template <int D, int G, typename Extra>
-__device__ inline void write_block_record(const float* st, int n_extra, Extra extra, float* dst) {
+// exp2(m - M) of a record with max m under the common max M; 0 for an
+// empty record (m = -inf)
+__device__ inline float exp2_or_zero(float m, float M) { return m == -INFINITY ? 0.f : exp2f(m - M); }
+
+// Block epilogue: merge the 4 wave states in st ([4][G][D+2]) into one
+// record per head, dst[h][0..D) = o, dst[h][D] = m, dst[h][D+1] = l
+// (G x (D+4) floats).  Called by all 256 threads after a barrier that made
+// st visible.
+template <int D, int G>
+__device__ inline void write_block_record(const float* st, float* dst) {
   constexpr int RS = D + kPartPad;
   for (int idx = threadIdx.x; idx < G * D; idx += 256) {
     const int h = idx / D, e = idx % D;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < 4; ++w) M = fmaxf(M, st[(w * G + h) * (D + 2) + D]);
-    for (int j = 0; j < n_extra; ++j) M = fmaxf(M, extra(j)[h * RS + D]);
-    float l2 = 0.f, o2 = 0.f;
+    float L = 0.f, O = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const float* r = st + (w * G + h) * (D + 2);
-      const float f = (r[D] == -INFINITY) ? 0.f : exp2f(r[D] - M);
-      l2 += f * r[D + 1];
-      o2 += f * r[e];
+      const float f = exp2_or_zero(r[D], M);
+      L += f * r[D + 1];
+      O += f * r[e];
     }
-    for (int j = 0; j < n_extra; ++j) {
-      const float* r = extra(j) + h * RS;
-      const float f = (r[D] == -INFINITY) ? 0.f : exp2f(r[D] - M);
-      l2 += f * r[D + 1];
-      o2 += f * r[e];
-    }
-    dst[h * RS + e] = o2;
+    dst[h * RS + e] = O;
     if (e == 0) {
       dst[h * RS + D] = M;
-      dst[h * RS + D + 1] = l2;
+      dst[h * RS + D + 1] = L;
     }
   }
 }

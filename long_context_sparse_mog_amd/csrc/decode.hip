@@ -40,6 +40,7 @@ struct DArgs {
   int32_t c_stride, s_stride, Hq, Hkv, n_sink, n_recent, residual, splits, nb_res;
   float scale_l2;    // scale * log2(e)
   float half_s2_l2;  // scale^2 / 2 * log2(e)
+  int32_t L_head_dim;
   DecodeWS ws;
 };
 
@@ -176,6 +177,7 @@ __global__ __launch_bounds__(256) void k_score_clusters(DArgs a) {
   const mog_unit U = a.L.units[u];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g0 = blockIdx.x * 16 + wave * 4;
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.ws.unit_rows[u] = 0;
   if (g0 >= U.C) return;
   const float* qb = a.q + ((int64_t)U.seq * a.Hq + (int64_t)U.kv_head * G) * D;
   float coef[G][EPL];
@@ -463,7 +465,10 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
         int rows = (lane < S && lds_sm[lane]) ? my_cnt : 0;
 #pragma unroll
         for (int o2 = 1; o2 < 64; o2 <<= 1) rows += __shfl_xor(rows, o2, 64);
-        if (lane == 0) a.ws.cl_rows[cg] = rows;
+        if (lane == 0) {
+          a.ws.cl_rows[cg] = rows;
+          atomicAdd(&a.ws.unit_rows[u], rows);
+        }
       }
       // residual of the subclusters a choosing head left out: wave w takes
       // subclusters w, w+4, ...
@@ -532,18 +537,242 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
 //    block also folds the residual partials p, p+splits, ... of its unit
 //    into its record.  Grid (splits, units).
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// 4a. Balanced assignment of the exact blocks: unit u reads T_u = anchors +
+//     rows of its chosen subclusters; each unit gets one block plus a share
+//     of the other `splits` blocks in proportion to T_u, written as a table
+//     block -> (unit, split, splits of the unit, first block of the unit);
+//     blocks left over exit at once.  One block of 1024 threads.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_assign_blocks(DArgs a, int n_units, int nblk) {
+  __shared__ int sh[16];
+  __shared__ long long tot_sh;
+  const int tid = threadIdx.x;
+  const int A = a.n_sink + a.n_recent;
+  long long part = 0;
+  for (int u = tid; u < n_units; u += 1024) part += (long long)A + a.ws.unit_rows[u];
+  for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+  __shared__ long long wsum[16];
+  if ((tid & 63) == 0) wsum[tid >> 6] = part;
+  __syncthreads();
+  if (tid == 0) {
+    long long t = 0;
+    for (int w = 0; w < 16; ++w) t += wsum[w];
+    tot_sh = t;
+  }
+  __syncthreads();
+  const long long total = tot_sh;
+  // every unit gets one block plus its share of the other nblk - n_units
+  // blocks, floor(T_u * extra / total): the shares sum to at most nblk;
+  // fewer extra blocks when there are under ~256 rows for each
+  long long extra = nblk - n_units;
+  const long long by_rows = (total + 255) / 256;
+  if (by_rows < extra) extra = by_rows;
+  int carry = 0;
+  for (int base = 0; base < n_units; base += 1024) {
+    const int u = base + tid;
+    int sp = 0;
+    if (u < n_units) {
+      const long long T = (long long)A + a.ws.unit_rows[u];
+      sp = 1 + (int)(total > 0 ? T * extra / total : 0);
+    }
+    int tot;
+    const int first = carry + block_excl_scan<1024>(sp, sh, tot);
+    if (u < n_units) {
+      a.ws.uinfo[2 * u] = first;
+      a.ws.uinfo[2 * u + 1] = sp;
+      for (int p = 0; p < sp && first + p < nblk; ++p) {
+        int32_t* e = a.ws.btab + 4 * (first + p);
+        e[0] = u;
+        e[1] = p;
+        e[2] = sp;
+        e[3] = first;
+      }
+    }
+    carry += tot;
+  }
+  for (int b = carry + tid; b < nblk; b += 1024) a.ws.btab[4 * b] = -1;
+}
+
+// A tile of at most 32 contiguous layout rows: element offset of its first
+// row, row count (0: no more tiles), mask of the heads that read it.
+struct TileDesc {
+  int64_t off;
+  int nrows;
+  uint32_t mask;
+  int src;  // 0: layout rows (k_mid / v_mid), 1: KV cache rows (anchors)
+};
+
+// A listed tile in LDS (16 bytes): offset, row count | src << 31, head mask.
+struct TileRec {
+  int64_t off;
+  int nrows_src;
+  uint32_t mask;
+};
+constexpr int kTileBatch = 64;  // tiles listed per wave before streaming them
+
+// Walks the chosen subclusters of a unit over a range [y, y1) of its
+// virtual cluster rows (vpre: exclusive prefix of the per-cluster counts,
+// in LDS), yielding 32-row tiles.  Adjacent subclusters chosen by the same
+// heads form one run.  Per-lane state holds the current cluster's S
+// subclusters (lane i: subcluster i); everything else is wave-uniform.
+struct RunCursor {
+  // anchor token segments of a contiguous cache (sinks, then recent); plain
+  // scalars so the cursor stays in registers
+  int64_t anc_pos0, anc_end0, anc_pos1, anc_end1;
+  int64_t anc_base;                // element offset of token 0 of the unit
+  int64_t y, y1;
+  int g, C, S, skip;
+  int64_t row_base;
+  const int* vpre;
+  unsigned long long chosen;
+  uint32_t my_m;
+  int my_st, my_en;
+  int run_pos, run_end;  // current run [run_pos, run_end) in unit rows
+  uint32_t run_mask;
+  int D;
+
+  __device__ void load_cluster(const DArgs& a, const mog_unit& U, int lane) {
+    const int64_t sg0 = U.sub_base + (int64_t)g * S;
+    const int32_t* off = a.L.sub_off + U.off_base + g * S;
+    my_m = 0u;
+    my_st = my_en = 0;
+    if (lane < S) {
+      my_m = a.ws.sub_mask[sg0 + lane];
+      my_st = off[lane];
+      my_en = off[lane + 1];
+    }
+    chosen = __ballot(my_m != 0u && my_en > my_st);
+  }
+
+  __device__ void begin(const DArgs& a, const mog_unit& U, const int* vp, int64_t y0, int64_t yend, int lane) {
+    anc_pos0 = anc_end0 = anc_pos1 = anc_end1 = 0;
+    anc_base = 0;
+    y = y0;
+    y1 = yend;
+    C = U.C;
+    S = U.S;
+    vpre = vp;
+    row_base = U.row_base;
+    D = 0;
+    run_pos = run_end = 0;
+    run_mask = 0u;
+    g = cluster_of(y);
+    skip = g < C ? (int)(y - vpre[g]) : 0;
+    if (g < C) load_cluster(a, U, lane);
+    else chosen = 0ull;
+  }
+
+  // the cluster holding virtual row yy (the last g with vpre[g] <= yy; it has
+  // rows since vpre[g+1] > yy), or C when yy is past the end
+  __device__ int cluster_of(int64_t yy) const {
+    if (yy >= vpre[C]) return C;
+    int lo = 0, hi = C;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (vpre[mid] <= yy) lo = mid; else hi = mid;
+    }
+    return lo;
+  }
+
+  // next run of the current range, or false when the range is done
+  __device__ bool next_run(const DArgs& a, const mog_unit& U, int lane) {
+    while (y < y1) {
+      while (!chosen) {
+        // all of cluster g consumed: the next row lives in cluster_of(y)
+        g = cluster_of(y);
+        if (g >= C) return false;
+        skip = (int)(y - vpre[g]);
+        load_cluster(a, U, lane);
+      }
+      const int i = __ffsll((long long)chosen) - 1;
+      const uint32_t m = (uint32_t)__shfl((int)my_m, i, 64);
+      const int st0 = __shfl(my_st, i, 64);
+      int en = __shfl(my_en, i, 64);
+      chosen &= chosen - 1ull;
+      while (chosen) {
+        const int j = __ffsll((long long)chosen) - 1;
+        if ((uint32_t)__shfl((int)my_m, j, 64) != m || __shfl(my_st, j, 64) != en) break;
+        en = __shfl(my_en, j, 64);
+        chosen &= chosen - 1ull;
+      }
+      const int len = en - st0;
+      if (skip >= len) {
+        skip -= len;
+        continue;
+      }
+      const int take = (int)((int64_t)(len - skip) < y1 - y ? (len - skip) : (y1 - y));
+      run_pos = st0 + skip;
+      run_end = run_pos + take;
+      run_mask = m;
+      y += take;
+      skip = 0;
+      return true;
+    }
+    return false;
+  }
+
+  // anchor part of the range: virtual rows [x0, x1) of [0, n_sink + n_recent)
+  __device__ void set_anchors(const DArgs& a, const mog_unit& U, int64_t x0, int64_t x1) {
+    const int64_t ns = a.n_sink;
+    anc_pos0 = x0;
+    anc_end0 = x1 < ns ? x1 : ns;
+    const int64_t r0 = x0 > ns ? x0 : ns;
+    anc_pos1 = U.N - a.n_recent + (r0 - ns);
+    anc_end1 = U.N - a.n_recent + (x1 - ns);
+    anc_base = kv_row_offset(a.kv, U.seq, U.kv_head, 0, a.L_head_dim);
+  }
+
+  __device__ TileDesc next(const DArgs& a, const mog_unit& U, int lane) {
+    TileDesc t;
+    t.nrows = 0;
+    t.off = 0;
+    t.mask = 0u;
+    t.src = 0;
+    if (anc_pos0 < anc_end0 || anc_pos1 < anc_end1) {
+      const bool first = anc_pos0 < anc_end0;
+      const int64_t pos = first ? anc_pos0 : anc_pos1;
+      const int64_t end = first ? anc_end0 : anc_end1;
+      const int n = end - pos < 32 ? (int)(end - pos) : 32;
+      t.off = anc_base + pos * a.L_head_dim;
+      t.nrows = n;
+      t.mask = 0xffffffffu;
+      t.src = 1;
+      if (first) anc_pos0 += n; else anc_pos1 += n;
+      return t;
+    }
+    if (y >= y1 && run_pos >= run_end) return t;
+    if (run_pos >= run_end && !next_run(a, U, lane)) return t;
+    const int n = run_end - run_pos < 32 ? run_end - run_pos : 32;
+    t.off = (row_base + run_pos) * a.L_head_dim;
+    t.nrows = n;
+    t.mask = run_mask;
+    run_pos += n;
+    return t;
+  }
+};
+
 template <int D, int G, typename Engine, typename T>
-__global__ __launch_bounds__(256) void k_exact(DArgs a) {
+__global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
   constexpr int RS = D + kPartPad;
   __shared__ u32x4 kvbuf[4][Engine::BUF];
   __shared__ float st[4 * G * (D + 2)];
   __shared__ int vpre[kMaxC + 1];
   __shared__ int sh[16];
-  const int u = blockIdx.y, p = blockIdx.x, tid = threadIdx.x;
+  __shared__ TileRec tiles[4][kTileBatch];
+  const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const mog_unit U = a.L.units[u];
+  const int32_t* be = a.ws.btab + 4 * blockIdx.x;
+  const int u = uni(be[0]);
+  if (u < 0) return;
+  const int p = uni(be[1]), splits_u = uni(be[2]);
+  const mog_unit U = uni_unit(a.L.units + u);
   const int C = U.C, S = U.S;
   const int A = a.n_sink + a.n_recent;
+  // query first: its loads overlap the cluster-row scan below
+  u32x4* buf = kvbuf[wave];
+  Engine acc;
+  acc.init(a.q + ((int64_t)U.seq * a.Hq + (int64_t)U.kv_head * G) * D, a.scale_l2, buf);
   {
     constexpr int EM = kMaxC / 256;
     const int E = (C + 255) / 256;
@@ -567,21 +796,17 @@ __global__ __launch_bounds__(256) void k_exact(DArgs a) {
     if (tid == 0) vpre[C] = total;
     __syncthreads();
   }
-  const int64_t Tt = A + vpre[C];
-  const int NW = a.splits * 4;
+  const int64_t Tt = A + uni(vpre[C]);
+  const int NW = splits_u * 4;
   const int w = p * 4 + wave;
   const int64_t r0 = (int64_t)w * Tt / NW;
   const int64_t r1 = (int64_t)(w + 1) * Tt / NW;
-  Engine acc;
-  acc.init(a.q + ((int64_t)U.seq * a.Hq + (int64_t)U.kv_head * G) * D, a.scale_l2);
-  u32x4* buf = kvbuf[wave];
   const T* kc = static_cast<const T*>(a.kv.k);
   const T* vc = static_cast<const T*>(a.kv.v);
   const uint32_t all = (1u << G) - 1u;
   int64_t x = r0;
-  if (x < r1 && x < A) {
-    // anchors from the KV cache: virtual row x < n_sink is token x, else
-    // token N - n_recent + (x - n_sink)
+  if (a.kv.paged && x < r1 && x < A) {
+    // anchors of a paged cache: rows gathered through the block table
     const KVRef kv = a.kv;
     const int seq = U.seq, kvh = U.kv_head;
     const int64_t xe = r1 < A ? r1 : A;
@@ -590,123 +815,147 @@ __global__ __launch_bounds__(256) void k_exact(DArgs a) {
       const int tok = sink ? (int)x : U.N - a.n_recent + (int)(x - a.n_sink);
       const int64_t seg_end = sink ? (a.n_sink < xe ? a.n_sink : xe) : xe;
       const int nr = (int)((seg_end - x) < 32 ? (seg_end - x) : 32);
-      if (!kv.paged) {
-        const int64_t base = kv_row_offset(kv, seq, kvh, tok, D);
-        acc.tile(buf, kc + base, vc + base, nr, all);
-      } else {
-        acc.tile_gather(buf, kc, vc, nr, all, [&](int i) { return kv_row_offset(kv, seq, kvh, tok + i, D); });
-      }
+      acc.tile_gather(buf, kc, vc, nr, all, [&](int i) { return kv_row_offset(kv, seq, kvh, tok + i, D); });
       x += nr;
     }
   }
   if (x < r1) {
     const T* km = static_cast<const T*>(a.L.k_mid);
     const T* vm = static_cast<const T*>(a.L.v_mid);
-    const int32_t* off = a.L.sub_off + U.off_base;
-    int64_t y = x - A;
-    const int64_t y1 = r1 - A;
-    int lo = 0, hi = C;  // last cluster g with vpre[g] <= y
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (vpre[mid] <= y) lo = mid; else hi = mid;
-    }
-    int g = lo;
-    while (y < y1 && g < C) {
-      if (vpre[g + 1] == vpre[g]) {
-        ++g;
-        continue;
-      }
-      int skip = (int)(y - vpre[g]);
-      // the S subclusters of cluster g, one per lane
-      const int64_t sg0 = U.sub_base + (int64_t)g * S;
-      uint32_t my_m = 0u;
-      int my_st = 0, my_en = 0;
-      if (lane < S) {
-        my_m = a.ws.sub_mask[sg0 + lane];
-        my_st = off[g * S + lane];
-        my_en = off[g * S + lane + 1];
-      }
-      unsigned long long chosen = __ballot(my_m != 0u && my_en > my_st);
-      while (chosen && y < y1) {
-        const int i = __ffsll((long long)chosen) - 1;
-        const uint32_t m = (uint32_t)__shfl((int)my_m, i, 64);
-        const int st0 = __shfl(my_st, i, 64);
-        int en = __shfl(my_en, i, 64);
-        chosen &= chosen - 1ull;
-        // absorb following subclusters chosen by the same heads
-        while (chosen) {
-          const int j = __ffsll((long long)chosen) - 1;
-          if ((uint32_t)__shfl((int)my_m, j, 64) != m || __shfl(my_st, j, 64) != en) break;
-          en = __shfl(my_en, j, 64);
-          chosen &= chosen - 1ull;
+    TileRec* tl = tiles[wave];
+    while (x < r1) {
+      // (1) list the next batch of tiles of [x, r1) in LDS; the cursor and
+      //     its metadata loads are dead before the streaming loop starts
+      int nt = 0;
+      {
+        RunCursor cur;
+        const int64_t xa = x > A ? x : A;
+        cur.begin(a, U, vpre, xa - A, r1 - A, lane);
+        if (x < A) cur.set_anchors(a, U, x, r1 < A ? r1 : A);
+        for (; nt < kTileBatch; ++nt) {
+          const TileDesc t = cur.next(a, U, lane);
+          if (t.nrows <= 0) break;
+          if (lane == 0) tl[nt] = TileRec{t.off, t.nrows | (t.src << 31), t.mask};
+          x += t.nrows;
         }
-        const int len = en - st0;
-        if (skip >= len) {
-          skip -= len;
-          continue;
-        }
-        const int take = (int)((int64_t)(len - skip) < y1 - y ? (len - skip) : (y1 - y));
-        const int64_t base = (U.row_base + st0 + skip) * D;
-        for (int t0 = 0; t0 < take; t0 += 32)
-          acc.tile(buf, km + base + (int64_t)t0 * D, vm + base + (int64_t)t0 * D, min(32, take - t0), m);
-        y += take;
-        skip = 0;
+        if (nt < kTileBatch) x = r1;
+        nt = uni(nt);
+        x = uni(x);
       }
-      ++g;
+      if (nt == 0) break;
+      // (2) stream the batch: the next tile's loads are in flight while the
+      //     current one is computed.  rd(i) is tile i of the batch, or past
+      //     the end an empty tile (0 rows: its loads read nothing), so every
+      //     load is issued unconditionally and the wait for a tile's
+      //     registers never has to cover the next tile's loads.
+      auto rd = [&](int i) {
+        const TileRec r = tl[i < nt ? i : nt - 1];
+        TileDesc t;
+        t.off = uni(r.off);
+        const int ns = uni(r.nrows_src);
+        t.nrows = i < nt ? (ns & 0x7fffffff) : 0;
+        t.src = (int)((uint32_t)ns >> 31);
+        t.mask = (uint32_t)uni((int)r.mask);
+        return t;
+      };
+      auto kp = [&](const TileDesc& t) { return (t.src ? kc : km) + t.off; };
+      auto vp = [&](const TileDesc& t) { return (t.src ? vc : vm) + t.off; };
+      if constexpr (Engine::PIPELINED) {
+        typename Engine::Regs ra, rb;
+        TileDesc ta = rd(0), tb;
+        Engine::load(kp(ta), vp(ta), ta.nrows, ra.k, ra.v);
+        // the scheduling barriers keep each tile's loads ahead of the
+        // previous tile's arithmetic (the scheduler would otherwise sink them
+        // to save registers and serialise load and compute)
+        for (int i = 0; i < nt; i += 2) {
+          tb = rd(i + 1);
+          Engine::load(kp(tb), vp(tb), tb.nrows, rb.k, rb.v);
+          __builtin_amdgcn_sched_barrier(0);
+          acc.compute(buf, ra.k, ra.v, ta.nrows, ta.mask);
+          if (i + 1 >= nt) break;
+          ta = rd(i + 2);
+          Engine::load(kp(ta), vp(ta), ta.nrows, ra.k, ra.v);
+          __builtin_amdgcn_sched_barrier(0);
+          acc.compute(buf, rb.k, rb.v, tb.nrows, tb.mask);
+        }
+      } else {
+        for (int i = 0; i < nt; ++i) {
+          const TileDesc t = rd(i);
+          acc.tile(buf, kp(t), vp(t), t.nrows, t.mask);
+        }
+      }
     }
   }
   acc.to_lds(st);
   __syncthreads();
-  const int nres = a.residual ? a.nb_res : 0;
-  const int n_extra = nres > p ? (nres - p + a.splits - 1) / a.splits : 0;
-  const float* rp = a.ws.res_part + (int64_t)u * a.nb_res * G * RS;
-  write_block_record<D, G>(st, n_extra, [&](int j) { return rp + (int64_t)(p + j * a.splits) * G * RS; },
-                           a.ws.ex_part + ((int64_t)u * a.splits + p) * G * RS);
+  write_block_record<D, G>(st, a.ws.ex_part + (int64_t)blockIdx.x * G * RS);
 }
 
 // ---------------------------------------------------------------------------
-// 5. Merge: per query head, the records of the unit's splits: one max, one
-//    weighted sum, one normalisation.  Grid (Hq, n_seq), 256 threads.
+// 5. Merge: per query head, the exact records of its unit (n_part per unit,
+//    or the range uinfo[u]) and the n_res residual records of the unit: one
+//    max, one weighted sum, one normalisation.  Grid (Hq, n_seq), 1024
+//    threads: (D/4)-lane groups each take every NG-th record with 16-byte
+//    loads, so all records of a head are in flight at about once.
 // ---------------------------------------------------------------------------
-constexpr int kMaxParts = 1024;
-
 template <int D>
-__global__ __launch_bounds__(256) void k_merge(const float* part, int n_part, int G, int Hq, int Hkv, float* out,
-                                               float* lse) {
+__global__ __launch_bounds__(1024) void k_merge(const float* part, int n_part, const int32_t* uinfo,
+                                                const float* res, int n_res, int G, int Hq, int Hkv, float* out,
+                                                float* lse) {
   constexpr int RS = D + kPartPad;
-  constexpr int NG = 256 / D;
-  __shared__ float wts[kMaxParts];
-  __shared__ float sh[8];
-  __shared__ float acc[NG][D];
+  constexpr int QL = D / 4;        // lanes per record (4 elements each)
+  constexpr int NG = 1024 / QL;    // records processed side by side
+  __shared__ float sh[32];
+  __shared__ float4 acc[NG][QL];
+  __shared__ float dsum[NG];
   const int hq = blockIdx.x, seq = blockIdx.y, tid = threadIdx.x;
   const int kvh = hq / G, h = hq % G;
   const int u = seq * Hkv + kvh;
-  const float* base = part + ((int64_t)u * n_part * G + h) * RS;
-  const int64_t stride = (int64_t)G * RS;
-  float M = -INFINITY;
-  for (int i = tid; i < n_part; i += 256) M = fmaxf(M, base[i * stride + D]);
-  M = block_max<256>(M, sh);
-  float den = 0.f;
-  for (int i = tid; i < n_part; i += 256) {
-    const float m = base[i * stride + D];
-    const float f = (m == -INFINITY) ? 0.f : exp2f(m - M);
-    wts[i] = f;
-    den += f * base[i * stride + D + 1];
+  int64_t first = (int64_t)u * n_part;
+  if (uinfo) {
+    first = uinfo[2 * u];
+    n_part = uinfo[2 * u + 1];
   }
-  den = block_sum<256>(den, sh);
-  const int d = tid % D, grp = tid / D;
-  float num = 0.f;
-#pragma unroll 8
-  for (int i = grp; i < n_part; i += NG) num += wts[i] * base[i * stride + d];
-  acc[grp][d] = num;
+  const int64_t stride = (int64_t)G * RS;
+  const float* eb = part + (first * G + h) * RS;
+  const float* rb = res ? res + ((int64_t)u * n_res * G + h) * RS : nullptr;
+  const int total = n_part + (res ? n_res : 0);
+  auto rec = [&](int i) { return i < n_part ? eb + i * stride : rb + (int64_t)(i - n_part) * stride; };
+  float M = -INFINITY;
+  for (int i = tid; i < total; i += 1024) M = fmaxf(M, rec(i)[D]);
+  M = block_max<1024>(M, sh);
+  const int q = tid % QL, grp = tid / QL;
+  float4 num = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+#pragma unroll 4
+  for (int i = grp; i < total; i += NG) {
+    const float* r = rec(i);
+    const float f = exp2_or_zero(r[D], M);
+    const float4 o = reinterpret_cast<const float4*>(r)[q];
+    num.x += f * o.x;
+    num.y += f * o.y;
+    num.z += f * o.z;
+    num.w += f * o.w;
+    den += f * r[D + 1];
+  }
+  acc[grp][q] = num;
+  if (q == 0) dsum[grp] = den;
   __syncthreads();
-  if (grp == 0) {
-    float t = 0.f;
-#pragma unroll
-    for (int k = 0; k < NG; ++k) t += acc[k][d];
+  if (tid < QL) {
+    float4 t = {0.f, 0.f, 0.f, 0.f};
+    float dn = 0.f;
+    for (int k = 0; k < NG; ++k) {
+      const float4 a = acc[k][tid];
+      t.x += a.x;
+      t.y += a.y;
+      t.z += a.z;
+      t.w += a.w;
+      dn += dsum[k];
+    }
     const int64_t orow = (int64_t)seq * Hq + hq;
-    out[orow * D + d] = den > 0.f ? t / den : 0.f;
-    if (lse && d == 0) lse[orow] = den > 0.f ? (M + log2f(den)) * kLn2 : -INFINITY;
+    const float inv = dn > 0.f ? 1.f / dn : 0.f;
+    reinterpret_cast<float4*>(out + orow * D)[tid] = float4{t.x * inv, t.y * inv, t.z * inv, t.w * inv};
+    if (lse && tid == 0) lse[orow] = dn > 0.f ? (M + log2f(dn)) * kLn2 : -INFINITY;
   }
 }
 
@@ -714,7 +963,7 @@ __global__ __launch_bounds__(256) void k_merge(const float* part, int n_part, in
 // Dense baseline: wave w of unit u covers tokens [w*N/NW, (w+1)*N/NW).
 // ---------------------------------------------------------------------------
 template <int D, int G, typename Engine, typename T>
-__global__ __launch_bounds__(256) void k_dense(KVRef kv, const float* q, int Hq, int Hkv, int splits,
+__global__ __launch_bounds__(256, 2) void k_dense(KVRef kv, const float* q, int Hq, int Hkv, int splits,
                                                float scale_l2, SeqArgs seq_args, float* ex_part) {
   constexpr int RS = D + kPartPad;
   __shared__ u32x4 kvbuf[4][Engine::BUF];
@@ -727,15 +976,37 @@ __global__ __launch_bounds__(256) void k_dense(KVRef kv, const float* q, int Hq,
   const int w = p * 4 + wave;
   const int t0 = (int)((int64_t)w * N / NW);
   const int t1 = (int)((int64_t)(w + 1) * N / NW);
+  u32x4* buf = kvbuf[wave];
   Engine acc;
-  acc.init(q + ((int64_t)seq * Hq + (int64_t)kvh * G) * D, scale_l2);
+  acc.init(q + ((int64_t)seq * Hq + (int64_t)kvh * G) * D, scale_l2, buf);
   const T* kc = static_cast<const T*>(kv.k);
   const T* vc = static_cast<const T*>(kv.v);
-  u32x4* buf = kvbuf[wave];
   if (!kv.paged) {
-    const int64_t base = kv_row_offset(kv, seq, kvh, 0, D);
-    for (int t = t0; t < t1; t += 32)
-      acc.tile(buf, kc + base + (int64_t)t * D, vc + base + (int64_t)t * D, min(32, t1 - t), 0xffffffffu);
+    const T* kb = kc + kv_row_offset(kv, seq, kvh, 0, D);
+    const T* vb = vc + kv_row_offset(kv, seq, kvh, 0, D);
+    if constexpr (Engine::PIPELINED) {
+      // rows of the tile at t (0 past the end: its loads read nothing, so
+      // every load is issued unconditionally)
+      auto nr = [&](int t) { return max(0, min(32, t1 - t)); };
+      typename Engine::Regs ra, rb;
+      int t = t0;
+      Engine::load(kb + (int64_t)t * D, vb + (int64_t)t * D, nr(t), ra.k, ra.v);
+      while (t < t1) {
+        const int tb = t + 32;
+        Engine::load(kb + (int64_t)tb * D, vb + (int64_t)tb * D, nr(tb), rb.k, rb.v);
+        __builtin_amdgcn_sched_barrier(0);  // loads stay ahead of the arithmetic
+        acc.compute(buf, ra.k, ra.v, nr(t), 0xffffffffu);
+        if (tb >= t1) break;
+        const int tc = tb + 32;
+        Engine::load(kb + (int64_t)tc * D, vb + (int64_t)tc * D, nr(tc), ra.k, ra.v);
+        __builtin_amdgcn_sched_barrier(0);
+        acc.compute(buf, rb.k, rb.v, nr(tb), 0xffffffffu);
+        t = tc;
+      }
+    } else {
+      for (int t = t0; t < t1; t += 32)
+        acc.tile(buf, kb + (int64_t)t * D, vb + (int64_t)t * D, min(32, t1 - t), 0xffffffffu);
+    }
   } else {
     for (int t = t0; t < t1; t += 32)
       acc.tile_gather(buf, kc, vc, min(32, t1 - t), 0xffffffffu,
@@ -743,8 +1014,7 @@ __global__ __launch_bounds__(256) void k_dense(KVRef kv, const float* q, int Hq,
   }
   acc.to_lds(st);
   __syncthreads();
-  write_block_record<D, G>(st, 0, [](int) { return (const float*)nullptr; },
-                           ex_part + ((int64_t)u * splits + p) * G * RS);
+  write_block_record<D, G>(st, ex_part + ((int64_t)u * splits + p) * G * RS);
 }
 
 // ---------------------------------------------------------------------------
@@ -794,15 +1064,23 @@ static hipError_t decode_impl(const DecodeLaunch& x, const DArgs& a, const Budge
   hipLaunchKernelGGL((k_score_clusters<D, G>), dim3((x.L.max_C + 15) / 16, nu), dim3(256), 0, s, a);
   hipLaunchKernelGGL(k_select_topc, dim3(G, nu), dim3(256), 0, s, a, b, G);
   hipLaunchKernelGGL((k_subclusters<D, G>), dim3(x.nb_res, nu), dim3(256), 0, s, a, b, x.nb_chosen);
-  if (x.ev_begin) hipEventRecord(x.ev_begin, s);
-  if (x.dtype == MOG_BF16) {
-    hipLaunchKernelGGL((k_exact<D, G, MfmaTile<D, G>, uint16_t>), dim3(x.splits, nu), dim3(256), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((k_exact<D, G, RowAcc<D, G>, float>), dim3(x.splits, nu), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_assign_blocks, dim3(1), dim3(1024), 0, s, a, nu, x.nblk);
+  if (x.ev_begin) {
+    const hipError_t e = hipEventRecord(x.ev_begin, s);
+    if (e != hipSuccess) return e;
   }
-  if (x.ev_end) hipEventRecord(x.ev_end, s);
-  hipLaunchKernelGGL((k_merge<D>), dim3(x.Hq, x.L.n_seq), dim3(256), 0, s, a.ws.ex_part, x.splits, G, x.Hq,
-                     x.L.n_kv_heads, x.out, x.lse);
+  if (x.dtype == MOG_BF16) {
+    hipLaunchKernelGGL((k_exact<D, G, MfmaTile<D, G>, uint16_t>), dim3(x.nblk), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((k_exact<D, G, RowAcc<D, G>, float>), dim3(x.nblk), dim3(256), 0, s, a);
+  }
+  if (x.ev_end) {
+    const hipError_t e = hipEventRecord(x.ev_end, s);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((k_merge<D>), dim3(x.Hq, x.L.n_seq), dim3(1024), 0, s, a.ws.ex_part, 0,
+                     (const int32_t*)a.ws.uinfo, x.residual ? (const float*)a.ws.res_part : nullptr, x.nb_res, G,
+                     x.Hq, x.L.n_kv_heads, x.out, x.lse);
   return hipGetLastError();
 }
 
@@ -848,6 +1126,7 @@ hipError_t launch_decode(const DecodeLaunch& x, hipStream_t s) {
   a.nb_res = x.nb_res;
   a.scale_l2 = x.scale * kLog2e;
   a.half_s2_l2 = 0.5f * x.scale * x.scale * kLog2e;
+  a.L_head_dim = x.D;
   a.ws = x.ws;
   BudgetArgs b;
   for (int i = 0; i < MOG_MAX_SEQ; ++i) {
@@ -860,7 +1139,10 @@ hipError_t launch_decode(const DecodeLaunch& x, hipStream_t s) {
 template <int D, int G>
 static hipError_t dense_impl(const DenseLaunch& x, hipStream_t s) {
   const int nu = x.seq.n_seq * x.n_kv_heads;
-  if (x.ev_begin) hipEventRecord(x.ev_begin, s);
+  if (x.ev_begin) {
+    const hipError_t e = hipEventRecord(x.ev_begin, s);
+    if (e != hipSuccess) return e;
+  }
   if (x.dtype == MOG_BF16) {
     hipLaunchKernelGGL((k_dense<D, G, MfmaTile<D, G>, uint16_t>), dim3(x.splits, nu), dim3(256), 0, s, x.kv, x.q,
                        x.Hq, x.n_kv_heads, x.splits, x.scale * kLog2e, x.seq, x.ex_part);
@@ -868,9 +1150,12 @@ static hipError_t dense_impl(const DenseLaunch& x, hipStream_t s) {
     hipLaunchKernelGGL((k_dense<D, G, RowAcc<D, G>, float>), dim3(x.splits, nu), dim3(256), 0, s, x.kv, x.q,
                        x.Hq, x.n_kv_heads, x.splits, x.scale * kLog2e, x.seq, x.ex_part);
   }
-  if (x.ev_end) hipEventRecord(x.ev_end, s);
-  hipLaunchKernelGGL((k_merge<D>), dim3(x.Hq, x.seq.n_seq), dim3(256), 0, s, x.ex_part, x.splits, G, x.Hq,
-                     x.n_kv_heads, x.out, x.lse);
+  if (x.ev_end) {
+    const hipError_t e = hipEventRecord(x.ev_end, s);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((k_merge<D>), dim3(x.Hq, x.seq.n_seq), dim3(1024), 0, s, x.ex_part, x.splits,
+                     (const int32_t*)nullptr, (const float*)nullptr, 0, G, x.Hq, x.n_kv_heads, x.out, x.lse);
   return hipGetLastError();
 }
 

@@ -93,8 +93,11 @@ struct DecodeWS {
   int32_t* cl_rank;     // [total_cl][G]      rank among a head's chosen clusters, or -1
   int32_t* cl_rows;     // [total_cl]         rows of the cluster read exactly (any head)
   uint32_t* sub_mask;   // [total_sub]        heads that chose the subcluster
+  int32_t* unit_rows;   // [n_units]          rows of chosen subclusters per unit
+  int32_t* btab;        // [nblk][4]          exact block -> unit, split, splits, first block
+  int32_t* uinfo;       // [n_units][2]       first exact block, splits
   float* res_part;      // [n_units][nb_res][G][D+4] residual partials
-  float* ex_part;       // [n_units][splits][G][D+4] exact (+ residual) partials
+  float* ex_part;       // [nblk][G][D+4]     exact-attention block records
 };
 
 struct DecodeLaunch {
@@ -109,7 +112,8 @@ struct DecodeLaunch {
   int32_t c_stride, s_stride;
   int32_t Hq, G, D, dtype;
   int32_t residual;
-  int32_t splits;
+  int32_t splits;       // target exact blocks in total (balanced over units)
+  int32_t nblk;         // exact blocks launched: splits + n_units
   int32_t nb_res;       // residual records per unit: nb_chosen + clusters/16
   int32_t nb_chosen;    // chosen-cluster blocks per unit (max G * top_c)
   float scale;
@@ -131,7 +135,10 @@ struct DenseLaunch {
 };
 
 constexpr int kRestClustersPerBlock = 16;  // residual-only blocks: 4 clusters per wave
-constexpr int kPartPad = 4;   // partial record = o[D], m, l, pad
+constexpr int kPartPad = 4;
+// blocks of the exact-attention kernel resident at once on the chip: 256
+// compute units x 2 (its registers allow 2 waves per SIMD)
+constexpr int kExactResidentBlocks = 512;   // partial record = o[D], m, l, pad
 
 hipError_t launch_layout_table(const mog_layout& L, const SeqArgs& seq, hipStream_t s);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t s);
@@ -166,6 +173,30 @@ hipError_t launch_build(const BuildLaunch& a, hipStream_t s);
 // Device helpers
 // ---------------------------------------------------------------------------
 #if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
+// Wave-uniform copies (scalar registers) of values every lane holds alike.
+__device__ inline int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ inline int64_t uni(int64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ inline mog_unit uni_unit(const mog_unit* p) {
+  const mog_unit x = *p;
+  mog_unit U;
+  U.seq = uni(x.seq);
+  U.kv_head = uni(x.kv_head);
+  U.N = uni(x.N);
+  U.n_mid = uni(x.n_mid);
+  U.C = uni(x.C);
+  U.S = uni(x.S);
+  U.reserved0 = U.reserved1 = 0;
+  U.row_base = uni(x.row_base);
+  U.cl_base = uni(x.cl_base);
+  U.sub_base = uni(x.sub_base);
+  U.off_base = uni(x.off_base);
+  return U;
+}
+
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
