@@ -156,7 +156,7 @@ typedef struct {
   int32_t residual;             /* 1: add the Gaussian estimate of the rest;
                                    0: exact part only, renormalised            */
   float scale;                  /* logit scale; 0 selects 1/sqrt(head_dim)      */
-  int32_t splits;               /* 0: automatic; else 1..1024.  mog_decode: the
+  int32_t splits;               /* 0: automatic; else 1..8192.  mog_decode: the
                                    exact-attention blocks shared by all units in
                                    proportion to the rows each reads (plus one
                                    per unit); mog_dense_decode: blocks per unit */

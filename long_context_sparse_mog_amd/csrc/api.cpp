@@ -167,7 +167,7 @@ KVRef make_kvref(const mog_kv* kv) {
 // ------------------------------------------------------------------------
 struct DecodePlan {
   int G, c_stride, s_stride, splits, nblk, nb_res, nb_chosen;
-  size_t o_clscore, o_clmask, o_clrank, o_clrows, o_submask, o_urows, o_btab, o_uinfo, o_res, o_ex, bytes;
+  size_t o_clscore, o_clmask, o_clrank, o_clrows, o_submask, o_urows, o_list, o_nch, o_uinfo, o_res, o_ex, bytes;
 };
 
 int seq_top(const int32_t* per, int dflt, int s) { return per ? per[s] : dflt; }
@@ -179,7 +179,7 @@ mog_status check_decode_params(const mog_decode_params* p, int n_kv_heads, int n
                 n_kv_heads);
   const int G = p->n_q_heads / n_kv_heads;
   if (G > kMaxG) return fail(MOG_ERR_UNSUPPORTED, "%d query heads per KV head (max %d)", G, kMaxG);
-  if (p->splits < 0 || p->splits > 1024) return fail(MOG_ERR_INVALID_ARG, "splits=%d outside [0, 1024]", p->splits);
+  if (p->splits < 0 || p->splits > 8192) return fail(MOG_ERR_INVALID_ARG, "splits=%d outside [0, 8192]", p->splits);
   if (!(p->scale >= 0.f) || isinf(p->scale)) return fail(MOG_ERR_INVALID_ARG, "scale must be finite and >= 0");
   for (int s = 0; s < n_seq; ++s) {
     const int c = seq_top(p->top_c_per_seq, p->top_c, s);
@@ -223,7 +223,8 @@ DecodePlan plan_decode(const mog_layout* L, const mog_decode_params* p) {
   d.o_clrows = o; o = align_up(o + (size_t)L->total_cl * 4);
   d.o_submask = o; o = align_up(o + (size_t)L->total_sub * 4);
   d.o_urows = o; o = align_up(o + (size_t)nu * 4);
-  d.o_btab = o; o = align_up(o + (size_t)d.nblk * 4 * 4);
+  d.o_list = o; o = align_up(o + (size_t)L->total_cl * 4);
+  d.o_nch = o; o = align_up(o + (size_t)nu * 4);
   d.o_uinfo = o; o = align_up(o + (size_t)nu * 2 * 4);
   d.o_res = o; o = align_up(o + (size_t)nu * d.nb_res * G * RS * 4);
   d.o_ex = o; o = align_up(o + (size_t)d.nblk * G * RS * 4);
@@ -511,7 +512,8 @@ mog_status mog_decode(const mog_layout* layout, const mog_kv* kv, const float* q
   x.ws.cl_rows = reinterpret_cast<int32_t*>(w + d.o_clrows);
   x.ws.sub_mask = reinterpret_cast<uint32_t*>(w + d.o_submask);
   x.ws.unit_rows = reinterpret_cast<int32_t*>(w + d.o_urows);
-  x.ws.btab = reinterpret_cast<int32_t*>(w + d.o_btab);
+  x.ws.cl_list = reinterpret_cast<int32_t*>(w + d.o_list);
+  x.ws.n_chosen = reinterpret_cast<int32_t*>(w + d.o_nch);
   x.ws.uinfo = reinterpret_cast<int32_t*>(w + d.o_uinfo);
   x.ws.res_part = reinterpret_cast<float*>(w + d.o_res);
   x.ws.ex_part = reinterpret_cast<float*>(w + d.o_ex);

@@ -37,7 +37,7 @@ struct DArgs {
   float* lse;
   int32_t* sel_c;
   int32_t* sel_s;
-  int32_t c_stride, s_stride, Hq, Hkv, n_sink, n_recent, residual, splits, nb_res;
+  int32_t c_stride, s_stride, Hq, Hkv, n_sink, n_recent, residual, splits, nb_res, n_units, nblk;
   float scale_l2;    // scale * log2(e)
   float half_s2_l2;  // scale^2 / 2 * log2(e)
   int32_t L_head_dim;
@@ -177,7 +177,6 @@ __global__ __launch_bounds__(256) void k_score_clusters(DArgs a) {
   const mog_unit U = a.L.units[u];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g0 = blockIdx.x * 16 + wave * 4;
-  if (blockIdx.x == 0 && threadIdx.x == 0) a.ws.unit_rows[u] = 0;
   if (g0 >= U.C) return;
   const float* qb = a.q + ((int64_t)U.seq * a.Hq + (int64_t)U.kv_head * G) * D;
   float coef[G][EPL];
@@ -201,114 +200,121 @@ __global__ __launch_bounds__(256) void k_score_clusters(DArgs a) {
     const float lg = n > 0 ? log2f((float)n) : -INFINITY;
 #pragma unroll
     for (int h = 0; h < G; ++h) a.ws.cl_score[cg * G + h] = n > 0 ? mine[h] + lg : -INFINITY;
-    a.ws.cl_mask[cg] = 0u;
   }
 }
 
 // ---------------------------------------------------------------------------
-// 2. Top-c clusters of one query head: radix select (four 8-bit digits, most
-//    significant first) of the c-th largest order-preserving key, then the
-//    keys above it and the lowest-index keys equal to it.  Empty clusters
-//    are never chosen.  Grid (G, units), 256 threads.
+// 2. Top-c clusters of every head of a unit, one wave per head.  Cluster i
+//    sits in lane i % 64, slot i / 64 of the wave's registers; a bitwise
+//    radix select (most significant bit first, one wave-wide count per bit)
+//    finds the key of the c-th largest score, then the keys above it and the
+//    lowest-index keys equal to it are chosen.  Empty clusters are never
+//    chosen.  The block then writes every cluster's head mask and the
+//    ascending list of clusters some head chose.  Grid (units), 64 G threads.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_select_topc(DArgs a, BudgetArgs b, int G) {
-  const int h = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
-  const mog_unit U = a.L.units[u];
-  const int C = U.C;
-  __shared__ uint32_t keys[kMaxC];
-  __shared__ int hist[256];
-  __shared__ int sh[16];
-  __shared__ int sh_b, sh_above;
+__device__ inline int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
 
+template <int G>
+__global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
+  constexpr int NT = 64 * G;
+  constexpr int KPL = kMaxC / 64;
+  __shared__ uint32_t umask[kMaxC];
+  __shared__ int sh[16];
+  const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63, h = tid >> 6;
+  const mog_unit U = uni_unit(a.L.units + u);
+  const int C = U.C;
+  for (int i = tid; i < C; i += NT) umask[i] = 0u;
+  if (tid == 0) a.ws.unit_rows[u] = 0;
+  uint32_t key[KPL];
   int nvalid = 0;
-  for (int i = tid; i < C; i += 256) {
-    const float sc = a.ws.cl_score[(U.cl_base + i) * G + h];
-    const bool valid = sc != -INFINITY;
-    keys[i] = valid ? float_key(sc) : 0u;
-    nvalid += valid;
+  // all loads first (clamped index, no branch around them), then the keys
+  float scv[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) scv[j] = a.ws.cl_score[(U.cl_base + min(64 * j + lane, C - 1)) * G + h];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const bool in = 64 * j + lane < C && scv[j] != -INFINITY;
+    key[j] = in ? float_key(scv[j]) : 0u;
+    nvalid += in;
   }
-  int total;
-  block_excl_scan<256>(nvalid, sh, total);
+  nvalid = wave_sum_i(nvalid);  // once; the per-bit counts below use ballots
   int want = b.top_c[U.seq];
   want = want < 0 ? 0 : want;
-  int kk = want < total ? want : total;
-  const int c_eff = kk;
-  uint32_t prefix = 0u, pmask = 0u;
-  if (c_eff > 0) {
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      hist[tid] = 0;
-      __syncthreads();
-      for (int i = tid; i < C; i += 256) {
-        const uint32_t k = keys[i];
-        if (k != 0u && (k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
+  const int c_eff = want < nvalid ? want : nvalid;
+  int kk = c_eff;
+  uint32_t prefix = 0u;
+  if (kk > 0) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t hi_mask = ~0u << bit, target = prefix | (1u << bit);
+      // slots past C hold key 0, which never matches a nonzero target; the
+      // groups of 8 slots past C are skipped with one uniform branch each
+      int cnt = 0;
+#pragma unroll
+      for (int jg = 0; jg < KPL / 8; ++jg) {
+        if (512 * jg >= C) break;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) cnt += __popcll(__ballot((key[8 * jg + jj] & hi_mask) == target));
       }
-      __syncthreads();
-      const int v = hist[255 - tid];
-      int tot;
-      const int excl = block_excl_scan<256>(v, sh, tot);
-      if (excl < kk && excl + v >= kk) {
-        sh_b = 255 - tid;
-        sh_above = excl;
-      }
-      __syncthreads();
-      kk -= sh_above;
-      prefix |= (uint32_t)sh_b << shift;
-      pmask |= 255u << shift;
-      __syncthreads();
+      if (cnt >= kk) prefix = target;
+      else kk -= cnt;
     }
   }
-  // keys > prefix are all chosen; kk of the keys == prefix, lowest index first
-  const int E = (C + 255) / 256;
-  const int lo = tid * E;
-  const int hi = min(C, lo + E);
-  int neq = 0;
-  if (c_eff > 0)
-    for (int i = lo; i < hi; ++i) neq += keys[i] == prefix;
-  int tot;
-  int eqr = block_excl_scan<256>(neq, sh, tot);
-  uint32_t selbits = 0u;
-  int nsel = 0;
-  if (c_eff > 0) {
-    for (int i = lo; i < hi; ++i) {
-      const uint32_t k = keys[i];
-      bool s = false;
-      if (k > prefix) {
-        s = true;
-      } else if (k == prefix) {
-        s = eqr < kk;
-        ++eqr;
-      }
-      if (s) {
-        selbits |= 1u << (i - lo);
-        ++nsel;
-      }
-    }
-  }
-  int r = block_excl_scan<256>(nsel, sh, tot);
+  // chosen: key > prefix, or key == prefix among the first kk ties (by index)
   const int hq = U.kv_head * G + h;
   const int64_t row = (int64_t)U.seq * a.Hq + hq;
-  for (int i = lo; i < hi; ++i) {
-    int rank = -1;
-    if ((selbits >> (i - lo)) & 1u) {
-      rank = r++;
-      atomicOr(&a.ws.cl_mask[U.cl_base + i], 1u << h);
-      if (a.sel_c) a.sel_c[row * a.c_stride + rank] = i;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int ties = 0, rank0 = 0;
+  __syncthreads();  // umask cleared
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    if (64 * j >= C) break;
+    const int i = 64 * j + lane;
+    const bool tie = c_eff > 0 && key[j] == prefix && key[j] != 0u;
+    const unsigned long long tb = __ballot(tie);
+    const bool sel = c_eff > 0 && key[j] != 0u && (key[j] > prefix || (tie && ties + __popcll(tb & below) < kk));
+    ties += __popcll(tb);
+    const unsigned long long sb = __ballot(sel);
+    const int rank = sel ? rank0 + __popcll(sb & below) : -1;
+    rank0 += __popcll(sb);
+    if (i < C) {
+      a.ws.cl_rank[(U.cl_base + i) * G + h] = rank;
+      if (sel) {
+        atomicOr(&umask[i], 1u << h);
+        if (a.sel_c) a.sel_c[row * a.c_stride + rank] = i;
+      }
     }
-    a.ws.cl_rank[(U.cl_base + i) * G + h] = rank;
   }
   if (a.sel_c)
-    for (int j = c_eff + tid; j < a.c_stride; j += 256) a.sel_c[row * a.c_stride + j] = -1;
+    for (int j = c_eff + lane; j < a.c_stride; j += 64) a.sel_c[row * a.c_stride + j] = -1;
   if (a.sel_s) {
     const int64_t base = row * a.c_stride * a.s_stride;
-    for (int j = c_eff * a.s_stride + tid; j < a.c_stride * a.s_stride; j += 256) a.sel_s[base + j] = -1;
+    for (int j = c_eff * a.s_stride + lane; j < a.c_stride * a.s_stride; j += 64) a.sel_s[base + j] = -1;
   }
+  __syncthreads();
+  // head masks and the ascending list of chosen clusters (thread t covers
+  // clusters [t E, t E + E))
+  const int E = (C + NT - 1) / NT;
+  const int lo = tid * E, hi = min(C, lo + E);
+  int cnt = 0;
+  for (int i = lo; i < hi; ++i) {
+    a.ws.cl_mask[U.cl_base + i] = umask[i];
+    cnt += umask[i] != 0u;
+  }
+  int total;
+  int pos = block_excl_scan<NT>(cnt, sh, total);
+  for (int i = lo; i < hi; ++i)
+    if (umask[i] != 0u) a.ws.cl_list[U.cl_base + pos++] = i;
+  if (tid == 0) a.ws.n_chosen[u] = total;
 }
 
 // ---------------------------------------------------------------------------
 // 3. Subclusters and residual.  Grid (nb_chosen + nb_rest, units):
-//    * block x < nb_chosen takes the x-th chosen cluster of its unit (in
-//      cluster order; found by a block scan of the head masks): scores its S
+//    * block x < nb_chosen takes the x-th chosen cluster of its unit (from
+//      the ascending list the top-c pass wrote), if any: scores its S
 //      subclusters for every head (one batch of row loads per wave), picks
 //      the top-s of each head that chose the cluster, writes the subcluster
 //      head masks and the cluster's exactly-read row count, and accumulates
@@ -351,8 +357,8 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
   __shared__ float st[4][G][D + 2];
   __shared__ float lds_sc[kMaxS][G];
   __shared__ uint32_t lds_sm[kMaxS];
+  __shared__ int lds_cnt[kMaxS];
   __shared__ int sh[16];
-  __shared__ int found;
   const int u = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const mog_unit U = a.L.units[u];
@@ -372,30 +378,8 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
   if ((int)blockIdx.x < nb_chosen) {
     // -------- the x-th chosen cluster ---------------------------------------
     const int x = blockIdx.x;
-    {
-      constexpr int EM = kMaxC / 256;
-      const int E = (C + 255) / 256;
-      int cnt = 0;
-#pragma unroll
-      for (int k = 0; k < EM; ++k) {
-        const int g = tid * E + k;
-        if (k < E && g < C) cnt += a.ws.cl_mask[U.cl_base + g] != 0u;
-      }
-      if (tid == 0) found = -1;
-      int total;
-      int base = block_excl_scan<256>(cnt, sh, total);
-      if (x >= base && x < base + cnt) {
-        for (int k = 0; k < EM; ++k) {
-          const int g = tid * E + k;
-          if (k < E && g < C && a.ws.cl_mask[U.cl_base + g] != 0u) {
-            if (base == x) found = g;
-            ++base;
-          }
-        }
-      }
-      __syncthreads();
-    }
-    const int g = found;
+    const int n_ch = a.ws.n_chosen[u], g_x = a.ws.cl_list[U.cl_base + x];  // x < nb_chosen <= C
+    const int g = x < uni(n_ch) ? uni(g_x) : -1;
     if (g >= 0) {
       const int64_t cg = U.cl_base + g;
       const int64_t sg0 = U.sub_base + (int64_t)g * S;
@@ -403,12 +387,27 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
       const float* qb = a.q + ((int64_t)U.seq * a.Hq + (int64_t)U.kv_head * G) * D;
       float coef[G][EPL];
       score_coefs<D, G>(a, qb, coef);
-      // scores: wave w takes rows w, w+4, ...
+      // scores: wave w takes rows w, w+4, ...; the value means of the same
+      // rows are loaded alongside for the residual below
       float xr[RPW][EPL];
+      float vb[RPW][VPL];
 #pragma unroll
       for (int k = 0; k < RPW; ++k) {
         const int i = min(wave + 4 * k, S - 1);
         load_floats<EPL>(a.L.sub_ms + (sg0 + i) * (2 * D) + lane * EPL, xr[k]);
+        if (a.residual) load_floats<VPL>(a.L.sub_vbar + (sg0 + i) * D + lane * VPL, vb[k]);
+      }
+      // subcluster sizes and (for the selection output) the cluster's rank
+      // per head, issued with the loads above
+      {
+        const int i = min(tid, S - 1);
+        const int c = off[g * S + i + 1] - off[g * S + i];
+        if (tid < S) lds_cnt[tid] = c;
+      }
+      int rc[G];
+      if (a.sel_s) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) rc[h] = a.ws.cl_rank[cg * G + h];
       }
 #pragma unroll
       for (int k = 0; k < RPW; ++k) {
@@ -428,18 +427,19 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
       // full scores (count term added; -inf for an empty subcluster)
       if (tid < S * G) {
         const int i = tid / G, h = tid % G;
-        const int cnt = off[g * S + i + 1] - off[g * S + i];
+        const int cnt = lds_cnt[i];
         lds_sc[i][h] = cnt > 0 ? lds_sc[i][h] + log2f((float)cnt) : -INFINITY;
       }
       __syncthreads();
       // top-s of each choosing head: wave w handles heads w, w+4
-      int my_cnt = 0;
-      if (lane < S) my_cnt = off[g * S + lane + 1] - off[g * S + lane];
+      const int my_cnt = lane < S ? lds_cnt[lane] : 0;
       const bool valid = lane < S && my_cnt > 0;
       int s_keep = b.top_s[U.seq];
       s_keep = s_keep < 0 ? 0 : s_keep;
-      for (int h = wave; h < G; h += 4) {
-        if (!((mask >> h) & 1u)) continue;
+#pragma unroll
+      for (int h0 = 0; h0 < G; h0 += 4) {
+        const int h = h0 + wave;
+        if (h >= G || !((mask >> h) & 1u)) continue;
         const float my = valid ? lds_sc[lane][h] : -INFINITY;
         int rank = 0;
 #pragma unroll
@@ -452,9 +452,11 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
         if (sel) atomicOr(&lds_sm[lane], 1u << h);
         if (a.sel_s) {
           const unsigned long long bal = __ballot(sel);
-          const int rc = a.ws.cl_rank[cg * G + h];
+          int rch = rc[0];
+#pragma unroll
+          for (int hh = 1; hh < G; ++hh) rch = hh == h ? rc[hh] : rch;
           const int hq = U.kv_head * G + h;
-          const int64_t base = (((int64_t)U.seq * a.Hq + hq) * a.c_stride + rc) * a.s_stride;
+          const int64_t base = (((int64_t)U.seq * a.Hq + hq) * a.c_stride + rch) * a.s_stride;
           if (sel) a.sel_s[base + __popcll(bal & ((1ull << lane) - 1ull))] = lane;
           for (int j = __popcll(bal) + lane; j < a.s_stride; j += 64) a.sel_s[base + j] = -1;
         }
@@ -473,14 +475,12 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
       // residual of the subclusters a choosing head left out: wave w takes
       // subclusters w, w+4, ...
       if (a.residual) {
-        float vb[RPW][VPL];
         uint32_t need[RPW];
 #pragma unroll
         for (int k = 0; k < RPW; ++k) {
           const int i = wave + 4 * k;
           need[k] = 0u;
-          if (i < S && off[g * S + i + 1] > off[g * S + i]) need[k] = mask & ~lds_sm[i];
-          if (need[k]) load_floats<VPL>(a.L.sub_vbar + (sg0 + i) * D + lane * VPL, vb[k]);
+          if (i < S && lds_cnt[i] > 0) need[k] = mask & ~lds_sm[i];
         }
 #pragma unroll
         for (int k = 0; k < RPW; ++k) {
@@ -494,21 +494,32 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
     }
   } else {
     // -------- residual of clusters left out, 4 clusters per wave ------------
+    // every load of the wave's 4 clusters is issued before any is used
+    // (clusters past C re-read the last one and are skipped)
     const int y = blockIdx.x - nb_chosen;
+    uint32_t mask[4];
+    int n_g[4];
+    float vb[4][VPL], sc[4][G];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int g = min(y * 16 + wave * 4 + k, C - 1);
+      const int64_t cg = U.cl_base + g;
+      mask[k] = a.ws.cl_mask[cg];
+      n_g[k] = off[(g + 1) * S] - off[g * S];
+      load_floats<VPL>(a.L.cl_vbar + cg * D + lane * VPL, vb[k]);
+#pragma unroll
+      for (int h = 0; h < G; ++h) sc[k][h] = a.ws.cl_score[cg * G + h];
+    }
+#pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int g = y * 16 + wave * 4 + k;
       if (g >= C) break;
-      const int64_t cg = U.cl_base + g;
-      const uint32_t mask = a.ws.cl_mask[cg];
-      if (mask == 0u && lane == 0) a.ws.cl_rows[cg] = 0;
-      const int n_g = off[(g + 1) * S] - off[g * S];
-      const uint32_t unchosen = n_g > 0 ? (all & ~mask) : 0u;
+      if (mask[k] == 0u && lane == 0) a.ws.cl_rows[U.cl_base + g] = 0;
+      const uint32_t unchosen = n_g[k] > 0 ? (all & ~mask[k]) : 0u;
       if (unchosen && a.residual) {
-        float vb[VPL];
-        load_floats<VPL>(a.L.cl_vbar + cg * D + lane * VPL, vb);
 #pragma unroll
         for (int h = 0; h < G; ++h)
-          if ((unchosen >> h) & 1u) add_group<VPL>(rm[h], rl[h], ro[h], a.ws.cl_score[cg * G + h], vb);
+          if ((unchosen >> h) & 1u) add_group<VPL>(rm[h], rl[h], ro[h], sc[k][h], vb[k]);
       }
     }
   }
@@ -538,60 +549,54 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
 //    into its record.  Grid (splits, units).
 // ---------------------------------------------------------------------------
 // ---------------------------------------------------------------------------
-// 4a. Balanced assignment of the exact blocks: unit u reads T_u = anchors +
-//     rows of its chosen subclusters; each unit gets one block plus a share
-//     of the other `splits` blocks in proportion to T_u, written as a table
-//     block -> (unit, split, splits of the unit, first block of the unit);
-//     blocks left over exit at once.  One block of 1024 threads.
+// 4a. Shares of the exact blocks.  Unit u reads T_u = anchors + rows of its
+//     chosen subclusters exactly; it gets 1 + floor(T_u * extra / total)
+//     blocks, extra = min(nblk - n_units, ceil(total / 256)) (so the shares
+//     sum to at most nblk and no block gets much under 256 rows), numbered
+//     unit by unit.  Every exact block and every merge block recomputes the
+//     shares from the per-unit row counts (a few KB): no table, no launch.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k_assign_blocks(DArgs a, int n_units, int nblk) {
-  __shared__ int sh[16];
-  __shared__ long long tot_sh;
+struct BlockShare {
+  int u;      // unit (-1: the block has no work)
+  int first;  // first block of the unit
+  int n;      // blocks of the unit
+};
+
+// want_block >= 0: the share holding that block; else the share of unit
+// want_unit.  All NT threads call it; the result is uniform.
+template <int NT>
+__device__ BlockShare find_share(const int32_t* unit_rows, int n_units, int nblk, int A, int want_block,
+                                 int want_unit) {
+  __shared__ long long tsum[NT / 64];
+  __shared__ int sh[NT / 64];
+  __shared__ BlockShare res;
   const int tid = threadIdx.x;
-  const int A = a.n_sink + a.n_recent;
   long long part = 0;
-  for (int u = tid; u < n_units; u += 1024) part += (long long)A + a.ws.unit_rows[u];
+  for (int v = tid; v < n_units; v += NT) part += (long long)A + unit_rows[v];
+#pragma unroll
   for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
-  __shared__ long long wsum[16];
-  if ((tid & 63) == 0) wsum[tid >> 6] = part;
+  if ((tid & 63) == 0) tsum[tid >> 6] = part;
+  if (tid == 0) res = BlockShare{-1, 0, 0};
   __syncthreads();
-  if (tid == 0) {
-    long long t = 0;
-    for (int w = 0; w < 16; ++w) t += wsum[w];
-    tot_sh = t;
-  }
-  __syncthreads();
-  const long long total = tot_sh;
-  // every unit gets one block plus its share of the other nblk - n_units
-  // blocks, floor(T_u * extra / total): the shares sum to at most nblk;
-  // fewer extra blocks when there are under ~256 rows for each
+  long long total = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) total += tsum[w];
   long long extra = nblk - n_units;
   const long long by_rows = (total + 255) / 256;
   if (by_rows < extra) extra = by_rows;
   int carry = 0;
-  for (int base = 0; base < n_units; base += 1024) {
-    const int u = base + tid;
+  for (int base = 0; base < n_units; base += NT) {
+    const int v = base + tid;
     int sp = 0;
-    if (u < n_units) {
-      const long long T = (long long)A + a.ws.unit_rows[u];
-      sp = 1 + (int)(total > 0 ? T * extra / total : 0);
-    }
+    if (v < n_units) sp = 1 + (int)(total > 0 ? ((long long)A + unit_rows[v]) * extra / total : 0);
     int tot;
-    const int first = carry + block_excl_scan<1024>(sp, sh, tot);
-    if (u < n_units) {
-      a.ws.uinfo[2 * u] = first;
-      a.ws.uinfo[2 * u + 1] = sp;
-      for (int p = 0; p < sp && first + p < nblk; ++p) {
-        int32_t* e = a.ws.btab + 4 * (first + p);
-        e[0] = u;
-        e[1] = p;
-        e[2] = sp;
-        e[3] = first;
-      }
-    }
+    const int first = carry + block_excl_scan<NT>(sp, sh, tot);
+    if (v < n_units && (v == want_unit || (want_block >= first && want_block < first + sp)))
+      res = BlockShare{v, first, sp};
     carry += tot;
   }
-  for (int b = carry + tid; b < nblk; b += 1024) a.ws.btab[4 * b] = -1;
+  __syncthreads();
+  return BlockShare{uni(res.u), uni(res.first), uni(res.n)};
 }
 
 // A tile of at most 32 contiguous layout rows: element offset of its first
@@ -762,13 +767,17 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
   __shared__ TileRec tiles[4][kTileBatch];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int32_t* be = a.ws.btab + 4 * blockIdx.x;
-  const int u = uni(be[0]);
+  const int A = a.n_sink + a.n_recent;
+  const BlockShare bs = find_share<256>(a.ws.unit_rows, a.n_units, a.nblk, A, blockIdx.x, -1);
+  const int u = bs.u;
   if (u < 0) return;
-  const int p = uni(be[1]), splits_u = uni(be[2]);
+  const int p = blockIdx.x - bs.first, splits_u = bs.n;
+  if (p == 0 && tid == 0) {
+    a.ws.uinfo[2 * u] = bs.first;
+    a.ws.uinfo[2 * u + 1] = bs.n;
+  }
   const mog_unit U = uni_unit(a.L.units + u);
   const int C = U.C, S = U.S;
-  const int A = a.n_sink + a.n_recent;
   // query first: its loads overlap the cluster-row scan below
   u32x4* buf = kvbuf[wave];
   Engine acc;
@@ -893,10 +902,11 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
 
 // ---------------------------------------------------------------------------
 // 5. Merge: per query head, the exact records of its unit (n_part per unit,
-//    or the range uinfo[u]) and the n_res residual records of the unit: one
-//    max, one weighted sum, one normalisation.  Grid (Hq, n_seq), 1024
-//    threads: (D/4)-lane groups each take every NG-th record with 16-byte
-//    loads, so all records of a head are in flight at about once.
+//    or the range uinfo[u] the exact pass wrote) and the n_res residual
+//    records of the unit, merged with one normalisation.  Grid (Hq, n_seq),
+//    1024 threads: (D/4)-lane groups each fold every NG-th record into a
+//    running (m, l, o) with 16-byte loads (one pass over the records), then
+//    the groups are combined under their common maximum.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(1024) void k_merge(const float* part, int n_part, const int32_t* uinfo,
@@ -904,10 +914,9 @@ __global__ __launch_bounds__(1024) void k_merge(const float* part, int n_part, c
                                                 float* lse) {
   constexpr int RS = D + kPartPad;
   constexpr int QL = D / 4;        // lanes per record (4 elements each)
-  constexpr int NG = 1024 / QL;    // records processed side by side
-  __shared__ float sh[32];
+  constexpr int NG = 1024 / QL;    // records folded side by side
   __shared__ float4 acc[NG][QL];
-  __shared__ float dsum[NG];
+  __shared__ float gm[NG], gl[NG];
   const int hq = blockIdx.x, seq = blockIdx.y, tid = threadIdx.x;
   const int kvh = hq / G, h = hq % G;
   const int u = seq * Hkv + kvh;
@@ -920,37 +929,43 @@ __global__ __launch_bounds__(1024) void k_merge(const float* part, int n_part, c
   const float* eb = part + (first * G + h) * RS;
   const float* rb = res ? res + ((int64_t)u * n_res * G + h) * RS : nullptr;
   const int total = n_part + (res ? n_res : 0);
-  auto rec = [&](int i) { return i < n_part ? eb + i * stride : rb + (int64_t)(i - n_part) * stride; };
-  float M = -INFINITY;
-  for (int i = tid; i < total; i += 1024) M = fmaxf(M, rec(i)[D]);
-  M = block_max<1024>(M, sh);
   const int q = tid % QL, grp = tid / QL;
-  float4 num = {0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
+  float m = -INFINITY, l = 0.f;
+  float4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
   for (int i = grp; i < total; i += NG) {
-    const float* r = rec(i);
-    const float f = exp2_or_zero(r[D], M);
-    const float4 o = reinterpret_cast<const float4*>(r)[q];
-    num.x += f * o.x;
-    num.y += f * o.y;
-    num.z += f * o.z;
-    num.w += f * o.w;
-    den += f * r[D + 1];
+    const float* r = i < n_part ? eb + i * stride : rb + (int64_t)(i - n_part) * stride;
+    const float mi = r[D], li = r[D + 1];
+    const float4 oi = reinterpret_cast<const float4*>(r)[q];
+    // branch-free, so the unrolled iterations' loads are all in flight
+    const float mn = fmaxf(m, mi);
+    const float fa = exp2_or_zero(m, mn), fb = exp2_or_zero(mi, mn);
+    l = l * fa + li * fb;
+    o.x = o.x * fa + oi.x * fb;
+    o.y = o.y * fa + oi.y * fb;
+    o.z = o.z * fa + oi.z * fb;
+    o.w = o.w * fa + oi.w * fb;
+    m = mn;
   }
-  acc[grp][q] = num;
-  if (q == 0) dsum[grp] = den;
+  acc[grp][q] = o;
+  if (q == 0) {
+    gm[grp] = m;
+    gl[grp] = l;
+  }
   __syncthreads();
   if (tid < QL) {
+    float M = -INFINITY;
+    for (int k = 0; k < NG; ++k) M = fmaxf(M, gm[k]);
     float4 t = {0.f, 0.f, 0.f, 0.f};
     float dn = 0.f;
     for (int k = 0; k < NG; ++k) {
-      const float4 a = acc[k][tid];
-      t.x += a.x;
-      t.y += a.y;
-      t.z += a.z;
-      t.w += a.w;
-      dn += dsum[k];
+      const float f = exp2_or_zero(gm[k], M);
+      const float4 a4 = acc[k][tid];
+      t.x += f * a4.x;
+      t.y += f * a4.y;
+      t.z += f * a4.z;
+      t.w += f * a4.w;
+      dn += f * gl[k];
     }
     const int64_t orow = (int64_t)seq * Hq + hq;
     const float inv = dn > 0.f ? 1.f / dn : 0.f;
@@ -1062,9 +1077,8 @@ template <int D, int G>
 static hipError_t decode_impl(const DecodeLaunch& x, const DArgs& a, const BudgetArgs& b, hipStream_t s) {
   const int nu = x.L.n_units;
   hipLaunchKernelGGL((k_score_clusters<D, G>), dim3((x.L.max_C + 15) / 16, nu), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(k_select_topc, dim3(G, nu), dim3(256), 0, s, a, b, G);
+  hipLaunchKernelGGL(k_select_topc<G>, dim3(nu), dim3(64 * G), 0, s, a, b);
   hipLaunchKernelGGL((k_subclusters<D, G>), dim3(x.nb_res, nu), dim3(256), 0, s, a, b, x.nb_chosen);
-  hipLaunchKernelGGL(k_assign_blocks, dim3(1), dim3(1024), 0, s, a, nu, x.nblk);
   if (x.ev_begin) {
     const hipError_t e = hipEventRecord(x.ev_begin, s);
     if (e != hipSuccess) return e;
@@ -1124,6 +1138,8 @@ hipError_t launch_decode(const DecodeLaunch& x, hipStream_t s) {
   a.residual = x.residual;
   a.splits = x.splits;
   a.nb_res = x.nb_res;
+  a.n_units = x.L.n_units;
+  a.nblk = x.nblk;
   a.scale_l2 = x.scale * kLog2e;
   a.half_s2_l2 = 0.5f * x.scale * x.scale * kLog2e;
   a.L_head_dim = x.D;

@@ -94,8 +94,9 @@ struct DecodeWS {
   int32_t* cl_rows;     // [total_cl]         rows of the cluster read exactly (any head)
   uint32_t* sub_mask;   // [total_sub]        heads that chose the subcluster
   int32_t* unit_rows;   // [n_units]          rows of chosen subclusters per unit
-  int32_t* btab;        // [nblk][4]          exact block -> unit, split, splits, first block
-  int32_t* uinfo;       // [n_units][2]       first exact block, splits
+  int32_t* cl_list;     // [total_cl]         per unit (at cl_base): chosen clusters, ascending
+  int32_t* n_chosen;    // [n_units]          length of the unit's list
+  int32_t* uinfo;       // [n_units][2]       first exact block of the unit, its blocks
   float* res_part;      // [n_units][nb_res][G][D+4] residual partials
   float* ex_part;       // [nblk][G][D+4]     exact-attention block records
 };
