@@ -268,6 +268,26 @@ def cpu_baseline(state, budget_s):
                        f"scaled to one step; host cores available {len(os.sched_getaffinity(0))}")
 
 
+def copy_calibration(n_bytes=1 << 30, reps=10):
+    """A plain copy of known size: each dispatch reads and writes n_bytes."""
+    import torch
+
+    a = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"copy_bytes_read": n_bytes, "copy_bytes_written": n_bytes, "ms": ms,
+                      "GBps_read_plus_write": 2 * n_bytes / (ms * 1e-3) / 1e9}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -277,6 +297,9 @@ def main():
     ap.add_argument("--no-128k", action="store_true", help="skip the N=128K workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 10 times (the reference kernel that "
+                         "scales rocprofv3 FETCH_SIZE/WRITE_SIZE to bytes) and print its rate")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -287,6 +310,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calib:
+        copy_calibration()
+        return
     from long_context_sparse_mog_amd import capi
 
     capi.lib()  # fail loudly when the HIP library is missing

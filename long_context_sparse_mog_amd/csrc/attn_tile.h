@@ -40,6 +40,30 @@ __device__ inline float row16_sum(float x) {
   return x;
 }
 
+// Sum over the wave, returned as a wave-uniform value: row sums by DPP, then
+// the row broadcasts 15 and 31 carry rows 0..2 into row 3, and lane 63's
+// total is read out.  No LDS traffic, unlike a shuffle-based reduction.
+__device__ inline float wave_sum_uniform(float x) {
+  x = row16_sum(x);
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xA, 0xF, false));  // row_bcast:15
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
+// Reduction of a 32-bit value over the wave with an associative op,
+// returned wave-uniform (same DPP pattern as wave_sum_uniform; `identity`
+// fills the rows the broadcasts leave out).
+template <typename Op>
+__device__ inline uint32_t wave_reduce_uniform(uint32_t x, Op op, uint32_t identity) {
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)x, 0x142, 0xA, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)x, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
 __device__ inline float wave_sum_dpp(float x) {
   x = row16_sum(x);
   x += __shfl_xor(x, 16, 64);

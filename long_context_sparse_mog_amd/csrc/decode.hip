@@ -159,7 +159,7 @@ __device__ inline void score_rows(const float (&x)[R][D / 32], const float (&coe
       float t = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) t += coef[h][e] * x[r][e];
-      t = wave_sum_dpp(t);
+      t = wave_sum_uniform(t);
       if (lane == r) mine[h] = t;
     }
   }
@@ -174,7 +174,7 @@ template <int D, int G>
 __global__ __launch_bounds__(256) void k_score_clusters(DArgs a) {
   constexpr int EPL = D / 32;
   const int u = blockIdx.y;
-  const mog_unit U = a.L.units[u];
+  const mog_unit U = uni_unit(a.L.units + u);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g0 = blockIdx.x * 16 + wave * 4;
   if (g0 >= U.C) return;
@@ -225,6 +225,7 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
   __shared__ uint32_t umask[kMaxC];
   __shared__ int sh[16];
   const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63, h = tid >> 6;
+  const int want_raw = b.top_c[u / a.Hkv];  // issued with the unit record
   const mog_unit U = uni_unit(a.L.units + u);
   const int C = U.C;
   for (int i = tid; i < C; i += NT) umask[i] = 0u;
@@ -242,28 +243,56 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
     nvalid += in;
   }
   nvalid = wave_sum_i(nvalid);  // once; the per-bit counts below use ballots
-  int want = b.top_c[U.seq];
-  want = want < 0 ? 0 : want;
+  const int want = want_raw < 0 ? 0 : want_raw;
   const int c_eff = want < nvalid ? want : nvalid;
-  int kk = c_eff;
-  uint32_t prefix = 0u;
+  // Radix select, most significant bit first.  hi_mask holds the decided
+  // bits and prefix their values; cand counts the keys that match the
+  // prefix on them, kk how many of those are still to be taken.  Bits that
+  // every valid key shares are decided without a count, and the search
+  // stops as soon as all remaining candidates are needed (cand == kk).
+  int kk = c_eff, cand = nvalid;
+  uint32_t prefix = 0u, hi_mask = 0u;
   if (kk > 0) {
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t hi_mask = ~0u << bit, target = prefix | (1u << bit);
+    uint32_t kor = 0u, kand = ~0u;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      kor |= key[j];
+      kand &= key[j] != 0u ? key[j] : ~0u;
+    }
+    kor = wave_reduce_uniform(kor, [](uint32_t x, uint32_t y) { return x | y; }, 0u);
+    kand = wave_reduce_uniform(kand, [](uint32_t x, uint32_t y) { return x & y; }, ~0u);
+    const uint32_t varying = kor ^ kand;
+    for (int bit = 31; bit >= 0 && cand > kk; --bit) {
+      const uint32_t m = 1u << bit;
+      hi_mask |= m;
+      if (!(varying & m)) {
+        prefix |= kand & m;
+        continue;
+      }
+      const uint32_t target = prefix | m;
       // slots past C hold key 0, which never matches a nonzero target; the
       // groups of 8 slots past C are skipped with one uniform branch each
+      // per-lane count without compares: (x == 0) as 1 - min(x, 1), so the
+      // slots do not serialise on the condition register; one wave sum
       int cnt = 0;
 #pragma unroll
       for (int jg = 0; jg < KPL / 8; ++jg) {
         if (512 * jg >= C) break;
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) cnt += __popcll(__ballot((key[8 * jg + jj] & hi_mask) == target));
+        for (int jj = 0; jj < 8; ++jj) cnt += 1 - (int)min((key[8 * jg + jj] & hi_mask) ^ target, 1u);
       }
-      if (cnt >= kk) prefix = target;
-      else kk -= cnt;
+      cnt = (int)wave_reduce_uniform((uint32_t)cnt, [](uint32_t x, uint32_t y) { return x + y; }, 0u);
+      if (cnt >= kk) {
+        prefix = target;
+        cand = cnt;
+      } else {
+        kk -= cnt;
+        cand -= cnt;
+      }
     }
   }
-  // chosen: key > prefix, or key == prefix among the first kk ties (by index)
+  // chosen: keys above the prefix on the decided bits, then the first kk
+  // (by index) of the keys that match it there
   const int hq = U.kv_head * G + h;
   const int64_t row = (int64_t)U.seq * a.Hq + hq;
   const unsigned long long below = (1ull << lane) - 1ull;
@@ -273,15 +302,16 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
   for (int j = 0; j < KPL; ++j) {
     if (64 * j >= C) break;
     const int i = 64 * j + lane;
-    const bool tie = c_eff > 0 && key[j] == prefix && key[j] != 0u;
+    const uint32_t kd = key[j] & hi_mask;
+    const bool tie = c_eff > 0 && kd == prefix && key[j] != 0u;
     const unsigned long long tb = __ballot(tie);
-    const bool sel = c_eff > 0 && key[j] != 0u && (key[j] > prefix || (tie && ties + __popcll(tb & below) < kk));
+    const bool sel = c_eff > 0 && key[j] != 0u && (kd > prefix || (tie && ties + __popcll(tb & below) < kk));
     ties += __popcll(tb);
     const unsigned long long sb = __ballot(sel);
     const int rank = sel ? rank0 + __popcll(sb & below) : -1;
     rank0 += __popcll(sb);
     if (i < C) {
-      a.ws.cl_rank[(U.cl_base + i) * G + h] = rank;
+      if (a.sel_s) a.ws.cl_rank[(U.cl_base + i) * G + h] = rank;  // read back only for sel_s
       if (sel) {
         atomicOr(&umask[i], 1u << h);
         if (a.sel_c) a.sel_c[row * a.c_stride + rank] = i;
@@ -295,19 +325,43 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
     for (int j = c_eff * a.s_stride + lane; j < a.c_stride * a.s_stride; j += 64) a.sel_s[base + j] = -1;
   }
   __syncthreads();
-  // head masks and the ascending list of chosen clusters (thread t covers
-  // clusters [t E, t E + E))
+  // head masks, the ascending list of chosen clusters, and for each chosen
+  // cluster the base of its tile slots: a prefix of ceil(rows/32) + S, the
+  // most tiles its chosen subclusters can make (thread t covers clusters
+  // [t E, t E + E); E <= EMAX)
+  constexpr int EMAX = (kMaxC + NT - 1) / NT;
   const int E = (C + NT - 1) / NT;
   const int lo = tid * E, hi = min(C, lo + E);
-  int cnt = 0;
-  for (int i = lo; i < hi; ++i) {
-    a.ws.cl_mask[U.cl_base + i] = umask[i];
-    cnt += umask[i] != 0u;
+  const int32_t* off = a.L.sub_off + U.off_base;
+  int bound[EMAX];
+#pragma unroll
+  for (int k = 0; k < EMAX; ++k) {
+    const int i = min(lo + k, C - 1);
+    bound[k] = (off[(i + 1) * U.S] - off[i * U.S] + 31) / 32 + U.S;
   }
-  int total;
+  int cnt = 0, ub = 0;
+#pragma unroll
+  for (int k = 0; k < EMAX; ++k) {
+    const int i = lo + k;
+    if (i < hi) {
+      a.ws.cl_mask[U.cl_base + i] = umask[i];
+      cnt += umask[i] != 0u;
+      ub += umask[i] != 0u ? bound[k] : 0;
+    }
+  }
+  int total, ub_total;
   int pos = block_excl_scan<NT>(cnt, sh, total);
-  for (int i = lo; i < hi; ++i)
-    if (umask[i] != 0u) a.ws.cl_list[U.cl_base + pos++] = i;
+  int tb = block_excl_scan<NT>(ub, sh, ub_total);
+#pragma unroll
+  for (int k = 0; k < EMAX; ++k) {
+    const int i = lo + k;
+    if (i < hi && umask[i] != 0u) {
+      a.ws.cl_list[U.cl_base + pos] = i;
+      a.ws.ch_tbase[U.cl_base + pos] = tb;
+      ++pos;
+      tb += bound[k];
+    }
+  }
   if (tid == 0) a.ws.n_chosen[u] = total;
 }
 
@@ -317,11 +371,12 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
 //      the ascending list the top-c pass wrote), if any: scores its S
 //      subclusters for every head (one batch of row loads per wave), picks
 //      the top-s of each head that chose the cluster, writes the subcluster
-//      head masks and the cluster's exactly-read row count, and accumulates
-//      the residual terms of the subclusters a choosing head left out;
+//      head masks, adds the rows read exactly to the unit's count, writes
+//      the cluster's exact tiles (runs of chosen subclusters cut into tiles
+//      of <= 32 rows) from its slot base, and accumulates the residual
+//      terms of the subclusters a choosing head left out;
 //    * block nb_chosen + y covers clusters [16y, 16y+16) (4 per wave): the
-//      residual terms of every head that left a cluster out, and a zero row
-//      count for clusters no head chose.
+//      residual terms of every head that left a cluster out.
 //    Every block writes one residual record per head (slot = block index).
 // ---------------------------------------------------------------------------
 template <int D, int G>
@@ -354,14 +409,17 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
   constexpr int VPL = D / 64;
   constexpr int RS = D + kPartPad;
   constexpr int RPW = kMaxS / 4;   // subcluster rows per wave
+  static_assert(kMaxS * G <= 256, "one thread per (subcluster, head) score");
   __shared__ float st[4][G][D + 2];
   __shared__ float lds_sc[kMaxS][G];
   __shared__ uint32_t lds_sm[kMaxS];
   __shared__ int lds_cnt[kMaxS];
+  __shared__ int lds_off[kMaxS + 1];
   __shared__ int sh[16];
   const int u = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const mog_unit U = a.L.units[u];
+  const int s_keep_raw = b.top_s[u / a.Hkv];  // issued with the unit record
+  const mog_unit U = uni_unit(a.L.units + u);
   const int S = U.S, C = U.C;
   const uint32_t all = (1u << G) - 1u;
   const int32_t* off = a.L.sub_off + U.off_base;
@@ -378,7 +436,8 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
   if ((int)blockIdx.x < nb_chosen) {
     // -------- the x-th chosen cluster ---------------------------------------
     const int x = blockIdx.x;
-    const int n_ch = a.ws.n_chosen[u], g_x = a.ws.cl_list[U.cl_base + x];  // x < nb_chosen <= C
+    // x < nb_chosen <= C, so the list entries are in range either way
+    const int n_ch = a.ws.n_chosen[u], g_x = a.ws.cl_list[U.cl_base + x], tb_x = a.ws.ch_tbase[U.cl_base + x];
     const int g = x < uni(n_ch) ? uni(g_x) : -1;
     if (g >= 0) {
       const int64_t cg = U.cl_base + g;
@@ -401,8 +460,12 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
       // per head, issued with the loads above
       {
         const int i = min(tid, S - 1);
-        const int c = off[g * S + i + 1] - off[g * S + i];
-        if (tid < S) lds_cnt[tid] = c;
+        const int o0 = off[g * S + i], o1 = off[g * S + i + 1];
+        if (tid < S) {
+          lds_cnt[tid] = o1 - o0;
+          lds_off[tid] = o0;
+        }
+        if (tid == S - 1) lds_off[S] = o1;
       }
       int rc[G];
       if (a.sel_s) {
@@ -418,36 +481,39 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
           float t = 0.f;
 #pragma unroll
           for (int e = 0; e < EPL; ++e) t += coef[h][e] * xr[k][e];
-          t = wave_sum_dpp(t);
+          t = wave_sum_uniform(t);
           if (lane == 0) lds_sc[i][h] = t;
         }
       }
       if (tid < kMaxS) lds_sm[tid] = 0u;
       __syncthreads();
       // full scores (count term added; -inf for an empty subcluster)
-      if (tid < S * G) {
+      // (rows past S are set to -inf too, so the rank loop below runs over
+      // all kMaxS rows without a branch)
+      if (tid < kMaxS * G) {
         const int i = tid / G, h = tid % G;
-        const int cnt = lds_cnt[i];
+        const int cnt = i < S ? lds_cnt[i] : 0;
         lds_sc[i][h] = cnt > 0 ? lds_sc[i][h] + log2f((float)cnt) : -INFINITY;
       }
       __syncthreads();
       // top-s of each choosing head: wave w handles heads w, w+4
       const int my_cnt = lane < S ? lds_cnt[lane] : 0;
       const bool valid = lane < S && my_cnt > 0;
-      int s_keep = b.top_s[U.seq];
-      s_keep = s_keep < 0 ? 0 : s_keep;
+      const int s_keep = s_keep_raw < 0 ? 0 : s_keep_raw;
 #pragma unroll
       for (int h0 = 0; h0 < G; h0 += 4) {
         const int h = h0 + wave;
         if (h >= G || !((mask >> h) & 1u)) continue;
         const float my = valid ? lds_sc[lane][h] : -INFINITY;
+        // all scores first, then a branch-free count (bitwise, not
+        // short-circuit, operators)
+        float osc[kMaxS];
+#pragma unroll
+        for (int j = 0; j < kMaxS; ++j) osc[j] = lds_sc[j][h];
         int rank = 0;
 #pragma unroll
-        for (int j = 0; j < kMaxS; ++j) {
-          if (j >= S) break;
-          const float o = lds_sc[j][h];
-          if (o != -INFINITY && (o > my || (o == my && j < lane))) ++rank;
-        }
+        for (int j = 0; j < kMaxS; ++j)
+          rank += (int)((osc[j] != -INFINITY) & ((osc[j] > my) | ((osc[j] == my) & (j < lane))));
         const bool sel = valid && rank < s_keep;
         if (sel) atomicOr(&lds_sm[lane], 1u << h);
         if (a.sel_s) {
@@ -467,10 +533,42 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
         int rows = (lane < S && lds_sm[lane]) ? my_cnt : 0;
 #pragma unroll
         for (int o2 = 1; o2 < 64; o2 <<= 1) rows += __shfl_xor(rows, o2, 64);
-        if (lane == 0) {
-          a.ws.cl_rows[cg] = rows;
-          atomicAdd(&a.ws.unit_rows[u], rows);
+        if (lane == 0) atomicAdd(&a.ws.unit_rows[u], rows);
+        // exact tiles of the cluster: a run is a maximal sequence of chosen
+        // nonempty subclusters with one head mask whose rows are contiguous
+        // (lane i: subcluster i); each run is cut into tiles of <= 32 rows,
+        // written run after run from the cluster's slot base
+        const int st = lane < S ? lds_off[lane] : 0;
+        const int en = lane < S ? lds_off[lane] + lds_cnt[lane] : 0;
+        const uint32_t m = lane < S ? lds_sm[lane] : 0u;
+        const bool live = m != 0u && en > st;
+        const unsigned long long below = (1ull << lane) - 1ull;
+        const unsigned long long lb = __ballot(live);
+        const unsigned long long lbb = lb & below;
+        const int prv = lbb ? 63 - __clzll((long long)lbb) : 0;
+        const uint32_t m_prv = (uint32_t)__shfl((int)m, prv, 64);
+        const int en_prv = __shfl(en, prv, 64);
+        const bool head = live && !(lbb != 0ull && m_prv == m && en_prv == st);
+        const unsigned long long hb = __ballot(head);
+        const unsigned long long later = hb & ~(below | (1ull << lane));
+        const int nxt = later ? __ffsll((long long)later) - 1 : 64;
+        const unsigned long long in_run = lb & (nxt >= 64 ? ~0ull : ((1ull << nxt) - 1ull));
+        const int last = in_run ? 63 - __clzll((long long)in_run) : 0;
+        const int run_en = __shfl(en, last, 64);
+        const int ntl = head ? (run_en - st + 31) / 32 : 0;
+        int incl = ntl;
+#pragma unroll
+        for (int o2 = 1; o2 < 64; o2 <<= 1) {
+          const int y = __shfl_up(incl, o2, 64);
+          if (lane >= o2) incl += y;
         }
+        const int n_tiles = __shfl(incl, 63, 64);
+        if (head) {
+          TileRec* dstt = a.ws.tiles + tile_unit_base(U.row_base, U.cl_base, u) + tb_x + (incl - ntl);
+          for (int r = st; r < run_en; r += 32, ++dstt)
+            *dstt = TileRec{(U.row_base + r) * (int64_t)a.L_head_dim, min(32, run_en - r), m};
+        }
+        if (lane == 0) a.ws.ch_ntiles[U.cl_base + x] = n_tiles;
       }
       // residual of the subclusters a choosing head left out: wave w takes
       // subclusters w, w+4, ...
@@ -514,7 +612,6 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
     for (int k = 0; k < 4; ++k) {
       const int g = y * 16 + wave * 4 + k;
       if (g >= C) break;
-      if (mask[k] == 0u && lane == 0) a.ws.cl_rows[U.cl_base + g] = 0;
       const uint32_t unchosen = n_g[k] > 0 ? (all & ~mask[k]) : 0u;
       if (unchosen && a.residual) {
 #pragma unroll
@@ -538,15 +635,12 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
 }
 
 // ---------------------------------------------------------------------------
-// 4. Exact split-K pass.  The rows a unit reads exactly are laid out
-//    virtually as [sink anchors | recent anchors | rows of every cluster's
-//    chosen subclusters, clusters in order]; wave w of the unit covers
-//    virtual rows [w*T/NW, (w+1)*T/NW).  Every block first scans the
-//    per-cluster row counts into LDS, then each wave locates its first
-//    cluster by binary search and walks the chosen subclusters (adjacent
-//    subclusters chosen by the same heads form one contiguous run).  The
-//    block also folds the residual partials p, p+splits, ... of its unit
-//    into its record.  Grid (splits, units).
+// 4. Exact split-K pass.  The tiles a unit reads exactly are numbered
+//    [sink anchor tiles | recent anchor tiles | tiles of the chosen clusters
+//    in list order]; wave w of the unit takes [w*NT/NW, (w+1)*NT/NW).  Every
+//    block scans the chosen clusters' tile counts into LDS; a wave lists its
+//    tiles (one per lane: binary search, then the 16-byte tile record) in
+//    LDS and streams them.  Grid: the exact blocks of every unit.
 // ---------------------------------------------------------------------------
 // ---------------------------------------------------------------------------
 // 4a. Shares of the exact blocks.  Unit u reads T_u = anchors + rows of its
@@ -608,161 +702,20 @@ struct TileDesc {
   int src;  // 0: layout rows (k_mid / v_mid), 1: KV cache rows (anchors)
 };
 
-// A listed tile in LDS (16 bytes): offset, row count | src << 31, head mask.
-struct TileRec {
-  int64_t off;
-  int nrows_src;
-  uint32_t mask;
-};
 constexpr int kTileBatch = 64;  // tiles listed per wave before streaming them
-
-// Walks the chosen subclusters of a unit over a range [y, y1) of its
-// virtual cluster rows (vpre: exclusive prefix of the per-cluster counts,
-// in LDS), yielding 32-row tiles.  Adjacent subclusters chosen by the same
-// heads form one run.  Per-lane state holds the current cluster's S
-// subclusters (lane i: subcluster i); everything else is wave-uniform.
-struct RunCursor {
-  // anchor token segments of a contiguous cache (sinks, then recent); plain
-  // scalars so the cursor stays in registers
-  int64_t anc_pos0, anc_end0, anc_pos1, anc_end1;
-  int64_t anc_base;                // element offset of token 0 of the unit
-  int64_t y, y1;
-  int g, C, S, skip;
-  int64_t row_base;
-  const int* vpre;
-  unsigned long long chosen;
-  uint32_t my_m;
-  int my_st, my_en;
-  int run_pos, run_end;  // current run [run_pos, run_end) in unit rows
-  uint32_t run_mask;
-  int D;
-
-  __device__ void load_cluster(const DArgs& a, const mog_unit& U, int lane) {
-    const int64_t sg0 = U.sub_base + (int64_t)g * S;
-    const int32_t* off = a.L.sub_off + U.off_base + g * S;
-    my_m = 0u;
-    my_st = my_en = 0;
-    if (lane < S) {
-      my_m = a.ws.sub_mask[sg0 + lane];
-      my_st = off[lane];
-      my_en = off[lane + 1];
-    }
-    chosen = __ballot(my_m != 0u && my_en > my_st);
-  }
-
-  __device__ void begin(const DArgs& a, const mog_unit& U, const int* vp, int64_t y0, int64_t yend, int lane) {
-    anc_pos0 = anc_end0 = anc_pos1 = anc_end1 = 0;
-    anc_base = 0;
-    y = y0;
-    y1 = yend;
-    C = U.C;
-    S = U.S;
-    vpre = vp;
-    row_base = U.row_base;
-    D = 0;
-    run_pos = run_end = 0;
-    run_mask = 0u;
-    g = cluster_of(y);
-    skip = g < C ? (int)(y - vpre[g]) : 0;
-    if (g < C) load_cluster(a, U, lane);
-    else chosen = 0ull;
-  }
-
-  // the cluster holding virtual row yy (the last g with vpre[g] <= yy; it has
-  // rows since vpre[g+1] > yy), or C when yy is past the end
-  __device__ int cluster_of(int64_t yy) const {
-    if (yy >= vpre[C]) return C;
-    int lo = 0, hi = C;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (vpre[mid] <= yy) lo = mid; else hi = mid;
-    }
-    return lo;
-  }
-
-  // next run of the current range, or false when the range is done
-  __device__ bool next_run(const DArgs& a, const mog_unit& U, int lane) {
-    while (y < y1) {
-      while (!chosen) {
-        // all of cluster g consumed: the next row lives in cluster_of(y)
-        g = cluster_of(y);
-        if (g >= C) return false;
-        skip = (int)(y - vpre[g]);
-        load_cluster(a, U, lane);
-      }
-      const int i = __ffsll((long long)chosen) - 1;
-      const uint32_t m = (uint32_t)__shfl((int)my_m, i, 64);
-      const int st0 = __shfl(my_st, i, 64);
-      int en = __shfl(my_en, i, 64);
-      chosen &= chosen - 1ull;
-      while (chosen) {
-        const int j = __ffsll((long long)chosen) - 1;
-        if ((uint32_t)__shfl((int)my_m, j, 64) != m || __shfl(my_st, j, 64) != en) break;
-        en = __shfl(my_en, j, 64);
-        chosen &= chosen - 1ull;
-      }
-      const int len = en - st0;
-      if (skip >= len) {
-        skip -= len;
-        continue;
-      }
-      const int take = (int)((int64_t)(len - skip) < y1 - y ? (len - skip) : (y1 - y));
-      run_pos = st0 + skip;
-      run_end = run_pos + take;
-      run_mask = m;
-      y += take;
-      skip = 0;
-      return true;
-    }
-    return false;
-  }
-
-  // anchor part of the range: virtual rows [x0, x1) of [0, n_sink + n_recent)
-  __device__ void set_anchors(const DArgs& a, const mog_unit& U, int64_t x0, int64_t x1) {
-    const int64_t ns = a.n_sink;
-    anc_pos0 = x0;
-    anc_end0 = x1 < ns ? x1 : ns;
-    const int64_t r0 = x0 > ns ? x0 : ns;
-    anc_pos1 = U.N - a.n_recent + (r0 - ns);
-    anc_end1 = U.N - a.n_recent + (x1 - ns);
-    anc_base = kv_row_offset(a.kv, U.seq, U.kv_head, 0, a.L_head_dim);
-  }
-
-  __device__ TileDesc next(const DArgs& a, const mog_unit& U, int lane) {
-    TileDesc t;
-    t.nrows = 0;
-    t.off = 0;
-    t.mask = 0u;
-    t.src = 0;
-    if (anc_pos0 < anc_end0 || anc_pos1 < anc_end1) {
-      const bool first = anc_pos0 < anc_end0;
-      const int64_t pos = first ? anc_pos0 : anc_pos1;
-      const int64_t end = first ? anc_end0 : anc_end1;
-      const int n = end - pos < 32 ? (int)(end - pos) : 32;
-      t.off = anc_base + pos * a.L_head_dim;
-      t.nrows = n;
-      t.mask = 0xffffffffu;
-      t.src = 1;
-      if (first) anc_pos0 += n; else anc_pos1 += n;
-      return t;
-    }
-    if (y >= y1 && run_pos >= run_end) return t;
-    if (run_pos >= run_end && !next_run(a, U, lane)) return t;
-    const int n = run_end - run_pos < 32 ? run_end - run_pos : 32;
-    t.off = (row_base + run_pos) * a.L_head_dim;
-    t.nrows = n;
-    t.mask = run_mask;
-    run_pos += n;
-    return t;
-  }
-};
 
 template <int D, int G, typename Engine, typename T>
 __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
   constexpr int RS = D + kPartPad;
   __shared__ u32x4 kvbuf[4][Engine::BUF];
-  __shared__ float st[4 * G * (D + 2)];
-  __shared__ int vpre[kMaxC + 1];
+  // the wave states of the epilogue reuse the tile buffers when they are
+  // large enough (after a barrier)
+  constexpr int ST = 4 * G * (D + 2);
+  constexpr bool ALIAS = sizeof(u32x4) * 4 * Engine::BUF >= sizeof(float) * ST;
+  __shared__ float st_own[ALIAS ? 1 : ST];
+  float* st = ALIAS ? reinterpret_cast<float*>(&kvbuf[0][0]) : st_own;
+  __shared__ int tpre[kMaxC + 1];  // exclusive prefix of the chosen clusters' tile counts
+  __shared__ int tbs[kMaxC];       // their tile-slot bases
   __shared__ int sh[16];
   __shared__ TileRec tiles[4][kTileBatch];
   const int tid = threadIdx.x;
@@ -782,76 +735,99 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
   u32x4* buf = kvbuf[wave];
   Engine acc;
   acc.init(a.q + ((int64_t)U.seq * a.Hq + (int64_t)U.kv_head * G) * D, a.scale_l2, buf);
+  // tile counts of the chosen clusters (in list order) -> exclusive prefix
+  const int n_ch = uni(a.ws.n_chosen[u]);
   {
     constexpr int EM = kMaxC / 256;
-    const int E = (C + 255) / 256;
-    int loc[EM];
+    const int E = (n_ch + 255) / 256;
+    int loc[EM], tbl[EM];
+#pragma unroll
+    for (int k = 0; k < EM; ++k) {
+      const int x = min(tid * E + k, C - 1);
+      loc[k] = a.ws.ch_ntiles[U.cl_base + x];
+      tbl[k] = a.ws.ch_tbase[U.cl_base + x];
+    }
     int sum = 0;
 #pragma unroll
     for (int k = 0; k < EM; ++k) {
-      const int g = tid * E + k;
-      const int v = (k < E && g < C) ? a.ws.cl_rows[U.cl_base + g] : 0;
-      loc[k] = v;
-      sum += v;
+      loc[k] = (k < E && tid * E + k < n_ch) ? loc[k] : 0;
+      sum += loc[k];
     }
     int total;
     int base = block_excl_scan<256>(sum, sh, total);
 #pragma unroll
     for (int k = 0; k < EM; ++k) {
-      const int g = tid * E + k;
-      if (k < E && g < C) vpre[g] = base;
+      const int x = tid * E + k;
+      if (k < E && x < n_ch) {
+        tpre[x] = base;
+        tbs[x] = tbl[k];
+      }
       base += loc[k];
     }
-    if (tid == 0) vpre[C] = total;
+    if (tid == 0) tpre[n_ch] = total;
     __syncthreads();
   }
-  const int64_t Tt = A + uni(vpre[C]);
+  // virtual tiles of the unit: [sink tiles | recent tiles | chosen clusters'
+  // tiles in list order]; wave w of the unit takes [w NT / NW, (w+1) NT / NW)
+  const int n_st = (a.n_sink + 31) / 32, n_rt = (a.n_recent + 31) / 32, n_at = n_st + n_rt;
+  const int NT = n_at + uni(tpre[n_ch]);
   const int NW = splits_u * 4;
   const int w = p * 4 + wave;
-  const int64_t r0 = (int64_t)w * Tt / NW;
-  const int64_t r1 = (int64_t)(w + 1) * Tt / NW;
+  int k0 = (int)((int64_t)w * NT / NW);
+  const int k1 = (int)((int64_t)(w + 1) * NT / NW);
   const T* kc = static_cast<const T*>(a.kv.k);
   const T* vc = static_cast<const T*>(a.kv.v);
   const uint32_t all = (1u << G) - 1u;
-  int64_t x = r0;
-  if (a.kv.paged && x < r1 && x < A) {
+  const KVRef kv = a.kv;
+  // first token and row count of anchor tile k (< n_at)
+  auto anchor_tile = [&](int k, int& tok, int& nr) {
+    if (k < n_st) {
+      tok = 32 * k;
+      nr = min(32, a.n_sink - 32 * k);
+    } else {
+      const int j = k - n_st;
+      tok = U.N - a.n_recent + 32 * j;
+      nr = min(32, a.n_recent - 32 * j);
+    }
+  };
+  if (kv.paged) {
     // anchors of a paged cache: rows gathered through the block table
-    const KVRef kv = a.kv;
-    const int seq = U.seq, kvh = U.kv_head;
-    const int64_t xe = r1 < A ? r1 : A;
-    while (x < xe) {
-      const bool sink = x < a.n_sink;
-      const int tok = sink ? (int)x : U.N - a.n_recent + (int)(x - a.n_sink);
-      const int64_t seg_end = sink ? (a.n_sink < xe ? a.n_sink : xe) : xe;
-      const int nr = (int)((seg_end - x) < 32 ? (seg_end - x) : 32);
-      acc.tile_gather(buf, kc, vc, nr, all, [&](int i) { return kv_row_offset(kv, seq, kvh, tok + i, D); });
-      x += nr;
+    for (; k0 < k1 && k0 < n_at; ++k0) {
+      int tok, nr;
+      anchor_tile(k0, tok, nr);
+      acc.tile_gather(buf, kc, vc, nr, all, [&](int i) { return kv_row_offset(kv, U.seq, U.kv_head, tok + i, D); });
     }
   }
-  if (x < r1) {
+  if (k0 < k1) {
     const T* km = static_cast<const T*>(a.L.k_mid);
     const T* vm = static_cast<const T*>(a.L.v_mid);
+    const TileRec* utiles = a.ws.tiles + tile_unit_base(U.row_base, U.cl_base, u);
     TileRec* tl = tiles[wave];
-    while (x < r1) {
-      // (1) list the next batch of tiles of [x, r1) in LDS; the cursor and
-      //     its metadata loads are dead before the streaming loop starts
-      int nt = 0;
-      {
-        RunCursor cur;
-        const int64_t xa = x > A ? x : A;
-        cur.begin(a, U, vpre, xa - A, r1 - A, lane);
-        if (x < A) cur.set_anchors(a, U, x, r1 < A ? r1 : A);
-        for (; nt < kTileBatch; ++nt) {
-          const TileDesc t = cur.next(a, U, lane);
-          if (t.nrows <= 0) break;
-          if (lane == 0) tl[nt] = TileRec{t.off, t.nrows | (t.src << 31), t.mask};
-          x += t.nrows;
+    const int64_t anc_base = kv.paged ? 0 : kv_row_offset(kv, U.seq, U.kv_head, 0, D);
+    while (k0 < k1) {
+      // (1) list the next batch in LDS, one tile per lane: an anchor tile
+      //     of a contiguous cache, or the chosen cluster's slot (binary
+      //     search of the prefix, then one 16-byte load)
+      const int nt = min(kTileBatch, k1 - k0);
+      if (lane < nt) {
+        const int k = k0 + lane;
+        TileRec r;
+        if (k < n_at) {
+          int tok, nr;
+          anchor_tile(k, tok, nr);
+          r = TileRec{anc_base + (int64_t)tok * D, nr | (int)0x80000000, 0xffffffffu};
+        } else {
+          const int kv_ = k - n_at;
+          int lo = 0, hi = n_ch;  // last x with tpre[x] <= kv_
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (tpre[mid] <= kv_) lo = mid; else hi = mid;
+          }
+          r = utiles[tbs[lo] + (kv_ - tpre[lo])];
         }
-        if (nt < kTileBatch) x = r1;
-        nt = uni(nt);
-        x = uni(x);
+        tl[lane] = r;
       }
-      if (nt == 0) break;
+      k0 += nt;
       // (2) stream the batch: the next tile's loads are in flight while the
       //     current one is computed.  rd(i) is tile i of the batch, or past
       //     the end an empty tile (0 rows: its loads read nothing), so every
@@ -895,6 +871,7 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
       }
     }
   }
+  __syncthreads();  // every wave is done with its tile buffer
   acc.to_lds(st);
   __syncthreads();
   write_block_record<D, G>(st, a.ws.ex_part + (int64_t)blockIdx.x * G * RS);

@@ -87,16 +87,36 @@ __device__ inline int64_t kv_row_offset(const KVRef& kv, int seq, int kvh, int t
 // ---------------------------------------------------------------------------
 // Decode launch block.
 // ---------------------------------------------------------------------------
+// One exact tile (16 bytes): element offset of its first row (in the layout
+// rows, or in the KV cache when the src bit is set), row count (<= 32) with
+// the src bit in bit 31, and the mask of the query heads that read it.
+struct TileRec {
+  int64_t off;
+  int32_t nrows_src;
+  uint32_t mask;
+};
+
+// Tile slots of a unit start here.  A chosen cluster of n rows yields at
+// most ceil(n/32) + S tiles (one partial tile per run, at most S runs), so
+// n_mid/32 + C (S + 1) + 1 slots per unit suffice; the base below grows by
+// at least that much from one unit to the next.
+__host__ __device__ inline int64_t tile_unit_base(int64_t row_base, int64_t cl_base, int u) {
+  return cl_base * (kMaxS + 1) + (row_base >> 5) + u;
+}
+
 struct DecodeWS {
   float* cl_score;      // [total_cl][G]      log2-domain scores
   uint32_t* cl_mask;    // [total_cl]         heads that chose the cluster
   int32_t* cl_rank;     // [total_cl][G]      rank among a head's chosen clusters, or -1
-  int32_t* cl_rows;     // [total_cl]         rows of the cluster read exactly (any head)
+                        //                    (written only when sel_s is requested)
   uint32_t* sub_mask;   // [total_sub]        heads that chose the subcluster
   int32_t* unit_rows;   // [n_units]          rows of chosen subclusters per unit
   int32_t* cl_list;     // [total_cl]         per unit (at cl_base): chosen clusters, ascending
   int32_t* n_chosen;    // [n_units]          length of the unit's list
   int32_t* uinfo;       // [n_units][2]       first exact block of the unit, its blocks
+  int32_t* ch_tbase;    // [total_cl]         per unit (at cl_base): tile-slot base of the x-th chosen cluster
+  int32_t* ch_ntiles;   // [total_cl]         per unit (at cl_base): tiles of the x-th chosen cluster
+  TileRec* tiles;       // [tile slots]       exact tiles, per unit at tile_unit_base()
   float* res_part;      // [n_units][nb_res][G][D+4] residual partials
   float* ex_part;       // [nblk][G][D+4]     exact-attention block records
 };
