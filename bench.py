@@ -226,6 +226,29 @@ def bench_workload(idx, steps, warmup, n_qsets, ev, with_errors=True):
     return res, state
 
 
+def build_timing(reps=3):
+    """mog_build (10 k-means rounds, subclusters, reorder, stats) of the
+    single-head 128K-key workload: median wall time over reps."""
+    import numpy as np
+    import torch
+
+    from long_context_sparse_mog_amd import ops, synth
+
+    wl = synth.build_workload()
+    b = synth.generate(wl, device="cuda", n_qsets=1)
+    kv = ops.KVCache.from_batch(b)
+    ops.mog_build(kv, wl.n_sink, wl.n_recent, kmeans_iters=wl.kmeans_iters, seed=1)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        t0 = time.time()
+        ops.mog_build(kv, wl.n_sink, wl.n_recent, kmeans_iters=wl.kmeans_iters, seed=1)
+        torch.cuda.synchronize()
+        ts.append(time.time() - t0)
+    return dict(workload=wl.name, n_keys=wl.seq_lens[0], kmeans_iters=wl.kmeans_iters,
+                seconds=float(np.median(ts)))
+
+
 def cpu_baseline(state, budget_s):
     """The CPU oracle (as it stands) decoding units of the same step on the
     host cores, given the GPU-built layout; extrapolated to a whole step."""
@@ -343,6 +366,8 @@ def main():
     ap.add_argument("--qsets", type=int, default=16)
     ap.add_argument("--no-128k", action="store_true", help="skip the N=128K workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the 4K, 32K and ragged workloads and the build timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 10 times (the reference kernel that "
@@ -368,6 +393,15 @@ def main():
     r128 = None
     if not args.no_128k:
         r128, _ = bench_workload(2, args.steps, args.warmup, args.qsets, ev)
+    others = {}
+    if not args.no_others:
+        keep = ("steps_per_s", "ms_per_step", "exact_kernel_ms", "exact_kernel_GBps", "frac_kv_read_per_head",
+                "frac_kv_read_union", "dense_ms_per_step", "speedup_vs_dense", "err_vs_dense_residual_mean",
+                "err_vs_dense_toponly_mean")
+        for idx in (0, 1, 4):
+            r, _ = bench_workload(idx, min(args.steps, 100), min(args.warmup, 10), args.qsets, ev)
+            others[r["workload"]] = {k: r[k] for k in keep}
+        others["build"] = build_timing()
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(st1m, args.cpu_seconds)
@@ -396,6 +430,7 @@ def main():
         "cpu_baseline": cpu,
         "at_1m": r1m,
         "at_128k": r128,
+        "other_workloads": others or None,
     }
     print(json.dumps(line), flush=True)
 

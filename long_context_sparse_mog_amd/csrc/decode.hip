@@ -205,9 +205,11 @@ __global__ __launch_bounds__(256) void k_score_clusters(DArgs a) {
 
 // ---------------------------------------------------------------------------
 // 2. Top-c clusters of every head of a unit, one wave per head.  Cluster i
-//    sits in lane i % 64, slot i / 64 of the wave's registers; a bitwise
-//    radix select (most significant bit first, one wave-wide count per bit)
-//    finds the key of the c-th largest score, then the keys above it and the
+//    sits in lane i % 64, slot i / 64 of the wave's registers.  A radix
+//    select, most significant bits first, finds the key of the c-th largest
+//    score: bits every valid key shares are decided at once, the next (up
+//    to) 8 varying bits by a histogram in the wave's LDS, and it stops as
+//    soon as every remaining candidate is needed.  The keys above it and the
 //    lowest-index keys equal to it are chosen.  Empty clusters are never
 //    chosen.  The block then writes every cluster's head mask and the
 //    ascending list of clusters some head chose.  Grid (units), 64 G threads.
@@ -218,21 +220,35 @@ __device__ inline int wave_sum_i(int v) {
   return v;
 }
 
+// bits 0..b set (b in [-1, 31])
+__device__ inline uint32_t mask_upto(int b) { return b >= 31 ? ~0u : ((1u << (b + 1)) - 1u); }
+
 template <int G>
 __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
   constexpr int NT = 64 * G;
   constexpr int KPL = kMaxC / 64;
-  __shared__ uint32_t umask[kMaxC];
+  __shared__ int hist[G][256];
+  __shared__ unsigned long long selb[G][KPL];  // per head: chosen lanes of slot j
   __shared__ int sh[16];
   const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63, h = tid >> 6;
   const int want_raw = b.top_c[u / a.Hkv];  // issued with the unit record
   const mog_unit U = uni_unit(a.L.units + u);
   const int C = U.C;
-  for (int i = tid; i < C; i += NT) umask[i] = 0u;
   if (tid == 0) a.ws.unit_rows[u] = 0;
   uint32_t key[KPL];
   int nvalid = 0;
-  // all loads first (clamped index, no branch around them), then the keys
+  // all loads first (clamped index, no branch around them), then the keys;
+  // the cluster sizes for the tile bounds below are loaded now as well
+  constexpr int EMAX = (kMaxC + NT - 1) / NT;
+  const int E = (C + NT - 1) / NT;
+  const int lo = tid * E, hi = min(C, lo + E);
+  const int32_t* off = a.L.sub_off + U.off_base;
+  int bound[EMAX];
+#pragma unroll
+  for (int k = 0; k < EMAX; ++k) {
+    const int i = min(lo + k, C - 1);
+    bound[k] = off[(i + 1) * U.S] - off[i * U.S];
+  }
   float scv[KPL];
 #pragma unroll
   for (int j = 0; j < KPL; ++j) scv[j] = a.ws.cl_score[(U.cl_base + min(64 * j + lane, C - 1)) * G + h];
@@ -242,14 +258,11 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
     key[j] = in ? float_key(scv[j]) : 0u;
     nvalid += in;
   }
-  nvalid = wave_sum_i(nvalid);  // once; the per-bit counts below use ballots
+  nvalid = wave_sum_i(nvalid);
   const int want = want_raw < 0 ? 0 : want_raw;
   const int c_eff = want < nvalid ? want : nvalid;
-  // Radix select, most significant bit first.  hi_mask holds the decided
-  // bits and prefix their values; cand counts the keys that match the
-  // prefix on them, kk how many of those are still to be taken.  Bits that
-  // every valid key shares are decided without a count, and the search
-  // stops as soon as all remaining candidates are needed (cand == kk).
+  // hi_mask: decided bits, prefix: their values; cand: keys matching the
+  // prefix there; kk: how many of those are still to be taken
   int kk = c_eff, cand = nvalid;
   uint32_t prefix = 0u, hi_mask = 0u;
   if (kk > 0) {
@@ -262,33 +275,61 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
     kor = wave_reduce_uniform(kor, [](uint32_t x, uint32_t y) { return x | y; }, 0u);
     kand = wave_reduce_uniform(kand, [](uint32_t x, uint32_t y) { return x & y; }, ~0u);
     const uint32_t varying = kor ^ kand;
-    for (int bit = 31; bit >= 0 && cand > kk; --bit) {
-      const uint32_t m = 1u << bit;
-      hi_mask |= m;
-      if (!(varying & m)) {
-        prefix |= kand & m;
-        continue;
+    int* hh = hist[h];
+    int top = 31;  // highest undecided bit
+    while (cand > kk && top >= 0) {
+      const uint32_t low = mask_upto(top);
+      const uint32_t rem = varying & low;
+      if (rem == 0u) {  // the candidates are all equal
+        prefix |= kand & low;
+        hi_mask |= low;
+        break;
       }
-      const uint32_t target = prefix | m;
-      // slots past C hold key 0, which never matches a nonzero target; the
-      // groups of 8 slots past C are skipped with one uniform branch each
-      // per-lane count without compares: (x == 0) as 1 - min(x, 1), so the
-      // slots do not serialise on the condition register; one wave sum
-      int cnt = 0;
+      const int nb = 31 - __clz(rem);  // next varying bit; bits (nb, top] shared
+      const uint32_t shared_bits = low & ~mask_upto(nb);
+      prefix |= kand & shared_bits;
+      hi_mask |= shared_bits;
+      const int w = nb + 1 < 8 ? nb + 1 : 8;
+      const int shift = nb - w + 1;
+      const uint32_t dmask = (1u << w) - 1u;
+      // histogram of the candidates' next digit (wave-private bins; a wave
+      // executes its LDS operations in order)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) hh[64 * k + lane] = 0;
+      __asm__ volatile("" ::: "memory");
 #pragma unroll
       for (int jg = 0; jg < KPL / 8; ++jg) {
         if (512 * jg >= C) break;
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) cnt += 1 - (int)min((key[8 * jg + jj] & hi_mask) ^ target, 1u);
+        for (int jj = 0; jj < 8; ++jj) {
+          const uint32_t kv = key[8 * jg + jj];
+          if (kv != 0u && (kv & hi_mask) == prefix) atomicAdd(&hh[(kv >> shift) & dmask], 1);
+        }
       }
-      cnt = (int)wave_reduce_uniform((uint32_t)cnt, [](uint32_t x, uint32_t y) { return x + y; }, 0u);
-      if (cnt >= kk) {
-        prefix = target;
-        cand = cnt;
-      } else {
-        kk -= cnt;
-        cand -= cnt;
+      __asm__ volatile("" ::: "memory");
+      // lane l holds digits 4l..4l+3; candidates with digits above lane l
+      const int c0 = hh[4 * lane], c1 = hh[4 * lane + 1], c2 = hh[4 * lane + 2], c3 = hh[4 * lane + 3];
+      const int part = c0 + c1 + c2 + c3;
+      int suf = part;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_down(suf, o, 64);
+        if (lane + o < 64) suf += y;
       }
+      const int a3 = suf - part, a2 = a3 + c3, a1 = a2 + c2, a0 = a1 + c1;
+      int dsel = -1, dab = 0, dcnt = 0;
+      if (a3 < kk && kk <= a3 + c3) { dsel = 4 * lane + 3; dab = a3; dcnt = c3; }
+      else if (a2 < kk && kk <= a2 + c2) { dsel = 4 * lane + 2; dab = a2; dcnt = c2; }
+      else if (a1 < kk && kk <= a1 + c1) { dsel = 4 * lane + 1; dab = a1; dcnt = c1; }
+      else if (a0 < kk && kk <= a0 + c0) { dsel = 4 * lane; dab = a0; dcnt = c0; }
+      const unsigned long long fb = __ballot(dsel >= 0);
+      const int src = fb ? __ffsll((long long)fb) - 1 : 0;
+      const int d = __builtin_amdgcn_readlane(dsel, src);
+      prefix |= (uint32_t)d << shift;
+      hi_mask |= dmask << shift;
+      kk -= __builtin_amdgcn_readlane(dab, src);
+      cand = __builtin_amdgcn_readlane(dcnt, src);
+      top = shift - 1;
     }
   }
   // chosen: keys above the prefix on the decided bits, then the first kk
@@ -296,27 +337,34 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
   const int hq = U.kv_head * G + h;
   const int64_t row = (int64_t)U.seq * a.Hq + hq;
   const unsigned long long below = (1ull << lane) - 1ull;
+  // (when every key matching the prefix is taken, cand == kk, no tie ranks
+  // are needed and the slots are independent)
+  const bool all_ties = cand == kk;
   int ties = 0, rank0 = 0;
-  __syncthreads();  // umask cleared
 #pragma unroll
   for (int j = 0; j < KPL; ++j) {
     if (64 * j >= C) break;
     const int i = 64 * j + lane;
     const uint32_t kd = key[j] & hi_mask;
-    const bool tie = c_eff > 0 && kd == prefix && key[j] != 0u;
-    const unsigned long long tb = __ballot(tie);
-    const bool sel = c_eff > 0 && key[j] != 0u && (kd > prefix || (tie && ties + __popcll(tb & below) < kk));
-    ties += __popcll(tb);
+    bool sel;
+    if (all_ties) {
+      sel = c_eff > 0 && key[j] != 0u && kd >= prefix;
+    } else {
+      const bool tie = c_eff > 0 && kd == prefix && key[j] != 0u;
+      const unsigned long long tb = __ballot(tie);
+      sel = c_eff > 0 && key[j] != 0u && (kd > prefix || (tie && ties + __popcll(tb & below) < kk));
+      ties += __popcll(tb);
+    }
     const unsigned long long sb = __ballot(sel);
-    const int rank = sel ? rank0 + __popcll(sb & below) : -1;
-    rank0 += __popcll(sb);
-    if (i < C) {
-      if (a.sel_s) a.ws.cl_rank[(U.cl_base + i) * G + h] = rank;  // read back only for sel_s
-      if (sel) {
-        atomicOr(&umask[i], 1u << h);
-        if (a.sel_c) a.sel_c[row * a.c_stride + rank] = i;
+    if (lane == 0) selb[h][j] = sb;
+    if (a.sel_c != nullptr || a.sel_s != nullptr) {
+      const int rank = sel ? rank0 + __popcll(sb & below) : -1;
+      if (i < C) {
+        if (a.sel_s) a.ws.cl_rank[(U.cl_base + i) * G + h] = rank;  // read back only for sel_s
+        if (sel && a.sel_c) a.sel_c[row * a.c_stride + rank] = i;
       }
     }
+    rank0 += __popcll(sb);
   }
   if (a.sel_c)
     for (int j = c_eff + lane; j < a.c_stride; j += 64) a.sel_c[row * a.c_stride + j] = -1;
@@ -329,24 +377,20 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
   // cluster the base of its tile slots: a prefix of ceil(rows/32) + S, the
   // most tiles its chosen subclusters can make (thread t covers clusters
   // [t E, t E + E); E <= EMAX)
-  constexpr int EMAX = (kMaxC + NT - 1) / NT;
-  const int E = (C + NT - 1) / NT;
-  const int lo = tid * E, hi = min(C, lo + E);
-  const int32_t* off = a.L.sub_off + U.off_base;
-  int bound[EMAX];
 #pragma unroll
-  for (int k = 0; k < EMAX; ++k) {
-    const int i = min(lo + k, C - 1);
-    bound[k] = (off[(i + 1) * U.S] - off[i * U.S] + 31) / 32 + U.S;
-  }
+  for (int k = 0; k < EMAX; ++k) bound[k] = (bound[k] + 31) / 32 + U.S;
+  uint32_t um[EMAX];
   int cnt = 0, ub = 0;
 #pragma unroll
   for (int k = 0; k < EMAX; ++k) {
     const int i = lo + k;
+    um[k] = 0u;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) um[k] |= (uint32_t)((selb[hh][(i >> 6) & (KPL - 1)] >> (i & 63)) & 1ull) << hh;
     if (i < hi) {
-      a.ws.cl_mask[U.cl_base + i] = umask[i];
-      cnt += umask[i] != 0u;
-      ub += umask[i] != 0u ? bound[k] : 0;
+      a.ws.cl_mask[U.cl_base + i] = um[k];
+      cnt += um[k] != 0u;
+      ub += um[k] != 0u ? bound[k] : 0;
     }
   }
   int total, ub_total;
@@ -355,7 +399,7 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
 #pragma unroll
   for (int k = 0; k < EMAX; ++k) {
     const int i = lo + k;
-    if (i < hi && umask[i] != 0u) {
+    if (i < hi && um[k] != 0u) {
       a.ws.cl_list[U.cl_base + pos] = i;
       a.ws.ch_tbase[U.cl_base + pos] = tb;
       ++pos;
