@@ -64,6 +64,22 @@ __device__ inline uint32_t wave_reduce_uniform(uint32_t x, Op op, uint32_t ident
   return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
+// Inclusive prefix sum over lanes 0..63 (lane l gets x_0 + ... + x_l): three
+// row shifts give each lane the sum of up to 4 lanes, shifts by 4 and 8 on
+// the banks that have a full source finish every row of 16, and the row
+// broadcasts 15 and 31 carry the row totals forward.
+__device__ inline int wave_incl_scan(int x) {
+  int s = x;
+  s += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  s += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  s += __builtin_amdgcn_update_dpp(0, x, 0x113, 0xF, 0xF, false);  // row_shr:3
+  s += __builtin_amdgcn_update_dpp(0, s, 0x114, 0xF, 0xE, false);  // row_shr:4, lanes 4..15 of a row
+  s += __builtin_amdgcn_update_dpp(0, s, 0x118, 0xF, 0xC, false);  // row_shr:8, lanes 8..15 of a row
+  s += __builtin_amdgcn_update_dpp(0, s, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  s += __builtin_amdgcn_update_dpp(0, s, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return s;
+}
+
 __device__ inline float wave_sum_dpp(float x) {
   x = row16_sum(x);
   x += __shfl_xor(x, 16, 64);

@@ -205,60 +205,52 @@ __global__ __launch_bounds__(256) void k_score_clusters(DArgs a) {
 
 // ---------------------------------------------------------------------------
 // 2. Top-c clusters of every head of a unit, one wave per head.  Cluster i
-//    sits in lane i % 64, slot i / 64 of the wave's registers.  A radix
-//    select, most significant bits first, finds the key of the c-th largest
-//    score: bits every valid key shares are decided at once, the next (up
-//    to) 8 varying bits by a histogram in the wave's LDS, and it stops as
-//    soon as every remaining candidate is needed.  The keys above it and the
-//    lowest-index keys equal to it are chosen.  Empty clusters are never
-//    chosen.  The block then writes every cluster's head mask and the
-//    ascending list of clusters some head chose.  Grid (units), 64 G threads.
+//    sits in lane i % 64, slot i / 64 of the wave's registers (KPL slots,
+//    enough for the largest unit).  A radix select, most significant bits
+//    first, finds the key of the c-th largest score: bits every valid key
+//    shares are decided at once, the next (up to) 8 varying bits by a
+//    histogram in the wave's LDS bins (suffix counts by a DPP scan), and it
+//    stops as soon as every remaining candidate is needed.  The keys above
+//    it and the lowest-index keys equal to it are chosen.  Empty clusters are
+//    never chosen.  The block then writes every cluster's head mask, the
+//    ascending list of clusters some head chose and their tile-slot bases
+//    (wave w takes the slots w, w + G, ...).  Grid (units), 64 G threads.
 // ---------------------------------------------------------------------------
-__device__ inline int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
 // bits 0..b set (b in [-1, 31])
 __device__ inline uint32_t mask_upto(int b) { return b >= 31 ? ~0u : ((1u << (b + 1)) - 1u); }
 
-template <int G>
+template <int G, int KPL>
 __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
-  constexpr int NT = 64 * G;
-  constexpr int KPL = kMaxC / 64;
-  __shared__ int hist[G][256];
+  constexpr int NSW = (KPL + G - 1) / G;  // tail slots per wave
+  __shared__ int hist[G][256 + 64];       // 256 digit bins, then one spare bin per lane
   __shared__ unsigned long long selb[G][KPL];  // per head: chosen lanes of slot j
-  __shared__ int sh[16];
+  __shared__ int slot_cnt[KPL], slot_tiles[KPL];
   const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63, h = tid >> 6;
-  const int want_raw = b.top_c[u / a.Hkv];  // issued with the unit record
+  const int want_raw = b.top_c[u / a.Hkv];
   const mog_unit U = uni_unit(a.L.units + u);
   const int C = U.C;
   if (tid == 0) a.ws.unit_rows[u] = 0;
-  uint32_t key[KPL];
-  int nvalid = 0;
-  // all loads first (clamped index, no branch around them), then the keys;
-  // the cluster sizes for the tile bounds below are loaded now as well
-  constexpr int EMAX = (kMaxC + NT - 1) / NT;
-  const int E = (C + NT - 1) / NT;
-  const int lo = tid * E, hi = min(C, lo + E);
-  const int32_t* off = a.L.sub_off + U.off_base;
-  int bound[EMAX];
-#pragma unroll
-  for (int k = 0; k < EMAX; ++k) {
-    const int i = min(lo + k, C - 1);
-    bound[k] = off[(i + 1) * U.S] - off[i * U.S];
-  }
+  // every load first (clamped indices): the head's scores, and the sizes of
+  // the clusters of this wave's tail slots
   float scv[KPL];
 #pragma unroll
   for (int j = 0; j < KPL; ++j) scv[j] = a.ws.cl_score[(U.cl_base + min(64 * j + lane, C - 1)) * G + h];
+  const int32_t* off = a.L.sub_off + U.off_base;
+  int bound[NSW];
+#pragma unroll
+  for (int t = 0; t < NSW; ++t) {
+    const int i = min(64 * (h + G * t) + lane, C - 1);
+    bound[t] = off[(i + 1) * U.S] - off[i * U.S];
+  }
+  uint32_t key[KPL];
+  int nvalid = 0;
 #pragma unroll
   for (int j = 0; j < KPL; ++j) {
     const bool in = 64 * j + lane < C && scv[j] != -INFINITY;
     key[j] = in ? float_key(scv[j]) : 0u;
     nvalid += in;
   }
-  nvalid = wave_sum_i(nvalid);
+  nvalid = (int)wave_reduce_uniform((uint32_t)nvalid, [](uint32_t x, uint32_t y) { return x + y; }, 0u);
   const int want = want_raw < 0 ? 0 : want_raw;
   const int c_eff = want < nvalid ? want : nvalid;
   // hi_mask: decided bits, prefix: their values; cand: keys matching the
@@ -292,36 +284,30 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
       const int w = nb + 1 < 8 ? nb + 1 : 8;
       const int shift = nb - w + 1;
       const uint32_t dmask = (1u << w) - 1u;
-      // histogram of the candidates' next digit (wave-private bins; a wave
+      // histogram of the candidates' next digit; keys that are not
+      // candidates go to the lane's spare bin, so there is no branch (a wave
       // executes its LDS operations in order)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) hh[64 * k + lane] = 0;
+      *reinterpret_cast<int4*>(&hh[4 * lane]) = make_int4(0, 0, 0, 0);
       __asm__ volatile("" ::: "memory");
 #pragma unroll
-      for (int jg = 0; jg < KPL / 8; ++jg) {
-        if (512 * jg >= C) break;
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const uint32_t kv = key[8 * jg + jj];
-          if (kv != 0u && (kv & hi_mask) == prefix) atomicAdd(&hh[(kv >> shift) & dmask], 1);
-        }
+      for (int j = 0; j < KPL; ++j) {
+        const uint32_t kv = key[j];
+        const bool m = kv != 0u && (kv & hi_mask) == prefix;
+        atomicAdd(&hh[m ? (int)((kv >> shift) & dmask) : 256 + lane], 1);
       }
       __asm__ volatile("" ::: "memory");
-      // lane l holds digits 4l..4l+3; candidates with digits above lane l
-      const int c0 = hh[4 * lane], c1 = hh[4 * lane + 1], c2 = hh[4 * lane + 2], c3 = hh[4 * lane + 3];
+      // lane l holds digits 252-4l .. 255-4l; candidates above its digits
+      // come from the lanes before it
+      const int4 cv = *reinterpret_cast<const int4*>(&hh[4 * (63 - lane)]);
+      const int c0 = cv.x, c1 = cv.y, c2 = cv.z, c3 = cv.w;
       const int part = c0 + c1 + c2 + c3;
-      int suf = part;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_down(suf, o, 64);
-        if (lane + o < 64) suf += y;
-      }
-      const int a3 = suf - part, a2 = a3 + c3, a1 = a2 + c2, a0 = a1 + c1;
+      const int a3 = wave_incl_scan(part) - part, a2 = a3 + c3, a1 = a2 + c2, a0 = a1 + c1;
+      const int dbase = 4 * (63 - lane);
       int dsel = -1, dab = 0, dcnt = 0;
-      if (a3 < kk && kk <= a3 + c3) { dsel = 4 * lane + 3; dab = a3; dcnt = c3; }
-      else if (a2 < kk && kk <= a2 + c2) { dsel = 4 * lane + 2; dab = a2; dcnt = c2; }
-      else if (a1 < kk && kk <= a1 + c1) { dsel = 4 * lane + 1; dab = a1; dcnt = c1; }
-      else if (a0 < kk && kk <= a0 + c0) { dsel = 4 * lane; dab = a0; dcnt = c0; }
+      if (a3 < kk && kk <= a2) { dsel = dbase + 3; dab = a3; dcnt = c3; }
+      else if (a2 < kk && kk <= a1) { dsel = dbase + 2; dab = a2; dcnt = c2; }
+      else if (a1 < kk && kk <= a0) { dsel = dbase + 1; dab = a1; dcnt = c1; }
+      else if (a0 < kk && kk <= a0 + c0) { dsel = dbase; dab = a0; dcnt = c0; }
       const unsigned long long fb = __ballot(dsel >= 0);
       const int src = fb ? __ffsll((long long)fb) - 1 : 0;
       const int d = __builtin_amdgcn_readlane(dsel, src);
@@ -333,38 +319,38 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
     }
   }
   // chosen: keys above the prefix on the decided bits, then the first kk
-  // (by index) of the keys that match it there
+  // (by index) of the keys that match it there.  When every key matching
+  // the prefix is taken (cand == kk) no tie ranks are needed.
   const int hq = U.kv_head * G + h;
   const int64_t row = (int64_t)U.seq * a.Hq + hq;
   const unsigned long long below = (1ull << lane) - 1ull;
-  // (when every key matching the prefix is taken, cand == kk, no tie ranks
-  // are needed and the slots are independent)
   const bool all_ties = cand == kk;
+  const bool want_sel = a.sel_c != nullptr || a.sel_s != nullptr;
   int ties = 0, rank0 = 0;
 #pragma unroll
   for (int j = 0; j < KPL; ++j) {
-    if (64 * j >= C) break;
     const int i = 64 * j + lane;
     const uint32_t kd = key[j] & hi_mask;
+    const bool valid = c_eff > 0 && key[j] != 0u;
     bool sel;
     if (all_ties) {
-      sel = c_eff > 0 && key[j] != 0u && kd >= prefix;
+      sel = valid && kd >= prefix;
     } else {
-      const bool tie = c_eff > 0 && kd == prefix && key[j] != 0u;
+      const bool tie = valid && kd == prefix;
       const unsigned long long tb = __ballot(tie);
-      sel = c_eff > 0 && key[j] != 0u && (kd > prefix || (tie && ties + __popcll(tb & below) < kk));
+      sel = valid && (kd > prefix || (tie && ties + __popcll(tb & below) < kk));
       ties += __popcll(tb);
     }
     const unsigned long long sb = __ballot(sel);
     if (lane == 0) selb[h][j] = sb;
-    if (a.sel_c != nullptr || a.sel_s != nullptr) {
+    if (want_sel) {
       const int rank = sel ? rank0 + __popcll(sb & below) : -1;
       if (i < C) {
         if (a.sel_s) a.ws.cl_rank[(U.cl_base + i) * G + h] = rank;  // read back only for sel_s
         if (sel && a.sel_c) a.sel_c[row * a.c_stride + rank] = i;
       }
+      rank0 += __popcll(sb);
     }
-    rank0 += __popcll(sb);
   }
   if (a.sel_c)
     for (int j = c_eff + lane; j < a.c_stride; j += 64) a.sel_c[row * a.c_stride + j] = -1;
@@ -373,40 +359,54 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
     for (int j = c_eff * a.s_stride + lane; j < a.c_stride * a.s_stride; j += 64) a.sel_s[base + j] = -1;
   }
   __syncthreads();
-  // head masks, the ascending list of chosen clusters, and for each chosen
-  // cluster the base of its tile slots: a prefix of ceil(rows/32) + S, the
-  // most tiles its chosen subclusters can make (thread t covers clusters
-  // [t E, t E + E); E <= EMAX)
+  // tail: cluster i = 64 j + lane.  A chosen cluster takes ceil(rows/32) + S
+  // tile slots, the most its chosen subclusters can make.  First the
+  // per-slot counts, then each slot's list positions and slot bases from
+  // the counts of the slots before it.
+  uint32_t um[NSW];
+  int tcnt[NSW];
 #pragma unroll
-  for (int k = 0; k < EMAX; ++k) bound[k] = (bound[k] + 31) / 32 + U.S;
-  uint32_t um[EMAX];
-  int cnt = 0, ub = 0;
+  for (int t = 0; t < NSW; ++t) {
+    const int j = h + G * t;
+    um[t] = 0u;
+    tcnt[t] = 0;
+    if (j < KPL) {
 #pragma unroll
-  for (int k = 0; k < EMAX; ++k) {
-    const int i = lo + k;
-    um[k] = 0u;
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) um[k] |= (uint32_t)((selb[hh][(i >> 6) & (KPL - 1)] >> (i & 63)) & 1ull) << hh;
-    if (i < hi) {
-      a.ws.cl_mask[U.cl_base + i] = um[k];
-      cnt += um[k] != 0u;
-      ub += um[k] != 0u ? bound[k] : 0;
+      for (int g = 0; g < G; ++g) um[t] |= (uint32_t)((selb[g][j] >> lane) & 1ull) << g;
+      if (64 * j + lane >= C) um[t] = 0u;
+      tcnt[t] = um[t] != 0u ? (bound[t] + 31) / 32 + U.S : 0;
+      const int n = __popcll(__ballot(um[t] != 0u));
+      const int nt = (int)wave_reduce_uniform((uint32_t)tcnt[t], [](uint32_t x, uint32_t y) { return x + y; }, 0u);
+      if (lane == 0) {
+        slot_cnt[j] = n;
+        slot_tiles[j] = nt;
+      }
     }
   }
-  int total, ub_total;
-  int pos = block_excl_scan<NT>(cnt, sh, total);
-  int tb = block_excl_scan<NT>(ub, sh, ub_total);
+  __syncthreads();
 #pragma unroll
-  for (int k = 0; k < EMAX; ++k) {
-    const int i = lo + k;
-    if (i < hi && um[k] != 0u) {
-      a.ws.cl_list[U.cl_base + pos] = i;
-      a.ws.ch_tbase[U.cl_base + pos] = tb;
-      ++pos;
-      tb += bound[k];
+  for (int t = 0; t < NSW; ++t) {
+    const int j = h + G * t;
+    if (j < KPL) {
+      const int i = 64 * j + lane;
+      const auto add = [](uint32_t x, uint32_t y) { return x + y; };
+      const int pos0 = (int)wave_reduce_uniform(lane < j ? (uint32_t)slot_cnt[lane] : 0u, add, 0u);
+      const int tb0 = (int)wave_reduce_uniform(lane < j ? (uint32_t)slot_tiles[lane] : 0u, add, 0u);
+      if (i < C) a.ws.cl_mask[U.cl_base + i] = um[t];
+      const bool ch = um[t] != 0u;
+      const int pos = pos0 + __popcll(__ballot(ch) & below);
+      const int tb = tb0 + wave_incl_scan(tcnt[t]) - tcnt[t];
+      if (ch) {
+        a.ws.cl_list[U.cl_base + pos] = i;
+        a.ws.ch_tbase[U.cl_base + pos] = tb;
+      }
     }
   }
-  if (tid == 0) a.ws.n_chosen[u] = total;
+  if (h == 0) {
+    const uint32_t c = lane < KPL ? (uint32_t)slot_cnt[lane] : 0u;
+    const int total = (int)wave_reduce_uniform(c, [](uint32_t x, uint32_t y) { return x + y; }, 0u);
+    if (lane == 0) a.ws.n_chosen[u] = total;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1098,7 +1098,14 @@ template <int D, int G>
 static hipError_t decode_impl(const DecodeLaunch& x, const DArgs& a, const BudgetArgs& b, hipStream_t s) {
   const int nu = x.L.n_units;
   hipLaunchKernelGGL((k_score_clusters<D, G>), dim3((x.L.max_C + 15) / 16, nu), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(k_select_topc<G>, dim3(nu), dim3(64 * G), 0, s, a, b);
+  if (x.L.max_C <= 256)
+    hipLaunchKernelGGL((k_select_topc<G, 4>), dim3(nu), dim3(64 * G), 0, s, a, b);
+  else if (x.L.max_C <= 512)
+    hipLaunchKernelGGL((k_select_topc<G, 8>), dim3(nu), dim3(64 * G), 0, s, a, b);
+  else if (x.L.max_C <= 1024)
+    hipLaunchKernelGGL((k_select_topc<G, 16>), dim3(nu), dim3(64 * G), 0, s, a, b);
+  else
+    hipLaunchKernelGGL((k_select_topc<G, kMaxC / 64>), dim3(nu), dim3(64 * G), 0, s, a, b);
   hipLaunchKernelGGL((k_subclusters<D, G>), dim3(x.nb_res, nu), dim3(256), 0, s, a, b, x.nb_chosen);
   if (x.ev_begin) {
     const hipError_t e = hipEventRecord(x.ev_begin, s);
