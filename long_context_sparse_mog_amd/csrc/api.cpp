@@ -167,7 +167,7 @@ KVRef make_kvref(const mog_kv* kv) {
 // ------------------------------------------------------------------------
 struct DecodePlan {
   int G, c_stride, s_stride, splits, nblk, nb_res, nb_chosen;
-  size_t o_clscore, o_clmask, o_clrank, o_submask, o_urows, o_list, o_nch, o_uinfo, o_tbase, o_ntl, o_tiles, o_res, o_ex, bytes;
+  size_t o_clscore, o_clmask, o_clrank, o_urows, o_list, o_nch, o_uinfo, o_tbase, o_ntl, o_tiles, o_res, o_ex, bytes;
 };
 
 int seq_top(const int32_t* per, int dflt, int s) { return per ? per[s] : dflt; }
@@ -217,16 +217,18 @@ DecodePlan plan_decode(const mog_layout* L, const mog_decode_params* p) {
   const int D = L->head_dim, G = d.G, RS = D + kPartPad;
   const int64_t nu = L->n_units;
   size_t o = kAlign;  // first 256 bytes: reserved, kept zero
-  d.o_clscore = o; o = align_up(o + (size_t)L->total_cl * G * 4);
-  d.o_clmask = o; o = align_up(o + (size_t)L->total_cl * 4);
-  d.o_clrank = o; o = align_up(o + (size_t)L->total_cl * G * 4);
-  d.o_submask = o; o = align_up(o + (size_t)L->total_sub * 4);
+  // per-cluster entries: max_C per unit, so a unit's entries start at
+  // u * max_C and kernels can address them before reading the unit table
+  const size_t ncw = (size_t)nu * L->max_C;
+  d.o_clscore = o; o = align_up(o + ncw * G * 4);
+  d.o_clmask = o; o = align_up(o + ncw * 4);
+  d.o_clrank = o; o = align_up(o + ncw * G * 4);
   d.o_urows = o; o = align_up(o + (size_t)nu * 4);
-  d.o_list = o; o = align_up(o + (size_t)L->total_cl * 4);
+  d.o_list = o; o = align_up(o + ncw * 4);
   d.o_nch = o; o = align_up(o + (size_t)nu * 4);
   d.o_uinfo = o; o = align_up(o + (size_t)nu * 2 * 4);
-  d.o_tbase = o; o = align_up(o + (size_t)L->total_cl * 4);
-  d.o_ntl = o; o = align_up(o + (size_t)L->total_cl * 4);
+  d.o_tbase = o; o = align_up(o + ncw * 4);
+  d.o_ntl = o; o = align_up(o + ncw * 4);
   d.o_tiles = o;
   o = align_up(o + (size_t)(tile_unit_base(L->total_mid, L->total_cl, (int)nu) + 2) * sizeof(TileRec));
   d.o_res = o; o = align_up(o + (size_t)nu * d.nb_res * G * RS * 4);
@@ -512,7 +514,6 @@ mog_status mog_decode(const mog_layout* layout, const mog_kv* kv, const float* q
   x.ws.cl_score = reinterpret_cast<float*>(w + d.o_clscore);
   x.ws.cl_mask = reinterpret_cast<uint32_t*>(w + d.o_clmask);
   x.ws.cl_rank = reinterpret_cast<int32_t*>(w + d.o_clrank);
-  x.ws.sub_mask = reinterpret_cast<uint32_t*>(w + d.o_submask);
   x.ws.unit_rows = reinterpret_cast<int32_t*>(w + d.o_urows);
   x.ws.cl_list = reinterpret_cast<int32_t*>(w + d.o_list);
   x.ws.n_chosen = reinterpret_cast<int32_t*>(w + d.o_nch);

@@ -38,6 +38,7 @@ struct DArgs {
   int32_t* sel_c;
   int32_t* sel_s;
   int32_t c_stride, s_stride, Hq, Hkv, n_sink, n_recent, residual, splits, nb_res, n_units, nblk;
+  int32_t cstride;   // per-cluster workspace entries per unit (the largest C)
   float scale_l2;    // scale * log2(e)
   float half_s2_l2;  // scale^2 / 2 * log2(e)
   int32_t L_head_dim;
@@ -195,11 +196,11 @@ __global__ __launch_bounds__(256) void k_score_clusters(DArgs a) {
   // lane k (< 4) now holds the scores of cluster g0 + k
   const int g = g0 + lane;
   if (lane < 4 && g < U.C) {
-    const int64_t cg = U.cl_base + g;
+    const int64_t cw = (int64_t)u * a.cstride + g;
     const int n = off[(g + 1) * U.S] - off[g * U.S];
     const float lg = n > 0 ? log2f((float)n) : -INFINITY;
 #pragma unroll
-    for (int h = 0; h < G; ++h) a.ws.cl_score[cg * G + h] = n > 0 ? mine[h] + lg : -INFINITY;
+    for (int h = 0; h < G; ++h) a.ws.cl_score[cw * G + h] = n > 0 ? mine[h] + lg : -INFINITY;
   }
 }
 
@@ -227,14 +228,16 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
   __shared__ int slot_cnt[KPL], slot_tiles[KPL];
   const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63, h = tid >> 6;
   const int want_raw = b.top_c[u / a.Hkv];
+  // the scores need only the unit index: their loads go out with the unit
+  // record's (entries past the unit's C are masked below)
+  const int64_t cw = (int64_t)u * a.cstride;
+  float scv[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) scv[j] = a.ws.cl_score[(cw + min(64 * j + lane, a.cstride - 1)) * G + h];
   const mog_unit U = uni_unit(a.L.units + u);
   const int C = U.C;
   if (tid == 0) a.ws.unit_rows[u] = 0;
-  // every load first (clamped indices): the head's scores, and the sizes of
-  // the clusters of this wave's tail slots
-  float scv[KPL];
-#pragma unroll
-  for (int j = 0; j < KPL; ++j) scv[j] = a.ws.cl_score[(U.cl_base + min(64 * j + lane, C - 1)) * G + h];
+  // the sizes of the clusters of this wave's tail slots
   const int32_t* off = a.L.sub_off + U.off_base;
   int bound[NSW];
 #pragma unroll
@@ -346,7 +349,7 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
     if (want_sel) {
       const int rank = sel ? rank0 + __popcll(sb & below) : -1;
       if (i < C) {
-        if (a.sel_s) a.ws.cl_rank[(U.cl_base + i) * G + h] = rank;  // read back only for sel_s
+        if (a.sel_s) a.ws.cl_rank[(cw + i) * G + h] = rank;  // read back only for sel_s
         if (sel && a.sel_c) a.sel_c[row * a.c_stride + rank] = i;
       }
       rank0 += __popcll(sb);
@@ -392,13 +395,13 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
       const auto add = [](uint32_t x, uint32_t y) { return x + y; };
       const int pos0 = (int)wave_reduce_uniform(lane < j ? (uint32_t)slot_cnt[lane] : 0u, add, 0u);
       const int tb0 = (int)wave_reduce_uniform(lane < j ? (uint32_t)slot_tiles[lane] : 0u, add, 0u);
-      if (i < C) a.ws.cl_mask[U.cl_base + i] = um[t];
+      if (i < C) a.ws.cl_mask[cw + i] = um[t];
       const bool ch = um[t] != 0u;
       const int pos = pos0 + __popcll(__ballot(ch) & below);
       const int tb = tb0 + wave_incl_scan(tcnt[t]) - tcnt[t];
       if (ch) {
-        a.ws.cl_list[U.cl_base + pos] = i;
-        a.ws.ch_tbase[U.cl_base + pos] = tb;
+        a.ws.cl_list[cw + pos] = i;
+        a.ws.ch_tbase[cw + pos] = tb;
       }
     }
   }
@@ -460,9 +463,19 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
   __shared__ int lds_cnt[kMaxS];
   __shared__ int lds_off[kMaxS + 1];
   __shared__ int sh[16];
-  const int u = blockIdx.y, tid = threadIdx.x;
+  const int u = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int s_keep_raw = b.top_s[u / a.Hkv];  // issued with the unit record
+  const int64_t cw = (int64_t)u * a.cstride;  // the unit's per-cluster workspace entries
+  // the x-th chosen cluster needs only the unit index: its loads go out with
+  // the unit record's
+  const int x = blockIdx.y;
+  int n_ch = 0, g_x = 0, tb_x = 0;
+  if (x < nb_chosen) {
+    n_ch = a.ws.n_chosen[u];
+    g_x = a.ws.cl_list[cw + x];
+    tb_x = a.ws.ch_tbase[cw + x];
+  }
   const mog_unit U = uni_unit(a.L.units + u);
   const int S = U.S, C = U.C;
   const uint32_t all = (1u << G) - 1u;
@@ -475,16 +488,14 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
 #pragma unroll
     for (int e = 0; e < VPL; ++e) ro[h][e] = 0.f;
   }
-  float* dst = a.ws.res_part + ((int64_t)u * a.nb_res + blockIdx.x) * G * RS;
+  float* dst = a.ws.res_part + ((int64_t)u * a.nb_res + x) * G * RS;
 
-  if ((int)blockIdx.x < nb_chosen) {
+  if (x < nb_chosen) {
     // -------- the x-th chosen cluster ---------------------------------------
-    const int x = blockIdx.x;
-    // x < nb_chosen <= C, so the list entries are in range either way
-    const int n_ch = a.ws.n_chosen[u], g_x = a.ws.cl_list[U.cl_base + x], tb_x = a.ws.ch_tbase[U.cl_base + x];
+    // (x < nb_chosen <= the largest C, so the list entries are in range)
     const int g = x < uni(n_ch) ? uni(g_x) : -1;
     if (g >= 0) {
-      const int64_t cg = U.cl_base + g;
+      const int64_t cg = cw + g;
       const int64_t sg0 = U.sub_base + (int64_t)g * S;
       const uint32_t mask = a.ws.cl_mask[cg];
       const float* qb = a.q + ((int64_t)U.seq * a.Hq + (int64_t)U.kv_head * G) * D;
@@ -500,8 +511,8 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
         load_floats<EPL>(a.L.sub_ms + (sg0 + i) * (2 * D) + lane * EPL, xr[k]);
         if (a.residual) load_floats<VPL>(a.L.sub_vbar + (sg0 + i) * D + lane * VPL, vb[k]);
       }
-      // subcluster sizes and (for the selection output) the cluster's rank
-      // per head, issued with the loads above
+      // subcluster bounds: thread i < S keeps subcluster i's for the tiles,
+      // and every wave the sizes of its own rows for the count term
       {
         const int i = min(tid, S - 1);
         const int o0 = off[g * S + i], o1 = off[g * S + i + 1];
@@ -511,68 +522,70 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
         }
         if (tid == S - 1) lds_off[S] = o1;
       }
-      int rc[G];
-      if (a.sel_s) {
+      int rcnt[RPW];
 #pragma unroll
-        for (int h = 0; h < G; ++h) rc[h] = a.ws.cl_rank[cg * G + h];
+      for (int k = 0; k < RPW; ++k) {
+        const int i = min(wave + 4 * k, S - 1);
+        rcnt[k] = off[g * S + i + 1] - off[g * S + i];
       }
+      if (tid < kMaxS) lds_sm[tid] = 0u;
+      // full scores (count term added; -inf for an empty subcluster and for
+      // the rows past S, so the ranking below runs over all kMaxS rows)
 #pragma unroll
       for (int k = 0; k < RPW; ++k) {
         const int i = wave + 4 * k;
-        if (i >= S) break;
+        if (i >= S) {
+          if (lane < G) lds_sc[i][lane] = -INFINITY;
+          continue;
+        }
+        const int cnt = uni(rcnt[k]);
+        const float lc = cnt > 0 ? log2f((float)cnt) : 0.f;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           float t = 0.f;
 #pragma unroll
           for (int e = 0; e < EPL; ++e) t += coef[h][e] * xr[k][e];
           t = wave_sum_uniform(t);
-          if (lane == 0) lds_sc[i][h] = t;
+          if (lane == 0) lds_sc[i][h] = cnt > 0 ? t + lc : -INFINITY;
         }
       }
-      if (tid < kMaxS) lds_sm[tid] = 0u;
       __syncthreads();
-      // full scores (count term added; -inf for an empty subcluster)
-      // (rows past S are set to -inf too, so the rank loop below runs over
-      // all kMaxS rows without a branch)
-      if (tid < kMaxS * G) {
-        const int i = tid / G, h = tid % G;
-        const int cnt = i < S ? lds_cnt[i] : 0;
-        lds_sc[i][h] = cnt > 0 ? lds_sc[i][h] + log2f((float)cnt) : -INFINITY;
-      }
-      __syncthreads();
-      // top-s of each choosing head: wave w handles heads w, w+4
-      const int my_cnt = lane < S ? lds_cnt[lane] : 0;
-      const bool valid = lane < S && my_cnt > 0;
+      // top-s of every choosing head at once: thread (i, h) ranks subcluster
+      // i's score among head h's (ties to the lower index)
       const int s_keep = s_keep_raw < 0 ? 0 : s_keep_raw;
-#pragma unroll
-      for (int h0 = 0; h0 < G; h0 += 4) {
-        const int h = h0 + wave;
-        if (h >= G || !((mask >> h) & 1u)) continue;
-        const float my = valid ? lds_sc[lane][h] : -INFINITY;
-        // all scores first, then a branch-free count (bitwise, not
-        // short-circuit, operators)
+      const int ti = tid / G, th = tid % G;
+      bool tsel = false;
+      if (tid < kMaxS * G) {
+        const float my = lds_sc[ti][th];
         float osc[kMaxS];
 #pragma unroll
-        for (int j = 0; j < kMaxS; ++j) osc[j] = lds_sc[j][h];
+        for (int j = 0; j < kMaxS; ++j) osc[j] = lds_sc[j][th];
+        // branch-free count (bitwise, not short-circuit, operators)
         int rank = 0;
 #pragma unroll
         for (int j = 0; j < kMaxS; ++j)
-          rank += (int)((osc[j] != -INFINITY) & ((osc[j] > my) | ((osc[j] == my) & (j < lane))));
-        const bool sel = valid && rank < s_keep;
-        if (sel) atomicOr(&lds_sm[lane], 1u << h);
-        if (a.sel_s) {
-          const unsigned long long bal = __ballot(sel);
-          int rch = rc[0];
-#pragma unroll
-          for (int hh = 1; hh < G; ++hh) rch = hh == h ? rc[hh] : rch;
-          const int hq = U.kv_head * G + h;
-          const int64_t base = (((int64_t)U.seq * a.Hq + hq) * a.c_stride + rch) * a.s_stride;
-          if (sel) a.sel_s[base + __popcll(bal & ((1ull << lane) - 1ull))] = lane;
-          for (int j = __popcll(bal) + lane; j < a.s_stride; j += 64) a.sel_s[base + j] = -1;
-        }
+          rank += (int)((osc[j] != -INFINITY) & ((osc[j] > my) | ((osc[j] == my) & (j < ti))));
+        tsel = my != -INFINITY && ((mask >> th) & 1u) && rank < s_keep;
+        if (tsel) atomicOr(&lds_sm[ti], 1u << th);
       }
       __syncthreads();
-      if (tid < S) a.ws.sub_mask[sg0 + tid] = lds_sm[tid];
+      if (a.sel_s && tid < kMaxS * G && ((mask >> th) & 1u)) {
+        // selection output: the head's chosen subclusters in index order,
+        // under the cluster's rank for the head, then -1
+        const int rch = a.ws.cl_rank[cg * G + th];
+        const int hq = U.kv_head * G + th;
+        const int64_t base = (((int64_t)U.seq * a.Hq + hq) * a.c_stride + rch) * a.s_stride;
+        int before = 0, all_h = 0;
+        for (int j = 0; j < kMaxS; ++j) {
+          const int bit = (int)((lds_sm[j] >> th) & 1u);
+          before += j < ti ? bit : 0;
+          all_h += bit;
+        }
+        if (tsel) a.sel_s[base + before] = ti;
+        if (ti == 0)
+          for (int j = all_h; j < a.s_stride; ++j) a.sel_s[base + j] = -1;
+      }
+      const int my_cnt = lane < S ? lds_cnt[lane] : 0;
       if (wave == 0) {
         int rows = (lane < S && lds_sm[lane]) ? my_cnt : 0;
 #pragma unroll
@@ -608,11 +621,11 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
         }
         const int n_tiles = __shfl(incl, 63, 64);
         if (head) {
-          TileRec* dstt = a.ws.tiles + tile_unit_base(U.row_base, U.cl_base, u) + tb_x + (incl - ntl);
+          TileRec* dstt = a.ws.tiles + tile_unit_base(U.row_base, U.cl_base, u) + uni(tb_x) + (incl - ntl);
           for (int r = st; r < run_en; r += 32, ++dstt)
             *dstt = TileRec{(U.row_base + r) * (int64_t)a.L_head_dim, min(32, run_en - r), m};
         }
-        if (lane == 0) a.ws.ch_ntiles[U.cl_base + x] = n_tiles;
+        if (lane == 0) a.ws.ch_ntiles[cw + x] = n_tiles;
       }
       // residual of the subclusters a choosing head left out: wave w takes
       // subclusters w, w+4, ...
@@ -638,17 +651,17 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
     // -------- residual of clusters left out, 4 clusters per wave ------------
     // every load of the wave's 4 clusters is issued before any is used
     // (clusters past C re-read the last one and are skipped)
-    const int y = blockIdx.x - nb_chosen;
+    const int y = x - nb_chosen;
     uint32_t mask[4];
     int n_g[4];
     float vb[4][VPL], sc[4][G];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int g = min(y * 16 + wave * 4 + k, C - 1);
-      const int64_t cg = U.cl_base + g;
+      const int64_t cg = cw + g;
       mask[k] = a.ws.cl_mask[cg];
       n_g[k] = off[(g + 1) * S] - off[g * S];
-      load_floats<VPL>(a.L.cl_vbar + cg * D + lane * VPL, vb[k]);
+      load_floats<VPL>(a.L.cl_vbar + (U.cl_base + g) * D + lane * VPL, vb[k]);
 #pragma unroll
       for (int h = 0; h < G; ++h) sc[k][h] = a.ws.cl_score[cg * G + h];
     }
@@ -779,17 +792,26 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
   u32x4* buf = kvbuf[wave];
   Engine acc;
   acc.init(a.q + ((int64_t)U.seq * a.Hq + (int64_t)U.kv_head * G) * D, a.scale_l2, buf);
-  // tile counts of the chosen clusters (in list order) -> exclusive prefix
+  // tile counts of the chosen clusters (in list order) -> exclusive prefix.
+  // A list of up to 256 clusters (the usual case) takes one entry per
+  // thread, loaded without waiting for the list length; a longer one E each.
+  const int64_t cw = (int64_t)u * a.cstride;
   const int n_ch = uni(a.ws.n_chosen[u]);
   {
     constexpr int EM = kMaxC / 256;
-    const int E = (n_ch + 255) / 256;
     int loc[EM], tbl[EM];
+    loc[0] = a.ws.ch_ntiles[cw + min(tid, a.cstride - 1)];
+    tbl[0] = a.ws.ch_tbase[cw + min(tid, a.cstride - 1)];
 #pragma unroll
-    for (int k = 0; k < EM; ++k) {
-      const int x = min(tid * E + k, C - 1);
-      loc[k] = a.ws.ch_ntiles[U.cl_base + x];
-      tbl[k] = a.ws.ch_tbase[U.cl_base + x];
+    for (int k = 1; k < EM; ++k) loc[k] = tbl[k] = 0;
+    const int E = (n_ch + 255) / 256;
+    if (E > 1) {
+#pragma unroll
+      for (int k = 0; k < EM; ++k) {
+        const int x = min(tid * E + k, a.cstride - 1);
+        loc[k] = a.ws.ch_ntiles[cw + x];
+        tbl[k] = a.ws.ch_tbase[cw + x];
+      }
     }
     int sum = 0;
 #pragma unroll
@@ -1106,7 +1128,7 @@ static hipError_t decode_impl(const DecodeLaunch& x, const DArgs& a, const Budge
     hipLaunchKernelGGL((k_select_topc<G, 16>), dim3(nu), dim3(64 * G), 0, s, a, b);
   else
     hipLaunchKernelGGL((k_select_topc<G, kMaxC / 64>), dim3(nu), dim3(64 * G), 0, s, a, b);
-  hipLaunchKernelGGL((k_subclusters<D, G>), dim3(x.nb_res, nu), dim3(256), 0, s, a, b, x.nb_chosen);
+  hipLaunchKernelGGL((k_subclusters<D, G>), dim3(nu, x.nb_res), dim3(256), 0, s, a, b, x.nb_chosen);
   if (x.ev_begin) {
     const hipError_t e = hipEventRecord(x.ev_begin, s);
     if (e != hipSuccess) return e;
@@ -1168,6 +1190,7 @@ hipError_t launch_decode(const DecodeLaunch& x, hipStream_t s) {
   a.nb_res = x.nb_res;
   a.n_units = x.L.n_units;
   a.nblk = x.nblk;
+  a.cstride = x.L.max_C;
   a.scale_l2 = x.scale * kLog2e;
   a.half_s2_l2 = 0.5f * x.scale * x.scale * kLog2e;
   a.L_head_dim = x.D;

@@ -104,21 +104,22 @@ __host__ __device__ inline int64_t tile_unit_base(int64_t row_base, int64_t cl_b
   return cl_base * (kMaxS + 1) + (row_base >> 5) + u;
 }
 
+// Per-cluster entries of unit u start at u * max_C (the largest C of the
+// layout), so a kernel can address them from the unit index alone.
 struct DecodeWS {
-  float* cl_score;      // [total_cl][G]      log2-domain scores
-  uint32_t* cl_mask;    // [total_cl]         heads that chose the cluster
-  int32_t* cl_rank;     // [total_cl][G]      rank among a head's chosen clusters, or -1
-                        //                    (written only when sel_s is requested)
-  uint32_t* sub_mask;   // [total_sub]        heads that chose the subcluster
-  int32_t* unit_rows;   // [n_units]          rows of chosen subclusters per unit
-  int32_t* cl_list;     // [total_cl]         per unit (at cl_base): chosen clusters, ascending
-  int32_t* n_chosen;    // [n_units]          length of the unit's list
-  int32_t* uinfo;       // [n_units][2]       first exact block of the unit, its blocks
-  int32_t* ch_tbase;    // [total_cl]         per unit (at cl_base): tile-slot base of the x-th chosen cluster
-  int32_t* ch_ntiles;   // [total_cl]         per unit (at cl_base): tiles of the x-th chosen cluster
-  TileRec* tiles;       // [tile slots]       exact tiles, per unit at tile_unit_base()
+  float* cl_score;      // [n_units * max_C][G]  log2-domain scores
+  uint32_t* cl_mask;    // [n_units * max_C]     heads that chose the cluster
+  int32_t* cl_rank;     // [n_units * max_C][G]  rank among a head's chosen clusters, or -1
+                        //                       (written only when sel_s is requested)
+  int32_t* unit_rows;   // [n_units]             rows of chosen subclusters per unit
+  int32_t* cl_list;     // [n_units * max_C]     per unit: chosen clusters, ascending
+  int32_t* n_chosen;    // [n_units]             length of the unit's list
+  int32_t* uinfo;       // [n_units][2]          first exact block of the unit, its blocks
+  int32_t* ch_tbase;    // [n_units * max_C]     per unit: tile-slot base of the x-th chosen cluster
+  int32_t* ch_ntiles;   // [n_units * max_C]     per unit: tiles of the x-th chosen cluster
+  TileRec* tiles;       // [tile slots]          exact tiles, per unit at tile_unit_base()
   float* res_part;      // [n_units][nb_res][G][D+4] residual partials
-  float* ex_part;       // [nblk][G][D+4]     exact-attention block records
+  float* ex_part;       // [nblk][G][D+4]        exact-attention block records
 };
 
 struct DecodeLaunch {
