@@ -470,14 +470,17 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
   // the x-th chosen cluster needs only the unit index: its loads go out with
   // the unit record's
   const int x = blockIdx.y;
-  int n_ch = 0, g_x = 0, tb_x = 0;
+  const int n_ch_raw = a.ws.n_chosen[u];
+  int g_x = 0, tb_x = 0;
   if (x < nb_chosen) {
-    n_ch = a.ws.n_chosen[u];
     g_x = a.ws.cl_list[cw + x];
     tb_x = a.ws.ch_tbase[cw + x];
   }
   const mog_unit U = uni_unit(a.L.units + u);
-  const int S = U.S, C = U.C;
+  const int S = U.S, C = U.C, n_ch = uni(n_ch_raw);
+  // the unit's records: one per chosen cluster, then one per rest block;
+  // slots past them (no such cluster in this unit) leave at once
+  if (x < nb_chosen ? x >= n_ch : (x - nb_chosen) * kRestClustersPerBlock >= C) return;
   const uint32_t all = (1u << G) - 1u;
   const int32_t* off = a.L.sub_off + U.off_base;
   float rm[G], rl[G], ro[G][VPL];
@@ -488,13 +491,13 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
 #pragma unroll
     for (int e = 0; e < VPL; ++e) ro[h][e] = 0.f;
   }
-  float* dst = a.ws.res_part + ((int64_t)u * a.nb_res + x) * G * RS;
+  float* dst = a.ws.res_part + ((int64_t)u * a.nb_res + (x < nb_chosen ? x : n_ch + x - nb_chosen)) * G * RS;
 
   if (x < nb_chosen) {
     // -------- the x-th chosen cluster ---------------------------------------
     // (x < nb_chosen <= the largest C, so the list entries are in range)
-    const int g = x < uni(n_ch) ? uni(g_x) : -1;
-    if (g >= 0) {
+    const int g = uni(g_x);
+    {
       const int64_t cg = cw + g;
       const int64_t sg0 = U.sub_base + (int64_t)g * S;
       const uint32_t mask = a.ws.cl_mask[cg];
@@ -587,10 +590,9 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
       }
       const int my_cnt = lane < S ? lds_cnt[lane] : 0;
       if (wave == 0) {
-        int rows = (lane < S && lds_sm[lane]) ? my_cnt : 0;
-#pragma unroll
-        for (int o2 = 1; o2 < 64; o2 <<= 1) rows += __shfl_xor(rows, o2, 64);
-        if (lane == 0) atomicAdd(&a.ws.unit_rows[u], rows);
+        const uint32_t rows = (lane < S && lds_sm[lane]) ? (uint32_t)my_cnt : 0u;
+        const int rsum = (int)wave_reduce_uniform(rows, [](uint32_t p, uint32_t q) { return p + q; }, 0u);
+        if (lane == 0) atomicAdd(&a.ws.unit_rows[u], rsum);
         // exact tiles of the cluster: a run is a maximal sequence of chosen
         // nonempty subclusters with one head mask whose rows are contiguous
         // (lane i: subcluster i); each run is cut into tiles of <= 32 rows,
@@ -613,13 +615,8 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
         const int last = in_run ? 63 - __clzll((long long)in_run) : 0;
         const int run_en = __shfl(en, last, 64);
         const int ntl = head ? (run_en - st + 31) / 32 : 0;
-        int incl = ntl;
-#pragma unroll
-        for (int o2 = 1; o2 < 64; o2 <<= 1) {
-          const int y = __shfl_up(incl, o2, 64);
-          if (lane >= o2) incl += y;
-        }
-        const int n_tiles = __shfl(incl, 63, 64);
+        const int incl = wave_incl_scan(ntl);
+        const int n_tiles = __builtin_amdgcn_readlane(incl, 63);
         if (head) {
           TileRec* dstt = a.ws.tiles + tile_unit_base(U.row_base, U.cl_base, u) + uni(tb_x) + (incl - ntl);
           for (int r = st; r < run_en; r += 32, ++dstt)
@@ -648,16 +645,17 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
       }
     }
   } else {
-    // -------- residual of clusters left out, 4 clusters per wave ------------
-    // every load of the wave's 4 clusters is issued before any is used
+    // -------- residual of clusters left out, RCW clusters per wave -----------
+    // every load of the wave's clusters is issued before any is used
     // (clusters past C re-read the last one and are skipped)
+    constexpr int RCW = kRestClustersPerBlock / 4;
     const int y = x - nb_chosen;
-    uint32_t mask[4];
-    int n_g[4];
-    float vb[4][VPL], sc[4][G];
+    uint32_t mask[RCW];
+    int n_g[RCW];
+    float vb[RCW][VPL], sc[RCW][G];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int g = min(y * 16 + wave * 4 + k, C - 1);
+    for (int k = 0; k < RCW; ++k) {
+      const int g = min(y * kRestClustersPerBlock + wave * RCW + k, C - 1);
       const int64_t cg = cw + g;
       mask[k] = a.ws.cl_mask[cg];
       n_g[k] = off[(g + 1) * S] - off[g * S];
@@ -666,8 +664,8 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
       for (int h = 0; h < G; ++h) sc[k][h] = a.ws.cl_score[cg * G + h];
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int g = y * 16 + wave * 4 + k;
+    for (int k = 0; k < RCW; ++k) {
+      const int g = y * kRestClustersPerBlock + wave * RCW + k;
       if (g >= C) break;
       const uint32_t unchosen = n_g[k] > 0 ? (all & ~mask[k]) : 0u;
       if (unchosen && a.residual) {
@@ -953,7 +951,8 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(1024) void k_merge(const float* part, int n_part, const int32_t* uinfo,
-                                                const float* res, int n_res, int G, int Hq, int Hkv, float* out,
+                                                const float* res, int res_stride, const int32_t* n_chosen,
+                                                const mog_unit* units, int G, int Hq, int Hkv, float* out,
                                                 float* lse) {
   constexpr int RS = D + kPartPad;
   constexpr int QL = D / 4;        // lanes per record (4 elements each)
@@ -970,7 +969,11 @@ __global__ __launch_bounds__(1024) void k_merge(const float* part, int n_part, c
   }
   const int64_t stride = (int64_t)G * RS;
   const float* eb = part + (first * G + h) * RS;
-  const float* rb = res ? res + ((int64_t)u * n_res * G + h) * RS : nullptr;
+  // residual records of the unit: one per chosen cluster, then one per
+  // kRestClustersPerBlock clusters
+  int n_res = 0;
+  if (res) n_res = n_chosen[u] + (units[u].C + kRestClustersPerBlock - 1) / kRestClustersPerBlock;
+  const float* rb = res ? res + ((int64_t)u * res_stride * G + h) * RS : nullptr;
   const int total = n_part + (res ? n_res : 0);
   const int q = tid % QL, grp = tid / QL;
   float m = -INFINITY, l = 0.f;
@@ -1143,8 +1146,9 @@ static hipError_t decode_impl(const DecodeLaunch& x, const DArgs& a, const Budge
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((k_merge<D>), dim3(x.Hq, x.L.n_seq), dim3(1024), 0, s, a.ws.ex_part, 0,
-                     (const int32_t*)a.ws.uinfo, x.residual ? (const float*)a.ws.res_part : nullptr, x.nb_res, G,
-                     x.Hq, x.L.n_kv_heads, x.out, x.lse);
+                     (const int32_t*)a.ws.uinfo, x.residual ? (const float*)a.ws.res_part : nullptr, x.nb_res,
+                     (const int32_t*)a.ws.n_chosen, (const mog_unit*)x.L.units, G, x.Hq, x.L.n_kv_heads, x.out,
+                     x.lse);
   return hipGetLastError();
 }
 
@@ -1222,7 +1226,8 @@ static hipError_t dense_impl(const DenseLaunch& x, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((k_merge<D>), dim3(x.Hq, x.seq.n_seq), dim3(1024), 0, s, x.ex_part, x.splits,
-                     (const int32_t*)nullptr, (const float*)nullptr, 0, G, x.Hq, x.n_kv_heads, x.out, x.lse);
+                     (const int32_t*)nullptr, (const float*)nullptr, 0, (const int32_t*)nullptr,
+                     (const mog_unit*)nullptr, G, x.Hq, x.n_kv_heads, x.out, x.lse);
   return hipGetLastError();
 }
 

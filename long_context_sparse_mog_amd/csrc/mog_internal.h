@@ -118,7 +118,8 @@ struct DecodeWS {
   int32_t* ch_tbase;    // [n_units * max_C]     per unit: tile-slot base of the x-th chosen cluster
   int32_t* ch_ntiles;   // [n_units * max_C]     per unit: tiles of the x-th chosen cluster
   TileRec* tiles;       // [tile slots]          exact tiles, per unit at tile_unit_base()
-  float* res_part;      // [n_units][nb_res][G][D+4] residual partials
+  float* res_part;      // [n_units][nb_res][G][D+4] residual partials: one per chosen
+                        //                       cluster, then one per rest block
   float* ex_part;       // [nblk][G][D+4]        exact-attention block records
 };
 
@@ -136,7 +137,7 @@ struct DecodeLaunch {
   int32_t residual;
   int32_t splits;       // target exact blocks in total (balanced over units)
   int32_t nblk;         // exact blocks launched: splits + n_units
-  int32_t nb_res;       // residual records per unit: nb_chosen + clusters/16
+  int32_t nb_res;       // residual record slots per unit: nb_chosen + max_C / kRestClustersPerBlock
   int32_t nb_chosen;    // chosen-cluster blocks per unit (max G * top_c)
   float scale;
   hipEvent_t ev_begin, ev_end;  // optional, around the exact kernel
@@ -156,7 +157,7 @@ struct DenseLaunch {
   float* ex_part;       // [n_units][splits][G][D+4]
 };
 
-constexpr int kRestClustersPerBlock = 16;  // residual-only blocks: 4 clusters per wave
+constexpr int kRestClustersPerBlock = 32;  // residual-only blocks: 8 clusters per wave
 constexpr int kPartPad = 4;
 // blocks of the exact-attention kernel resident at once on the chip: 256
 // compute units x 2 (its registers allow 2 waves per SIMD)
