@@ -171,31 +171,33 @@ __device__ inline void score_rows(const float (&x)[R][D / 32], const float (&coe
 //    scale^2/2 sum_i q_{h,i}^2 var_{g,i}); -inf for an empty cluster.
 //    Grid (ceil(maxC/16), units); each wave loads 4 cluster rows at once.
 // ---------------------------------------------------------------------------
+constexpr int kScoreRowsPerWave = 4;  // clusters scored per wave (16 per block)
+
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_score_clusters(DArgs a) {
   constexpr int EPL = D / 32;
   const int u = blockIdx.y;
   const mog_unit U = uni_unit(a.L.units + u);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g0 = blockIdx.x * 16 + wave * 4;
+  const int g0 = blockIdx.x * (4 * kScoreRowsPerWave) + wave * kScoreRowsPerWave;
   if (g0 >= U.C) return;
   const float* qb = a.q + ((int64_t)U.seq * a.Hq + (int64_t)U.kv_head * G) * D;
   float coef[G][EPL];
   score_coefs<D, G>(a, qb, coef);
   const int32_t* off = a.L.sub_off + U.off_base;
-  float x[4][EPL];
+  float x[kScoreRowsPerWave][EPL];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < kScoreRowsPerWave; ++k) {
     const int g = min(g0 + k, U.C - 1);
     load_floats<EPL>(a.L.cl_ms + (U.cl_base + g) * (2 * D) + lane * EPL, x[k]);
   }
   float mine[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) mine[h] = 0.f;
-  score_rows<D, G, 4>(x, coef, lane, mine);
-  // lane k (< 4) now holds the scores of cluster g0 + k
+  score_rows<D, G, kScoreRowsPerWave>(x, coef, lane, mine);
+  // lane k (< kScoreRowsPerWave) now holds the scores of cluster g0 + k
   const int g = g0 + lane;
-  if (lane < 4 && g < U.C) {
+  if (lane < kScoreRowsPerWave && g < U.C) {
     const int64_t cw = (int64_t)u * a.cstride + g;
     const int n = off[(g + 1) * U.S] - off[g * U.S];
     const float lg = n > 0 ? log2f((float)n) : -INFINITY;
@@ -504,15 +506,12 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
       const float* qb = a.q + ((int64_t)U.seq * a.Hq + (int64_t)U.kv_head * G) * D;
       float coef[G][EPL];
       score_coefs<D, G>(a, qb, coef);
-      // scores: wave w takes rows w, w+4, ...; the value means of the same
-      // rows are loaded alongside for the residual below
+      // scores: wave w takes rows w, w+4, ...
       float xr[RPW][EPL];
-      float vb[RPW][VPL];
 #pragma unroll
       for (int k = 0; k < RPW; ++k) {
         const int i = min(wave + 4 * k, S - 1);
         load_floats<EPL>(a.L.sub_ms + (sg0 + i) * (2 * D) + lane * EPL, xr[k]);
-        if (a.residual) load_floats<VPL>(a.L.sub_vbar + (sg0 + i) * D + lane * VPL, vb[k]);
       }
       // subcluster bounds: thread i < S keeps subcluster i's for the tiles,
       // and every wave the sizes of its own rows for the count term
@@ -572,6 +571,14 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
         if (tsel) atomicOr(&lds_sm[ti], 1u << th);
       }
       __syncthreads();
+      // the value means of the same rows, for the residual below (issued
+      // now, so their registers are not held through the ranking)
+      float vb[RPW][VPL];
+      if (a.residual) {
+#pragma unroll
+        for (int k = 0; k < RPW; ++k)
+          load_floats<VPL>(a.L.sub_vbar + (sg0 + min(wave + 4 * k, S - 1)) * D + lane * VPL, vb[k]);
+      }
       if (a.sel_s && tid < kMaxS * G && ((mask >> th) & 1u)) {
         // selection output: the head's chosen subclusters in index order,
         // under the cluster's rank for the head, then -1
@@ -1122,7 +1129,8 @@ hipError_t launch_layout_table(const mog_layout& L, const SeqArgs& seq, hipStrea
 template <int D, int G>
 static hipError_t decode_impl(const DecodeLaunch& x, const DArgs& a, const BudgetArgs& b, hipStream_t s) {
   const int nu = x.L.n_units;
-  hipLaunchKernelGGL((k_score_clusters<D, G>), dim3((x.L.max_C + 15) / 16, nu), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_score_clusters<D, G>), dim3((x.L.max_C + 4 * kScoreRowsPerWave - 1) / (4 * kScoreRowsPerWave), nu),
+                     dim3(256), 0, s, a);
   if (x.L.max_C <= 256)
     hipLaunchKernelGGL((k_select_topc<G, 4>), dim3(nu), dim3(64 * G), 0, s, a, b);
   else if (x.L.max_C <= 512)
