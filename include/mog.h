@@ -165,6 +165,12 @@ typedef struct {
   hipEvent_t exact_begin;       /* optional (NULL: unused): recorded on the    */
   hipEvent_t exact_end;         /* stream right before / after the exact-      */
                                 /* attention kernel, for timing it alone       */
+  int32_t exact_repeat;         /* timing aid: 0 or 1 launches the exact-      */
+                                /* attention kernel once; n in 2..64 launches  */
+                                /* it n times back to back between the two     */
+                                /* events (each launch redoes the same work,   */
+                                /* results are unchanged), so the events' own  */
+                                /* overhead is spread over n launches          */
 } mog_decode_params;
 
 typedef enum { MOG_OP_BUILD = 0, MOG_OP_DECODE = 1, MOG_OP_DENSE = 2 } mog_op;

@@ -180,6 +180,8 @@ mog_status check_decode_params(const mog_decode_params* p, int n_kv_heads, int n
   const int G = p->n_q_heads / n_kv_heads;
   if (G > kMaxG) return fail(MOG_ERR_UNSUPPORTED, "%d query heads per KV head (max %d)", G, kMaxG);
   if (p->splits < 0 || p->splits > 8192) return fail(MOG_ERR_INVALID_ARG, "splits=%d outside [0, 8192]", p->splits);
+  if (p->exact_repeat < 0 || p->exact_repeat > 64)
+    return fail(MOG_ERR_INVALID_ARG, "exact_repeat=%d outside [0, 64]", p->exact_repeat);
   if (!(p->scale >= 0.f) || isinf(p->scale)) return fail(MOG_ERR_INVALID_ARG, "scale must be finite and >= 0");
   for (int s = 0; s < n_seq; ++s) {
     const int c = seq_top(p->top_c_per_seq, p->top_c, s);
@@ -510,6 +512,7 @@ mog_status mog_decode(const mog_layout* layout, const mog_kv* kv, const float* q
   x.scale = params->scale > 0.f ? params->scale : 1.0f / sqrtf((float)kv->head_dim);
   x.ev_begin = params->exact_begin;
   x.ev_end = params->exact_end;
+  x.repeat = std::max(1, params->exact_repeat);
   char* w = static_cast<char*>(ws);
   x.ws.cl_score = reinterpret_cast<float*>(w + d.o_clscore);
   x.ws.cl_mask = reinterpret_cast<uint32_t*>(w + d.o_clmask);
@@ -554,6 +557,7 @@ mog_status mog_dense_decode(const mog_kv* kv, const float* q, const mog_decode_p
   x.scale = params->scale > 0.f ? params->scale : 1.0f / sqrtf((float)kv->head_dim);
   x.ev_begin = params->exact_begin;
   x.ev_end = params->exact_end;
+  x.repeat = std::max(1, params->exact_repeat);
   x.ex_part = reinterpret_cast<float*>(static_cast<char*>(ws) + d.o_ex);
   hipError_t e = launch_dense(x, stream);
   if (e != hipSuccess) return fail(MOG_ERR_HIP, "dense launch: %s", hipGetErrorString(e));

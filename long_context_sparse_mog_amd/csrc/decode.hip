@@ -1144,10 +1144,12 @@ static hipError_t decode_impl(const DecodeLaunch& x, const DArgs& a, const Budge
     const hipError_t e = hipEventRecord(x.ev_begin, s);
     if (e != hipSuccess) return e;
   }
-  if (x.dtype == MOG_BF16) {
-    hipLaunchKernelGGL((k_exact<D, G, MfmaTile<D, G>, uint16_t>), dim3(x.nblk), dim3(256), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((k_exact<D, G, RowAcc<D, G>, float>), dim3(x.nblk), dim3(256), 0, s, a);
+  for (int r = 0; r < x.repeat; ++r) {
+    if (x.dtype == MOG_BF16) {
+      hipLaunchKernelGGL((k_exact<D, G, MfmaTile<D, G>, uint16_t>), dim3(x.nblk), dim3(256), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((k_exact<D, G, RowAcc<D, G>, float>), dim3(x.nblk), dim3(256), 0, s, a);
+    }
   }
   if (x.ev_end) {
     const hipError_t e = hipEventRecord(x.ev_end, s);
@@ -1222,12 +1224,14 @@ static hipError_t dense_impl(const DenseLaunch& x, hipStream_t s) {
     const hipError_t e = hipEventRecord(x.ev_begin, s);
     if (e != hipSuccess) return e;
   }
-  if (x.dtype == MOG_BF16) {
-    hipLaunchKernelGGL((k_dense<D, G, MfmaTile<D, G>, uint16_t>), dim3(x.splits, nu), dim3(256), 0, s, x.kv, x.q,
-                       x.Hq, x.n_kv_heads, x.splits, x.scale * kLog2e, x.seq, x.ex_part);
-  } else {
-    hipLaunchKernelGGL((k_dense<D, G, RowAcc<D, G>, float>), dim3(x.splits, nu), dim3(256), 0, s, x.kv, x.q,
-                       x.Hq, x.n_kv_heads, x.splits, x.scale * kLog2e, x.seq, x.ex_part);
+  for (int r = 0; r < x.repeat; ++r) {
+    if (x.dtype == MOG_BF16) {
+      hipLaunchKernelGGL((k_dense<D, G, MfmaTile<D, G>, uint16_t>), dim3(x.splits, nu), dim3(256), 0, s, x.kv, x.q,
+                         x.Hq, x.n_kv_heads, x.splits, x.scale * kLog2e, x.seq, x.ex_part);
+    } else {
+      hipLaunchKernelGGL((k_dense<D, G, RowAcc<D, G>, float>), dim3(x.splits, nu), dim3(256), 0, s, x.kv, x.q,
+                         x.Hq, x.n_kv_heads, x.splits, x.scale * kLog2e, x.seq, x.ex_part);
+    }
   }
   if (x.ev_end) {
     const hipError_t e = hipEventRecord(x.ev_end, s);

@@ -141,6 +141,7 @@ struct DecodeLaunch {
   int32_t nb_chosen;    // chosen-cluster blocks per unit (max G * top_c)
   float scale;
   hipEvent_t ev_begin, ev_end;  // optional, around the exact kernel
+  int32_t repeat;               // exact-kernel launches between the events (>= 1)
   DecodeWS ws;
 };
 
@@ -154,6 +155,7 @@ struct DenseLaunch {
   int32_t splits;
   float scale;
   hipEvent_t ev_begin, ev_end;  // optional, around the dense kernel
+  int32_t repeat;               // dense-kernel launches between the events (>= 1)
   float* ex_part;       // [n_units][splits][G][D+4]
 };
 

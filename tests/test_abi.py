@@ -146,6 +146,12 @@ def test_decode_and_dense_validation(L):
     p.top_c = -1
     assert L.mog_workspace_size(capi.MOG_OP_DENSE, C.byref(kv), None, None, C.byref(p), C.byref(out)) == capi.MOG_ERR_INVALID_ARG
     p.top_c = 4
+    for bad in (-1, 65):   # timing aid: 0..64 launches
+        p.exact_repeat = bad
+        assert L.mog_workspace_size(capi.MOG_OP_DENSE, C.byref(kv), None, None, C.byref(p), C.byref(out)) == capi.MOG_ERR_INVALID_ARG
+    p.exact_repeat = 64
+    assert L.mog_workspace_size(capi.MOG_OP_DENSE, C.byref(kv), None, None, C.byref(p), C.byref(out)) == capi.MOG_OK
+    p.exact_repeat = 0
     # dense with a NULL q / NULL workspace
     assert L.mog_dense_decode(C.byref(kv), None, C.byref(p), C.c_void_p(0x1000), None, C.c_void_p(0x1000), 1 << 30, None) == capi.MOG_ERR_INVALID_ARG
     assert L.mog_dense_decode(C.byref(kv), C.c_void_p(0x1000), C.byref(p), C.c_void_p(0x1000), None, None, 1 << 30, None) == capi.MOG_ERR_INVALID_ARG
