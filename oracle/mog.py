@@ -47,6 +47,16 @@ in the design notes of the repository):
       than the budget all nonempty ones are chosen.
   R8  Every query head makes its own selection (GQA heads sharing a KV head
       are independent instances).
+  R9  Optional shared selection for the G query heads of a KV head (the
+      DuoAttention review, page 2, "Limitations" and its closing
+      discussion: query heads that share a KV head couple their needs).
+      Each head's group scores are turned into estimated fractions of its
+      attention mass, exp(score - LSE_h) with LSE_h the log-sum-exp of the
+      head's nonempty cluster scores; a cluster's group score is the sum of
+      these fractions over the heads, the subclusters of a chosen cluster
+      are scored the same way (same LSE_h), and every head then uses the one
+      top-c / top-s selection.  The exact read per KV head is then capped at
+      one head's budget.
 """
 
 from __future__ import annotations
@@ -403,8 +413,34 @@ def _softmax_merge(logw, vals):
     return (w @ vals) / den, m + np.log(den)
 
 
+def shared_selection(L: UnitLayout, Q, top_c, top_s, scale=None):
+    """One selection for all query heads of a KV head (reading R9): returns
+    (chosen cluster ids ascending, [chosen subcluster ids ascending per chosen
+    cluster]) and the per-cluster group scores."""
+    Q = np.atleast_2d(np.asarray(Q, dtype=np.float64))
+    G, d = Q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    C, S = L.C, L.S
+    cl_cnt, sub_cnt = L.cl_count, L.sub_count
+    valid = cl_cnt > 0
+    sc = np.stack([group_log_mass(Q[h], cl_cnt, L.cl_mu, L.cl_var, scale) for h in range(G)])
+    lse = np.array([np.logaddexp.reduce(sc[h][valid]) for h in range(G)])
+    gs = np.where(valid, np.exp(sc - lse[:, None]).sum(axis=0), 0.0)
+    chosen = top_by_score(gs, top_c, valid)
+    picks = []
+    for j in chosen:
+        g0 = j * S
+        sv = sub_cnt[g0:g0 + S] > 0
+        ss = np.stack([group_log_mass(Q[h], sub_cnt[g0:g0 + S], L.sub_mu[g0:g0 + S], L.sub_var[g0:g0 + S], scale)
+                       for h in range(G)])
+        gss = np.where(sv, np.exp(ss - lse[:, None]).sum(axis=0), 0.0)
+        picks.append(top_by_score(gss, top_s, sv))
+    return chosen, picks, gs
+
+
 def decode_unit(L: UnitLayout, K, V, Q, top_c, top_s, scale=None, residual=True,
-                sel_override=None):
+                sel_override=None, shared=False):
     """One decode step for the query heads that share one KV head.
 
     K, V: float64 [N][d] of the sequence (anchors are read from here, the
@@ -413,7 +449,8 @@ def decode_unit(L: UnitLayout, K, V, Q, top_c, top_s, scale=None, residual=True,
     ``lse_top`` (exact part only, renormalised), ``sel_c`` (per head, chosen
     cluster ids ascending), ``sel_s`` (per head, per chosen cluster, chosen
     subcluster ids ascending) and ``n_exact`` (rows attended exactly per head).
-    ``sel_override`` = (sel_c, sel_s) replaces the selection.
+    ``sel_override`` = (sel_c, sel_s) replaces the selection; ``shared``
+    takes the one selection of reading R9 for every head.
     """
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
@@ -428,6 +465,9 @@ def decode_unit(L: UnitLayout, K, V, Q, top_c, top_s, scale=None, residual=True,
 
     res = dict(out=np.zeros((G, d)), lse=np.zeros(G), out_top=np.zeros((G, d)),
                lse_top=np.zeros(G), sel_c=[], sel_s=[], n_exact=np.zeros(G, np.int64))
+    if shared and sel_override is None:
+        ch, pk, _ = shared_selection(L, Q, top_c, top_s, scale)
+        sel_override = ([ch] * G, [pk] * G)
     for h in range(G):
         q = Q[h]
         sc = group_log_mass(q, cl_cnt, L.cl_mu, L.cl_var, scale)
@@ -499,7 +539,7 @@ def dense_attention(K, V, Q, scale=None):
 
 
 def decode_batch(layouts, K, V, Q, n_kv_heads, top_c, top_s, scale=None,
-                 residual=True, units=None):
+                 residual=True, units=None, shared=False):
     """Decode every (or the listed) (seq, KV head) unit.
 
     ``layouts[u]`` with u = seq * n_kv_heads + kv_head; ``K[seq][kvh]`` and
@@ -518,7 +558,7 @@ def decode_batch(layouts, K, V, Q, n_kv_heads, top_c, top_s, scale=None,
                 continue
             out[u] = decode_unit(layouts[u], K[seq][kvh], V[seq][kvh],
                                  Q[seq][kvh * G:(kvh + 1) * G], top_c[seq], top_s[seq],
-                                 scale=scale, residual=residual)
+                                 scale=scale, residual=residual, shared=shared)
     return out
 
 

@@ -471,6 +471,120 @@ def test_selection_override_and_top_only():
 
 
 # ---------------------------------------------------------------------------
+# Shared selection per KV head (reading R9)
+# ---------------------------------------------------------------------------
+
+
+def _brute_force_shared(L, K, V, Q, c, s, scale):
+    """Shared selection from plain per-group exponentials: each head's
+    estimated masses exp(score) divided by the head's total over the
+    nonempty clusters, summed over the heads; then every head's output by
+    the literal quotient of sums (selection shared)."""
+    N, C, S = L.N, L.C, L.S
+    cnt_c, cnt_s = L.cl_count, L.sub_count
+    lab_s = L.subcluster_labels()
+    f64 = lambda a: np.asarray(a, dtype=np.float64)
+
+    def mass(q, n, mu, var):
+        return n * math.exp(scale * float(q @ mu) + 0.5 * scale ** 2 * float((q * q) @ var))
+
+    G = Q.shape[0]
+    tot = [sum(mass(Q[h], cnt_c[j], L.cl_mu[j], L.cl_var[j]) for j in range(C) if cnt_c[j]) for h in range(G)]
+    gsc = [(sum(mass(Q[h], cnt_c[j], L.cl_mu[j], L.cl_var[j]) / tot[h] for h in range(G)), j)
+           for j in range(C) if cnt_c[j]]
+    chosen = {j for _, j in sorted(gsc, key=lambda t: (-t[0], t[1]))[:c]}
+    chosen_sub = set()
+    for j in chosen:
+        gss = [(sum(mass(Q[h], cnt_s[g], L.sub_mu[g], L.sub_var[g]) / tot[h] for h in range(G)), g)
+               for g in range(j * S, j * S + S) if cnt_s[g]]
+        chosen_sub |= {g for _, g in sorted(gss, key=lambda t: (-t[0], t[1]))[:s]}
+    outs = []
+    for h in range(G):
+        q = Q[h]
+        num, den = np.zeros(K.shape[1]), 0.0
+        for t in range(N):
+            if not (L.n_sink <= t < N - L.n_recent) or lab_s[t - L.n_sink] in chosen_sub:
+                w = math.exp(scale * float(q @ K[t]))
+                num += w * V[t]
+                den += w
+        for j in range(C):
+            if cnt_c[j] and j not in chosen:
+                w = mass(q, cnt_c[j], L.cl_mu[j], L.cl_var[j])
+                num += w * f64(L.cl_vbar[j])
+                den += w
+        for g in range(C * S):
+            if cnt_s[g] and g // S in chosen and g not in chosen_sub:
+                w = mass(q, cnt_s[g], L.sub_mu[g], L.sub_var[g])
+                num += w * f64(L.sub_vbar[g])
+                den += w
+        outs.append(num / den)
+    return np.array(outs), sorted(chosen), sorted(chosen_sub)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_shared_selection_matches_brute_force_tiny(seed):
+    rng = np.random.default_rng(300 + seed)
+    N, d = 120, 4
+    K = mixture_keys(rng, N, d, 6)
+    V = rng.normal(0, 1, (N, d))
+    L = O.build_unit(K, V, 3, 5, 10, O.unit_state(seed, 0, 0, 1))
+    # heads of very different logit scales: the per-head normalisation is
+    # what keeps one of them from deciding alone
+    Q = rng.normal(0, 1, (3, d)) * np.array([[0.3], [1.5], [4.0]])
+    scale = 0.5
+    for c, s in [(1, 1), (2, 2), (4, 3), (L.C, L.S)]:
+        r = O.decode_unit(L, K, V, Q, c, s, scale=scale, shared=True)
+        out, ch, chs = _brute_force_shared(L, K, V, Q, c, s, scale)
+        assert rel(r["out"], out) < 1e-11
+        for h in range(3):
+            assert list(r["sel_c"][h]) == ch
+            got = sorted(int(j) * L.S + int(i) for j, p in zip(r["sel_c"][h], r["sel_s"][h]) for i in p)
+            assert got == chs
+
+
+def test_shared_selection_single_head_is_per_head():
+    K, V = _small_unit(seed=9)
+    L = O.build_unit(K, V, 4, 16, 10, O.unit_state(2, 0, 0, 1))
+    q = np.random.default_rng(4).normal(0, 1, (1, K.shape[1]))
+    a = O.decode_unit(L, K, V, q, 3, 2)
+    b = O.decode_unit(L, K, V, q, 3, 2, shared=True)
+    assert list(a["sel_c"][0]) == list(b["sel_c"][0])
+    assert all(list(x) == list(y) for x, y in zip(a["sel_s"][0], b["sel_s"][0]))
+    assert rel(b["out"], a["out"]) == 0.0
+
+
+def test_shared_selection_identical_heads_is_per_head():
+    K, V = _small_unit(seed=10)
+    L = O.build_unit(K, V, 4, 16, 10, O.unit_state(3, 0, 0, 1))
+    q = np.random.default_rng(5).normal(0, 1, K.shape[1])
+    Q = np.stack([q, q, q, q])
+    a = O.decode_unit(L, K, V, Q, 3, 2)
+    b = O.decode_unit(L, K, V, Q, 3, 2, shared=True)
+    for h in range(4):
+        assert list(a["sel_c"][h]) == list(b["sel_c"][h])
+    assert rel(b["out"], a["out"]) < 1e-15
+
+
+def test_shared_selection_caps_the_union():
+    K, V = _small_unit(seed=11, N=1500, m=20)
+    L = O.build_unit(K, V, 4, 16, 10, O.unit_state(6, 0, 0, 1))
+    Q = np.random.default_rng(6).normal(0, 1, (5, K.shape[1])) * 2.0
+    c, s = 4, 2
+    per = O.decode_unit(L, K, V, Q, c, s)
+    sh = O.decode_unit(L, K, V, Q, c, s, shared=True)
+    union_c = set().union(*[set(int(j) for j in x) for x in sh["sel_c"]])
+    assert len(union_c) == min(c, int((L.cl_count > 0).sum()))
+    assert all(len(p) <= s for p in sh["sel_s"][0])
+    # subclusters read once for the KV head: at most one head's budget c s
+    # shared; the per-head selections read their union
+    subs = lambda r: set().union(*[set(int(j) * L.S + int(i) for j, p in zip(r["sel_c"][h], r["sel_s"][h]) for i in p)
+                                   for h in range(5)])
+    assert len(subs(sh)) <= c * s
+    assert len(subs(per)) >= max(len(set(int(j) * L.S + int(i) for j, p in zip(per["sel_c"][h], per["sel_s"][h])
+                                         for i in p)) for h in range(5))
+
+
+# ---------------------------------------------------------------------------
 # Dense attention: textbook special cases
 # ---------------------------------------------------------------------------
 
