@@ -119,7 +119,7 @@ def selection_volume(wl, lay, sel_c, sel_s, offs):
                 kv_row_bytes=kv_rows_bytes, step_bytes=kv_rows_bytes + stat_bytes)
 
 
-def bench_workload(idx, steps, warmup, n_qsets, ev, with_errors=True):
+def bench_workload(idx, steps, warmup, n_qsets, ev, with_errors=True, shared_too=False):
     import numpy as np
     import torch
 
@@ -140,10 +140,10 @@ def bench_workload(idx, steps, warmup, n_qsets, ev, with_errors=True):
     out = torch.empty_like(qs[0])
     lse = torch.empty(qs[0].shape[:2], device="cuda")
 
-    def params_with_events(n, residual=True):
+    def params_with_events(n, residual=True, shared=False):
         ps, pairs = [], []
         for _ in range(n):
-            p = ops.decode_params(wl.n_q_heads, list(wl.top_c), list(wl.top_s), residual=residual)
+            p = ops.decode_params(wl.n_q_heads, list(wl.top_c), list(wl.top_s), residual=residual, shared=shared)
             a, z = ev.create(), ev.create()
             p.exact_begin, p.exact_end = a, z
             # the exact kernel runs EXACT_REPEAT times between the events, so
@@ -232,6 +232,29 @@ def bench_workload(idx, steps, warmup, n_qsets, ev, with_errors=True):
         er, et = torch.cat(err_res), torch.cat(err_top)
         res.update(err_vs_dense_residual_mean=float(er.mean()), err_vs_dense_residual_max=float(er.max()),
                    err_vs_dense_toponly_mean=float(et.mean()), err_vs_dense_toponly_max=float(et.max()))
+    if shared_too:
+        # the same step with one selection per KV head (the heads' summed
+        # mass fractions): steps/s, exact kernel, rows read, error vs dense
+        p0s = ops.decode_params(wl.n_q_heads, list(wl.top_c), list(wl.top_s), shared=True)
+        pms, pairs_s = params_with_events(steps, shared=True)
+        ms_s, ex_s = timed(lambda q, p: ops.mog_decode(lay, kv, q, p, out=out, lse=lse, ws=ws), p0s, pms, pairs_s,
+                           steps, warmup)
+        vols_s, err_s = [], []
+        for t in range(n_qsets):
+            o, _, sc, ss = ops.mog_decode(lay, kv, qs[t], p0s, want_sel=True)
+            vols_s.append(selection_volume(wl, lay, sc.cpu().numpy(), ss.cpu().numpy(), offs))
+            if with_errors and t < 4:
+                od, _ = ops.mog_dense_decode(kv, qs[t], pd0)
+                err_s.append((torch.linalg.norm(o - od, dim=-1) / torch.linalg.norm(od, dim=-1)).flatten())
+        mean_s = lambda k: float(np.mean([v[k] for v in vols_s]))
+        res["shared_selection"] = dict(
+            steps_per_s=1000.0 / ms_s, ms_per_step=ms_s, exact_kernel_ms=ex_s,
+            exact_kernel_bytes=mean_s("kv_row_bytes"),
+            exact_kernel_GBps=mean_s("kv_row_bytes") / (ex_s * 1e-3) / 1e9,
+            frac_kv_read_union=mean_s("rows_union") / mean_s("n_tokens"),
+            speedup_vs_dense=dense_ms / ms_s,
+            err_vs_dense_residual_mean=float(torch.cat(err_s).mean()) if err_s else None,
+            err_vs_dense_residual_max=float(torch.cat(err_s).max()) if err_s else None)
     state = dict(wl=wl, b=b, lay=lay, qs=qs, e=e)
     return res, state
 
@@ -378,6 +401,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the 4K, 32K and ragged workloads and the build timing")
+    ap.add_argument("--no-shared", action="store_true",
+                    help="skip the 1M step with one selection per KV head")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 10 times (the reference kernel that "
@@ -399,7 +424,7 @@ def main():
 
     capi.lib()  # fail loudly when the HIP library is missing
     ev = HipEvents()
-    r1m, st1m = bench_workload(3, args.steps, args.warmup, args.qsets, ev)
+    r1m, st1m = bench_workload(3, args.steps, args.warmup, args.qsets, ev, shared_too=not args.no_shared)
     r128 = None
     if not args.no_128k:
         r128, _ = bench_workload(2, args.steps, args.warmup, args.qsets, ev)

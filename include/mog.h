@@ -160,6 +160,14 @@ typedef struct {
                                    exact-attention blocks shared by all units in
                                    proportion to the rows each reads (plus one
                                    per unit); mog_dense_decode: blocks per unit */
+  int32_t shared_selection;     /* 0: every query head selects its own clusters
+                                   and subclusters; 1: one selection per KV
+                                   head, by the sum over its query heads of
+                                   each head's estimated mass fraction
+                                   exp(score - LSE_head) (DuoAttention review,
+                                   page 2, Limitations: heads sharing a KV head
+                                   couple their needs); the exact read per KV
+                                   head is then capped at one head's budget   */
   const int32_t* top_c_per_seq; /* HOST [n_seq] or NULL (then top_c)           */
   const int32_t* top_s_per_seq; /* HOST [n_seq] or NULL (then top_s)           */
   hipEvent_t exact_begin;       /* optional (NULL: unused): recorded on the    */

@@ -58,7 +58,8 @@ class mog_build_params(C.Structure):
 
 class mog_decode_params(C.Structure):
     _fields_ = [("n_q_heads", i32), ("top_c", i32), ("top_s", i32), ("residual", i32),
-                ("scale", C.c_float), ("splits", i32), ("top_c_per_seq", C.POINTER(i32)),
+                ("scale", C.c_float), ("splits", i32), ("shared_selection", i32),
+                ("top_c_per_seq", C.POINTER(i32)),
                 ("top_s_per_seq", C.POINTER(i32)), ("exact_begin", vp), ("exact_end", vp),
                 ("exact_repeat", i32)]
 

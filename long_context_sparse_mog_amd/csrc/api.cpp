@@ -167,7 +167,7 @@ KVRef make_kvref(const mog_kv* kv) {
 // ------------------------------------------------------------------------
 struct DecodePlan {
   int G, c_stride, s_stride, splits, nblk, nb_res, nb_chosen;
-  size_t o_clscore, o_clmask, o_clrank, o_urows, o_list, o_nch, o_uinfo, o_tbase, o_ntl, o_tiles, o_res, o_ex, bytes;
+  size_t o_clscore, o_cllse, o_clmask, o_clrank, o_urows, o_list, o_nch, o_uinfo, o_tbase, o_ntl, o_tiles, o_res, o_ex, bytes;
 };
 
 int seq_top(const int32_t* per, int dflt, int s) { return per ? per[s] : dflt; }
@@ -180,6 +180,8 @@ mog_status check_decode_params(const mog_decode_params* p, int n_kv_heads, int n
   const int G = p->n_q_heads / n_kv_heads;
   if (G > kMaxG) return fail(MOG_ERR_UNSUPPORTED, "%d query heads per KV head (max %d)", G, kMaxG);
   if (p->splits < 0 || p->splits > 8192) return fail(MOG_ERR_INVALID_ARG, "splits=%d outside [0, 8192]", p->splits);
+  if (p->shared_selection != 0 && p->shared_selection != 1)
+    return fail(MOG_ERR_INVALID_ARG, "shared_selection=%d (0 or 1)", p->shared_selection);
   if (p->exact_repeat < 0 || p->exact_repeat > 64)
     return fail(MOG_ERR_INVALID_ARG, "exact_repeat=%d outside [0, 64]", p->exact_repeat);
   if (!(p->scale >= 0.f) || isinf(p->scale)) return fail(MOG_ERR_INVALID_ARG, "scale must be finite and >= 0");
@@ -223,6 +225,7 @@ DecodePlan plan_decode(const mog_layout* L, const mog_decode_params* p) {
   // u * max_C and kernels can address them before reading the unit table
   const size_t ncw = (size_t)nu * L->max_C;
   d.o_clscore = o; o = align_up(o + ncw * G * 4);
+  d.o_cllse = o; o = align_up(o + (size_t)nu * G * 4);
   d.o_clmask = o; o = align_up(o + ncw * 4);
   d.o_clrank = o; o = align_up(o + ncw * G * 4);
   d.o_urows = o; o = align_up(o + (size_t)nu * 4);
@@ -505,6 +508,7 @@ mog_status mog_decode(const mog_layout* layout, const mog_kv* kv, const float* q
   x.D = kv->head_dim;
   x.dtype = kv->dtype;
   x.residual = params->residual ? 1 : 0;
+  x.shared = params->shared_selection;
   x.splits = d.splits;
   x.nblk = d.nblk;
   x.nb_res = d.nb_res;
@@ -515,6 +519,7 @@ mog_status mog_decode(const mog_layout* layout, const mog_kv* kv, const float* q
   x.repeat = std::max(1, params->exact_repeat);
   char* w = static_cast<char*>(ws);
   x.ws.cl_score = reinterpret_cast<float*>(w + d.o_clscore);
+  x.ws.cl_lse = reinterpret_cast<float*>(w + d.o_cllse);
   x.ws.cl_mask = reinterpret_cast<uint32_t*>(w + d.o_clmask);
   x.ws.cl_rank = reinterpret_cast<int32_t*>(w + d.o_clrank);
   x.ws.unit_rows = reinterpret_cast<int32_t*>(w + d.o_urows);

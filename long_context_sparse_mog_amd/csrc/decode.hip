@@ -37,7 +37,7 @@ struct DArgs {
   float* lse;
   int32_t* sel_c;
   int32_t* sel_s;
-  int32_t c_stride, s_stride, Hq, Hkv, n_sink, n_recent, residual, splits, nb_res, n_units, nblk;
+  int32_t c_stride, s_stride, Hq, Hkv, n_sink, n_recent, residual, shared, splits, nb_res, n_units, nblk;
   int32_t cstride;   // per-cluster workspace entries per unit (the largest C)
   float scale_l2;    // scale * log2(e)
   float half_s2_l2;  // scale^2 / 2 * log2(e)
@@ -228,6 +228,7 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
   __shared__ int hist[G][256 + 64];       // 256 digit bins, then one spare bin per lane
   __shared__ unsigned long long selb[G][KPL];  // per head: chosen lanes of slot j
   __shared__ int slot_cnt[KPL], slot_tiles[KPL];
+  __shared__ float gsum[64 * KPL];  // shared selection: summed mass fractions
   const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63, h = tid >> 6;
   const int want_raw = b.top_c[u / a.Hkv];
   // the scores need only the unit index: their loads go out with the unit
@@ -246,6 +247,35 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
   for (int t = 0; t < NSW; ++t) {
     const int i = min(64 * (h + G * t) + lane, C - 1);
     bound[t] = off[(i + 1) * U.S] - off[i * U.S];
+  }
+  if (a.shared) {
+    // one selection per KV head: the key of a cluster is the sum over the
+    // heads of the head's estimated mass fraction 2^(score - L_h), L_h the
+    // log2 of the head's total over its nonempty clusters; summed in head
+    // order through LDS, so every wave then holds the same keys
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j)
+      if (64 * j + lane < C) mx = fmaxf(mx, scv[j]);
+    mx = wave_max(mx);
+    float sm = 0.f;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) sm += (64 * j + lane < C && scv[j] != -INFINITY) ? exp2f(scv[j] - mx) : 0.f;
+    const float lh = mx + log2f(wave_sum_uniform(sm));
+    if (lane == 0) a.ws.cl_lse[(int64_t)u * G + h] = lh;
+    for (int hh = 0; hh < G; ++hh) {
+      if (h == hh) {
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+          const float f = (64 * j + lane < C && scv[j] != -INFINITY) ? exp2f(scv[j] - lh) : 0.f;
+          gsum[64 * j + lane] = hh == 0 ? f : gsum[64 * j + lane] + f;
+        }
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int j = 0; j < KPL; ++j)
+      if (scv[j] != -INFINITY) scv[j] = gsum[64 * j + lane];
   }
   uint32_t key[KPL];
   int nvalid = 0;
@@ -461,6 +491,7 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
   static_assert(kMaxS * G <= 256, "one thread per (subcluster, head) score");
   __shared__ float st[4][G][D + 2];
   __shared__ float lds_sc[kMaxS][G];
+  __shared__ float lds_gs[kMaxS];  // shared selection: summed mass fractions
   __shared__ uint32_t lds_sm[kMaxS];
   __shared__ int lds_cnt[kMaxS];
   __shared__ int lds_off[kMaxS + 1];
@@ -552,16 +583,32 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
         }
       }
       __syncthreads();
+      if (a.shared) {
+        // one selection per KV head: a subcluster's key is the sum over the
+        // heads of 2^(score - L_h), L_h the head's log2 total over clusters
+        if (tid < kMaxS) {
+          float gsv = 0.f;
+          bool any = false;
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const float v = lds_sc[tid][h];
+            any |= v != -INFINITY;
+            gsv += v != -INFINITY ? exp2f(v - a.ws.cl_lse[(int64_t)u * G + h]) : 0.f;
+          }
+          lds_gs[tid] = any ? gsv : -INFINITY;
+        }
+        __syncthreads();
+      }
       // top-s of every choosing head at once: thread (i, h) ranks subcluster
-      // i's score among head h's (ties to the lower index)
+      // i's score among head h's, or the shared keys (ties to the lower index)
       const int s_keep = s_keep_raw < 0 ? 0 : s_keep_raw;
       const int ti = tid / G, th = tid % G;
       bool tsel = false;
       if (tid < kMaxS * G) {
-        const float my = lds_sc[ti][th];
+        const float my = a.shared ? lds_gs[ti] : lds_sc[ti][th];
         float osc[kMaxS];
 #pragma unroll
-        for (int j = 0; j < kMaxS; ++j) osc[j] = lds_sc[j][th];
+        for (int j = 0; j < kMaxS; ++j) osc[j] = a.shared ? lds_gs[j] : lds_sc[j][th];
         // branch-free count (bitwise, not short-circuit, operators)
         int rank = 0;
 #pragma unroll
@@ -1200,6 +1247,7 @@ hipError_t launch_decode(const DecodeLaunch& x, hipStream_t s) {
   a.n_sink = x.L.n_sink;
   a.n_recent = x.L.n_recent;
   a.residual = x.residual;
+  a.shared = x.shared;
   a.splits = x.splits;
   a.nb_res = x.nb_res;
   a.n_units = x.L.n_units;

@@ -108,6 +108,7 @@ __host__ __device__ inline int64_t tile_unit_base(int64_t row_base, int64_t cl_b
 // layout), so a kernel can address them from the unit index alone.
 struct DecodeWS {
   float* cl_score;      // [n_units * max_C][G]  log2-domain scores
+  float* cl_lse;        // [n_units][G]          shared selection: log2 of each head's total estimated mass
   uint32_t* cl_mask;    // [n_units * max_C]     heads that chose the cluster
   int32_t* cl_rank;     // [n_units * max_C][G]  rank among a head's chosen clusters, or -1
                         //                       (written only when sel_s is requested)
@@ -135,6 +136,7 @@ struct DecodeLaunch {
   int32_t c_stride, s_stride;
   int32_t Hq, G, D, dtype;
   int32_t residual;
+  int32_t shared;       // one selection per KV head
   int32_t splits;       // target exact blocks in total (balanced over units)
   int32_t nblk;         // exact blocks launched: splits + n_units
   int32_t nb_res;       // residual record slots per unit: nb_chosen + max_C / kRestClustersPerBlock

@@ -172,13 +172,15 @@ def mog_layout_init(kv: KVCache, n_sink, n_recent, device="cuda", stream=None) -
     return Layout(L, mem)
 
 
-def decode_params(n_q_heads, top_c, top_s, residual=True, scale=0.0, splits=0):
-    """mog_decode_params; ``top_c``/``top_s`` are ints or per-sequence lists."""
+def decode_params(n_q_heads, top_c, top_s, residual=True, scale=0.0, splits=0, shared=False):
+    """mog_decode_params; ``top_c``/``top_s`` are ints or per-sequence lists;
+    ``shared``: one selection per KV head instead of one per query head."""
     p = capi.mog_decode_params()
     p.n_q_heads = n_q_heads
     p.residual = 1 if residual else 0
     p.scale = float(scale)
     p.splits = int(splits)
+    p.shared_selection = 1 if shared else 0
     keep = []
     if isinstance(top_c, (list, tuple)):
         arr = capi.int_array(top_c)

@@ -11,6 +11,7 @@ import numpy as np
 import oracle as O
 
 NEAR_TIE = 1e-5  # absolute, on float64 oracle scores (natural log)
+NEAR_TIE_SHARED = 1e-4  # relative, on the shared group scores (sums of mass fractions)
 
 
 def unit_layout_arrays(L: "O.UnitLayout") -> dict:
@@ -46,9 +47,9 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
-def _cutoff_ok(scores, valid, chosen_gpu, chosen_ora, k):
+def _cutoff_ok(scores, valid, chosen_gpu, chosen_ora, k, rel_tol=None):
     """Selections may differ only where oracle scores are within NEAR_TIE of
-    the k-th best score."""
+    the k-th best score (or within rel_tol of it, relative)."""
     if set(chosen_gpu) == set(chosen_ora):
         return True
     idx = np.nonzero(valid)[0]
@@ -57,17 +58,39 @@ def _cutoff_ok(scores, valid, chosen_gpu, chosen_ora, k):
         return False
     cut = np.sort(scores[idx])[::-1][kk - 1]
     diff = set(chosen_gpu) ^ set(chosen_ora)
-    return all(abs(scores[i] - cut) <= NEAR_TIE for i in diff) and len(chosen_gpu) == len(chosen_ora)
+    tol = NEAR_TIE if rel_tol is None else rel_tol * abs(cut)
+    return all(abs(scores[i] - cut) <= tol for i in diff) and len(chosen_gpu) == len(chosen_ora)
+
+
+def _shared_scores(L, Q, scale):
+    """Group scores of the shared selection (oracle reading R9): clusters,
+    and a function giving a chosen cluster's subcluster group scores."""
+    G = Q.shape[0]
+    valid = L.cl_count > 0
+    sc = np.stack([O.group_log_mass(Q[h], L.cl_count, L.cl_mu, L.cl_var, scale) for h in range(G)])
+    lse = np.array([np.logaddexp.reduce(sc[h][valid]) for h in range(G)])
+    gs = np.where(valid, np.exp(sc - lse[:, None]).sum(axis=0), 0.0)
+
+    def sub(j):
+        g0 = j * L.S
+        sv = L.sub_count[g0:g0 + L.S] > 0
+        ss = np.stack([O.group_log_mass(Q[h], L.sub_count[g0:g0 + L.S], L.sub_mu[g0:g0 + L.S],
+                                        L.sub_var[g0:g0 + L.S], scale) for h in range(G)])
+        return np.where(sv, np.exp(ss - lse[:, None]).sum(axis=0), 0.0)
+
+    return gs, sub
 
 
 def compare_unit(L, K, V, Q, c, s, gpu_out, gpu_lse, gpu_sel_c, gpu_sel_s, tol, residual=True,
-                 scale=None):
+                 scale=None, shared=False):
     """Compare one unit's GPU results with the oracle's.  Returns a dict of
     the errors; raises AssertionError on a selection mismatch that is not a
-    near tie."""
+    near tie.  ``shared``: one selection per KV head (oracle reading R9)."""
     G, d = Q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    ref = O.decode_unit(L, K, V, Q, c, s, scale=scale, residual=residual)
+    ref = O.decode_unit(L, K, V, Q, c, s, scale=scale, residual=residual, shared=shared)
+    if shared:
+        gs, gs_sub = _shared_scores(L, Q, scale)
     sel_c_gpu, sel_s_gpu = [], []
     ties = 0
     for h in range(G):
@@ -79,8 +102,11 @@ def compare_unit(L, K, V, Q, c, s, gpu_out, gpu_lse, gpu_sel_c, gpu_sel_s, tol, 
         sel_s_gpu.append(subs)
         oc = [int(x) for x in ref["sel_c"][h]]
         if gc != oc:
-            sc = O.group_log_mass(Q[h], L.cl_count, L.cl_mu, L.cl_var, scale)
-            assert _cutoff_ok(sc, L.cl_count > 0, gc, oc, c), (h, gc, oc)
+            if shared:
+                assert _cutoff_ok(gs, L.cl_count > 0, gc, oc, c, NEAR_TIE_SHARED), (h, gc, oc)
+            else:
+                sc = O.group_log_mass(Q[h], L.cl_count, L.cl_mu, L.cl_var, scale)
+                assert _cutoff_ok(sc, L.cl_count > 0, gc, oc, c), (h, gc, oc)
             ties += 1
         for r, j in enumerate(gc):
             if j in oc:
@@ -88,9 +114,13 @@ def compare_unit(L, K, V, Q, c, s, gpu_out, gpu_lse, gpu_sel_c, gpu_sel_s, tol, 
                 gsub = [int(x) for x in subs[r]]
                 if gsub != osub:
                     g0 = j * L.S
-                    ss = O.group_log_mass(Q[h], L.sub_count[g0:g0 + L.S], L.sub_mu[g0:g0 + L.S],
-                                          L.sub_var[g0:g0 + L.S], scale)
-                    assert _cutoff_ok(ss, L.sub_count[g0:g0 + L.S] > 0, gsub, osub, s), (h, j, gsub, osub)
+                    if shared:
+                        assert _cutoff_ok(gs_sub(j), L.sub_count[g0:g0 + L.S] > 0, gsub, osub, s,
+                                          NEAR_TIE_SHARED), (h, j, gsub, osub)
+                    else:
+                        ss = O.group_log_mass(Q[h], L.sub_count[g0:g0 + L.S], L.sub_mu[g0:g0 + L.S],
+                                              L.sub_var[g0:g0 + L.S], scale)
+                        assert _cutoff_ok(ss, L.sub_count[g0:g0 + L.S] > 0, gsub, osub, s), (h, j, gsub, osub)
                     ties += 1
     if ties:
         ref = O.decode_unit(L, K, V, Q, c, s, scale=scale, residual=residual,

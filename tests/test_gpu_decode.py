@@ -29,9 +29,9 @@ def tol_of(wl):
     return 1e-5 if wl.dtype == "fp32" else 2e-3
 
 
-def run_decode_case(wl, residual=True, top_c=None, top_s=None, qset=0, n_qsets=1, splits=0):
+def run_decode_case(wl, residual=True, top_c=None, top_s=None, qset=0, n_qsets=1, splits=0, shared=False):
     say(f"[case] {wl.name} lens={wl.seq_lens} Hq={wl.n_q_heads} Hkv={wl.n_kv_heads} "
-        f"D={wl.head_dim} {wl.dtype} c={top_c or wl.top_c} s={top_s or wl.top_s} res={residual}")
+        f"D={wl.head_dim} {wl.dtype} c={top_c or wl.top_c} s={top_s or wl.top_s} res={residual} shared={shared}")
     b = synth.generate(wl, device="cuda", n_qsets=n_qsets)
     kv = ops.KVCache.from_batch(b)
     lays = build_oracle_layouts(b)
@@ -39,7 +39,7 @@ def run_decode_case(wl, residual=True, top_c=None, top_s=None, qset=0, n_qsets=1
                             [unit_layout_arrays(lays[u]) for u in range(wl.n_seq * wl.n_kv_heads)])
     tc = top_c if top_c is not None else wl.top_c
     ts = top_s if top_s is not None else wl.top_s
-    params = ops.decode_params(wl.n_q_heads, list(tc), list(ts), residual=residual, splits=splits)
+    params = ops.decode_params(wl.n_q_heads, list(tc), list(ts), residual=residual, splits=splits, shared=shared)
     q = b.Q[qset].contiguous()
     out, lse, sel_c, sel_s = ops.mog_decode(lay, kv, q, params, want_sel=True)
     torch.cuda.synchronize()
@@ -54,7 +54,7 @@ def run_decode_case(wl, residual=True, top_c=None, top_s=None, qset=0, n_qsets=1
             Q = q[s, h * G:(h + 1) * G].cpu().numpy().astype(np.float64)
             hs = slice(h * G, (h + 1) * G)
             r = compare_unit(lays[u], K, V, Q, tc[s], ts[s], out[s, hs], lse[s, hs], sel_c[s, hs],
-                             sel_s[s, hs], tol_of(wl), residual=residual)
+                             sel_s[s, hs], tol_of(wl), residual=residual, shared=shared)
             assert r["lse_err"] < (1e-5 if wl.dtype == "fp32" else 1e-3) * max(1.0, float(np.abs(lse[s, hs]).max()))
             worst = max(worst, r["max_rel"])
     say(f"  worst per-head rel L2 = {worst:.3e}")
@@ -160,6 +160,26 @@ def test_dense_matches_oracle(wl):
             for g in range(G):
                 assert rel_l2(out[s, h * G + g], o[g]) < (1e-5 if wl.dtype == "fp32" else 1e-4)
             np.testing.assert_allclose(lse[s, h * G:(h + 1) * G], l, rtol=1e-5, atol=1e-4)
+
+
+# one selection per KV head (oracle reading R9)
+def test_shared_selection_gqa5_reduced():
+    run_decode_case(synth.config(3, seq_lens=[12000], n_kv_heads=2, n_q_heads=10, n_components=128), shared=True)
+
+
+def test_shared_selection_ragged_paged_reduced():
+    run_decode_case(synth.config(4, seq_lens=[3000, 9000, 1000], n_kv_heads=2, n_q_heads=8,
+                                 high_entropy_heads=(1,), n_components=64), shared=True)
+
+
+@pytest.mark.parametrize("G", [1, 8])
+def test_shared_selection_group_sizes(G):
+    run_decode_case(synth.config(1, seq_lens=[3000], n_kv_heads=1, n_q_heads=G, n_components=32), shared=True)
+
+
+def test_shared_selection_fp32_top_only():
+    wl = synth.config(1, seq_lens=[5000], n_kv_heads=1, n_q_heads=4, n_components=32, dtype="fp32")
+    run_decode_case(wl, residual=False, shared=True)
 
 
 def test_decode_is_deterministic():

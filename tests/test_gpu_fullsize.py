@@ -24,13 +24,13 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_fullsize(wl, units, qset=0):
+def run_fullsize(wl, units, qset=0, shared=False):
     say(f"[full] {wl.name} n_seq={wl.n_seq} Hq={wl.n_q_heads} Hkv={wl.n_kv_heads} "
         f"max_len={wl.max_len} units={units}")
     b = synth.generate(wl, device="cuda", n_qsets=qset + 1)
     kv = ops.KVCache.from_batch(b)
     lay = ops.mog_build(kv, wl.n_sink, wl.n_recent, kmeans_iters=wl.kmeans_iters, seed=1)
-    params = ops.decode_params(wl.n_q_heads, list(wl.top_c), list(wl.top_s))
+    params = ops.decode_params(wl.n_q_heads, list(wl.top_c), list(wl.top_s), shared=shared)
     q = b.Q[qset].contiguous()
     out, lse, sel_c, sel_s = ops.mog_decode(lay, kv, q, params, want_sel=True)
     torch.cuda.synchronize()
@@ -44,7 +44,7 @@ def run_fullsize(wl, units, qset=0):
         Q = q[s, h * G:(h + 1) * G].cpu().numpy().astype(np.float64)
         hs = slice(h * G, (h + 1) * G)
         r = compare_unit(L, K, V, Q, wl.top_c[s], wl.top_s[s], out[s, hs], lse[s, hs], sel_c[s, hs],
-                         sel_s[s, hs], 2e-3)
+                         sel_s[s, hs], 2e-3, shared=shared)
         assert r["lse_err"] < 1e-3 * max(1.0, float(np.abs(lse[s, hs]).max()))
         say(f"  unit {u} (seq {s}, len {wl.seq_lens[s]}, kv head {h}): worst rel L2 {r['max_rel']:.2e}, "
             f"near ties {r['ties']}")
@@ -55,6 +55,10 @@ def run_fullsize(wl, units, qset=0):
 
 def test_fullsize_gqa_32k_all_units():
     run_fullsize(synth.config(1), list(range(8)))
+
+
+def test_fullsize_gqa_1m_shared_selection_sampled():
+    run_fullsize(synth.config(3), [2, 5], qset=1, shared=True)
 
 
 def test_fullsize_mha_128k_sampled():
