@@ -47,7 +47,7 @@ in the design notes of the repository):
       than the budget all nonempty ones are chosen.
   R8  Every query head makes its own selection (GQA heads sharing a KV head
       are independent instances).
-  R9  Optional shared selection for the G query heads of a KV head (the
+  R14 Optional shared selection for the G query heads of a KV head (the
       DuoAttention review, page 2, "Limitations" and its closing
       discussion: query heads that share a KV head couple their needs).
       Each head's group scores are turned into estimated fractions of its
@@ -414,7 +414,7 @@ def _softmax_merge(logw, vals):
 
 
 def shared_selection(L: UnitLayout, Q, top_c, top_s, scale=None):
-    """One selection for all query heads of a KV head (reading R9): returns
+    """One selection for all query heads of a KV head (reading R14): returns
     (chosen cluster ids ascending, [chosen subcluster ids ascending per chosen
     cluster]) and the per-cluster group scores."""
     Q = np.atleast_2d(np.asarray(Q, dtype=np.float64))
@@ -450,7 +450,7 @@ def decode_unit(L: UnitLayout, K, V, Q, top_c, top_s, scale=None, residual=True,
     cluster ids ascending), ``sel_s`` (per head, per chosen cluster, chosen
     subcluster ids ascending) and ``n_exact`` (rows attended exactly per head).
     ``sel_override`` = (sel_c, sel_s) replaces the selection; ``shared``
-    takes the one selection of reading R9 for every head.
+    takes the one selection of reading R14 for every head.
     """
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)

@@ -63,7 +63,7 @@ def _cutoff_ok(scores, valid, chosen_gpu, chosen_ora, k, rel_tol=None):
 
 
 def _shared_scores(L, Q, scale):
-    """Group scores of the shared selection (oracle reading R9): clusters,
+    """Group scores of the shared selection (oracle reading R14): clusters,
     and a function giving a chosen cluster's subcluster group scores."""
     G = Q.shape[0]
     valid = L.cl_count > 0
@@ -85,7 +85,7 @@ def compare_unit(L, K, V, Q, c, s, gpu_out, gpu_lse, gpu_sel_c, gpu_sel_s, tol, 
                  scale=None, shared=False):
     """Compare one unit's GPU results with the oracle's.  Returns a dict of
     the errors; raises AssertionError on a selection mismatch that is not a
-    near tie.  ``shared``: one selection per KV head (oracle reading R9)."""
+    near tie.  ``shared``: one selection per KV head (oracle reading R14)."""
     G, d = Q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     ref = O.decode_unit(L, K, V, Q, c, s, scale=scale, residual=residual, shared=shared)

@@ -162,7 +162,7 @@ def test_dense_matches_oracle(wl):
             np.testing.assert_allclose(lse[s, h * G:(h + 1) * G], l, rtol=1e-5, atol=1e-4)
 
 
-# one selection per KV head (oracle reading R9)
+# one selection per KV head (oracle reading R14)
 def test_shared_selection_gqa5_reduced():
     run_decode_case(synth.config(3, seq_lens=[12000], n_kv_heads=2, n_q_heads=10, n_components=128), shared=True)
 

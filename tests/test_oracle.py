@@ -471,7 +471,7 @@ def test_selection_override_and_top_only():
 
 
 # ---------------------------------------------------------------------------
-# Shared selection per KV head (reading R9)
+# Shared selection per KV head (reading R14)
 # ---------------------------------------------------------------------------
 
 
