@@ -28,6 +28,8 @@ from .mog import (  # noqa: F401
     UnitLayout,
     build_unit,
     layout_from_assignment,
+    fold_tokens,
+    shared_selection,
     decode_unit,
     dense_attention,
     decode_batch,

@@ -57,6 +57,15 @@ in the design notes of the repository):
       are scored the same way (same LSE_h), and every head then uses the one
       top-c / top-s selection.  The exact read per KV head is then capped at
       one head's budget.
+  R15 Incremental decode: the cache grows by appended tokens, and the tokens
+      that leave the recent window (oldest first) join the middle region.
+      Each goes to the cluster whose mean key is nearest (squared distance,
+      ties to the lower id; an empty cluster's kept centroid counts), then
+      to the nearest nonempty subcluster of that cluster (subcluster 0 if
+      none); both groups' count, mean key, population variance and mean value
+      are updated by Welford's running formulas, and the token's rows are
+      kept in a fold area and read exactly whenever its subcluster is chosen.
+      C, S and the rest of the partition stay until the next build.
 """
 
 from __future__ import annotations
@@ -259,6 +268,10 @@ class UnitLayout:
     init_ids: list = field(default_factory=list)
     sub_init_ids: dict = field(default_factory=dict)
     sse_trace: list = field(default_factory=list)
+    # tokens folded into the middle region after the build (reading R15):
+    # their positions and global subcluster ids, oldest first
+    fold_pos: list = field(default_factory=list)
+    fold_sub: list = field(default_factory=list)
 
     @property
     def n_mid(self) -> int:
@@ -266,11 +279,25 @@ class UnitLayout:
 
     @property
     def sub_count(self) -> np.ndarray:
-        return np.diff(self.sub_off)
+        cnt = np.diff(self.sub_off)
+        if self.fold_sub:
+            cnt = cnt + np.bincount(np.asarray(self.fold_sub, np.int64), minlength=self.C * self.S)
+        return cnt
 
     @property
     def cl_count(self) -> np.ndarray:
-        return self.sub_off[self.S::self.S] - self.sub_off[:-1:self.S]
+        sc = self.sub_count
+        return np.add.reduceat(sc, np.arange(0, self.C * self.S, self.S))
+
+    def group_rows(self, g: int) -> np.ndarray:
+        """Token positions of subcluster g: its reordered rows, then the
+        tokens folded into it."""
+        rows = self.perm[self.sub_off[g]:self.sub_off[g + 1]]
+        if self.fold_sub:
+            extra = [p for p, q in zip(self.fold_pos, self.fold_sub) if q == g]
+            if extra:
+                rows = np.concatenate([rows, np.asarray(extra, dtype=rows.dtype)])
+        return rows
 
     def cluster_labels(self) -> np.ndarray:
         """Cluster id of each middle-region key, indexed by position - n_sink."""
@@ -371,6 +398,55 @@ def build_unit(K, V, n_sink, n_recent, iters, state, init_ids=None, sub_init_ids
     lay.sub_init_ids = used_sub_init
     lay.sse_trace = trace
     return lay
+
+
+# ---------------------------------------------------------------------------
+# Incremental decode (reading R15)
+# ---------------------------------------------------------------------------
+
+
+def _welford_add(n, mu, var, vbar, k, v):
+    """Running update of (mean key, population variance, mean value) of a
+    group of n members by one more member (k, v): Welford's formulas,
+    computed in float64 from the stored float32 values, stored float32."""
+    n1 = n + 1
+    mu = np.asarray(mu, np.float64)
+    delta = k - mu
+    mu1 = mu + delta / n1
+    var1 = (n * np.asarray(var, np.float64) + delta * (k - mu1)) / n1
+    vbar1 = np.asarray(vbar, np.float64) + (v - np.asarray(vbar, np.float64)) / n1
+    return mu1.astype(np.float32), var1.astype(np.float32), vbar1.astype(np.float32)
+
+
+def fold_tokens(L: UnitLayout, K, V, n_new: int) -> UnitLayout:
+    """The layout after the sequence grew by n_new tokens (K, V: float64
+    [N + n_new][d] of the grown sequence): the n_new tokens that leave the
+    recent window join the middle region as in reading R15.  Returns a new
+    layout; ``L`` is unchanged."""
+    import copy
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    out = copy.deepcopy(L)
+    C, S = out.C, out.S
+    for t in range(L.N - L.n_recent, L.N - L.n_recent + n_new):
+        k, v = K[t], V[t]
+        d2 = ((out.cl_mu.astype(np.float64) - k) ** 2).sum(axis=1)
+        j = int(np.argmin(d2))  # first minimum: ties to the lower id
+        cnt = out.sub_count[j * S:(j + 1) * S]
+        i = 0
+        if (cnt > 0).any():
+            ds = ((out.sub_mu[j * S:(j + 1) * S].astype(np.float64) - k) ** 2).sum(axis=1)
+            ds = np.where(cnt > 0, ds, np.inf)
+            i = int(np.argmin(ds))
+        g = j * S + i
+        ncl, nsub = int(out.cl_count[j]), int(cnt[i])
+        out.cl_mu[j], out.cl_var[j], out.cl_vbar[j] = _welford_add(ncl, out.cl_mu[j], out.cl_var[j], out.cl_vbar[j], k, v)
+        out.sub_mu[g], out.sub_var[g], out.sub_vbar[g] = _welford_add(nsub, out.sub_mu[g], out.sub_var[g],
+                                                                      out.sub_vbar[g], k, v)
+        out.fold_pos.append(t)
+        out.fold_sub.append(g)
+    out.N = L.N + n_new
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -498,7 +574,7 @@ def decode_unit(L: UnitLayout, K, V, Q, top_c, top_s, scale=None, residual=True,
                 if sub_cnt[g] == 0:
                     continue
                 if i in pick_set:
-                    exact_rows.append(L.perm[L.sub_off[g]:L.sub_off[g + 1]])
+                    exact_rows.append(L.group_rows(g))
                 else:
                     r_logw.append(ss[i])
                     r_vals.append(L.sub_vbar[g].astype(np.float64))

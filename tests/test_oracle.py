@@ -585,6 +585,87 @@ def test_shared_selection_caps_the_union():
 
 
 # ---------------------------------------------------------------------------
+# Incremental decode: folding the tokens that leave the recent window (R15)
+# ---------------------------------------------------------------------------
+
+
+def _grown_unit(seed, N=600, grow=40, d=6, n_sink=4, n_recent=16):
+    rng = np.random.default_rng(seed)
+    K = mixture_keys(rng, N + grow, d, 10)
+    V = rng.normal(0, 1, (N + grow, d))
+    L = O.build_unit(K[:N], V[:N], n_sink, n_recent, 10, O.unit_state(seed, 0, 0, 1))
+    return K, V, L
+
+
+def test_fold_stats_equal_direct_group_stats():
+    """Welford's running updates reach the two-pass statistics of the grown
+    groups (closed form), and every folded token went to its nearest group."""
+    K, V, L = _grown_unit(21)
+    F = O.fold_tokens(L, K, V, 40)
+    S = L.S
+    members = {}
+    for g in range(L.C * S):
+        members[g] = list(F.group_rows(g))
+    for j in range(L.C):
+        rows = np.concatenate([members[j * S + i] for i in range(S)])
+        if rows.size:
+            _, mu, s, vb = O.group_stats(K[rows], V[rows])
+            np.testing.assert_allclose(F.cl_mu[j], mu, rtol=1e-5, atol=1e-5)
+            np.testing.assert_allclose(F.cl_var[j], s, rtol=1e-4, atol=1e-5)
+            np.testing.assert_allclose(F.cl_vbar[j], vb, rtol=1e-5, atol=1e-5)
+    for g, rows in members.items():
+        if len(rows):
+            _, mu, s, vb = O.group_stats(K[rows], V[rows])
+            np.testing.assert_allclose(F.sub_mu[g], mu, rtol=1e-5, atol=1e-5)
+            np.testing.assert_allclose(F.sub_var[g], s, rtol=1e-4, atol=1e-5)
+    # nearest cluster at the time of the fold: replay the folds one by one
+    cur = L
+    for step, t in enumerate(F.fold_pos):
+        d2 = ((cur.cl_mu.astype(np.float64) - K[t]) ** 2).sum(axis=1)
+        assert F.fold_sub[step] // S == int(np.flatnonzero(d2 == d2.min())[0])
+        cur = O.fold_tokens(cur, K[:cur.N + 1], V[:cur.N + 1], 1)
+    assert cur.fold_sub == F.fold_sub
+
+
+def test_fold_all_selected_is_dense_on_the_grown_sequence():
+    K, V, L = _grown_unit(22)
+    F = O.fold_tokens(L, K, V, 40)
+    assert F.N == K.shape[0] and len(F.fold_pos) == 40
+    Q = np.random.default_rng(3).normal(0, 1, (2, K.shape[1]))
+    r = O.decode_unit(F, K, V, Q, F.C, F.S)
+    o, l = O.dense_attention(K, V, Q)
+    assert rel(r["out"], o) < 1e-12
+    np.testing.assert_allclose(r["lse"], l, rtol=1e-12)
+
+
+def test_fold_zero_tokens_and_one_at_a_time():
+    K, V, L = _grown_unit(23, grow=12)
+    F0 = O.fold_tokens(L, K, V, 0)
+    assert F0.N == L.N and F0.fold_pos == [] and np.array_equal(F0.cl_mu, L.cl_mu)
+    Fa = O.fold_tokens(L, K, V, 12)
+    Fb = L
+    for k in range(12):
+        Fb = O.fold_tokens(Fb, K[:L.N + k + 1], V[:L.N + k + 1], 1)
+    assert Fa.fold_sub == Fb.fold_sub and Fa.fold_pos == Fb.fold_pos
+    assert np.array_equal(Fa.sub_mu, Fb.sub_mu) and np.array_equal(Fa.cl_var, Fb.cl_var)
+
+
+def test_fold_into_an_empty_group_makes_a_singleton():
+    rng = np.random.default_rng(7)
+    d, N = 4, 200
+    K = mixture_keys(rng, N + 1, d, 4)
+    V = rng.normal(0, 1, (N + 1, d))
+    L = O.build_unit(K[:N], V[:N], 2, 8, 10, O.unit_state(1, 0, 0, 1))
+    # a far key: its nearest cluster is the one whose mean we place there
+    j = int(np.argmax(L.cl_count))
+    K[N - 8] = L.cl_mu[j].astype(np.float64) + 1e-3
+    F = O.fold_tokens(L, K, V, 1)
+    assert F.fold_sub[0] // L.S == j
+    g = F.fold_sub[0]
+    assert F.sub_count[g] == L.sub_count[g] + 1
+
+
+# ---------------------------------------------------------------------------
 # Dense attention: textbook special cases
 # ---------------------------------------------------------------------------
 
