@@ -59,13 +59,14 @@ in the design notes of the repository):
       one head's budget.
   R15 Incremental decode: the cache grows by appended tokens, and the tokens
       that leave the recent window (oldest first) join the middle region.
-      Each goes to the cluster whose mean key is nearest (squared distance,
-      ties to the lower id; an empty cluster's kept centroid counts), then
-      to the nearest nonempty subcluster of that cluster (subcluster 0 if
-      none); both groups' count, mean key, population variance and mean value
-      are updated by Welford's running formulas, and the token's rows are
-      kept in a fold area and read exactly whenever its subcluster is chosen.
-      C, S and the rest of the partition stay until the next build.
+      Each goes to the nonempty cluster whose mean key is nearest (squared
+      distance, ties to the lower id; an empty cluster has no Gaussian, its
+      stored statistics are placeholders), then to the nearest nonempty
+      subcluster of that cluster; both groups' count, mean key, population
+      variance and mean value are updated by Welford's running formulas, and
+      the token's rows are kept in a fold area and read exactly whenever its
+      subcluster is chosen.  C, S and the rest of the partition stay until
+      the next build.
 """
 
 from __future__ import annotations
@@ -431,13 +432,11 @@ def fold_tokens(L: UnitLayout, K, V, n_new: int) -> UnitLayout:
     for t in range(L.N - L.n_recent, L.N - L.n_recent + n_new):
         k, v = K[t], V[t]
         d2 = ((out.cl_mu.astype(np.float64) - k) ** 2).sum(axis=1)
+        d2 = np.where(out.cl_count > 0, d2, np.inf)
         j = int(np.argmin(d2))  # first minimum: ties to the lower id
         cnt = out.sub_count[j * S:(j + 1) * S]
-        i = 0
-        if (cnt > 0).any():
-            ds = ((out.sub_mu[j * S:(j + 1) * S].astype(np.float64) - k) ** 2).sum(axis=1)
-            ds = np.where(cnt > 0, ds, np.inf)
-            i = int(np.argmin(ds))
+        ds = ((out.sub_mu[j * S:(j + 1) * S].astype(np.float64) - k) ** 2).sum(axis=1)
+        i = int(np.argmin(np.where(cnt > 0, ds, np.inf)))
         g = j * S + i
         ncl, nsub = int(out.cl_count[j]), int(cnt[i])
         out.cl_mu[j], out.cl_var[j], out.cl_vbar[j] = _welford_add(ncl, out.cl_mu[j], out.cl_var[j], out.cl_vbar[j], k, v)

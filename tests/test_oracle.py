@@ -622,7 +622,12 @@ def test_fold_stats_equal_direct_group_stats():
     cur = L
     for step, t in enumerate(F.fold_pos):
         d2 = ((cur.cl_mu.astype(np.float64) - K[t]) ** 2).sum(axis=1)
+        d2[cur.cl_count == 0] = np.inf
         assert F.fold_sub[step] // S == int(np.flatnonzero(d2 == d2.min())[0])
+        g = F.fold_sub[step]
+        ds = ((cur.sub_mu[g - g % S:g - g % S + S].astype(np.float64) - K[t]) ** 2).sum(axis=1)
+        ds[cur.sub_count[g - g % S:g - g % S + S] == 0] = np.inf
+        assert g % S == int(np.flatnonzero(ds == ds.min())[0])
         cur = O.fold_tokens(cur, K[:cur.N + 1], V[:cur.N + 1], 1)
     assert cur.fold_sub == F.fold_sub
 
@@ -650,19 +655,30 @@ def test_fold_zero_tokens_and_one_at_a_time():
     assert np.array_equal(Fa.sub_mu, Fb.sub_mu) and np.array_equal(Fa.cl_var, Fb.cl_var)
 
 
-def test_fold_into_an_empty_group_makes_a_singleton():
+def test_fold_skips_empty_clusters_and_lands_near_its_key():
+    """A key placed on a nonempty cluster's mean joins that cluster; a key at
+    the zero placeholder mean of an empty cluster joins a nonempty one, and
+    the empty cluster stays empty."""
     rng = np.random.default_rng(7)
-    d, N = 4, 200
-    K = mixture_keys(rng, N + 1, d, 4)
-    V = rng.normal(0, 1, (N + 1, d))
-    L = O.build_unit(K[:N], V[:N], 2, 8, 10, O.unit_state(1, 0, 0, 1))
-    # a far key: its nearest cluster is the one whose mean we place there
+    d, N, n_sink, n_recent = 4, 200, 2, 8
+    K = mixture_keys(rng, N + 2, d, 4) + 5.0
+    V = rng.normal(0, 1, (N + 2, d))
+    n_mid = N - n_sink - n_recent
+    C, S = 4, 3
+    # clusters 0..2 by the first coordinate's tercile, cluster 3 empty
+    x = K[n_sink:N - n_recent, 0]
+    cl = np.digitize(x, np.quantile(x, [1 / 3, 2 / 3]))
+    sub = np.arange(n_mid) % S
+    L = O.layout_from_assignment(K[:N], V[:N], n_sink, n_recent, C, S, cl, sub)
+    assert L.cl_count[3] == 0 and not L.cl_mu[3].any()
     j = int(np.argmax(L.cl_count))
-    K[N - 8] = L.cl_mu[j].astype(np.float64) + 1e-3
-    F = O.fold_tokens(L, K, V, 1)
-    assert F.fold_sub[0] // L.S == j
-    g = F.fold_sub[0]
-    assert F.sub_count[g] == L.sub_count[g] + 1
+    K[N - n_recent] = L.cl_mu[j].astype(np.float64) + 1e-3
+    K[N - n_recent + 1] = 0.0  # nearer to the placeholder than to any mean
+    F = O.fold_tokens(L, K, V, 2)
+    assert F.fold_sub[0] // S == j
+    assert F.sub_count[F.fold_sub[0]] == L.sub_count[F.fold_sub[0]] + 1
+    assert F.fold_sub[1] // S != 3 and F.cl_count[3] == 0
+    assert F.cl_count.sum() == L.cl_count.sum() + 2
 
 
 # ---------------------------------------------------------------------------
