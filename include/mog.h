@@ -32,7 +32,7 @@
  * Limits: head_dim 64 or 128; 1 <= n_q_heads / n_kv_heads <= 8;
  * n_seq <= MOG_MAX_SEQ; per-sequence length N with n_sink + n_recent < N and
  * N <= MOG_MAX_LEN; keys within |k| < 65536 (the build sums them in 64-bit
- * fixed point).
+ * fixed point); at most MOG_MAX_FOLD tokens folded per unit between builds.
  */
 #ifndef MOG_H
 #define MOG_H
@@ -48,13 +48,15 @@ extern "C" {
 
 #define MOG_MAX_SEQ 256
 #define MOG_MAX_LEN (1 << 22)
+#define MOG_MAX_FOLD (1 << 15)
 
 typedef enum {
   MOG_OK = 0,
   MOG_ERR_INVALID_ARG = 1, /* null pointer, bad size, inconsistent shapes   */
   MOG_ERR_UNSUPPORTED = 2, /* a valid request this build does not cover    */
   MOG_ERR_WORKSPACE = 3,   /* workspace or layout buffer too small          */
-  MOG_ERR_HIP = 4          /* a HIP launch or runtime call failed           */
+  MOG_ERR_HIP = 4,         /* a HIP launch or runtime call failed           */
+  MOG_ERR_CAPACITY = 5     /* a layout's fold area is full: build again     */
 } mog_status;
 
 typedef enum { MOG_F32 = 0, MOG_BF16 = 1 } mog_dtype;
@@ -94,18 +96,22 @@ typedef struct {
   int32_t dtype;            /* dtype of the reordered K/V copy (= the cache's) */
   int32_t n_sink;           /* anchors at the start of every sequence */
   int32_t n_recent;         /* anchors at the end of every sequence   */
-  const int32_t* seq_lens;  /* HOST [n_seq] */
+  int32_t fold_capacity;    /* rows per unit kept for mog_append, 0..MOG_MAX_FOLD */
+  const int32_t* seq_lens;  /* HOST [n_seq] lengths at the build */
 } mog_dims;
 
 /* Per-unit geometry, one unit = one (sequence, KV head); unit id
- * u = seq * n_kv_heads + kv_head.  C = min(ceil(sqrt(N)), N_mid) clusters,
- * S = ceil(log2(N)) subclusters per cluster, N_mid = N - n_sink - n_recent
- * middle-region tokens (the clustered part). */
+ * u = seq * n_kv_heads + kv_head.  With N_b the length at the build:
+ * C = min(ceil(sqrt(N_b)), n_mid) clusters, S = ceil(log2(N_b)) subclusters
+ * per cluster, n_mid = N_b - n_sink - n_recent middle-region tokens (the
+ * clustered part).  N is the current length, N_b + n_fold: mog_append
+ * folds the tokens that leave the recent window into the partition. */
 typedef struct {
   int32_t seq, kv_head;
   int32_t N, n_mid;
   int32_t C, S;
-  int32_t reserved0, reserved1;
+  int32_t n_fold;   /* tokens folded since the build (rows in the fold area)  */
+  int32_t reserved1;
   int64_t row_base; /* first row of this unit in k_mid / v_mid / perm        */
   int64_t cl_base;  /* first cluster of this unit in cl_ms / cl_vbar         */
   int64_t sub_base; /* first subcluster of this unit in sub_ms / sub_vbar    */
@@ -114,8 +120,11 @@ typedef struct {
 
 /* A built (or imported) cluster layout.  Plain descriptor: every pointer
  * points into the caller's layout buffer.
- *  k_mid, v_mid  [total_mid][head_dim] dtype: the middle region of every unit,
- *                rows ordered by (cluster, subcluster, token position).
+ *  k_mid, v_mid  [total_mid + n_units * fold_capacity][head_dim] dtype: the
+ *                middle region of every unit, rows ordered by (cluster,
+ *                subcluster, token position); then the fold area: row
+ *                total_mid + u * fold_capacity + f holds the f-th token
+ *                folded into unit u.
  *  perm          [total_mid] int32: token position of every reordered row.
  *  sub_off       per unit C*S+1 int32 row offsets relative to row_base;
  *                subcluster i of cluster j owns rows [sub_off[j*S+i],
@@ -123,12 +132,22 @@ typedef struct {
  *  cl_ms, sub_ms [groups][2*head_dim] float32: mean key (first head_dim
  *                entries) then diagonal population variance of the keys.
  *  cl_vbar, sub_vbar [groups][head_dim] float32: mean value.
- *  units         DEVICE copy of the mog_unit table (n_units entries). */
+ *                Group statistics cover the folded tokens too.
+ *  fold_sub      [n_units][fold_capacity] int32: subcluster (j*S+i, within
+ *                the unit) of every folded token, in fold order.
+ *  fold_pos      [n_units][fold_capacity] int32: its token position.
+ *  cl_fold, sub_fold [groups] int32: folded tokens per cluster / subcluster
+ *                (a group holds its sub_off rows plus these).
+ *  units         DEVICE copy of the mog_unit table (n_units entries).
+ *  seq_lens      current lengths; fold_count[s] of them were folded, so
+ *                seq_lens[s] - fold_count[s] is the length at the build. */
 typedef struct {
   int32_t n_seq, n_kv_heads, head_dim, dtype, n_sink, n_recent;
   int32_t n_units;
   int32_t max_C, max_S;
+  int32_t fold_capacity;
   int32_t seq_lens[MOG_MAX_SEQ];
+  int32_t fold_count[MOG_MAX_SEQ];
   int64_t total_mid, total_cl, total_sub, total_off;
   mog_unit* units;
   void* k_mid;
@@ -139,13 +158,17 @@ typedef struct {
   float* cl_vbar;
   float* sub_ms;
   float* sub_vbar;
+  int32_t* fold_sub;
+  int32_t* fold_pos;
+  int32_t* cl_fold;
+  int32_t* sub_fold;
 } mog_layout;
 
 typedef struct {
   int32_t kmeans_iters; /* Lloyd rounds before the final assignment (10)   */
   int32_t n_sink;
   int32_t n_recent;
-  int32_t reserved;
+  int32_t fold_capacity; /* rows per unit kept for mog_append (0: none)    */
   uint64_t seed;        /* seeds the Forgy initialisation of every unit    */
 } mog_build_params;
 
@@ -190,8 +213,9 @@ mog_status mog_layout_size(const mog_dims* dims, size_t* bytes);
 
 /* Carve `layout_mem` (DEVICE, >= mog_layout_size bytes, 256-byte aligned)
  * into a layout for `dims`, fill `out` (host) and enqueue the write of the
- * device unit table.  mog_build calls this itself; it is exported so a
- * caller can import a layout computed elsewhere by writing the arrays. */
+ * device unit table and the zeroing of the fold counts.  mog_build calls
+ * this itself; it is exported so a caller can import a layout computed
+ * elsewhere by writing the arrays (cl_fold / sub_fold must stay zero). */
 mog_status mog_layout_init(const mog_dims* dims, void* layout_mem, size_t layout_bytes,
                            mog_layout* out, hipStream_t stream);
 
@@ -242,6 +266,26 @@ mog_status mog_decode(const mog_layout* layout, const mog_kv* kv, const float* q
                       const mog_decode_params* params, float* out, float* lse,
                       int32_t* sel_c, int32_t* sel_s, void* ws, size_t ws_bytes,
                       hipStream_t stream);
+
+/* Incremental decode (Iceberg Attention abstract: the partition is built
+ * once after prefill and then serves every decode step).  The sequences of
+ * `kv` are the layout's sequences grown by a_s = kv->seq_lens[s] -
+ * layout->seq_lens[s] >= 0 tokens.  The a_s tokens that leave the recent
+ * window, positions [N_s - n_recent, N_s - n_recent + a_s) with N_s =
+ * layout->seq_lens[s], are folded into the partition one by one, oldest
+ * first: each joins the nonempty cluster whose mean key is nearest (squared
+ * distance in float64, ties to the lower id), then the nearest nonempty
+ * subcluster of that cluster; both groups' count, mean key, population
+ * variance and mean value are updated by Welford's running formulas
+ * (float64 from the stored float32, stored float32), and the token's K/V
+ * rows are copied into the unit's fold area, from which mog_decode reads
+ * them whenever their subcluster is chosen.  C, S and the rest of the
+ * partition are kept.  Updates layout->seq_lens and layout->fold_count
+ * (HOST) and enqueues the device updates on `stream`; no workspace.
+ * MOG_ERR_CAPACITY (nothing enqueued, layout unchanged) when a sequence's
+ * folded tokens would exceed layout->fold_capacity: build again.  Calls on
+ * one layout must not overlap with each other or with mog_decode. */
+mog_status mog_append(const mog_kv* kv, mog_layout* layout, hipStream_t stream);
 
 /* Exact dense decode attention over all tokens of every sequence (the
  * in-library baseline): out = softmax(scale K q)^T V.  Same q/out/lse/ws

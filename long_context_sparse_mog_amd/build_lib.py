@@ -22,7 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_lib")
 OBJ_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(OUT_DIR, "libmog.so")
-SOURCES = ["api.cpp", "decode.hip", "build.hip"]
+SOURCES = ["api.cpp", "decode.hip", "build.hip", "append.hip"]
 HEADERS = ["mog_internal.h", "attn_tile.h"]
 ARCH = "gfx950"
 

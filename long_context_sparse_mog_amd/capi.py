@@ -13,8 +13,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "lib
 
 MOG_MAX_SEQ = 256
 MOG_MAX_LEN = 1 << 22
+MOG_MAX_FOLD = 1 << 15
 
-MOG_OK, MOG_ERR_INVALID_ARG, MOG_ERR_UNSUPPORTED, MOG_ERR_WORKSPACE, MOG_ERR_HIP = range(5)
+(MOG_OK, MOG_ERR_INVALID_ARG, MOG_ERR_UNSUPPORTED, MOG_ERR_WORKSPACE, MOG_ERR_HIP,
+ MOG_ERR_CAPACITY) = range(6)
 MOG_F32, MOG_BF16 = 0, 1
 MOG_KV_CONTIGUOUS, MOG_KV_PAGED = 0, 1
 MOG_OP_BUILD, MOG_OP_DECODE, MOG_OP_DENSE = 0, 1, 2
@@ -33,26 +35,29 @@ class mog_kv(C.Structure):
 
 class mog_dims(C.Structure):
     _fields_ = [("n_seq", i32), ("n_kv_heads", i32), ("head_dim", i32), ("dtype", i32),
-                ("n_sink", i32), ("n_recent", i32), ("seq_lens", C.POINTER(i32))]
+                ("n_sink", i32), ("n_recent", i32), ("fold_capacity", i32),
+                ("seq_lens", C.POINTER(i32))]
 
 
 class mog_unit(C.Structure):
     _fields_ = [("seq", i32), ("kv_head", i32), ("N", i32), ("n_mid", i32), ("C", i32),
-                ("S", i32), ("reserved0", i32), ("reserved1", i32), ("row_base", i64),
+                ("S", i32), ("n_fold", i32), ("reserved1", i32), ("row_base", i64),
                 ("cl_base", i64), ("sub_base", i64), ("off_base", i64)]
 
 
 class mog_layout(C.Structure):
     _fields_ = [("n_seq", i32), ("n_kv_heads", i32), ("head_dim", i32), ("dtype", i32),
                 ("n_sink", i32), ("n_recent", i32), ("n_units", i32), ("max_C", i32),
-                ("max_S", i32), ("seq_lens", i32 * MOG_MAX_SEQ), ("total_mid", i64),
+                ("max_S", i32), ("fold_capacity", i32), ("seq_lens", i32 * MOG_MAX_SEQ),
+                ("fold_count", i32 * MOG_MAX_SEQ), ("total_mid", i64),
                 ("total_cl", i64), ("total_sub", i64), ("total_off", i64), ("units", vp),
                 ("k_mid", vp), ("v_mid", vp), ("perm", vp), ("sub_off", vp), ("cl_ms", vp),
-                ("cl_vbar", vp), ("sub_ms", vp), ("sub_vbar", vp)]
+                ("cl_vbar", vp), ("sub_ms", vp), ("sub_vbar", vp), ("fold_sub", vp),
+                ("fold_pos", vp), ("cl_fold", vp), ("sub_fold", vp)]
 
 
 class mog_build_params(C.Structure):
-    _fields_ = [("kmeans_iters", i32), ("n_sink", i32), ("n_recent", i32), ("reserved", i32),
+    _fields_ = [("kmeans_iters", i32), ("n_sink", i32), ("n_recent", i32), ("fold_capacity", i32),
                 ("seed", C.c_uint64)]
 
 
@@ -76,6 +81,7 @@ SIGNATURES = {
                         C.c_size_t, C.POINTER(mog_layout), vp]),
     "mog_decode": (i32, [C.POINTER(mog_layout), C.POINTER(mog_kv), vp,
                          C.POINTER(mog_decode_params), vp, vp, vp, vp, vp, C.c_size_t, vp]),
+    "mog_append": (i32, [C.POINTER(mog_kv), C.POINTER(mog_layout), vp]),
     "mog_dense_decode": (i32, [C.POINTER(mog_kv), vp, C.POINTER(mog_decode_params), vp, vp, vp,
                                C.c_size_t, vp]),
     "mog_status_string": (C.c_char_p, [i32]),

@@ -50,7 +50,8 @@ struct Totals {
 
 struct LayoutPlan {
   Totals t;
-  size_t o_units, o_kmid, o_vmid, o_perm, o_suboff, o_clms, o_clvb, o_subms, o_subvb, bytes;
+  size_t o_units, o_kmid, o_vmid, o_perm, o_suboff, o_clms, o_clvb, o_subms, o_subvb;
+  size_t o_foldsub, o_foldpos, o_clfold, o_subfold, bytes;
 };
 
 mog_status check_dims(const mog_dims* d) {
@@ -63,6 +64,8 @@ mog_status check_dims(const mog_dims* d) {
   if (d->dtype != MOG_F32 && d->dtype != MOG_BF16) return fail(MOG_ERR_UNSUPPORTED, "dtype=%d", d->dtype);
   if (d->n_sink < 0 || d->n_recent < 0)
     return fail(MOG_ERR_INVALID_ARG, "negative anchor count (n_sink=%d, n_recent=%d)", d->n_sink, d->n_recent);
+  if (d->fold_capacity < 0 || d->fold_capacity > MOG_MAX_FOLD)
+    return fail(MOG_ERR_INVALID_ARG, "fold_capacity=%d outside [0, %d]", d->fold_capacity, MOG_MAX_FOLD);
   if (!d->seq_lens) return fail(MOG_ERR_INVALID_ARG, "seq_lens is NULL");
   for (int s = 0; s < d->n_seq; ++s) {
     const int N = d->seq_lens[s];
@@ -87,16 +90,22 @@ LayoutPlan plan_layout(const mog_dims* d) {
   }
   const int64_t nu = (int64_t)d->n_seq * d->n_kv_heads;
   const int D = d->head_dim;
+  // K/V rows: the reordered middle regions, then each unit's fold area
+  const size_t rows = (size_t)p.t.mid + (size_t)nu * d->fold_capacity;
   size_t o = 0;
   p.o_units = o; o = align_up(o + nu * sizeof(mog_unit));
-  p.o_kmid = o; o = align_up(o + (size_t)p.t.mid * D * esize(d->dtype));
-  p.o_vmid = o; o = align_up(o + (size_t)p.t.mid * D * esize(d->dtype));
+  p.o_kmid = o; o = align_up(o + rows * D * esize(d->dtype));
+  p.o_vmid = o; o = align_up(o + rows * D * esize(d->dtype));
   p.o_perm = o; o = align_up(o + (size_t)p.t.mid * 4);
   p.o_suboff = o; o = align_up(o + (size_t)p.t.off * 4);
   p.o_clms = o; o = align_up(o + (size_t)p.t.cl * 2 * D * 4);
   p.o_clvb = o; o = align_up(o + (size_t)p.t.cl * D * 4);
   p.o_subms = o; o = align_up(o + (size_t)p.t.sub * 2 * D * 4);
   p.o_subvb = o; o = align_up(o + (size_t)p.t.sub * D * 4);
+  p.o_foldsub = o; o = align_up(o + (size_t)nu * d->fold_capacity * 4);
+  p.o_foldpos = o; o = align_up(o + (size_t)nu * d->fold_capacity * 4);
+  p.o_clfold = o; o = align_up(o + (size_t)p.t.cl * 4);
+  p.o_subfold = o; o = align_up(o + (size_t)p.t.sub * 4);
   p.bytes = o;
   return p;
 }
@@ -205,7 +214,7 @@ DecodePlan plan_decode(const mog_layout* L, const mog_decode_params* p) {
     const int sk = seq_top(p->top_s_per_seq, p->top_s, s);
     d.c_stride = std::max(d.c_stride, c);
     d.s_stride = std::max(d.s_stride, sk);
-    const UnitSizes z = unit_sizes(L->seq_lens[s], L->n_sink, L->n_recent);
+    const UnitSizes z = unit_sizes(L->seq_lens[s] - L->fold_count[s], L->n_sink, L->n_recent);
     d.nb_chosen = std::max<int>(d.nb_chosen, std::min(z.C, d.G * std::min(c, z.C)));
   }
   if (p->splits > 0) {
@@ -235,7 +244,8 @@ DecodePlan plan_decode(const mog_layout* L, const mog_decode_params* p) {
   d.o_tbase = o; o = align_up(o + ncw * 4);
   d.o_ntl = o; o = align_up(o + ncw * 4);
   d.o_tiles = o;
-  o = align_up(o + (size_t)(tile_unit_base(L->total_mid, L->total_cl, (int)nu) + 2) * sizeof(TileRec));
+  o = align_up(o + (size_t)(tile_unit_base(L->total_mid, L->total_cl, (int)nu, L->fold_capacity) + 2) *
+                       sizeof(TileRec));
   d.o_res = o; o = align_up(o + (size_t)nu * d.nb_res * G * RS * 4);
   d.o_ex = o; o = align_up(o + (size_t)d.nblk * G * RS * 4);
   d.bytes = o;
@@ -266,6 +276,21 @@ DensePlan plan_dense(const mog_kv* kv, const mog_decode_params* p) {
   return d;
 }
 
+mog_status check_layout_arrays(const mog_layout* L) {
+  if (!L->units || !L->k_mid || !L->v_mid || !L->sub_off || !L->cl_ms || !L->cl_vbar || !L->sub_ms ||
+      !L->sub_vbar || !L->cl_fold || !L->sub_fold)
+    return fail(MOG_ERR_INVALID_ARG, "layout has NULL arrays (not initialised?)");
+  if (L->fold_capacity < 0 || L->fold_capacity > MOG_MAX_FOLD)
+    return fail(MOG_ERR_INVALID_ARG, "layout fold_capacity=%d outside [0, %d]", L->fold_capacity, MOG_MAX_FOLD);
+  if (L->fold_capacity > 0 && (!L->fold_sub || !L->fold_pos))
+    return fail(MOG_ERR_INVALID_ARG, "layout has NULL fold arrays");
+  for (int s = 0; s < L->n_seq; ++s)
+    if (L->fold_count[s] < 0 || L->fold_count[s] > L->fold_capacity)
+      return fail(MOG_ERR_INVALID_ARG, "layout fold_count[%d]=%d outside [0, %d]", s, L->fold_count[s],
+                  L->fold_capacity);
+  return MOG_OK;
+}
+
 mog_status check_layout_vs_kv(const mog_layout* L, const mog_kv* kv) {
   if (!L) return fail(MOG_ERR_INVALID_ARG, "layout is NULL");
   if (L->n_seq != kv->n_seq || L->n_kv_heads != kv->n_kv_heads || L->head_dim != kv->head_dim ||
@@ -277,10 +302,7 @@ mog_status check_layout_vs_kv(const mog_layout* L, const mog_kv* kv) {
     if (L->seq_lens[s] != kv->seq_lens[s])
       return fail(MOG_ERR_INVALID_ARG, "sequence %d: layout length %d, kv length %d", s, L->seq_lens[s],
                   kv->seq_lens[s]);
-  if (!L->units || !L->k_mid || !L->v_mid || !L->sub_off || !L->cl_ms || !L->cl_vbar || !L->sub_ms ||
-      !L->sub_vbar)
-    return fail(MOG_ERR_INVALID_ARG, "layout has NULL arrays (not initialised?)");
-  return MOG_OK;
+  return check_layout_arrays(L);
 }
 
 // ------------------------------------------------------------------------
@@ -299,6 +321,7 @@ mog_status check_build(const mog_kv* kv, const mog_build_params* bp, mog_dims* d
   d.dtype = kv->dtype;
   d.n_sink = bp->n_sink;
   d.n_recent = bp->n_recent;
+  d.fold_capacity = bp->fold_capacity;
   d.seq_lens = kv->seq_lens;
   if ((st = check_dims(&d)) != MOG_OK) return st;
   *dims_out = d;
@@ -348,6 +371,7 @@ const char* mog_status_string(mog_status st) {
     case MOG_ERR_UNSUPPORTED: return "unsupported";
     case MOG_ERR_WORKSPACE: return "workspace too small";
     case MOG_ERR_HIP: return "HIP error";
+    case MOG_ERR_CAPACITY: return "fold area full (build again)";
   }
   return "unknown status";
 }
@@ -383,6 +407,7 @@ static mog_status layout_carve(const mog_dims* dims, void* mem, size_t mem_bytes
   L.n_units = dims->n_seq * dims->n_kv_heads;
   L.max_C = p.t.max_C;
   L.max_S = p.t.max_S;
+  L.fold_capacity = dims->fold_capacity;
   for (int s = 0; s < dims->n_seq; ++s) L.seq_lens[s] = dims->seq_lens[s];
   L.total_mid = p.t.mid;
   L.total_cl = p.t.cl;
@@ -397,6 +422,10 @@ static mog_status layout_carve(const mog_dims* dims, void* mem, size_t mem_bytes
   L.cl_vbar = reinterpret_cast<float*>(b + p.o_clvb);
   L.sub_ms = reinterpret_cast<float*>(b + p.o_subms);
   L.sub_vbar = reinterpret_cast<float*>(b + p.o_subvb);
+  L.fold_sub = dims->fold_capacity ? reinterpret_cast<int32_t*>(b + p.o_foldsub) : nullptr;
+  L.fold_pos = dims->fold_capacity ? reinterpret_cast<int32_t*>(b + p.o_foldpos) : nullptr;
+  L.cl_fold = reinterpret_cast<int32_t*>(b + p.o_clfold);
+  L.sub_fold = reinterpret_cast<int32_t*>(b + p.o_subfold);
   *out = L;
   return MOG_OK;
 }
@@ -418,15 +447,16 @@ mog_status mog_layout_unit(const mog_layout* L, int32_t unit, mog_unit* out) {
   if (!L || !out) return fail(MOG_ERR_INVALID_ARG, "NULL argument");
   if (unit < 0 || unit >= L->n_units) return fail(MOG_ERR_INVALID_ARG, "unit %d outside [0, %d)", unit, L->n_units);
   const int s = unit / L->n_kv_heads, kvh = unit % L->n_kv_heads;
+  // geometry follows from the lengths at the build
   int64_t row = 0, cl = 0, sub = 0, offb = 0;
   for (int s2 = 0; s2 < s; ++s2) {
-    const UnitSizes z = unit_sizes(L->seq_lens[s2], L->n_sink, L->n_recent);
+    const UnitSizes z = unit_sizes(L->seq_lens[s2] - L->fold_count[s2], L->n_sink, L->n_recent);
     row += (int64_t)L->n_kv_heads * z.n_mid;
     cl += (int64_t)L->n_kv_heads * z.C;
     sub += (int64_t)L->n_kv_heads * z.C * z.S;
     offb += (int64_t)L->n_kv_heads * (z.C * z.S + 1);
   }
-  const UnitSizes z = unit_sizes(L->seq_lens[s], L->n_sink, L->n_recent);
+  const UnitSizes z = unit_sizes(L->seq_lens[s] - L->fold_count[s], L->n_sink, L->n_recent);
   mog_unit U;
   U.seq = s;
   U.kv_head = kvh;
@@ -434,7 +464,8 @@ mog_status mog_layout_unit(const mog_layout* L, int32_t unit, mog_unit* out) {
   U.n_mid = z.n_mid;
   U.C = z.C;
   U.S = z.S;
-  U.reserved0 = U.reserved1 = 0;
+  U.n_fold = L->fold_count[s];
+  U.reserved1 = 0;
   U.row_base = row + (int64_t)kvh * z.n_mid;
   U.cl_base = cl + (int64_t)kvh * z.C;
   U.sub_base = sub + (int64_t)kvh * z.C * z.S;
@@ -533,6 +564,46 @@ mog_status mog_decode(const mog_layout* layout, const mog_kv* kv, const float* q
   x.ws.ex_part = reinterpret_cast<float*>(w + d.o_ex);
   hipError_t e = launch_decode(x, stream);
   if (e != hipSuccess) return fail(MOG_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+mog_status mog_append(const mog_kv* kv, mog_layout* layout, hipStream_t stream) {
+  mog_status st;
+  if ((st = check_kv(kv)) != MOG_OK) return st;
+  if (!layout) return fail(MOG_ERR_INVALID_ARG, "layout is NULL");
+  const mog_layout* L = layout;
+  if (L->n_seq != kv->n_seq || L->n_kv_heads != kv->n_kv_heads || L->head_dim != kv->head_dim ||
+      L->dtype != kv->dtype)
+    return fail(MOG_ERR_INVALID_ARG, "layout (n_seq=%d, n_kv_heads=%d, head_dim=%d, dtype=%d) does not match kv "
+                "(%d, %d, %d, %d)", L->n_seq, L->n_kv_heads, L->head_dim, L->dtype, kv->n_seq, kv->n_kv_heads,
+                kv->head_dim, kv->dtype);
+  if ((st = check_layout_arrays(L)) != MOG_OK) return st;
+  AppendLaunch x;
+  memset(&x, 0, sizeof(x));
+  int total = 0;
+  for (int s = 0; s < L->n_seq; ++s) {
+    const int a = kv->seq_lens[s] - L->seq_lens[s];
+    if (a < 0)
+      return fail(MOG_ERR_INVALID_ARG, "sequence %d: kv length %d below the layout's %d", s, kv->seq_lens[s],
+                  L->seq_lens[s]);
+    if (L->fold_count[s] + a > L->fold_capacity)
+      return fail(MOG_ERR_CAPACITY, "sequence %d: %d folded + %d new tokens exceed the fold capacity %d", s,
+                  L->fold_count[s], a, L->fold_capacity);
+    x.seq[s].len = L->seq_lens[s];
+    x.seq[s].n_new = (uint16_t)a;
+    x.seq[s].f0 = (uint16_t)L->fold_count[s];
+    total += a;
+  }
+  if (total == 0) return ok();
+  x.L = *L;
+  x.kv = make_kvref(kv);
+  x.n_seq = L->n_seq;
+  hipError_t e = launch_append(x, stream);
+  if (e != hipSuccess) return fail(MOG_ERR_HIP, "append launch: %s", hipGetErrorString(e));
+  for (int s = 0; s < L->n_seq; ++s) {
+    layout->fold_count[s] += x.seq[s].n_new;
+    layout->seq_lens[s] += x.seq[s].n_new;
+  }
   return ok();
 }
 

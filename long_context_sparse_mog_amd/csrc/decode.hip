@@ -27,6 +27,14 @@ struct LayoutRef {
   const float* cl_vbar;
   const float* sub_ms;
   const float* sub_vbar;
+  // folded tokens (incremental decode): per-group counts, and per unit the
+  // subcluster of every fold row; unit u's fold rows start at layout row
+  // fold_row0 + u * fold_cap
+  const int32_t* cl_fold;
+  const int32_t* sub_fold;
+  const int32_t* fold_sub;
+  int64_t fold_row0;
+  int32_t fold_cap;
 };
 
 struct DArgs {
@@ -199,7 +207,7 @@ __global__ __launch_bounds__(256) void k_score_clusters(DArgs a) {
   const int g = g0 + lane;
   if (lane < kScoreRowsPerWave && g < U.C) {
     const int64_t cw = (int64_t)u * a.cstride + g;
-    const int n = off[(g + 1) * U.S] - off[g * U.S];
+    const int n = off[(g + 1) * U.S] - off[g * U.S] + a.L.cl_fold[U.cl_base + g];
     const float lg = n > 0 ? log2f((float)n) : -INFINITY;
 #pragma unroll
     for (int h = 0; h < G; ++h) a.ws.cl_score[cw * G + h] = n > 0 ? mine[h] + lg : -INFINITY;
@@ -240,13 +248,15 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
   const mog_unit U = uni_unit(a.L.units + u);
   const int C = U.C;
   if (tid == 0) a.ws.unit_rows[u] = 0;
-  // the sizes of the clusters of this wave's tail slots
+  // the sizes of the clusters of this wave's tail slots: reordered rows and
+  // folded rows
   const int32_t* off = a.L.sub_off + U.off_base;
-  int bound[NSW];
+  int bound[NSW], bfold[NSW];
 #pragma unroll
   for (int t = 0; t < NSW; ++t) {
     const int i = min(64 * (h + G * t) + lane, C - 1);
     bound[t] = off[(i + 1) * U.S] - off[i * U.S];
+    bfold[t] = a.L.cl_fold[U.cl_base + i];
   }
   if (a.shared) {
     // one selection per KV head: the key of a cluster is the sum over the
@@ -395,7 +405,7 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
   }
   __syncthreads();
   // tail: cluster i = 64 j + lane.  A chosen cluster takes ceil(rows/32) + S
-  // tile slots, the most its chosen subclusters can make.  First the
+  // + folded rows tile slots, the most its chosen subclusters can make.  First the
   // per-slot counts, then each slot's list positions and slot bases from
   // the counts of the slots before it.
   uint32_t um[NSW];
@@ -409,7 +419,7 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
 #pragma unroll
       for (int g = 0; g < G; ++g) um[t] |= (uint32_t)((selb[g][j] >> lane) & 1ull) << g;
       if (64 * j + lane >= C) um[t] = 0u;
-      tcnt[t] = um[t] != 0u ? (bound[t] + 31) / 32 + U.S : 0;
+      tcnt[t] = um[t] != 0u ? (bound[t] + 31) / 32 + U.S + bfold[t] : 0;
       const int n = __popcll(__ballot(um[t] != 0u));
       const int nt = (int)wave_reduce_uniform((uint32_t)tcnt[t], [](uint32_t x, uint32_t y) { return x + y; }, 0u);
       if (lane == 0) {
@@ -493,7 +503,8 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
   __shared__ float lds_sc[kMaxS][G];
   __shared__ float lds_gs[kMaxS];  // shared selection: summed mass fractions
   __shared__ uint32_t lds_sm[kMaxS];
-  __shared__ int lds_cnt[kMaxS];
+  __shared__ int lds_cnt[kMaxS];   // reordered rows of each subcluster
+  __shared__ int lds_fcnt[kMaxS];  // folded rows of each subcluster
   __shared__ int lds_off[kMaxS + 1];
   __shared__ int sh[16];
   const int u = blockIdx.x, tid = threadIdx.x;
@@ -549,8 +560,10 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
       {
         const int i = min(tid, S - 1);
         const int o0 = off[g * S + i], o1 = off[g * S + i + 1];
+        const int fc = a.L.sub_fold[sg0 + i];
         if (tid < S) {
           lds_cnt[tid] = o1 - o0;
+          lds_fcnt[tid] = fc;
           lds_off[tid] = o0;
         }
         if (tid == S - 1) lds_off[S] = o1;
@@ -559,7 +572,7 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
 #pragma unroll
       for (int k = 0; k < RPW; ++k) {
         const int i = min(wave + 4 * k, S - 1);
-        rcnt[k] = off[g * S + i + 1] - off[g * S + i];
+        rcnt[k] = off[g * S + i + 1] - off[g * S + i] + a.L.sub_fold[sg0 + i];
       }
       if (tid < kMaxS) lds_sm[tid] = 0u;
       // full scores (count term added; -inf for an empty subcluster and for
@@ -643,8 +656,9 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
           for (int j = all_h; j < a.s_stride; ++j) a.sel_s[base + j] = -1;
       }
       const int my_cnt = lane < S ? lds_cnt[lane] : 0;
+      const int my_fcnt = lane < S ? lds_fcnt[lane] : 0;
       if (wave == 0) {
-        const uint32_t rows = (lane < S && lds_sm[lane]) ? (uint32_t)my_cnt : 0u;
+        const uint32_t rows = (lane < S && lds_sm[lane]) ? (uint32_t)(my_cnt + my_fcnt) : 0u;
         const int rsum = (int)wave_reduce_uniform(rows, [](uint32_t p, uint32_t q) { return p + q; }, 0u);
         if (lane == 0) atomicAdd(&a.ws.unit_rows[u], rsum);
         // exact tiles of the cluster: a run is a maximal sequence of chosen
@@ -671,12 +685,39 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
         const int ntl = head ? (run_en - st + 31) / 32 : 0;
         const int incl = wave_incl_scan(ntl);
         const int n_tiles = __builtin_amdgcn_readlane(incl, 63);
+        TileRec* ctiles = a.ws.tiles + tile_unit_base(U.row_base, U.cl_base, u, a.L.fold_cap) + uni(tb_x);
         if (head) {
-          TileRec* dstt = a.ws.tiles + tile_unit_base(U.row_base, U.cl_base, u) + uni(tb_x) + (incl - ntl);
+          TileRec* dstt = ctiles + (incl - ntl);
           for (int r = st; r < run_en; r += 32, ++dstt)
             *dstt = TileRec{(U.row_base + r) * (int64_t)a.L_head_dim, min(32, run_en - r), m};
         }
-        if (lane == 0) a.ws.ch_ntiles[cw + x] = n_tiles;
+        int n_all = n_tiles;
+        // folded rows of the chosen subclusters, after the reordered ones:
+        // the unit's fold rows are scanned 64 at a time (lane l: row f0 + l);
+        // a tile is a run of consecutive fold rows with one head mask, cut at
+        // every 32nd row
+        if (__ballot(lane < S && m != 0u && my_fcnt > 0)) {
+          const int nf = U.n_fold;
+          const int32_t* fs = a.L.fold_sub + (int64_t)u * a.L.fold_cap;
+          const int64_t frow = a.L.fold_row0 + (int64_t)u * a.L.fold_cap;
+          TileRec* ft = ctiles + n_tiles;
+          int nt = 0;
+          for (int f0 = 0; f0 < nf; f0 += 64) {
+            const int f = f0 + lane;
+            const int li = (f < nf ? fs[f] : -1) - g * S;
+            const uint32_t fm = (li >= 0 && li < S) ? lds_sm[li] : 0u;
+            const uint32_t fm_prv = (uint32_t)__shfl_up((int)fm, 1, 64);
+            const bool cont = fm != 0u && (lane & 31) != 0 && fm_prv == fm;
+            const bool fhead = fm != 0u && !cont;
+            const unsigned long long fhb = __ballot(fhead);
+            const unsigned long long after = __ballot(!cont) & ~((2ull << lane) - 1ull);
+            const int fend = after ? __ffsll((long long)after) - 1 : 64;
+            if (fhead) ft[nt + __popcll(fhb & below)] = TileRec{(frow + f) * (int64_t)a.L_head_dim, fend - lane, fm};
+            nt += __popcll(fhb);
+          }
+          n_all += nt;
+        }
+        if (lane == 0) a.ws.ch_ntiles[cw + x] = n_all;
       }
       // residual of the subclusters a choosing head left out: wave w takes
       // subclusters w, w+4, ...
@@ -686,7 +727,7 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
         for (int k = 0; k < RPW; ++k) {
           const int i = wave + 4 * k;
           need[k] = 0u;
-          if (i < S && lds_cnt[i] > 0) need[k] = mask & ~lds_sm[i];
+          if (i < S && lds_cnt[i] + lds_fcnt[i] > 0) need[k] = mask & ~lds_sm[i];
         }
 #pragma unroll
         for (int k = 0; k < RPW; ++k) {
@@ -712,7 +753,7 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
       const int g = min(y * kRestClustersPerBlock + wave * RCW + k, C - 1);
       const int64_t cg = cw + g;
       mask[k] = a.ws.cl_mask[cg];
-      n_g[k] = off[(g + 1) * S] - off[g * S];
+      n_g[k] = off[(g + 1) * S] - off[g * S] + a.L.cl_fold[U.cl_base + g];
       load_floats<VPL>(a.L.cl_vbar + (U.cl_base + g) * D + lane * VPL, vb[k]);
 #pragma unroll
       for (int h = 0; h < G; ++h) sc[k][h] = a.ws.cl_score[cg * G + h];
@@ -919,7 +960,7 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
   if (k0 < k1) {
     const T* km = static_cast<const T*>(a.L.k_mid);
     const T* vm = static_cast<const T*>(a.L.v_mid);
-    const TileRec* utiles = a.ws.tiles + tile_unit_base(U.row_base, U.cl_base, u);
+    const TileRec* utiles = a.ws.tiles + tile_unit_base(U.row_base, U.cl_base, u, a.L.fold_cap);
     TileRec* tl = tiles[wave];
     const int64_t anc_base = kv.paged ? 0 : kv_row_offset(kv, U.seq, U.kv_head, 0, D);
     while (k0 < k1) {
@@ -1135,7 +1176,14 @@ __global__ __launch_bounds__(256, 2) void k_dense(KVRef kv, const float* q, int 
 // ---------------------------------------------------------------------------
 // Unit table of a layout (same arithmetic as the host carving).
 // ---------------------------------------------------------------------------
-__global__ void k_layout_table(mog_unit* units, SeqArgs seq, int Hkv, int n_sink, int n_recent) {
+__global__ void k_layout_table(mog_unit* units, SeqArgs seq, int Hkv, int n_sink, int n_recent,
+                               int32_t* cl_fold, int64_t n_cl, int32_t* sub_fold, int64_t n_sub) {
+  // no folded tokens yet: zero the per-group fold counts
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_cl + n_sub; i += step) {
+    if (i < n_cl) cl_fold[i] = 0;
+    else sub_fold[i - n_cl] = 0;
+  }
   const int u = blockIdx.x * blockDim.x + threadIdx.x;
   if (u >= seq.n_seq * Hkv) return;
   const int s = u / Hkv, kvh = u % Hkv;
@@ -1155,7 +1203,8 @@ __global__ void k_layout_table(mog_unit* units, SeqArgs seq, int Hkv, int n_sink
   U.n_mid = z.n_mid;
   U.C = z.C;
   U.S = z.S;
-  U.reserved0 = U.reserved1 = 0;
+  U.n_fold = 0;
+  U.reserved1 = 0;
   U.row_base = row + (int64_t)kvh * z.n_mid;
   U.cl_base = cl + (int64_t)kvh * z.C;
   U.sub_base = sub + (int64_t)kvh * z.C * z.S;
@@ -1168,8 +1217,10 @@ __global__ void k_layout_table(mog_unit* units, SeqArgs seq, int Hkv, int n_sink
 // ---------------------------------------------------------------------------
 hipError_t launch_layout_table(const mog_layout& L, const SeqArgs& seq, hipStream_t s) {
   const int n = L.n_units;
-  hipLaunchKernelGGL(k_layout_table, dim3((n + 255) / 256), dim3(256), 0, s, L.units, seq,
-                     L.n_kv_heads, L.n_sink, L.n_recent);
+  const int64_t n_cnt = L.total_cl + L.total_sub;
+  const int64_t nb = max((int64_t)(n + 255) / 256, min((n_cnt + 255) / 256, (int64_t)1024));
+  hipLaunchKernelGGL(k_layout_table, dim3((unsigned)nb), dim3(256), 0, s, L.units, seq, L.n_kv_heads, L.n_sink,
+                     L.n_recent, L.cl_fold, L.total_cl, L.sub_fold, L.total_sub);
   return hipGetLastError();
 }
 
@@ -1234,6 +1285,11 @@ hipError_t launch_decode(const DecodeLaunch& x, hipStream_t s) {
   a.L.cl_vbar = x.L.cl_vbar;
   a.L.sub_ms = x.L.sub_ms;
   a.L.sub_vbar = x.L.sub_vbar;
+  a.L.cl_fold = x.L.cl_fold;
+  a.L.sub_fold = x.L.sub_fold;
+  a.L.fold_sub = x.L.fold_sub;
+  a.L.fold_row0 = x.L.total_mid;
+  a.L.fold_cap = x.L.fold_capacity;
   a.kv = x.kv;
   a.q = x.q;
   a.out = x.out;

@@ -96,12 +96,13 @@ struct TileRec {
   uint32_t mask;
 };
 
-// Tile slots of a unit start here.  A chosen cluster of n rows yields at
-// most ceil(n/32) + S tiles (one partial tile per run, at most S runs), so
-// n_mid/32 + C (S + 1) + 1 slots per unit suffice; the base below grows by
-// at least that much from one unit to the next.
-__host__ __device__ inline int64_t tile_unit_base(int64_t row_base, int64_t cl_base, int u) {
-  return cl_base * (kMaxS + 1) + (row_base >> 5) + u;
+// Tile slots of a unit start here.  A chosen cluster of n reordered rows and
+// f folded rows yields at most ceil(n/32) + S + f tiles (one partial tile
+// per run, at most S runs; a folded row in a tile of its own at worst), so
+// n_mid/32 + C (S + 1) + 1 + fold_cap slots per unit suffice; the base below
+// grows by at least that much from one unit to the next.
+__host__ __device__ inline int64_t tile_unit_base(int64_t row_base, int64_t cl_base, int u, int fold_cap) {
+  return cl_base * (kMaxS + 1) + (row_base >> 5) + (int64_t)u * (1 + fold_cap);
 }
 
 // Per-cluster entries of unit u start at u * max_C (the largest C of the
@@ -168,6 +169,24 @@ constexpr int kPartPad = 4;
 constexpr int kExactResidentBlocks = 512;   // partial record = o[D], m, l, pad
 
 hipError_t launch_layout_table(const mog_layout& L, const SeqArgs& seq, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Append (incremental decode) launch block.
+// ---------------------------------------------------------------------------
+struct AppendSeq {
+  int32_t len;     // sequence length before the append
+  uint16_t n_new;  // tokens to fold
+  uint16_t f0;     // tokens folded before (first fold row to write)
+};
+
+struct AppendLaunch {
+  mog_layout L;
+  KVRef kv;
+  int32_t n_seq;
+  AppendSeq seq[MOG_MAX_SEQ];
+};
+
+hipError_t launch_append(const AppendLaunch& a, hipStream_t s);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t s);
 hipError_t launch_dense(const DenseLaunch& a, hipStream_t s);
 
@@ -216,7 +235,8 @@ __device__ inline mog_unit uni_unit(const mog_unit* p) {
   U.n_mid = uni(x.n_mid);
   U.C = uni(x.C);
   U.S = uni(x.S);
-  U.reserved0 = U.reserved1 = 0;
+  U.n_fold = uni(x.n_fold);
+  U.reserved1 = 0;
   U.row_base = uni(x.row_base);
   U.cl_base = uni(x.cl_base);
   U.sub_base = uni(x.sub_base);

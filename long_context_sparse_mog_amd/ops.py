@@ -80,6 +80,10 @@ class KVCache:
     def head_dim(self):
         return self.c.head_dim
 
+    def with_lens(self, seq_lens):
+        """The same cache tensors with other sequence lengths (a grown cache)."""
+        return KVCache(self.k, self.v, seq_lens, self.block_table)
+
     @classmethod
     def from_batch(cls, b, paged=None):
         """From a ``synth.Batch``; paged follows the workload unless given."""
@@ -111,12 +115,22 @@ class Layout:
         return self.mem[off:off + nbytes].view(dtype)
 
     def arrays(self):
-        """Typed device views of every layout array (all units)."""
+        """Typed device views of every layout array (all units).  ``k_mid`` /
+        ``v_mid`` include the fold area after the reordered rows."""
         c, D = self.c, self.c.head_dim
         kd = torch.bfloat16 if c.dtype == capi.MOG_BF16 else torch.float32
+        rows = c.total_mid + c.n_units * c.fold_capacity
+        cap = c.n_units * c.fold_capacity
+        fold = {}
+        if cap:
+            fold = dict(fold_sub=self._view(c.fold_sub, cap, torch.int32).view(c.n_units, -1),
+                        fold_pos=self._view(c.fold_pos, cap, torch.int32).view(c.n_units, -1))
         return dict(
-            k_mid=self._view(c.k_mid, c.total_mid * D, kd).view(-1, D),
-            v_mid=self._view(c.v_mid, c.total_mid * D, kd).view(-1, D),
+            **fold,
+            cl_fold=self._view(c.cl_fold, c.total_cl, torch.int32),
+            sub_fold=self._view(c.sub_fold, c.total_sub, torch.int32),
+            k_mid=self._view(c.k_mid, rows * D, kd).view(-1, D),
+            v_mid=self._view(c.v_mid, rows * D, kd).view(-1, D),
             perm=self._view(c.perm, c.total_mid, torch.int32),
             sub_off=self._view(c.sub_off, c.total_off, torch.int32),
             cl_ms=self._view(c.cl_ms, c.total_cl * 2 * D, torch.float32).view(-1, 2 * D),
@@ -136,8 +150,19 @@ class Layout:
         sb = slice(U.sub_base, U.sub_base + C_ * S)
         ms_c = a["cl_ms"][cl].cpu().numpy()
         ms_s = a["sub_ms"][sb].cpu().numpy()
+        nf = U.n_fold
+        fold = dict(fold_sub=np.zeros(0, np.int64), fold_pos=np.zeros(0, np.int64), fold_k=None, fold_v=None)
+        if nf:
+            f0 = self.c.total_mid + u * self.c.fold_capacity
+            fold = dict(fold_sub=a["fold_sub"][u, :nf].cpu().numpy().astype(np.int64),
+                        fold_pos=a["fold_pos"][u, :nf].cpu().numpy().astype(np.int64),
+                        fold_k=a["k_mid"][f0:f0 + nf].float().cpu().numpy(),
+                        fold_v=a["v_mid"][f0:f0 + nf].float().cpu().numpy())
         return dict(
-            N=U.N, C=C_, S=S, n_mid=U.n_mid, seq=U.seq, kv_head=U.kv_head,
+            **fold,
+            cl_fold=a["cl_fold"][cl].cpu().numpy().astype(np.int64),
+            sub_fold=a["sub_fold"][sb].cpu().numpy().astype(np.int64),
+            N=U.N, C=C_, S=S, n_mid=U.n_mid, n_fold=nf, seq=U.seq, kv_head=U.kv_head,
             perm=a["perm"][rows].cpu().numpy().astype(np.int64),
             sub_off=a["sub_off"][U.off_base:U.off_base + C_ * S + 1].cpu().numpy().astype(np.int64),
             cl_mu=ms_c[:, :D], cl_var=ms_c[:, D:], cl_vbar=a["cl_vbar"][cl].cpu().numpy(),
@@ -145,24 +170,24 @@ class Layout:
         )
 
 
-def _dims(n_seq, n_kv_heads, head_dim, dtype, n_sink, n_recent, seq_lens):
+def _dims(n_seq, n_kv_heads, head_dim, dtype, n_sink, n_recent, seq_lens, fold_capacity=0):
     lens = capi.int_array(seq_lens)
-    d = capi.mog_dims(n_seq, n_kv_heads, head_dim, dtype, n_sink, n_recent,
+    d = capi.mog_dims(n_seq, n_kv_heads, head_dim, dtype, n_sink, n_recent, fold_capacity,
                       C.cast(lens, C.POINTER(capi.i32)))
     return d, lens
 
 
-def mog_layout_size(n_kv_heads, head_dim, dtype, n_sink, n_recent, seq_lens) -> int:
-    d, _keep = _dims(len(seq_lens), n_kv_heads, head_dim, dtype, n_sink, n_recent, seq_lens)
+def mog_layout_size(n_kv_heads, head_dim, dtype, n_sink, n_recent, seq_lens, fold_capacity=0) -> int:
+    d, _keep = _dims(len(seq_lens), n_kv_heads, head_dim, dtype, n_sink, n_recent, seq_lens, fold_capacity)
     out = C.c_size_t()
     check(lib().mog_layout_size(C.byref(d), C.byref(out)), "mog_layout_size")
     return out.value
 
 
-def mog_layout_init(kv: KVCache, n_sink, n_recent, device="cuda", stream=None) -> Layout:
+def mog_layout_init(kv: KVCache, n_sink, n_recent, device="cuda", stream=None, fold_capacity=0) -> Layout:
     """Allocate and carve an empty layout for ``kv`` (for importing arrays)."""
     d, _keep = _dims(kv.c.n_seq, kv.c.n_kv_heads, kv.c.head_dim, kv.c.dtype, n_sink, n_recent,
-                     kv.seq_lens)
+                     kv.seq_lens, fold_capacity)
     nbytes = C.c_size_t()
     check(lib().mog_layout_size(C.byref(d), C.byref(nbytes)), "mog_layout_size")
     mem = torch.zeros(nbytes.value, dtype=torch.uint8, device=device)
@@ -216,11 +241,13 @@ def workspace(nbytes, device="cuda"):
     return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
-def mog_build(kv: KVCache, n_sink, n_recent, kmeans_iters=10, seed=0, ws=None, stream=None) -> Layout:
-    """Prefill-side build; allocates the layout (and the workspace unless given)."""
-    bp = capi.mog_build_params(kmeans_iters, n_sink, n_recent, 0, seed)
+def mog_build(kv: KVCache, n_sink, n_recent, kmeans_iters=10, seed=0, ws=None, stream=None,
+              fold_capacity=0) -> Layout:
+    """Prefill-side build; allocates the layout (and the workspace unless given).
+    ``fold_capacity``: rows per unit kept for mog_append."""
+    bp = capi.mog_build_params(kmeans_iters, n_sink, n_recent, fold_capacity, seed)
     d, _keep = _dims(kv.c.n_seq, kv.c.n_kv_heads, kv.c.head_dim, kv.c.dtype, n_sink, n_recent,
-                     kv.seq_lens)
+                     kv.seq_lens, fold_capacity)
     nbytes = C.c_size_t()
     check(lib().mog_layout_size(C.byref(d), C.byref(nbytes)), "mog_layout_size")
     mem = torch.empty(nbytes.value, dtype=torch.uint8, device=kv.k.device)
@@ -233,6 +260,12 @@ def mog_build(kv: KVCache, n_sink, n_recent, kmeans_iters=10, seed=0, ws=None, s
     lay = Layout(L, mem)
     lay._build_ws = ws
     return lay
+
+
+def mog_append(layout: Layout, kv: KVCache, stream=None) -> None:
+    """Fold the tokens that left the recent window since the layout was
+    built (``kv`` holds the grown sequences); updates ``layout`` in place."""
+    check(lib().mog_append(C.byref(kv.c), C.byref(layout.c), _stream(stream)), "mog_append")
 
 
 def mog_decode(layout: Layout, kv: KVCache, q, params, out=None, lse=None, want_sel=False,
@@ -281,7 +314,7 @@ def mog_dense_decode(kv: KVCache, q, params, out=None, lse=None, ws=None, stream
 
 
 def import_layout(kv: KVCache, n_sink, n_recent, units, k_rows=None, v_rows=None,
-                  stream=None) -> Layout:
+                  stream=None, fold_capacity=0) -> Layout:
     """Place a layout computed elsewhere into a fresh library layout.
 
     ``units[u]`` is a dict with ``perm`` (token position of every reordered
@@ -289,7 +322,7 @@ def import_layout(kv: KVCache, n_sink, n_recent, units, k_rows=None, v_rows=None
     ``cl_vbar``, ``sub_mu``, ``sub_var``, ``sub_vbar``.  The reordered K/V
     rows are gathered from ``kv`` on the device.
     """
-    lay = mog_layout_init(kv, n_sink, n_recent, device=kv.k.device, stream=stream)
+    lay = mog_layout_init(kv, n_sink, n_recent, device=kv.k.device, stream=stream, fold_capacity=fold_capacity)
     a = lay.arrays()
     dev = kv.k.device
     D = kv.head_dim

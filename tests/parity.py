@@ -20,11 +20,14 @@ def unit_layout_arrays(L: "O.UnitLayout") -> dict:
 
 
 def oracle_layout_from_export(ex: dict, n_sink: int, n_recent: int) -> "O.UnitLayout":
-    """An oracle UnitLayout holding a layout downloaded from the device."""
+    """An oracle UnitLayout holding a layout downloaded from the device
+    (with the tokens folded into it, if any)."""
     return O.UnitLayout(N=ex["N"], n_sink=n_sink, n_recent=n_recent, C=ex["C"], S=ex["S"],
                         perm=ex["perm"], sub_off=ex["sub_off"], cl_mu=ex["cl_mu"],
                         cl_var=ex["cl_var"], cl_vbar=ex["cl_vbar"], sub_mu=ex["sub_mu"],
-                        sub_var=ex["sub_var"], sub_vbar=ex["sub_vbar"])
+                        sub_var=ex["sub_var"], sub_vbar=ex["sub_vbar"],
+                        fold_pos=[int(x) for x in ex.get("fold_pos", [])],
+                        fold_sub=[int(x) for x in ex.get("fold_sub", [])])
 
 
 def build_oracle_layouts(batch, iters=10, seed=0, units=None):

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     out = subprocess.run(["nm", "-D", "--defined-only", capi.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (mog_\w+)", out))
     assert set(names) == exported, (set(names) ^ exported)
@@ -65,9 +65,10 @@ def test_struct_layout_matches_c(tmp_path):
             assert int(got[f"{name}.{f}"]) == getattr(cls, f).offset, f"{name}.{f}"
 
 
-def _dims(lens, n_sink=64, n_recent=256, hkv=8, d=128, dtype=capi.MOG_BF16):
+def _dims(lens, n_sink=64, n_recent=256, hkv=8, d=128, dtype=capi.MOG_BF16, fold_capacity=0):
     arr = capi.int_array(lens)
-    return capi.mog_dims(len(lens), hkv, d, dtype, n_sink, n_recent, C.cast(arr, C.POINTER(capi.i32))), arr
+    return capi.mog_dims(len(lens), hkv, d, dtype, n_sink, n_recent, fold_capacity,
+                         C.cast(arr, C.POINTER(capi.i32))), arr
 
 
 def test_layout_size_matches_geometry(L):
@@ -75,8 +76,17 @@ def test_layout_size_matches_geometry(L):
     out = C.c_size_t()
     assert L.mog_layout_size(C.byref(d), C.byref(out)) == capi.MOG_OK
     n_mid, Cc, S, D = 1048576 - 320, 1024, 20, 128
-    expect = 8 * (2 * n_mid * D * 2 + n_mid * 4 + (Cc * S + 1) * 4 + Cc * 3 * D * 4 + Cc * S * 3 * D * 4)
+    # rows, perm, offsets, group statistics, per-group fold counts
+    expect = 8 * (2 * n_mid * D * 2 + n_mid * 4 + (Cc * S + 1) * 4 + Cc * 3 * D * 4 + Cc * S * 3 * D * 4
+                  + (Cc + Cc * S) * 4)
     assert expect <= out.value <= expect + 16 * 256
+    # a fold area: K/V rows, their subcluster and position, per unit
+    cap = 1000
+    d2, keep2 = _dims([1048576], fold_capacity=cap)
+    out2 = C.c_size_t()
+    assert L.mog_layout_size(C.byref(d2), C.byref(out2)) == capi.MOG_OK
+    grow = 8 * cap * (2 * D * 2 + 2 * 4)
+    assert grow <= out2.value - out.value <= grow + 8 * 256
 
 
 def test_layout_unit_geometry(L):
@@ -100,6 +110,19 @@ def test_layout_unit_geometry(L):
         sub += Cc * S
         off += Cc * S + 1
     assert L.mog_layout_unit(C.byref(lay), 6, C.byref(U)) == capi.MOG_ERR_INVALID_ARG
+    # after folding: the geometry follows the lengths at the build, N the
+    # current length
+    lay.fold_capacity = 100
+    lay.seq_lens[0] = lens[0] + 37
+    lay.fold_count[0] = 37
+    row = 0
+    for u in range(6):
+        U = capi.mog_unit()
+        assert L.mog_layout_unit(C.byref(lay), u, C.byref(U)) == capi.MOG_OK
+        n_mid, Cc, S = O.unit_dims(lens[u // 2], 4, 64)
+        assert (U.N, U.n_mid, U.C, U.S, U.row_base) == (lens[u // 2] + (37 if u < 2 else 0), n_mid, Cc, S, row)
+        assert U.n_fold == (37 if u < 2 else 0)
+        row += n_mid
 
 
 @pytest.mark.parametrize("bad, status", [
@@ -109,6 +132,8 @@ def test_layout_unit_geometry(L):
     (dict(lens=[5000], n_sink=-1), capi.MOG_ERR_INVALID_ARG),
     (dict(lens=[5000], dtype=7), capi.MOG_ERR_UNSUPPORTED),
     (dict(lens=[]), capi.MOG_ERR_INVALID_ARG),
+    (dict(lens=[5000], fold_capacity=-1), capi.MOG_ERR_INVALID_ARG),
+    (dict(lens=[5000], fold_capacity=capi.MOG_MAX_FOLD + 1), capi.MOG_ERR_INVALID_ARG),
 ])
 def test_layout_size_rejects(L, bad, status):
     lens = bad.pop("lens")
@@ -192,7 +217,48 @@ def test_build_validation(L):
     assert L.mog_build(C.byref(kv), C.byref(bp), C.c_void_p(0x1000), 64, C.c_void_p(0x1000), 1 << 40, C.byref(lay), None) == capi.MOG_ERR_WORKSPACE
 
 
+def _host_layout(lens, cap, folded):
+    """A layout descriptor whose arrays are never dereferenced (validation
+    fails first, or there is nothing to enqueue)."""
+    lay = capi.mog_layout()
+    lay.n_seq, lay.n_kv_heads, lay.head_dim, lay.dtype = len(lens), 8, 128, capi.MOG_BF16
+    lay.n_sink, lay.n_recent, lay.n_units, lay.fold_capacity = 64, 256, 8 * len(lens), cap
+    for i, (x, f) in enumerate(zip(lens, folded)):
+        lay.seq_lens[i] = x
+        lay.fold_count[i] = f
+    for name in ("units", "k_mid", "v_mid", "perm", "sub_off", "cl_ms", "cl_vbar", "sub_ms", "sub_vbar",
+                 "fold_sub", "fold_pos", "cl_fold", "sub_fold"):
+        setattr(lay, name, 0x10000)
+    return lay
+
+
+def test_append_validation(L):
+    lay = _host_layout([5000, 6000], cap=10, folded=[3, 0])
+    # nothing grew: nothing to enqueue, layout unchanged
+    kv, keep = _kv([5000, 6000])
+    assert L.mog_append(C.byref(kv), C.byref(lay), None) == capi.MOG_OK
+    assert list(lay.seq_lens[:2]) == [5000, 6000] and list(lay.fold_count[:2]) == [3, 0]
+    # a sequence shorter than the layout's
+    kv, keep = _kv([4999, 6000])
+    assert L.mog_append(C.byref(kv), C.byref(lay), None) == capi.MOG_ERR_INVALID_ARG
+    # 3 folded + 8 new > 10: build again; nothing changed
+    kv, keep = _kv([5008, 6001])
+    assert L.mog_append(C.byref(kv), C.byref(lay), None) == capi.MOG_ERR_CAPACITY
+    assert "capacity" in L.mog_last_error().decode()
+    assert list(lay.seq_lens[:2]) == [5000, 6000] and list(lay.fold_count[:2]) == [3, 0]
+    # a layout without a fold area cannot grow at all
+    lay0 = _host_layout([5000], cap=0, folded=[0])
+    kv, keep = _kv([5001])
+    assert L.mog_append(C.byref(kv), C.byref(lay0), None) == capi.MOG_ERR_CAPACITY
+    # shape mismatch, and a fold count beyond the capacity
+    kv, keep = _kv([5000])
+    assert L.mog_append(C.byref(kv), C.byref(lay), None) == capi.MOG_ERR_INVALID_ARG
+    bad = _host_layout([5000], cap=4, folded=[5])
+    assert L.mog_append(C.byref(kv), C.byref(bad), None) == capi.MOG_ERR_INVALID_ARG
+    assert L.mog_append(C.byref(kv), None, None) == capi.MOG_ERR_INVALID_ARG
+
+
 def test_status_strings(L):
-    for s in range(5):
+    for s in range(6):
         assert L.mog_status_string(s).decode()
     assert L.mog_status_string(99).decode() == "unknown status"
