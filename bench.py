@@ -259,6 +259,67 @@ def bench_workload(idx, steps, warmup, n_qsets, ev, with_errors=True, shared_too
     return res, state
 
 
+def incremental_bench(state, steps, warmup):
+    """Incremental decode on the same workload: the layout is built on the
+    first N - 2T tokens (T = warmup + steps) with a fold area of 2T rows, then
+    (A) T single-token appends alone, (B) T steps of one single-token append
+    (mog_append) plus one decode (mog_decode) on the grown cache, (C) decode
+    alone on the final cache.  Timed with torch events around the K timed
+    calls of each phase (after W untimed ones)."""
+    import torch
+
+    from long_context_sparse_mog_amd import capi, ops
+
+    wl, b, qs = state["wl"], state["b"], state["qs"]
+    nq = len(qs)
+    T = steps + warmup
+    kv_full = ops.KVCache.from_batch(b)
+    n0 = [L - 2 * T for L in wl.seq_lens]
+    kvs = [kv_full.with_lens([x + i for x in n0]) for i in range(2 * T + 1)]
+    lay = ops.mog_build(kvs[0], wl.n_sink, wl.n_recent, kmeans_iters=wl.kmeans_iters, seed=1, fold_capacity=2 * T)
+    p0 = ops.decode_params(wl.n_q_heads, list(wl.top_c), list(wl.top_s))
+    ws = ops.workspace(ops.mog_workspace_size(capi.MOG_OP_DECODE, layout=lay, params=p0))
+    out = torch.empty_like(qs[0])
+    lse = torch.empty(qs[0].shape[:2], device="cuda")
+    torch.cuda.synchronize()
+
+    def burst(fn, lo):
+        for i in range(lo, lo + warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(lo + warmup, lo + T):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    append_ms = burst(lambda i: ops.mog_append(lay, kvs[i + 1]), 0)
+
+    def step(i):
+        ops.mog_append(lay, kvs[i + 1])
+        ops.mog_decode(lay, kvs[i + 1], qs[i % nq], p0, out=out, lse=lse, ws=ws)
+
+    step_ms = burst(step, T)
+    decode_ms = burst(lambda i: ops.mog_decode(lay, kvs[2 * T], qs[i % nq], p0, out=out, lse=lse, ws=ws), 0)
+    # approximation error at the final length, folded layout vs dense
+    pd = ops.decode_params(wl.n_q_heads, 1, 1)
+    errs = []
+    for t in range(min(4, nq)):
+        o = ops.mog_decode(lay, kvs[2 * T], qs[t], p0)[0]
+        od, _ = ops.mog_dense_decode(kvs[2 * T], qs[t], pd)
+        errs.append((torch.linalg.norm(o - od, dim=-1) / torch.linalg.norm(od, dim=-1)).flatten())
+    er = torch.cat(errs)
+    res = dict(steps_per_s=1000.0 / step_ms, ms_per_step=step_ms, append_ms=append_ms,
+               decode_only_ms=decode_ms, folded_tokens_at_end=2 * T, seq_len_at_build=n0[0],
+               err_vs_dense_residual_mean=float(er.mean()), err_vs_dense_residual_max=float(er.max()))
+    del lay, ws, kvs
+    torch.cuda.empty_cache()
+    return res
+
+
 def build_timing(reps=3):
     """mog_build (10 k-means rounds, subclusters, reorder, stats) of the
     single-head 128K-key workload: median wall time over reps."""
@@ -403,6 +464,8 @@ def main():
                     help="skip the 4K, 32K and ragged workloads and the build timing")
     ap.add_argument("--no-shared", action="store_true",
                     help="skip the 1M step with one selection per KV head")
+    ap.add_argument("--no-incremental", action="store_true",
+                    help="skip the 1M incremental-decode steps (append one token + decode)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 10 times (the reference kernel that "
@@ -425,6 +488,8 @@ def main():
     capi.lib()  # fail loudly when the HIP library is missing
     ev = HipEvents()
     r1m, st1m = bench_workload(3, args.steps, args.warmup, args.qsets, ev, shared_too=not args.no_shared)
+    if not args.no_incremental:
+        r1m["incremental"] = incremental_bench(st1m, args.steps, args.warmup)
     r128 = None
     if not args.no_128k:
         r128, _ = bench_workload(2, args.steps, args.warmup, args.qsets, ev)

@@ -139,6 +139,7 @@ typedef struct {
  *  cl_fold, sub_fold [groups] int32: folded tokens per cluster / subcluster
  *                (a group holds its sub_off rows plus these).
  *  units         DEVICE copy of the mog_unit table (n_units entries).
+ *  append_scratch  library-internal working memory of mog_append.
  *  seq_lens      current lengths; fold_count[s] of them were folded, so
  *                seq_lens[s] - fold_count[s] is the length at the build. */
 typedef struct {
@@ -162,6 +163,7 @@ typedef struct {
   int32_t* fold_pos;
   int32_t* cl_fold;
   int32_t* sub_fold;
+  void* append_scratch;
 } mog_layout;
 
 typedef struct {

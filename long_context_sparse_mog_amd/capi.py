@@ -53,7 +53,8 @@ class mog_layout(C.Structure):
                 ("total_cl", i64), ("total_sub", i64), ("total_off", i64), ("units", vp),
                 ("k_mid", vp), ("v_mid", vp), ("perm", vp), ("sub_off", vp), ("cl_ms", vp),
                 ("cl_vbar", vp), ("sub_ms", vp), ("sub_vbar", vp), ("fold_sub", vp),
-                ("fold_pos", vp), ("cl_fold", vp), ("sub_fold", vp)]
+                ("fold_pos", vp), ("cl_fold", vp), ("sub_fold", vp),
+                ("append_scratch", vp)]
 
 
 class mog_build_params(C.Structure):

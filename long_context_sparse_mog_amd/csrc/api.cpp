@@ -51,7 +51,7 @@ struct Totals {
 struct LayoutPlan {
   Totals t;
   size_t o_units, o_kmid, o_vmid, o_perm, o_suboff, o_clms, o_clvb, o_subms, o_subvb;
-  size_t o_foldsub, o_foldpos, o_clfold, o_subfold, bytes;
+  size_t o_foldsub, o_foldpos, o_clfold, o_subfold, o_appws, bytes;
 };
 
 mog_status check_dims(const mog_dims* d) {
@@ -106,6 +106,7 @@ LayoutPlan plan_layout(const mog_dims* d) {
   p.o_foldpos = o; o = align_up(o + (size_t)nu * d->fold_capacity * 4);
   p.o_clfold = o; o = align_up(o + (size_t)p.t.cl * 4);
   p.o_subfold = o; o = align_up(o + (size_t)p.t.sub * 4);
+  p.o_appws = o; o = align_up(o + append_scratch_bytes(nu));
   p.bytes = o;
   return p;
 }
@@ -278,7 +279,7 @@ DensePlan plan_dense(const mog_kv* kv, const mog_decode_params* p) {
 
 mog_status check_layout_arrays(const mog_layout* L) {
   if (!L->units || !L->k_mid || !L->v_mid || !L->sub_off || !L->cl_ms || !L->cl_vbar || !L->sub_ms ||
-      !L->sub_vbar || !L->cl_fold || !L->sub_fold)
+      !L->sub_vbar || !L->cl_fold || !L->sub_fold || !L->append_scratch)
     return fail(MOG_ERR_INVALID_ARG, "layout has NULL arrays (not initialised?)");
   if (L->fold_capacity < 0 || L->fold_capacity > MOG_MAX_FOLD)
     return fail(MOG_ERR_INVALID_ARG, "layout fold_capacity=%d outside [0, %d]", L->fold_capacity, MOG_MAX_FOLD);
@@ -426,6 +427,7 @@ static mog_status layout_carve(const mog_dims* dims, void* mem, size_t mem_bytes
   L.fold_pos = dims->fold_capacity ? reinterpret_cast<int32_t*>(b + p.o_foldpos) : nullptr;
   L.cl_fold = reinterpret_cast<int32_t*>(b + p.o_clfold);
   L.sub_fold = reinterpret_cast<int32_t*>(b + p.o_subfold);
+  L.append_scratch = b + p.o_appws;
   *out = L;
   return MOG_OK;
 }

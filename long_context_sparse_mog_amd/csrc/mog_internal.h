@@ -179,6 +179,21 @@ struct AppendSeq {
   uint16_t f0;     // tokens folded before (first fold row to write)
 };
 
+// mog_append: a token's cluster scan is shared by up to kAppendMaxBlocks
+// blocks per unit (about kAppendRowsPerBlock clusters each); each leaves
+// its winner in a slot, and a per-unit counter finds the last block.  Slots
+// and counters live in the layout buffer (mog_layout.append_scratch).
+constexpr int kAppendThreads = 512;
+constexpr int kAppendRowsPerBlock = 128;
+constexpr int kAppendMaxBlocks = 16;
+struct AppendSlot {
+  double d2;
+  int32_t id, n, nf, pad;
+};
+__host__ __device__ inline size_t append_scratch_bytes(int64_t n_units) {
+  return (size_t)n_units * (kAppendMaxBlocks * sizeof(AppendSlot) + sizeof(int32_t));
+}
+
 struct AppendLaunch {
   mog_layout L;
   KVRef kv;

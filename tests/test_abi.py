@@ -227,7 +227,7 @@ def _host_layout(lens, cap, folded):
         lay.seq_lens[i] = x
         lay.fold_count[i] = f
     for name in ("units", "k_mid", "v_mid", "perm", "sub_off", "cl_ms", "cl_vbar", "sub_ms", "sub_vbar",
-                 "fold_sub", "fold_pos", "cl_fold", "sub_fold"):
+                 "fold_sub", "fold_pos", "cl_fold", "sub_fold", "append_scratch"):
         setattr(lay, name, 0x10000)
     return lay
 

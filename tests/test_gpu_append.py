@@ -34,10 +34,13 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_append_case(wl, grow, chunks=None, cap=None, shared=False, residual=True, top=None, qset=0):
+def run_append_case(wl, grow, chunks=None, cap=None, shared=False, residual=True, top=None, qset=0,
+                    units=None, grown_wl=None):
     """``wl`` at its build lengths; ``grow[s]`` tokens appended to sequence s,
     in the calls ``chunks`` (a list of per-sequence increments summing to
-    ``grow``, default one call)."""
+    ``grow``, default one call).  ``units``: the (sequence, KV head) units
+    checked against the oracle (default all); ``grown_wl``: the workload the
+    cache is drawn from (default ``wl`` at the grown lengths)."""
     n = wl.n_seq
     chunks = chunks or [list(grow)]
     assert [sum(c[s] for c in chunks) for s in range(n)] == list(grow)
@@ -46,13 +49,14 @@ def run_append_case(wl, grow, chunks=None, cap=None, shared=False, residual=True
     grown = [L + g for L, g in zip(build_lens, grow)]
     say(f"[append] {wl.name} build lens={build_lens} grow={list(grow)} chunks={len(chunks)} cap={cap} "
         f"Hq={wl.n_q_heads} Hkv={wl.n_kv_heads} D={wl.head_dim} {wl.dtype} shared={shared}")
-    wg = replace(wl, seq_lens=grown)
+    wg = grown_wl or replace(wl, seq_lens=grown)
+    assert list(wg.seq_lens) == grown
     b = synth.generate(wg, device="cuda", n_qsets=qset + 1)
     kv_full = ops.KVCache.from_batch(b)
     kv0 = kv_full.with_lens(build_lens)
     lay = ops.mog_build(kv0, wl.n_sink, wl.n_recent, kmeans_iters=wl.kmeans_iters, seed=3, fold_capacity=cap)
-    units = range(n * wl.n_kv_heads)
-    ex0 = [lay.export_unit(u) for u in units]
+    units = list(range(n * wl.n_kv_heads)) if units is None else list(units)
+    ex0 = {u: lay.export_unit(u) for u in units}
     lens = list(build_lens)
     for c in chunks:
         lens = [L + a for L, a in zip(lens, c)]

@@ -8,6 +8,7 @@ ties and outputs must be within 2e-3 per-head relative L2 (bf16 K/V).
 """
 
 import sys
+from dataclasses import replace
 
 import numpy as np
 import pytest
@@ -85,3 +86,15 @@ def test_maximum_length_single_head():
     wl = synth.config(3, n_q_heads=4, n_kv_heads=1, seq_lens=[L], n_components=2048,
                       name="gqa-4q1kv-d128-4M-bf16", budget_kappa=34 / 203)
     run_fullsize(wl, [0])
+
+
+def test_fullsize_gqa_1m_incremental_sampled():
+    """The 1M workload's cache, the layout built on its first N - 300 tokens,
+    then 300 tokens appended (one, one, then 298 at once); fold state and one
+    decode step checked on two units."""
+    from test_gpu_append import run_append_case
+    wl = synth.config(3)
+    grow = 300
+    wb = replace(wl, seq_lens=[wl.seq_lens[0] - grow])
+    run_append_case(wb, [grow], chunks=[[1], [1], [grow - 2]], units=[0, 5], grown_wl=wl)
+    torch.cuda.empty_cache()
