@@ -29,6 +29,9 @@ from .mog import (  # noqa: F401
     build_unit,
     layout_from_assignment,
     fold_tokens,
+    positive_features,
+    with_feature_summaries,
+    fm_log_mass,
     shared_selection,
     decode_unit,
     dense_attention,

@@ -67,6 +67,19 @@ in the design notes of the repository):
       the token's rows are kept in a fold area and read exactly whenever its
       subcluster is chosen.  C, S and the rest of the partition stay until
       the next build.
+  R16 Feature-map residual (the retrieval-completion page's abstract: the
+      mid-region numerator and denominator left out of the exact part are
+      estimated from a fixed-size feature-map summary computed at prefill).
+      The feature map is the positive random-feature map of the softmax
+      kernel, phi(x) = exp(W x - |x|^2 / 2) / sqrt(m) with the m rows of W
+      drawn from N(0, I_d) (an input), so that E[phi(x).phi(y)] = exp(x.y);
+      with x = sqrt(scale) q and y = sqrt(scale) k this estimates
+      exp(scale q.k).  Every cluster and subcluster g keeps the fixed-size
+      sum Z_g = sum over its members of phi(sqrt(scale) k) (m numbers), and
+      in this mode an unchosen group's estimated mass is phi(sqrt(scale) q).Z_g
+      instead of the Gaussian exp(score); its value estimate stays the mean
+      value, and the merge is the same.  Selection is unchanged.  Folded
+      tokens add their features to both groups' sums.
 """
 
 from __future__ import annotations
@@ -273,6 +286,12 @@ class UnitLayout:
     # their positions and global subcluster ids, oldest first
     fold_pos: list = field(default_factory=list)
     fold_sub: list = field(default_factory=list)
+    # feature-map summaries (reading R16), float32: the map's W [m][d], its
+    # scale, and per group the feature sums [C][m] and [C*S][m]; None if absent
+    fm_w: np.ndarray = None
+    fm_scale: float = None
+    cl_z: np.ndarray = None
+    sub_z: np.ndarray = None
 
     @property
     def n_mid(self) -> int:
@@ -442,10 +461,66 @@ def fold_tokens(L: UnitLayout, K, V, n_new: int) -> UnitLayout:
         out.cl_mu[j], out.cl_var[j], out.cl_vbar[j] = _welford_add(ncl, out.cl_mu[j], out.cl_var[j], out.cl_vbar[j], k, v)
         out.sub_mu[g], out.sub_var[g], out.sub_vbar[g] = _welford_add(nsub, out.sub_mu[g], out.sub_var[g],
                                                                       out.sub_vbar[g], k, v)
+        if out.cl_z is not None:
+            ph = positive_features(math.sqrt(out.fm_scale) * k, out.fm_w)[0]
+            out.cl_z[j] = (out.cl_z[j].astype(np.float64) + ph).astype(np.float32)
+            out.sub_z[g] = (out.sub_z[g].astype(np.float64) + ph).astype(np.float32)
         out.fold_pos.append(t)
         out.fold_sub.append(g)
     out.N = L.N + n_new
     return out
+
+
+# ---------------------------------------------------------------------------
+# Feature-map summaries (reading R16)
+# ---------------------------------------------------------------------------
+
+
+def positive_features(X, W):
+    """phi(x) = exp(W x - |x|^2 / 2) / sqrt(m) for every row x of X: the
+    positive random features of the softmax kernel (for rows of W drawn from
+    N(0, I), E[phi(x).phi(y)] = exp(x.y))."""
+    X = np.atleast_2d(np.asarray(X, dtype=np.float64))
+    W = np.asarray(W, dtype=np.float64)
+    m = W.shape[0]
+    return np.exp(X @ W.T - 0.5 * (X * X).sum(axis=1, keepdims=True)) / math.sqrt(m)
+
+
+def with_feature_summaries(L: UnitLayout, K, W, scale=None) -> UnitLayout:
+    """A copy of ``L`` holding, for every cluster and subcluster, the sum of
+    phi(sqrt(scale) k) over its members (reordered rows and folded tokens),
+    computed in float64 and stored float32."""
+    import copy
+    K = np.asarray(K, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float32)
+    d = K.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = copy.deepcopy(L)
+    m = W.shape[0]
+    sub_z = np.zeros((L.C * L.S, m))
+    for g in range(L.C * L.S):
+        rows = L.group_rows(g)
+        if rows.size:
+            sub_z[g] = positive_features(math.sqrt(scale) * K[rows], W).sum(axis=0)
+    cl_z = np.zeros((L.C, m))
+    for j in range(L.C):
+        rows = np.concatenate([L.group_rows(j * L.S + i) for i in range(L.S)])
+        if rows.size:
+            cl_z[j] = positive_features(math.sqrt(scale) * K[rows], W).sum(axis=0)
+    out.fm_w, out.fm_scale = W, float(scale)
+    out.cl_z, out.sub_z = cl_z.astype(np.float32), sub_z.astype(np.float32)
+    return out
+
+
+def fm_log_mass(q, Z, W, scale):
+    """ln(phi(sqrt(scale) q).Z_g) for every row Z_g of Z (-inf where the
+    estimate is 0): the feature-map estimate of sum exp(scale q.k) over the
+    group's members."""
+    ph = positive_features(math.sqrt(scale) * np.asarray(q, np.float64), W)[0]
+    mass = np.asarray(Z, np.float64) @ ph
+    with np.errstate(divide="ignore"):
+        return np.where(mass > 0, np.log(np.maximum(mass, 1e-300)), -np.inf)
 
 
 # ---------------------------------------------------------------------------
@@ -515,7 +590,7 @@ def shared_selection(L: UnitLayout, Q, top_c, top_s, scale=None):
 
 
 def decode_unit(L: UnitLayout, K, V, Q, top_c, top_s, scale=None, residual=True,
-                sel_override=None, shared=False):
+                sel_override=None, shared=False, feature_residual=False):
     """One decode step for the query heads that share one KV head.
 
     K, V: float64 [N][d] of the sequence (anchors are read from here, the
@@ -525,7 +600,9 @@ def decode_unit(L: UnitLayout, K, V, Q, top_c, top_s, scale=None, residual=True,
     cluster ids ascending), ``sel_s`` (per head, per chosen cluster, chosen
     subcluster ids ascending) and ``n_exact`` (rows attended exactly per head).
     ``sel_override`` = (sel_c, sel_s) replaces the selection; ``shared``
-    takes the one selection of reading R14 for every head.
+    takes the one selection of reading R14 for every head;
+    ``feature_residual`` estimates the left-out groups' masses from the
+    layout's feature-map summaries (reading R16) instead of exp(score).
     """
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
@@ -543,9 +620,13 @@ def decode_unit(L: UnitLayout, K, V, Q, top_c, top_s, scale=None, residual=True,
     if shared and sel_override is None:
         ch, pk, _ = shared_selection(L, Q, top_c, top_s, scale)
         sel_override = ([ch] * G, [pk] * G)
+    if feature_residual and (L.cl_z is None or not np.isclose(L.fm_scale, scale)):
+        raise ValueError("feature-map residual needs summaries built with the decode scale")
     for h in range(G):
         q = Q[h]
         sc = group_log_mass(q, cl_cnt, L.cl_mu, L.cl_var, scale)
+        # the residual's log-mass of every cluster / subcluster
+        r_cl = fm_log_mass(q, L.cl_z, L.fm_w, scale) if feature_residual else sc
         if sel_override is not None:
             chosen = np.asarray(sel_override[0][h], dtype=np.int64)
         else:
@@ -555,7 +636,7 @@ def decode_unit(L: UnitLayout, K, V, Q, top_c, top_s, scale=None, residual=True,
         chosen_set = set(int(j) for j in chosen)
         for j in range(C):
             if cl_cnt[j] > 0 and j not in chosen_set:
-                r_logw.append(sc[j])
+                r_logw.append(r_cl[j])
                 r_vals.append(L.cl_vbar[j].astype(np.float64))
         sel_s_h = []
         for jj, j in enumerate(chosen):
@@ -568,6 +649,7 @@ def decode_unit(L: UnitLayout, K, V, Q, top_c, top_s, scale=None, residual=True,
                 picks = top_by_score(ss, top_s, sub_cnt[g0:g0 + S] > 0)
             sel_s_h.append(picks)
             pick_set = set(int(i) for i in picks)
+            r_sub = fm_log_mass(q, L.sub_z[g0:g0 + S], L.fm_w, scale) if feature_residual else ss
             for i in range(S):
                 g = g0 + i
                 if sub_cnt[g] == 0:
@@ -575,7 +657,7 @@ def decode_unit(L: UnitLayout, K, V, Q, top_c, top_s, scale=None, residual=True,
                 if i in pick_set:
                     exact_rows.append(L.group_rows(g))
                 else:
-                    r_logw.append(ss[i])
+                    r_logw.append(r_sub[i])
                     r_vals.append(L.sub_vbar[g].astype(np.float64))
         rows = np.concatenate(exact_rows)
         e_logw = scale * (K[rows] @ q)

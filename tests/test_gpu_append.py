@@ -161,3 +161,23 @@ def test_append_beyond_capacity_is_refused():
     assert e.value.status == capi.MOG_ERR_CAPACITY
     assert list(lay.c.seq_lens[:1]) == [3050] and list(lay.c.fold_count[:1]) == [50]
     torch.cuda.synchronize()
+
+
+def test_append_full_then_rebuild_then_append():
+    """The periodic re-build: once the fold area is full the caller builds
+    again on the grown cache and keeps appending; the new layout is a plain
+    build at the grown length (C and S follow the new N), and the folds after
+    it match the oracle's as before."""
+    wl = synth.config(1, seq_lens=[4200], n_kv_heads=2, n_q_heads=8, n_components=32)
+    total = 4200 + 64 + 40
+    wg = replace(wl, seq_lens=[total])
+    b = synth.generate(wg, device="cuda")
+    kv = ops.KVCache.from_batch(b)
+    lay = ops.mog_build(kv.with_lens([4200]), wl.n_sink, wl.n_recent, fold_capacity=64)
+    ops.mog_append(lay, kv.with_lens([4264]))
+    with pytest.raises(capi.MogError) as e:
+        ops.mog_append(lay, kv.with_lens([4265]))
+    assert e.value.status == capi.MOG_ERR_CAPACITY
+    # re-build on the grown cache, then continue with the next 40 tokens
+    wb = replace(wl, seq_lens=[4264])
+    run_append_case(wb, [40], cap=64, grown_wl=wg)

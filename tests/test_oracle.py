@@ -703,3 +703,104 @@ def test_dense_special_cases():
     q = rng.normal(0, 1, 3)
     _, lse = O.dense_attention(K, V, q, scale=0.7)
     assert lse[0] == pytest.approx(logsumexp(0.7 * K @ q), rel=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Feature-map residual (R16)
+# ---------------------------------------------------------------------------
+
+
+def test_positive_features_estimate_the_softmax_kernel():
+    """E[phi(x).phi(y)] = exp(x.y): with w ~ N(0, I) each feature product is
+    exp(w.(x+y) - |x|^2/2 - |y|^2/2), whose mean is exp(|x+y|^2/2 - |x|^2/2 -
+    |y|^2/2) = exp(x.y) (the Gaussian moment generating function).  A
+    million features land within a few standard errors of it."""
+    rng = np.random.default_rng(31)
+    d, m = 4, 1_000_000
+    x = rng.normal(0, 0.4, d)
+    y = rng.normal(0, 0.4, d)
+    W = rng.normal(0, 1, (m, d))
+    est = float(O.positive_features(x, W)[0] @ O.positive_features(y, W)[0])
+    exact = math.exp(x @ y)
+    var = math.exp(2 * (x + y) @ (x + y) - x @ x - y @ y) - exact ** 2
+    assert abs(est - exact) < 5 * math.sqrt(var / m)
+    # every feature is positive, and their squared norm estimates exp(|x|^2)
+    f = O.positive_features(x, W)[0]
+    assert (f > 0).all()
+    assert abs(f @ f - math.exp(x @ x)) < 0.02 * math.exp(x @ x)
+
+
+def test_feature_residual_with_zero_projection_is_a_closed_form():
+    """With W = 0 every feature is exp(-|x|^2/2)/sqrt(m), so a group's
+    estimated mass is exp(-s|q|^2/2) sum_t exp(-s|k_t|^2/2) exactly; with no
+    cluster chosen, the decode output is the merge of the anchors with these
+    masses times the mean values."""
+    rng = np.random.default_rng(32)
+    d, N, ns, nr = 3, 120, 2, 6
+    K = mixture_keys(rng, N, d, 3)
+    V = rng.normal(0, 1, (N, d))
+    L = O.build_unit(K, V, ns, nr, 10, O.unit_state(2, 0, 0, 1))
+    W = np.zeros((5, d), np.float32)
+    s = 0.7
+    F = O.with_feature_summaries(L, K, W, scale=s)
+    q = rng.normal(0, 1, d)
+    r = O.decode_unit(F, K, V, q[None], 0, 0, scale=s, feature_residual=True)
+    anchors = np.r_[0:ns, N - nr:N]
+    num = (np.exp(s * K[anchors] @ q)[:, None] * V[anchors]).sum(0)
+    den = np.exp(s * K[anchors] @ q).sum()
+    for j in range(L.C):
+        rows = np.concatenate([L.group_rows(j * L.S + i) for i in range(L.S)])
+        if rows.size:
+            w = math.exp(-s * (q @ q) / 2) * np.exp(-s * (K[rows] ** 2).sum(1) / 2).sum()
+            num = num + w * F.cl_vbar[j].astype(np.float64)
+            den += w
+    np.testing.assert_allclose(r["out"][0], num / den, rtol=1e-6)
+
+
+def test_feature_residual_recovers_dense_attention_with_many_features():
+    """No cluster chosen: anchors exact, the whole middle region estimated
+    from feature sums.  With groups of near-equal values the mean-value model
+    is close, and with 200k features the estimate of the mass is close: the
+    output approaches dense attention (and the lse the dense lse)."""
+    rng = np.random.default_rng(33)
+    d, N = 4, 200
+    K = 0.3 * rng.normal(0, 1, (N, d))
+    V = rng.normal(0, 1, (N, d))
+    L = O.build_unit(K, V, 2, 6, 10, O.unit_state(3, 0, 0, 1))
+    # every subcluster a singleton group: mean value = the token's value
+    lab = L.cluster_labels()
+    sub = np.empty(L.n_mid, np.int64)
+    for j in range(L.C):
+        members = np.flatnonzero(lab == j)
+        sub[members] = np.arange(members.size)
+    S = int(sub.max()) + 1
+    L2 = O.layout_from_assignment(K, V, 2, 6, L.C, S, lab, sub)
+    W = rng.normal(0, 1, (200_000, d)).astype(np.float32)
+    F = O.with_feature_summaries(L2, K, W, scale=1.0)
+    Q = rng.normal(0, 0.3, (2, d))
+    r = O.decode_unit(F, K, V, Q, F.C, 0, scale=1.0, feature_residual=True)
+    o, lse = O.dense_attention(K, V, Q, scale=1.0)
+    # per-group relative standard deviation sqrt((e^{|x|^2+|y|^2} - 1) / m)
+    # is about 2e-3 here
+    assert rel(r["out"], o) < 1e-2
+    np.testing.assert_allclose(r["lse"], lse, atol=5e-3)
+    # the Gaussian residual on the same singletons is exact (s = 0) up to
+    # the float32 storage of the statistics
+    g = O.decode_unit(F, K, V, Q, F.C, 0, scale=1.0)
+    assert rel(g["out"], o) < 1e-6
+    # the selection does not depend on the residual mode
+    g = O.decode_unit(F, K, V, Q, 2, 1, scale=1.0)
+    f = O.decode_unit(F, K, V, Q, 2, 1, scale=1.0, feature_residual=True)
+    assert all(np.array_equal(a, b) for a, b in zip(g["sel_c"], f["sel_c"]))
+
+
+def test_feature_sums_follow_the_folds():
+    """Folding adds each token's features to its two groups: the running
+    sums equal the sums recomputed over the grown groups' members."""
+    K, V, L = _grown_unit(24, grow=30)
+    W = np.random.default_rng(5).normal(0, 1, (16, K.shape[1])).astype(np.float32)
+    F0 = O.with_feature_summaries(L, K, W)
+    F = O.fold_tokens(F0, K, V, 30)
+    R = O.with_feature_summaries(F, K, W)
+    np.testing.assert_allclose(F.cl_z, R.cl_z, rtol=1e-5)
+    np.testing.assert_allclose(F.sub_z, R.sub_z, rtol=1e-5)
