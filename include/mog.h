@@ -97,6 +97,7 @@ typedef struct {
   int32_t n_sink;           /* anchors at the start of every sequence */
   int32_t n_recent;         /* anchors at the end of every sequence   */
   int32_t fold_capacity;    /* rows per unit kept for mog_append, 0..MOG_MAX_FOLD */
+  int32_t fm_dim;           /* features per group summary: 0 (none), 64, 128, 256 */
   const int32_t* seq_lens;  /* HOST [n_seq] lengths at the build */
 } mog_dims;
 
@@ -138,6 +139,11 @@ typedef struct {
  *  fold_pos      [n_units][fold_capacity] int32: its token position.
  *  cl_fold, sub_fold [groups] int32: folded tokens per cluster / subcluster
  *                (a group holds its sub_off rows plus these).
+ *  fm_w          [fm_dim][head_dim] float32: the feature map's projection
+ *                (a copy of the build's), fm_scale its logit scale.
+ *  cl_fz, sub_fz [groups][fm_dim] float32: per group the sum over its
+ *                members of phi(sqrt(fm_scale) k), phi(x) = exp(W x -
+ *                |x|^2 / 2) / sqrt(fm_dim) (NULL when fm_dim is 0).
  *  units         DEVICE copy of the mog_unit table (n_units entries).
  *  append_scratch  library-internal working memory of mog_append.
  *  seq_lens      current lengths; fold_count[s] of them were folded, so
@@ -147,6 +153,8 @@ typedef struct {
   int32_t n_units;
   int32_t max_C, max_S;
   int32_t fold_capacity;
+  int32_t fm_dim;
+  float fm_scale;
   int32_t seq_lens[MOG_MAX_SEQ];
   int32_t fold_count[MOG_MAX_SEQ];
   int64_t total_mid, total_cl, total_sub, total_off;
@@ -164,6 +172,9 @@ typedef struct {
   int32_t* cl_fold;
   int32_t* sub_fold;
   void* append_scratch;
+  float* fm_w;
+  float* cl_fz;
+  float* sub_fz;
 } mog_layout;
 
 typedef struct {
@@ -172,6 +183,10 @@ typedef struct {
   int32_t n_recent;
   int32_t fold_capacity; /* rows per unit kept for mog_append (0: none)    */
   uint64_t seed;        /* seeds the Forgy initialisation of every unit    */
+  int32_t fm_dim;       /* feature-map summaries: 0 (none), 64, 128, 256   */
+  float fm_scale;       /* their logit scale; 0 selects 1/sqrt(head_dim)   */
+  const float* fm_w;    /* DEVICE [fm_dim][head_dim] float32, rows drawn from
+                           N(0, I) by the caller; read during the build    */
 } mog_build_params;
 
 typedef struct {
@@ -179,6 +194,12 @@ typedef struct {
   int32_t top_c;                /* clusters attended exactly per query head     */
   int32_t top_s;                /* subclusters per chosen cluster               */
   int32_t residual;             /* 1: add the Gaussian estimate of the rest;
+                                   2: add the feature-map estimate of the rest
+                                   (retrieval-completion page, abstract: each
+                                   left-out group's mass is phi(sqrt(s) q).Z_g
+                                   from the layout's summaries, its value the
+                                   mean value; needs fm_dim > 0 and the scale
+                                   the summaries were built with);
                                    0: exact part only, renormalised            */
   float scale;                  /* logit scale; 0 selects 1/sqrt(head_dim)      */
   int32_t splits;               /* 0: automatic; else 1..8192.  mog_decode: the

@@ -35,7 +35,7 @@ class mog_kv(C.Structure):
 
 class mog_dims(C.Structure):
     _fields_ = [("n_seq", i32), ("n_kv_heads", i32), ("head_dim", i32), ("dtype", i32),
-                ("n_sink", i32), ("n_recent", i32), ("fold_capacity", i32),
+                ("n_sink", i32), ("n_recent", i32), ("fold_capacity", i32), ("fm_dim", i32),
                 ("seq_lens", C.POINTER(i32))]
 
 
@@ -48,18 +48,19 @@ class mog_unit(C.Structure):
 class mog_layout(C.Structure):
     _fields_ = [("n_seq", i32), ("n_kv_heads", i32), ("head_dim", i32), ("dtype", i32),
                 ("n_sink", i32), ("n_recent", i32), ("n_units", i32), ("max_C", i32),
-                ("max_S", i32), ("fold_capacity", i32), ("seq_lens", i32 * MOG_MAX_SEQ),
+                ("max_S", i32), ("fold_capacity", i32), ("fm_dim", i32), ("fm_scale", C.c_float),
+                ("seq_lens", i32 * MOG_MAX_SEQ),
                 ("fold_count", i32 * MOG_MAX_SEQ), ("total_mid", i64),
                 ("total_cl", i64), ("total_sub", i64), ("total_off", i64), ("units", vp),
                 ("k_mid", vp), ("v_mid", vp), ("perm", vp), ("sub_off", vp), ("cl_ms", vp),
                 ("cl_vbar", vp), ("sub_ms", vp), ("sub_vbar", vp), ("fold_sub", vp),
                 ("fold_pos", vp), ("cl_fold", vp), ("sub_fold", vp),
-                ("append_scratch", vp)]
+                ("append_scratch", vp), ("fm_w", vp), ("cl_fz", vp), ("sub_fz", vp)]
 
 
 class mog_build_params(C.Structure):
     _fields_ = [("kmeans_iters", i32), ("n_sink", i32), ("n_recent", i32), ("fold_capacity", i32),
-                ("seed", C.c_uint64)]
+                ("seed", C.c_uint64), ("fm_dim", i32), ("fm_scale", C.c_float), ("fm_w", vp)]
 
 
 class mog_decode_params(C.Structure):

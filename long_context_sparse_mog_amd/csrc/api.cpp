@@ -51,7 +51,7 @@ struct Totals {
 struct LayoutPlan {
   Totals t;
   size_t o_units, o_kmid, o_vmid, o_perm, o_suboff, o_clms, o_clvb, o_subms, o_subvb;
-  size_t o_foldsub, o_foldpos, o_clfold, o_subfold, o_appws, bytes;
+  size_t o_foldsub, o_foldpos, o_clfold, o_subfold, o_appws, o_fmw, o_clfz, o_subfz, bytes;
 };
 
 mog_status check_dims(const mog_dims* d) {
@@ -66,6 +66,8 @@ mog_status check_dims(const mog_dims* d) {
     return fail(MOG_ERR_INVALID_ARG, "negative anchor count (n_sink=%d, n_recent=%d)", d->n_sink, d->n_recent);
   if (d->fold_capacity < 0 || d->fold_capacity > MOG_MAX_FOLD)
     return fail(MOG_ERR_INVALID_ARG, "fold_capacity=%d outside [0, %d]", d->fold_capacity, MOG_MAX_FOLD);
+  if (d->fm_dim != 0 && d->fm_dim != 64 && d->fm_dim != 128 && d->fm_dim != 256)
+    return fail(MOG_ERR_UNSUPPORTED, "fm_dim=%d (supported: 0, 64, 128, 256)", d->fm_dim);
   if (!d->seq_lens) return fail(MOG_ERR_INVALID_ARG, "seq_lens is NULL");
   for (int s = 0; s < d->n_seq; ++s) {
     const int N = d->seq_lens[s];
@@ -107,6 +109,10 @@ LayoutPlan plan_layout(const mog_dims* d) {
   p.o_clfold = o; o = align_up(o + (size_t)p.t.cl * 4);
   p.o_subfold = o; o = align_up(o + (size_t)p.t.sub * 4);
   p.o_appws = o; o = align_up(o + append_scratch_bytes(nu));
+  const size_t F = (size_t)d->fm_dim;
+  p.o_fmw = o; o = align_up(o + F * D * 4);
+  p.o_clfz = o; o = align_up(o + (size_t)p.t.cl * F * 4);
+  p.o_subfz = o; o = align_up(o + (size_t)p.t.sub * F * 4);
   p.bytes = o;
   return p;
 }
@@ -177,7 +183,8 @@ KVRef make_kvref(const mog_kv* kv) {
 // ------------------------------------------------------------------------
 struct DecodePlan {
   int G, c_stride, s_stride, splits, nblk, nb_res, nb_chosen;
-  size_t o_clscore, o_cllse, o_clmask, o_clrank, o_urows, o_list, o_nch, o_uinfo, o_tbase, o_ntl, o_tiles, o_res, o_ex, bytes;
+  size_t o_clscore, o_cllse, o_clmask, o_clrank, o_urows, o_list, o_nch, o_uinfo, o_tbase, o_ntl, o_tiles, o_res, o_ex;
+  size_t o_fq, bytes;
 };
 
 int seq_top(const int32_t* per, int dflt, int s) { return per ? per[s] : dflt; }
@@ -190,6 +197,8 @@ mog_status check_decode_params(const mog_decode_params* p, int n_kv_heads, int n
   const int G = p->n_q_heads / n_kv_heads;
   if (G > kMaxG) return fail(MOG_ERR_UNSUPPORTED, "%d query heads per KV head (max %d)", G, kMaxG);
   if (p->splits < 0 || p->splits > 8192) return fail(MOG_ERR_INVALID_ARG, "splits=%d outside [0, 8192]", p->splits);
+  if (p->residual < 0 || p->residual > 2)
+    return fail(MOG_ERR_INVALID_ARG, "residual=%d (0: none, 1: Gaussian, 2: feature map)", p->residual);
   if (p->shared_selection != 0 && p->shared_selection != 1)
     return fail(MOG_ERR_INVALID_ARG, "shared_selection=%d (0 or 1)", p->shared_selection);
   if (p->exact_repeat < 0 || p->exact_repeat > 64)
@@ -249,6 +258,9 @@ DecodePlan plan_decode(const mog_layout* L, const mog_decode_params* p) {
                        sizeof(TileRec));
   d.o_res = o; o = align_up(o + (size_t)nu * d.nb_res * G * RS * 4);
   d.o_ex = o; o = align_up(o + (size_t)d.nblk * G * RS * 4);
+  // feature-map residual: each query head's features, [n_units][G][fm_dim]
+  d.o_fq = o;
+  if (p->residual == 2) o = align_up(o + (size_t)nu * G * L->fm_dim * 4);
   d.bytes = o;
   return d;
 }
@@ -285,6 +297,10 @@ mog_status check_layout_arrays(const mog_layout* L) {
     return fail(MOG_ERR_INVALID_ARG, "layout fold_capacity=%d outside [0, %d]", L->fold_capacity, MOG_MAX_FOLD);
   if (L->fold_capacity > 0 && (!L->fold_sub || !L->fold_pos))
     return fail(MOG_ERR_INVALID_ARG, "layout has NULL fold arrays");
+  if (L->fm_dim != 0 && L->fm_dim != 64 && L->fm_dim != 128 && L->fm_dim != 256)
+    return fail(MOG_ERR_INVALID_ARG, "layout fm_dim=%d", L->fm_dim);
+  if (L->fm_dim && (!L->fm_w || !L->cl_fz || !L->sub_fz || !(L->fm_scale > 0.f) || isinf(L->fm_scale)))
+    return fail(MOG_ERR_INVALID_ARG, "layout has fm_dim=%d but no feature-map arrays or scale", L->fm_dim);
   for (int s = 0; s < L->n_seq; ++s)
     if (L->fold_count[s] < 0 || L->fold_count[s] > L->fold_capacity)
       return fail(MOG_ERR_INVALID_ARG, "layout fold_count[%d]=%d outside [0, %d]", s, L->fold_count[s],
@@ -323,8 +339,15 @@ mog_status check_build(const mog_kv* kv, const mog_build_params* bp, mog_dims* d
   d.n_sink = bp->n_sink;
   d.n_recent = bp->n_recent;
   d.fold_capacity = bp->fold_capacity;
+  d.fm_dim = bp->fm_dim;
   d.seq_lens = kv->seq_lens;
   if ((st = check_dims(&d)) != MOG_OK) return st;
+  if (bp->fm_dim) {
+    if (!bp->fm_w) return fail(MOG_ERR_INVALID_ARG, "fm_dim=%d but fm_w is NULL", bp->fm_dim);
+    if (!aligned(bp->fm_w, 16)) return fail(MOG_ERR_INVALID_ARG, "fm_w must be 16-byte aligned");
+    if (!(bp->fm_scale >= 0.f) || isinf(bp->fm_scale))
+      return fail(MOG_ERR_INVALID_ARG, "fm_scale must be finite and >= 0");
+  }
   *dims_out = d;
   return MOG_OK;
 }
@@ -428,6 +451,13 @@ static mog_status layout_carve(const mog_dims* dims, void* mem, size_t mem_bytes
   L.cl_fold = reinterpret_cast<int32_t*>(b + p.o_clfold);
   L.sub_fold = reinterpret_cast<int32_t*>(b + p.o_subfold);
   L.append_scratch = b + p.o_appws;
+  L.fm_dim = dims->fm_dim;
+  L.fm_scale = 1.0f / sqrtf((float)dims->head_dim);
+  if (dims->fm_dim) {
+    L.fm_w = reinterpret_cast<float*>(b + p.o_fmw);
+    L.cl_fz = reinterpret_cast<float*>(b + p.o_clfz);
+    L.sub_fz = reinterpret_cast<float*>(b + p.o_subfz);
+  }
   *out = L;
   return MOG_OK;
 }
@@ -514,6 +544,14 @@ mog_status mog_decode(const mog_layout* layout, const mog_kv* kv, const float* q
   for (int s = 0; s < kv->n_seq; ++s)
     if (kv->seq_lens[s] - layout->n_sink - layout->n_recent < 1)
       return fail(MOG_ERR_INVALID_ARG, "sequence %d has no middle region", s);
+  const float scale = params->scale > 0.f ? params->scale : 1.0f / sqrtf((float)kv->head_dim);
+  if (params->residual == 2) {
+    if (layout->fm_dim == 0)
+      return fail(MOG_ERR_INVALID_ARG, "residual=2 needs a layout built with feature-map summaries (fm_dim > 0)");
+    if (scale != layout->fm_scale)
+      return fail(MOG_ERR_INVALID_ARG, "residual=2: decode scale %g differs from the summaries' scale %g", scale,
+                  layout->fm_scale);
+  }
   const DecodePlan d = plan_decode(layout, params);
   if (ws_bytes < d.bytes) return fail(MOG_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, d.bytes);
   // with a zero budget there is nothing to report
@@ -540,17 +578,18 @@ mog_status mog_decode(const mog_layout* layout, const mog_kv* kv, const float* q
   x.G = d.G;
   x.D = kv->head_dim;
   x.dtype = kv->dtype;
-  x.residual = params->residual ? 1 : 0;
+  x.residual = params->residual;
   x.shared = params->shared_selection;
   x.splits = d.splits;
   x.nblk = d.nblk;
   x.nb_res = d.nb_res;
   x.nb_chosen = d.nb_chosen;
-  x.scale = params->scale > 0.f ? params->scale : 1.0f / sqrtf((float)kv->head_dim);
+  x.scale = scale;
   x.ev_begin = params->exact_begin;
   x.ev_end = params->exact_end;
   x.repeat = std::max(1, params->exact_repeat);
   char* w = static_cast<char*>(ws);
+  x.ws.fq = params->residual == 2 ? reinterpret_cast<float*>(w + d.o_fq) : nullptr;
   x.ws.cl_score = reinterpret_cast<float*>(w + d.o_clscore);
   x.ws.cl_lse = reinterpret_cast<float*>(w + d.o_cllse);
   x.ws.cl_mask = reinterpret_cast<uint32_t*>(w + d.o_clmask);
@@ -667,6 +706,11 @@ mog_status mog_build(const mog_kv* kv, const mog_build_params* params, void* lay
   x.dtype = d.dtype;
   x.iters = params->kmeans_iters;
   x.seed = params->seed;
+  if (params->fm_dim) {
+    L.fm_scale = params->fm_scale > 0.f ? params->fm_scale : 1.0f / sqrtf((float)d.head_dim);
+    x.L = L;
+    x.fm_w = params->fm_w;
+  }
   char* w = static_cast<char*>(ws);
   x.ws.cent = reinterpret_cast<float*>(w + bpn.o_cent);
   x.ws.cent_norm = reinterpret_cast<float*>(w + bpn.o_norm);

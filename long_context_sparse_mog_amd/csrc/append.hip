@@ -35,6 +35,12 @@ struct AArgs {
   void* k_mid;
   void* v_mid;
   int64_t fold_row0;  // first fold-area row (unit u's start at fold_row0 + u * fold_cap)
+  // feature-map summaries (fm_dim > 0): projection and per-group sums
+  const float* fm_w;
+  float* cl_fz;
+  float* sub_fz;
+  int32_t fm_dim;
+  float fm_sqrt_scale;
   AppendSlot* slots;   // [n_units][kAppendMaxBlocks] per-block winners
   int32_t* counters;   // [n_units] blocks done with the current token
   int32_t fold_cap, n_recent;
@@ -181,6 +187,7 @@ __global__ __launch_bounds__(kAppendThreads) void k_append(AArgs a, int it) {
   __shared__ double w_d2[NW];
   __shared__ int w_id[NW], w_n[NW], w_f[NW];
   __shared__ int sel[4];  // last block: is it last, subcluster, its size, its fold count
+  __shared__ float xs[D];  // last block: sqrt(scale) k for the feature map
   const int u = blockIdx.y, p = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const mog_unit U = uni_unit(a.units + u);
   const AppendSeq sq = a.seq[U.seq];
@@ -342,6 +349,24 @@ __global__ __launch_bounds__(kAppendThreads) void k_append(AArgs a, int it) {
     welford_add(a.sub_ms[sg * (2 * D) + tid], a.sub_ms[sg * (2 * D) + D + tid], a.sub_vbar[sg * D + tid], sel[2], k,
                 v, a.sub_ms + sg * (2 * D) + tid, a.sub_ms + sg * (2 * D) + D + tid, a.sub_vbar + sg * D + tid);
   }
+  if (a.fm_dim) {
+    // the token's features join both groups' feature sums
+    if (tid < D) xs[tid] = a.fm_sqrt_scale * to_f(kx_t);
+    __syncthreads();
+    const int m = a.fm_dim;
+    if (tid < m) {
+      const float* w = a.fm_w + (int64_t)tid * D;
+      float t = 0.f, xx = 0.f;
+#pragma unroll 8
+      for (int e = 0; e < D; ++e) {
+        t += w[e] * xs[e];
+        xx += xs[e] * xs[e];
+      }
+      const float ph = expf(t - 0.5f * xx) * rsqrtf((float)m);
+      a.cl_fz[cg * m + tid] += ph;
+      a.sub_fz[sg * m + tid] += ph;
+    }
+  }
   if (tid == 0) {
     a.cl_fold[cg] = cf + 1;
     a.sub_fold[sg] = sel[3] + 1;
@@ -384,6 +409,11 @@ hipError_t launch_append(const AppendLaunch& x, hipStream_t s) {
   a.fold_row0 = x.L.total_mid;
   a.fold_cap = x.L.fold_capacity;
   a.n_recent = x.L.n_recent;
+  a.fm_w = x.L.fm_w;
+  a.cl_fz = x.L.cl_fz;
+  a.sub_fz = x.L.sub_fz;
+  a.fm_dim = x.L.fm_dim;
+  a.fm_sqrt_scale = sqrtf(x.L.fm_scale);
   a.slots = static_cast<AppendSlot*>(x.L.append_scratch);
   a.counters = reinterpret_cast<int32_t*>(a.slots + (int64_t)x.L.n_units * kAppendMaxBlocks);
   for (int i = 0; i < MOG_MAX_SEQ; ++i) a.seq[i] = x.seq[i];

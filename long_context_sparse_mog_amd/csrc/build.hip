@@ -58,6 +58,13 @@ struct BArgs {
   float* sub_ms;
   float* sub_vbar;
   unsigned long long seed;
+  // feature-map summaries
+  const float* fm_w_in;
+  float* fm_w;
+  float* cl_fz;
+  float* sub_fz;
+  int fm_dim;
+  float fm_sqrt_scale;
 };
 
 template <typename T>
@@ -614,6 +621,72 @@ __global__ __launch_bounds__(256) void k_group_stats(BArgs a) {
   }
 }
 
+// 6. Feature-map summaries (retrieval-completion page, abstract: a
+//    fixed-size feature-map summary of the keys, computed at prefill): per
+//    group the sum over its members of phi(x) = exp(W x - |x|^2 / 2) /
+//    sqrt(m), x = sqrt(s) k.  Thread (i, ph) holds row i of W in registers
+//    and takes every NPH-th row of each subcluster (rows staged 32 at a time
+//    in LDS with their |x|^2); sums are float32.  Block (0, 0) also copies W
+//    into the layout.
+template <int D, typename T>
+__global__ __launch_bounds__(256) void k_fm_summaries(BArgs a) {
+  constexpr int RB = 32;  // rows staged at once
+  __shared__ float xs[RB][D];
+  __shared__ float xx[RB];
+  __shared__ float part[256];
+  const int u = blockIdx.y, j = blockIdx.x, tid = threadIdx.x;
+  const int m = a.fm_dim, NPH = 256 / m;
+  if (u == 0 && j == 0)
+    for (int e = tid; e < m * D; e += 256) a.fm_w[e] = a.fm_w_in[e];
+  const mog_unit U = a.units[u];
+  if (j >= U.C) return;
+  const int S = U.S;
+  const int fi = tid % m, ph = tid / m;
+  float w[D];
+#pragma unroll
+  for (int e = 0; e < D; e += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(a.fm_w_in + (int64_t)fi * D + e);
+    w[e] = v.x; w[e + 1] = v.y; w[e + 2] = v.z; w[e + 3] = v.w;
+  }
+  const int32_t* off = a.sub_off + U.off_base;
+  const T* km = static_cast<const T*>(a.k_mid);
+  const float sq = a.fm_sqrt_scale, inv_sqrt_m = rsqrtf((float)m);
+  float zc = 0.f;
+  for (int i = 0; i < S; ++i) {
+    const int r0 = off[j * S + i], r1 = off[j * S + i + 1];
+    float zs = 0.f;
+    for (int rb = r0; rb < r1; rb += RB) {
+      const int nr = min(RB, r1 - rb);
+      __syncthreads();
+      for (int e = tid; e < nr * D; e += 256)
+        xs[e / D][e % D] = sq * elem<T>(km, (U.row_base + rb) * D + e);
+      __syncthreads();
+      if (tid < nr) {
+        float t = 0.f;
+#pragma unroll 8
+        for (int e = 0; e < D; ++e) t += xs[tid][e] * xs[tid][e];
+        xx[tid] = t;
+      }
+      __syncthreads();
+      for (int r = ph; r < nr; r += NPH) {
+        float t = 0.f;
+#pragma unroll
+        for (int e = 0; e < D; ++e) t += w[e] * xs[r][e];
+        zs += expf(t - 0.5f * xx[r]);
+      }
+    }
+    part[tid] = zs;
+    __syncthreads();
+    if (ph == 0) {
+      float t = 0.f;
+      for (int p = 0; p < NPH; ++p) t += part[p * m + fi];
+      a.sub_fz[(U.sub_base + (int64_t)j * S + i) * m + fi] = t * inv_sqrt_m;
+      zc += t;
+    }
+  }
+  if (ph == 0) a.cl_fz[(U.cl_base + j) * m + fi] = zc * inv_sqrt_m;
+}
+
 // ---------------------------------------------------------------------------
 // Launcher
 // ---------------------------------------------------------------------------
@@ -661,6 +734,15 @@ static hipError_t build_impl(const BuildLaunch& x, hipStream_t s) {
   constexpr int RPB = 4 * (64 / (D / (16 / (int)sizeof(T))));
   hipLaunchKernelGGL((k_gather_rows<D, T>), dim3((max_mid + RPB - 1) / RPB, nu), dim3(256), 0, s, a);
   hipLaunchKernelGGL((k_group_stats<D, T>), dim3(maxC, nu), dim3(256), 0, s, a);
+  if (x.L.fm_dim) {
+    a.fm_w_in = x.fm_w;
+    a.fm_w = x.L.fm_w;
+    a.cl_fz = x.L.cl_fz;
+    a.sub_fz = x.L.sub_fz;
+    a.fm_dim = x.L.fm_dim;
+    a.fm_sqrt_scale = sqrtf(x.L.fm_scale);
+    hipLaunchKernelGGL((k_fm_summaries<D, T>), dim3(maxC, nu), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

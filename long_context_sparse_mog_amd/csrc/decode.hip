@@ -35,6 +35,11 @@ struct LayoutRef {
   const int32_t* fold_sub;
   int64_t fold_row0;
   int32_t fold_cap;
+  // feature-map summaries: projection [fm_dim][D], per-group feature sums
+  const float* fm_w;
+  const float* cl_fz;
+  const float* sub_fz;
+  int32_t fm_dim;
 };
 
 struct DArgs {
@@ -49,6 +54,8 @@ struct DArgs {
   int32_t cstride;   // per-cluster workspace entries per unit (the largest C)
   float scale_l2;    // scale * log2(e)
   float half_s2_l2;  // scale^2 / 2 * log2(e)
+  float sqrt_scale;  // feature-map residual: the map is applied to sqrt(scale) q
+  int32_t score_blocks;  // blocks of the cluster-score kernel per unit that score clusters
   int32_t L_head_dim;
   DecodeWS ws;
 };
@@ -181,10 +188,38 @@ __device__ inline void score_rows(const float (&x)[R][D / 32], const float (&coe
 // ---------------------------------------------------------------------------
 constexpr int kScoreRowsPerWave = 4;  // clusters scored per wave (16 per block)
 
+// Feature-map residual: log2 of the features of every query head,
+// fq[u][h][i] = log2(e) (sqrt(s) w_i.q_h - s |q_h|^2 / 2) (the 1/sqrt(m) factor
+// is applied where the features are used).  One thread per (head, feature).
+template <int D, int G>
+__device__ inline void query_features(const DArgs& a, int u, int blk) {
+  const int m = a.L.fm_dim;
+  const int pi = blk * 256 + threadIdx.x;
+  if (pi >= G * m) return;
+  const int h = pi / m, i = pi % m;
+  const int seq = u / a.Hkv, kvh = u % a.Hkv;
+  const float* q = a.q + ((int64_t)seq * a.Hq + (int64_t)kvh * G + h) * D;
+  const float* w = a.L.fm_w + (int64_t)i * D;
+  float dot = 0.f, qq = 0.f;
+#pragma unroll 8
+  for (int e = 0; e < D; e += 4) {
+    const float4 qv = *reinterpret_cast<const float4*>(q + e);
+    const float4 wv = *reinterpret_cast<const float4*>(w + e);
+    dot += wv.x * qv.x + wv.y * qv.y + wv.z * qv.z + wv.w * qv.w;
+    qq += qv.x * qv.x + qv.y * qv.y + qv.z * qv.z + qv.w * qv.w;
+  }
+  const float s = a.sqrt_scale;
+  a.ws.fq[((int64_t)u * G + h) * m + i] = kLog2e * (s * dot - 0.5f * s * s * qq);
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_score_clusters(DArgs a) {
   constexpr int EPL = D / 32;
   const int u = blockIdx.y;
+  if ((int)blockIdx.x >= a.score_blocks) {
+    query_features<D, G>(a, u, blockIdx.x - a.score_blocks);
+    return;
+  }
   const mog_unit U = uni_unit(a.L.units + u);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g0 = blockIdx.x * (4 * kScoreRowsPerWave) + wave * kScoreRowsPerWave;
@@ -492,6 +527,25 @@ __device__ inline void write_residual_record(float (*st)[G][D + 2], float* dst) 
   }
 }
 
+// Feature-map residual: the weight (log2 of the estimated mass) of a group
+// whose feature sums z the wave holds (z[k]: feature lane + 64 k), for head h:
+// log2(sum_i e_h[i] z[i]) + max_h, with e_h = 2^(fq_h - max_h) in LDS.
+__device__ inline float fm_weight(const float (&z)[4], const float* e_h, float base_h, int FM) {
+  const int lane = threadIdx.x & 63;
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (64 * k < FM) s += e_h[lane + 64 * k] * z[k];
+  s = wave_sum_uniform(s);
+  return s > 0.f ? base_h + log2f(s) : -INFINITY;
+}
+
+__device__ inline void load_fz(const float* row, int FM, float (&z)[4]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) z[k] = 64 * k < FM ? row[lane + 64 * k] : 0.f;
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int nb_chosen) {
   constexpr int EPL = D / 32;
@@ -507,6 +561,8 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
   __shared__ int lds_fcnt[kMaxS];  // folded rows of each subcluster
   __shared__ int lds_off[kMaxS + 1];
   __shared__ int sh[16];
+  __shared__ float lds_fe[G][256];  // feature-map residual: 2^(fq - max) per head
+  __shared__ float lds_fbase[G];    // and max - log2(m) / 2
   const int u = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int s_keep_raw = b.top_s[u / a.Hkv];  // issued with the unit record
@@ -526,6 +582,26 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
   // slots past them (no such cluster in this unit) leave at once
   if (x < nb_chosen ? x >= n_ch : (x - nb_chosen) * kRestClustersPerBlock >= C) return;
   const uint32_t all = (1u << G) - 1u;
+  const bool fmr = a.residual == 2;
+  const int FM = a.L.fm_dim;
+  if (fmr) {
+    // every head's features, scaled by their maximum (read after the next
+    // barrier)
+    for (int h = wave; h < G; h += 4) {
+      const float* fqh = a.ws.fq + ((int64_t)u * G + h) * FM;
+      float v[4], mx = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[k] = 64 * k < FM ? fqh[lane + 64 * k] : -INFINITY;
+        mx = fmaxf(mx, v[k]);
+      }
+      mx = wave_max(mx);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (64 * k < FM) lds_fe[h][lane + 64 * k] = exp2f(v[k] - mx);
+      if (lane == 0) lds_fbase[h] = mx - 0.5f * log2f((float)FM);
+    }
+  }
   const int32_t* off = a.L.sub_off + U.off_base;
   float rm[G], rl[G], ro[G][VPL];
 #pragma unroll
@@ -729,13 +805,30 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
           need[k] = 0u;
           if (i < S && lds_cnt[i] + lds_fcnt[i] > 0) need[k] = mask & ~lds_sm[i];
         }
+        if (fmr) {
+          // the feature-map estimate of each left-out subcluster's mass
+          float z[RPW][4];
 #pragma unroll
-        for (int k = 0; k < RPW; ++k) {
-          if (!need[k]) continue;
-          const int i = wave + 4 * k;
+          for (int k = 0; k < RPW; ++k) load_fz(a.L.sub_fz + (sg0 + min(wave + 4 * k, S - 1)) * FM, FM, z[k]);
 #pragma unroll
-          for (int h = 0; h < G; ++h)
-            if ((need[k] >> h) & 1u) add_group<VPL>(rm[h], rl[h], ro[h], lds_sc[i][h], vb[k]);
+          for (int k = 0; k < RPW; ++k) {
+            if (!need[k]) continue;
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+              if (!((need[k] >> h) & 1u)) continue;
+              const float w = fm_weight(z[k], lds_fe[h], lds_fbase[h], FM);
+              if (w != -INFINITY) add_group<VPL>(rm[h], rl[h], ro[h], w, vb[k]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < RPW; ++k) {
+            if (!need[k]) continue;
+            const int i = wave + 4 * k;
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+              if ((need[k] >> h) & 1u) add_group<VPL>(rm[h], rl[h], ro[h], lds_sc[i][h], vb[k]);
+          }
         }
       }
     }
@@ -745,6 +838,33 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
     // (clusters past C re-read the last one and are skipped)
     constexpr int RCW = kRestClustersPerBlock / 4;
     const int y = x - nb_chosen;
+    if (fmr && a.residual) {
+      // the feature-map estimate of each left-out cluster's mass
+      uint32_t mask[RCW];
+      int n_g[RCW];
+      float vb[RCW][VPL], z[RCW][4];
+#pragma unroll
+      for (int k = 0; k < RCW; ++k) {
+        const int g = min(y * kRestClustersPerBlock + wave * RCW + k, C - 1);
+        mask[k] = a.ws.cl_mask[cw + g];
+        n_g[k] = off[(g + 1) * S] - off[g * S] + a.L.cl_fold[U.cl_base + g];
+        load_floats<VPL>(a.L.cl_vbar + (U.cl_base + g) * D + lane * VPL, vb[k]);
+        load_fz(a.L.cl_fz + (U.cl_base + g) * FM, FM, z[k]);
+      }
+      __syncthreads();  // the feature table
+#pragma unroll
+      for (int k = 0; k < RCW; ++k) {
+        const int g = y * kRestClustersPerBlock + wave * RCW + k;
+        if (g >= C) break;
+        const uint32_t unchosen = n_g[k] > 0 ? (all & ~mask[k]) : 0u;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          if (!((unchosen >> h) & 1u)) continue;
+          const float w = fm_weight(z[k], lds_fe[h], lds_fbase[h], FM);
+          if (w != -INFINITY) add_group<VPL>(rm[h], rl[h], ro[h], w, vb[k]);
+        }
+      }
+    } else {
     uint32_t mask[RCW];
     int n_g[RCW];
     float vb[RCW][VPL], sc[RCW][G];
@@ -768,6 +888,7 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
         for (int h = 0; h < G; ++h)
           if ((unchosen >> h) & 1u) add_group<VPL>(rm[h], rl[h], ro[h], sc[k][h], vb[k]);
       }
+    }
     }
   }
 
@@ -1232,8 +1353,8 @@ hipError_t launch_layout_table(const mog_layout& L, const SeqArgs& seq, hipStrea
 template <int D, int G>
 static hipError_t decode_impl(const DecodeLaunch& x, const DArgs& a, const BudgetArgs& b, hipStream_t s) {
   const int nu = x.L.n_units;
-  hipLaunchKernelGGL((k_score_clusters<D, G>), dim3((x.L.max_C + 4 * kScoreRowsPerWave - 1) / (4 * kScoreRowsPerWave), nu),
-                     dim3(256), 0, s, a);
+  const int fblocks = x.residual == 2 ? (G * x.L.fm_dim + 255) / 256 : 0;
+  hipLaunchKernelGGL((k_score_clusters<D, G>), dim3(a.score_blocks + fblocks, nu), dim3(256), 0, s, a);
   if (x.L.max_C <= 256)
     hipLaunchKernelGGL((k_select_topc<G, 4>), dim3(nu), dim3(64 * G), 0, s, a, b);
   else if (x.L.max_C <= 512)
@@ -1295,6 +1416,12 @@ hipError_t launch_decode(const DecodeLaunch& x, hipStream_t s) {
   a.L.fold_sub = x.L.fold_sub;
   a.L.fold_row0 = x.L.total_mid;
   a.L.fold_cap = x.L.fold_capacity;
+  a.L.fm_w = x.L.fm_w;
+  a.L.cl_fz = x.L.cl_fz;
+  a.L.sub_fz = x.L.sub_fz;
+  a.L.fm_dim = x.L.fm_dim;
+  a.sqrt_scale = sqrtf(x.scale);
+  a.score_blocks = (x.L.max_C + 4 * kScoreRowsPerWave - 1) / (4 * kScoreRowsPerWave);
   a.kv = x.kv;
   a.q = x.q;
   a.out = x.out;

@@ -123,6 +123,7 @@ struct DecodeWS {
   float* res_part;      // [n_units][nb_res][G][D+4] residual partials: one per chosen
                         //                       cluster, then one per rest block
   float* ex_part;       // [nblk][G][D+4]        exact-attention block records
+  float* fq;            // [n_units][G][fm_dim]  feature-map residual: log2 of each head's features
 };
 
 struct DecodeLaunch {
@@ -136,7 +137,7 @@ struct DecodeLaunch {
   int32_t* sel_s;
   int32_t c_stride, s_stride;
   int32_t Hq, G, D, dtype;
-  int32_t residual;
+  int32_t residual;     // 0 none, 1 Gaussian, 2 feature map
   int32_t shared;       // one selection per KV head
   int32_t splits;       // target exact blocks in total (balanced over units)
   int32_t nblk;         // exact blocks launched: splits + n_units
@@ -225,6 +226,7 @@ struct BuildLaunch {
   SeqArgs seq;
   int32_t D, dtype, iters;
   uint64_t seed;
+  const float* fm_w;  // feature-map projection to summarise with (fm_dim > 0)
   BuildWS ws;
 };
 

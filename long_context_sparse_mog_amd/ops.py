@@ -125,6 +125,11 @@ class Layout:
         if cap:
             fold = dict(fold_sub=self._view(c.fold_sub, cap, torch.int32).view(c.n_units, -1),
                         fold_pos=self._view(c.fold_pos, cap, torch.int32).view(c.n_units, -1))
+        if c.fm_dim:
+            m = c.fm_dim
+            fold.update(fm_w=self._view(c.fm_w, m * D, torch.float32).view(m, D),
+                        cl_fz=self._view(c.cl_fz, c.total_cl * m, torch.float32).view(-1, m),
+                        sub_fz=self._view(c.sub_fz, c.total_sub * m, torch.float32).view(-1, m))
         return dict(
             **fold,
             cl_fold=self._view(c.cl_fold, c.total_cl, torch.int32),
@@ -158,6 +163,9 @@ class Layout:
                         fold_pos=a["fold_pos"][u, :nf].cpu().numpy().astype(np.int64),
                         fold_k=a["k_mid"][f0:f0 + nf].float().cpu().numpy(),
                         fold_v=a["v_mid"][f0:f0 + nf].float().cpu().numpy())
+        if self.c.fm_dim:
+            fold.update(fm_w=a["fm_w"].cpu().numpy(), fm_scale=float(self.c.fm_scale),
+                        cl_z=a["cl_fz"][cl].cpu().numpy(), sub_z=a["sub_fz"][sb].cpu().numpy())
         return dict(
             **fold,
             cl_fold=a["cl_fold"][cl].cpu().numpy().astype(np.int64),
@@ -170,24 +178,26 @@ class Layout:
         )
 
 
-def _dims(n_seq, n_kv_heads, head_dim, dtype, n_sink, n_recent, seq_lens, fold_capacity=0):
+def _dims(n_seq, n_kv_heads, head_dim, dtype, n_sink, n_recent, seq_lens, fold_capacity=0, fm_dim=0):
     lens = capi.int_array(seq_lens)
-    d = capi.mog_dims(n_seq, n_kv_heads, head_dim, dtype, n_sink, n_recent, fold_capacity,
+    d = capi.mog_dims(n_seq, n_kv_heads, head_dim, dtype, n_sink, n_recent, fold_capacity, fm_dim,
                       C.cast(lens, C.POINTER(capi.i32)))
     return d, lens
 
 
-def mog_layout_size(n_kv_heads, head_dim, dtype, n_sink, n_recent, seq_lens, fold_capacity=0) -> int:
-    d, _keep = _dims(len(seq_lens), n_kv_heads, head_dim, dtype, n_sink, n_recent, seq_lens, fold_capacity)
+def mog_layout_size(n_kv_heads, head_dim, dtype, n_sink, n_recent, seq_lens, fold_capacity=0, fm_dim=0) -> int:
+    d, _keep = _dims(len(seq_lens), n_kv_heads, head_dim, dtype, n_sink, n_recent, seq_lens, fold_capacity,
+                     fm_dim)
     out = C.c_size_t()
     check(lib().mog_layout_size(C.byref(d), C.byref(out)), "mog_layout_size")
     return out.value
 
 
-def mog_layout_init(kv: KVCache, n_sink, n_recent, device="cuda", stream=None, fold_capacity=0) -> Layout:
+def mog_layout_init(kv: KVCache, n_sink, n_recent, device="cuda", stream=None, fold_capacity=0,
+                    fm_dim=0) -> Layout:
     """Allocate and carve an empty layout for ``kv`` (for importing arrays)."""
     d, _keep = _dims(kv.c.n_seq, kv.c.n_kv_heads, kv.c.head_dim, kv.c.dtype, n_sink, n_recent,
-                     kv.seq_lens, fold_capacity)
+                     kv.seq_lens, fold_capacity, fm_dim)
     nbytes = C.c_size_t()
     check(lib().mog_layout_size(C.byref(d), C.byref(nbytes)), "mog_layout_size")
     mem = torch.zeros(nbytes.value, dtype=torch.uint8, device=device)
@@ -199,10 +209,11 @@ def mog_layout_init(kv: KVCache, n_sink, n_recent, device="cuda", stream=None, f
 
 def decode_params(n_q_heads, top_c, top_s, residual=True, scale=0.0, splits=0, shared=False):
     """mog_decode_params; ``top_c``/``top_s`` are ints or per-sequence lists;
+    ``residual``: False/0 none, True/1 Gaussian, 2 or "fm" feature map;
     ``shared``: one selection per KV head instead of one per query head."""
     p = capi.mog_decode_params()
     p.n_q_heads = n_q_heads
-    p.residual = 1 if residual else 0
+    p.residual = 2 if residual in (2, "fm") else (1 if residual else 0)
     p.scale = float(scale)
     p.splits = int(splits)
     p.shared_selection = 1 if shared else 0
@@ -242,12 +253,21 @@ def workspace(nbytes, device="cuda"):
 
 
 def mog_build(kv: KVCache, n_sink, n_recent, kmeans_iters=10, seed=0, ws=None, stream=None,
-              fold_capacity=0) -> Layout:
+              fold_capacity=0, fm_w=None, fm_scale=0.0) -> Layout:
     """Prefill-side build; allocates the layout (and the workspace unless given).
-    ``fold_capacity``: rows per unit kept for mog_append."""
-    bp = capi.mog_build_params(kmeans_iters, n_sink, n_recent, fold_capacity, seed)
+    ``fold_capacity``: rows per unit kept for mog_append; ``fm_w``: a device
+    float32 [m][head_dim] projection for feature-map summaries (m = 64, 128
+    or 256), ``fm_scale`` their logit scale (0: 1/sqrt(head_dim))."""
+    fm_dim = 0
+    if fm_w is not None:
+        _require_cuda(fm_w)
+        if fm_w.dtype != torch.float32 or not fm_w.is_contiguous() or fm_w.dim() != 2:
+            raise ValueError("fm_w must be a contiguous float32 [m][head_dim] tensor")
+        fm_dim = fm_w.shape[0]
+    bp = capi.mog_build_params(kmeans_iters, n_sink, n_recent, fold_capacity, seed, fm_dim, float(fm_scale),
+                               _vp(fm_w))
     d, _keep = _dims(kv.c.n_seq, kv.c.n_kv_heads, kv.c.head_dim, kv.c.dtype, n_sink, n_recent,
-                     kv.seq_lens, fold_capacity)
+                     kv.seq_lens, fold_capacity, fm_dim)
     nbytes = C.c_size_t()
     check(lib().mog_layout_size(C.byref(d), C.byref(nbytes)), "mog_layout_size")
     mem = torch.empty(nbytes.value, dtype=torch.uint8, device=kv.k.device)
@@ -322,7 +342,10 @@ def import_layout(kv: KVCache, n_sink, n_recent, units, k_rows=None, v_rows=None
     ``cl_vbar``, ``sub_mu``, ``sub_var``, ``sub_vbar``.  The reordered K/V
     rows are gathered from ``kv`` on the device.
     """
-    lay = mog_layout_init(kv, n_sink, n_recent, device=kv.k.device, stream=stream, fold_capacity=fold_capacity)
+    fm = units[0].get("cl_z") if units else None
+    fm_dim = 0 if fm is None else int(np.asarray(fm).shape[1])
+    lay = mog_layout_init(kv, n_sink, n_recent, device=kv.k.device, stream=stream, fold_capacity=fold_capacity,
+                          fm_dim=fm_dim)
     a = lay.arrays()
     dev = kv.k.device
     D = kv.head_dim
@@ -355,4 +378,14 @@ def import_layout(kv: KVCache, n_sink, n_recent, units, k_rows=None, v_rows=None
         a["sub_ms"][sb, :D] = f32(src["sub_mu"])
         a["sub_ms"][sb, D:] = f32(src["sub_var"])
         a["sub_vbar"][sb] = f32(src["sub_vbar"])
+        if fm_dim:
+            a["cl_fz"][cl] = f32(src["cl_z"])
+            a["sub_fz"][sb] = f32(src["sub_z"])
+    if fm_dim:
+        a["fm_w"][:] = torch.as_tensor(np.asarray(units[0]["fm_w"], np.float32), device=dev)
+        sc = float(units[0]["fm_scale"])
+        # (the carved default is the library's own 1/sqrt(head_dim), the
+        # value a decode with scale 0 compares against)
+        if abs(sc * math.sqrt(D) - 1.0) > 1e-6:
+            lay.c.fm_scale = sc
     return lay

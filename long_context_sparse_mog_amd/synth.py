@@ -290,3 +290,12 @@ def to_paged(b: Batch):
     b.pool_K, b.pool_V = pool_K, pool_V
     b.block_table = torch.as_tensor(bt, device=dev)
     return b
+
+
+def feature_map_w(m: int, d: int, seed: int = BASE_SEED + 99, device="cpu") -> torch.Tensor:
+    """A seeded float32 [m][d] projection with N(0, 1) entries (the random
+    draws of the feature-map summaries; both the library and the oracle take
+    it as an input)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return torch.randn(m, d, generator=g).to(device)

@@ -15,8 +15,11 @@ NEAR_TIE_SHARED = 1e-4  # relative, on the shared group scores (sums of mass fra
 
 
 def unit_layout_arrays(L: "O.UnitLayout") -> dict:
-    return dict(perm=L.perm, sub_off=L.sub_off, cl_mu=L.cl_mu, cl_var=L.cl_var, cl_vbar=L.cl_vbar,
-                sub_mu=L.sub_mu, sub_var=L.sub_var, sub_vbar=L.sub_vbar)
+    out = dict(perm=L.perm, sub_off=L.sub_off, cl_mu=L.cl_mu, cl_var=L.cl_var, cl_vbar=L.cl_vbar,
+               sub_mu=L.sub_mu, sub_var=L.sub_var, sub_vbar=L.sub_vbar)
+    if L.cl_z is not None:
+        out.update(cl_z=L.cl_z, sub_z=L.sub_z, fm_w=L.fm_w, fm_scale=L.fm_scale)
+    return out
 
 
 def oracle_layout_from_export(ex: dict, n_sink: int, n_recent: int) -> "O.UnitLayout":
@@ -27,7 +30,9 @@ def oracle_layout_from_export(ex: dict, n_sink: int, n_recent: int) -> "O.UnitLa
                         cl_var=ex["cl_var"], cl_vbar=ex["cl_vbar"], sub_mu=ex["sub_mu"],
                         sub_var=ex["sub_var"], sub_vbar=ex["sub_vbar"],
                         fold_pos=[int(x) for x in ex.get("fold_pos", [])],
-                        fold_sub=[int(x) for x in ex.get("fold_sub", [])])
+                        fold_sub=[int(x) for x in ex.get("fold_sub", [])],
+                        fm_w=ex.get("fm_w"), fm_scale=ex.get("fm_scale"), cl_z=ex.get("cl_z"),
+                        sub_z=ex.get("sub_z"))
 
 
 def build_oracle_layouts(batch, iters=10, seed=0, units=None):
@@ -86,12 +91,15 @@ def _shared_scores(L, Q, scale):
 
 def compare_unit(L, K, V, Q, c, s, gpu_out, gpu_lse, gpu_sel_c, gpu_sel_s, tol, residual=True,
                  scale=None, shared=False):
+    # residual: False, True (Gaussian) or "fm" (feature map)
     """Compare one unit's GPU results with the oracle's.  Returns a dict of
     the errors; raises AssertionError on a selection mismatch that is not a
     near tie.  ``shared``: one selection per KV head (oracle reading R14)."""
     G, d = Q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    ref = O.decode_unit(L, K, V, Q, c, s, scale=scale, residual=residual, shared=shared)
+    fmr = residual == "fm"
+    ref = O.decode_unit(L, K, V, Q, c, s, scale=scale, residual=bool(residual), shared=shared,
+                        feature_residual=fmr)
     if shared:
         gs, gs_sub = _shared_scores(L, Q, scale)
     sel_c_gpu, sel_s_gpu = [], []
@@ -126,8 +134,8 @@ def compare_unit(L, K, V, Q, c, s, gpu_out, gpu_lse, gpu_sel_c, gpu_sel_s, tol, 
                         assert _cutoff_ok(ss, L.sub_count[g0:g0 + L.S] > 0, gsub, osub, s), (h, j, gsub, osub)
                     ties += 1
     if ties:
-        ref = O.decode_unit(L, K, V, Q, c, s, scale=scale, residual=residual,
-                            sel_override=(sel_c_gpu, sel_s_gpu))
+        ref = O.decode_unit(L, K, V, Q, c, s, scale=scale, residual=bool(residual),
+                            sel_override=(sel_c_gpu, sel_s_gpu), feature_residual=fmr)
     errs = [rel_l2(gpu_out[h], ref["out"][h]) for h in range(G)]
     lse_err = float(np.max(np.abs(np.asarray(gpu_lse, np.float64) - ref["lse"])))
     assert max(errs) <= tol, (errs, tol)

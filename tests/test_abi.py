@@ -65,9 +65,9 @@ def test_struct_layout_matches_c(tmp_path):
             assert int(got[f"{name}.{f}"]) == getattr(cls, f).offset, f"{name}.{f}"
 
 
-def _dims(lens, n_sink=64, n_recent=256, hkv=8, d=128, dtype=capi.MOG_BF16, fold_capacity=0):
+def _dims(lens, n_sink=64, n_recent=256, hkv=8, d=128, dtype=capi.MOG_BF16, fold_capacity=0, fm_dim=0):
     arr = capi.int_array(lens)
-    return capi.mog_dims(len(lens), hkv, d, dtype, n_sink, n_recent, fold_capacity,
+    return capi.mog_dims(len(lens), hkv, d, dtype, n_sink, n_recent, fold_capacity, fm_dim,
                          C.cast(arr, C.POINTER(capi.i32))), arr
 
 
@@ -87,6 +87,12 @@ def test_layout_size_matches_geometry(L):
     assert L.mog_layout_size(C.byref(d2), C.byref(out2)) == capi.MOG_OK
     grow = 8 * cap * (2 * D * 2 + 2 * 4)
     assert grow <= out2.value - out.value <= grow + 8 * 256
+    # feature-map summaries: the projection and m floats per group
+    d3, keep3 = _dims([1048576], fm_dim=128)
+    out3 = C.c_size_t()
+    assert L.mog_layout_size(C.byref(d3), C.byref(out3)) == capi.MOG_OK
+    grow = 128 * D * 4 + 8 * (Cc + Cc * S) * 128 * 4
+    assert grow <= out3.value - out.value <= grow + 4 * 256
 
 
 def test_layout_unit_geometry(L):
@@ -134,6 +140,7 @@ def test_layout_unit_geometry(L):
     (dict(lens=[]), capi.MOG_ERR_INVALID_ARG),
     (dict(lens=[5000], fold_capacity=-1), capi.MOG_ERR_INVALID_ARG),
     (dict(lens=[5000], fold_capacity=capi.MOG_MAX_FOLD + 1), capi.MOG_ERR_INVALID_ARG),
+    (dict(lens=[5000], fm_dim=100), capi.MOG_ERR_UNSUPPORTED),
 ])
 def test_layout_size_rejects(L, bad, status):
     lens = bad.pop("lens")
@@ -215,6 +222,33 @@ def test_build_validation(L):
     assert L.mog_build(C.byref(kv), C.byref(bp), C.c_void_p(0x1001), 1 << 40, C.c_void_p(0x1000), 1 << 40, C.byref(lay), None) == capi.MOG_ERR_INVALID_ARG
     # layout memory too small
     assert L.mog_build(C.byref(kv), C.byref(bp), C.c_void_p(0x1000), 64, C.c_void_p(0x1000), 1 << 40, C.byref(lay), None) == capi.MOG_ERR_WORKSPACE
+    # feature-map summaries without a projection, with an odd size, a negative scale
+    bp.fm_dim = 128
+    assert L.mog_workspace_size(capi.MOG_OP_BUILD, C.byref(kv), None, C.byref(bp), None, C.byref(out)) == capi.MOG_ERR_INVALID_ARG
+    bp.fm_w = 0x4000
+    assert L.mog_workspace_size(capi.MOG_OP_BUILD, C.byref(kv), None, C.byref(bp), None, C.byref(out)) == capi.MOG_OK
+    bp.fm_scale = -1.0
+    assert L.mog_workspace_size(capi.MOG_OP_BUILD, C.byref(kv), None, C.byref(bp), None, C.byref(out)) == capi.MOG_ERR_INVALID_ARG
+    bp.fm_scale, bp.fm_dim = 0.0, 96
+    assert L.mog_workspace_size(capi.MOG_OP_BUILD, C.byref(kv), None, C.byref(bp), None, C.byref(out)) == capi.MOG_ERR_UNSUPPORTED
+
+
+def test_feature_residual_validation(L):
+    kv, keep = _kv([5000])
+    lay = _host_layout([5000], cap=0, folded=[0])
+    p = capi.mog_decode_params(n_q_heads=32, top_c=4, top_s=2, residual=2, scale=0.0, splits=0)
+    args = (C.c_void_p(0x1000), C.byref(p), C.c_void_p(0x1000), None, None, None, C.c_void_p(0x1000), 1 << 40, None)
+    # residual=2 on a layout without summaries
+    assert L.mog_decode(C.byref(lay), C.byref(kv), *args) == capi.MOG_ERR_INVALID_ARG
+    assert "fm_dim" in L.mog_last_error().decode()
+    # summaries built with another scale
+    lay.fm_dim, lay.fm_scale = 128, 0.5
+    for name in ("fm_w", "cl_fz", "sub_fz"):
+        setattr(lay, name, 0x20000)
+    assert L.mog_decode(C.byref(lay), C.byref(kv), *args) == capi.MOG_ERR_INVALID_ARG
+    assert "scale" in L.mog_last_error().decode()
+    p.residual = 3
+    assert L.mog_decode(C.byref(lay), C.byref(kv), *args) == capi.MOG_ERR_INVALID_ARG
 
 
 def _host_layout(lens, cap, folded):
