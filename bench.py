@@ -320,6 +320,61 @@ def incremental_bench(state, steps, warmup):
     return res
 
 
+def feature_residual_comparison(steps, warmup, n_qsets, m=128):
+    """The ragged paged workload (KV heads 0-3 mixture keys, 4-7 isotropic
+    keys with near-uniform attention) built with feature-map summaries (m
+    features): the Gaussian residual against the feature-map residual, error
+    against dense per head class (mean per-head relative L2 over the query
+    sets) and steps/s of each."""
+    import torch
+
+    from long_context_sparse_mog_amd import capi, ops, synth
+
+    wl = synth.config(4)
+    b = synth.generate(wl, device="cuda", n_qsets=n_qsets, keep_contiguous=False)
+    kv = ops.KVCache.from_batch(b)
+    W = synth.feature_map_w(m, wl.head_dim, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.time()
+    lay = ops.mog_build(kv, wl.n_sink, wl.n_recent, kmeans_iters=wl.kmeans_iters, seed=1, fm_w=W)
+    torch.cuda.synchronize()
+    build_s = time.time() - t0
+    qs = [b.Q[i].contiguous() for i in range(n_qsets)]
+    out = torch.empty_like(qs[0])
+    lse = torch.empty(qs[0].shape[:2], device="cuda")
+    pd = ops.decode_params(wl.n_q_heads, 1, 1)
+    res = dict(workload=wl.name, fm_dim=m, build_s_with_summaries=build_s)
+    G = wl.group
+    he = set(wl.high_entropy_heads)
+    for name, mode in (("gaussian", True), ("feature_map", "fm"), ("top_only", False)):
+        p = ops.decode_params(wl.n_q_heads, list(wl.top_c), list(wl.top_s), residual=mode)
+        ws = ops.workspace(ops.mog_workspace_size(capi.MOG_OP_DECODE, layout=lay, params=p))
+        for i in range(warmup):
+            ops.mog_decode(lay, kv, qs[i % n_qsets], p, out=out, lse=lse, ws=ws)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            ops.mog_decode(lay, kv, qs[i % n_qsets], p, out=out, lse=lse, ws=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        err_mix, err_he = [], []
+        for t in range(min(4, n_qsets)):
+            o = ops.mog_decode(lay, kv, qs[t], p)[0]
+            od, _ = ops.mog_dense_decode(kv, qs[t], pd)
+            e = (torch.linalg.norm(o - od, dim=-1) / torch.linalg.norm(od, dim=-1)).cpu()
+            for hq in range(wl.n_q_heads):
+                (err_he if hq // G in he else err_mix).append(e[:, hq])
+        res[name] = dict(steps_per_s=1000.0 / ms, ms_per_step=ms,
+                         err_vs_dense_mixture_heads=float(torch.cat(err_mix).mean()),
+                         err_vs_dense_high_entropy_heads=float(torch.cat(err_he).mean()))
+    del lay, kv, b
+    torch.cuda.empty_cache()
+    return res
+
+
 def build_timing(reps=3):
     """mog_build (10 k-means rounds, subclusters, reorder, stats) of the
     single-head 128K-key workload: median wall time over reps."""
@@ -502,6 +557,8 @@ def main():
             r, _ = bench_workload(idx, min(args.steps, 100), min(args.warmup, 10), args.qsets, ev)
             others[r["workload"]] = {k: r[k] for k in keep}
         others["build"] = build_timing()
+        others["feature_map_residual"] = feature_residual_comparison(min(args.steps, 100), min(args.warmup, 10),
+                                                                     args.qsets)
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(st1m, args.cpu_seconds)
