@@ -98,6 +98,10 @@ typedef struct {
   int32_t n_recent;         /* anchors at the end of every sequence   */
   int32_t fold_capacity;    /* rows per unit kept for mog_append, 0..MOG_MAX_FOLD */
   int32_t fm_dim;           /* features per group summary: 0 (none), 64, 128, 256 */
+  int32_t rows_external;    /* 1: k_mid / v_mid are caller arrays outside the
+                               layout buffer (mog_layout_rows gives their
+                               size), e.g. pinned host memory the GPU reads
+                               over the host link; 0: carved from the buffer */
   const int32_t* seq_lens;  /* HOST [n_seq] lengths at the build */
 } mog_dims;
 
@@ -175,6 +179,7 @@ typedef struct {
   float* fm_w;
   float* cl_fz;
   float* sub_fz;
+  int32_t rows_external;  /* k_mid / v_mid live outside the layout buffer */
 } mog_layout;
 
 typedef struct {
@@ -187,6 +192,13 @@ typedef struct {
   float fm_scale;       /* their logit scale; 0 selects 1/sqrt(head_dim)   */
   const float* fm_w;    /* DEVICE [fm_dim][head_dim] float32, rows drawn from
                            N(0, I) by the caller; read during the build    */
+  void* rows_k;         /* NULL, or caller arrays of mog_layout_rows rows of */
+  void* rows_v;         /* head_dim elements each, 16-byte aligned, that the
+                           GPU can address (device memory, or pinned host
+                           memory: the KV-offload setting of the retrieval-
+                           completion page's abstract, where only the rows a
+                           step selects cross the host link); they then hold
+                           k_mid / v_mid instead of the layout buffer      */
 } mog_build_params;
 
 typedef struct {
@@ -234,11 +246,18 @@ typedef enum { MOG_OP_BUILD = 0, MOG_OP_DECODE = 1, MOG_OP_DENSE = 2 } mog_op;
 /* Bytes of the layout buffer for `dims`.  Pure host computation. */
 mog_status mog_layout_size(const mog_dims* dims, size_t* bytes);
 
+/* Rows of k_mid (and of v_mid) for `dims`: the middle regions of every unit
+ * plus their fold areas, sum over units of (N - n_sink - n_recent) +
+ * n_units * fold_capacity.  An external row array holds rows * head_dim
+ * elements of the dtype.  Pure host computation. */
+mog_status mog_layout_rows(const mog_dims* dims, int64_t* rows);
+
 /* Carve `layout_mem` (DEVICE, >= mog_layout_size bytes, 256-byte aligned)
  * into a layout for `dims`, fill `out` (host) and enqueue the write of the
  * device unit table and the zeroing of the fold counts.  mog_build calls
  * this itself; it is exported so a caller can import a layout computed
- * elsewhere by writing the arrays (cl_fold / sub_fold must stay zero). */
+ * elsewhere by writing the arrays (cl_fold / sub_fold must stay zero).
+ * With dims->rows_external the caller also sets out->k_mid / out->v_mid. */
 mog_status mog_layout_init(const mog_dims* dims, void* layout_mem, size_t layout_bytes,
                            mog_layout* out, hipStream_t stream);
 

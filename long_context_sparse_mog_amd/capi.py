@@ -36,7 +36,7 @@ class mog_kv(C.Structure):
 class mog_dims(C.Structure):
     _fields_ = [("n_seq", i32), ("n_kv_heads", i32), ("head_dim", i32), ("dtype", i32),
                 ("n_sink", i32), ("n_recent", i32), ("fold_capacity", i32), ("fm_dim", i32),
-                ("seq_lens", C.POINTER(i32))]
+                ("rows_external", i32), ("seq_lens", C.POINTER(i32))]
 
 
 class mog_unit(C.Structure):
@@ -55,12 +55,14 @@ class mog_layout(C.Structure):
                 ("k_mid", vp), ("v_mid", vp), ("perm", vp), ("sub_off", vp), ("cl_ms", vp),
                 ("cl_vbar", vp), ("sub_ms", vp), ("sub_vbar", vp), ("fold_sub", vp),
                 ("fold_pos", vp), ("cl_fold", vp), ("sub_fold", vp),
-                ("append_scratch", vp), ("fm_w", vp), ("cl_fz", vp), ("sub_fz", vp)]
+                ("append_scratch", vp), ("fm_w", vp), ("cl_fz", vp), ("sub_fz", vp),
+                ("rows_external", i32)]
 
 
 class mog_build_params(C.Structure):
     _fields_ = [("kmeans_iters", i32), ("n_sink", i32), ("n_recent", i32), ("fold_capacity", i32),
-                ("seed", C.c_uint64), ("fm_dim", i32), ("fm_scale", C.c_float), ("fm_w", vp)]
+                ("seed", C.c_uint64), ("fm_dim", i32), ("fm_scale", C.c_float), ("fm_w", vp),
+                ("rows_k", vp), ("rows_v", vp)]
 
 
 class mog_decode_params(C.Structure):
@@ -74,6 +76,7 @@ class mog_decode_params(C.Structure):
 # name -> (restype, argtypes); every name is declared in include/mog.h
 SIGNATURES = {
     "mog_layout_size": (i32, [C.POINTER(mog_dims), C.POINTER(C.c_size_t)]),
+    "mog_layout_rows": (i32, [C.POINTER(mog_dims), C.POINTER(i64)]),
     "mog_layout_init": (i32, [C.POINTER(mog_dims), vp, C.c_size_t, C.POINTER(mog_layout), vp]),
     "mog_layout_unit": (i32, [C.POINTER(mog_layout), i32, C.POINTER(mog_unit)]),
     "mog_workspace_size": (i32, [i32, C.POINTER(mog_kv), C.POINTER(mog_layout),

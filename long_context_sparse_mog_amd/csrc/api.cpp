@@ -68,6 +68,8 @@ mog_status check_dims(const mog_dims* d) {
     return fail(MOG_ERR_INVALID_ARG, "fold_capacity=%d outside [0, %d]", d->fold_capacity, MOG_MAX_FOLD);
   if (d->fm_dim != 0 && d->fm_dim != 64 && d->fm_dim != 128 && d->fm_dim != 256)
     return fail(MOG_ERR_UNSUPPORTED, "fm_dim=%d (supported: 0, 64, 128, 256)", d->fm_dim);
+  if (d->rows_external != 0 && d->rows_external != 1)
+    return fail(MOG_ERR_INVALID_ARG, "rows_external=%d (0 or 1)", d->rows_external);
   if (!d->seq_lens) return fail(MOG_ERR_INVALID_ARG, "seq_lens is NULL");
   for (int s = 0; s < d->n_seq; ++s) {
     const int N = d->seq_lens[s];
@@ -93,7 +95,8 @@ LayoutPlan plan_layout(const mog_dims* d) {
   const int64_t nu = (int64_t)d->n_seq * d->n_kv_heads;
   const int D = d->head_dim;
   // K/V rows: the reordered middle regions, then each unit's fold area
-  const size_t rows = (size_t)p.t.mid + (size_t)nu * d->fold_capacity;
+  // (none in the buffer when the caller keeps them elsewhere)
+  const size_t rows = d->rows_external ? 0 : (size_t)p.t.mid + (size_t)nu * d->fold_capacity;
   size_t o = 0;
   p.o_units = o; o = align_up(o + nu * sizeof(mog_unit));
   p.o_kmid = o; o = align_up(o + rows * D * esize(d->dtype));
@@ -340,6 +343,11 @@ mog_status check_build(const mog_kv* kv, const mog_build_params* bp, mog_dims* d
   d.n_recent = bp->n_recent;
   d.fold_capacity = bp->fold_capacity;
   d.fm_dim = bp->fm_dim;
+  d.rows_external = (bp->rows_k || bp->rows_v) ? 1 : 0;
+  if (d.rows_external && !(bp->rows_k && bp->rows_v))
+    return fail(MOG_ERR_INVALID_ARG, "rows_k and rows_v must both be set or both be NULL");
+  if (d.rows_external && (!aligned(bp->rows_k, 16) || !aligned(bp->rows_v, 16)))
+    return fail(MOG_ERR_INVALID_ARG, "rows_k and rows_v must be 16-byte aligned");
   d.seq_lens = kv->seq_lens;
   if ((st = check_dims(&d)) != MOG_OK) return st;
   if (bp->fm_dim) {
@@ -402,6 +410,15 @@ const char* mog_status_string(mog_status st) {
 
 const char* mog_last_error(void) { return g_last_error.c_str(); }
 
+mog_status mog_layout_rows(const mog_dims* dims, int64_t* rows) {
+  mog_status st = check_dims(dims);
+  if (st != MOG_OK) return st;
+  if (!rows) return fail(MOG_ERR_INVALID_ARG, "rows is NULL");
+  const LayoutPlan p = plan_layout(dims);
+  *rows = p.t.mid + (int64_t)dims->n_seq * dims->n_kv_heads * dims->fold_capacity;
+  return ok();
+}
+
 mog_status mog_layout_size(const mog_dims* dims, size_t* bytes) {
   mog_status st = check_dims(dims);
   if (st != MOG_OK) return st;
@@ -438,8 +455,9 @@ static mog_status layout_carve(const mog_dims* dims, void* mem, size_t mem_bytes
   L.total_sub = p.t.sub;
   L.total_off = p.t.off;
   L.units = reinterpret_cast<mog_unit*>(b + p.o_units);
-  L.k_mid = b + p.o_kmid;
-  L.v_mid = b + p.o_vmid;
+  L.rows_external = dims->rows_external;
+  L.k_mid = dims->rows_external ? nullptr : b + p.o_kmid;  // external: set by the caller
+  L.v_mid = dims->rows_external ? nullptr : b + p.o_vmid;
   L.perm = reinterpret_cast<int32_t*>(b + p.o_perm);
   L.sub_off = reinterpret_cast<int32_t*>(b + p.o_suboff);
   L.cl_ms = reinterpret_cast<float*>(b + p.o_clms);
@@ -693,6 +711,10 @@ mog_status mog_build(const mog_kv* kv, const mog_build_params* params, void* lay
   if (ws_bytes < bpn.bytes) return fail(MOG_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, bpn.bytes);
   mog_layout L;
   if ((st = layout_carve(&d, layout_mem, layout_bytes, &L)) != MOG_OK) return st;
+  if (d.rows_external) {
+    L.k_mid = params->rows_k;
+    L.v_mid = params->rows_v;
+  }
   SeqArgs sa;
   fill_seq_args(sa, d.n_seq, d.seq_lens);
   hipError_t e = launch_layout_table(L, sa, stream);

@@ -34,6 +34,14 @@ def _require_cuda(*ts):
             raise ValueError("libmog works on device tensors only")
 
 
+def _require_gpu_addressable(*ts):
+    """Device tensors, or pinned host tensors (which the GPU reads over the
+    host link)."""
+    for t in ts:
+        if t is not None and not (t.is_cuda or t.is_pinned()):
+            raise ValueError("libmog reads device tensors or pinned host tensors only")
+
+
 class KVCache:
     """A batch of KV caches as the library sees it.
 
@@ -43,7 +51,9 @@ class KVCache:
     """
 
     def __init__(self, k, v, seq_lens, block_table=None):
-        _require_cuda(k, v, block_table)
+        # (k and v may be pinned host memory: the offloaded-cache setting)
+        _require_gpu_addressable(k, v)
+        _require_cuda(block_table)
         if k.dtype not in _DTYPES or v.dtype != k.dtype:
             raise ValueError("k/v must both be float32 or bfloat16")
         if not (k.is_contiguous() and v.is_contiguous()):
@@ -94,11 +104,14 @@ class KVCache:
 
 
 class Layout:
-    """A cluster layout living in ``mem`` (a uint8 device tensor)."""
+    """A cluster layout living in ``mem`` (a uint8 device tensor); with
+    external rows, k_mid / v_mid live in the tensors ``rows`` (e.g. pinned
+    host memory)."""
 
-    def __init__(self, c_layout, mem):
+    def __init__(self, c_layout, mem, rows=None):
         self.c = c_layout
         self.mem = mem
+        self.rows = rows
 
     @property
     def n_units(self):
@@ -121,6 +134,11 @@ class Layout:
         kd = torch.bfloat16 if c.dtype == capi.MOG_BF16 else torch.float32
         rows = c.total_mid + c.n_units * c.fold_capacity
         cap = c.n_units * c.fold_capacity
+        if self.rows is not None:
+            kr, vr = (t.view(kd).view(-1, D)[:rows] for t in self.rows)
+        else:
+            kr = self._view(c.k_mid, rows * D, kd).view(-1, D)
+            vr = self._view(c.v_mid, rows * D, kd).view(-1, D)
         fold = {}
         if cap:
             fold = dict(fold_sub=self._view(c.fold_sub, cap, torch.int32).view(c.n_units, -1),
@@ -134,8 +152,8 @@ class Layout:
             **fold,
             cl_fold=self._view(c.cl_fold, c.total_cl, torch.int32),
             sub_fold=self._view(c.sub_fold, c.total_sub, torch.int32),
-            k_mid=self._view(c.k_mid, rows * D, kd).view(-1, D),
-            v_mid=self._view(c.v_mid, rows * D, kd).view(-1, D),
+            k_mid=kr,
+            v_mid=vr,
             perm=self._view(c.perm, c.total_mid, torch.int32),
             sub_off=self._view(c.sub_off, c.total_off, torch.int32),
             cl_ms=self._view(c.cl_ms, c.total_cl * 2 * D, torch.float32).view(-1, 2 * D),
@@ -178,9 +196,10 @@ class Layout:
         )
 
 
-def _dims(n_seq, n_kv_heads, head_dim, dtype, n_sink, n_recent, seq_lens, fold_capacity=0, fm_dim=0):
+def _dims(n_seq, n_kv_heads, head_dim, dtype, n_sink, n_recent, seq_lens, fold_capacity=0, fm_dim=0,
+          rows_external=0):
     lens = capi.int_array(seq_lens)
-    d = capi.mog_dims(n_seq, n_kv_heads, head_dim, dtype, n_sink, n_recent, fold_capacity, fm_dim,
+    d = capi.mog_dims(n_seq, n_kv_heads, head_dim, dtype, n_sink, n_recent, fold_capacity, fm_dim, rows_external,
                       C.cast(lens, C.POINTER(capi.i32)))
     return d, lens
 
@@ -253,21 +272,30 @@ def workspace(nbytes, device="cuda"):
 
 
 def mog_build(kv: KVCache, n_sink, n_recent, kmeans_iters=10, seed=0, ws=None, stream=None,
-              fold_capacity=0, fm_w=None, fm_scale=0.0) -> Layout:
+              fold_capacity=0, fm_w=None, fm_scale=0.0, rows_host=False) -> Layout:
     """Prefill-side build; allocates the layout (and the workspace unless given).
     ``fold_capacity``: rows per unit kept for mog_append; ``fm_w``: a device
     float32 [m][head_dim] projection for feature-map summaries (m = 64, 128
-    or 256), ``fm_scale`` their logit scale (0: 1/sqrt(head_dim))."""
+    or 256), ``fm_scale`` their logit scale (0: 1/sqrt(head_dim));
+    ``rows_host``: keep the reordered K/V rows in pinned host memory (the
+    GPU reads the chosen ones over the host link)."""
     fm_dim = 0
     if fm_w is not None:
         _require_cuda(fm_w)
         if fm_w.dtype != torch.float32 or not fm_w.is_contiguous() or fm_w.dim() != 2:
             raise ValueError("fm_w must be a contiguous float32 [m][head_dim] tensor")
         fm_dim = fm_w.shape[0]
-    bp = capi.mog_build_params(kmeans_iters, n_sink, n_recent, fold_capacity, seed, fm_dim, float(fm_scale),
-                               _vp(fm_w))
     d, _keep = _dims(kv.c.n_seq, kv.c.n_kv_heads, kv.c.head_dim, kv.c.dtype, n_sink, n_recent,
-                     kv.seq_lens, fold_capacity, fm_dim)
+                     kv.seq_lens, fold_capacity, fm_dim, 1 if rows_host else 0)
+    rows = None
+    if rows_host:
+        n = C.c_int64()
+        check(lib().mog_layout_rows(C.byref(d), C.byref(n)), "mog_layout_rows")
+        nbytes_rows = n.value * kv.head_dim * kv.k.element_size()
+        rows = tuple(torch.empty(max(nbytes_rows, 16), dtype=torch.uint8, pin_memory=True) for _ in range(2))
+    bp = capi.mog_build_params(kmeans_iters, n_sink, n_recent, fold_capacity, seed, fm_dim, float(fm_scale),
+                               _vp(fm_w), rows[0].data_ptr() if rows else None,
+                               rows[1].data_ptr() if rows else None)
     nbytes = C.c_size_t()
     check(lib().mog_layout_size(C.byref(d), C.byref(nbytes)), "mog_layout_size")
     mem = torch.empty(nbytes.value, dtype=torch.uint8, device=kv.k.device)
@@ -277,7 +305,7 @@ def mog_build(kv: KVCache, n_sink, n_recent, kmeans_iters=10, seed=0, ws=None, s
     L = capi.mog_layout()
     check(lib().mog_build(C.byref(kv.c), C.byref(bp), _vp(mem), nbytes.value, _vp(ws), ws.numel(),
                           C.byref(L), _stream(stream)), "mog_build")
-    lay = Layout(L, mem)
+    lay = Layout(L, mem, rows)
     lay._build_ws = ws
     return lay
 

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     out = subprocess.run(["nm", "-D", "--defined-only", capi.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (mog_\w+)", out))
     assert set(names) == exported, (set(names) ^ exported)
@@ -67,7 +67,7 @@ def test_struct_layout_matches_c(tmp_path):
 
 def _dims(lens, n_sink=64, n_recent=256, hkv=8, d=128, dtype=capi.MOG_BF16, fold_capacity=0, fm_dim=0):
     arr = capi.int_array(lens)
-    return capi.mog_dims(len(lens), hkv, d, dtype, n_sink, n_recent, fold_capacity, fm_dim,
+    return capi.mog_dims(len(lens), hkv, d, dtype, n_sink, n_recent, fold_capacity, fm_dim, 0,
                          C.cast(arr, C.POINTER(capi.i32))), arr
 
 
@@ -93,6 +93,15 @@ def test_layout_size_matches_geometry(L):
     assert L.mog_layout_size(C.byref(d3), C.byref(out3)) == capi.MOG_OK
     grow = 128 * D * 4 + 8 * (Cc + Cc * S) * 128 * 4
     assert grow <= out3.value - out.value <= grow + 4 * 256
+    # external rows: none in the buffer; mog_layout_rows counts them
+    d4, keep4 = _dims([1048576], fold_capacity=cap)
+    d4.rows_external = 1
+    out4 = C.c_size_t()
+    assert L.mog_layout_size(C.byref(d4), C.byref(out4)) == capi.MOG_OK
+    assert out2.value - out4.value >= 2 * (8 * (n_mid + cap)) * D * 2
+    rows = C.c_int64()
+    assert L.mog_layout_rows(C.byref(d4), C.byref(rows)) == capi.MOG_OK
+    assert rows.value == 8 * (n_mid + cap)
 
 
 def test_layout_unit_geometry(L):
@@ -231,6 +240,14 @@ def test_build_validation(L):
     assert L.mog_workspace_size(capi.MOG_OP_BUILD, C.byref(kv), None, C.byref(bp), None, C.byref(out)) == capi.MOG_ERR_INVALID_ARG
     bp.fm_scale, bp.fm_dim = 0.0, 96
     assert L.mog_workspace_size(capi.MOG_OP_BUILD, C.byref(kv), None, C.byref(bp), None, C.byref(out)) == capi.MOG_ERR_UNSUPPORTED
+    bp.fm_dim = 0
+    # external rows: both arrays or neither, 16-byte aligned
+    bp.rows_k = 0x50000
+    assert L.mog_workspace_size(capi.MOG_OP_BUILD, C.byref(kv), None, C.byref(bp), None, C.byref(out)) == capi.MOG_ERR_INVALID_ARG
+    bp.rows_v = 0x60008
+    assert L.mog_workspace_size(capi.MOG_OP_BUILD, C.byref(kv), None, C.byref(bp), None, C.byref(out)) == capi.MOG_ERR_INVALID_ARG
+    bp.rows_v = 0x60000
+    assert L.mog_workspace_size(capi.MOG_OP_BUILD, C.byref(kv), None, C.byref(bp), None, C.byref(out)) == capi.MOG_OK
 
 
 def test_feature_residual_validation(L):
