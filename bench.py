@@ -375,6 +375,71 @@ def feature_residual_comparison(steps, warmup, n_qsets, m=128):
     return res
 
 
+def offload_bench(state, steps, ev, n_dense=4):
+    """The same workload with the layout's reordered K/V rows in pinned host
+    memory (anchors and statistics stay in HBM): MoG decode steps/s, the
+    exact kernel's time and achieved host-link rate on the rows it reads
+    (the same selections as the HBM-resident run, so the same algorithmic
+    bytes), and the dense baseline reading a pinned host copy of the whole
+    cache."""
+    import torch
+
+    from long_context_sparse_mog_amd import capi, ops
+
+    wl, b, qs = state["wl"], state["b"], state["qs"]
+    nq = len(qs)
+    kv = ops.KVCache.from_batch(b)
+    t0 = time.time()
+    lay = ops.mog_build(kv, wl.n_sink, wl.n_recent, kmeans_iters=wl.kmeans_iters, seed=1, rows_host=True)
+    torch.cuda.synchronize()
+    build_s = time.time() - t0
+    p0 = ops.decode_params(wl.n_q_heads, list(wl.top_c), list(wl.top_s))
+    ws = ops.workspace(ops.mog_workspace_size(capi.MOG_OP_DECODE, layout=lay, params=p0))
+    out = torch.empty_like(qs[0])
+    lse = torch.empty(qs[0].shape[:2], device="cuda")
+    for i in range(2):
+        ops.mog_decode(lay, kv, qs[i % nq], p0, out=out, lse=lse, ws=ws)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        ops.mog_decode(lay, kv, qs[i % nq], p0, out=out, lse=lse, ws=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    kern = []
+    for i in range(min(steps, 8)):
+        p = ops.decode_params(wl.n_q_heads, list(wl.top_c), list(wl.top_s))
+        a, z = ev.create(), ev.create()
+        p.exact_begin, p.exact_end = a, z
+        ops.mog_decode(lay, kv, qs[i % nq], p, out=out, lse=lse, ws=ws)
+        torch.cuda.synchronize()
+        kern.append(ev.elapsed_ms(a, z))
+    exact_ms = sum(kern) / len(kern)
+    del lay, ws
+    torch.cuda.empty_cache()
+    # dense over a pinned host copy of the cache
+    kh = torch.empty(b.K.shape, dtype=b.K.dtype, pin_memory=True)
+    vh = torch.empty(b.V.shape, dtype=b.V.dtype, pin_memory=True)
+    kh.copy_(b.K)
+    vh.copy_(b.V)
+    kvh = ops.KVCache(kh, vh, wl.seq_lens)
+    pd = ops.decode_params(wl.n_q_heads, 1, 1)
+    ops.mog_dense_decode(kvh, qs[0], pd, out=out, lse=lse)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(n_dense):
+        ops.mog_dense_decode(kvh, qs[i % nq], pd, out=out, lse=lse)
+    e1.record()
+    torch.cuda.synchronize()
+    dense_ms = e0.elapsed_time(e1) / n_dense
+    del kh, vh, kvh
+    return dict(rows_in="pinned host memory", steps_per_s=1000.0 / ms, ms_per_step=ms, exact_kernel_ms=exact_ms,
+                build_s=build_s, dense_from_host_ms_per_step=dense_ms, dense_from_host_GBps=wl.kv_bytes() / (dense_ms * 1e-3) / 1e9,
+                speedup_vs_dense_from_host=dense_ms / ms)
+
+
 def build_timing(reps=3):
     """mog_build (10 k-means rounds, subclusters, reorder, stats) of the
     single-head 128K-key workload: median wall time over reps."""
@@ -521,6 +586,8 @@ def main():
                     help="skip the 1M step with one selection per KV head")
     ap.add_argument("--no-incremental", action="store_true",
                     help="skip the 1M incremental-decode steps (append one token + decode)")
+    ap.add_argument("--no-offload", action="store_true",
+                    help="skip the 1M step with the layout rows in pinned host memory")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 10 times (the reference kernel that "
@@ -545,6 +612,11 @@ def main():
     r1m, st1m = bench_workload(3, args.steps, args.warmup, args.qsets, ev, shared_too=not args.no_shared)
     if not args.no_incremental:
         r1m["incremental"] = incremental_bench(st1m, args.steps, args.warmup)
+    if not args.no_offload:
+        off = offload_bench(st1m, 20, ev)
+        # the exact kernel reads the same rows as in HBM: its algorithmic bytes
+        off["exact_kernel_GBps_host_link"] = r1m["exact_kernel_bytes"] / (off["exact_kernel_ms"] * 1e-3) / 1e9
+        r1m["offload"] = off
     r128 = None
     if not args.no_128k:
         r128, _ = bench_workload(2, args.steps, args.warmup, args.qsets, ev)
