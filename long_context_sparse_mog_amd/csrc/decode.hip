@@ -242,7 +242,7 @@ __global__ __launch_bounds__(256) void k_score_clusters(DArgs a) {
   const int g = g0 + lane;
   if (lane < kScoreRowsPerWave && g < U.C) {
     const int64_t cw = (int64_t)u * a.cstride + g;
-    const int n = off[(g + 1) * U.S] - off[g * U.S] + a.L.cl_fold[U.cl_base + g];
+    const int n = off[(g + 1) * U.S] - off[g * U.S] + (a.L.fold_cap ? a.L.cl_fold[U.cl_base + g] : 0);
     const float lg = n > 0 ? log2f((float)n) : -INFINITY;
 #pragma unroll
     for (int h = 0; h < G; ++h) a.ws.cl_score[cw * G + h] = n > 0 ? mine[h] + lg : -INFINITY;
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
   for (int t = 0; t < NSW; ++t) {
     const int i = min(64 * (h + G * t) + lane, C - 1);
     bound[t] = off[(i + 1) * U.S] - off[i * U.S];
-    bfold[t] = a.L.cl_fold[U.cl_base + i];
+    bfold[t] = a.L.fold_cap ? a.L.cl_fold[U.cl_base + i] : 0;
   }
   if (a.shared) {
     // one selection per KV head: the key of a cluster is the sum over the
@@ -636,7 +636,7 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
       {
         const int i = min(tid, S - 1);
         const int o0 = off[g * S + i], o1 = off[g * S + i + 1];
-        const int fc = a.L.sub_fold[sg0 + i];
+        const int fc = a.L.fold_cap ? a.L.sub_fold[sg0 + i] : 0;
         if (tid < S) {
           lds_cnt[tid] = o1 - o0;
           lds_fcnt[tid] = fc;
@@ -648,7 +648,7 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
 #pragma unroll
       for (int k = 0; k < RPW; ++k) {
         const int i = min(wave + 4 * k, S - 1);
-        rcnt[k] = off[g * S + i + 1] - off[g * S + i] + a.L.sub_fold[sg0 + i];
+        rcnt[k] = off[g * S + i + 1] - off[g * S + i] + (a.L.fold_cap ? a.L.sub_fold[sg0 + i] : 0);
       }
       if (tid < kMaxS) lds_sm[tid] = 0u;
       // full scores (count term added; -inf for an empty subcluster and for
@@ -806,17 +806,17 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
           if (i < S && lds_cnt[i] + lds_fcnt[i] > 0) need[k] = mask & ~lds_sm[i];
         }
         if (fmr) {
-          // the feature-map estimate of each left-out subcluster's mass
-          float z[RPW][4];
-#pragma unroll
-          for (int k = 0; k < RPW; ++k) load_fz(a.L.sub_fz + (sg0 + min(wave + 4 * k, S - 1)) * FM, FM, z[k]);
+          // the feature-map estimate of each left-out subcluster's mass (one
+          // row at a time: this mode keeps the Gaussian path's registers)
 #pragma unroll
           for (int k = 0; k < RPW; ++k) {
             if (!need[k]) continue;
+            float z[4];
+            load_fz(a.L.sub_fz + (sg0 + wave + 4 * k) * FM, FM, z);
 #pragma unroll
             for (int h = 0; h < G; ++h) {
               if (!((need[k] >> h) & 1u)) continue;
-              const float w = fm_weight(z[k], lds_fe[h], lds_fbase[h], FM);
+              const float w = fm_weight(z, lds_fe[h], lds_fbase[h], FM);
               if (w != -INFINITY) add_group<VPL>(rm[h], rl[h], ro[h], w, vb[k]);
             }
           }
@@ -839,29 +839,35 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
     constexpr int RCW = kRestClustersPerBlock / 4;
     const int y = x - nb_chosen;
     if (fmr && a.residual) {
-      // the feature-map estimate of each left-out cluster's mass
-      uint32_t mask[RCW];
-      int n_g[RCW];
-      float vb[RCW][VPL], z[RCW][4];
-#pragma unroll
-      for (int k = 0; k < RCW; ++k) {
-        const int g = min(y * kRestClustersPerBlock + wave * RCW + k, C - 1);
-        mask[k] = a.ws.cl_mask[cw + g];
-        n_g[k] = off[(g + 1) * S] - off[g * S] + a.L.cl_fold[U.cl_base + g];
-        load_floats<VPL>(a.L.cl_vbar + (U.cl_base + g) * D + lane * VPL, vb[k]);
-        load_fz(a.L.cl_fz + (U.cl_base + g) * FM, FM, z[k]);
-      }
+      // the feature-map estimate of each left-out cluster's mass, RCW / 2
+      // clusters' loads at a time (this mode keeps the Gaussian path's
+      // registers)
+      constexpr int HALF = RCW / 2;
       __syncthreads();  // the feature table
+#pragma unroll 1
+      for (int k0 = 0; k0 < RCW; k0 += HALF) {
+        uint32_t mask[HALF];
+        int n_g[HALF];
+        float vb[HALF][VPL], z[HALF][4];
 #pragma unroll
-      for (int k = 0; k < RCW; ++k) {
-        const int g = y * kRestClustersPerBlock + wave * RCW + k;
-        if (g >= C) break;
-        const uint32_t unchosen = n_g[k] > 0 ? (all & ~mask[k]) : 0u;
+        for (int k = 0; k < HALF; ++k) {
+          const int g = min(y * kRestClustersPerBlock + wave * RCW + k0 + k, C - 1);
+          mask[k] = a.ws.cl_mask[cw + g];
+          n_g[k] = off[(g + 1) * S] - off[g * S] + (a.L.fold_cap ? a.L.cl_fold[U.cl_base + g] : 0);
+          load_floats<VPL>(a.L.cl_vbar + (U.cl_base + g) * D + lane * VPL, vb[k]);
+          load_fz(a.L.cl_fz + (U.cl_base + g) * FM, FM, z[k]);
+        }
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          if (!((unchosen >> h) & 1u)) continue;
-          const float w = fm_weight(z[k], lds_fe[h], lds_fbase[h], FM);
-          if (w != -INFINITY) add_group<VPL>(rm[h], rl[h], ro[h], w, vb[k]);
+        for (int k = 0; k < HALF; ++k) {
+          const int g = y * kRestClustersPerBlock + wave * RCW + k0 + k;
+          if (g >= C) break;
+          const uint32_t unchosen = n_g[k] > 0 ? (all & ~mask[k]) : 0u;
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            if (!((unchosen >> h) & 1u)) continue;
+            const float w = fm_weight(z[k], lds_fe[h], lds_fbase[h], FM);
+            if (w != -INFINITY) add_group<VPL>(rm[h], rl[h], ro[h], w, vb[k]);
+          }
         }
       }
     } else {
@@ -873,7 +879,7 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
       const int g = min(y * kRestClustersPerBlock + wave * RCW + k, C - 1);
       const int64_t cg = cw + g;
       mask[k] = a.ws.cl_mask[cg];
-      n_g[k] = off[(g + 1) * S] - off[g * S] + a.L.cl_fold[U.cl_base + g];
+      n_g[k] = off[(g + 1) * S] - off[g * S] + (a.L.fold_cap ? a.L.cl_fold[U.cl_base + g] : 0);
       load_floats<VPL>(a.L.cl_vbar + (U.cl_base + g) * D + lane * VPL, vb[k]);
 #pragma unroll
       for (int h = 0; h < G; ++h) sc[k][h] = a.ws.cl_score[cg * G + h];
