@@ -181,3 +181,12 @@ def test_append_full_then_rebuild_then_append():
     # re-build on the grown cache, then continue with the next 40 tokens
     wb = replace(wl, seq_lens=[4264])
     run_append_case(wb, [40], cap=64, grown_wl=wg)
+
+
+def test_append_tiny_units():
+    """Units with two middle tokens at the build (C = 2 clusters), each grown
+    by 12 tokens one call at a time into a fold area of 12 rows; and a fold
+    area of a single row."""
+    wl = synth.config(0, seq_lens=[70, 71], n_sink=4, n_recent=64, top_c=[1, 2], top_s=[1, 3])
+    run_append_case(wl, [12, 12], chunks=[[1, 1]] * 12)
+    run_append_case(synth.config(0, seq_lens=[300]), [1], cap=1)

@@ -98,3 +98,55 @@ def test_fullsize_gqa_1m_incremental_sampled():
     wb = replace(wl, seq_lens=[wl.seq_lens[0] - grow])
     run_append_case(wb, [grow], chunks=[[1], [1], [grow - 2]], units=[0, 5], grown_wl=wl)
     torch.cuda.empty_cache()
+
+
+def test_fullsize_gqa_1m_feature_residual_sampled():
+    """The 1M workload built with feature-map summaries (m = 128): summaries
+    of two units against the oracle's sums over the same members, and one
+    decode step with the feature-map residual on them."""
+    from test_gpu_fm import check_summaries
+    wl = synth.config(3)
+    say(f"[full fm] {wl.name}")
+    b = synth.generate(wl, device="cuda")
+    kv = ops.KVCache.from_batch(b)
+    W = synth.feature_map_w(128, wl.head_dim, device="cuda")
+    lay = ops.mog_build(kv, wl.n_sink, wl.n_recent, kmeans_iters=wl.kmeans_iters, seed=1, fm_w=W)
+    params = ops.decode_params(wl.n_q_heads, list(wl.top_c), list(wl.top_s), residual="fm")
+    q = b.Q[0].contiguous()
+    out, lse, sel_c, sel_s = ops.mog_decode(lay, kv, q, params, want_sel=True)
+    torch.cuda.synchronize()
+    out, lse, sel_c, sel_s = out.cpu().numpy(), lse.cpu().numpy(), sel_c.cpu().numpy(), sel_s.cpu().numpy()
+    G = wl.group
+    for u in (1, 6):
+        ex = lay.export_unit(u)
+        K, V = b.unit_kv(0, u)
+        check_summaries(ex, K, wl, W.cpu().numpy())
+        L = oracle_layout_from_export(ex, wl.n_sink, wl.n_recent)
+        Q = q[0, u * G:(u + 1) * G].cpu().numpy().astype(np.float64)
+        hs = slice(u * G, (u + 1) * G)
+        r = compare_unit(L, K, V, Q, wl.top_c[0], wl.top_s[0], out[0, hs], lse[0, hs], sel_c[0, hs], sel_s[0, hs],
+                         2e-3, residual="fm")
+        say(f"  unit {u}: worst rel L2 {r['max_rel']:.2e}, near ties {r['ties']}")
+        del K, V
+    del b, kv, lay
+    torch.cuda.empty_cache()
+
+
+def test_fullsize_gqa_1m_offloaded_rows():
+    """The 1M workload with the layout's rows in pinned host memory: the
+    decode step is bit-identical to the HBM-resident one (same kernels, rows
+    read over the host link)."""
+    wl = synth.config(3)
+    say(f"[full offload] {wl.name}")
+    b = synth.generate(wl, device="cuda")
+    kv = ops.KVCache.from_batch(b)
+    dev = ops.mog_build(kv, wl.n_sink, wl.n_recent, kmeans_iters=wl.kmeans_iters, seed=1)
+    host = ops.mog_build(kv, wl.n_sink, wl.n_recent, kmeans_iters=wl.kmeans_iters, seed=1, rows_host=True)
+    params = ops.decode_params(wl.n_q_heads, list(wl.top_c), list(wl.top_s))
+    q = b.Q[0].contiguous()
+    a = ops.mog_decode(dev, kv, q, params, want_sel=True)
+    h = ops.mog_decode(host, kv, q, params, want_sel=True)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(a, h))
+    del b, kv, dev, host
+    torch.cuda.empty_cache()
