@@ -260,6 +260,184 @@ __global__ __launch_bounds__(256) void k_assign(BArgs a, int accumulate) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 2'. The same assignment for bf16 keys on the matrix cores: the x.mu of 64
+//     keys per wave against 64 centroids per stage are 16x16 tiles of
+//     v_mfma_f32_16x16x32_bf16.  Keys are the A operand straight from their
+//     rows (lane (g, n): key n of the tile, dimensions 32 s + 8 g .. + 7);
+//     each centroid is split into bf16 high and low parts (hi + lo carries
+//     about 16 mantissa bits) staged in LDS in B-operand order, and both
+//     parts accumulate into one float32 tile, so a distance
+//     ||mu||^2 - 2 x.mu differs from the float32 one by about 2^-16 of
+//     |x||mu|.  Lane (g, n) of a result tile holds keys 4g .. 4g+3 against
+//     centroid n; a running argmin per lane (centroids visited in increasing
+//     id) and a 16-lane reduction (ties to the lower id) finish the key.
+//     Stages are double-buffered.  256 keys per block.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ inline uint32_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_assign_mfma(BArgs a, int accumulate) {
+  constexpr int KS = D / 32;    // k-steps of 32 dimensions
+  constexpr int RT = 4;         // 16-key row tiles per wave
+  constexpr int KPB = 4 * 16 * RT;
+  constexpr int CT = 4;         // 16-centroid column tiles per stage
+  __shared__ uint4 cf[2][2][KS][CT][64];  // [buffer][hi, lo][k-step][column tile][lane]
+  __shared__ float cn[2][16 * CT];
+  __shared__ int lab[KPB];
+  const int u = blockIdx.y;
+  const mog_unit U = a.units[u];
+  const int k0 = blockIdx.x * KPB;
+  if (k0 >= U.n_mid) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, n = lane & 15;
+  const int C = U.C;
+  const uint16_t* kb = static_cast<const uint16_t*>(a.kv.k);
+  // A fragments of the wave's 64 keys (zero past the middle region)
+  uint4 af[RT][KS];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int key = k0 + wave * 16 * RT + rt * 16 + n;
+    if (key < U.n_mid) {
+      const int64_t off = kv_row_offset(a.kv, U.seq, U.kv_head, a.n_sink + key, D) + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) af[rt][ks] = *reinterpret_cast<const uint4*>(kb + off + 32 * ks);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) af[rt][ks] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  // stage centroids [c0, c0 + 64) into buffer b: thread (c, q) converts
+  // dimensions [q D/4, (q+1) D/4) of centroid c
+  auto stage = [&](int b, int c0) {
+    const int c = tid >> 2, q = tid & 3;
+    const int cid = c0 + c;
+#pragma unroll
+    for (int d0 = q * (D / 4); d0 < (q + 1) * (D / 4); d0 += 8) {
+      float x[8];
+      if (cid < C) {
+        const float4* p = reinterpret_cast<const float4*>(a.cent + (U.cl_base + cid) * D + d0);
+        const float4 v0 = p[0], v1 = p[1];
+        x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
+        x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = 0.f;
+      }
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t h0 = bf16_rne(x[2 * e]), h1 = bf16_rne(x[2 * e + 1]);
+        const uint32_t l0 = bf16_rne(x[2 * e] - __uint_as_float(h0 << 16));
+        const uint32_t l1 = bf16_rne(x[2 * e + 1] - __uint_as_float(h1 << 16));
+        hi[e] = h0 | (h1 << 16);
+        lo[e] = l0 | (l1 << 16);
+      }
+      const int ks = d0 / 32, gg = (d0 % 32) / 8;
+      const int ct = c / 16, ln = (c % 16) + 16 * gg;
+      cf[b][0][ks][ct][ln] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      cf[b][1][ks][ct][ln] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    }
+    if (tid < 16 * CT) cn[b][tid] = c0 + tid < C ? a.cent_norm[U.cl_base + c0 + tid] : INFINITY;
+  };
+  float best[RT][4];
+  int bid[RT][4];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      best[rt][i] = INFINITY;
+      bid[rt][i] = 0x7fffffff;
+    }
+  const int nst = (C + 16 * CT - 1) / (16 * CT);
+  stage(0, 0);
+  __syncthreads();
+  for (int t = 0; t < nst; ++t) {
+    const int b = t & 1;
+    if (t + 1 < nst) stage(b ^ 1, (t + 1) * 16 * CT);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      f32x4_t acc[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, cf[b][0][ks][ct][lane]);
+        const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, cf[b][1][ks][ct][lane]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, af[rt][ks]);
+          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, acc[rt], 0, 0, 0);
+          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, acc[rt], 0, 0, 0);
+        }
+      }
+      const int cid = t * 16 * CT + ct * 16 + n;
+      const float nrm = cn[b][ct * 16 + n];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float dist = nrm - 2.f * acc[rt][i];
+          if (dist < best[rt][i]) {  // a lane's centroids come in increasing id
+            best[rt][i] = dist;
+            bid[rt][i] = cid;
+          }
+        }
+    }
+    __syncthreads();
+  }
+  // the 16 lanes of a row group hold the same keys against different
+  // centroids: reduce (ties to the lower id)
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) {
+        const float od = __shfl_xor(best[rt][i], o, 64);
+        const int oi = __shfl_xor(bid[rt][i], o, 64);
+        if (od < best[rt][i] || (od == best[rt][i] && oi < bid[rt][i])) {
+          best[rt][i] = od;
+          bid[rt][i] = oi;
+        }
+      }
+    }
+  const int nk = min(KPB, U.n_mid - k0);
+  if (n == 0) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kk = wave * 16 * RT + rt * 16 + 4 * g + i;
+        int id = bid[rt][i];
+        if (id < 0 || id >= C) id = 0;  // only reachable for non-finite keys
+        lab[kk] = id;
+        if (kk < nk) {
+          a.labels[U.row_base + k0 + kk] = id;
+          atomicAdd(&a.counts[U.cl_base + id], 1);
+        }
+      }
+  }
+  if (!accumulate) return;
+  __syncthreads();
+  // fixed-point sums of every key into its cluster: a wave per key, lanes
+  // over the dimensions
+  for (int kk = wave; kk < nk; kk += 4) {
+    const int64_t off = kv_row_offset(a.kv, U.seq, U.kv_head, a.n_sink + k0 + kk, D);
+    const int64_t dst = (U.cl_base + lab[kk]) * D;
+    for (int d = lane; d < D; d += 64) {
+      const long long fx = __float2ll_rn(elem<uint16_t>(kb, off + d) * kFixScale);
+      atomicAdd(&a.sums[dst + d], (unsigned long long)fx);
+    }
+  }
+}
+
 // 2b. New centroid = fixed-point sum / count (empty keeps); zero the sums.
 template <int D>
 __global__ __launch_bounds__(256) void k_update(BArgs a) {
@@ -376,7 +554,7 @@ template <int D, typename T>
 __global__ __launch_bounds__(256) void k_subkmeans(BArgs a, int iters) {
   __shared__ float cen[kMaxS][D];
   __shared__ float cnorm[kMaxS];
-  __shared__ float acc[2][kMaxS][D];
+  __shared__ unsigned long long accq[kMaxS][D];  // fixed-point sums of the members
   __shared__ int scount[kMaxS];
   __shared__ int sstart[kMaxS + 1];
   __shared__ int ids[kMaxS];
@@ -443,23 +621,31 @@ __global__ __launch_bounds__(256) void k_subkmeans(BArgs a, int iters) {
       cnorm[tid] = s;
     }
     if (tid < kMaxS) scount[tid] = 0;
+    if (round < iters)
+      for (int idx = tid; idx < k * D; idx += 256) accq[idx / D][idx % D] = 0ull;
     __syncthreads();
-    // assignment: one member per thread
+    // assignment: one member per thread, which then adds the member into its
+    // subcluster's fixed-point sums (integer adds: the order does not
+    // matter)
     for (int m = tid; m < n; m += 256) {
       const int64_t ro = kv_row_offset(a.kv, U.seq, U.kv_head, a.n_sink + mem[m], D);
+      // the whole row in registers (one batch of 16-byte loads)
+      float x[D];
+#pragma unroll
+      for (int d0 = 0; d0 < D; d0 += 8) {
+        float t8[8];
+        load8<T>(kb, ro + d0, t8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[d0 + e] = t8[e];
+      }
       float dot[kMaxS];
 #pragma unroll
       for (int c = 0; c < kMaxS; ++c) dot[c] = 0.f;
-      for (int d0 = 0; d0 < D; d0 += 8) {
-        float x[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = elem<T>(kb, ro + d0 + e);
+      for (int c = 0; c < kMaxS; ++c) {
+        if (c < k) {
 #pragma unroll
-        for (int c = 0; c < kMaxS; ++c) {
-          if (c < k) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) dot[c] += x[e] * cen[c][d0 + e];
-          }
+          for (int d = 0; d < D; ++d) dot[c] += x[d] * cen[c][d];
         }
       }
       float best = INFINITY;
@@ -476,22 +662,19 @@ __global__ __launch_bounds__(256) void k_subkmeans(BArgs a, int iters) {
       }
       sl[m] = bid;
       atomicAdd(&scount[bid], 1);
-    }
-    __syncthreads();
-    if (round == iters) break;
-    // update: thread (d, phase) sums its dimension over its half of the members
-    const int d = tid % D, ph = tid / D;          // D=128: 2 phases, D=64: 4 phases (use first 2)
-    if (ph < 2) {
-      for (int c = 0; c < k; ++c) acc[ph][c][d] = 0.f;
-      for (int m = ph; m < n; m += 2) {
-        const int c = sl[m];
-        acc[ph][c][d] += elem<T>(kb, kv_row_offset(a.kv, U.seq, U.kv_head, a.n_sink + mem[m], D) + d);
+      if (round < iters) {
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+          atomicAdd(&accq[bid][d], (unsigned long long)__float2ll_rn(x[d] * kFixScale));
       }
     }
     __syncthreads();
+    if (round == iters) break;
+    // update: new centroid = sum / count (an empty subcluster keeps its own)
     for (int idx = tid; idx < k * D; idx += 256) {
       const int c = idx / D, dd = idx % D;
-      if (scount[c] > 0) cen[c][dd] = (acc[0][c][dd] + acc[1][c][dd]) / (float)scount[c];
+      if (scount[c] > 0)
+        cen[c][dd] = (float)((double)(long long)accq[c][dd] / ((double)scount[c] * (double)kFixScale));
     }
     __syncthreads();
   }
@@ -723,11 +906,18 @@ static hipError_t build_impl(const BuildLaunch& x, hipStream_t s) {
   const int maxC = x.L.max_C;
   hipLaunchKernelGGL(k_forgy, dim3(nu), dim3(256), 0, s, a);
   hipLaunchKernelGGL((k_init_centroids<D, T>), dim3((maxC + 3) / 4, nu), dim3(256), 0, s, a);
+  // bf16 keys: the matrix-core assignment; float32 keys: the float32 one
+  auto assign = [&](int accumulate) {
+    if constexpr (sizeof(T) == 2)
+      hipLaunchKernelGGL((k_assign_mfma<D>), dim3((max_mid + 255) / 256, nu), dim3(256), 0, s, a, accumulate);
+    else
+      hipLaunchKernelGGL((k_assign<D, T>), dim3((max_mid + 63) / 64, nu), dim3(256), 0, s, a, accumulate);
+  };
   for (int it = 0; it < x.iters; ++it) {
-    hipLaunchKernelGGL((k_assign<D, T>), dim3((max_mid + 63) / 64, nu), dim3(256), 0, s, a, 1);
+    assign(1);
     hipLaunchKernelGGL((k_update<D>), dim3((maxC + 3) / 4, nu), dim3(256), 0, s, a);
   }
-  hipLaunchKernelGGL((k_assign<D, T>), dim3((max_mid + 63) / 64, nu), dim3(256), 0, s, a, 0);
+  assign(0);
   hipLaunchKernelGGL(k_cluster_starts, dim3(nu), dim3(1024), 0, s, a);
   hipLaunchKernelGGL(k_group_members, dim3((maxC + 7) / 8, nu), dim3(1024), 0, s, a);
   hipLaunchKernelGGL((k_subkmeans<D, T>), dim3(maxC, nu), dim3(256), 0, s, a, x.iters);
