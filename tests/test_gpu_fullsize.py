@@ -150,3 +150,16 @@ def test_fullsize_gqa_1m_offloaded_rows():
     assert all(torch.equal(x, y) for x, y in zip(a, h))
     del b, kv, dev, host
     torch.cuda.empty_cache()
+
+
+def test_maximum_length_incremental():
+    """N = 2^22 - 64 built, then 64 tokens appended in two calls: C = 2048
+    clusters, so the append's cluster scan is spread over its largest block
+    count (16 per unit); fold state and a decode step against the oracle."""
+    from test_gpu_append import run_append_case
+    L = 1 << 22
+    wl = synth.config(3, n_q_heads=4, n_kv_heads=1, seq_lens=[L], n_components=2048,
+                      name="gqa-4q1kv-d128-4M-bf16", budget_kappa=34 / 203)
+    wb = replace(wl, seq_lens=[L - 64])
+    run_append_case(wb, [64], chunks=[[1], [63]], grown_wl=wl)
+    torch.cuda.empty_cache()
