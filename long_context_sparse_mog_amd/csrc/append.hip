@@ -42,7 +42,6 @@ struct AArgs {
   int32_t fm_dim;
   float fm_sqrt_scale;
   AppendSlot* slots;   // [n_units][kAppendMaxBlocks] per-block winners
-  int32_t* counters;   // [n_units] blocks done with the current token
   int32_t fold_cap, n_recent;
   AppendSeq seq[MOG_MAX_SEQ];
 };
@@ -168,13 +167,13 @@ __host__ __device__ inline int append_blocks(int C) {
 // row gets its float64 distance from the same registers, and the float64
 // minimum (ties to the lower id) over all groups decides.
 //
-// One launch per folded token (token index `it` of every sequence's new
-// tokens).  Grid (append_blocks(max C), units): block p of unit u scans
-// clusters [p C / P, (p + 1) C / P), writes its winner to the unit's slot p
-// and counts itself done; the block that finds every other block done (an
-// atomic counter, no waiting) takes the winners' minimum, picks the
-// subcluster, applies the running updates, writes the fold bookkeeping and
-// clears the counter for the next launch.
+// Two launches per folded token (token index `it` of every sequence's new
+// tokens).  k_append, grid (append_blocks(max C), units): block p of unit u
+// scans clusters [p C / P, (p + 1) C / P) and writes its winner to the
+// unit's slot p.  k_append_apply, one block per unit, then takes the
+// winners' minimum, picks the subcluster, applies the running updates and
+// writes the fold bookkeeping (the kernel boundary orders the slots before
+// it; no fences or counters).
 template <int D, typename T>
 __global__ __launch_bounds__(kAppendThreads) void k_append(AArgs a, int it) {
   constexpr int NW = kAppendThreads / 64;
@@ -186,8 +185,6 @@ __global__ __launch_bounds__(kAppendThreads) void k_append(AArgs a, int it) {
   constexpr float kSlack = 1e-30f;
   __shared__ double w_d2[NW];
   __shared__ int w_id[NW], w_n[NW], w_f[NW];
-  __shared__ int sel[4];  // last block: is it last, subcluster, its size, its fold count
-  __shared__ float xs[D];  // last block: sqrt(scale) k for the feature map
   const int u = blockIdx.y, p = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const mog_unit U = uni_unit(a.units + u);
   const AppendSeq sq = a.seq[U.seq];
@@ -262,17 +259,35 @@ __global__ __launch_bounds__(kAppendThreads) void k_append(AArgs a, int it) {
     int bj = lane < NW ? w_id[lane] : 0x7fffffff;
     int cn = lane < NW ? w_n[lane] : 0, cf = lane < NW ? w_f[lane] : 0;
     wave_argmin<1>(bd, bj, cn, cf);
-    if (lane == 0) {
-      slots[p] = AppendSlot{bd, bj, cn, cf, 0};
-      __threadfence();  // the slot is visible before the count
-      const int done = atomicAdd(a.counters + u, 1);
-      sel[0] = done == P - 1;
-    }
+    if (lane == 0) slots[p] = AppendSlot{bd, bj, cn, cf, 0};
   }
-  __syncthreads();
-  if (!sel[0]) return;
-  // ---- the last block of the unit: every slot is written ----
-  __threadfence();
+}
+
+template <int D, typename T>
+__global__ __launch_bounds__(256) void k_append_apply(AArgs a, int it) {
+  constexpr int LPC = D / 8;
+  constexpr int CPW = 64 / LPC;
+  __shared__ int sel[4];   // (unused), subcluster, its size, its fold count
+  __shared__ float xs[D];  // sqrt(scale) k for the feature map
+  const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const mog_unit U = uni_unit(a.units + u);
+  const AppendSeq sq = a.seq[U.seq];
+  const int C = U.C, S = U.S, P = append_blocks(C);
+  if (it >= sq.n_new) return;
+  const int32_t* off = a.sub_off + U.off_base;
+  const int part = lane % LPC, row_in = lane / LPC;
+  const T* kc = static_cast<const T*>(a.kv.k);
+  const T* vc = static_cast<const T*>(a.kv.v);
+  const int t = sq.len - a.n_recent + it;
+  const int f = sq.f0 + it;
+  const int64_t src = kv_row_offset(a.kv, U.seq, U.kv_head, t, D);
+  float kx[8];
+  load_key8<T>(kc + src + part * 8, kx);
+  double kd[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) kd[e] = (double)kx[e];
+  const bool have_kd = true;
+  const AppendSlot* slots = a.slots + (int64_t)u * kAppendMaxBlocks;
   double bd = INFINITY;
   int bj = 0x7fffffff, cn = 0, cf = 0;
   if (lane < P) {
@@ -374,7 +389,6 @@ __global__ __launch_bounds__(kAppendThreads) void k_append(AArgs a, int it) {
     a.fold_pos[(int64_t)u * a.fold_cap + f] = t;
     a.units[u].N = sq.len + it + 1;
     a.units[u].n_fold = f + 1;
-    a.counters[u] = 0;  // for the next launch
   }
 }
 
@@ -385,6 +399,7 @@ static hipError_t append_impl(const AppendLaunch& x, const AArgs& a, hipStream_t
   const dim3 grid(append_blocks(x.L.max_C), x.L.n_units);
   for (int it = 0; it < max_new; ++it) {
     hipLaunchKernelGGL((k_append<D, T>), grid, dim3(kAppendThreads), 0, s, a, it);
+    hipLaunchKernelGGL((k_append_apply<D, T>), dim3(x.L.n_units), dim3(256), 0, s, a, it);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -415,7 +430,6 @@ hipError_t launch_append(const AppendLaunch& x, hipStream_t s) {
   a.fm_dim = x.L.fm_dim;
   a.fm_sqrt_scale = sqrtf(x.L.fm_scale);
   a.slots = static_cast<AppendSlot*>(x.L.append_scratch);
-  a.counters = reinterpret_cast<int32_t*>(a.slots + (int64_t)x.L.n_units * kAppendMaxBlocks);
   for (int i = 0; i < MOG_MAX_SEQ; ++i) a.seq[i] = x.seq[i];
   const bool bf = x.L.dtype == MOG_BF16;
   if (x.L.head_dim == 128) return bf ? append_impl<128, uint16_t>(x, a, s) : append_impl<128, float>(x, a, s);

@@ -1301,61 +1301,8 @@ __global__ __launch_bounds__(256, 2) void k_dense(KVRef kv, const float* q, int 
 }
 
 // ---------------------------------------------------------------------------
-// Unit table of a layout (same arithmetic as the host carving).
-// ---------------------------------------------------------------------------
-__global__ void k_layout_table(mog_unit* units, SeqArgs seq, int Hkv, int n_sink, int n_recent,
-                               int32_t* cl_fold, int64_t n_cl, int32_t* sub_fold, int64_t n_sub,
-                               int32_t* app_counters) {
-  // no folded tokens yet: zero the per-group fold counts and the append
-  // counters
-  const int64_t step = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_cl + n_sub; i += step) {
-    if (i < n_cl) cl_fold[i] = 0;
-    else sub_fold[i - n_cl] = 0;
-  }
-  const int u = blockIdx.x * blockDim.x + threadIdx.x;
-  if (u >= seq.n_seq * Hkv) return;
-  const int s = u / Hkv, kvh = u % Hkv;
-  int64_t row = 0, cl = 0, sub = 0, offb = 0;
-  for (int s2 = 0; s2 < s; ++s2) {
-    const UnitSizes z = unit_sizes(seq.len[s2], n_sink, n_recent);
-    row += (int64_t)Hkv * z.n_mid;
-    cl += (int64_t)Hkv * z.C;
-    sub += (int64_t)Hkv * z.C * z.S;
-    offb += (int64_t)Hkv * (z.C * z.S + 1);
-  }
-  const UnitSizes z = unit_sizes(seq.len[s], n_sink, n_recent);
-  mog_unit U;
-  U.seq = s;
-  U.kv_head = kvh;
-  U.N = seq.len[s];
-  U.n_mid = z.n_mid;
-  U.C = z.C;
-  U.S = z.S;
-  U.n_fold = 0;
-  U.reserved1 = 0;
-  U.row_base = row + (int64_t)kvh * z.n_mid;
-  U.cl_base = cl + (int64_t)kvh * z.C;
-  U.sub_base = sub + (int64_t)kvh * z.C * z.S;
-  U.off_base = offb + (int64_t)kvh * (z.C * z.S + 1);
-  units[u] = U;
-  app_counters[u] = 0;
-}
-
-// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_layout_table(const mog_layout& L, const SeqArgs& seq, hipStream_t s) {
-  const int n = L.n_units;
-  const int64_t n_cnt = L.total_cl + L.total_sub;
-  const int64_t nb = max((int64_t)(n + 255) / 256, min((n_cnt + 255) / 256, (int64_t)1024));
-  hipLaunchKernelGGL(k_layout_table, dim3((unsigned)nb), dim3(256), 0, s, L.units, seq, L.n_kv_heads, L.n_sink,
-                     L.n_recent, L.cl_fold, L.total_cl, L.sub_fold, L.total_sub,
-                     reinterpret_cast<int32_t*>(static_cast<AppendSlot*>(L.append_scratch) +
-                                                (int64_t)L.n_units * kAppendMaxBlocks));
-  return hipGetLastError();
-}
-
 template <int D, int G>
 static hipError_t decode_impl(const DecodeLaunch& x, const DArgs& a, const BudgetArgs& b, hipStream_t s) {
   const int nu = x.L.n_units;

@@ -182,8 +182,8 @@ struct AppendSeq {
 
 // mog_append: a token's cluster scan is shared by up to kAppendMaxBlocks
 // blocks per unit (about kAppendRowsPerBlock clusters each); each leaves
-// its winner in a slot, and a per-unit counter finds the last block.  Slots
-// and counters live in the layout buffer (mog_layout.append_scratch).
+// its winner in a slot of the layout buffer (mog_layout.append_scratch),
+// which the next kernel reads.
 constexpr int kAppendThreads = 512;
 constexpr int kAppendRowsPerBlock = 128;
 constexpr int kAppendMaxBlocks = 16;
@@ -192,7 +192,7 @@ struct AppendSlot {
   int32_t id, n, nf, pad;
 };
 __host__ __device__ inline size_t append_scratch_bytes(int64_t n_units) {
-  return (size_t)n_units * (kAppendMaxBlocks * sizeof(AppendSlot) + sizeof(int32_t));
+  return (size_t)n_units * kAppendMaxBlocks * sizeof(AppendSlot);
 }
 
 struct AppendLaunch {
