@@ -91,6 +91,88 @@ __device__ inline float wave_sum_dpp(float x) {
 __device__ inline float swap8(float x) { return dpp<0x128>(x); }  // row_ror:8
 
 // ---------------------------------------------------------------------------
+// Reduce-scatter over the wave: every lane holds V partial values (V <= 64);
+// afterwards lane l holds the wave sum of value rs_index<V>(l).  Six lane
+// exchanges are taken in turn: row mirror (partner l ^ 15 in its row of 16),
+// half-row mirror (l ^ 7 in its 8), l ^ 2, l ^ 1 (DPP), l ^ 16 (swizzle) and
+// l ^ 32 (permute).  In each of the first H = ceil(log2 V) of them a lane keeps
+// the half of its values its lane bit selects (b3, b2, b1, b0, b4, b5 in that
+// order) and adds the partner's copy of that half, which the partner sends
+// because it keeps the other half; partners always agree on the bits of the
+// earlier exchanges, so they hold the same values.  The remaining exchanges
+// add the last value.  This takes about 3V lane operations where V separate
+// wave sums take about 7V.  When V < 64, 64 / 2^H lanes hold each sum.
+// ---------------------------------------------------------------------------
+template <int V>
+struct RsSteps {
+  static_assert(V >= 1 && V <= 64, "reduce-scatter of up to 64 values");
+  static constexpr int H = V <= 1 ? 0 : V <= 2 ? 1 : V <= 4 ? 2 : V <= 8 ? 3 : V <= 16 ? 4 : V <= 32 ? 5 : 6;
+  static constexpr int P = 1 << H;  // values after padding with zeros
+};
+
+// one exchange on the first N values of w: halve them when N > 1, else add
+template <int N, typename X>
+__device__ inline void rs_exchange(float* w, bool upper, X partner) {
+  if constexpr (N > 1) {
+#pragma unroll
+    for (int j = 0; j < N / 2; ++j) {
+      const float lo = w[j], hi = w[j + N / 2];
+      const float keep = upper ? hi : lo, send = upper ? lo : hi;
+      w[j] = keep + partner(send);
+    }
+  } else {
+    w[0] += partner(w[0]);
+  }
+}
+
+__device__ inline float lane_xor16(float x) {
+  // ds_swizzle bit mode: and 0x1f, or 0, xor 0x10 (lane ^ 16 in each 32)
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+}
+
+template <int V>
+__device__ inline float wave_reduce_scatter(const float (&v)[V]) {
+  constexpr int P = RsSteps<V>::P;
+  const int lane = threadIdx.x & 63;
+  float w[P];
+#pragma unroll
+  for (int j = 0; j < P; ++j) w[j] = j < V ? v[j] : 0.f;
+  constexpr int N0 = P, N1 = N0 > 1 ? N0 / 2 : 1, N2 = N1 > 1 ? N1 / 2 : 1, N3 = N2 > 1 ? N2 / 2 : 1,
+                N4 = N3 > 1 ? N3 / 2 : 1, N5 = N4 > 1 ? N4 / 2 : 1;
+  rs_exchange<N0>(w, (lane >> 3) & 1, [](float x) { return dpp<0x140>(x); });  // row mirror
+  rs_exchange<N1>(w, (lane >> 2) & 1, [](float x) { return dpp<0x141>(x); });  // half-row mirror
+  rs_exchange<N2>(w, (lane >> 1) & 1, [](float x) { return dpp<0x4E>(x); });   // l ^ 2
+  rs_exchange<N3>(w, lane & 1, [](float x) { return dpp<0xB1>(x); });          // l ^ 1
+  rs_exchange<N4>(w, (lane >> 4) & 1, [](float x) { return lane_xor16(x); });
+  rs_exchange<N5>(w, (lane >> 5) & 1, [](float x) { return __shfl_xor(x, 32, 64); });
+  return w[0];
+}
+
+// index of the value whose sum wave_reduce_scatter<V> leaves in lane l
+template <int V>
+__device__ inline int rs_index(int l) {
+  constexpr int H = RsSteps<V>::H;
+  const int bits[6] = {(l >> 3) & 1, (l >> 2) & 1, (l >> 1) & 1, l & 1, (l >> 4) & 1, (l >> 5) & 1};
+  int j = 0;
+#pragma unroll
+  for (int s = 0; s < H; ++s) j = 2 * j + bits[s];
+  return j;
+}
+
+// whether lane l reports its sum: lanes that differ only in the bits of the
+// plain-add exchanges hold the same index; the one with those bits clear
+// reports it (if the index is below V)
+template <int V>
+__device__ inline bool rs_owner(int l) {
+  constexpr int H = RsSteps<V>::H;
+  constexpr int order[6] = {3, 2, 1, 0, 4, 5};  // lane bit decided by each exchange
+  int undecided = 0;
+#pragma unroll
+  for (int s = H; s < 6; ++s) undecided |= 1 << order[s];
+  return (l & undecided) == 0 && rs_index<V>(l) < V;
+}
+
+// ---------------------------------------------------------------------------
 // MFMA tile engine (bf16)
 // ---------------------------------------------------------------------------
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -162,25 +162,6 @@ __device__ inline void score_coefs(const DArgs& a, const float* qb, float (&coef
   }
 }
 
-// Scores of R group rows (already loaded, x[r][EPL] per lane): lane r ends
-// up holding the G scores of row r (without the count term).
-template <int D, int G, int R>
-__device__ inline void score_rows(const float (&x)[R][D / 32], const float (&coef)[G][D / 32], int lane,
-                                  float (&mine)[G]) {
-  constexpr int EPL = D / 32;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float t = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) t += coef[h][e] * x[r][e];
-      t = wave_sum_uniform(t);
-      if (lane == r) mine[h] = t;
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // 1. Cluster scores: score[g][h] = log2 n_g + log2e (scale q_h.mu_g +
 //    scale^2/2 sum_i q_{h,i}^2 var_{g,i}); -inf for an empty cluster.
@@ -234,18 +215,26 @@ __global__ __launch_bounds__(256) void k_score_clusters(DArgs a) {
     const int g = min(g0 + k, U.C - 1);
     load_floats<EPL>(a.L.cl_ms + (U.cl_base + g) * (2 * D) + lane * EPL, x[k]);
   }
-  float mine[G];
+  // the R x G partial dot products, summed over the lanes by one
+  // reduce-scatter: one lane then holds each (cluster, head) score
+  constexpr int R = kScoreRowsPerWave;
+  float part[R * G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) mine[h] = 0.f;
-  score_rows<D, G, kScoreRowsPerWave>(x, coef, lane, mine);
-  // lane k (< kScoreRowsPerWave) now holds the scores of cluster g0 + k
-  const int g = g0 + lane;
-  if (lane < kScoreRowsPerWave && g < U.C) {
+  for (int k = 0; k < R; ++k) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float t = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) t += coef[h][e] * x[k][e];
+      part[k * G + h] = t;
+    }
+  }
+  const float t = wave_reduce_scatter<R * G>(part);
+  const int j = rs_index<R * G>(lane), g = g0 + j / G;
+  if (rs_owner<R * G>(lane) && g < U.C) {
     const int64_t cw = (int64_t)u * a.cstride + g;
     const int n = off[(g + 1) * U.S] - off[g * U.S] + (a.L.fold_cap ? a.L.cl_fold[U.cl_base + g] : 0);
-    const float lg = n > 0 ? log2f((float)n) : -INFINITY;
-#pragma unroll
-    for (int h = 0; h < G; ++h) a.ws.cl_score[cw * G + h] = n > 0 ? mine[h] + lg : -INFINITY;
+    a.ws.cl_score[cw * G + j % G] = n > 0 ? t + log2f((float)n) : -INFINITY;
   }
 }
 
@@ -490,7 +479,11 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. Subclusters and residual.  Grid (nb_chosen + nb_rest, units):
+// 3. Subclusters and residual.  Grid (units, nb_rest + nb_chosen); blocks
+//    are numbered x (record slot order) as below, but the rest blocks come
+//    first in the grid, so the dispatcher starts them together with the
+//    chosen-cluster blocks instead of after every chosen slot (most of which
+//    find no cluster and leave):
 //    * block x < nb_chosen takes the x-th chosen cluster of its unit (from
 //      the ascending list the top-c pass wrote), if any: scores its S
 //      subclusters for every head (one batch of row loads per wave), picks
@@ -551,15 +544,16 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
   constexpr int EPL = D / 32;
   constexpr int VPL = D / 64;
   constexpr int RS = D + kPartPad;
-  constexpr int RPW = kMaxS / 4;   // subcluster rows per wave
-  static_assert(kMaxS * G <= 256, "one thread per (subcluster, head) score");
+  constexpr int SR = kDecodeSubRows;
+  constexpr int RPW = SR / 4;   // subcluster rows per wave
+  static_assert(SR * G <= 256, "one thread per (subcluster, head) score");
   __shared__ float st[4][G][D + 2];
-  __shared__ float lds_sc[kMaxS][G];
-  __shared__ float lds_gs[kMaxS];  // shared selection: summed mass fractions
-  __shared__ uint32_t lds_sm[kMaxS];
-  __shared__ int lds_cnt[kMaxS];   // reordered rows of each subcluster
-  __shared__ int lds_fcnt[kMaxS];  // folded rows of each subcluster
-  __shared__ int lds_off[kMaxS + 1];
+  __shared__ float lds_sc[SR][G];
+  __shared__ float lds_gs[SR];  // shared selection: summed mass fractions
+  __shared__ uint32_t lds_sm[SR];
+  __shared__ int lds_cnt[SR];   // reordered rows of each subcluster
+  __shared__ int lds_fcnt[SR];  // folded rows of each subcluster
+  __shared__ int lds_off[SR + 1];
   __shared__ int sh[16];
   __shared__ float lds_fe[G][256];  // feature-map residual: 2^(fq - max) per head
   __shared__ float lds_fbase[G];    // and max - log2(m) / 2
@@ -569,7 +563,8 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
   const int64_t cw = (int64_t)u * a.cstride;  // the unit's per-cluster workspace entries
   // the x-th chosen cluster needs only the unit index: its loads go out with
   // the unit record's
-  const int x = blockIdx.y;
+  const int n_rest_blocks = a.nb_res - nb_chosen;
+  const int x = (int)blockIdx.y < n_rest_blocks ? nb_chosen + (int)blockIdx.y : (int)blockIdx.y - n_rest_blocks;
   const int n_ch_raw = a.ws.n_chosen[u];
   int g_x = 0, tb_x = 0;
   if (x < nb_chosen) {
@@ -644,38 +639,55 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
         }
         if (tid == S - 1) lds_off[S] = o1;
       }
+      // the value means of the same rows, for the residual below: issued
+      // with the score rows where the registers allow it (at G >= 2 the
+      // occupancy is set by the other path), else after the ranking
+      constexpr bool kEarlyVb = G >= 2;
+      float vb[RPW][VPL];
+      if (kEarlyVb && a.residual) {
+#pragma unroll
+        for (int k = 0; k < RPW; ++k)
+          load_floats<VPL>(a.L.sub_vbar + (sg0 + min(wave + 4 * k, S - 1)) * D + lane * VPL, vb[k]);
+      }
+      // (the scheduler would otherwise sink these loads to their use)
+      if constexpr (kEarlyVb) __builtin_amdgcn_sched_barrier(0);
       int rcnt[RPW];
 #pragma unroll
       for (int k = 0; k < RPW; ++k) {
         const int i = min(wave + 4 * k, S - 1);
         rcnt[k] = off[g * S + i + 1] - off[g * S + i] + (a.L.fold_cap ? a.L.sub_fold[sg0 + i] : 0);
       }
-      if (tid < kMaxS) lds_sm[tid] = 0u;
+      if (tid < SR) lds_sm[tid] = 0u;
       // full scores (count term added; -inf for an empty subcluster and for
-      // the rows past S, so the ranking below runs over all kMaxS rows)
+      // the rows past S, so the ranking below runs over all SR rows): the
+      // wave's RPW x G partial dot products are summed over the lanes by one
+      // reduce-scatter, after which one lane holds each (row, head) score
+      {
+        float part[RPW * G];
 #pragma unroll
-      for (int k = 0; k < RPW; ++k) {
-        const int i = wave + 4 * k;
-        if (i >= S) {
-          if (lane < G) lds_sc[i][lane] = -INFINITY;
-          continue;
+        for (int k = 0; k < RPW; ++k) {
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            float t = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) t += coef[h][e] * xr[k][e];
+            part[k * G + h] = t;
+          }
         }
-        const int cnt = uni(rcnt[k]);
-        const float lc = cnt > 0 ? log2f((float)cnt) : 0.f;
+        const float t = wave_reduce_scatter<RPW * G>(part);
+        if (rs_owner<RPW * G>(lane)) {
+          const int j = rs_index<RPW * G>(lane), k = j / G, h = j % G, i = wave + 4 * k;
+          int cnt = 0;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float t = 0.f;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) t += coef[h][e] * xr[k][e];
-          t = wave_sum_uniform(t);
-          if (lane == 0) lds_sc[i][h] = cnt > 0 ? t + lc : -INFINITY;
+          for (int kk = 0; kk < RPW; ++kk) cnt = kk == k ? rcnt[kk] : cnt;
+          lds_sc[i][h] = (i < S && cnt > 0) ? t + log2f((float)cnt) : -INFINITY;
         }
       }
       __syncthreads();
       if (a.shared) {
         // one selection per KV head: a subcluster's key is the sum over the
         // heads of 2^(score - L_h), L_h the head's log2 total over clusters
-        if (tid < kMaxS) {
+        if (tid < SR) {
           float gsv = 0.f;
           bool any = false;
 #pragma unroll
@@ -693,36 +705,35 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
       const int s_keep = s_keep_raw < 0 ? 0 : s_keep_raw;
       const int ti = tid / G, th = tid % G;
       bool tsel = false;
-      if (tid < kMaxS * G) {
+      if (tid < SR * G) {
         const float my = a.shared ? lds_gs[ti] : lds_sc[ti][th];
-        float osc[kMaxS];
+        float osc[SR];
 #pragma unroll
-        for (int j = 0; j < kMaxS; ++j) osc[j] = a.shared ? lds_gs[j] : lds_sc[j][th];
+        for (int j = 0; j < SR; ++j) osc[j] = a.shared ? lds_gs[j] : lds_sc[j][th];
         // branch-free count (bitwise, not short-circuit, operators)
         int rank = 0;
 #pragma unroll
-        for (int j = 0; j < kMaxS; ++j)
+        for (int j = 0; j < SR; ++j)
           rank += (int)((osc[j] != -INFINITY) & ((osc[j] > my) | ((osc[j] == my) & (j < ti))));
         tsel = my != -INFINITY && ((mask >> th) & 1u) && rank < s_keep;
         if (tsel) atomicOr(&lds_sm[ti], 1u << th);
       }
       __syncthreads();
-      // the value means of the same rows, for the residual below (issued
-      // now, so their registers are not held through the ranking)
-      float vb[RPW][VPL];
-      if (a.residual) {
+      // (G = 1: issued now, so their registers are not held through the
+      // ranking)
+      if (!kEarlyVb && a.residual) {
 #pragma unroll
         for (int k = 0; k < RPW; ++k)
           load_floats<VPL>(a.L.sub_vbar + (sg0 + min(wave + 4 * k, S - 1)) * D + lane * VPL, vb[k]);
       }
-      if (a.sel_s && tid < kMaxS * G && ((mask >> th) & 1u)) {
+      if (a.sel_s && tid < SR * G && ((mask >> th) & 1u)) {
         // selection output: the head's chosen subclusters in index order,
         // under the cluster's rank for the head, then -1
         const int rch = a.ws.cl_rank[cg * G + th];
         const int hq = U.kv_head * G + th;
         const int64_t base = (((int64_t)U.seq * a.Hq + hq) * a.c_stride + rch) * a.s_stride;
         int before = 0, all_h = 0;
-        for (int j = 0; j < kMaxS; ++j) {
+        for (int j = 0; j < SR; ++j) {
           const int bit = (int)((lds_sm[j] >> th) & 1u);
           before += j < ti ? bit : 0;
           all_h += bit;
@@ -871,30 +882,36 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
         }
       }
     } else {
-    uint32_t mask[RCW];
-    int n_g[RCW];
-    float vb[RCW][VPL], sc[RCW][G];
+      // RB clusters' loads at a time, so this path needs no more registers
+      // than the chosen-cluster path
+      constexpr int RB = RCW / 2;
+#pragma unroll 1
+      for (int k0 = 0; k0 < RCW; k0 += RB) {
+        uint32_t mask[RB];
+        int n_g[RB];
+        float vb[RB][VPL], sc[RB][G];
 #pragma unroll
-    for (int k = 0; k < RCW; ++k) {
-      const int g = min(y * kRestClustersPerBlock + wave * RCW + k, C - 1);
-      const int64_t cg = cw + g;
-      mask[k] = a.ws.cl_mask[cg];
-      n_g[k] = off[(g + 1) * S] - off[g * S] + (a.L.fold_cap ? a.L.cl_fold[U.cl_base + g] : 0);
-      load_floats<VPL>(a.L.cl_vbar + (U.cl_base + g) * D + lane * VPL, vb[k]);
+        for (int k = 0; k < RB; ++k) {
+          const int g = min(y * kRestClustersPerBlock + wave * RCW + k0 + k, C - 1);
+          const int64_t cg = cw + g;
+          mask[k] = a.ws.cl_mask[cg];
+          n_g[k] = off[(g + 1) * S] - off[g * S] + (a.L.fold_cap ? a.L.cl_fold[U.cl_base + g] : 0);
+          load_floats<VPL>(a.L.cl_vbar + (U.cl_base + g) * D + lane * VPL, vb[k]);
 #pragma unroll
-      for (int h = 0; h < G; ++h) sc[k][h] = a.ws.cl_score[cg * G + h];
-    }
+          for (int h = 0; h < G; ++h) sc[k][h] = a.ws.cl_score[cg * G + h];
+        }
 #pragma unroll
-    for (int k = 0; k < RCW; ++k) {
-      const int g = y * kRestClustersPerBlock + wave * RCW + k;
-      if (g >= C) break;
-      const uint32_t unchosen = n_g[k] > 0 ? (all & ~mask[k]) : 0u;
-      if (unchosen && a.residual) {
+        for (int k = 0; k < RB; ++k) {
+          const int g = y * kRestClustersPerBlock + wave * RCW + k0 + k;
+          if (g >= C) break;
+          const uint32_t unchosen = n_g[k] > 0 ? (all & ~mask[k]) : 0u;
+          if (unchosen && a.residual) {
 #pragma unroll
-        for (int h = 0; h < G; ++h)
-          if ((unchosen >> h) & 1u) add_group<VPL>(rm[h], rl[h], ro[h], sc[k][h], vb[k]);
+            for (int h = 0; h < G; ++h)
+              if ((unchosen >> h) & 1u) add_group<VPL>(rm[h], rl[h], ro[h], sc[k][h], vb[k]);
+          }
+        }
       }
-    }
     }
   }
 

@@ -14,6 +14,11 @@ constexpr int kWave = 64;
 constexpr int kMaxG = 8;        // query heads per KV head
 constexpr int kMaxS = 32;       // subclusters per cluster (N <= 2^22 gives S <= 22)
 constexpr int kMaxC = 2048;     // clusters per unit (N <= 2^22 gives C <= 2048)
+// subcluster rows the decode kernels hold per cluster: S = ceil(log2 n) <= 22
+// for n <= 2^22, rounded up to a multiple of 4 (one row per wave and step)
+constexpr int kDecodeSubRows = 24;
+static_assert(MOG_MAX_LEN <= (1 << 22) && kDecodeSubRows >= 22 && kDecodeSubRows % 4 == 0,
+              "every subcluster of a cluster fits the decode kernels' rows");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
