@@ -131,6 +131,39 @@ def test_budget_larger_than_partition():
     assert rel_l2(out[0], o) < 2e-3
 
 
+@pytest.mark.parametrize("c", [3, 17, 40, 64, 65, 120])
+def test_exact_ties_go_to_lower_index(c):
+    """A zero query makes every group's score its log count, so groups of
+    equal size tie exactly in any precision: the chosen clusters and
+    subclusters must be exactly the oracle's (ties to the lower index), for
+    budgets from a few clusters to most of them."""
+    wl = synth.config(1, seq_lens=[20000], n_kv_heads=1, n_q_heads=2, n_components=64, top_c=[c],
+                      top_s=[3])
+    say(f"[case] zero query, {wl.seq_lens} keys, c={c}")
+    b = synth.generate(wl, device="cuda", n_qsets=1)
+    kv = ops.KVCache.from_batch(b)
+    lays = build_oracle_layouts(b)
+    lay = ops.import_layout(kv, wl.n_sink, wl.n_recent, [unit_layout_arrays(lays[0])])
+    params = ops.decode_params(wl.n_q_heads, [c], [3])
+    q = torch.zeros_like(b.Q[0]).contiguous()
+    out, lse, sel_c, sel_s = ops.mog_decode(lay, kv, q, params, want_sel=True)
+    torch.cuda.synchronize()
+    sel_c, sel_s = sel_c.cpu().numpy(), sel_s.cpu().numpy()
+    K, V = b.unit_kv(0, 0)
+    G, D = wl.group, wl.head_dim
+    counts = lays[0].cl_count
+    assert len(set(counts[counts > 0].tolist())) < int((counts > 0).sum()), "no equal-size clusters"
+    ref = O.decode_unit(lays[0], K, V, np.zeros((G, D)), c, 3, scale=1.0 / math.sqrt(D))
+    for h in range(G):
+        gc = [int(x) for x in sel_c[0, h] if x >= 0]
+        assert gc == [int(x) for x in ref["sel_c"][h]], (h, gc, ref["sel_c"][h])
+        for r in range(len(gc)):
+            gs = [int(x) for x in sel_s[0, h, r] if x >= 0]
+            assert gs == [int(x) for x in ref["sel_s"][h][r]], (h, r, gs, ref["sel_s"][h][r])
+    o, _ = O.dense_attention(K, V, np.zeros((G, D)))
+    say(f"  {len(gc)} clusters chosen; rel L2 vs dense {rel_l2(out[0].cpu().numpy(), o):.2e}")
+
+
 # ---------------------------------------------------------------------------
 # dense baseline
 # ---------------------------------------------------------------------------
