@@ -1184,9 +1184,11 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
 // 5. Merge: per query head, the exact records of its unit (n_part per unit,
 //    or the range uinfo[u] the exact pass wrote) and the n_res residual
 //    records of the unit, merged with one normalisation.  Grid (Hq, n_seq),
-//    1024 threads: (D/4)-lane groups each fold every NG-th record into a
-//    running (m, l, o) with 16-byte loads (one pass over the records), then
-//    the groups are combined under their common maximum.
+//    1024 threads: (D/8)-lane groups each fold every NG-th record into a
+//    running (m, l, o) with two 16-byte loads per lane (one pass over the
+//    records, NG of them in flight); then every group rescales its state to
+//    the block maximum, the groups of a wave are summed by lane exchanges
+//    and the waves' sums through LDS.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(1024) void k_merge(const float* part, int n_part, const int32_t* uinfo,
@@ -1194,11 +1196,13 @@ __global__ __launch_bounds__(1024) void k_merge(const float* part, int n_part, c
                                                 const mog_unit* units, int G, int Hq, int Hkv, float* out,
                                                 float* lse) {
   constexpr int RS = D + kPartPad;
-  constexpr int QL = D / 4;        // lanes per record (4 elements each)
+  constexpr int QL = D / 8;        // lanes per record (8 elements each)
   constexpr int NG = 1024 / QL;    // records folded side by side
-  __shared__ float4 acc[NG][QL];
-  __shared__ float gm[NG], gl[NG];
+  constexpr int NW = 1024 / 64;
+  __shared__ float4 wo[NW][QL][2];
+  __shared__ float wm[NW], wl[NW];
   const int hq = blockIdx.x, seq = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int kvh = hq / G, h = hq % G;
   const int u = seq * Hkv + kvh;
   int64_t first = (int64_t)u * n_part;
@@ -1216,41 +1220,59 @@ __global__ __launch_bounds__(1024) void k_merge(const float* part, int n_part, c
   const int total = n_part + (res ? n_res : 0);
   const int q = tid % QL, grp = tid / QL;
   float m = -INFINITY, l = 0.f;
-  float4 o = {0.f, 0.f, 0.f, 0.f};
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
   for (int i = grp; i < total; i += NG) {
     const float* r = i < n_part ? eb + i * stride : rb + (int64_t)(i - n_part) * stride;
     const float mi = r[D], li = r[D + 1];
-    const float4 oi = reinterpret_cast<const float4*>(r)[q];
+    const float4 a0 = reinterpret_cast<const float4*>(r)[2 * q];
+    const float4 a1 = reinterpret_cast<const float4*>(r)[2 * q + 1];
+    const float oi[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
     // branch-free, so the unrolled iterations' loads are all in flight
     const float mn = fmaxf(m, mi);
     const float fa = exp2_or_zero(m, mn), fb = exp2_or_zero(mi, mn);
     l = l * fa + li * fb;
-    o.x = o.x * fa + oi.x * fb;
-    o.y = o.y * fa + oi.y * fb;
-    o.z = o.z * fa + oi.z * fb;
-    o.w = o.w * fa + oi.w * fb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = o[e] * fa + oi[e] * fb;
     m = mn;
   }
-  acc[grp][q] = o;
-  if (q == 0) {
-    gm[grp] = m;
-    gl[grp] = l;
+  // block maximum of the groups' m
+  const float mw = wave_max(m);
+  if (lane == 0) wm[wave] = mw;
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w]);
+  // every group under M, then the sum over the wave's groups (lanes
+  // q, q + QL, q + 2 QL, ...)
+  const float f = exp2_or_zero(m, M);
+  l *= f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] *= f;
+#pragma unroll
+  for (int sft = QL; sft < 64; sft <<= 1) {
+    l += __shfl_xor(l, sft, 64);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] += __shfl_xor(o[e], sft, 64);
+  }
+  if (lane < QL) {
+    wo[wave][lane][0] = float4{o[0], o[1], o[2], o[3]};
+    wo[wave][lane][1] = float4{o[4], o[5], o[6], o[7]};
+    if (lane == 0) wl[wave] = l;
   }
   __syncthreads();
-  if (tid < QL) {
-    float M = -INFINITY;
-    for (int k = 0; k < NG; ++k) M = fmaxf(M, gm[k]);
+  // thread t < D / 4 sums 4 elements over the waves
+  if (tid < D / 4) {
     float4 t = {0.f, 0.f, 0.f, 0.f};
     float dn = 0.f;
-    for (int k = 0; k < NG; ++k) {
-      const float f = exp2_or_zero(gm[k], M);
-      const float4 a4 = acc[k][tid];
-      t.x += f * a4.x;
-      t.y += f * a4.y;
-      t.z += f * a4.z;
-      t.w += f * a4.w;
-      dn += f * gl[k];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float4 a4 = reinterpret_cast<const float4*>(wo[w])[tid];
+      t.x += a4.x;
+      t.y += a4.y;
+      t.z += a4.z;
+      t.w += a4.w;
+      dn += wl[w];
     }
     const int64_t orow = (int64_t)seq * Hq + hq;
     const float inv = dn > 0.f ? 1.f / dn : 0.f;
