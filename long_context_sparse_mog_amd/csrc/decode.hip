@@ -1221,7 +1221,10 @@ __global__ __launch_bounds__(1024) void k_merge(const float* part, int n_part, c
   const int q = tid % QL, grp = tid / QL;
   float m = -INFINITY, l = 0.f;
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
+  // two records per group in flight: 2 NG = 128 records per pass at D = 128
+  // (a unit has up to a few hundred), and registers for two blocks per
+  // compute unit
+#pragma unroll 2
   for (int i = grp; i < total; i += NG) {
     const float* r = i < n_part ? eb + i * stride : rb + (int64_t)(i - n_part) * stride;
     const float mi = r[D], li = r[D + 1];
