@@ -492,8 +492,9 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
 //      the cluster's exact tiles (runs of chosen subclusters cut into tiles
 //      of <= 32 rows) from its slot base, and accumulates the residual
 //      terms of the subclusters a choosing head left out;
-//    * block nb_chosen + y covers clusters [16y, 16y+16) (4 per wave): the
-//      residual terms of every head that left a cluster out.
+//    * block nb_chosen + y covers clusters [32y, 32y+32) (8 per wave, in
+//      two load batches of 4): the residual terms of every head that left a
+//      cluster out.
 //    Every block writes one residual record per head (slot = block index).
 // ---------------------------------------------------------------------------
 template <int D, int G>
