@@ -53,7 +53,7 @@ extern "C" {
 typedef enum {
   MOG_OK = 0,
   MOG_ERR_INVALID_ARG = 1, /* null pointer, bad size, inconsistent shapes   */
-  MOG_ERR_UNSUPPORTED = 2, /* a valid request this build does not cover    */
+  MOG_ERR_UNSUPPORTED = 2, /* a valid request the library does not cover  */
   MOG_ERR_WORKSPACE = 3,   /* workspace or layout buffer too small          */
   MOG_ERR_HIP = 4,         /* a HIP launch or runtime call failed           */
   MOG_ERR_CAPACITY = 5     /* a layout's fold area is full: build again     */
