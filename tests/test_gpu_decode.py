@@ -99,8 +99,10 @@ def test_config4_ragged_paged_reduced():
                                  high_entropy_heads=(1,), n_components=64))
 
 
-@pytest.mark.parametrize("G", [3, 8])
+@pytest.mark.parametrize("G", [2, 3, 6, 7, 8])
 def test_other_group_sizes(G):
+    # the score kernels' reduce-scatter takes 4G and 6G values per wave:
+    # from 8 up to 48, padded to a power of two, over five or six exchanges
     run_decode_case(synth.config(1, seq_lens=[3000], n_kv_heads=1, n_q_heads=G, n_components=32))
 
 
