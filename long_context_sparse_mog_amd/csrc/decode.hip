@@ -232,9 +232,8 @@ __global__ __launch_bounds__(256) void k_score_clusters(DArgs a) {
   const float t = wave_reduce_scatter<R * G>(part);
   const int j = rs_index<R * G>(lane), g = g0 + j / G;
   if (rs_owner<R * G>(lane) && g < U.C) {
-    const int64_t cw = (int64_t)u * a.cstride + g;
     const int n = off[(g + 1) * U.S] - off[g * U.S] + (a.L.fold_cap ? a.L.cl_fold[U.cl_base + g] : 0);
-    a.ws.cl_score[cw * G + j % G] = n > 0 ? t + log2f((float)n) : -INFINITY;
+    a.ws.cl_score[((int64_t)u * G + j % G) * a.cstride + g] = n > 0 ? t + log2f((float)n) : -INFINITY;
   }
 }
 
@@ -268,7 +267,7 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
   const int64_t cw = (int64_t)u * a.cstride;
   float scv[KPL];
 #pragma unroll
-  for (int j = 0; j < KPL; ++j) scv[j] = a.ws.cl_score[(cw + min(64 * j + lane, a.cstride - 1)) * G + h];
+  for (int j = 0; j < KPL; ++j) scv[j] = a.ws.cl_score[((int64_t)u * G + h) * a.cstride + min(64 * j + lane, a.cstride - 1)];
   const mog_unit U = uni_unit(a.L.units + u);
   const int C = U.C;
   if (tid == 0) a.ws.unit_rows[u] = 0;
@@ -899,7 +898,7 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
           n_g[k] = off[(g + 1) * S] - off[g * S] + (a.L.fold_cap ? a.L.cl_fold[U.cl_base + g] : 0);
           load_floats<VPL>(a.L.cl_vbar + (U.cl_base + g) * D + lane * VPL, vb[k]);
 #pragma unroll
-          for (int h = 0; h < G; ++h) sc[k][h] = a.ws.cl_score[cg * G + h];
+          for (int h = 0; h < G; ++h) sc[k][h] = a.ws.cl_score[((int64_t)u * G + h) * a.cstride + g];
         }
 #pragma unroll
         for (int k = 0; k < RB; ++k) {

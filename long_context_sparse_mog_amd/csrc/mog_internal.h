@@ -113,7 +113,7 @@ __host__ __device__ inline int64_t tile_unit_base(int64_t row_base, int64_t cl_b
 // Per-cluster entries of unit u start at u * max_C (the largest C of the
 // layout), so a kernel can address them from the unit index alone.
 struct DecodeWS {
-  float* cl_score;      // [n_units * max_C][G]  log2-domain scores
+  float* cl_score;      // [n_units][G][max_C]  log2-domain scores (head-major: a head's scores are contiguous)
   float* cl_lse;        // [n_units][G]          shared selection: log2 of each head's total estimated mass
   uint32_t* cl_mask;    // [n_units * max_C]     heads that chose the cluster
   int32_t* cl_rank;     // [n_units * max_C][G]  rank among a head's chosen clusters, or -1
