@@ -452,14 +452,17 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
     }
   }
   __syncthreads();
+  // exclusive prefixes of the slots' counts (lane l: slot l), read per slot
+  const int sc_l = lane < KPL ? slot_cnt[lane] : 0, st_l = lane < KPL ? slot_tiles[lane] : 0;
+  const int sc_inc = wave_incl_scan(sc_l), st_inc = wave_incl_scan(st_l);
+  const int sc_exc = sc_inc - sc_l, st_exc = st_inc - st_l;
 #pragma unroll
   for (int t = 0; t < NSW; ++t) {
     const int j = h + G * t;
     if (j < KPL) {
       const int i = 64 * j + lane;
-      const auto add = [](uint32_t x, uint32_t y) { return x + y; };
-      const int pos0 = (int)wave_reduce_uniform(lane < j ? (uint32_t)slot_cnt[lane] : 0u, add, 0u);
-      const int tb0 = (int)wave_reduce_uniform(lane < j ? (uint32_t)slot_tiles[lane] : 0u, add, 0u);
+      const int pos0 = __builtin_amdgcn_readlane(sc_exc, j);
+      const int tb0 = __builtin_amdgcn_readlane(st_exc, j);
       if (i < C) a.ws.cl_mask[cw + i] = um[t];
       const bool ch = um[t] != 0u;
       const int pos = pos0 + __popcll(__ballot(ch) & below);
@@ -470,11 +473,8 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
       }
     }
   }
-  if (h == 0) {
-    const uint32_t c = lane < KPL ? (uint32_t)slot_cnt[lane] : 0u;
-    const int total = (int)wave_reduce_uniform(c, [](uint32_t x, uint32_t y) { return x + y; }, 0u);
-    if (lane == 0) a.ws.n_chosen[u] = total;
-  }
+  const int total = __builtin_amdgcn_readlane(sc_inc, 63);
+  if (h == 0 && lane == 0) a.ws.n_chosen[u] = total;
 }
 
 // ---------------------------------------------------------------------------
