@@ -432,19 +432,21 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
   // per-slot counts, then each slot's list positions and slot bases from
   // the counts of the slots before it.
   uint32_t um[NSW];
-  int tcnt[NSW];
+  int tcnt[NSW], tinc[NSW];
 #pragma unroll
   for (int t = 0; t < NSW; ++t) {
     const int j = h + G * t;
     um[t] = 0u;
     tcnt[t] = 0;
+    tinc[t] = 0;
     if (j < KPL) {
 #pragma unroll
       for (int g = 0; g < G; ++g) um[t] |= (uint32_t)((selb[g][j] >> lane) & 1ull) << g;
       if (64 * j + lane >= C) um[t] = 0u;
       tcnt[t] = um[t] != 0u ? (bound[t] + 31) / 32 + U.S + bfold[t] : 0;
       const int n = __popcll(__ballot(um[t] != 0u));
-      const int nt = (int)wave_reduce_uniform((uint32_t)tcnt[t], [](uint32_t x, uint32_t y) { return x + y; }, 0u);
+      tinc[t] = wave_incl_scan(tcnt[t]);  // the slot's total in lane 63; the bases below
+      const int nt = __builtin_amdgcn_readlane(tinc[t], 63);
       if (lane == 0) {
         slot_cnt[j] = n;
         slot_tiles[j] = nt;
@@ -466,7 +468,7 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
       if (i < C) a.ws.cl_mask[cw + i] = um[t];
       const bool ch = um[t] != 0u;
       const int pos = pos0 + __popcll(__ballot(ch) & below);
-      const int tb = tb0 + wave_incl_scan(tcnt[t]) - tcnt[t];
+      const int tb = tb0 + tinc[t] - tcnt[t];
       if (ch) {
         a.ws.cl_list[cw + pos] = i;
         a.ws.ch_tbase[cw + pos] = tb;
