@@ -885,8 +885,8 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
       }
     } else {
       // RB clusters' loads at a time, so this path needs no more registers
-      // than the chosen-cluster path
-      constexpr int RB = RCW / 2;
+      // than the chosen-cluster path (at G = 1 all of them fit at once)
+      constexpr int RB = G == 1 ? RCW : RCW / 2;
 #pragma unroll 1
       for (int k0 = 0; k0 < RCW; k0 += RB) {
         uint32_t mask[RB];
