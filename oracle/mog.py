@@ -200,13 +200,24 @@ def centroid_sse(X: np.ndarray, mu: np.ndarray, a: np.ndarray) -> float:
 
 def partition_sse(X: np.ndarray, labels: np.ndarray) -> float:
     """k-means objective of a partition: sum over groups of the squared
-    distances of the members to their group mean."""
-    total = 0.0
-    for g in np.unique(labels):
-        Xg = X[labels == g]
-        dev = Xg - Xg.mean(axis=0)
-        total += float(np.einsum("nd,nd->", dev, dev))
-    return total
+    distances of the members to their group mean.
+
+    The rows are sorted by label so that each group is one contiguous block;
+    a block's mean is its sum divided by its size, and every member's
+    deviation from it is squared and added up.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    labels = np.asarray(labels)
+    if labels.size == 0:
+        return 0.0
+    order = np.argsort(labels, kind="stable")
+    lab = labels[order]
+    Xs = X[order]
+    starts = np.flatnonzero(np.r_[True, lab[1:] != lab[:-1]])
+    counts = np.diff(np.r_[starts, lab.size])
+    means = np.add.reduceat(Xs, starts, axis=0) / counts[:, None]
+    dev = Xs - np.repeat(means, counts, axis=0)
+    return float(np.einsum("nd,nd->", dev, dev))
 
 
 def _recenter(X: np.ndarray, a: np.ndarray, mu_old: np.ndarray) -> np.ndarray:

@@ -214,6 +214,93 @@ def _all_partitions(n, k):
             yield np.array(lab)
 
 
+def test_partition_sse_hand_example():
+    # groups {0, 2} (mean 1), {5, 7} (mean 6), {100}: 1 + 1 + 1 + 1 + 0 = 4;
+    # rows out of label order and label values not 0..k-1
+    X = np.array([[5.0], [0.0], [100.0], [7.0], [2.0]])
+    lab = np.array([9, 4, 1, 9, 4])
+    assert O.partition_sse(X, lab) == 4.0
+    # one group of everything: sum of squared deviations from the grand mean
+    assert O.partition_sse(X, np.zeros(5, int)) == pytest.approx(float(((X - X.mean()) ** 2).sum()), rel=1e-15)
+    # singletons have no deviation; an empty input has none either
+    assert O.partition_sse(X, np.arange(5)) == 0.0
+    assert O.partition_sse(np.zeros((0, 3)), np.zeros(0, int)) == 0.0
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_partition_sse_brute_force_and_identities(seed):
+    rng = np.random.default_rng(seed)
+    n, d, k = 40, 5, 6
+    X = rng.normal(0, 2, (n, d)) + 3.0
+    lab = rng.integers(0, k, n) * 7 + 3
+    # the definition with plain Python loops
+    ref = 0.0
+    for g in set(lab.tolist()):
+        rows = [i for i in range(n) if lab[i] == g]
+        mean = [sum(X[i][e] for i in rows) / len(rows) for e in range(d)]
+        ref += sum((X[i][e] - mean[e]) ** 2 for i in rows for e in range(d))
+    got = O.partition_sse(X, lab)
+    assert got == pytest.approx(ref, rel=1e-12)
+    # Koenig-Huygens: sum |x|^2 - sum_g n_g |mu_g|^2
+    kh = float((X * X).sum())
+    for g in np.unique(lab):
+        m = X[lab == g]
+        kh -= m.shape[0] * float((m.mean(0) ** 2).sum())
+    assert got == pytest.approx(kh, rel=1e-9)
+    # relabelling, reordering rows and translating leave it unchanged
+    perm = rng.permutation(n)
+    relab = {int(g): int(i) for i, g in enumerate(rng.permutation(np.unique(lab)))}
+    lab2 = np.array([relab[int(x)] for x in lab])
+    assert O.partition_sse(X[perm], lab2[perm]) == pytest.approx(got, rel=1e-12)
+    assert O.partition_sse(X - 11.0, lab) == pytest.approx(got, rel=1e-9)
+    # moving one point to another group changes it by the textbook amount:
+    # removing x from a group of n with mean mu lowers the SSE by
+    # n/(n-1) |x - mu|^2, adding it to a group of m with mean nu raises it
+    # by m/(m+1) |x - nu|^2
+    i = int(np.argmax(np.bincount(lab)))  # a point whose group has >= 2 members
+    src = lab == lab[i]
+    i = int(np.flatnonzero(src)[0])
+    dst_g = next(g for g in np.unique(lab) if g != lab[i])
+    dst = lab == dst_g
+    nn, mm = src.sum(), dst.sum()
+    mu, nu = X[src].mean(0), X[dst].mean(0)
+    moved = lab.copy()
+    moved[i] = dst_g
+    delta = -nn / (nn - 1) * float(((X[i] - mu) ** 2).sum()) + mm / (mm + 1) * float(((X[i] - nu) ** 2).sum())
+    assert O.partition_sse(X, moved) == pytest.approx(got + delta, rel=1e-9)
+
+
+def test_subkmeans_converges_to_a_lloyd_fixed_point_per_cluster():
+    # with many rounds the sub-k-means of every cluster stops at a Lloyd
+    # fixed point: each member is nearest (squared distance) the mean of its
+    # own subcluster among the cluster's nonempty subclusters, and a cluster
+    # of n members uses at most min(S, n) subclusters
+    rng = np.random.default_rng(11)
+    K = mixture_keys(rng, 1200, 6, 10, spread=0.6)
+    V = rng.normal(0, 1, K.shape)
+    L = O.build_unit(K, V, 0, 0, 60, O.unit_state(2, 0, 0, 1))
+    lab_c, lab_s = L.cluster_labels(), L.subcluster_labels()
+    Xm = K[:L.n_mid]
+    multi = 0
+    for j in range(L.C):
+        rows = np.flatnonzero(lab_c == j)
+        if rows.size == 0:
+            continue
+        subs = np.unique(lab_s[rows])
+        assert subs.size <= min(L.S, rows.size)
+        # k = min(S, n) distinct members started the cluster's sub-k-means
+        init = L.sub_init_ids[j]
+        assert len(init) == min(L.S, rows.size) and len(set(init)) == len(init)
+        assert set(init) <= set(rows.tolist())
+        assert np.all(subs // L.S == j)
+        means = np.stack([Xm[lab_s == g].mean(0) for g in subs])
+        d2 = ((Xm[rows][:, None, :] - means[None]) ** 2).sum(-1)
+        own = np.searchsorted(subs, lab_s[rows])
+        assert np.all(d2[np.arange(rows.size), own] <= d2.min(1) * (1 + 1e-9) + 1e-12), j
+        multi += subs.size > 1
+    assert multi > L.C // 2  # most clusters were really split
+
+
 def test_kmeans_brute_force_optimum_tiny():
     rng = np.random.default_rng(2)
     # three well separated blobs of three points: Lloyd from any Forgy init
