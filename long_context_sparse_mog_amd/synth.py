@@ -36,8 +36,9 @@ def budget_for_length(L: int, n_sink: int, n_recent: int, frac: float = 0.05, ka
     expected exact rows (anchors plus c*s average-sized subclusters) stay
     within frac*L.  The groups the log-mass score picks are larger than
     average (their score carries ln n), so a workload scales c by ``kappa``,
-    measured so that the mean share of the sequence a query head actually
-    reads stays within frac (see ``calibrate.py``)."""
+    chosen by decoding the workload's query sets on the GPU and reading the
+    mean share of the sequence a query head attends exactly, so that it
+    stays within frac."""
     C = _isqrt_ceil(L)
     S = max(1, (L - 1).bit_length())
     s = -(-S // 4)
@@ -110,8 +111,8 @@ def config(i: int, **override) -> Workload:
     elif i == 3:
         wl = Workload(name="gqa-40q8kv-d128-1M-bf16", n_seq=1, n_q_heads=40, n_kv_heads=8,
                       head_dim=128, seq_lens=[1048576], dtype="bf16", n_sink=64, n_recent=256,
-                      top_c=[34], top_s=[5], n_components=2048, outlier_dims=2,
-                      budget_kappa=34 / 203, seed=BASE_SEED + 3)
+                      top_c=[32], top_s=[5], n_components=2048, outlier_dims=2,
+                      budget_kappa=32 / 203, seed=BASE_SEED + 3)
     elif i == 4:
         rng = np.random.default_rng(BASE_SEED + 4)
         lens = [int(math.floor(math.exp(rng.uniform(math.log(8192), math.log(262144)))))

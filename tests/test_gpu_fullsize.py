@@ -25,9 +25,12 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_fullsize(wl, units, qset=0, shared=False):
+def run_fullsize(wl, units, qset=0, shared=False, check_build=()):
+    """``check_build``: units whose built layout is also checked (a valid
+    partition in (cluster, subcluster, position) order, and every statistic
+    equal to the oracle's statistic of that partition)."""
     say(f"[full] {wl.name} n_seq={wl.n_seq} Hq={wl.n_q_heads} Hkv={wl.n_kv_heads} "
-        f"max_len={wl.max_len} units={units}")
+        f"max_len={wl.max_len} units={units} build-checked={list(check_build)}")
     b = synth.generate(wl, device="cuda", n_qsets=qset + 1)
     kv = ops.KVCache.from_batch(b)
     lay = ops.mog_build(kv, wl.n_sink, wl.n_recent, kmeans_iters=wl.kmeans_iters, seed=1)
@@ -40,8 +43,13 @@ def run_fullsize(wl, units, qset=0, shared=False):
     G = wl.group
     for u in units:
         s, h = divmod(u, wl.n_kv_heads)
-        L = oracle_layout_from_export(lay.export_unit(u), wl.n_sink, wl.n_recent)
+        ex = lay.export_unit(u)
+        L = oracle_layout_from_export(ex, wl.n_sink, wl.n_recent)
         K, V = b.unit_kv(s, h)
+        if u in check_build:
+            from test_gpu_build import check_built_unit
+            check_built_unit(ex, K, V, wl)
+            say(f"  unit {u}: built layout and statistics match the oracle's for its partition")
         Q = q[s, h * G:(h + 1) * G].cpu().numpy().astype(np.float64)
         hs = slice(h * G, (h + 1) * G)
         r = compare_unit(L, K, V, Q, wl.top_c[s], wl.top_s[s], out[s, hs], lse[s, hs], sel_c[s, hs],
@@ -63,11 +71,39 @@ def test_fullsize_gqa_1m_shared_selection_sampled():
 
 
 def test_fullsize_mha_128k_sampled():
-    run_fullsize(synth.config(2), [0, 45, 127])
+    run_fullsize(synth.config(2), [0, 45, 127], check_build=(45,))
 
 
 def test_fullsize_gqa_1m_sampled():
-    run_fullsize(synth.config(3), [0, 7])
+    run_fullsize(synth.config(3), [0, 3, 7], check_build=(3,))
+
+
+def test_fullsize_dense_1m_sampled():
+    """mog_dense_decode over the whole 1M-token cache, in the launch
+    configuration the benchmark times (automatic split count), against the
+    oracle's dense attention on two KV heads (all 5 query heads of each)."""
+    import oracle as O
+    wl = synth.config(3)
+    say(f"[full dense] {wl.name}")
+    b = synth.generate(wl, device="cuda")
+    kv = ops.KVCache.from_batch(b)
+    q = b.Q[0].contiguous()
+    out, lse = ops.mog_dense_decode(kv, q, ops.decode_params(wl.n_q_heads, 1, 1))
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    G = wl.group
+    for h in (1, 6):
+        K, V = b.unit_kv(0, h)
+        Q = q[0, h * G:(h + 1) * G].cpu().numpy().astype(np.float64)
+        ref_o, ref_l = O.dense_attention(K, V, Q)
+        errs = [float(np.linalg.norm(out[0, h * G + g] - ref_o[g]) / np.linalg.norm(ref_o[g])) for g in range(G)]
+        lerr = float(np.max(np.abs(lse[0, h * G:(h + 1) * G] - ref_l)))
+        say(f"  kv head {h}: worst rel L2 {max(errs):.2e}, lse err {lerr:.2e}")
+        assert max(errs) <= 2e-3
+        assert lerr <= 1e-3 * max(1.0, float(np.abs(ref_l).max()))
+        del K, V
+    del b, kv
+    torch.cuda.empty_cache()
 
 
 def test_fullsize_ragged_paged_sampled():

@@ -15,7 +15,7 @@ def test_budgets_of_the_workloads():
     wl = synth.config(4)
     assert wl.n_seq == 16 and all(8192 <= L <= 262144 for L in wl.seq_lens)
     # measured budgets of the workloads (mean per-head read share <= 5%)
-    assert synth.config(1).top_c == [8] and synth.config(3).top_c == [34]
+    assert synth.config(1).top_c == [8] and synth.config(3).top_c == [32]
     assert synth.config(2).top_c == [18] * 4
     assert synth.budget_for_length(262144, 64, 256, kappa=0.35) == (31, 5)
 
