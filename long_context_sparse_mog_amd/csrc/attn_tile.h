@@ -376,7 +376,7 @@ struct MfmaTile {
   }
 
   // Combine the lanes of the wave and store its state (o[D], m, l) per head
-  // in st[wave][h][0..D+1].
+  // in st[wave][h][0..D+1] (rows of D + 4 floats).
   __device__ void to_lds(float* st) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, n = lane & 15;
     float lt = l;
@@ -388,7 +388,7 @@ struct MfmaTile {
       for (int j = 0; j < 4; ++j) o[b][j] += swap8(o[b][j]);
     }
     if (n < G) {
-      float* w = st + (wave * G + n) * (D + 2);
+      float* w = st + (wave * G + n) * (D + kPartPad);
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
 #pragma unroll
@@ -507,7 +507,7 @@ struct RowAcc {
     if (lane < LPR) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float* w = st + (wave * G + h) * (D + 2);
+        float* w = st + (wave * G + h) * (D + kPartPad);
 #pragma unroll
         for (int e = 0; e < 8; ++e) w[lane * 8 + e] = o[h][e];
         if (lane == 0) {
@@ -524,31 +524,41 @@ struct RowAcc {
 // empty record (m = -inf)
 __device__ inline float exp2_or_zero(float m, float M) { return m == -INFINITY ? 0.f : exp2f(m - M); }
 
-// Block epilogue: merge the 4 wave states in st ([4][G][D+2]) into one
-// record per head, dst[h][0..D) = o, dst[h][D] = m, dst[h][D+1] = l
-// (G x (D+4) floats).  Called by all 256 threads after a barrier that made
-// st visible.
+// Block epilogue: merge the 4 wave states in st ([4][G][D+4]: o[D], m, l,
+// two pad words, so every row starts 16-byte aligned) into one record per
+// head, dst[h][0..D) = o, dst[h][D] = m, dst[h][D+1] = l (G x (D+4) floats).
+// One float4 of o per thread.  Called by all 256 threads after a barrier that
+// made st visible.
 template <int D, int G>
 __device__ inline void write_block_record(const float* st, float* dst) {
   constexpr int RS = D + kPartPad;
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int h = idx / D, e = idx % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, st[(w * G + h) * (D + 2) + D]);
-    float L = 0.f, O = 0.f;
+  constexpr int Q = D / 4;
+  for (int idx = threadIdx.x; idx < G * Q; idx += 256) {
+    const int h = idx / Q, e4 = idx % Q;
+    float mw[4], lw[4];
+    float4 ow[4];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float* r = st + (w * G + h) * (D + 2);
-      const float f = exp2_or_zero(r[D], M);
-      L += f * r[D + 1];
-      O += f * r[e];
+      const float* r = st + (w * G + h) * RS;
+      const float2 ml = *reinterpret_cast<const float2*>(r + D);
+      mw[w] = ml.x;
+      lw[w] = ml.y;
+      ow[w] = reinterpret_cast<const float4*>(r)[e4];
     }
-    dst[h * RS + e] = O;
-    if (e == 0) {
-      dst[h * RS + D] = M;
-      dst[h * RS + D + 1] = L;
+    const float M = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
+    float L = 0.f;
+    float4 O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = exp2_or_zero(mw[w], M);
+      L += f * lw[w];
+      O.x += f * ow[w].x;
+      O.y += f * ow[w].y;
+      O.z += f * ow[w].z;
+      O.w += f * ow[w].w;
     }
+    reinterpret_cast<float4*>(dst + h * RS)[e4] = O;
+    if (e4 == 0) *reinterpret_cast<float2*>(dst + h * RS + D) = float2{M, L};
   }
 }
 

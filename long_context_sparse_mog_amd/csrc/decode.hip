@@ -498,30 +498,6 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
 //      cluster out.
 //    Every block writes one residual record per head (slot = block index).
 // ---------------------------------------------------------------------------
-template <int D, int G>
-__device__ inline void write_residual_record(float (*st)[G][D + 2], float* dst) {
-  constexpr int RS = D + kPartPad;
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int h = idx / D, e = idx % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, st[w][h][D]);
-    float l = 0.f, o = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = st[w][h][D];
-      const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-      l += f * st[w][h][D + 1];
-      o += f * st[w][h][e];
-    }
-    dst[h * RS + e] = o;
-    if (e == 0) {
-      dst[h * RS + D] = M;
-      dst[h * RS + D + 1] = l;
-    }
-  }
-}
-
 // Feature-map residual: the weight (log2 of the estimated mass) of a group
 // whose feature sums z the wave holds (z[k]: feature lane + 64 k), for head h:
 // log2(sum_i e_h[i] z[i]) + max_h, with e_h = 2^(fq_h - max_h) in LDS.
@@ -549,7 +525,7 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
   constexpr int SR = kDecodeSubRows;
   constexpr int RPW = SR / 4;   // subcluster rows per wave
   static_assert(SR * G <= 256, "one thread per (subcluster, head) score");
-  __shared__ float st[4][G][D + 2];
+  __shared__ float st[4][G][D + kPartPad];  // wave states, as write_block_record reads them
   __shared__ float lds_sc[SR][G];
   __shared__ float lds_gs[SR];  // shared selection: summed mass fractions
   __shared__ uint32_t lds_sm[SR];
@@ -775,10 +751,27 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
         const int incl = wave_incl_scan(ntl);
         const int n_tiles = __builtin_amdgcn_readlane(incl, 63);
         TileRec* ctiles = a.ws.tiles + tile_unit_base(U.row_base, U.cl_base, u, a.L.fold_cap) + uni(tb_x);
-        if (head) {
-          TileRec* dstt = ctiles + (incl - ntl);
-          for (int r = st; r < run_en; r += 32, ++dstt)
-            *dstt = TileRec{(U.row_base + r) * (int64_t)a.L_head_dim, min(32, run_en - r), m};
+        // the tiles are written by every lane (tiles t = lane, lane + 64, ...):
+        // tile t belongs to the run whose head lane j has tile range
+        // [incl_j - ntl_j, incl_j); the runs are visited in a wave-uniform loop
+        const int tfirst = incl - ntl;
+        for (int t0 = 0; t0 < n_tiles; t0 += 64) {
+          const int t = t0 + lane;
+          int64_t toff = 0;
+          int tn = 0;
+          uint32_t tm = 0u;
+          for (unsigned long long bits = hb; bits; bits &= bits - 1ull) {
+            const int j = __ffsll((long long)bits) - 1;
+            const int ts = __builtin_amdgcn_readlane(tfirst, j);
+            const int tc = __builtin_amdgcn_readlane(ntl, j);
+            if (t >= ts && t < ts + tc) {
+              const int r = __builtin_amdgcn_readlane(st, j) + 32 * (t - ts);
+              toff = (U.row_base + r) * (int64_t)a.L_head_dim;
+              tn = min(32, __builtin_amdgcn_readlane(run_en, j) - r);
+              tm = (uint32_t)__builtin_amdgcn_readlane((int)m, j);
+            }
+          }
+          if (t < n_tiles) ctiles[t] = TileRec{toff, tn, tm};
         }
         int n_all = n_tiles;
         // folded rows of the chosen subclusters, after the reordered ones:
@@ -927,7 +920,7 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
     }
   }
   __syncthreads();
-  write_residual_record<D, G>(st, dst);
+  write_block_record<D, G>(&st[0][0][0], dst);
 }
 
 // ---------------------------------------------------------------------------
@@ -1006,7 +999,7 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
   __shared__ u32x4 kvbuf[4][Engine::BUF];
   // the wave states of the epilogue reuse the tile buffers when they are
   // large enough (after a barrier)
-  constexpr int ST = 4 * G * (D + 2);
+  constexpr int ST = 4 * G * (D + kPartPad);
   constexpr bool ALIAS = sizeof(u32x4) * 4 * Engine::BUF >= sizeof(float) * ST;
   __shared__ float st_own[ALIAS ? 1 : ST];
   float* st = ALIAS ? reinterpret_cast<float*>(&kvbuf[0][0]) : st_own;
@@ -1241,16 +1234,11 @@ __global__ __launch_bounds__(1024) void k_merge(const float* part, int n_part, c
     for (int e = 0; e < 8; ++e) o[e] = o[e] * fa + oi[e] * fb;
     m = mn;
   }
-  // block maximum of the groups' m
+  // every group under the wave maximum, then the sum over the wave's groups
+  // (lanes q, q + QL, q + 2 QL, ...); the waves' states meet in LDS after one
+  // barrier and are rescaled to the block maximum there
   const float mw = wave_max(m);
-  if (lane == 0) wm[wave] = mw;
-  __syncthreads();
-  float M = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w]);
-  // every group under M, then the sum over the wave's groups (lanes
-  // q, q + QL, q + 2 QL, ...)
-  const float f = exp2_or_zero(m, M);
+  const float f = exp2_or_zero(m, mw);
   l *= f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] *= f;
@@ -1263,21 +1251,28 @@ __global__ __launch_bounds__(1024) void k_merge(const float* part, int n_part, c
   if (lane < QL) {
     wo[wave][lane][0] = float4{o[0], o[1], o[2], o[3]};
     wo[wave][lane][1] = float4{o[4], o[5], o[6], o[7]};
-    if (lane == 0) wl[wave] = l;
+    if (lane == 0) {
+      wm[wave] = mw;
+      wl[wave] = l;
+    }
   }
   __syncthreads();
   // thread t < D / 4 sums 4 elements over the waves
   if (tid < D / 4) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w]);
     float4 t = {0.f, 0.f, 0.f, 0.f};
     float dn = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
+      const float fw = exp2_or_zero(wm[w], M);
       const float4 a4 = reinterpret_cast<const float4*>(wo[w])[tid];
-      t.x += a4.x;
-      t.y += a4.y;
-      t.z += a4.z;
-      t.w += a4.w;
-      dn += wl[w];
+      t.x += fw * a4.x;
+      t.y += fw * a4.y;
+      t.z += fw * a4.z;
+      t.w += fw * a4.w;
+      dn += fw * wl[w];
     }
     const int64_t orow = (int64_t)seq * Hq + hq;
     const float inv = dn > 0.f ? 1.f / dn : 0.f;
@@ -1294,7 +1289,7 @@ __global__ __launch_bounds__(256, 2) void k_dense(KVRef kv, const float* q, int 
                                                float scale_l2, SeqArgs seq_args, float* ex_part) {
   constexpr int RS = D + kPartPad;
   __shared__ u32x4 kvbuf[4][Engine::BUF];
-  __shared__ float st[4 * G * (D + 2)];
+  __shared__ float st[4 * G * (D + kPartPad)];
   const int u = blockIdx.y, p = blockIdx.x;
   const int wave = threadIdx.x >> 6;
   const int seq = u / Hkv, kvh = u % Hkv;
