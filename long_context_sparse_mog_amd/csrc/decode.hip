@@ -325,7 +325,95 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
   // prefix there; kk: how many of those are still to be taken
   int kk = c_eff, cand = nvalid;
   uint32_t prefix = 0u, hi_mask = 0u;
-  if (kk > 0) {
+  bool resolved = false;
+  if (kk > 0 && kk < nvalid) {
+    // One 256-bin histogram of the valid values over [lo, hi]: value x goes
+    // to bin floor((hi - x) * 256 / (hi - lo)) (at most 255).  Rounded
+    // subtraction and scaling are monotone, so a value in a lower bin is
+    // strictly larger than every value in a higher bin: the chosen keys are
+    // those of the bins before the one where the count reaches c, plus the
+    // best of that boundary bin, ranked exactly by key and index when it
+    // holds at most 64 keys.  A more crowded boundary bin falls back to the
+    // radix select below.
+    float vhi = -INFINITY, vlo = INFINITY;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      if (key[j] != 0u) {
+        vhi = fmaxf(vhi, scv[j]);
+        vlo = fminf(vlo, scv[j]);
+      }
+    }
+    vhi = __uint_as_float(wave_reduce_uniform(
+        __float_as_uint(vhi), [](uint32_t x, uint32_t y) { return __float_as_uint(fmaxf(__uint_as_float(x), __uint_as_float(y))); },
+        __float_as_uint(-INFINITY)));
+    vlo = __uint_as_float(wave_reduce_uniform(
+        __float_as_uint(vlo), [](uint32_t x, uint32_t y) { return __float_as_uint(fminf(__uint_as_float(x), __uint_as_float(y))); },
+        __float_as_uint(INFINITY)));
+    const float inv = vhi > vlo ? 256.f / (vhi - vlo) : 0.f;
+    int bin[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) bin[j] = key[j] != 0u ? (int)fminf(255.f, (vhi - scv[j]) * inv) : 256 + lane;
+    int* hh = hist[h];
+    *reinterpret_cast<int4*>(&hh[4 * lane]) = make_int4(0, 0, 0, 0);
+    __asm__ volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) atomicAdd(&hh[bin[j]], 1);
+    __asm__ volatile("" ::: "memory");
+    // lane l holds bins 4l .. 4l+3 (bins in increasing order = values in
+    // decreasing order); the keys before its bins come from the lanes before
+    const int4 cv = *reinterpret_cast<const int4*>(&hh[4 * lane]);
+    const int part = cv.x + cv.y + cv.z + cv.w;
+    const int b0 = wave_incl_scan(part) - part, b1 = b0 + cv.x, b2 = b1 + cv.y, b3 = b2 + cv.z;
+    int dsel = -1, dbef = 0, dcnt = 0;
+    if (b0 < kk && kk <= b1) { dsel = 4 * lane; dbef = b0; dcnt = cv.x; }
+    else if (b1 < kk && kk <= b2) { dsel = 4 * lane + 1; dbef = b1; dcnt = cv.y; }
+    else if (b2 < kk && kk <= b3) { dsel = 4 * lane + 2; dbef = b2; dcnt = cv.z; }
+    else if (b3 < kk && kk <= b3 + cv.w) { dsel = 4 * lane + 3; dbef = b3; dcnt = cv.w; }
+    const unsigned long long fb = __ballot(dsel >= 0);
+    const int src = fb ? __ffsll((long long)fb) - 1 : 0;
+    const int bsel = __builtin_amdgcn_readlane(dsel, src);
+    const int nbef = __builtin_amdgcn_readlane(dbef, src);
+    const int nbin = __builtin_amdgcn_readlane(dcnt, src);
+    if (fb != 0ull && nbin <= 64) {
+      // the boundary bin's keys, one per lane, in the wave's LDS bins
+      // (every lane has read its bins above; a wave's LDS operations run
+      // in order)
+      int nmine = 0;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) nmine += bin[j] == bsel;
+      int pos = wave_incl_scan(nmine) - nmine;
+      uint32_t* lk = reinterpret_cast<uint32_t*>(hh);
+      int* li = hh + 64;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) {
+        if (bin[j] == bsel) {
+          lk[pos] = key[j];
+          li[pos] = 64 * j + lane;
+          ++pos;
+        }
+      }
+      __asm__ volatile("" ::: "memory");
+      const uint32_t myk = lane < nbin ? lk[lane] : 0u;
+      const int myi = lane < nbin ? li[lane] : 0;
+      int rk = 0;
+      for (int t = 0; t < nbin; ++t) {
+        const uint32_t kt = lk[t];
+        const int it = li[t];
+        rk += (int)((kt > myk) | ((kt == myk) & (it < myi)));
+      }
+      const int need = kk - nbef;  // keys still to be taken from the bin (>= 1)
+      const unsigned long long cb = __ballot(lane < nbin && rk == need - 1);
+      const uint32_t kcut = (uint32_t)__builtin_amdgcn_readlane((int)myk, __ffsll((long long)cb) - 1);
+      const int n_gt = __popcll(__ballot(lane < nbin && myk > kcut));
+      const int n_eq = __popcll(__ballot(lane < nbin && myk == kcut));
+      prefix = kcut;
+      hi_mask = ~0u;
+      kk = need - n_gt;
+      cand = n_eq;
+      resolved = true;
+    }
+  }
+  if (kk > 0 && !resolved) {
     uint32_t kor = 0u, kand = ~0u;
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
@@ -927,7 +1015,7 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
 // 4. Exact split-K pass.  The tiles a unit reads exactly are numbered
 //    [sink anchor tiles | recent anchor tiles | tiles of the chosen clusters
 //    in list order]; wave w of the unit takes [w*NT/NW, (w+1)*NT/NW).  Every
-//    block scans the chosen clusters' tile counts into LDS; a wave lists its
+//    wave scans the chosen clusters' tile counts into LDS; a wave lists its
 //    tiles (one per lane: binary search, then the 16-byte tile record) in
 //    LDS and streams them.  Grid: the exact blocks of every unit.
 // ---------------------------------------------------------------------------
@@ -936,8 +1024,9 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
 //     chosen subclusters exactly; it gets 1 + floor(T_u * extra / total)
 //     blocks, extra = min(nblk - n_units, ceil(total / 256)) (so the shares
 //     sum to at most nblk and no block gets much under 256 rows), numbered
-//     unit by unit.  Every exact block and every merge block recomputes the
-//     shares from the per-unit row counts (a few KB): no table, no launch.
+//     unit by unit.  Every wave of every exact block recomputes the shares
+//     from the per-unit row counts (a few KB): no table, no launch, no
+//     barrier.
 // ---------------------------------------------------------------------------
 struct BlockShare {
   int u;      // unit (-1: the block has no work)
@@ -945,41 +1034,37 @@ struct BlockShare {
   int n;      // blocks of the unit
 };
 
-// want_block >= 0: the share holding that block; else the share of unit
-// want_unit.  All NT threads call it; the result is uniform.
-template <int NT>
-__device__ BlockShare find_share(const int32_t* unit_rows, int n_units, int nblk, int A, int want_block,
-                                 int want_unit) {
-  __shared__ long long tsum[NT / 64];
-  __shared__ int sh[NT / 64];
-  __shared__ BlockShare res;
-  const int tid = threadIdx.x;
+// The share holding block want_block, found by one wave on its own (every
+// wave of a block computes the same, so no barrier is needed): the units'
+// totals by lane sums, the block numbers by a lane scan, 64 units at a time.
+__device__ BlockShare wave_find_share(const int32_t* unit_rows, int n_units, int nblk, int A, int want_block) {
+  const int lane = threadIdx.x & 63;
   long long part = 0;
-  for (int v = tid; v < n_units; v += NT) part += (long long)A + unit_rows[v];
+  for (int v = lane; v < n_units; v += 64) part += (long long)A + unit_rows[v];
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
-  if ((tid & 63) == 0) tsum[tid >> 6] = part;
-  if (tid == 0) res = BlockShare{-1, 0, 0};
-  __syncthreads();
-  long long total = 0;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) total += tsum[w];
+  const long long total = part;
   long long extra = nblk - n_units;
   const long long by_rows = (total + 255) / 256;
   if (by_rows < extra) extra = by_rows;
+  BlockShare res{-1, 0, 0};
   int carry = 0;
-  for (int base = 0; base < n_units; base += NT) {
-    const int v = base + tid;
+  for (int base = 0; base < n_units; base += 64) {
+    const int v = base + lane;
     int sp = 0;
     if (v < n_units) sp = 1 + (int)(total > 0 ? ((long long)A + unit_rows[v]) * extra / total : 0);
-    int tot;
-    const int first = carry + block_excl_scan<NT>(sp, sh, tot);
-    if (v < n_units && (v == want_unit || (want_block >= first && want_block < first + sp)))
-      res = BlockShare{v, first, sp};
-    carry += tot;
+    const int incl = wave_incl_scan(sp);
+    const int first = carry + incl - sp;
+    const unsigned long long hit = __ballot(v < n_units && want_block >= first && want_block < first + sp);
+    if (hit) {
+      const int src = __ffsll((long long)hit) - 1;
+      res = BlockShare{__builtin_amdgcn_readlane(v, src), __builtin_amdgcn_readlane(first, src),
+                       __builtin_amdgcn_readlane(sp, src)};
+      break;
+    }
+    carry += __builtin_amdgcn_readlane(incl, 63);
   }
-  __syncthreads();
-  return BlockShare{uni(res.u), uni(res.first), uni(res.n)};
+  return res;
 }
 
 // A tile of at most 32 contiguous layout rows: element offset of its first
@@ -992,6 +1077,7 @@ struct TileDesc {
 };
 
 constexpr int kTileBatch = 64;  // tiles listed per wave before streaming them
+constexpr int kWaveListMax = 256;  // chosen clusters a wave scans on its own (4 per lane)
 
 template <int D, int G, typename Engine, typename T>
 __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
@@ -1005,12 +1091,14 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
   float* st = ALIAS ? reinterpret_cast<float*>(&kvbuf[0][0]) : st_own;
   __shared__ int tpre[kMaxC + 1];  // exclusive prefix of the chosen clusters' tile counts
   __shared__ int tbs[kMaxC];       // their tile-slot bases
+  __shared__ int wtpre[4][kWaveListMax + 1];  // the same per wave, for lists of up to 256
+  __shared__ int wtbs[4][kWaveListMax];
   __shared__ int sh[16];
   __shared__ TileRec tiles[4][kTileBatch];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int A = a.n_sink + a.n_recent;
-  const BlockShare bs = find_share<256>(a.ws.unit_rows, a.n_units, a.nblk, A, blockIdx.x, -1);
+  const BlockShare bs = wave_find_share(a.ws.unit_rows, a.n_units, a.nblk, A, blockIdx.x);
   const int u = bs.u;
   if (u < 0) return;
   const int p = blockIdx.x - bs.first, splits_u = bs.n;
@@ -1020,30 +1108,59 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
   }
   const mog_unit U = uni_unit(a.L.units + u);
   const int C = U.C, S = U.S;
-  // query first: its loads overlap the cluster-row scan below
   u32x4* buf = kvbuf[wave];
   Engine acc;
-  acc.init(a.q + ((int64_t)U.seq * a.Hq + (int64_t)U.kv_head * G) * D, a.scale_l2, buf);
   // tile counts of the chosen clusters (in list order) -> exclusive prefix.
-  // A list of up to 256 clusters (the usual case) takes one entry per
-  // thread, loaded without waiting for the list length; a longer one E each.
+  // Lists of up to 256 clusters (the usual case): each wave loads the four
+  // entries of each lane without waiting for the list length (issued before
+  // the query's loads, so one wait covers both) and scans them itself into
+  // its own LDS rows, with no barrier.  Longer lists: a block scan, E entries
+  // per thread.
   const int64_t cw = (int64_t)u * a.cstride;
-  const int n_ch = uni(a.ws.n_chosen[u]);
-  {
-    constexpr int EM = kMaxC / 256;
-    int loc[EM], tbl[EM];
-    loc[0] = a.ws.ch_ntiles[cw + min(tid, a.cstride - 1)];
-    tbl[0] = a.ws.ch_tbase[cw + min(tid, a.cstride - 1)];
+  const int n_ch_raw = a.ws.n_chosen[u];
+  int wl[4], wt[4];
 #pragma unroll
-    for (int k = 1; k < EM; ++k) loc[k] = tbl[k] = 0;
-    const int E = (n_ch + 255) / 256;
-    if (E > 1) {
+  for (int k = 0; k < 4; ++k) {
+    const int x = min(4 * lane + k, a.cstride - 1);
+    wl[k] = a.ws.ch_ntiles[cw + x];
+    wt[k] = a.ws.ch_tbase[cw + x];
+  }
+  acc.init(a.q + ((int64_t)U.seq * a.Hq + (int64_t)U.kv_head * G) * D, a.scale_l2, buf);
+  const int n_ch = uni(n_ch_raw);
+  const int* tp = tpre;  // the prefix the listing searches, and the slot bases
+  const int* tb = tbs;
+  if (n_ch <= kWaveListMax) {
+    int* wp = wtpre[wave];
+    int* wb = wtbs[wave];
+    int sum = 0;
 #pragma unroll
-      for (int k = 0; k < EM; ++k) {
-        const int x = min(tid * E + k, a.cstride - 1);
-        loc[k] = a.ws.ch_ntiles[cw + x];
-        tbl[k] = a.ws.ch_tbase[cw + x];
+    for (int k = 0; k < 4; ++k) {
+      wl[k] = 4 * lane + k < n_ch ? wl[k] : 0;
+      sum += wl[k];
+    }
+    const int incl = wave_incl_scan(sum);
+    int base = incl - sum;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (4 * lane + k < n_ch) {
+        wp[4 * lane + k] = base;
+        wb[4 * lane + k] = wt[k];
       }
+      base += wl[k];
+    }
+    if (lane == 63) wp[n_ch] = incl;
+    __asm__ volatile("" ::: "memory");  // (a wave's LDS operations run in order)
+    tp = wp;
+    tb = wb;
+  } else {
+    constexpr int EM = kMaxC / 256;
+    const int E = (n_ch + 255) / 256;
+    int loc[EM], tbl[EM];
+#pragma unroll
+    for (int k = 0; k < EM; ++k) {
+      const int x = min(tid * E + k, a.cstride - 1);
+      loc[k] = a.ws.ch_ntiles[cw + x];
+      tbl[k] = a.ws.ch_tbase[cw + x];
     }
     int sum = 0;
 #pragma unroll
@@ -1068,7 +1185,7 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
   // virtual tiles of the unit: [sink tiles | recent tiles | chosen clusters'
   // tiles in list order]; wave w of the unit takes [w NT / NW, (w+1) NT / NW)
   const int n_st = (a.n_sink + 31) / 32, n_rt = (a.n_recent + 31) / 32, n_at = n_st + n_rt;
-  const int NT = n_at + uni(tpre[n_ch]);
+  const int NT = n_at + uni(tp[n_ch]);
   const int NW = splits_u * 4;
   const int w = p * 4 + wave;
   int k0 = (int)((int64_t)w * NT / NW);
@@ -1116,12 +1233,12 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
           r = TileRec{anc_base + (int64_t)tok * D, nr | (int)0x80000000, 0xffffffffu};
         } else {
           const int kv_ = k - n_at;
-          int lo = 0, hi = n_ch;  // last x with tpre[x] <= kv_
+          int lo = 0, hi = n_ch;  // last x with tp[x] <= kv_
           while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
-            if (tpre[mid] <= kv_) lo = mid; else hi = mid;
+            if (tp[mid] <= kv_) lo = mid; else hi = mid;
           }
-          r = utiles[tbs[lo] + (kv_ - tpre[lo])];
+          r = utiles[tb[lo] + (kv_ - tp[lo])];
         }
         tl[lane] = r;
       }
