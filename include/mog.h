@@ -309,6 +309,29 @@ mog_status mog_decode(const mog_layout* layout, const mog_kv* kv, const float* q
                       int32_t* sel_c, int32_t* sel_s, void* ws, size_t ws_bytes,
                       hipStream_t stream);
 
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * decode step as mog_decode (same arguments, kernels and results) with the
+ * workspace taken from the library's own static device scratch of
+ * MOG_DECODE_NOALLOC_MAX_WS bytes instead of a caller buffer.  Allocates
+ * nothing, on the host or the device.
+ *  - The scratch is one file-scope device array: every GPU the library runs
+ *    on holds its own copy of MOG_DECODE_NOALLOC_MAX_WS bytes until the
+ *    process ends.  Its address on a device is looked up on the first call
+ *    made with that device current, and kept.
+ *  - Every call on a GPU uses that GPU's one scratch, which keeps the last
+ *    call's contents: calls that overlap on one GPU (other streams, other
+ *    threads) race and must not be issued.  No part of it has to start at
+ *    zero: each call writes every entry before reading it.
+ *  - MOG_ERR_WORKSPACE (nothing enqueued) when the step needs more than
+ *    MOG_DECODE_NOALLOC_MAX_WS bytes (mog_workspace_size(MOG_OP_DECODE)
+ *    tells how many it needs); mog_decode with a caller workspace then
+ *    serves it. */
+#define MOG_DECODE_NOALLOC_MAX_WS ((size_t)64 << 20)
+mog_status mog_decode_noalloc(const mog_layout* layout, const mog_kv* kv, const float* q,
+                              const mog_decode_params* params, float* out, float* lse,
+                              int32_t* sel_c, int32_t* sel_s, hipStream_t stream);
+
 /* Incremental decode (Iceberg Attention abstract: the partition is built
  * once after prefill and then serves every decode step).  The sequences of
  * `kv` are the layout's sequences grown by a_s = kv->seq_lens[s] -

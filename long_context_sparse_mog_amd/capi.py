@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "lib
 MOG_MAX_SEQ = 256
 MOG_MAX_LEN = 1 << 22
 MOG_MAX_FOLD = 1 << 15
+MOG_DECODE_NOALLOC_MAX_WS = 64 << 20
 
 (MOG_OK, MOG_ERR_INVALID_ARG, MOG_ERR_UNSUPPORTED, MOG_ERR_WORKSPACE, MOG_ERR_HIP,
  MOG_ERR_CAPACITY) = range(6)
@@ -86,6 +87,8 @@ SIGNATURES = {
                         C.c_size_t, C.POINTER(mog_layout), vp]),
     "mog_decode": (i32, [C.POINTER(mog_layout), C.POINTER(mog_kv), vp,
                          C.POINTER(mog_decode_params), vp, vp, vp, vp, vp, C.c_size_t, vp]),
+    "mog_decode_noalloc": (i32, [C.POINTER(mog_layout), C.POINTER(mog_kv), vp,
+                                 C.POINTER(mog_decode_params), vp, vp, vp, vp, vp]),
     "mog_append": (i32, [C.POINTER(mog_kv), C.POINTER(mog_layout), vp]),
     "mog_dense_decode": (i32, [C.POINTER(mog_kv), vp, C.POINTER(mog_decode_params), vp, vp, vp,
                                C.c_size_t, vp]),

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "mog_internal.h"
@@ -547,9 +548,11 @@ mog_status mog_workspace_size(mog_op op, const mog_kv* kv, const mog_layout* lay
   return fail(MOG_ERR_INVALID_ARG, "unknown op %d", (int)op);
 }
 
-mog_status mog_decode(const mog_layout* layout, const mog_kv* kv, const float* q, const mog_decode_params* params,
-                      float* out, float* lse, int32_t* sel_c, int32_t* sel_s, void* ws, size_t ws_bytes,
-                      hipStream_t stream) {
+// The decode step with its workspace (`static_ws`: the library's own scratch
+// of mog_decode_noalloc, whose size limit gets its own error text).
+static mog_status decode_with_ws(const mog_layout* layout, const mog_kv* kv, const float* q,
+                                 const mog_decode_params* params, float* out, float* lse, int32_t* sel_c,
+                                 int32_t* sel_s, void* ws, size_t ws_bytes, bool static_ws, hipStream_t stream) {
   mog_status st;
   if ((st = check_kv(kv)) != MOG_OK) return st;
   if ((st = check_layout_vs_kv(layout, kv)) != MOG_OK) return st;
@@ -571,7 +574,13 @@ mog_status mog_decode(const mog_layout* layout, const mog_kv* kv, const float* q
                   layout->fm_scale);
   }
   const DecodePlan d = plan_decode(layout, params);
-  if (ws_bytes < d.bytes) return fail(MOG_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, d.bytes);
+  if (ws_bytes < d.bytes) {
+    if (static_ws)
+      return fail(MOG_ERR_WORKSPACE,
+                  "this decode needs %zu bytes of scratch, above the %zu of the library's static scratch "
+                  "(MOG_DECODE_NOALLOC_MAX_WS); call mog_decode with a workspace instead", d.bytes, ws_bytes);
+    return fail(MOG_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, d.bytes);
+  }
   // with a zero budget there is nothing to report
   if (d.c_stride == 0) sel_c = sel_s = nullptr;
   if (d.s_stride == 0) sel_s = nullptr;
@@ -624,6 +633,57 @@ mog_status mog_decode(const mog_layout* layout, const mog_kv* kv, const float* q
   hipError_t e = launch_decode(x, stream);
   if (e != hipSuccess) return fail(MOG_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // extern "C"
+
+// Scratch of mog_decode_noalloc: device memory of the code object, one copy
+// on every GPU the library runs on, held until the process ends.  In host
+// code `scratch` only names the symbol; its device address on the current
+// GPU comes from hipGetSymbolAddress, looked up once per device and kept.
+static __device__ __align__(256) unsigned char scratch[MOG_DECODE_NOALLOC_MAX_WS];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+mog_status static_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOG_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOG_ERR_UNSUPPORTED, "device %d (the scratch table holds %d)", dev,
+                                                 kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOG_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MOG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mog_status mog_decode(const mog_layout* layout, const mog_kv* kv, const float* q, const mog_decode_params* params,
+                      float* out, float* lse, int32_t* sel_c, int32_t* sel_s, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  return decode_with_ws(layout, kv, q, params, out, lse, sel_c, sel_s, ws, ws_bytes, false, stream);
+}
+
+mog_status mog_decode_noalloc(const mog_layout* layout, const mog_kv* kv, const float* q,
+                              const mog_decode_params* params, float* out, float* lse, int32_t* sel_c,
+                              int32_t* sel_s, hipStream_t stream) {
+  void* ws = nullptr;
+  const mog_status st = static_scratch(&ws);
+  if (st != MOG_OK) return st;
+  return decode_with_ws(layout, kv, q, params, out, lse, sel_c, sel_s, ws, MOG_DECODE_NOALLOC_MAX_WS, true, stream);
 }
 
 mog_status mog_append(const mog_kv* kv, mog_layout* layout, hipStream_t stream) {

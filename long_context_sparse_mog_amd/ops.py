@@ -344,6 +344,19 @@ def mog_decode(layout: Layout, kv: KVCache, q, params, out=None, lse=None, want_
     return out, lse, sel_c, sel_s
 
 
+def mog_decode_noalloc(layout: Layout, kv: KVCache, q, params, out, lse=None, sel_c=None, sel_s=None,
+                       stream=None):
+    """One decode step on the library's static device scratch (no workspace
+    argument; the library allocates nothing).  ``out`` (and ``lse``,
+    ``sel_c``, ``sel_s`` if given) are caller tensors, as in mog_decode."""
+    _require_cuda(q, out, lse, sel_c, sel_s)
+    if q.dtype != torch.float32 or not q.is_contiguous():
+        raise ValueError("q must be contiguous float32 [n_seq][Hq][D]")
+    check(lib().mog_decode_noalloc(C.byref(layout.c), C.byref(kv.c), _vp(q), C.byref(params), _vp(out),
+                                   _vp(lse), _vp(sel_c), _vp(sel_s), _stream(stream)), "mog_decode_noalloc")
+    return out, lse, sel_c, sel_s
+
+
 def mog_dense_decode(kv: KVCache, q, params, out=None, lse=None, ws=None, stream=None):
     """Dense exact decode attention (the in-library baseline).  Returns (out, lse)."""
     _require_cuda(q)
