@@ -10,8 +10,14 @@ around it on its stream), and the CPU oracle timed on a bounded sample.
 
 A step is one full decode pass (cluster scoring, top-c, subcluster scoring
 and top-s, exact attention, residual, merge) over one batch of queries; the
-KV cache and its cluster layout are resident in HBM when timing starts and
-queries rotate through pre-generated sets so selections change every step.
+KV cache and its cluster layout are resident in HBM when timing starts,
+queries rotate through pre-generated sets so selections change every step,
+and consecutive steps run on three copies of the cache and layout in other
+memory, so the last-level cache cannot serve a step the bytes of the one
+before.  Reported per workload: the mean over the timed steps (the value),
+the p10 / p50 / p90 of per-step times, the time per step of a replayed HIP
+graph of the same steps, and the exact and dense kernels alone, timed by the
+events their own dispatches set.
 """
 
 from __future__ import annotations
@@ -29,11 +35,6 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoG decode-attention steps/s at N=128K and 1M + achieved HBM GB/s"
 HBM_PEAK_GBPS = 8000.0
-
-
-# launches of the exact (and dense) kernel between one pair of HIP events in
-# the event pass: the events' own cost is spread over them
-EXACT_REPEAT = 8
 
 
 class HipEvents:
@@ -119,7 +120,105 @@ def selection_volume(wl, lay, sel_c, sel_s, offs):
                 kv_row_bytes=kv_rows_bytes, step_bytes=kv_rows_bytes + stat_bytes)
 
 
-def bench_workload(idx, steps, warmup, n_qsets, ev, with_errors=True, shared_too=False):
+def replicate(wl, b, kv0, lay0, replicas):
+    """Copies of the cache in other device memory, each with its own layout
+    (the build is deterministic, so selections and results are the same):
+    a step on copy i % R never re-reads what the step before it touched, so
+    the 256 MB last-level cache cannot serve repeated bytes."""
+    import torch
+
+    from long_context_sparse_mog_amd import ops
+
+    reps = [(kv0, lay0)]
+    for _ in range(1, replicas):
+        if wl.paged:
+            kv = ops.KVCache(b.pool_K.clone(), b.pool_V.clone(), wl.seq_lens, b.block_table)
+        else:
+            kv = ops.KVCache(b.K.clone(), b.V.clone(), wl.seq_lens)
+        lay = ops.mog_build(kv, wl.n_sink, wl.n_recent, kmeans_iters=wl.kmeans_iters, seed=1)
+        reps.append((kv, lay))
+    torch.cuda.synchronize()
+    return reps
+
+
+def time_steps(step, k, w):
+    """W untimed warmup steps, then exactly K timed steps (torch events around
+    them): ms per step.  Then K more steps with an event after each: the
+    p10 / p50 / p90 of the per-step times."""
+    import numpy as np
+    import torch
+
+    for i in range(w):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(k):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    mean = e0.elapsed_time(e1) / k
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(k + 1)]
+    evs[0].record()
+    for i in range(k):
+        step(i)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(k)])
+    return mean, dict(p10=float(np.percentile(per, 10)), p50=float(np.percentile(per, 50)),
+                      p90=float(np.percentile(per, 90)))
+
+
+def time_graph(step, n_inner, k, check):
+    """n_inner steps captured in one HIP graph, replayed until at least K
+    steps ran (after one untimed replay): ms per step.  ``check()`` then
+    compares the graph's last outputs with an eager run; None if they
+    differ."""
+    import torch
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(0)  # (warm the allocator and the library on the capture stream)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(n_inner):
+            step(i)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, -(-k // n_inner))
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * n_inner)
+    ok = check()
+    del g
+    return ms if ok else None
+
+
+def kernel_event_ms(run, n, ev):
+    """Mean duration of the exact (or dense) kernel over n single launches,
+    from the events its own dispatch sets (one pair per step)."""
+    import torch
+
+    pairs = []
+    for i in range(n):
+        a, z = ev.create(), ev.create()
+        run(i, a, z)
+        pairs.append((a, z))
+    torch.cuda.synchronize()
+    return sum(ev.elapsed_ms(a, z) for a, z in pairs) / n
+
+
+def bench_workload(idx, steps, warmup, n_qsets, ev, with_errors=True, shared_too=False, replicas=3,
+                   graph=True):
     import numpy as np
     import torch
 
@@ -136,63 +235,50 @@ def bench_workload(idx, steps, warmup, n_qsets, ev, with_errors=True, shared_too
     lay = ops.mog_build(kv, wl.n_sink, wl.n_recent, kmeans_iters=wl.kmeans_iters, seed=1)
     torch.cuda.synchronize()
     build_s = time.time() - t0
+    reps = replicate(wl, b, kv, lay, replicas)
+    R = len(reps)
     qs = [b.Q[i].contiguous() for i in range(n_qsets)]
     out = torch.empty_like(qs[0])
     lse = torch.empty(qs[0].shape[:2], device="cuda")
-
-    def params_with_events(n, residual=True, shared=False):
-        ps, pairs = [], []
-        for _ in range(n):
-            p = ops.decode_params(wl.n_q_heads, list(wl.top_c), list(wl.top_s), residual=residual, shared=shared)
-            a, z = ev.create(), ev.create()
-            p.exact_begin, p.exact_end = a, z
-            # the exact kernel runs EXACT_REPEAT times between the events, so
-            # the events' own cost is spread over the launches
-            p.exact_repeat = EXACT_REPEAT
-            ps.append(p)
-            pairs.append((a, z))
-        return ps, pairs
 
     p0 = ops.decode_params(wl.n_q_heads, list(wl.top_c), list(wl.top_s))
     ws = ops.workspace(ops.mog_workspace_size(capi.MOG_OP_DECODE, layout=lay, params=p0))
     pd0 = ops.decode_params(wl.n_q_heads, 1, 1)
     wsd = ops.workspace(ops.mog_workspace_size(capi.MOG_OP_DENSE, kv=kv, params=pd0))
 
-    def timed(fn, plain, plist, pairs, k, w):
-        """W warmup steps, then exactly K timed steps with no events inside
-        them (ms per step); then the same steps again with HIP events around
-        the dominant kernel on the library's stream (its mean duration)."""
-        for i in range(w):
-            fn(qs[i % n_qsets], plain)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(k):
-            fn(qs[i % n_qsets], plain)
-        e1.record()
-        torch.cuda.synchronize()
-        total_ms = e0.elapsed_time(e1)
-        for i in range(len(plist)):
-            fn(qs[i % n_qsets], plist[i])
-        torch.cuda.synchronize()
-        kern = [ev.elapsed_ms(a, z) / max(1, p.exact_repeat) for (a, z), p in zip(pairs, plist)]
-        return total_ms / k, sum(kern) / len(kern)
+    def mog_step(p):
+        return lambda i: ops.mog_decode(reps[i % R][1], reps[i % R][0], qs[i % n_qsets], p, out=out, lse=lse, ws=ws)
 
-    pm, pairs_m = params_with_events(steps)
-    mog_ms, exact_ms = timed(lambda q, p: ops.mog_decode(lay, kv, q, p, out=out, lse=lse, ws=ws), p0, pm,
-                             pairs_m, steps, warmup)
-    dsteps = max(10, steps // 4)
-    pdl = []
-    pairs_d = []
-    for _ in range(dsteps):
-        p = ops.decode_params(wl.n_q_heads, 1, 1)
-        a, z = ev.create(), ev.create()
+    def dense_step(i):
+        ops.mog_dense_decode(reps[i % R][0], qs[i % n_qsets], pd0, out=out, lse=lse, ws=wsd)
+
+    def with_events(p_kw, i, a, z, dense=False):
+        p = ops.decode_params(wl.n_q_heads, *( (1, 1) if dense else (list(wl.top_c), list(wl.top_s)) ), **p_kw)
         p.exact_begin, p.exact_end = a, z
-        pdl.append(p)
-        pairs_d.append((a, z))
-    dense_ms, dense_kern_ms = timed(lambda q, p: ops.mog_dense_decode(kv, q, p, out=out, lse=lse, ws=wsd), pd0,
-                                    pdl, pairs_d, dsteps, max(2, warmup // 2))
+        if dense:
+            ops.mog_dense_decode(reps[i % R][0], qs[i % n_qsets], p, out=out, lse=lse, ws=wsd)
+        else:
+            ops.mog_decode(reps[i % R][1], reps[i % R][0], qs[i % n_qsets], p, out=out, lse=lse, ws=ws)
+
+    n_ev = min(steps, 64)
+    mog_ms, mog_pct = time_steps(mog_step(p0), steps, warmup)
+    exact_ms = kernel_event_ms(lambda i, a, z: with_events({}, i, a, z), n_ev, ev)
+    graph_ms = None
+    if graph:
+        n_inner = R * n_qsets // math.gcd(R, n_qsets)
+
+        def check():
+            ref = torch.empty_like(out)
+            last = n_inner - 1
+            got = out.clone()
+            ops.mog_decode(reps[last % R][1], reps[last % R][0], qs[last % n_qsets], p0, out=ref, ws=ws)
+            torch.cuda.synchronize()
+            return torch.equal(got, ref)
+
+        graph_ms = time_graph(mog_step(p0), n_inner, steps, check)
+    dsteps = max(10, steps // 4)
+    dense_ms, dense_pct = time_steps(dense_step, dsteps, max(2, warmup // 2))
+    dense_kern_ms = kernel_event_ms(lambda i, a, z: with_events({}, i, a, z, dense=True), min(dsteps, 16), ev)
 
     # selections and errors (outside the timed region)
     offs = [lay.export_unit(u)["sub_off"] for u in range(lay.n_units)]
@@ -216,14 +302,17 @@ def bench_workload(idx, steps, warmup, n_qsets, ev, with_errors=True, shared_too
         workload=wl.name, n_seq=wl.n_seq, seq_lens=wl.seq_lens if wl.n_seq <= 4 else "ragged",
         n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads, head_dim=wl.head_dim, dtype=wl.dtype,
         top_c=wl.top_c[0] if len(set(wl.top_c)) == 1 else "per-seq", top_s=wl.top_s[0] if len(set(wl.top_s)) == 1 else "per-seq",
+        replicas=R,
         steps_per_s=1000.0 / mog_ms, ms_per_step=mog_ms,
+        ms_p10=mog_pct["p10"], ms_p50=mog_pct["p50"], ms_p90=mog_pct["p90"],
+        graph_ms_per_step=graph_ms,
         exact_kernel_ms=exact_ms,
         step_bytes=mean("step_bytes"), exact_kernel_bytes=mean("kv_row_bytes"),
         hbm_GBps=mean("step_bytes") / (mog_ms * 1e-3) / 1e9,
         exact_kernel_GBps=mean("kv_row_bytes") / (exact_ms * 1e-3) / 1e9,
         frac_kv_read_union=mean("rows_union") / mean("n_tokens"),
         frac_kv_read_per_head=mean("rows_per_head") / mean("n_tokens"),
-        dense_ms_per_step=dense_ms, dense_kernel_ms=dense_kern_ms,
+        dense_ms_per_step=dense_ms, dense_ms_p50=dense_pct["p50"], dense_kernel_ms=dense_kern_ms,
         dense_GBps=dense_bytes / (dense_kern_ms * 1e-3) / 1e9,
         speedup_vs_dense=dense_ms / mog_ms,
         build_s=build_s, gen_s=gen_s,
@@ -236,9 +325,8 @@ def bench_workload(idx, steps, warmup, n_qsets, ev, with_errors=True, shared_too
         # the same step with one selection per KV head (the heads' summed
         # mass fractions): steps/s, exact kernel, rows read, error vs dense
         p0s = ops.decode_params(wl.n_q_heads, list(wl.top_c), list(wl.top_s), shared=True)
-        pms, pairs_s = params_with_events(steps, shared=True)
-        ms_s, ex_s = timed(lambda q, p: ops.mog_decode(lay, kv, q, p, out=out, lse=lse, ws=ws), p0s, pms, pairs_s,
-                           steps, warmup)
+        ms_s, pct_s = time_steps(mog_step(p0s), steps, warmup)
+        ex_s = kernel_event_ms(lambda i, a, z: with_events({"shared": True}, i, a, z), n_ev, ev)
         vols_s, err_s = [], []
         for t in range(n_qsets):
             o, _, sc, ss = ops.mog_decode(lay, kv, qs[t], p0s, want_sel=True)
@@ -248,13 +336,15 @@ def bench_workload(idx, steps, warmup, n_qsets, ev, with_errors=True, shared_too
                 err_s.append((torch.linalg.norm(o - od, dim=-1) / torch.linalg.norm(od, dim=-1)).flatten())
         mean_s = lambda k: float(np.mean([v[k] for v in vols_s]))
         res["shared_selection"] = dict(
-            steps_per_s=1000.0 / ms_s, ms_per_step=ms_s, exact_kernel_ms=ex_s,
+            steps_per_s=1000.0 / ms_s, ms_per_step=ms_s, ms_p50=pct_s["p50"], exact_kernel_ms=ex_s,
             exact_kernel_bytes=mean_s("kv_row_bytes"),
             exact_kernel_GBps=mean_s("kv_row_bytes") / (ex_s * 1e-3) / 1e9,
             frac_kv_read_union=mean_s("rows_union") / mean_s("n_tokens"),
             speedup_vs_dense=dense_ms / ms_s,
             err_vs_dense_residual_mean=float(torch.cat(err_s).mean()) if err_s else None,
             err_vs_dense_residual_max=float(torch.cat(err_s).max()) if err_s else None)
+    del reps[1:]
+    torch.cuda.empty_cache()
     state = dict(wl=wl, b=b, lay=lay, qs=qs, e=e)
     return res, state
 
@@ -622,7 +712,8 @@ def main():
         r128, _ = bench_workload(2, args.steps, args.warmup, args.qsets, ev)
     others = {}
     if not args.no_others:
-        keep = ("steps_per_s", "ms_per_step", "exact_kernel_ms", "exact_kernel_GBps", "frac_kv_read_per_head",
+        keep = ("replicas", "steps_per_s", "ms_per_step", "ms_p10", "ms_p50", "ms_p90", "graph_ms_per_step",
+                "exact_kernel_ms", "exact_kernel_GBps", "step_bytes", "hbm_GBps", "frac_kv_read_per_head",
                 "frac_kv_read_union", "dense_ms_per_step", "speedup_vs_dense", "err_vs_dense_residual_mean",
                 "err_vs_dense_toponly_mean")
         for idx in (0, 1, 4):
@@ -653,9 +744,13 @@ def main():
                    "q_heads": r1m["n_q_heads"], "kv_heads": r1m["n_kv_heads"], "head_dim": r1m["head_dim"],
                    "top_c": r1m["top_c"], "top_s": r1m["top_s"]},
         "hbm_GBps": r1m["hbm_GBps"],
-        "roofline": {"bound": "hbm", "kernel": "k_exact (exact split-K attention, MFMA bf16)",
+        "roofline": {"bound": "hbm", "kernel": "k_exact only (exact split-K attention, MFMA bf16; the dominant "
+                                                "kernel, timed by its own dispatch events over single launches)",
                      "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
                      "traffic": profiled_traffic()},
+        "step_roofline": {"bound": "hbm", "what": "the whole decode step: algorithmic step bytes / ms_per_step",
+                          "bytes": r1m["step_bytes"], "achieved": r1m["hbm_GBps"], "peak": HBM_PEAK_GBPS,
+                          "unit": "GB/s", "frac": r1m["hbm_GBps"] / HBM_PEAK_GBPS},
         "cpu_baseline": cpu,
         "at_1m": r1m,
         "at_128k": r128,

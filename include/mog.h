@@ -228,15 +228,16 @@ typedef struct {
                                    head is then capped at one head's budget   */
   const int32_t* top_c_per_seq; /* HOST [n_seq] or NULL (then top_c)           */
   const int32_t* top_s_per_seq; /* HOST [n_seq] or NULL (then top_s)           */
-  hipEvent_t exact_begin;       /* optional (NULL: unused): recorded on the    */
-  hipEvent_t exact_end;         /* stream right before / after the exact-      */
-                                /* attention kernel, for timing it alone       */
+  hipEvent_t exact_begin;       /* optional (NULL: unused): set by the dispatch */
+  hipEvent_t exact_end;         /* of the exact-attention kernel itself to its  */
+                                /* start / end time (hipExtLaunchKernel), for  */
+                                /* timing that kernel alone                    */
   int32_t exact_repeat;         /* timing aid: 0 or 1 launches the exact-      */
                                 /* attention kernel once; n in 2..64 launches  */
-                                /* it n times back to back between the two     */
-                                /* events (each launch redoes the same work,   */
-                                /* results are unchanged), so the events' own  */
-                                /* overhead is spread over n launches          */
+                                /* it n times back to back (each launch redoes */
+                                /* the same work, results are unchanged), the  */
+                                /* events then spanning the first start to the */
+                                /* last end                                    */
 } mog_decode_params;
 
 typedef enum { MOG_OP_BUILD = 0, MOG_OP_DECODE = 1, MOG_OP_DENSE = 2 } mog_op;

@@ -13,6 +13,8 @@
 //
 // All softmax bookkeeping is in the base-2 log domain: a logit x is carried
 // as x*log2(e) so every exponential is an exp2.
+#include <hip/hip_ext.h>
+
 #include "attn_tile.h"
 #include "mog_internal.h"
 
@@ -1473,20 +1475,15 @@ static hipError_t decode_impl(const DecodeLaunch& x, const DArgs& a, const Budge
   else
     hipLaunchKernelGGL((k_select_topc<G, kMaxC / 64>), dim3(nu), dim3(64 * G), 0, s, a, b);
   hipLaunchKernelGGL((k_subclusters<D, G>), dim3(nu, x.nb_res), dim3(256), 0, s, a, b, x.nb_chosen);
-  if (x.ev_begin) {
-    const hipError_t e = hipEventRecord(x.ev_begin, s);
-    if (e != hipSuccess) return e;
-  }
+  // the timing events (if any) are taken by the dispatches themselves: the
+  // start of the first exact launch and the end of the last
   for (int r = 0; r < x.repeat; ++r) {
+    hipEvent_t e0 = r == 0 ? x.ev_begin : nullptr, e1 = r + 1 == x.repeat ? x.ev_end : nullptr;
     if (x.dtype == MOG_BF16) {
-      hipLaunchKernelGGL((k_exact<D, G, MfmaTile<D, G>, uint16_t>), dim3(x.nblk), dim3(256), 0, s, a);
+      hipExtLaunchKernelGGL((k_exact<D, G, MfmaTile<D, G>, uint16_t>), dim3(x.nblk), dim3(256), 0, s, e0, e1, 0, a);
     } else {
-      hipLaunchKernelGGL((k_exact<D, G, RowAcc<D, G>, float>), dim3(x.nblk), dim3(256), 0, s, a);
+      hipExtLaunchKernelGGL((k_exact<D, G, RowAcc<D, G>, float>), dim3(x.nblk), dim3(256), 0, s, e0, e1, 0, a);
     }
-  }
-  if (x.ev_end) {
-    const hipError_t e = hipEventRecord(x.ev_end, s);
-    if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((k_merge<D>), dim3(x.Hq, x.L.n_seq), dim3(1024), 0, s, a.ws.ex_part, 0,
                      (const int32_t*)a.ws.uinfo, x.residual ? (const float*)a.ws.res_part : nullptr, x.nb_res,
@@ -1565,22 +1562,15 @@ hipError_t launch_decode(const DecodeLaunch& x, hipStream_t s) {
 template <int D, int G>
 static hipError_t dense_impl(const DenseLaunch& x, hipStream_t s) {
   const int nu = x.seq.n_seq * x.n_kv_heads;
-  if (x.ev_begin) {
-    const hipError_t e = hipEventRecord(x.ev_begin, s);
-    if (e != hipSuccess) return e;
-  }
   for (int r = 0; r < x.repeat; ++r) {
+    hipEvent_t e0 = r == 0 ? x.ev_begin : nullptr, e1 = r + 1 == x.repeat ? x.ev_end : nullptr;
     if (x.dtype == MOG_BF16) {
-      hipLaunchKernelGGL((k_dense<D, G, MfmaTile<D, G>, uint16_t>), dim3(x.splits, nu), dim3(256), 0, s, x.kv, x.q,
-                         x.Hq, x.n_kv_heads, x.splits, x.scale * kLog2e, x.seq, x.ex_part);
+      hipExtLaunchKernelGGL((k_dense<D, G, MfmaTile<D, G>, uint16_t>), dim3(x.splits, nu), dim3(256), 0, s, e0, e1, 0,
+                            x.kv, x.q, x.Hq, x.n_kv_heads, x.splits, x.scale * kLog2e, x.seq, x.ex_part);
     } else {
-      hipLaunchKernelGGL((k_dense<D, G, RowAcc<D, G>, float>), dim3(x.splits, nu), dim3(256), 0, s, x.kv, x.q,
-                         x.Hq, x.n_kv_heads, x.splits, x.scale * kLog2e, x.seq, x.ex_part);
+      hipExtLaunchKernelGGL((k_dense<D, G, RowAcc<D, G>, float>), dim3(x.splits, nu), dim3(256), 0, s, e0, e1, 0,
+                            x.kv, x.q, x.Hq, x.n_kv_heads, x.splits, x.scale * kLog2e, x.seq, x.ex_part);
     }
-  }
-  if (x.ev_end) {
-    const hipError_t e = hipEventRecord(x.ev_end, s);
-    if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((k_merge<D>), dim3(x.Hq, x.seq.n_seq), dim3(1024), 0, s, x.ex_part, x.splits,
                      (const int32_t*)nullptr, (const float*)nullptr, 0, (const int32_t*)nullptr,
