@@ -80,6 +80,14 @@ in the design notes of the repository):
       instead of the Gaussian exp(score); its value estimate stays the mean
       value, and the merge is the same.  Selection is unchanged.  Folded
       tokens add their features to both groups' sums.
+      The page estimates the left-out numerator from the summary as well:
+      with the per-group value summary Z^v_g = sum over the members of
+      phi(sqrt(scale) k) v^T (m x d numbers), a left-out group adds
+      phi(sqrt(scale) q).Z^v_g to the numerator and phi(sqrt(scale) q).Z_g to
+      the denominator (``feature_numerator``).  The oracle implements both
+      numerator models; the library implements the mean-value one (a value
+      summary holds m*d floats per group, more than the group's rows at the
+      workloads' group sizes).
 """
 
 from __future__ import annotations
@@ -303,6 +311,10 @@ class UnitLayout:
     fm_scale: float = None
     cl_z: np.ndarray = None
     sub_z: np.ndarray = None
+    # value summaries of the feature-map numerator, float32 [C][m][d] and
+    # [C*S][m][d] (sums of phi(sqrt(scale) k) v^T); None if absent
+    cl_zv: np.ndarray = None
+    sub_zv: np.ndarray = None
 
     @property
     def n_mid(self) -> int:
@@ -476,6 +488,10 @@ def fold_tokens(L: UnitLayout, K, V, n_new: int) -> UnitLayout:
             ph = positive_features(math.sqrt(out.fm_scale) * k, out.fm_w)[0]
             out.cl_z[j] = (out.cl_z[j].astype(np.float64) + ph).astype(np.float32)
             out.sub_z[g] = (out.sub_z[g].astype(np.float64) + ph).astype(np.float32)
+            if out.cl_zv is not None:
+                pv = np.outer(ph, v)
+                out.cl_zv[j] = (out.cl_zv[j].astype(np.float64) + pv).astype(np.float32)
+                out.sub_zv[g] = (out.sub_zv[g].astype(np.float64) + pv).astype(np.float32)
         out.fold_pos.append(t)
         out.fold_sub.append(g)
     out.N = L.N + n_new
@@ -497,10 +513,11 @@ def positive_features(X, W):
     return np.exp(X @ W.T - 0.5 * (X * X).sum(axis=1, keepdims=True)) / math.sqrt(m)
 
 
-def with_feature_summaries(L: UnitLayout, K, W, scale=None) -> UnitLayout:
+def with_feature_summaries(L: UnitLayout, K, W, scale=None, V=None) -> UnitLayout:
     """A copy of ``L`` holding, for every cluster and subcluster, the sum of
     phi(sqrt(scale) k) over its members (reordered rows and folded tokens),
-    computed in float64 and stored float32."""
+    computed in float64 and stored float32; with the values V also the value
+    summaries, the sums of phi(sqrt(scale) k) v^T."""
     import copy
     K = np.asarray(K, dtype=np.float64)
     W = np.asarray(W, dtype=np.float32)
@@ -509,18 +526,30 @@ def with_feature_summaries(L: UnitLayout, K, W, scale=None) -> UnitLayout:
         scale = 1.0 / math.sqrt(d)
     out = copy.deepcopy(L)
     m = W.shape[0]
+    with_v = V is not None
+    if with_v:
+        V = np.asarray(V, dtype=np.float64)
     sub_z = np.zeros((L.C * L.S, m))
+    sub_zv = np.zeros((L.C * L.S, m, V.shape[1]), np.float32) if with_v else None
     for g in range(L.C * L.S):
         rows = L.group_rows(g)
         if rows.size:
-            sub_z[g] = positive_features(math.sqrt(scale) * K[rows], W).sum(axis=0)
+            ph = positive_features(math.sqrt(scale) * K[rows], W)
+            sub_z[g] = ph.sum(axis=0)
+            if with_v:
+                sub_zv[g] = ph.T @ V[rows]
     cl_z = np.zeros((L.C, m))
+    cl_zv = np.zeros((L.C, m, V.shape[1]), np.float32) if with_v else None
     for j in range(L.C):
         rows = np.concatenate([L.group_rows(j * L.S + i) for i in range(L.S)])
         if rows.size:
-            cl_z[j] = positive_features(math.sqrt(scale) * K[rows], W).sum(axis=0)
+            ph = positive_features(math.sqrt(scale) * K[rows], W)
+            cl_z[j] = ph.sum(axis=0)
+            if with_v:
+                cl_zv[j] = ph.T @ V[rows]
     out.fm_w, out.fm_scale = W, float(scale)
     out.cl_z, out.sub_z = cl_z.astype(np.float32), sub_z.astype(np.float32)
+    out.cl_zv, out.sub_zv = cl_zv, sub_zv
     return out
 
 
@@ -601,7 +630,7 @@ def shared_selection(L: UnitLayout, Q, top_c, top_s, scale=None):
 
 
 def decode_unit(L: UnitLayout, K, V, Q, top_c, top_s, scale=None, residual=True,
-                sel_override=None, shared=False, feature_residual=False):
+                sel_override=None, shared=False, feature_residual=False, feature_numerator=False):
     """One decode step for the query heads that share one KV head.
 
     K, V: float64 [N][d] of the sequence (anchors are read from here, the
@@ -613,7 +642,10 @@ def decode_unit(L: UnitLayout, K, V, Q, top_c, top_s, scale=None, residual=True,
     ``sel_override`` = (sel_c, sel_s) replaces the selection; ``shared``
     takes the one selection of reading R14 for every head;
     ``feature_residual`` estimates the left-out groups' masses from the
-    layout's feature-map summaries (reading R16) instead of exp(score).
+    layout's feature-map summaries (reading R16) instead of exp(score);
+    ``feature_numerator`` (with it) also takes their numerators from the
+    value summaries, phi(sqrt(scale) q).Z^v_g, instead of mass times the mean
+    value.
     """
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
@@ -633,11 +665,20 @@ def decode_unit(L: UnitLayout, K, V, Q, top_c, top_s, scale=None, residual=True,
         sel_override = ([ch] * G, [pk] * G)
     if feature_residual and (L.cl_z is None or not np.isclose(L.fm_scale, scale)):
         raise ValueError("feature-map residual needs summaries built with the decode scale")
+    if feature_numerator and (not feature_residual or L.cl_zv is None):
+        raise ValueError("the feature-map numerator needs feature_residual and value summaries")
     for h in range(G):
         q = Q[h]
         sc = group_log_mass(q, cl_cnt, L.cl_mu, L.cl_var, scale)
-        # the residual's log-mass of every cluster / subcluster
+        # the residual's log-mass of every cluster / subcluster, and the value
+        # estimate of a left-out group: its mean value, or (feature-map
+        # numerator) phi.Z^v_g / phi.Z_g, so that mass * value = phi.Z^v_g
         r_cl = fm_log_mass(q, L.cl_z, L.fm_w, scale) if feature_residual else sc
+        if feature_numerator:
+            ph_q = positive_features(math.sqrt(scale) * q, L.fm_w)[0]
+
+            def group_value(zv, z):
+                return (ph_q @ zv.astype(np.float64)) / float(ph_q @ z.astype(np.float64))
         if sel_override is not None:
             chosen = np.asarray(sel_override[0][h], dtype=np.int64)
         else:
@@ -648,7 +689,8 @@ def decode_unit(L: UnitLayout, K, V, Q, top_c, top_s, scale=None, residual=True,
         for j in range(C):
             if cl_cnt[j] > 0 and j not in chosen_set:
                 r_logw.append(r_cl[j])
-                r_vals.append(L.cl_vbar[j].astype(np.float64))
+                r_vals.append(group_value(L.cl_zv[j], L.cl_z[j]) if feature_numerator
+                              else L.cl_vbar[j].astype(np.float64))
         sel_s_h = []
         for jj, j in enumerate(chosen):
             g0 = j * S
@@ -669,7 +711,8 @@ def decode_unit(L: UnitLayout, K, V, Q, top_c, top_s, scale=None, residual=True,
                     exact_rows.append(L.group_rows(g))
                 else:
                     r_logw.append(r_sub[i])
-                    r_vals.append(L.sub_vbar[g].astype(np.float64))
+                    r_vals.append(group_value(L.sub_zv[g], L.sub_z[g]) if feature_numerator
+                                  else L.sub_vbar[g].astype(np.float64))
         rows = np.concatenate(exact_rows)
         e_logw = scale * (K[rows] @ q)
         e_vals = V[rows]

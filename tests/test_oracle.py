@@ -891,3 +891,67 @@ def test_feature_sums_follow_the_folds():
     R = O.with_feature_summaries(F, K, W)
     np.testing.assert_allclose(F.cl_z, R.cl_z, rtol=1e-5)
     np.testing.assert_allclose(F.sub_z, R.sub_z, rtol=1e-5)
+
+
+def test_feature_numerator_with_zero_projection_is_a_closed_form():
+    """With W = 0 every feature is exp(-|x|^2/2)/sqrt(m), so a left-out
+    group's numerator estimate is exp(-s|q|^2/2) sum_t exp(-s|k_t|^2/2) v_t
+    and its denominator estimate the same sum without v_t, exactly: the
+    output is the merge of the anchors with these terms."""
+    rng = np.random.default_rng(34)
+    d, N, ns, nr = 3, 120, 2, 6
+    K = mixture_keys(rng, N, d, 3)
+    V = rng.normal(0, 1, (N, d))
+    L = O.build_unit(K, V, ns, nr, 10, O.unit_state(4, 0, 0, 1))
+    W = np.zeros((5, d), np.float32)
+    s = 0.7
+    F = O.with_feature_summaries(L, K, W, scale=s, V=V)
+    q = rng.normal(0, 1, d)
+    r = O.decode_unit(F, K, V, q[None], 0, 0, scale=s, feature_residual=True, feature_numerator=True)
+    anchors = np.r_[0:ns, N - nr:N]
+    num = (np.exp(s * K[anchors] @ q)[:, None] * V[anchors]).sum(0)
+    den = np.exp(s * K[anchors] @ q).sum()
+    mid = np.arange(ns, N - nr)
+    w = math.exp(-s * (q @ q) / 2) * np.exp(-s * (K[mid] ** 2).sum(1) / 2)
+    num = num + (w[:, None] * V[mid]).sum(0)
+    den += w.sum()
+    np.testing.assert_allclose(r["out"][0], num / den, rtol=1e-5)
+
+
+def test_feature_numerator_recovers_dense_attention_for_any_groups():
+    """No cluster chosen, ordinary k-means groups (not singletons): with the
+    value summaries both the numerator and the denominator of every group
+    converge to the exact sums as the features grow, so the output
+    approaches dense attention; the mean-value model does not (its error is
+    a property of the groups, not of the features)."""
+    rng = np.random.default_rng(35)
+    d, N = 4, 240
+    K = 0.3 * rng.normal(0, 1, (N, d))
+    # values that follow the keys: inside a group the attention-weighted mean
+    # value differs from the plain mean
+    V = 3.0 * K + 0.1 * rng.normal(0, 1, (N, d))
+    L = O.build_unit(K, V, 2, 6, 10, O.unit_state(5, 0, 0, 1))
+    assert L.sub_count.max() > 1
+    W = rng.normal(0, 1, (200_000, d)).astype(np.float32)
+    F = O.with_feature_summaries(L, K, W, scale=1.0, V=V)
+    # |q|^2 + |k|^2 stays near 1, so each group's estimates have a relative
+    # standard deviation of about sqrt((e - 1) / m) = 3e-3
+    Q = rng.normal(0, 0.4, (2, d))
+    o, lse = O.dense_attention(K, V, Q, scale=1.0)
+    full = O.decode_unit(F, K, V, Q, 0, 0, scale=1.0, feature_residual=True, feature_numerator=True)
+    mean_value = O.decode_unit(F, K, V, Q, 0, 0, scale=1.0, feature_residual=True)
+    assert rel(full["out"], o) < 2e-2
+    np.testing.assert_allclose(full["lse"], lse, atol=1e-2)
+    assert rel(mean_value["out"], o) > 5 * rel(full["out"], o)
+    # the denominators (and so the lse) of the two models are the same
+    np.testing.assert_allclose(full["lse"], mean_value["lse"], rtol=1e-12)
+
+
+def test_feature_value_sums_follow_the_folds():
+    K, V, L = _grown_unit(25, grow=20)
+    W = np.random.default_rng(6).normal(0, 1, (8, K.shape[1])).astype(np.float32)
+    F0 = O.with_feature_summaries(L, K, W, V=V)
+    F = O.fold_tokens(F0, K, V, 20)
+    R = O.with_feature_summaries(F, K, W, V=V)
+    np.testing.assert_allclose(F.cl_zv, R.cl_zv, rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(F.sub_zv, R.sub_zv, rtol=1e-5, atol=1e-6)
