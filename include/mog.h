@@ -56,7 +56,11 @@ typedef enum {
   MOG_ERR_UNSUPPORTED = 2, /* a valid request the library does not cover  */
   MOG_ERR_WORKSPACE = 3,   /* workspace or layout buffer too small          */
   MOG_ERR_HIP = 4,         /* a HIP launch or runtime call failed           */
-  MOG_ERR_CAPACITY = 5     /* a layout's fold area is full: build again     */
+  MOG_ERR_CAPACITY = 5,    /* a layout's fold area is full: build again     */
+  /* Not statuses: these two give the type the range of int32_t, so any int
+   * a C caller passes (e.g. to mog_status_string) is a valid value of it. */
+  MOG_STATUS_RANGE_MIN_ = -0x7fffffff - 1,
+  MOG_STATUS_RANGE_MAX_ = 0x7fffffff
 } mog_status;
 
 typedef enum { MOG_F32 = 0, MOG_BF16 = 1 } mog_dtype;
@@ -240,7 +244,14 @@ typedef struct {
                                 /* last end                                    */
 } mog_decode_params;
 
-typedef enum { MOG_OP_BUILD = 0, MOG_OP_DECODE = 1, MOG_OP_DENSE = 2 } mog_op;
+typedef enum {
+  MOG_OP_BUILD = 0,
+  MOG_OP_DECODE = 1,
+  MOG_OP_DENSE = 2,
+  /* not operations: the range of int32_t, as for mog_status */
+  MOG_OP_RANGE_MIN_ = -0x7fffffff - 1,
+  MOG_OP_RANGE_MAX_ = 0x7fffffff
+} mog_op;
 
 /* ---------------------------------------------------------------------- */
 

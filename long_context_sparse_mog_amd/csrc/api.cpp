@@ -398,7 +398,7 @@ mog_status build_workspace_bytes(const mog_kv* kv, const mog_build_params* bp, s
 extern "C" {
 
 const char* mog_status_string(mog_status st) {
-  switch (st) {
+  switch ((int)st) {
     case MOG_OK: return "ok";
     case MOG_ERR_INVALID_ARG: return "invalid argument";
     case MOG_ERR_UNSUPPORTED: return "unsupported";
@@ -529,7 +529,7 @@ mog_status mog_workspace_size(mog_op op, const mog_kv* kv, const mog_layout* lay
                               const mog_decode_params* dp, size_t* bytes) {
   if (!bytes) return fail(MOG_ERR_INVALID_ARG, "bytes is NULL");
   mog_status st;
-  switch (op) {
+  switch ((int)op) {
     case MOG_OP_DECODE: {
       if (!layout) return fail(MOG_ERR_INVALID_ARG, "layout is NULL");
       if ((st = check_decode_params(dp, layout->n_kv_heads, layout->n_seq)) != MOG_OK) return st;
