@@ -13,7 +13,8 @@
 //    accumulator in exactly the layout the P^T operand needs, split into
 //    high/low parts the same way, and O^T += V^T P^T takes V^T fragments
 //    from LDS with transpose reads.
-//  * RowAcc (fp32 K/V): plain VALU, 16 (D=128) or 8 (D=64) lanes per row.
+//  * RowAcc (fp32 K/V, or bf16 widened on load): plain VALU, 16 (D=128) or
+//    8 (D=64) lanes per row.
 #pragma once
 
 #include "mog_internal.h"
@@ -405,7 +406,7 @@ struct MfmaTile {
 // ---------------------------------------------------------------------------
 // VALU row engine (fp32 K/V): LPR = D/8 lanes per row, 8 elements per lane.
 // ---------------------------------------------------------------------------
-template <int D, int G>
+template <int D, int G, typename T = float>
 struct RowAcc {
   static constexpr int LPR = D / 8;
   static constexpr int RPI = 64 / LPR;
@@ -431,20 +432,20 @@ struct RowAcc {
   struct Regs {
     u32x4 k[1], v[1];
   };
-  __device__ static void load(const float*, const float*, int, u32x4 (&)[1], u32x4 (&)[1]) {}
+  __device__ static void load(const T*, const T*, int, u32x4 (&)[1], u32x4 (&)[1]) {}
   __device__ void compute(u32x4*, const u32x4 (&)[1], const u32x4 (&)[1], int, uint32_t) {}
 
-  __device__ void tile(u32x4*, const float* kp, const float* vp, int nrows, uint32_t mask) {
+  __device__ void tile(u32x4*, const T* kp, const T* vp, int nrows, uint32_t mask) {
     rows(kp, vp, nrows, mask, [](int i) { return (int64_t)i * D; });
   }
 
   template <typename RowOff>
-  __device__ void tile_gather(u32x4*, const float* kb, const float* vb, int nrows, uint32_t mask, RowOff rowoff) {
+  __device__ void tile_gather(u32x4*, const T* kb, const T* vb, int nrows, uint32_t mask, RowOff rowoff) {
     rows(kb, vb, nrows, mask, rowoff);
   }
 
   template <typename RowOff>
-  __device__ void rows(const float* kb, const float* vb, int n, uint32_t mask, RowOff rowoff) {
+  __device__ void rows(const T* kb, const T* vb, int n, uint32_t mask, RowOff rowoff) {
     const int lane = threadIdx.x & 63;
     const int sub = lane % LPR, slot = lane / LPR;
     for (int r = 0; r < n; r += RPI) {
@@ -453,8 +454,8 @@ struct RowAcc {
       float k8[8], v8[8];
       if (valid) {
         const int64_t ro = rowoff(my) + sub * 8;
-        load8<float>(kb, ro, k8);
-        load8<float>(vb, ro, v8);
+        load8<T>(kb, ro, k8);
+        load8<T>(vb, ro, v8);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) k8[e] = v8[e] = 0.f;
