@@ -187,7 +187,7 @@ KVRef make_kvref(const mog_kv* kv) {
 // ------------------------------------------------------------------------
 struct DecodePlan {
   int G, c_stride, s_stride, splits, nblk, nb_res, nb_chosen;
-  size_t o_clscore, o_cllse, o_clmask, o_clrank, o_urows, o_list, o_nch, o_uinfo, o_tbase, o_ntl, o_tiles, o_res, o_ex;
+  size_t o_clscore, o_cllse, o_clmask, o_cltiles, o_clrank, o_urows, o_list, o_nch, o_uinfo, o_tbase, o_ntl, o_tiles, o_res, o_ex;
   size_t o_fq, bytes;
 };
 
@@ -250,6 +250,7 @@ DecodePlan plan_decode(const mog_layout* L, const mog_decode_params* p) {
   d.o_clscore = o; o = align_up(o + ncw * G * 4);
   d.o_cllse = o; o = align_up(o + (size_t)nu * G * 4);
   d.o_clmask = o; o = align_up(o + ncw * 4);
+  d.o_cltiles = o; o = align_up(o + ncw * 4);
   d.o_clrank = o; o = align_up(o + ncw * G * 4);
   d.o_urows = o; o = align_up(o + (size_t)nu * 4);
   d.o_list = o; o = align_up(o + ncw * 4);
@@ -620,6 +621,7 @@ static mog_status decode_with_ws(const mog_layout* layout, const mog_kv* kv, con
   x.ws.cl_score = reinterpret_cast<float*>(w + d.o_clscore);
   x.ws.cl_lse = reinterpret_cast<float*>(w + d.o_cllse);
   x.ws.cl_mask = reinterpret_cast<uint32_t*>(w + d.o_clmask);
+  x.ws.cl_tiles = reinterpret_cast<int32_t*>(w + d.o_cltiles);
   x.ws.cl_rank = reinterpret_cast<int32_t*>(w + d.o_clrank);
   x.ws.unit_rows = reinterpret_cast<int32_t*>(w + d.o_urows);
   x.ws.cl_list = reinterpret_cast<int32_t*>(w + d.o_list);

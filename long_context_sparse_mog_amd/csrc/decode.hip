@@ -234,8 +234,14 @@ __global__ __launch_bounds__(256) void k_score_clusters(DArgs a) {
   const float t = wave_reduce_scatter<R * G>(part);
   const int j = rs_index<R * G>(lane), g = g0 + j / G;
   if (rs_owner<R * G>(lane) && g < U.C) {
-    const int n = off[(g + 1) * U.S] - off[g * U.S] + (a.L.fold_cap ? a.L.cl_fold[U.cl_base + g] : 0);
+    const int nr = off[(g + 1) * U.S] - off[g * U.S];
+    const int nf = a.L.fold_cap ? a.L.cl_fold[U.cl_base + g] : 0;
+    const int n = nr + nf;
     a.ws.cl_score[((int64_t)u * G + j % G) * a.cstride + g] = n > 0 ? t + log2f((float)n) : -INFINITY;
+    // the most tile slots the cluster can need if chosen (one partial tile
+    // per run, at most S runs, a folded row alone at worst), read by the
+    // top-c kernel with the scores
+    if (j % G == 0) a.ws.cl_tiles[(int64_t)u * a.cstride + g] = (nr + 31) / 32 + U.S + nf;
   }
 }
 
@@ -270,19 +276,14 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
   float scv[KPL];
 #pragma unroll
   for (int j = 0; j < KPL; ++j) scv[j] = a.ws.cl_score[((int64_t)u * G + h) * a.cstride + min(64 * j + lane, a.cstride - 1)];
+  // the tile-slot bounds of the clusters of this wave's tail slots (written
+  // by the score kernel beside the scores)
+  int bound[NSW];
+#pragma unroll
+  for (int t = 0; t < NSW; ++t) bound[t] = a.ws.cl_tiles[cw + min(64 * (h + G * t) + lane, a.cstride - 1)];
   const mog_unit U = uni_unit(a.L.units + u);
   const int C = U.C;
   if (tid == 0) a.ws.unit_rows[u] = 0;
-  // the sizes of the clusters of this wave's tail slots: reordered rows and
-  // folded rows
-  const int32_t* off = a.L.sub_off + U.off_base;
-  int bound[NSW], bfold[NSW];
-#pragma unroll
-  for (int t = 0; t < NSW; ++t) {
-    const int i = min(64 * (h + G * t) + lane, C - 1);
-    bound[t] = off[(i + 1) * U.S] - off[i * U.S];
-    bfold[t] = a.L.fold_cap ? a.L.cl_fold[U.cl_base + i] : 0;
-  }
   if (a.shared) {
     // one selection per KV head: the key of a cluster is the sum over the
     // heads of the head's estimated mass fraction 2^(score - L_h), L_h the
@@ -533,7 +534,7 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
 #pragma unroll
       for (int g = 0; g < G; ++g) um[t] |= (uint32_t)((selb[g][j] >> lane) & 1ull) << g;
       if (64 * j + lane >= C) um[t] = 0u;
-      tcnt[t] = um[t] != 0u ? (bound[t] + 31) / 32 + U.S + bfold[t] : 0;
+      tcnt[t] = um[t] != 0u ? bound[t] : 0;
       const int n = __popcll(__ballot(um[t] != 0u));
       tinc[t] = wave_incl_scan(tcnt[t]);  // the slot's total in lane 63; the bases below
       const int nt = __builtin_amdgcn_readlane(tinc[t], 63);
@@ -684,15 +685,20 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
       const int64_t cg = cw + g;
       const int64_t sg0 = U.sub_base + (int64_t)g * S;
       const uint32_t mask = a.ws.cl_mask[cg];
-      const float* qb = a.q + ((int64_t)U.seq * a.Hq + (int64_t)U.kv_head * G) * D;
+      // a budget of S or more subclusters per chosen cluster reads every
+      // nonempty one: no scores, no ranking, nothing left out of the cluster
+      const bool whole = s_keep_raw >= S;
       float coef[G][EPL];
-      score_coefs<D, G>(a, qb, coef);
       // scores: wave w takes rows w, w+4, ...
       float xr[RPW][EPL];
+      if (!whole) {
+        const float* qb = a.q + ((int64_t)U.seq * a.Hq + (int64_t)U.kv_head * G) * D;
+        score_coefs<D, G>(a, qb, coef);
 #pragma unroll
-      for (int k = 0; k < RPW; ++k) {
-        const int i = min(wave + 4 * k, S - 1);
-        load_floats<EPL>(a.L.sub_ms + (sg0 + i) * (2 * D) + lane * EPL, xr[k]);
+        for (int k = 0; k < RPW; ++k) {
+          const int i = min(wave + 4 * k, S - 1);
+          load_floats<EPL>(a.L.sub_ms + (sg0 + i) * (2 * D) + lane * EPL, xr[k]);
+        }
       }
       // subcluster bounds: thread i < S keeps subcluster i's for the tiles,
       // and every wave the sizes of its own rows for the count term
@@ -712,13 +718,22 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
       // occupancy is set by the other path), else after the ranking
       constexpr bool kEarlyVb = G >= 2;
       float vb[RPW][VPL];
-      if (kEarlyVb && a.residual) {
+      if (kEarlyVb && a.residual && !whole) {
 #pragma unroll
         for (int k = 0; k < RPW; ++k)
           load_floats<VPL>(a.L.sub_vbar + (sg0 + min(wave + 4 * k, S - 1)) * D + lane * VPL, vb[k]);
       }
       // (the scheduler would otherwise sink these loads to their use)
       if constexpr (kEarlyVb) __builtin_amdgcn_sched_barrier(0);
+      const int s_keep = s_keep_raw < 0 ? 0 : s_keep_raw;
+      const int ti = tid / G, th = tid % G;
+      bool tsel = false;
+      if (whole) {
+        __syncthreads();  // the bounds
+        if (tid < SR) lds_sm[tid] = (tid < S && lds_cnt[tid] + lds_fcnt[tid] > 0) ? mask : 0u;
+        __syncthreads();
+        tsel = tid < SR * G && ((lds_sm[ti] >> th) & 1u);
+      } else {
       int rcnt[RPW];
 #pragma unroll
       for (int k = 0; k < RPW; ++k) {
@@ -770,9 +785,6 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
       }
       // top-s of every choosing head at once: thread (i, h) ranks subcluster
       // i's score among head h's, or the shared keys (ties to the lower index)
-      const int s_keep = s_keep_raw < 0 ? 0 : s_keep_raw;
-      const int ti = tid / G, th = tid % G;
-      bool tsel = false;
       if (tid < SR * G) {
         const float my = a.shared ? lds_gs[ti] : lds_sc[ti][th];
         float osc[SR];
@@ -794,6 +806,7 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
         for (int k = 0; k < RPW; ++k)
           load_floats<VPL>(a.L.sub_vbar + (sg0 + min(wave + 4 * k, S - 1)) * D + lane * VPL, vb[k]);
       }
+      }  // (not whole)
       if (a.sel_s && tid < SR * G && ((mask >> th) & 1u)) {
         // selection output: the head's chosen subclusters in index order,
         // under the cluster's rank for the head, then -1
@@ -1127,7 +1140,9 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
     wl[k] = a.ws.ch_ntiles[cw + x];
     wt[k] = a.ws.ch_tbase[cw + x];
   }
-  acc.init(a.q + ((int64_t)U.seq * a.Hq + (int64_t)U.kv_head * G) * D, a.scale_l2, buf);
+  // (unit u is sequence u / Hkv, KV head u % Hkv: the query's address does
+  // not wait for the unit record)
+  acc.init(a.q + ((int64_t)(u / a.Hkv) * a.Hq + (int64_t)(u % a.Hkv) * G) * D, a.scale_l2, buf);
   const int n_ch = uni(n_ch_raw);
   const int* tp = tpre;  // the prefix the listing searches, and the slot bases
   const int* tb = tbs;

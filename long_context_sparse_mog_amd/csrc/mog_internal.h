@@ -116,6 +116,7 @@ struct DecodeWS {
   float* cl_score;      // [n_units][G][max_C]  log2-domain scores (head-major: a head's scores are contiguous)
   float* cl_lse;        // [n_units][G]          shared selection: log2 of each head's total estimated mass
   uint32_t* cl_mask;    // [n_units * max_C]     heads that chose the cluster
+  int32_t* cl_tiles;    // [n_units * max_C]     tile slots the cluster needs at most if chosen
   int32_t* cl_rank;     // [n_units * max_C][G]  rank among a head's chosen clusters, or -1
                         //                       (written only when sel_s is requested)
   int32_t* unit_rows;   // [n_units]             rows of chosen subclusters per unit

@@ -29,19 +29,23 @@ def _isqrt_ceil(n: int) -> int:
     return r if r * r == n else r + 1
 
 
-def budget_for_length(L: int, n_sink: int, n_recent: int, frac: float = 0.05, kappa: float = 1.0):
+def budget_for_length(L: int, n_sink: int, n_recent: int, frac: float = 0.05, kappa: float = 1.0,
+                      split=None):
     """Per-query-head exact budget (top_c, top_s) for a length-L sequence.
 
-    Average-size rule: s = ceil(S/4) and c is the largest count whose
-    expected exact rows (anchors plus c*s average-sized subclusters) stay
-    within frac*L.  The groups the log-mass score picks are larger than
-    average (their score carries ln n), so a workload scales c by ``kappa``,
-    chosen by decoding the workload's query sets on the GPU and reading the
-    mean share of the sequence a query head attends exactly, so that it
-    stays within frac."""
+    Average-size rule: s subclusters per chosen cluster (``split``: None for
+    ceil(S/4), "whole" for all S, i.e. whole clusters, or a number) and c
+    the largest count whose expected exact rows (anchors plus c*s
+    average-sized subclusters) stay within frac*L.  The groups the log-mass
+    score picks are larger than average (their score carries ln n), so a
+    workload scales c by ``kappa``, chosen by decoding the workload's query
+    sets on the GPU and reading the mean share of the sequence a query head
+    attends exactly, so that it stays within frac.  The split of each
+    workload is the one with the lowest error against dense attention at
+    that read (measured on the GPU over the workload's query sets)."""
     C = _isqrt_ceil(L)
     S = max(1, (L - 1).bit_length())
-    s = -(-S // 4)
+    s = S if split == "whole" else (-(-S // 4) if split is None else min(int(split), S))
     n_mid = L - n_sink - n_recent
     per_sub = n_mid / (C * S)
     c = int(math.floor((frac * L - (n_sink + n_recent)) / (s * per_sub)))
@@ -72,6 +76,7 @@ class Workload:
     seed: int = BASE_SEED
     kmeans_iters: int = 10
     budget_kappa: float = 1.0       # scale of the average-size budget rule
+    budget_split: object = None     # subclusters per chosen cluster: None (S/4), "whole" or a number
     notes: str = ""
 
     @property
@@ -101,28 +106,30 @@ def config(i: int, **override) -> Workload:
     elif i == 1:
         wl = Workload(name="gqa-32q8kv-d128-32K-bf16", n_seq=1, n_q_heads=32, n_kv_heads=8,
                       head_dim=128, seq_lens=[32768], dtype="bf16", n_sink=64, n_recent=256,
-                      top_c=[8], top_s=[4], n_components=512, outlier_dims=2,
-                      budget_kappa=8 / 27, seed=BASE_SEED + 1)
+                      top_c=[4], top_s=[15], n_components=512, outlier_dims=2,
+                      budget_kappa=4 / 7, budget_split="whole", seed=BASE_SEED + 1)
     elif i == 2:
         wl = Workload(name="mha-4x32h-d128-128K-bf16", n_seq=4, n_q_heads=32, n_kv_heads=32,
                       head_dim=128, seq_lens=[131072] * 4, dtype="bf16", n_sink=64,
-                      n_recent=256, top_c=[18] * 4, top_s=[5] * 4, n_components=512,
-                      outlier_dims=2, needles=16, budget_kappa=18 / 58, seed=BASE_SEED + 2)
+                      n_recent=256, top_c=[38] * 4, top_s=[2] * 4, n_components=512,
+                      outlier_dims=2, needles=16, budget_kappa=38 / 147, budget_split=2,
+                      seed=BASE_SEED + 2)
     elif i == 3:
         wl = Workload(name="gqa-40q8kv-d128-1M-bf16", n_seq=1, n_q_heads=40, n_kv_heads=8,
                       head_dim=128, seq_lens=[1048576], dtype="bf16", n_sink=64, n_recent=256,
-                      top_c=[32], top_s=[5], n_components=2048, outlier_dims=2,
-                      budget_kappa=32 / 203, seed=BASE_SEED + 3)
+                      top_c=[17], top_s=[20], n_components=2048, outlier_dims=2,
+                      budget_kappa=17 / 50, budget_split="whole", seed=BASE_SEED + 3)
     elif i == 4:
         rng = np.random.default_rng(BASE_SEED + 4)
         lens = [int(math.floor(math.exp(rng.uniform(math.log(8192), math.log(262144)))))
                 for _ in range(16)]
-        bud = [budget_for_length(L, 64, 256, kappa=0.35) for L in lens]
+        bud = [budget_for_length(L, 64, 256, kappa=0.7, split="whole") for L in lens]
         wl = Workload(name="ragged-16seq-8K-256K-paged-bf16", n_seq=16, n_q_heads=32,
                       n_kv_heads=8, head_dim=128, seq_lens=lens, dtype="bf16", n_sink=64,
                       n_recent=256, top_c=[b[0] for b in bud], top_s=[b[1] for b in bud],
                       n_components=512, outlier_dims=2, high_entropy_heads=(4, 5, 6, 7),
-                      paged=True, page_size=16, budget_kappa=0.35, seed=BASE_SEED + 4)
+                      paged=True, page_size=16, budget_kappa=0.7, budget_split="whole",
+                      seed=BASE_SEED + 4)
     else:
         raise ValueError(f"no workload {i}")
     if "seq_lens" in override:
@@ -130,7 +137,8 @@ def config(i: int, **override) -> Workload:
         if "top_c" not in override:
             bud = [budget_for_length(L, override.get("n_sink", wl.n_sink),
                                      override.get("n_recent", wl.n_recent),
-                                     kappa=override.get("budget_kappa", wl.budget_kappa))
+                                     kappa=override.get("budget_kappa", wl.budget_kappa),
+                                     split=override.get("budget_split", wl.budget_split))
                    for L in override["seq_lens"]]
             override["top_c"] = [b[0] for b in bud]
             override["top_s"] = [b[1] for b in bud]

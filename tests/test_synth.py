@@ -14,10 +14,15 @@ def test_budgets_of_the_workloads():
     assert synth.budget_for_length(262144, 64, 256) == (90, 5)
     wl = synth.config(4)
     assert wl.n_seq == 16 and all(8192 <= L <= 262144 for L in wl.seq_lens)
-    # measured budgets of the workloads (mean per-head read share <= 5%)
-    assert synth.config(1).top_c == [8] and synth.config(3).top_c == [32]
-    assert synth.config(2).top_c == [18] * 4
+    # measured budgets of the workloads (mean per-head read share <= 5%),
+    # with the split of the lowest error against dense attention
+    assert (synth.config(1).top_c, synth.config(1).top_s) == ([4], [15])
+    assert (synth.config(3).top_c, synth.config(3).top_s) == ([17], [20])
+    assert (synth.config(2).top_c, synth.config(2).top_s) == ([38] * 4, [2] * 4)
     assert synth.budget_for_length(262144, 64, 256, kappa=0.35) == (31, 5)
+    # whole clusters: s = S; a fixed split is capped at S
+    assert synth.budget_for_length(262144, 64, 256, split="whole") == (25, 18)
+    assert synth.budget_for_length(4096, 4, 64, split=40)[1] == 12
 
 
 def test_generate_deterministic_and_shaped():
