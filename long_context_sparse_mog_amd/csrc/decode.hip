@@ -584,8 +584,8 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
 //      the cluster's exact tiles (runs of chosen subclusters cut into tiles
 //      of <= 32 rows) from its slot base, and accumulates the residual
 //      terms of the subclusters a choosing head left out;
-//    * block nb_chosen + y covers clusters [32y, 32y+32) (8 per wave, in
-//      two load batches of 4): the residual terms of every head that left a
+//    * block nb_chosen + y covers clusters [16y, 16y+16) (4 per wave, all
+//      loads at once): the residual terms of every head that left a
 //      cluster out.
 //    Every block writes one residual record per head (slot = block index).
 // ---------------------------------------------------------------------------
@@ -980,20 +980,18 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
         }
       }
     } else {
-      // RB clusters' loads at a time, so this path needs no more registers
-      // than the chosen-cluster path (at G = 1 all of them fit at once)
-      constexpr int RB = G == 1 ? RCW : RCW / 2;
+      // all RCW clusters' loads at once (an empty cluster scores -inf for
+      // every head, so its size is not needed)
+      constexpr int RB = RCW;
 #pragma unroll 1
       for (int k0 = 0; k0 < RCW; k0 += RB) {
         uint32_t mask[RB];
-        int n_g[RB];
         float vb[RB][VPL], sc[RB][G];
 #pragma unroll
         for (int k = 0; k < RB; ++k) {
           const int g = min(y * kRestClustersPerBlock + wave * RCW + k0 + k, C - 1);
           const int64_t cg = cw + g;
           mask[k] = a.ws.cl_mask[cg];
-          n_g[k] = off[(g + 1) * S] - off[g * S] + (a.L.fold_cap ? a.L.cl_fold[U.cl_base + g] : 0);
           load_floats<VPL>(a.L.cl_vbar + (U.cl_base + g) * D + lane * VPL, vb[k]);
 #pragma unroll
           for (int h = 0; h < G; ++h) sc[k][h] = a.ws.cl_score[((int64_t)u * G + h) * a.cstride + g];
@@ -1002,7 +1000,7 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
         for (int k = 0; k < RB; ++k) {
           const int g = y * kRestClustersPerBlock + wave * RCW + k0 + k;
           if (g >= C) break;
-          const uint32_t unchosen = n_g[k] > 0 ? (all & ~mask[k]) : 0u;
+          const uint32_t unchosen = sc[k][0] != -INFINITY ? (all & ~mask[k]) : 0u;
           if (unchosen && a.residual) {
 #pragma unroll
             for (int h = 0; h < G; ++h)
