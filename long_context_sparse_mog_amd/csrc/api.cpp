@@ -187,7 +187,7 @@ KVRef make_kvref(const mog_kv* kv) {
 // ------------------------------------------------------------------------
 struct DecodePlan {
   int G, c_stride, s_stride, splits, nblk, nb_res, nb_chosen;
-  size_t o_clscore, o_cllse, o_clmask, o_cltiles, o_clrank, o_urows, o_list, o_nch, o_uinfo, o_tbase, o_ntl, o_tiles, o_res, o_ex;
+  size_t o_clscore, o_cllse, o_clmask, o_cltiles, o_clrow0, o_chrow0, o_chnm, o_clrank, o_urows, o_list, o_nch, o_uinfo, o_tbase, o_ntl, o_tiles, o_res, o_ex;
   size_t o_fq, bytes;
 };
 
@@ -251,6 +251,9 @@ DecodePlan plan_decode(const mog_layout* L, const mog_decode_params* p) {
   d.o_cllse = o; o = align_up(o + (size_t)nu * G * 4);
   d.o_clmask = o; o = align_up(o + ncw * 4);
   d.o_cltiles = o; o = align_up(o + ncw * 4);
+  d.o_clrow0 = o; o = align_up(o + ncw * 4);
+  d.o_chrow0 = o; o = align_up(o + ncw * 4);
+  d.o_chnm = o; o = align_up(o + ncw * 4);
   d.o_clrank = o; o = align_up(o + ncw * G * 4);
   d.o_urows = o; o = align_up(o + (size_t)nu * 4);
   d.o_list = o; o = align_up(o + ncw * 4);
@@ -612,6 +615,14 @@ static mog_status decode_with_ws(const mog_layout* layout, const mog_kv* kv, con
   x.nblk = d.nblk;
   x.nb_res = d.nb_res;
   x.nb_chosen = d.nb_chosen;
+  // whole-cluster step: every chosen cluster is read entirely, so there are
+  // no subclusters to score or rank
+  x.whole = params->residual != 2 && layout->fold_capacity == 0 && sel_s == nullptr &&
+            d.nb_chosen <= kWaveListMax;
+  for (int s = 0; s < kv->n_seq && x.whole; ++s) {
+    const UnitSizes z = unit_sizes(layout->seq_lens[s] - layout->fold_count[s], layout->n_sink, layout->n_recent);
+    x.whole = x.seq.top_s[s] >= z.S;
+  }
   x.scale = scale;
   x.ev_begin = params->exact_begin;
   x.ev_end = params->exact_end;
@@ -622,6 +633,9 @@ static mog_status decode_with_ws(const mog_layout* layout, const mog_kv* kv, con
   x.ws.cl_lse = reinterpret_cast<float*>(w + d.o_cllse);
   x.ws.cl_mask = reinterpret_cast<uint32_t*>(w + d.o_clmask);
   x.ws.cl_tiles = reinterpret_cast<int32_t*>(w + d.o_cltiles);
+  x.ws.cl_row0 = reinterpret_cast<int32_t*>(w + d.o_clrow0);
+  x.ws.ch_row0 = reinterpret_cast<int32_t*>(w + d.o_chrow0);
+  x.ws.ch_nm = reinterpret_cast<uint32_t*>(w + d.o_chnm);
   x.ws.cl_rank = reinterpret_cast<int32_t*>(w + d.o_clrank);
   x.ws.unit_rows = reinterpret_cast<int32_t*>(w + d.o_urows);
   x.ws.cl_list = reinterpret_cast<int32_t*>(w + d.o_list);

@@ -59,6 +59,8 @@ struct DArgs {
   float sqrt_scale;  // feature-map residual: the map is applied to sqrt(scale) q
   int32_t score_blocks;  // blocks of the cluster-score kernel per unit that score clusters
   int32_t L_head_dim;
+  int32_t whole;          // whole-cluster step (top-c lists the tiles, no subcluster kernel)
+  int32_t rest_per_unit;  // residual blocks per unit: ceil(largest C / kRestClustersPerBlock)
   DecodeWS ws;
 };
 
@@ -240,8 +242,17 @@ __global__ __launch_bounds__(256) void k_score_clusters(DArgs a) {
     a.ws.cl_score[((int64_t)u * G + j % G) * a.cstride + g] = n > 0 ? t + log2f((float)n) : -INFINITY;
     // the most tile slots the cluster can need if chosen (one partial tile
     // per run, at most S runs, a folded row alone at worst), read by the
-    // top-c kernel with the scores
-    if (j % G == 0) a.ws.cl_tiles[(int64_t)u * a.cstride + g] = (nr + 31) / 32 + U.S + nf;
+    // top-c kernel with the scores; a whole-cluster step reads every row of
+    // a chosen cluster, one run: its size and first row instead
+    if (j % G == 0) {
+      const int64_t cg = (int64_t)u * a.cstride + g;
+      if (a.whole) {
+        a.ws.cl_tiles[cg] = nr;
+        a.ws.cl_row0[cg] = off[g * U.S];
+      } else {
+        a.ws.cl_tiles[cg] = (nr + 31) / 32 + U.S + nf;
+      }
+    }
   }
 }
 
@@ -256,8 +267,16 @@ __global__ __launch_bounds__(256) void k_score_clusters(DArgs a) {
 //    it and the lowest-index keys equal to it are chosen.  Empty clusters are
 //    never chosen.  The block then writes every cluster's head mask, the
 //    ascending list of clusters some head chose and their tile-slot bases
-//    (wave w takes the slots w, w + G, ...).  Grid (units), 64 G threads.
+//    (wave w takes the slots w, w + G, ...).  A whole-cluster step writes,
+//    in place of the list and the slot bases, each chosen cluster's first
+//    row and (rows | head mask << 24), which the exact kernel cuts into
+//    tiles, and the unit's exact row count, which the subcluster kernel
+//    writes otherwise.  Grid (units), 64 G threads.
 // ---------------------------------------------------------------------------
+// s_waitcnt immediate of "vmcnt(0)" on gfx9-family chips (vmcnt in bits 3:0
+// and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // bits 0..b set (b in [-1, 31])
 __device__ inline uint32_t mask_upto(int b) { return b >= 31 ? ~0u : ((1u << (b + 1)) - 1u); }
 
@@ -267,6 +286,7 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
   __shared__ int hist[G][256 + 64];       // 256 digit bins, then one spare bin per lane
   __shared__ unsigned long long selb[G][KPL];  // per head: chosen lanes of slot j
   __shared__ int slot_cnt[KPL], slot_tiles[KPL];
+  __shared__ int wave_rows[G];  // whole-cluster step: rows of each wave's chosen clusters
   __shared__ float gsum[64 * KPL];  // shared selection: summed mass fractions
   const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63, h = tid >> 6;
   const int want_raw = b.top_c[u / a.Hkv];
@@ -278,12 +298,16 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
   for (int j = 0; j < KPL; ++j) scv[j] = a.ws.cl_score[((int64_t)u * G + h) * a.cstride + min(64 * j + lane, a.cstride - 1)];
   // the tile-slot bounds of the clusters of this wave's tail slots (written
   // by the score kernel beside the scores)
-  int bound[NSW];
+  int bound[NSW], row0[NSW];
 #pragma unroll
-  for (int t = 0; t < NSW; ++t) bound[t] = a.ws.cl_tiles[cw + min(64 * (h + G * t) + lane, a.cstride - 1)];
+  for (int t = 0; t < NSW; ++t) {
+    const int64_t cg = cw + min(64 * (h + G * t) + lane, a.cstride - 1);
+    bound[t] = a.ws.cl_tiles[cg];
+    row0[t] = a.whole ? a.ws.cl_row0[cg] : 0;
+  }
   const mog_unit U = uni_unit(a.L.units + u);
   const int C = U.C;
-  if (tid == 0) a.ws.unit_rows[u] = 0;
+  if (tid == 0 && !a.whole) a.ws.unit_rows[u] = 0;  // the subcluster kernel adds to it
   if (a.shared) {
     // one selection per KV head: the key of a cluster is the sum over the
     // heads of the head's estimated mass fraction 2^(score - L_h), L_h the
@@ -486,6 +510,17 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
   const bool all_ties = cand == kk;
   const bool want_sel = a.sel_c != nullptr || a.sel_s != nullptr;
   int ties = 0, rank0 = 0;
+  if (all_ties && !want_sel) {
+    // (the usual case: no tie to rank and nothing to report) lane j keeps
+    // slot j's chosen lanes and writes them
+    unsigned long long mine = 0ull;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const unsigned long long sb = __ballot(c_eff > 0 && key[j] != 0u && (key[j] & hi_mask) >= prefix);
+      mine = lane == j ? sb : mine;
+    }
+    if (lane < KPL) selb[h][lane] = mine;
+  } else {
 #pragma unroll
   for (int j = 0; j < KPL; ++j) {
     const int i = 64 * j + lane;
@@ -511,6 +546,7 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
       rank0 += __popcll(sb);
     }
   }
+  }
   if (a.sel_c)
     for (int j = c_eff + lane; j < a.c_stride; j += 64) a.sel_c[row * a.c_stride + j] = -1;
   if (a.sel_s) {
@@ -519,11 +555,13 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
   }
   __syncthreads();
   // tail: cluster i = 64 j + lane.  A chosen cluster takes ceil(rows/32) + S
-  // + folded rows tile slots, the most its chosen subclusters can make.  First the
-  // per-slot counts, then each slot's list positions and slot bases from
-  // the counts of the slots before it.
+  // + folded rows tile slots, the most its chosen subclusters can make.
+  // First the per-slot counts, then each slot's list positions and slot
+  // bases from the counts of the slots before it (a whole-cluster step needs
+  // the positions only).
   uint32_t um[NSW];
   int tcnt[NSW], tinc[NSW];
+  int wrows = 0;
 #pragma unroll
   for (int t = 0; t < NSW; ++t) {
     const int j = h + G * t;
@@ -534,17 +572,30 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
 #pragma unroll
       for (int g = 0; g < G; ++g) um[t] |= (uint32_t)((selb[g][j] >> lane) & 1ull) << g;
       if (64 * j + lane >= C) um[t] = 0u;
-      tcnt[t] = um[t] != 0u ? bound[t] : 0;
       const int n = __popcll(__ballot(um[t] != 0u));
-      tinc[t] = wave_incl_scan(tcnt[t]);  // the slot's total in lane 63; the bases below
-      const int nt = __builtin_amdgcn_readlane(tinc[t], 63);
+      int nt = 0;
+      if (a.whole) {
+        wrows += um[t] != 0u ? bound[t] : 0;
+      } else {
+        tcnt[t] = um[t] != 0u ? bound[t] : 0;
+        tinc[t] = wave_incl_scan(tcnt[t]);  // the slot's total in lane 63; the bases below
+        nt = __builtin_amdgcn_readlane(tinc[t], 63);
+      }
       if (lane == 0) {
         slot_cnt[j] = n;
         slot_tiles[j] = nt;
       }
     }
   }
+  if (a.whole) {
+    wrows = (int)wave_reduce_uniform((uint32_t)wrows, [](uint32_t x, uint32_t y) { return x + y; }, 0u);
+    if (lane == 0) wave_rows[h] = wrows;
+  }
   __syncthreads();
+  // every load of the kernel has landed by now; waiting for them here, before
+  // the list and tile stores, keeps the uses below from waiting on those
+  // stores (the vector memory counter counts stores too)
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   // exclusive prefixes of the slots' counts (lane l: slot l), read per slot
   const int sc_l = lane < KPL ? slot_cnt[lane] : 0, st_l = lane < KPL ? slot_tiles[lane] : 0;
   const int sc_inc = wave_incl_scan(sc_l), st_inc = wave_incl_scan(st_l);
@@ -561,13 +612,25 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
       const int pos = pos0 + __popcll(__ballot(ch) & below);
       const int tb = tb0 + tinc[t] - tcnt[t];
       if (ch) {
-        a.ws.cl_list[cw + pos] = i;
-        a.ws.ch_tbase[cw + pos] = tb;
+        if (a.whole) {
+          a.ws.ch_row0[cw + pos] = row0[t];
+          a.ws.ch_nm[cw + pos] = (uint32_t)bound[t] | um[t] << 24;
+        } else {
+          a.ws.cl_list[cw + pos] = i;
+          a.ws.ch_tbase[cw + pos] = tb;
+        }
       }
     }
   }
   const int total = __builtin_amdgcn_readlane(sc_inc, 63);
-  if (h == 0 && lane == 0) a.ws.n_chosen[u] = total;
+  if (h == 0 && lane == 0) {
+    a.ws.n_chosen[u] = total;
+    if (a.whole) {
+      int rows = 0;
+      for (int w = 0; w < G; ++w) rows += wave_rows[w];
+      a.ws.unit_rows[u] = rows;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -606,6 +669,59 @@ __device__ inline void load_fz(const float* row, int FM, float (&z)[4]) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int k = 0; k < 4; ++k) z[k] = 64 * k < FM ? row[lane + 64 * k] : 0.f;
+}
+
+// Gaussian residual of clusters [16 y, 16 y + 16) of unit u: every head that
+// left a cluster out adds its term 2^score v-bar, 4 clusters per wave with
+// every load issued before any is used (clusters past C re-read the last one
+// and are skipped; an empty cluster scores -inf for every head, so its size
+// is not needed).
+template <int D, int G>
+__device__ inline void rest_clusters(const DArgs& a, int u, int C, int64_t cl_base, int y, float (&rm)[G],
+                                     float (&rl)[G], float (&ro)[G][D / 64]) {
+  constexpr int VPL = D / 64;
+  constexpr int RCW = kRestClustersPerBlock / 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t cw = (int64_t)u * a.cstride;
+  const uint32_t all = (1u << G) - 1u;
+  uint32_t mask[RCW];
+  float vb[RCW][VPL], sc[RCW][G];
+#pragma unroll
+  for (int k = 0; k < RCW; ++k) {
+    const int g = min(y * kRestClustersPerBlock + wave * RCW + k, C - 1);
+    mask[k] = a.ws.cl_mask[cw + g];
+    load_floats<VPL>(a.L.cl_vbar + (cl_base + g) * D + lane * VPL, vb[k]);
+#pragma unroll
+    for (int h = 0; h < G; ++h) sc[k][h] = a.ws.cl_score[((int64_t)u * G + h) * a.cstride + g];
+  }
+#pragma unroll
+  for (int k = 0; k < RCW; ++k) {
+    const int g = y * kRestClustersPerBlock + wave * RCW + k;
+    if (g >= C) break;
+    const uint32_t unchosen = sc[k][0] != -INFINITY ? (all & ~mask[k]) : 0u;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      if ((unchosen >> h) & 1u) add_group<VPL>(rm[h], rl[h], ro[h], sc[k][h], vb[k]);
+  }
+}
+
+// A wave's per-head states into rows wave * G + h of st (stride D + kPartPad),
+// as write_block_record reads them.
+template <int D, int G>
+__device__ inline void store_wave_states(float* st, const float (&rm)[G], const float (&rl)[G],
+                                         const float (&ro)[G][D / 64]) {
+  constexpr int VPL = D / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float* r = st + (wave * G + h) * (D + kPartPad);
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) r[lane * VPL + e] = ro[h][e];
+    if (lane == 0) {
+      r[D] = rm[h];
+      r[D + 1] = rl[h];
+    }
+  }
 }
 
 template <int D, int G>
@@ -979,47 +1095,12 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
           }
         }
       }
-    } else {
-      // all RCW clusters' loads at once (an empty cluster scores -inf for
-      // every head, so its size is not needed)
-      constexpr int RB = RCW;
-#pragma unroll 1
-      for (int k0 = 0; k0 < RCW; k0 += RB) {
-        uint32_t mask[RB];
-        float vb[RB][VPL], sc[RB][G];
-#pragma unroll
-        for (int k = 0; k < RB; ++k) {
-          const int g = min(y * kRestClustersPerBlock + wave * RCW + k0 + k, C - 1);
-          const int64_t cg = cw + g;
-          mask[k] = a.ws.cl_mask[cg];
-          load_floats<VPL>(a.L.cl_vbar + (U.cl_base + g) * D + lane * VPL, vb[k]);
-#pragma unroll
-          for (int h = 0; h < G; ++h) sc[k][h] = a.ws.cl_score[((int64_t)u * G + h) * a.cstride + g];
-        }
-#pragma unroll
-        for (int k = 0; k < RB; ++k) {
-          const int g = y * kRestClustersPerBlock + wave * RCW + k0 + k;
-          if (g >= C) break;
-          const uint32_t unchosen = sc[k][0] != -INFINITY ? (all & ~mask[k]) : 0u;
-          if (unchosen && a.residual) {
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-              if ((unchosen >> h) & 1u) add_group<VPL>(rm[h], rl[h], ro[h], sc[k][h], vb[k]);
-          }
-        }
-      }
+    } else if (a.residual) {
+      rest_clusters<D, G>(a, u, C, U.cl_base, y, rm, rl, ro);
     }
   }
 
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-#pragma unroll
-    for (int e = 0; e < VPL; ++e) st[wave][h][lane * VPL + e] = ro[h][e];
-    if (lane == 0) {
-      st[wave][h][D] = rm[h];
-      st[wave][h][D + 1] = rl[h];
-    }
-  }
+  store_wave_states<D, G>(&st[0][0][0], rm, rl, ro);
   __syncthreads();
   write_block_record<D, G>(&st[0][0][0], dst);
 }
@@ -1090,7 +1171,6 @@ struct TileDesc {
 };
 
 constexpr int kTileBatch = 64;  // tiles listed per wave before streaming them
-constexpr int kWaveListMax = 256;  // chosen clusters a wave scans on its own (4 per lane)
 
 template <int D, int G, typename Engine, typename T>
 __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
@@ -1102,14 +1182,39 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
   constexpr bool ALIAS = sizeof(u32x4) * 4 * Engine::BUF >= sizeof(float) * ST;
   __shared__ float st_own[ALIAS ? 1 : ST];
   float* st = ALIAS ? reinterpret_cast<float*>(&kvbuf[0][0]) : st_own;
-  __shared__ int tpre[kMaxC + 1];  // exclusive prefix of the chosen clusters' tile counts
-  __shared__ int tbs[kMaxC];       // their tile-slot bases
-  __shared__ int wtpre[4][kWaveListMax + 1];  // the same per wave, for lists of up to 256
-  __shared__ int wtbs[4][kWaveListMax];
+  // the chosen clusters in list order, for the tile listing: the block's
+  // (lists longer than kWaveListMax: exclusive prefix of the tile counts,
+  // then tile-slot bases) or each wave's own copy (prefix | slot bases, or a
+  // whole-cluster step's first rows | its rows and head masks)
+  constexpr int kBlockList = 2 * kMaxC + 1, kWaveList = 3 * kWaveListMax + 1;
+  __shared__ int lists[kBlockList > 4 * kWaveList ? kBlockList : 4 * kWaveList];
   __shared__ int sh[16];
   __shared__ TileRec tiles[4][kTileBatch];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  if ((int)blockIdx.x >= a.nblk) {
+    // whole-cluster step: the Gaussian residual of the clusters some head
+    // left out, in blocks after the exact ones (dispatched as exact blocks
+    // retire); record y of unit u covers clusters [16 y, 16 y + 16)
+    const int r = (int)blockIdx.x - a.nblk;
+    const int u = r / a.rest_per_unit, y = r % a.rest_per_unit;
+    const mog_unit U = uni_unit(a.L.units + u);
+    if (y * kRestClustersPerBlock >= U.C) return;
+    constexpr int VPL = D / 64;
+    float rm[G], rl[G], ro[G][VPL];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      rm[h] = -INFINITY;
+      rl[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) ro[h][e] = 0.f;
+    }
+    rest_clusters<D, G>(a, u, U.C, U.cl_base, y, rm, rl, ro);
+    store_wave_states<D, G>(st, rm, rl, ro);
+    __syncthreads();
+    write_block_record<D, G>(st, a.ws.res_part + ((int64_t)u * a.nb_res + y) * G * RS);
+    return;
+  }
   const int A = a.n_sink + a.n_recent;
   const BlockShare bs = wave_find_share(a.ws.unit_rows, a.n_units, a.nblk, A, blockIdx.x);
   const int u = bs.u;
@@ -1131,27 +1236,35 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
   // per thread.
   const int64_t cw = (int64_t)u * a.cstride;
   const int n_ch_raw = a.ws.n_chosen[u];
+  // (a whole-cluster step: rows | head mask << 24 and first rows)
+  const int32_t* la = a.whole ? reinterpret_cast<const int32_t*>(a.ws.ch_nm) : a.ws.ch_ntiles;
+  const int32_t* lb = a.whole ? a.ws.ch_row0 : a.ws.ch_tbase;
   int wl[4], wt[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int x = min(4 * lane + k, a.cstride - 1);
-    wl[k] = a.ws.ch_ntiles[cw + x];
-    wt[k] = a.ws.ch_tbase[cw + x];
+    wl[k] = la[cw + x];
+    wt[k] = lb[cw + x];
   }
   // (unit u is sequence u / Hkv, KV head u % Hkv: the query's address does
   // not wait for the unit record)
   acc.init(a.q + ((int64_t)(u / a.Hkv) * a.Hq + (int64_t)(u % a.Hkv) * G) * D, a.scale_l2, buf);
-  const int n_ch = uni(n_ch_raw);
-  const int* tp = tpre;  // the prefix the listing searches, and the slot bases
-  const int* tb = tbs;
+  // (a whole-cluster step has at most kWaveListMax chosen clusters; the
+  // clamp only keeps every list access in range)
+  const int n_ch = a.whole ? min(uni(n_ch_raw), kWaveListMax) : uni(n_ch_raw);
+  const int* tp = lists;  // the prefix the listing searches, and the slot bases (or first rows)
+  const int* tb = lists + kMaxC + 1;
+  const int* tn = nullptr;  // a whole-cluster step's rows | head masks
   if (n_ch <= kWaveListMax) {
-    int* wp = wtpre[wave];
-    int* wb = wtbs[wave];
-    int sum = 0;
+    int* wp = lists + wave * kWaveList;
+    int* wb = wp + kWaveListMax + 1;
+    int* wn = wb + kWaveListMax;
+    int cnt[4], sum = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      wl[k] = 4 * lane + k < n_ch ? wl[k] : 0;
-      sum += wl[k];
+      const bool in = 4 * lane + k < n_ch;
+      cnt[k] = !in ? 0 : a.whole ? (int)((((uint32_t)wl[k] & 0xffffffu) + 31u) >> 5) : wl[k];
+      sum += cnt[k];
     }
     const int incl = wave_incl_scan(sum);
     int base = incl - sum;
@@ -1160,14 +1273,18 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
       if (4 * lane + k < n_ch) {
         wp[4 * lane + k] = base;
         wb[4 * lane + k] = wt[k];
+        if (a.whole) wn[4 * lane + k] = wl[k];
       }
-      base += wl[k];
+      base += cnt[k];
     }
     if (lane == 63) wp[n_ch] = incl;
     __asm__ volatile("" ::: "memory");  // (a wave's LDS operations run in order)
     tp = wp;
     tb = wb;
+    tn = wn;
   } else {
+    int* tpre = lists;
+    int* tbs = lists + kMaxC + 1;
     constexpr int EM = kMaxC / 256;
     const int E = (n_ch + 255) / 256;
     int loc[EM], tbl[EM];
@@ -1253,7 +1370,15 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
             const int mid = (lo + hi) >> 1;
             if (tp[mid] <= kv_) lo = mid; else hi = mid;
           }
-          r = utiles[tb[lo] + (kv_ - tp[lo])];
+          const int jt = kv_ - tp[lo];
+          if (a.whole) {
+            // tile jt of a whole cluster: its rows from the first, 32 at a time
+            const uint32_t nm = (uint32_t)tn[lo];
+            r = TileRec{(U.row_base + tb[lo] + 32 * jt) * (int64_t)D, min(32, (int)(nm & 0xffffffu) - 32 * jt),
+                        nm >> 24};
+          } else {
+            r = utiles[tb[lo] + jt];
+          }
         }
         tl[lane] = r;
       }
@@ -1339,10 +1464,11 @@ __global__ __launch_bounds__(1024) void k_merge(const float* part, int n_part, c
   }
   const int64_t stride = (int64_t)G * RS;
   const float* eb = part + (first * G + h) * RS;
-  // residual records of the unit: one per chosen cluster, then one per
-  // kRestClustersPerBlock clusters
+  // residual records of the unit: one per chosen cluster (none without
+  // n_chosen: a whole-cluster step leaves nothing out of a chosen cluster),
+  // then one per kRestClustersPerBlock clusters
   int n_res = 0;
-  if (res) n_res = n_chosen[u] + (units[u].C + kRestClustersPerBlock - 1) / kRestClustersPerBlock;
+  if (res) n_res = (n_chosen ? n_chosen[u] : 0) + (units[u].C + kRestClustersPerBlock - 1) / kRestClustersPerBlock;
   const float* rb = res ? res + ((int64_t)u * res_stride * G + h) * RS : nullptr;
   const int total = n_part + (res ? n_res : 0);
   const int q = tid % QL, grp = tid / QL;
@@ -1487,21 +1613,25 @@ static hipError_t decode_impl(const DecodeLaunch& x, const DArgs& a, const Budge
     hipLaunchKernelGGL((k_select_topc<G, 16>), dim3(nu), dim3(64 * G), 0, s, a, b);
   else
     hipLaunchKernelGGL((k_select_topc<G, kMaxC / 64>), dim3(nu), dim3(64 * G), 0, s, a, b);
-  hipLaunchKernelGGL((k_subclusters<D, G>), dim3(nu, x.nb_res), dim3(256), 0, s, a, b, x.nb_chosen);
+  if (!x.whole) hipLaunchKernelGGL((k_subclusters<D, G>), dim3(nu, x.nb_res), dim3(256), 0, s, a, b, x.nb_chosen);
+  // a whole-cluster step's residual blocks follow the exact blocks
+  const int nrest = x.whole && x.residual ? nu * a.rest_per_unit : 0;
   // the timing events (if any) are taken by the dispatches themselves: the
   // start of the first exact launch and the end of the last
   for (int r = 0; r < x.repeat; ++r) {
     hipEvent_t e0 = r == 0 ? x.ev_begin : nullptr, e1 = r + 1 == x.repeat ? x.ev_end : nullptr;
     if (x.dtype == MOG_BF16) {
-      hipExtLaunchKernelGGL((k_exact<D, G, MfmaTile<D, G>, uint16_t>), dim3(x.nblk), dim3(256), 0, s, e0, e1, 0, a);
+      hipExtLaunchKernelGGL((k_exact<D, G, MfmaTile<D, G>, uint16_t>), dim3(x.nblk + nrest), dim3(256), 0, s, e0,
+                            e1, 0, a);
     } else {
-      hipExtLaunchKernelGGL((k_exact<D, G, RowAcc<D, G>, float>), dim3(x.nblk), dim3(256), 0, s, e0, e1, 0, a);
+      hipExtLaunchKernelGGL((k_exact<D, G, RowAcc<D, G>, float>), dim3(x.nblk + nrest), dim3(256), 0, s, e0, e1, 0,
+                            a);
     }
   }
   hipLaunchKernelGGL((k_merge<D>), dim3(x.Hq, x.L.n_seq), dim3(1024), 0, s, a.ws.ex_part, 0,
                      (const int32_t*)a.ws.uinfo, x.residual ? (const float*)a.ws.res_part : nullptr, x.nb_res,
-                     (const int32_t*)a.ws.n_chosen, (const mog_unit*)x.L.units, G, x.Hq, x.L.n_kv_heads, x.out,
-                     x.lse);
+                     x.whole ? nullptr : (const int32_t*)a.ws.n_chosen, (const mog_unit*)x.L.units, G, x.Hq,
+                     x.L.n_kv_heads, x.out, x.lse);
   return hipGetLastError();
 }
 
@@ -1563,6 +1693,8 @@ hipError_t launch_decode(const DecodeLaunch& x, hipStream_t s) {
   a.scale_l2 = x.scale * kLog2e;
   a.half_s2_l2 = 0.5f * x.scale * x.scale * kLog2e;
   a.L_head_dim = x.D;
+  a.whole = x.whole;
+  a.rest_per_unit = (x.L.max_C + kRestClustersPerBlock - 1) / kRestClustersPerBlock;
   a.ws = x.ws;
   BudgetArgs b;
   for (int i = 0; i < MOG_MAX_SEQ; ++i) {

@@ -14,6 +14,7 @@ constexpr int kWave = 64;
 constexpr int kMaxG = 8;        // query heads per KV head
 constexpr int kMaxS = 32;       // subclusters per cluster (N <= 2^22 gives S <= 22)
 constexpr int kMaxC = 2048;     // clusters per unit (N <= 2^22 gives C <= 2048)
+constexpr int kWaveListMax = 256;  // chosen clusters per unit an exact wave lists on its own (4 per lane)
 // subcluster rows the decode kernels hold per cluster: S = ceil(log2 n) <= 22
 // for n <= 2^22, rounded up to a multiple of 4 (one row per wave and step)
 constexpr int kDecodeSubRows = 24;
@@ -117,6 +118,8 @@ struct DecodeWS {
   float* cl_lse;        // [n_units][G]          shared selection: log2 of each head's total estimated mass
   uint32_t* cl_mask;    // [n_units * max_C]     heads that chose the cluster
   int32_t* cl_tiles;    // [n_units * max_C]     tile slots the cluster needs at most if chosen
+                        //                       (whole-cluster steps: its reordered rows)
+  int32_t* cl_row0;     // [n_units * max_C]     whole-cluster steps: the cluster's first row in the unit
   int32_t* cl_rank;     // [n_units * max_C][G]  rank among a head's chosen clusters, or -1
                         //                       (written only when sel_s is requested)
   int32_t* unit_rows;   // [n_units]             rows of chosen subclusters per unit
@@ -125,6 +128,9 @@ struct DecodeWS {
   int32_t* uinfo;       // [n_units][2]          first exact block of the unit, its blocks
   int32_t* ch_tbase;    // [n_units * max_C]     per unit: tile-slot base of the x-th chosen cluster
   int32_t* ch_ntiles;   // [n_units * max_C]     per unit: tiles of the x-th chosen cluster
+  int32_t* ch_row0;     // [n_units * max_C]     whole-cluster steps, per unit: first row of the x-th
+                        //                       chosen cluster in the unit
+  uint32_t* ch_nm;      // [n_units * max_C]     whole-cluster steps: its rows | head mask << 24
   TileRec* tiles;       // [tile slots]          exact tiles, per unit at tile_unit_base()
   float* res_part;      // [n_units][nb_res][G][D+4] residual partials: one per chosen
                         //                       cluster, then one per rest block
@@ -149,6 +155,12 @@ struct DecodeLaunch {
   int32_t nblk;         // exact blocks launched: splits + n_units
   int32_t nb_res;       // residual record slots per unit: nb_chosen + max_C / kRestClustersPerBlock
   int32_t nb_chosen;    // chosen-cluster blocks per unit (max G * top_c)
+  int32_t whole;        // whole-cluster step: every sequence's top_s reaches its S, no folded
+                        // rows, Gaussian residual or none, no subcluster output, at most
+                        // kWaveListMax chosen clusters per unit.  The top-c kernel writes each
+                        // chosen cluster's rows and head mask, the exact kernel cuts them into
+                        // tiles, the residual of the clusters left out runs in blocks after the
+                        // exact ones, and the subcluster kernel is skipped.
   float scale;
   hipEvent_t ev_begin, ev_end;  // optional, around the exact kernel
   int32_t repeat;               // exact-kernel launches between the events (>= 1)

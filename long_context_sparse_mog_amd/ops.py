@@ -318,7 +318,12 @@ def mog_append(layout: Layout, kv: KVCache, stream=None) -> None:
 
 def mog_decode(layout: Layout, kv: KVCache, q, params, out=None, lse=None, want_sel=False,
                ws=None, stream=None):
-    """One decode step.  Returns (out, lse, sel_c, sel_s)."""
+    """One decode step.  Returns (out, lse, sel_c, sel_s).
+
+    ``want_sel``: False (no selection output), True (chosen clusters and
+    subclusters) or ``"c"`` (chosen clusters only).  Asking for the
+    subclusters always runs the subcluster kernel; without them a budget of
+    whole clusters (top_s >= S everywhere) skips it."""
     _require_cuda(q)
     if q.dtype != torch.float32 or not q.is_contiguous():
         raise ValueError("q must be contiguous float32 [n_seq][Hq][D]")
@@ -333,8 +338,9 @@ def mog_decode(layout: Layout, kv: KVCache, q, params, out=None, lse=None, want_
         ss = [params.top_s_per_seq[i] for i in range(n_seq)] if params.top_s_per_seq else [params.top_s]
         cmax, smax = max(cs), max(ss)
         sel_c = torch.full((n_seq, Hq, max(cmax, 1)), -1, dtype=torch.int32, device=q.device)
-        sel_s = torch.full((n_seq, Hq, max(cmax, 1), max(smax, 1)), -1, dtype=torch.int32,
-                           device=q.device)
+        if want_sel != "c":
+            sel_s = torch.full((n_seq, Hq, max(cmax, 1), max(smax, 1)), -1, dtype=torch.int32,
+                               device=q.device)
     need = mog_workspace_size(capi.MOG_OP_DECODE, layout=layout, params=params)
     if ws is None or ws.numel() < need:
         ws = workspace(need, q.device)

@@ -94,8 +94,14 @@ def compare_unit(L, K, V, Q, c, s, gpu_out, gpu_lse, gpu_sel_c, gpu_sel_s, tol, 
     # residual: False, True (Gaussian) or "fm" (feature map)
     """Compare one unit's GPU results with the oracle's.  Returns a dict of
     the errors; raises AssertionError on a selection mismatch that is not a
-    near tie.  ``shared``: one selection per KV head (oracle reading R14)."""
+    near tie.  ``shared``: one selection per KV head (oracle reading R14).
+    ``gpu_sel_s`` None: a budget of whole clusters (s >= S), whose chosen
+    subclusters are every nonempty one of each chosen cluster."""
     G, d = Q.shape
+    if gpu_sel_s is None:
+        assert s >= L.S, (s, L.S)
+        gpu_sel_s = [[np.flatnonzero(L.sub_count[int(j) * L.S:(int(j) + 1) * L.S] > 0) if j >= 0 else []
+                      for j in gpu_sel_c[h]] for h in range(G)]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     fmr = residual == "fm"
     ref = O.decode_unit(L, K, V, Q, c, s, scale=scale, residual=bool(residual), shared=shared,

@@ -29,9 +29,14 @@ def tol_of(wl):
     return 1e-5 if wl.dtype == "fp32" else 2e-3
 
 
-def run_decode_case(wl, residual=True, top_c=None, top_s=None, qset=0, n_qsets=1, splits=0, shared=False):
+def run_decode_case(wl, residual=True, top_c=None, top_s=None, qset=0, n_qsets=1, splits=0, shared=False,
+                    sel=True, zero_q=False):
+    # sel: True asks for the chosen clusters and subclusters (the subcluster
+    # kernel runs), "c" for the clusters only (a whole-cluster budget then
+    # skips it)
     say(f"[case] {wl.name} lens={wl.seq_lens} Hq={wl.n_q_heads} Hkv={wl.n_kv_heads} "
-        f"D={wl.head_dim} {wl.dtype} c={top_c or wl.top_c} s={top_s or wl.top_s} res={residual} shared={shared}")
+        f"D={wl.head_dim} {wl.dtype} c={top_c or wl.top_c} s={top_s or wl.top_s} res={residual} shared={shared} "
+        f"sel={sel}")
     b = synth.generate(wl, device="cuda", n_qsets=n_qsets)
     kv = ops.KVCache.from_batch(b)
     lays = build_oracle_layouts(b)
@@ -41,10 +46,13 @@ def run_decode_case(wl, residual=True, top_c=None, top_s=None, qset=0, n_qsets=1
     ts = top_s if top_s is not None else wl.top_s
     params = ops.decode_params(wl.n_q_heads, list(tc), list(ts), residual=residual, splits=splits, shared=shared)
     q = b.Q[qset].contiguous()
-    out, lse, sel_c, sel_s = ops.mog_decode(lay, kv, q, params, want_sel=True)
+    if zero_q:
+        q.zero_()
+    out, lse, sel_c, sel_s = ops.mog_decode(lay, kv, q, params, want_sel=sel)
     torch.cuda.synchronize()
     out, lse = out.cpu().numpy(), lse.cpu().numpy()
-    sel_c, sel_s = sel_c.cpu().numpy(), sel_s.cpu().numpy()
+    sel_c = sel_c.cpu().numpy()
+    sel_s = sel_s.cpu().numpy() if sel_s is not None else None
     G = wl.group
     worst = 0.0
     for s in range(wl.n_seq):
@@ -54,7 +62,8 @@ def run_decode_case(wl, residual=True, top_c=None, top_s=None, qset=0, n_qsets=1
             Q = q[s, h * G:(h + 1) * G].cpu().numpy().astype(np.float64)
             hs = slice(h * G, (h + 1) * G)
             r = compare_unit(lays[u], K, V, Q, tc[s], ts[s], out[s, hs], lse[s, hs], sel_c[s, hs],
-                             sel_s[s, hs], tol_of(wl), residual=residual, shared=shared)
+                             None if sel_s is None else sel_s[s, hs], tol_of(wl), residual=residual,
+                             shared=shared)
             assert r["lse_err"] < (1e-5 if wl.dtype == "fp32" else 1e-3) * max(1.0, float(np.abs(lse[s, hs]).max()))
             worst = max(worst, r["max_rel"])
     say(f"  worst per-head rel L2 = {worst:.3e}")
@@ -164,6 +173,80 @@ def test_exact_ties_go_to_lower_index(c):
             assert gs == [int(x) for x in ref["sel_s"][h][r]], (h, r, gs, ref["sel_s"][h][r])
     o, _ = O.dense_attention(K, V, np.zeros((G, D)))
     say(f"  {len(gc)} clusters chosen; rel L2 vs dense {rel_l2(out[0].cpu().numpy(), o):.2e}")
+
+
+# ---------------------------------------------------------------------------
+# whole-cluster budgets (top_s >= S) without the subcluster output: the top-c
+# kernel lists the chosen clusters' tiles, the residual of the clusters left
+# out runs in blocks after the exact ones, and no subcluster kernel runs
+# ---------------------------------------------------------------------------
+WHOLE = {
+    "cfg1r": lambda: synth.config(1, seq_lens=[8192], n_kv_heads=2, n_q_heads=8, n_components=64),
+    "cfg3r": lambda: synth.config(3, seq_lens=[12000], n_kv_heads=2, n_q_heads=10, n_components=128),
+    "cfg4r-paged": lambda: synth.config(4, seq_lens=[3000, 9000, 1000], n_kv_heads=2, n_q_heads=8,
+                                        high_entropy_heads=(1,), n_components=64),
+    "fp32": lambda: synth.config(1, seq_lens=[5000], n_kv_heads=1, n_q_heads=4, n_components=32, dtype="fp32"),
+    "d64": lambda: synth.config(1, seq_lens=[4000], n_kv_heads=2, n_q_heads=4, head_dim=64, n_components=32),
+}
+
+
+@pytest.mark.parametrize("name", list(WHOLE))
+def test_whole_cluster_path(name):
+    wl = WHOLE[name]()
+    assert all(s >= math.ceil(math.log2(L)) for s, L in zip(wl.top_s, wl.seq_lens))
+    run_decode_case(wl, sel="c")
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 6, 7, 8])
+def test_whole_cluster_group_sizes(G):
+    run_decode_case(synth.config(1, seq_lens=[3000], n_kv_heads=1, n_q_heads=G, n_components=32), sel="c")
+
+
+def test_whole_cluster_top_only_and_shared():
+    run_decode_case(WHOLE["cfg1r"](), residual=False, sel="c")
+    run_decode_case(WHOLE["cfg3r"](), shared=True, sel="c")
+
+
+def test_whole_cluster_splits():
+    run_decode_case(WHOLE["fp32"](), splits=1, sel="c")
+    run_decode_case(WHOLE["fp32"](), splits=37, sel="c")
+
+
+def test_whole_cluster_edges():
+    # no cluster chosen (only anchors and the residual), and a budget above
+    # the partition (every cluster whole: dense attention)
+    run_decode_case(synth.config(0), top_c=[0], top_s=[12], sel="c")
+    wl = synth.config(1, seq_lens=[1500], n_kv_heads=1, n_q_heads=2, n_components=16, top_c=[500], top_s=[100])
+    b, kv, lays, out = run_decode_case(wl, sel="c")
+    K, V = b.unit_kv(0, 0)
+    o, _ = O.dense_attention(K, V, b.Q[0, 0].cpu().numpy())
+    assert rel_l2(out[0], o) < 2e-3
+
+
+def test_whole_cluster_zero_query_ties():
+    # every score is a log count: equal-size clusters tie exactly
+    wl = synth.config(1, seq_lens=[20000], n_kv_heads=1, n_q_heads=2, n_components=64, top_c=[40], top_s=[15])
+    run_decode_case(wl, sel="c", zero_q=True)
+
+
+@pytest.mark.parametrize("name", ["cfg3r", "cfg4r-paged"])
+def test_whole_and_subcluster_paths_agree(name):
+    """The two paths list the same exact tiles in the same order (bit-equal
+    exact records) and sum the same residual terms in another order."""
+    wl = WHOLE[name]()
+    b = synth.generate(wl, device="cuda")
+    kv = ops.KVCache.from_batch(b)
+    lay = ops.mog_build(kv, wl.n_sink, wl.n_recent, kmeans_iters=wl.kmeans_iters, seed=1)
+    params = ops.decode_params(wl.n_q_heads, list(wl.top_c), list(wl.top_s))
+    q = b.Q[0].contiguous()
+    ow, lw, cw, _ = ops.mog_decode(lay, kv, q, params, want_sel="c")
+    os_, ls_, cs, ss = ops.mog_decode(lay, kv, q, params, want_sel=True)
+    torch.cuda.synchronize()
+    assert torch.equal(cw, cs)
+    d = ((ow - os_).norm(dim=-1) / os_.norm(dim=-1)).max().item()
+    say(f"[paths] {name}: max per-head rel difference {d:.2e}, lse {(lw - ls_).abs().max().item():.2e}")
+    assert d < 1e-5
+    assert torch.allclose(lw, ls_, rtol=0, atol=1e-5 * max(1.0, ls_.abs().max().item()))
 
 
 # ---------------------------------------------------------------------------

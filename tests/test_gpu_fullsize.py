@@ -25,21 +25,31 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_fullsize(wl, units, qset=0, shared=False, check_build=()):
+def run_fullsize(wl, units, qset=0, shared=False, check_build=(), sels=None):
     """``check_build``: units whose built layout is also checked (a valid
     partition in (cluster, subcluster, position) order, and every statistic
-    equal to the oracle's statistic of that partition)."""
+    equal to the oracle's statistic of that partition).  ``sels``: the
+    selection outputs asked for, one decode each on the same layout: "c"
+    (the chosen clusters; with a whole-cluster budget this is the path the
+    benchmark times, no subcluster kernel) or True (clusters and
+    subclusters: the subcluster kernel always runs).  Default: "c" for a
+    whole-cluster budget, else True."""
     say(f"[full] {wl.name} n_seq={wl.n_seq} Hq={wl.n_q_heads} Hkv={wl.n_kv_heads} "
-        f"max_len={wl.max_len} units={units} build-checked={list(check_build)}")
+        f"max_len={wl.max_len} units={units} build-checked={list(check_build)} sels={sels}")
     b = synth.generate(wl, device="cuda", n_qsets=qset + 1)
     kv = ops.KVCache.from_batch(b)
     lay = ops.mog_build(kv, wl.n_sink, wl.n_recent, kmeans_iters=wl.kmeans_iters, seed=1)
     params = ops.decode_params(wl.n_q_heads, list(wl.top_c), list(wl.top_s), shared=shared)
+    if sels is None:
+        whole = all(wl.top_s[s] >= lay.unit(s * wl.n_kv_heads).S for s in range(wl.n_seq))
+        sels = ("c",) if whole else (True,)
     q = b.Q[qset].contiguous()
-    out, lse, sel_c, sel_s = ops.mog_decode(lay, kv, q, params, want_sel=True)
-    torch.cuda.synchronize()
-    out, lse = out.cpu().numpy(), lse.cpu().numpy()
-    sel_c, sel_s = sel_c.cpu().numpy(), sel_s.cpu().numpy()
+    runs = []
+    for sel in sels:
+        out, lse, sel_c, sel_s = ops.mog_decode(lay, kv, q, params, want_sel=sel)
+        torch.cuda.synchronize()
+        runs.append((sel, out.cpu().numpy(), lse.cpu().numpy(), sel_c.cpu().numpy(),
+                     None if sel_s is None else sel_s.cpu().numpy()))
     G = wl.group
     for u in units:
         s, h = divmod(u, wl.n_kv_heads)
@@ -52,11 +62,12 @@ def run_fullsize(wl, units, qset=0, shared=False, check_build=()):
             say(f"  unit {u}: built layout and statistics match the oracle's for its partition")
         Q = q[s, h * G:(h + 1) * G].cpu().numpy().astype(np.float64)
         hs = slice(h * G, (h + 1) * G)
-        r = compare_unit(L, K, V, Q, wl.top_c[s], wl.top_s[s], out[s, hs], lse[s, hs], sel_c[s, hs],
-                         sel_s[s, hs], 2e-3, shared=shared)
-        assert r["lse_err"] < 1e-3 * max(1.0, float(np.abs(lse[s, hs]).max()))
-        say(f"  unit {u} (seq {s}, len {wl.seq_lens[s]}, kv head {h}): worst rel L2 {r['max_rel']:.2e}, "
-            f"near ties {r['ties']}")
+        for sel, out, lse, sel_c, sel_s in runs:
+            r = compare_unit(L, K, V, Q, wl.top_c[s], wl.top_s[s], out[s, hs], lse[s, hs], sel_c[s, hs],
+                             None if sel_s is None else sel_s[s, hs], 2e-3, shared=shared)
+            assert r["lse_err"] < 1e-3 * max(1.0, float(np.abs(lse[s, hs]).max()))
+            say(f"  unit {u} (seq {s}, len {wl.seq_lens[s]}, kv head {h}, sel {sel}): worst rel L2 "
+                f"{r['max_rel']:.2e}, near ties {r['ties']}")
         del K, V
     del b, kv, lay
     torch.cuda.empty_cache()
@@ -67,7 +78,7 @@ def test_fullsize_gqa_32k_all_units():
 
 
 def test_fullsize_gqa_1m_shared_selection_sampled():
-    run_fullsize(synth.config(3), [2, 5], qset=1, shared=True)
+    run_fullsize(synth.config(3), [2, 5], qset=1, shared=True, sels=(True,))
 
 
 def test_fullsize_mha_128k_sampled():
@@ -121,7 +132,7 @@ def test_maximum_length_single_head():
     L = 1 << 22
     wl = synth.config(3, n_q_heads=4, n_kv_heads=1, seq_lens=[L], n_components=2048,
                       name="gqa-4q1kv-d128-4M-bf16", budget_kappa=34 / 203)
-    run_fullsize(wl, [0])
+    run_fullsize(wl, [0], sels=("c", True))
 
 
 def test_fullsize_gqa_1m_incremental_sampled():
