@@ -244,6 +244,13 @@ struct MfmaTile {
     return r < nrows ? r : nrows - 1;
   }
 
+  // Cache policy of the K/V stream loads: non-temporal (bit 1 of the buffer
+  // instruction's cache-policy operand, "nt" on gfx94x/gfx950).  Each row is
+  // read once per step, and without the hint the stream displaces the decode
+  // kernels' code and their small per-unit arrays from the L2 every step, so
+  // the short kernels of the next step start cold.
+  static constexpr int kStreamPolicy = 2;
+
   // Raw buffer resource over `bytes` bytes at p: a lane whose offset is at
   // or past `bytes` reads zeros and touches no memory.
   __device__ static __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
@@ -272,11 +279,11 @@ struct MfmaTile {
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        kr[NC * t + c] = __builtin_amdgcn_raw_buffer_load_b128(rk, kb, t * 16 * (D * 2) + c * 64, 0);
+        kr[NC * t + c] = __builtin_amdgcn_raw_buffer_load_b128(rk, kb, t * 16 * (D * 2) + c * 64, kStreamPolicy);
     }
     const int vb = (lane / PPR) * (D * 2) + (lane % PPR) * 16;
 #pragma unroll
-    for (int i = 0; i < NLI; ++i) vr[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vb, i * RPI * (D * 2), 0);
+    for (int i = 0; i < NLI; ++i) vr[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vb, i * RPI * (D * 2), kStreamPolicy);
   }
 
   // Contiguous rows: row i of the tile at kp + i*D (elements).
@@ -298,13 +305,14 @@ struct MfmaTile {
       const int r = 16 * t + (lane & 15);
       const int64_t off = rowoff(r < nrows ? r : nrows - 1) + (lane >> 4) * 8;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) kr[NC * t + c] = *reinterpret_cast<const u32x4*>(kb + off + 32 * c);
+      for (int c = 0; c < NC; ++c)
+        kr[NC * t + c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + off + 32 * c));
     }
 #pragma unroll
     for (int i = 0; i < NLI; ++i) {
       const int r = lane / PPR + RPI * i;
       const int64_t off = rowoff(r < nrows ? r : nrows - 1) + (lane % PPR) * 8;
-      vr[i] = *reinterpret_cast<const u32x4*>(vb + off);
+      vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + off));  // (the stream policy)
     }
     compute(buf, kr, vr, nrows, mask);
   }
