@@ -132,17 +132,21 @@ __device__ inline void add_group(float& m, float& l, float (&o)[VPL], float w, c
   m = mn;
 }
 
+// N consecutive floats of a group-statistics row.  Each row is read once per
+// step, so the loads are non-temporal (they leave the L2 to the small
+// per-unit arrays and the kernels' code).
 template <int N>
 __device__ inline void load_floats(const float* p, float (&x)[N]) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
   if constexpr (N == 4) {
-    float4 t = *reinterpret_cast<const float4*>(p);
+    const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
     x[0] = t.x; x[1] = t.y; x[2] = t.z; x[3] = t.w;
   } else if constexpr (N == 2) {
-    float2 t = *reinterpret_cast<const float2*>(p);
+    const f32x2 t = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(p));
     x[0] = t.x; x[1] = t.y;
   } else {
 #pragma unroll
-    for (int i = 0; i < N; ++i) x[i] = p[i];
+    for (int i = 0; i < N; ++i) x[i] = __builtin_nontemporal_load(p + i);
   }
 }
 
