@@ -265,25 +265,31 @@ struct MfmaTile {
   static_assert(2 * NC == NLI, "K and V tiles take the same registers");
 
   // Load a tile of contiguous rows (row i at kp + i*D elements) with buffer
-  // loads over exactly nrows rows: one offset register each for K and V,
-  // row steps in the immediate/scalar offset (both count in the hardware
-  // range check).  Rows at or past nrows read zeros and touch no memory;
-  // their probability is zero.
+  // loads over exactly nrows rows.  A lane's row offset is its row clamped
+  // to the tile's last row (row 0 of an empty tile), so every address lies
+  // in the tile whatever the range check covers; the row goes in the
+  // per-lane offset, column steps in the instruction's immediate, and the
+  // scalar offset is zero.  The descriptor's range (nrows rows) makes an
+  // empty tile's loads return zeros without a memory access.  Rows at or
+  // past nrows get probability zero in compute(), by position.
   __device__ static void load(const uint16_t* kp, const uint16_t* vp, int nrows, u32x4 (&kr)[NLI],
                               u32x4 (&vr)[NLI]) {
     const int lane = threadIdx.x & 63;
+    const int last = nrows > 0 ? nrows - 1 : 0;
     const uint32_t bytes = (uint32_t)nrows * (D * 2);
     const __amdgpu_buffer_rsrc_t rk = rsrc(kp, bytes), rv = rsrc(vp, bytes);
-    const int kb = (lane & 15) * (D * 2) + (lane >> 4) * 16;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+      const int kb = min((lane & 15) + 16 * t, last) * (D * 2) + (lane >> 4) * 16;
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        kr[NC * t + c] = __builtin_amdgcn_raw_buffer_load_b128(rk, kb, t * 16 * (D * 2) + c * 64, kStreamPolicy);
+        kr[NC * t + c] = __builtin_amdgcn_raw_buffer_load_b128(rk, kb + c * 64, 0, kStreamPolicy);
     }
-    const int vb = (lane / PPR) * (D * 2) + (lane % PPR) * 16;
 #pragma unroll
-    for (int i = 0; i < NLI; ++i) vr[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vb, i * RPI * (D * 2), kStreamPolicy);
+    for (int i = 0; i < NLI; ++i) {
+      const int vb = min(lane / PPR + RPI * i, last) * (D * 2) + (lane % PPR) * 16;
+      vr[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vb, 0, kStreamPolicy);
+    }
   }
 
   // Contiguous rows: row i of the tile at kp + i*D (elements).
