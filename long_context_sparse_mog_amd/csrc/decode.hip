@@ -61,8 +61,34 @@ struct DArgs {
   int32_t L_head_dim;
   int32_t whole;          // whole-cluster step (top-c lists the tiles, no subcluster kernel)
   int32_t rest_per_unit;  // residual blocks per unit: ceil(largest C / kRestClustersPerBlock)
+  // every unit has the same geometry (equal lengths and fold counts at the
+  // build): its record follows from its index (uni_C > 0), else it is loaded
+  int32_t uni_C, uni_S, uni_nmid, uni_N, uni_nfold;
   DecodeWS ws;
 };
+
+// Unit u's record: computed from the index for a layout of equal units (the
+// unit table's own rule: units in order, C clusters, C*S subclusters, C*S+1
+// offsets and n_mid rows each), else loaded.
+__device__ inline mog_unit unit_record(const DArgs& a, int u) {
+  if (a.uni_C > 0) {
+    mog_unit U;
+    U.seq = u / a.Hkv;
+    U.kv_head = u % a.Hkv;
+    U.N = a.uni_N;
+    U.n_mid = a.uni_nmid;
+    U.C = a.uni_C;
+    U.S = a.uni_S;
+    U.n_fold = a.uni_nfold;
+    U.reserved1 = 0;
+    U.row_base = (int64_t)u * a.uni_nmid;
+    U.cl_base = (int64_t)u * a.uni_C;
+    U.sub_base = (int64_t)u * a.uni_C * a.uni_S;
+    U.off_base = (int64_t)u * (a.uni_C * a.uni_S + 1);
+    return U;
+  }
+  return uni_unit(a.L.units + u);
+}
 
 struct BudgetArgs {
   int16_t top_c[MOG_MAX_SEQ];
@@ -209,7 +235,7 @@ __global__ __launch_bounds__(256) void k_score_clusters(DArgs a) {
     query_features<D, G>(a, u, blockIdx.x - a.score_blocks);
     return;
   }
-  const mog_unit U = uni_unit(a.L.units + u);
+  const mog_unit U = unit_record(a, u);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g0 = blockIdx.x * (4 * kScoreRowsPerWave) + wave * kScoreRowsPerWave;
   if (g0 >= U.C) return;
@@ -288,7 +314,7 @@ template <int G, int KPL>
 __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
   constexpr int NSW = (KPL + G - 1) / G;  // tail slots per wave
   __shared__ int hist[G][256 + 64];       // 256 digit bins, then one spare bin per lane
-  __shared__ unsigned long long selb[G][KPL];  // per head: chosen lanes of slot j
+  __shared__ uint32_t lmask[64 * KPL];     // per cluster: the heads that chose it
   __shared__ int slot_cnt[KPL], slot_tiles[KPL];
   __shared__ int wave_rows[G];  // whole-cluster step: rows of each wave's chosen clusters
   __shared__ float gsum[64 * KPL];  // shared selection: summed mass fractions
@@ -312,6 +338,10 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
   const mog_unit U = uni_unit(a.L.units + u);
   const int C = U.C;
   if (tid == 0 && !a.whole) a.ws.unit_rows[u] = 0;  // the subcluster kernel adds to it
+  // (cleared while the score loads are in flight; the heads OR their bits in
+  // after the barrier)
+  for (int i = tid; i < 64 * KPL; i += 64 * G) lmask[i] = 0u;
+  __syncthreads();
   if (a.shared) {
     // one selection per KV head: the key of a cluster is the sum over the
     // heads of the head's estimated mass fraction 2^(score - L_h), L_h the
@@ -517,13 +547,11 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
   if (all_ties && !want_sel) {
     // (the usual case: no tie to rank and nothing to report) lane j keeps
     // slot j's chosen lanes and writes them
-    unsigned long long mine = 0ull;
+    if (c_eff > 0) {
 #pragma unroll
-    for (int j = 0; j < KPL; ++j) {
-      const unsigned long long sb = __ballot(c_eff > 0 && key[j] != 0u && (key[j] & hi_mask) >= prefix);
-      mine = lane == j ? sb : mine;
+      for (int j = 0; j < KPL; ++j)
+        if ((key[j] != 0u) & ((key[j] & hi_mask) >= prefix)) atomicOr(&lmask[64 * j + lane], 1u << h);
     }
-    if (lane < KPL) selb[h][lane] = mine;
   } else {
 #pragma unroll
   for (int j = 0; j < KPL; ++j) {
@@ -540,7 +568,7 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
       ties += __popcll(tb);
     }
     const unsigned long long sb = __ballot(sel);
-    if (lane == 0) selb[h][j] = sb;
+    if (sel) atomicOr(&lmask[i], 1u << h);
     if (want_sel) {
       const int rank = sel ? rank0 + __popcll(sb & below) : -1;
       if (i < C) {
@@ -573,8 +601,7 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
     tcnt[t] = 0;
     tinc[t] = 0;
     if (j < KPL) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) um[t] |= (uint32_t)((selb[g][j] >> lane) & 1ull) << g;
+      um[t] = lmask[64 * j + lane];
       if (64 * j + lane >= C) um[t] = 0u;
       const int n = __popcll(__ballot(um[t] != 0u));
       int nt = 0;
@@ -1698,6 +1725,18 @@ hipError_t launch_decode(const DecodeLaunch& x, hipStream_t s) {
   a.half_s2_l2 = 0.5f * x.scale * x.scale * kLog2e;
   a.L_head_dim = x.D;
   a.whole = x.whole;
+  {
+    // equal units: every sequence with the first one's length and fold count
+    bool eq = true;
+    for (int s = 1; s < x.L.n_seq; ++s)
+      eq = eq && x.L.seq_lens[s] == x.L.seq_lens[0] && x.L.fold_count[s] == x.L.fold_count[0];
+    const UnitSizes z = unit_sizes(x.L.seq_lens[0] - x.L.fold_count[0], x.L.n_sink, x.L.n_recent);
+    a.uni_C = eq ? z.C : 0;
+    a.uni_S = z.S;
+    a.uni_nmid = z.n_mid;
+    a.uni_N = x.L.seq_lens[0];
+    a.uni_nfold = x.L.fold_count[0];
+  }
   a.rest_per_unit = (x.L.max_C + kRestClustersPerBlock - 1) / kRestClustersPerBlock;
   a.ws = x.ws;
   BudgetArgs b;
