@@ -1546,26 +1546,35 @@ __global__ __launch_bounds__(1024) void k_merge(const float* part, int n_part, c
     }
   }
   __syncthreads();
-  // thread t < D / 4 sums 4 elements over the waves
-  if (tid < D / 4) {
-    float M = -INFINITY;
+  // every thread: wave state w = tid % NW, elements 2p, 2p + 1 (p = tid / NW);
+  // the NW states of one element pair sit in NW adjacent lanes, which take
+  // the block maximum, the rescaled sums and the denominator by lane
+  // exchanges
+  static_assert(NW == 16 && 1024 / NW >= D / 2, "16 wave states, one element pair per 16 lanes");
+  {
+    const int w = tid % NW, pr = tid / NW;
+    const float mv = wm[w];
+    float M = mv;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w]);
-    float4 t = {0.f, 0.f, 0.f, 0.f};
-    float dn = 0.f;
+    for (int sft = 1; sft < NW; sft <<= 1) M = fmaxf(M, __shfl_xor(M, sft, 64));
+    const float fw = exp2_or_zero(mv, M);
+    const float* ow = reinterpret_cast<const float*>(wo[w]);  // the state's D elements in order
+    float t0 = 0.f, t1 = 0.f;
+    if (pr < D / 2) {
+      const float2 v = reinterpret_cast<const float2*>(ow)[pr];
+      t0 = fw * v.x;
+      t1 = fw * v.y;
+    }
+    float dn = fw * wl[w];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float fw = exp2_or_zero(wm[w], M);
-      const float4 a4 = reinterpret_cast<const float4*>(wo[w])[tid];
-      t.x += fw * a4.x;
-      t.y += fw * a4.y;
-      t.z += fw * a4.z;
-      t.w += fw * a4.w;
-      dn += fw * wl[w];
+    for (int sft = 1; sft < NW; sft <<= 1) {
+      t0 += __shfl_xor(t0, sft, 64);
+      t1 += __shfl_xor(t1, sft, 64);
+      dn += __shfl_xor(dn, sft, 64);
     }
     const int64_t orow = (int64_t)seq * Hq + hq;
     const float inv = dn > 0.f ? 1.f / dn : 0.f;
-    reinterpret_cast<float4*>(out + orow * D)[tid] = float4{t.x * inv, t.y * inv, t.z * inv, t.w * inv};
+    if (w == 0 && pr < D / 2) reinterpret_cast<float2*>(out + orow * D)[pr] = float2{t0 * inv, t1 * inv};
     if (lse && tid == 0) lse[orow] = dn > 0.f ? (M + log2f(dn)) * kLn2 : -INFINITY;
   }
 }
