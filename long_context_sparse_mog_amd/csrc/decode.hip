@@ -665,7 +665,7 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. Subclusters and residual.  Grid (units, nb_rest + nb_chosen); blocks
+// 3. Subclusters and residual.  Grid (units, n_rest + nb_chosen); blocks
 //    are numbered x (record slot order) as below, but the rest blocks come
 //    first in the grid, so the dispatcher starts them together with the
 //    chosen-cluster blocks instead of after every chosen slot (most of which
@@ -678,10 +678,12 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
 //      the cluster's exact tiles (runs of chosen subclusters cut into tiles
 //      of <= 32 rows) from its slot base, and accumulates the residual
 //      terms of the subclusters a choosing head left out;
-//    * block nb_chosen + y covers clusters [16y, 16y+16) (4 per wave, all
-//      loads at once): the residual terms of every head that left a
-//      cluster out.
-//    Every block writes one residual record per head (slot = block index).
+//    * block nb_chosen + y (feature-map residual only; the Gaussian
+//      residual of whole clusters left out runs in blocks at the end of the
+//      exact launch) covers clusters [16y, 16y+16): the residual terms of
+//      every head that left a cluster out.
+//    Every block writes one residual record per head: the chosen clusters'
+//    in slots [0, n_chosen), the rest after them.
 // ---------------------------------------------------------------------------
 // Feature-map residual: the weight (log2 of the estimated mass) of a group
 // whose feature sums z the wave holds (z[k]: feature lane + 64 k), for head h:
@@ -756,7 +758,7 @@ __device__ inline void store_wave_states(float* st, const float (&rm)[G], const 
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int nb_chosen) {
+__global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int nb_chosen, int n_rest_blocks) {
   constexpr int EPL = D / 32;
   constexpr int VPL = D / 64;
   constexpr int RS = D + kPartPad;
@@ -779,7 +781,6 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
   const int64_t cw = (int64_t)u * a.cstride;  // the unit's per-cluster workspace entries
   // the x-th chosen cluster needs only the unit index: its loads go out with
   // the unit record's
-  const int n_rest_blocks = a.nb_res - nb_chosen;
   const int x = (int)blockIdx.y < n_rest_blocks ? nb_chosen + (int)blockIdx.y : (int)blockIdx.y - n_rest_blocks;
   const int n_ch_raw = a.ws.n_chosen[u];
   int g_x = 0, tb_x = 0;
@@ -1224,11 +1225,13 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   if ((int)blockIdx.x >= a.nblk) {
-    // whole-cluster step: the Gaussian residual of the clusters some head
-    // left out, in blocks after the exact ones (dispatched as exact blocks
-    // retire); record y of unit u covers clusters [16 y, 16 y + 16)
+    // the Gaussian residual of the clusters some head left out, in blocks
+    // after the exact ones (dispatched as exact blocks retire); record y of
+    // unit u covers clusters [16 y, 16 y + 16), after the unit's chosen-
+    // cluster records (none for a whole-cluster step)
     const int r = (int)blockIdx.x - a.nblk;
     const int u = r / a.rest_per_unit, y = r % a.rest_per_unit;
+    const int n_ch_raw = a.whole ? 0 : a.ws.n_chosen[u];
     const mog_unit U = uni_unit(a.L.units + u);
     if (y * kRestClustersPerBlock >= U.C) return;
     constexpr int VPL = D / 64;
@@ -1243,7 +1246,7 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
     rest_clusters<D, G>(a, u, U.C, U.cl_base, y, rm, rl, ro);
     store_wave_states<D, G>(st, rm, rl, ro);
     __syncthreads();
-    write_block_record<D, G>(st, a.ws.res_part + ((int64_t)u * a.nb_res + y) * G * RS);
+    write_block_record<D, G>(st, a.ws.res_part + ((int64_t)u * a.nb_res + uni(n_ch_raw) + y) * G * RS);
     return;
   }
   const int A = a.n_sink + a.n_recent;
@@ -1653,9 +1656,17 @@ static hipError_t decode_impl(const DecodeLaunch& x, const DArgs& a, const Budge
     hipLaunchKernelGGL((k_select_topc<G, 16>), dim3(nu), dim3(64 * G), 0, s, a, b);
   else
     hipLaunchKernelGGL((k_select_topc<G, kMaxC / 64>), dim3(nu), dim3(64 * G), 0, s, a, b);
-  if (!x.whole) hipLaunchKernelGGL((k_subclusters<D, G>), dim3(nu, x.nb_res), dim3(256), 0, s, a, b, x.nb_chosen);
-  // a whole-cluster step's residual blocks follow the exact blocks
-  const int nrest = x.whole && x.residual ? nu * a.rest_per_unit : 0;
+  // the Gaussian residual of the clusters left out runs in blocks after the
+  // exact ones, in the spread of their end times; the feature-map residual's
+  // in the subcluster kernel; none without a residual
+  if (!x.whole) {
+    const int nrest_sub = x.residual == 2 ? a.rest_per_unit : 0;
+    // (no chosen cluster anywhere and no feature-map residual: nothing to do)
+    if (x.nb_chosen + nrest_sub > 0)
+      hipLaunchKernelGGL((k_subclusters<D, G>), dim3(nu, x.nb_chosen + nrest_sub), dim3(256), 0, s, a, b,
+                         x.nb_chosen, nrest_sub);
+  }
+  const int nrest = x.residual == 1 ? nu * a.rest_per_unit : 0;
   // the timing events (if any) are taken by the dispatches themselves: the
   // start of the first exact launch and the end of the last
   for (int r = 0; r < x.repeat; ++r) {
