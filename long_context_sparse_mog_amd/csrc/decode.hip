@@ -680,7 +680,8 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
 //      terms of the subclusters a choosing head left out;
 //    * block nb_chosen + y (feature-map residual only; the Gaussian
 //      residual of whole clusters left out runs in blocks at the end of the
-//      exact launch) covers clusters [16y, 16y+16): the residual terms of
+//      exact launch) covers clusters [R y, R y + R), R =
+//      kRestClustersPerBlock: the residual terms of
 //      every head that left a cluster out.
 //    Every block writes one residual record per head: the chosen clusters'
 //    in slots [0, n_chosen), the rest after them.
@@ -704,37 +705,43 @@ __device__ inline void load_fz(const float* row, int FM, float (&z)[4]) {
   for (int k = 0; k < 4; ++k) z[k] = 64 * k < FM ? row[lane + 64 * k] : 0.f;
 }
 
-// Gaussian residual of clusters [16 y, 16 y + 16) of unit u: every head that
-// left a cluster out adds its term 2^score v-bar, 4 clusters per wave with
-// every load issued before any is used (clusters past C re-read the last one
-// and are skipped; an empty cluster scores -inf for every head, so its size
-// is not needed).
+// Gaussian residual of clusters [R y, R y + R) of unit u (R =
+// kRestClustersPerBlock): every head that left a cluster out adds its term
+// 2^score v-bar.  A wave takes R / 4 clusters, in batches whose loads are all
+// issued before any is used: the whole share at once where its registers
+// stay within 128 per lane (clusters past C re-read the last one and are
+// skipped; an empty cluster scores -inf for every head, so its size is not
+// needed).
 template <int D, int G>
 __device__ inline void rest_clusters(const DArgs& a, int u, int C, int64_t cl_base, int y, float (&rm)[G],
                                      float (&rl)[G], float (&ro)[G][D / 64]) {
   constexpr int VPL = D / 64;
   constexpr int RCW = kRestClustersPerBlock / 4;
+  constexpr int RB = (VPL + G + 1) * RCW <= 128 ? RCW : RCW / 2;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t cw = (int64_t)u * a.cstride;
   const uint32_t all = (1u << G) - 1u;
-  uint32_t mask[RCW];
-  float vb[RCW][VPL], sc[RCW][G];
+  const int g0 = y * kRestClustersPerBlock + wave * RCW;
 #pragma unroll
-  for (int k = 0; k < RCW; ++k) {
-    const int g = min(y * kRestClustersPerBlock + wave * RCW + k, C - 1);
-    mask[k] = a.ws.cl_mask[cw + g];
-    load_floats<VPL>(a.L.cl_vbar + (cl_base + g) * D + lane * VPL, vb[k]);
+  for (int k0 = 0; k0 < RCW; k0 += RB) {
+    uint32_t mask[RB];
+    float vb[RB][VPL], sc[RB][G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) sc[k][h] = a.ws.cl_score[((int64_t)u * G + h) * a.cstride + g];
-  }
+    for (int k = 0; k < RB; ++k) {
+      const int g = min(g0 + k0 + k, C - 1);
+      mask[k] = a.ws.cl_mask[cw + g];
+      load_floats<VPL>(a.L.cl_vbar + (cl_base + g) * D + lane * VPL, vb[k]);
 #pragma unroll
-  for (int k = 0; k < RCW; ++k) {
-    const int g = y * kRestClustersPerBlock + wave * RCW + k;
-    if (g >= C) break;
-    const uint32_t unchosen = sc[k][0] != -INFINITY ? (all & ~mask[k]) : 0u;
+      for (int h = 0; h < G; ++h) sc[k][h] = a.ws.cl_score[((int64_t)u * G + h) * a.cstride + g];
+    }
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-      if ((unchosen >> h) & 1u) add_group<VPL>(rm[h], rl[h], ro[h], sc[k][h], vb[k]);
+    for (int k = 0; k < RB; ++k) {
+      const bool in_c = g0 + k0 + k < C;
+      const uint32_t unchosen = in_c && sc[k][0] != -INFINITY ? (all & ~mask[k]) : 0u;
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        if ((unchosen >> h) & 1u) add_group<VPL>(rm[h], rl[h], ro[h], sc[k][h], vb[k]);
+    }
   }
 }
 
@@ -1096,10 +1103,10 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
     constexpr int RCW = kRestClustersPerBlock / 4;
     const int y = x - nb_chosen;
     if (fmr && a.residual) {
-      // the feature-map estimate of each left-out cluster's mass, RCW / 2
+      // the feature-map estimate of each left-out cluster's mass, HALF
       // clusters' loads at a time (this mode keeps the Gaussian path's
       // registers)
-      constexpr int HALF = RCW / 2;
+      constexpr int HALF = 2;
       __syncthreads();  // the feature table
 #pragma unroll 1
       for (int k0 = 0; k0 < RCW; k0 += HALF) {
@@ -1127,8 +1134,6 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
           }
         }
       }
-    } else if (a.residual) {
-      rest_clusters<D, G>(a, u, C, U.cl_base, y, rm, rl, ro);
     }
   }
 
@@ -1147,12 +1152,15 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
 // ---------------------------------------------------------------------------
 // ---------------------------------------------------------------------------
 // 4a. Shares of the exact blocks.  Unit u reads T_u = anchors + rows of its
-//     chosen subclusters exactly; it gets 1 + floor(T_u * extra / total)
-//     blocks, extra = min(nblk - n_units, ceil(total / 256)) (so the shares
-//     sum to at most nblk and no block gets much under 256 rows), numbered
-//     unit by unit.  Every wave of every exact block recomputes the shares
-//     from the per-unit row counts (a few KB): no table, no launch, no
-//     barrier.
+//     chosen subclusters exactly; it gets n_u(r) = 1 + floor(T_u * r) blocks,
+//     numbered unit by unit, for the largest scale r found by bisection with
+//     sum_u n_u(r) <= B, B = min(nblk, n_units + ceil(total / 256)) (so no
+//     block gets much under 256 rows).  This bounds the heaviest block by
+//     the smallest load the block count allows, up to rounding: with many
+//     units of a few blocks each, a fixed scale (r = (B - n_units) / total)
+//     leaves up to one block per unit unused and its siblings a third more
+//     work.  With many blocks per unit the fixed scale is kept.  Every wave of every exact block recomputes the shares from the
+//     per-unit row counts (a few KB): no table, no launch, no barrier.
 // ---------------------------------------------------------------------------
 struct BlockShare {
   int u;      // unit (-1: the block has no work)
@@ -1161,24 +1169,68 @@ struct BlockShare {
 };
 
 // The share holding block want_block, found by one wave on its own (every
-// wave of a block computes the same, so no barrier is needed): the units'
-// totals by lane sums, the block numbers by a lane scan, 64 units at a time.
+// wave of a block computes the same, so no barrier is needed): lane l holds
+// the totals of units l + 64 k (k < kShareRegs) in registers, the counts
+// are wave sums, the block numbers a lane scan.  Past 64 kShareRegs units
+// the scale is the fixed one, the units read 64 at a time.
+constexpr int kShareRegs = 4;
+constexpr int kShareIters = 10;
+
 __device__ BlockShare wave_find_share(const int32_t* unit_rows, int n_units, int nblk, int A, int want_block) {
   const int lane = threadIdx.x & 63;
+  const bool in_regs = n_units <= 64 * kShareRegs;
+  float w[kShareRegs];
   long long part = 0;
-  for (int v = lane; v < n_units; v += 64) part += (long long)A + unit_rows[v];
+  if (in_regs) {
+#pragma unroll
+    for (int k = 0; k < kShareRegs; ++k) {
+      const int v = lane + 64 * k;
+      const int t = v < n_units ? A + unit_rows[v] : -1;
+      w[k] = (float)t;
+      part += t < 0 ? 0 : t;
+    }
+  } else {
+    for (int v = lane; v < n_units; v += 64) part += (long long)A + unit_rows[v];
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
   const long long total = part;
-  long long extra = nblk - n_units;
   const long long by_rows = (total + 255) / 256;
-  if (by_rows < extra) extra = by_rows;
+  const int B = (int)(nblk - n_units < by_rows ? nblk : n_units + by_rows);
+  // blocks n_u(r) summed over the units (r >= 0: monotone in r)
+  auto count = [&](float r) {
+    int c = 0;
+#pragma unroll
+    for (int k = 0; k < kShareRegs; ++k) c += w[k] >= 0.f ? 1 + (int)floorf(w[k] * r) : 0;
+    return (int)wave_reduce_uniform((uint32_t)c, [](uint32_t x, uint32_t y) { return x + y; }, 0u);
+  };
+  float r = total > 0 ? (float)(B - n_units) / (float)total : 0.f;
+  // (with 32 or more blocks per unit beyond its first, the fixed scale
+  // already leaves at most a few percent of a block per unit unused)
+  if (in_regs && total > 0 && B - n_units < 32 * n_units) {
+    // bisection on [lo, hi): lo meets the bound (r = 0 always does, as
+    // n_units <= nblk), hi = (B + 1) / total cannot (sum >= total * r)
+    float lo = count(r) <= B ? r : 0.f, hi = (float)(B + 1) / (float)total * 1.001f;
+    for (int it = 0; it < kShareIters; ++it) {
+      const float mid = 0.5f * (lo + hi);
+      if (count(mid) <= B) lo = mid;
+      else hi = mid;
+    }
+    r = lo;
+  }
   BlockShare res{-1, 0, 0};
   int carry = 0;
-  for (int base = 0; base < n_units; base += 64) {
+  for (int base = 0, k = 0; base < n_units; base += 64, ++k) {
     const int v = base + lane;
     int sp = 0;
-    if (v < n_units) sp = 1 + (int)(total > 0 ? ((long long)A + unit_rows[v]) * extra / total : 0);
+    if (in_regs) {
+#pragma unroll
+      for (int kk = 0; kk < kShareRegs; ++kk)
+        if (kk == k && w[kk] >= 0.f) sp = 1 + (int)floorf(w[kk] * r);
+    } else if (v < n_units) {
+      // fixed scale in exact integers: sum <= n_units + (B - n_units)
+      sp = 1 + (int)(total > 0 ? ((long long)A + unit_rows[v]) * (B - n_units) / total : 0);
+    }
     const int incl = wave_incl_scan(sp);
     const int first = carry + incl - sp;
     const unsigned long long hit = __ballot(v < n_units && want_block >= first && want_block < first + sp);
@@ -1227,7 +1279,8 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
   if ((int)blockIdx.x >= a.nblk) {
     // the Gaussian residual of the clusters some head left out, in blocks
     // after the exact ones (dispatched as exact blocks retire); record y of
-    // unit u covers clusters [16 y, 16 y + 16), after the unit's chosen-
+    // unit u covers clusters [R y, R y + R) (R = kRestClustersPerBlock),
+    // after the unit's chosen-
     // cluster records (none for a whole-cluster step)
     const int r = (int)blockIdx.x - a.nblk;
     const int u = r / a.rest_per_unit, y = r % a.rest_per_unit;

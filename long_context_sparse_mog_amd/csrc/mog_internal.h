@@ -181,7 +181,7 @@ struct DenseLaunch {
   float* ex_part;       // [n_units][splits][G][D+4]
 };
 
-constexpr int kRestClustersPerBlock = 16;  // residual-only blocks: 4 clusters per wave
+constexpr int kRestClustersPerBlock = 64;  // residual-only blocks: 16 clusters per wave
 constexpr int kPartPad = 4;
 // blocks of the exact-attention kernel resident at once on the chip: 256
 // compute units x 2 (its registers allow 2 waves per SIMD)
