@@ -1174,7 +1174,7 @@ struct BlockShare {
 // are wave sums, the block numbers a lane scan.  Past 64 kShareRegs units
 // the scale is the fixed one, the units read 64 at a time.
 constexpr int kShareRegs = 4;
-constexpr int kShareIters = 10;
+constexpr int kShareRounds = 3;
 
 __device__ BlockShare wave_find_share(const int32_t* unit_rows, int n_units, int nblk, int A, int want_block) {
   const int lane = threadIdx.x & 63;
@@ -1198,23 +1198,33 @@ __device__ BlockShare wave_find_share(const int32_t* unit_rows, int n_units, int
   const long long by_rows = (total + 255) / 256;
   const int B = (int)(nblk - n_units < by_rows ? nblk : n_units + by_rows);
   // blocks n_u(r) summed over the units (r >= 0: monotone in r)
-  auto count = [&](float r) {
+  auto part_count = [&](float r) {
     int c = 0;
 #pragma unroll
     for (int k = 0; k < kShareRegs; ++k) c += w[k] >= 0.f ? 1 + (int)floorf(w[k] * r) : 0;
-    return (int)wave_reduce_uniform((uint32_t)c, [](uint32_t x, uint32_t y) { return x + y; }, 0u);
+    return (uint32_t)c;
   };
+  auto add = [](uint32_t x, uint32_t y) { return x + y; };
   float r = total > 0 ? (float)(B - n_units) / (float)total : 0.f;
   // (with 32 or more blocks per unit beyond its first, the fixed scale
   // already leaves at most a few percent of a block per unit unused)
   if (in_regs && total > 0 && B - n_units < 32 * n_units) {
-    // bisection on [lo, hi): lo meets the bound (r = 0 always does, as
-    // n_units <= nblk), hi = (B + 1) / total cannot (sum >= total * r)
-    float lo = count(r) <= B ? r : 0.f, hi = (float)(B + 1) / (float)total * 1.001f;
-    for (int it = 0; it < kShareIters; ++it) {
-      const float mid = 0.5f * (lo + hi);
-      if (count(mid) <= B) lo = mid;
-      else hi = mid;
+    // 4-ary search on [lo, hi): lo meets the bound (r = 0 always does, as
+    // n_units <= nblk), hi = (B + 1) / total cannot (the sum exceeds
+    // total * r); each round counts three interior points, whose wave sums
+    // are independent of each other
+    float lo = (int)wave_reduce_uniform(part_count(r), add, 0u) <= B ? r : 0.f;
+    float hi = (float)(B + 1) / (float)total * 1.001f;
+    for (int it = 0; it < kShareRounds; ++it) {
+      const float d = 0.25f * (hi - lo);
+      const float c1 = lo + d, c2 = lo + 2.f * d, c3 = lo + 3.f * d;
+      const int n1 = (int)wave_reduce_uniform(part_count(c1), add, 0u);
+      const int n2 = (int)wave_reduce_uniform(part_count(c2), add, 0u);
+      const int n3 = (int)wave_reduce_uniform(part_count(c3), add, 0u);
+      if (n3 <= B) lo = c3;
+      else if (n2 <= B) { lo = c2; hi = c3; }
+      else if (n1 <= B) { lo = c1; hi = c2; }
+      else hi = c1;
     }
     r = lo;
   }
