@@ -764,6 +764,57 @@ __device__ inline void store_wave_states(float* st, const float (&rm)[G], const 
   }
 }
 
+// Exact tiles of a chosen cluster (lane i: subcluster i, rows [st, en) of
+// the unit's middle rows, head mask m; m = 0 for a subcluster no head
+// chose): a run is a maximal sequence of chosen nonempty subclusters with
+// one head mask whose rows are contiguous; each run is cut into tiles of
+// <= 32 rows, written run after run to ctiles.  Returns the tile count
+// (wave-uniform).  Called by a whole wave.
+__device__ inline int write_run_tiles(TileRec* ctiles, int64_t row_base, int64_t row_elems, int st, int en,
+                                      uint32_t m) {
+  const int lane = threadIdx.x & 63;
+  const bool live = m != 0u && en > st;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  const unsigned long long lb = __ballot(live);
+  const unsigned long long lbb = lb & below;
+  const int prv = lbb ? 63 - __clzll((long long)lbb) : 0;
+  const uint32_t m_prv = (uint32_t)__shfl((int)m, prv, 64);
+  const int en_prv = __shfl(en, prv, 64);
+  const bool head = live && !(lbb != 0ull && m_prv == m && en_prv == st);
+  const unsigned long long hb = __ballot(head);
+  const unsigned long long later = hb & ~(below | (1ull << lane));
+  const int nxt = later ? __ffsll((long long)later) - 1 : 64;
+  const unsigned long long in_run = lb & (nxt >= 64 ? ~0ull : ((1ull << nxt) - 1ull));
+  const int last = in_run ? 63 - __clzll((long long)in_run) : 0;
+  const int run_en = __shfl(en, last, 64);
+  const int ntl = head ? (run_en - st + 31) / 32 : 0;
+  const int incl = wave_incl_scan(ntl);
+  const int n_tiles = __builtin_amdgcn_readlane(incl, 63);
+  // the tiles are written by every lane (tiles t = lane, lane + 64, ...):
+  // tile t belongs to the run whose head lane j has tile range
+  // [incl_j - ntl_j, incl_j); the runs are visited in a wave-uniform loop
+  const int tfirst = incl - ntl;
+  for (int t0 = 0; t0 < n_tiles; t0 += 64) {
+    const int t = t0 + lane;
+    int64_t toff = 0;
+    int tn = 0;
+    uint32_t tm = 0u;
+    for (unsigned long long bits = hb; bits; bits &= bits - 1ull) {
+      const int j = __ffsll((long long)bits) - 1;
+      const int ts = __builtin_amdgcn_readlane(tfirst, j);
+      const int tc = __builtin_amdgcn_readlane(ntl, j);
+      if (t >= ts && t < ts + tc) {
+        const int r = __builtin_amdgcn_readlane(st, j) + 32 * (t - ts);
+        toff = (row_base + r) * row_elems;
+        tn = min(32, __builtin_amdgcn_readlane(run_en, j) - r);
+        tm = (uint32_t)__builtin_amdgcn_readlane((int)m, j);
+      }
+    }
+    if (t < n_tiles) ctiles[t] = TileRec{toff, tn, tm};
+  }
+  return n_tiles;
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int nb_chosen, int n_rest_blocks) {
   constexpr int EPL = D / 32;
@@ -984,53 +1035,13 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
         const uint32_t rows = (lane < S && lds_sm[lane]) ? (uint32_t)(my_cnt + my_fcnt) : 0u;
         const int rsum = (int)wave_reduce_uniform(rows, [](uint32_t p, uint32_t q) { return p + q; }, 0u);
         if (lane == 0) atomicAdd(&a.ws.unit_rows[u], rsum);
-        // exact tiles of the cluster: a run is a maximal sequence of chosen
-        // nonempty subclusters with one head mask whose rows are contiguous
-        // (lane i: subcluster i); each run is cut into tiles of <= 32 rows,
-        // written run after run from the cluster's slot base
+        // exact tiles of the cluster, from its slot base
         const int st = lane < S ? lds_off[lane] : 0;
         const int en = lane < S ? lds_off[lane] + lds_cnt[lane] : 0;
         const uint32_t m = lane < S ? lds_sm[lane] : 0u;
-        const bool live = m != 0u && en > st;
         const unsigned long long below = (1ull << lane) - 1ull;
-        const unsigned long long lb = __ballot(live);
-        const unsigned long long lbb = lb & below;
-        const int prv = lbb ? 63 - __clzll((long long)lbb) : 0;
-        const uint32_t m_prv = (uint32_t)__shfl((int)m, prv, 64);
-        const int en_prv = __shfl(en, prv, 64);
-        const bool head = live && !(lbb != 0ull && m_prv == m && en_prv == st);
-        const unsigned long long hb = __ballot(head);
-        const unsigned long long later = hb & ~(below | (1ull << lane));
-        const int nxt = later ? __ffsll((long long)later) - 1 : 64;
-        const unsigned long long in_run = lb & (nxt >= 64 ? ~0ull : ((1ull << nxt) - 1ull));
-        const int last = in_run ? 63 - __clzll((long long)in_run) : 0;
-        const int run_en = __shfl(en, last, 64);
-        const int ntl = head ? (run_en - st + 31) / 32 : 0;
-        const int incl = wave_incl_scan(ntl);
-        const int n_tiles = __builtin_amdgcn_readlane(incl, 63);
         TileRec* ctiles = a.ws.tiles + tile_unit_base(U.row_base, U.cl_base, u, a.L.fold_cap) + uni(tb_x);
-        // the tiles are written by every lane (tiles t = lane, lane + 64, ...):
-        // tile t belongs to the run whose head lane j has tile range
-        // [incl_j - ntl_j, incl_j); the runs are visited in a wave-uniform loop
-        const int tfirst = incl - ntl;
-        for (int t0 = 0; t0 < n_tiles; t0 += 64) {
-          const int t = t0 + lane;
-          int64_t toff = 0;
-          int tn = 0;
-          uint32_t tm = 0u;
-          for (unsigned long long bits = hb; bits; bits &= bits - 1ull) {
-            const int j = __ffsll((long long)bits) - 1;
-            const int ts = __builtin_amdgcn_readlane(tfirst, j);
-            const int tc = __builtin_amdgcn_readlane(ntl, j);
-            if (t >= ts && t < ts + tc) {
-              const int r = __builtin_amdgcn_readlane(st, j) + 32 * (t - ts);
-              toff = (U.row_base + r) * (int64_t)a.L_head_dim;
-              tn = min(32, __builtin_amdgcn_readlane(run_en, j) - r);
-              tm = (uint32_t)__builtin_amdgcn_readlane((int)m, j);
-            }
-          }
-          if (t < n_tiles) ctiles[t] = TileRec{toff, tn, tm};
-        }
+        const int n_tiles = write_run_tiles(ctiles, U.row_base, a.L_head_dim, st, en, m);
         int n_all = n_tiles;
         // folded rows of the chosen subclusters, after the reordered ones:
         // the unit's fold rows are scanned 64 at a time (lane l: row f0 + l);
@@ -1140,6 +1151,173 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
   store_wave_states<D, G>(&st[0][0][0], rm, rl, ro);
   __syncthreads();
   write_block_record<D, G>(&st[0][0][0], dst);
+}
+
+// ---------------------------------------------------------------------------
+// 3b. Subclusters, one wave per chosen cluster (selection per query head,
+//     Gaussian residual or none, no folded rows): wave w of block (u, y)
+//     takes the unit's chosen cluster x = 4 y + w and does alone, with no
+//     barrier, what a block of the kernel above does for it:
+//     * the S subcluster scores (count term included) in chunks of
+//       kSubChunk rows: each chunk's G x kSubChunk dot products are summed
+//       over the lanes by one reduce-scatter while the next chunk's rows
+//       load, and the scores go to the wave's LDS row, head-major;
+//     * the top-s of each head that chose the cluster, by rank counts over
+//       that row (ties to the lower index), lane i holding subcluster i's
+//       head mask;
+//     * the selection output, the rows read exactly added to the unit's
+//       count, and the cluster's exact tiles from its slot base;
+//     * the residual record of the subclusters a choosing head left out.
+//     A chosen cluster's work is thus one wave's chain, and many more
+//     chosen clusters are in flight per compute unit than with a block each.
+// ---------------------------------------------------------------------------
+constexpr int kSubChunk = 8;
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_sub_wave(DArgs a, BudgetArgs b, int nb_chosen) {
+  constexpr int EPL = D / 32;
+  constexpr int VPL = D / 64;
+  constexpr int RS = D + kPartPad;
+  constexpr int SR = kDecodeSubRows;
+  constexpr int RC = kSubChunk;
+  constexpr int NCH = SR / RC;
+  static_assert(SR % RC == 0 && SR % 4 == 0, "whole chunks, float4 rows");
+  static_assert(RC * G <= 64, "one lane per (row, head) sum of a chunk");
+  __shared__ float4 lsc4[4][G][SR / 4];  // each wave's scores [head][subcluster]
+  const int u = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int x = (int)blockIdx.y * 4 + wave;
+  const int64_t cw = (int64_t)u * a.cstride;
+  const int s_keep_raw = b.top_s[u / a.Hkv];
+  const int n_ch_raw = a.ws.n_chosen[u];
+  // (entries below nb_chosen <= the largest C are in range; they are used
+  // only for x < n_chosen)
+  const int xs = min(x, nb_chosen - 1);
+  const int g_raw = a.ws.cl_list[cw + xs];
+  const int tb_raw = a.ws.ch_tbase[cw + xs];
+  const mog_unit U = uni_unit(a.L.units + u);
+  if (x >= uni(n_ch_raw)) return;
+  const int g = uni(g_raw), S = U.S;
+  const int64_t cg = cw + g;
+  const int64_t sg0 = U.sub_base + (int64_t)g * S;
+  const uint32_t mask = (uint32_t)uni((int)a.ws.cl_mask[cg]);
+  // subcluster bounds: lane i <= S holds offset i
+  const int32_t* off = a.L.sub_off + U.off_base + (int64_t)g * S;
+  const int o_i = off[min(lane, S)];
+  const int o_n = __shfl_down(o_i, 1, 64);
+  const int cnt = lane < S ? o_n - o_i : 0;
+  const int s_keep = s_keep_raw < 0 ? 0 : s_keep_raw;
+  float* sc = reinterpret_cast<float*>(&lsc4[wave][0][0]);  // sc[h * SR + i]
+  uint32_t sm = 0u;  // lane i: the heads that chose subcluster i
+  if (s_keep >= S) {
+    // a budget of S or more reads every nonempty subcluster of the cluster
+    sm = (lane < S && cnt > 0) ? mask : 0u;
+  } else {
+    float coef[G][EPL];
+    score_coefs<D, G>(a, a.q + ((int64_t)U.seq * a.Hq + (int64_t)U.kv_head * G) * D, coef);
+    float xr[2][RC][EPL];
+    auto load_chunk = [&](int c, float (&dst)[RC][EPL]) {
+#pragma unroll
+      for (int k = 0; k < RC; ++k)
+        load_floats<EPL>(a.L.sub_ms + (sg0 + min(c * RC + k, S - 1)) * (2 * D) + lane * EPL, dst[k]);
+    };
+    load_chunk(0, xr[0]);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if (c + 1 < NCH) load_chunk(c + 1, xr[(c + 1) & 1]);
+      float part[RC * G];
+#pragma unroll
+      for (int k = 0; k < RC; ++k) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float t = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) t += coef[h][e] * xr[c & 1][k][e];
+          part[k * G + h] = t;
+        }
+      }
+      const float t = wave_reduce_scatter<RC * G>(part);
+      const int j = rs_index<RC * G>(lane), i = c * RC + j / G, h = j % G;
+      const int ci = __shfl(cnt, i & 63, 64);
+      // (rows past S score -inf, so every row of the LDS row is written)
+      if (rs_owner<RC * G>(lane)) sc[h * SR + i] = (i < S && ci > 0) ? t + log2f((float)ci) : -INFINITY;
+    }
+    __asm__ volatile("" ::: "memory");  // (a wave's LDS operations run in order)
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (!((mask >> h) & 1u)) continue;
+      const float my = lane < SR ? sc[h * SR + lane] : -INFINITY;
+      // branch-free rank count (bitwise, not short-circuit, operators)
+      int rank = 0;
+#pragma unroll
+      for (int j4 = 0; j4 < SR / 4; ++j4) {
+        const float4 o4 = lsc4[wave][h][j4];
+        const float ov[4] = {o4.x, o4.y, o4.z, o4.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int j = 4 * j4 + q;
+          rank += (int)((ov[q] != -INFINITY) & ((ov[q] > my) | ((ov[q] == my) & (j < lane))));
+        }
+      }
+      if (lane < S && my != -INFINITY && rank < s_keep) sm |= 1u << h;
+    }
+  }
+  const unsigned long long below = (1ull << lane) - 1ull;
+  if (a.sel_s) {
+    // the head's chosen subclusters in index order, under the cluster's rank
+    // for the head, then -1
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (!((mask >> h) & 1u)) continue;
+      const bool mine = (sm >> h) & 1u;
+      const unsigned long long bits = __ballot(mine);
+      const int rch = a.ws.cl_rank[cg * G + h];
+      const int64_t base = (((int64_t)U.seq * a.Hq + U.kv_head * G + h) * a.c_stride + rch) * a.s_stride;
+      if (mine) a.sel_s[base + __popcll(bits & below)] = lane;
+      for (int j = __popcll(bits) + lane; j < a.s_stride; j += 64) a.sel_s[base + j] = -1;
+    }
+  }
+  {
+    const uint32_t rows = (lane < S && sm != 0u) ? (uint32_t)cnt : 0u;
+    const int rsum = (int)wave_reduce_uniform(rows, [](uint32_t p, uint32_t q) { return p + q; }, 0u);
+    if (lane == 0) atomicAdd(&a.ws.unit_rows[u], rsum);
+  }
+  TileRec* ctiles = a.ws.tiles + tile_unit_base(U.row_base, U.cl_base, u, a.L.fold_cap) + uni(tb_raw);
+  const int n_tiles =
+      write_run_tiles(ctiles, U.row_base, a.L_head_dim, lane < S ? o_i : 0, lane < S ? o_n : 0, lane < S ? sm : 0u);
+  if (lane == 0) a.ws.ch_ntiles[cw + x] = n_tiles;
+  if (!a.residual) return;
+  // residual of the subclusters a choosing head left out: every lane holds
+  // VPL elements of each such subcluster's value mean
+  const uint32_t need = (lane < S && cnt > 0) ? (mask & ~sm) : 0u;
+  const unsigned long long any_need = __ballot(need != 0u);
+  float vb[SR][VPL];
+#pragma unroll
+  for (int k = 0; k < SR; ++k)
+    if ((any_need >> k) & 1ull) load_floats<VPL>(a.L.sub_vbar + (sg0 + k) * D + lane * VPL, vb[k]);
+  float rm[G], rl[G], ro[G][VPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    rm[h] = -INFINITY;
+    rl[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) ro[h][e] = 0.f;
+  }
+#pragma unroll
+  for (int k = 0; k < SR; ++k) {
+    if (!((any_need >> k) & 1ull)) continue;
+    const uint32_t nk = (uint32_t)__builtin_amdgcn_readlane((int)need, k);
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      if ((nk >> h) & 1u) add_group<VPL>(rm[h], rl[h], ro[h], sc[h * SR + k], vb[k]);
+  }
+  // the wave's record: one (o, m, l) row per head
+  float* dst = a.ws.res_part + ((int64_t)u * a.nb_res + x) * G * RS;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) dst[h * RS + lane * VPL + e] = ro[h][e];
+    if (lane == 0) *reinterpret_cast<float2*>(dst + h * RS + D) = float2{rm[h], rl[h]};
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1723,11 +1901,17 @@ static hipError_t decode_impl(const DecodeLaunch& x, const DArgs& a, const Budge
   // exact ones, in the spread of their end times; the feature-map residual's
   // in the subcluster kernel; none without a residual
   if (!x.whole) {
-    const int nrest_sub = x.residual == 2 ? a.rest_per_unit : 0;
-    // (no chosen cluster anywhere and no feature-map residual: nothing to do)
-    if (x.nb_chosen + nrest_sub > 0)
-      hipLaunchKernelGGL((k_subclusters<D, G>), dim3(nu, x.nb_chosen + nrest_sub), dim3(256), 0, s, a, b,
-                         x.nb_chosen, nrest_sub);
+    if (x.residual != 2 && !x.shared && x.L.fold_capacity == 0) {
+      // one wave per chosen cluster
+      if (x.nb_chosen > 0)
+        hipLaunchKernelGGL((k_sub_wave<D, G>), dim3(nu, (x.nb_chosen + 3) / 4), dim3(256), 0, s, a, b, x.nb_chosen);
+    } else {
+      const int nrest_sub = x.residual == 2 ? a.rest_per_unit : 0;
+      // (no chosen cluster anywhere and no feature-map residual: nothing to do)
+      if (x.nb_chosen + nrest_sub > 0)
+        hipLaunchKernelGGL((k_subclusters<D, G>), dim3(nu, x.nb_chosen + nrest_sub), dim3(256), 0, s, a, b,
+                           x.nb_chosen, nrest_sub);
+    }
   }
   const int nrest = x.residual == 1 ? nu * a.rest_per_unit : 0;
   // the timing events (if any) are taken by the dispatches themselves: the
