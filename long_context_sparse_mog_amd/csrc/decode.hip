@@ -250,8 +250,13 @@ __global__ __launch_bounds__(256) void k_score_clusters(DArgs a) {
     load_floats<EPL>(a.L.cl_ms + (U.cl_base + g) * (2 * D) + lane * EPL, x[k]);
   }
   // the R x G partial dot products, summed over the lanes by one
-  // reduce-scatter: one lane then holds each (cluster, head) score
+  // reduce-scatter: one lane then holds each (cluster, head) score; the
+  // lane's cluster is known now, so its bounds load with the rows
   constexpr int R = kScoreRowsPerWave;
+  const int j = rs_index<R * G>(lane), g = g0 + j / G;
+  const int gc = min(g, U.C - 1);
+  const int ob0 = off[gc * U.S], ob1 = off[(gc + 1) * U.S];
+  const int nf = a.L.fold_cap ? a.L.cl_fold[U.cl_base + gc] : 0;
   float part[R * G];
 #pragma unroll
   for (int k = 0; k < R; ++k) {
@@ -264,10 +269,8 @@ __global__ __launch_bounds__(256) void k_score_clusters(DArgs a) {
     }
   }
   const float t = wave_reduce_scatter<R * G>(part);
-  const int j = rs_index<R * G>(lane), g = g0 + j / G;
   if (rs_owner<R * G>(lane) && g < U.C) {
-    const int nr = off[(g + 1) * U.S] - off[g * U.S];
-    const int nf = a.L.fold_cap ? a.L.cl_fold[U.cl_base + g] : 0;
+    const int nr = ob1 - ob0;
     const int n = nr + nf;
     a.ws.cl_score[((int64_t)u * G + j % G) * a.cstride + g] = n > 0 ? t + log2f((float)n) : -INFINITY;
     // the most tile slots the cluster can need if chosen (one partial tile
@@ -278,7 +281,7 @@ __global__ __launch_bounds__(256) void k_score_clusters(DArgs a) {
       const int64_t cg = (int64_t)u * a.cstride + g;
       if (a.whole) {
         a.ws.cl_tiles[cg] = nr;
-        a.ws.cl_row0[cg] = off[g * U.S];
+        a.ws.cl_row0[cg] = ob0;
       } else {
         a.ws.cl_tiles[cg] = (nr + 31) / 32 + U.S + nf;
       }
