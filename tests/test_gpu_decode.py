@@ -126,6 +126,26 @@ def test_bf16_d64():
                                  n_components=32))
 
 
+@pytest.mark.parametrize("residual", [True, False])
+def test_subcluster_budgets_mixed(residual):
+    # per-sequence subcluster budgets below S, zero and above S in one batch;
+    # checked against the oracle with the selection outputs, and the same
+    # step without them must give the same bits
+    wl = synth.config(4, seq_lens=[3000, 9000, 1000], n_kv_heads=2, n_q_heads=8, high_entropy_heads=(1,),
+                      n_components=64)
+    tc, ts = [6, 4, 3], [2, 0, 40]
+    b, kv, lays, out = run_decode_case(wl, residual=residual, top_c=tc, top_s=ts)
+    lay = ops.import_layout(kv, wl.n_sink, wl.n_recent,
+                            [unit_layout_arrays(lays[u]) for u in range(wl.n_seq * wl.n_kv_heads)])
+    params = ops.decode_params(wl.n_q_heads, tc, ts, residual=residual)
+    q = b.Q[0].contiguous()
+    o1, l1, _, _ = ops.mog_decode(lay, kv, q, params, want_sel=True)
+    o2, l2, _, _ = ops.mog_decode(lay, kv, q, params, want_sel=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert np.array_equal(o1.cpu().numpy(), out)
+
+
 @pytest.mark.parametrize("ns,nr,L", [(0, 16, 700), (16, 0, 700), (0, 0, 500), (2, 3, 6), (4, 4, 9)])
 def test_anchor_edges(ns, nr, L):
     wl = synth.config(1, seq_lens=[L], n_kv_heads=1, n_q_heads=2, n_components=8, n_sink=ns,
