@@ -1373,9 +1373,16 @@ __device__ BlockShare wave_find_share(const int32_t* unit_rows, int n_units, int
   } else {
     for (int v = lane; v < n_units; v += 64) part += (long long)A + unit_rows[v];
   }
+  long long total;
+  if (in_regs) {
+    // (at most 256 units of at most 2^22 + A rows: the sum fits 32 bits, and
+    // DPP sums are cheaper than 64-bit lane exchanges)
+    total = (long long)wave_reduce_uniform((uint32_t)part, [](uint32_t x, uint32_t y) { return x + y; }, 0u);
+  } else {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
-  const long long total = part;
+    for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+    total = part;
+  }
   const long long by_rows = (total + 255) / 256;
   const int B = (int)(nblk - n_units < by_rows ? nblk : n_units + by_rows);
   // blocks n_u(r) summed over the units (r >= 0: monotone in r)
