@@ -240,7 +240,7 @@ DecodePlan plan_decode(const mog_layout* L, const mog_decode_params* p) {
     d.splits = std::max(1, kExactResidentBlocks - L->n_units);
   }
   d.nblk = d.splits + L->n_units;
-  d.nb_res = d.nb_chosen + (int)ceil_div(L->max_C, kRestClustersPerBlock);
+  d.nb_res = d.nb_chosen + (int)ceil_div(L->max_C, kRestClustersSmall);  // (the smaller residual blocks: most records)
   const int D = L->head_dim, G = d.G, RS = D + kPartPad;
   const int64_t nu = L->n_units;
   size_t o = kAlign;  // first 256 bytes: reserved, kept zero

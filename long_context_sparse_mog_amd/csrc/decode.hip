@@ -60,7 +60,8 @@ struct DArgs {
   int32_t score_blocks;  // blocks of the cluster-score kernel per unit that score clusters
   int32_t L_head_dim;
   int32_t whole;          // whole-cluster step (top-c lists the tiles, no subcluster kernel)
-  int32_t rest_per_unit;  // residual blocks per unit: ceil(largest C / kRestClustersPerBlock)
+  int32_t rest_cl;        // clusters per residual block (rest_clusters_per_block)
+  int32_t rest_per_unit;  // residual blocks per unit: ceil(largest C / rest_cl)
   // every unit has the same geometry (equal lengths and fold counts at the
   // build): its record follows from its index (uni_C > 0), else it is loaded
   int32_t uni_C, uni_S, uni_nmid, uni_N, uni_nfold;
@@ -708,23 +709,21 @@ __device__ inline void load_fz(const float* row, int FM, float (&z)[4]) {
   for (int k = 0; k < 4; ++k) z[k] = 64 * k < FM ? row[lane + 64 * k] : 0.f;
 }
 
-// Gaussian residual of clusters [R y, R y + R) of unit u (R =
-// kRestClustersPerBlock): every head that left a cluster out adds its term
-// 2^score v-bar.  A wave takes R / 4 clusters, in batches whose loads are all
-// issued before any is used: the whole share at once where its registers
-// stay within 128 per lane (clusters past C re-read the last one and are
+// Gaussian residual of clusters [R y, R y + R) of unit u (R = 4 RCW): every
+// head that left a cluster out adds its term 2^score v-bar.  A wave takes RCW
+// clusters, in batches whose loads are all issued before any is used: the
+// whole share at once where its registers stay within 128 per lane (clusters past C re-read the last one and are
 // skipped; an empty cluster scores -inf for every head, so its size is not
 // needed).
-template <int D, int G>
+template <int D, int G, int RCW>
 __device__ inline void rest_clusters(const DArgs& a, int u, int C, int64_t cl_base, int y, float (&rm)[G],
                                      float (&rl)[G], float (&ro)[G][D / 64]) {
   constexpr int VPL = D / 64;
-  constexpr int RCW = kRestClustersPerBlock / 4;
   constexpr int RB = (VPL + G + 1) * RCW <= 128 ? RCW : RCW / 2;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t cw = (int64_t)u * a.cstride;
   const uint32_t all = (1u << G) - 1u;
-  const int g0 = y * kRestClustersPerBlock + wave * RCW;
+  const int g0 = (y * 4 + wave) * RCW;
 #pragma unroll
   for (int k0 = 0; k0 < RCW; k0 += RB) {
     uint32_t mask[RB];
@@ -1477,14 +1476,14 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
   if ((int)blockIdx.x >= a.nblk) {
     // the Gaussian residual of the clusters some head left out, in blocks
     // after the exact ones (dispatched as exact blocks retire); record y of
-    // unit u covers clusters [R y, R y + R) (R = kRestClustersPerBlock),
+    // unit u covers clusters [R y, R y + R) (R = rest_cl),
     // after the unit's chosen-
     // cluster records (none for a whole-cluster step)
     const int r = (int)blockIdx.x - a.nblk;
     const int u = r / a.rest_per_unit, y = r % a.rest_per_unit;
     const int n_ch_raw = a.whole ? 0 : a.ws.n_chosen[u];
     const mog_unit U = uni_unit(a.L.units + u);
-    if (y * kRestClustersPerBlock >= U.C) return;
+    if (y * a.rest_cl >= U.C) return;
     constexpr int VPL = D / 64;
     float rm[G], rl[G], ro[G][VPL];
 #pragma unroll
@@ -1494,7 +1493,10 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
 #pragma unroll
       for (int e = 0; e < VPL; ++e) ro[h][e] = 0.f;
     }
-    rest_clusters<D, G>(a, u, U.C, U.cl_base, y, rm, rl, ro);
+    if (a.rest_cl == kRestClustersSmall)
+      rest_clusters<D, G, kRestClustersSmall / 4>(a, u, U.C, U.cl_base, y, rm, rl, ro);
+    else
+      rest_clusters<D, G, kRestClustersPerBlock / 4>(a, u, U.C, U.cl_base, y, rm, rl, ro);
     store_wave_states<D, G>(st, rm, rl, ro);
     __syncthreads();
     write_block_record<D, G>(st, a.ws.res_part + ((int64_t)u * a.nb_res + uni(n_ch_raw) + y) * G * RS);
@@ -1729,9 +1731,9 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(1024) void k_merge(const float* part, int n_part, const int32_t* uinfo,
-                                                const float* res, int res_stride, const int32_t* n_chosen,
-                                                const mog_unit* units, int G, int Hq, int Hkv, float* out,
-                                                float* lse) {
+                                                const float* res, int res_stride, int rest_cl,
+                                                const int32_t* n_chosen, const mog_unit* units, int G, int Hq,
+                                                int Hkv, float* out, float* lse) {
   constexpr int RS = D + kPartPad;
   constexpr int QL = D / 8;        // lanes per record (8 elements each)
   constexpr int NG = 1024 / QL;    // records folded side by side
@@ -1751,9 +1753,9 @@ __global__ __launch_bounds__(1024) void k_merge(const float* part, int n_part, c
   const float* eb = part + (first * G + h) * RS;
   // residual records of the unit: one per chosen cluster (none without
   // n_chosen: a whole-cluster step leaves nothing out of a chosen cluster),
-  // then one per kRestClustersPerBlock clusters
+  // then one per rest_cl clusters
   int n_res = 0;
-  if (res) n_res = (n_chosen ? n_chosen[u] : 0) + (units[u].C + kRestClustersPerBlock - 1) / kRestClustersPerBlock;
+  if (res) n_res = (n_chosen ? n_chosen[u] : 0) + (units[u].C + rest_cl - 1) / rest_cl;
   const float* rb = res ? res + ((int64_t)u * res_stride * G + h) * RS : nullptr;
   const int total = n_part + (res ? n_res : 0);
   const int q = tid % QL, grp = tid / QL;
@@ -1938,8 +1940,8 @@ static hipError_t decode_impl(const DecodeLaunch& x, const DArgs& a, const Budge
   }
   hipLaunchKernelGGL((k_merge<D>), dim3(x.Hq, x.L.n_seq), dim3(1024), 0, s, a.ws.ex_part, 0,
                      (const int32_t*)a.ws.uinfo, x.residual ? (const float*)a.ws.res_part : nullptr, x.nb_res,
-                     x.whole ? nullptr : (const int32_t*)a.ws.n_chosen, (const mog_unit*)x.L.units, G, x.Hq,
-                     x.L.n_kv_heads, x.out, x.lse);
+                     a.rest_cl, x.whole ? nullptr : (const int32_t*)a.ws.n_chosen, (const mog_unit*)x.L.units, G,
+                     x.Hq, x.L.n_kv_heads, x.out, x.lse);
   return hipGetLastError();
 }
 
@@ -2014,7 +2016,8 @@ hipError_t launch_decode(const DecodeLaunch& x, hipStream_t s) {
     a.uni_N = x.L.seq_lens[0];
     a.uni_nfold = x.L.fold_count[0];
   }
-  a.rest_per_unit = (x.L.max_C + kRestClustersPerBlock - 1) / kRestClustersPerBlock;
+  a.rest_cl = rest_clusters_per_block(x.residual, x.L.n_units, x.L.max_C);
+  a.rest_per_unit = (x.L.max_C + a.rest_cl - 1) / a.rest_cl;
   a.ws = x.ws;
   BudgetArgs b;
   for (int i = 0; i < MOG_MAX_SEQ; ++i) {
@@ -2038,7 +2041,7 @@ static hipError_t dense_impl(const DenseLaunch& x, hipStream_t s) {
     }
   }
   hipLaunchKernelGGL((k_merge<D>), dim3(x.Hq, x.seq.n_seq), dim3(1024), 0, s, x.ex_part, x.splits,
-                     (const int32_t*)nullptr, (const float*)nullptr, 0, (const int32_t*)nullptr,
+                     (const int32_t*)nullptr, (const float*)nullptr, 0, 1, (const int32_t*)nullptr,
                      (const mog_unit*)nullptr, G, x.Hq, x.n_kv_heads, x.out, x.lse);
   return hipGetLastError();
 }

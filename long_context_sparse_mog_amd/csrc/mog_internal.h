@@ -153,7 +153,7 @@ struct DecodeLaunch {
   int32_t shared;       // one selection per KV head
   int32_t splits;       // target exact blocks in total (balanced over units)
   int32_t nblk;         // exact blocks launched: splits + n_units
-  int32_t nb_res;       // residual record slots per unit: nb_chosen + max_C / kRestClustersPerBlock
+  int32_t nb_res;       // residual record slots per unit: nb_chosen + ceil(max_C / kRestClustersSmall)
   int32_t nb_chosen;    // chosen-cluster blocks per unit (max G * top_c)
   int32_t whole;        // whole-cluster step: every sequence's top_s reaches its S, no folded
                         // rows, Gaussian residual or none, no subcluster output, at most
@@ -181,7 +181,19 @@ struct DenseLaunch {
   float* ex_part;       // [n_units][splits][G][D+4]
 };
 
-constexpr int kRestClustersPerBlock = 64;  // residual-only blocks: 16 clusters per wave
+// Residual-only blocks (the clusters some head left out) take
+// kRestClustersPerBlock clusters (16 per wave), or kRestClustersSmall (4 per
+// wave) when that makes at most kRestSmallMaxBlocks of them in all: few
+// small blocks fit in the spread of the exact blocks' end times, many queue
+// behind them.  The feature-map residual always takes the large blocks.
+constexpr int kRestClustersPerBlock = 64;
+constexpr int kRestClustersSmall = 16;
+constexpr int kRestSmallMaxBlocks = 1024;
+__host__ __device__ inline int rest_clusters_per_block(int residual, int n_units, int max_C) {
+  if (residual == 2) return kRestClustersPerBlock;
+  const int64_t small = (int64_t)n_units * ((max_C + kRestClustersSmall - 1) / kRestClustersSmall);
+  return small <= kRestSmallMaxBlocks ? kRestClustersSmall : kRestClustersPerBlock;
+}
 constexpr int kPartPad = 4;
 // blocks of the exact-attention kernel resident at once on the chip: 256
 // compute units x 2 (its registers allow 2 waves per SIMD)
