@@ -186,7 +186,7 @@ KVRef make_kvref(const mog_kv* kv) {
 // Decode geometry
 // ------------------------------------------------------------------------
 struct DecodePlan {
-  int G, c_stride, s_stride, splits, nblk, nb_res, nb_chosen;
+  int G, c_stride, s_stride, splits, nblk, nb_res, nb_chosen, half;
   size_t o_clscore, o_cllse, o_clmask, o_cltiles, o_clrow0, o_chrow0, o_chnm, o_clrank, o_urows, o_list, o_nch, o_uinfo, o_tbase, o_ntl, o_tiles, o_res, o_ex;
   size_t o_fq, bytes;
 };
@@ -240,6 +240,10 @@ DecodePlan plan_decode(const mog_layout* L, const mog_decode_params* p) {
     d.splits = std::max(1, kExactResidentBlocks - L->n_units);
   }
   d.nblk = d.splits + L->n_units;
+  // exact blocks in halves of 2 waves with units of their own (finer shares)
+  // when more than 16 units split the blocks and every unit's chosen list
+  // fits a wave's own list
+  d.half = (L->n_units > kExactResidentBlocks / 32 && d.nb_chosen <= kWaveListMax) ? 1 : 0;
   d.nb_res = d.nb_chosen + (int)ceil_div(L->max_C, kRestClustersSmall);  // (the smaller residual blocks: most records)
   const int D = L->head_dim, G = d.G, RS = D + kPartPad;
   const int64_t nu = L->n_units;
@@ -265,7 +269,7 @@ DecodePlan plan_decode(const mog_layout* L, const mog_decode_params* p) {
   o = align_up(o + (size_t)(tile_unit_base(L->total_mid, L->total_cl, (int)nu, L->fold_capacity) + 2) *
                        sizeof(TileRec));
   d.o_res = o; o = align_up(o + (size_t)nu * d.nb_res * G * RS * 4);
-  d.o_ex = o; o = align_up(o + (size_t)d.nblk * G * RS * 4);
+  d.o_ex = o; o = align_up(o + (size_t)d.nblk * (d.half ? 2 : 1) * G * RS * 4);
   // feature-map residual: each query head's features, [n_units][G][fm_dim]
   d.o_fq = o;
   if (p->residual == 2) o = align_up(o + (size_t)nu * G * L->fm_dim * 4);
@@ -613,6 +617,7 @@ static mog_status decode_with_ws(const mog_layout* layout, const mog_kv* kv, con
   x.shared = params->shared_selection;
   x.splits = d.splits;
   x.nblk = d.nblk;
+  x.half = d.half;
   x.nb_res = d.nb_res;
   x.nb_chosen = d.nb_chosen;
   // whole-cluster step: every chosen cluster is read entirely, so there are

@@ -539,32 +539,35 @@ struct RowAcc {
 // empty record (m = -inf)
 __device__ inline float exp2_or_zero(float m, float M) { return m == -INFINITY ? 0.f : exp2f(m - M); }
 
-// Block epilogue: merge the 4 wave states in st ([4][G][D+4]: o[D], m, l,
-// two pad words, so every row starts 16-byte aligned) into one record per
-// head, dst[h][0..D) = o, dst[h][D] = m, dst[h][D+1] = l (G x (D+4) floats).
-// One float4 of o per thread.  Called by all 256 threads after a barrier that
+// Epilogue: merge NWS wave states in st, rows (w0 + w) G + h for w < NWS
+// (st is [4][G][D+4]: o[D], m, l, two pad words, so every row starts 16-byte
+// aligned), into one record per head, dst[h][0..D) = o, dst[h][D] = m,
+// dst[h][D+1] = l (G x (D+4) floats).  One float4 of o per thread; thread t
+// of the nt threads that write this record.  Called after a barrier that
 // made st visible.
-template <int D, int G>
-__device__ inline void write_block_record(const float* st, float* dst) {
+template <int D, int G, int NWS>
+__device__ inline void write_record(const float* st, int w0, float* dst, int t, int nt) {
   constexpr int RS = D + kPartPad;
   constexpr int Q = D / 4;
-  for (int idx = threadIdx.x; idx < G * Q; idx += 256) {
+  for (int idx = t; idx < G * Q; idx += nt) {
     const int h = idx / Q, e4 = idx % Q;
-    float mw[4], lw[4];
-    float4 ow[4];
+    float mw[NWS], lw[NWS];
+    float4 ow[NWS];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float* r = st + (w * G + h) * RS;
+    for (int w = 0; w < NWS; ++w) {
+      const float* r = st + ((w0 + w) * G + h) * RS;
       const float2 ml = *reinterpret_cast<const float2*>(r + D);
       mw[w] = ml.x;
       lw[w] = ml.y;
       ow[w] = reinterpret_cast<const float4*>(r)[e4];
     }
-    const float M = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
+    float M = mw[0];
+#pragma unroll
+    for (int w = 1; w < NWS; ++w) M = fmaxf(M, mw[w]);
     float L = 0.f;
     float4 O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NWS; ++w) {
       const float f = exp2_or_zero(mw[w], M);
       L += f * lw[w];
       O.x += f * ow[w].x;
@@ -575,6 +578,12 @@ __device__ inline void write_block_record(const float* st, float* dst) {
     reinterpret_cast<float4*>(dst + h * RS)[e4] = O;
     if (e4 == 0) *reinterpret_cast<float2*>(dst + h * RS + D) = float2{M, L};
   }
+}
+
+// Block epilogue: the 4 wave states of a block, all 256 threads.
+template <int D, int G>
+__device__ inline void write_block_record(const float* st, float* dst) {
+  write_record<D, G, 4>(st, 0, dst, threadIdx.x, 256);
 }
 
 }  // namespace mog

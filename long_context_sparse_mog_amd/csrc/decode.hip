@@ -60,6 +60,7 @@ struct DArgs {
   int32_t score_blocks;  // blocks of the cluster-score kernel per unit that score clusters
   int32_t L_head_dim;
   int32_t whole;          // whole-cluster step (top-c lists the tiles, no subcluster kernel)
+  int32_t half;           // exact blocks in halves of 2 waves, each with a unit share of its own
   int32_t rest_cl;        // clusters per residual block (rest_clusters_per_block)
   int32_t rest_per_unit;  // residual blocks per unit: ceil(largest C / rest_cl)
   // every unit has the same geometry (equal lengths and fold counts at the
@@ -1356,7 +1357,8 @@ struct BlockShare {
 constexpr int kShareRegs = 4;
 constexpr int kShareRounds = 3;
 
-__device__ BlockShare wave_find_share(const int32_t* unit_rows, int n_units, int nblk, int A, int want_block) {
+__device__ BlockShare wave_find_share(const int32_t* unit_rows, int n_units, int nblk, int A, int want_block,
+                                      int min_rows) {
   const int lane = threadIdx.x & 63;
   const bool in_regs = n_units <= 64 * kShareRegs;
   float w[kShareRegs];
@@ -1382,7 +1384,7 @@ __device__ BlockShare wave_find_share(const int32_t* unit_rows, int n_units, int
     for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
     total = part;
   }
-  const long long by_rows = (total + 255) / 256;
+  const long long by_rows = (total + min_rows - 1) / min_rows;
   const int B = (int)(nblk - n_units < by_rows ? nblk : n_units + by_rows);
   // blocks n_u(r) summed over the units (r >= 0: monotone in r)
   auto part_count = [&](float r) {
@@ -1503,212 +1505,226 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
     return;
   }
   const int A = a.n_sink + a.n_recent;
-  const BlockShare bs = wave_find_share(a.ws.unit_rows, a.n_units, a.nblk, A, blockIdx.x);
+  // Shares: one per block, or with `half` one per half block (waves 0-1
+  // and 2-3 serve units of their own: finer shares when many units split
+  // the blocks)
+  const int WPS = a.half ? 2 : 4;                   // waves per share
+  const int hf = a.half ? wave >> 1 : 0;            // the wave's share in the block
+  const int ws_wave = a.half ? wave & 1 : wave;     // the wave's index in its share
+  const int slot = a.half ? 2 * (int)blockIdx.x + hf : (int)blockIdx.x;
+  const BlockShare bs = wave_find_share(a.ws.unit_rows, a.n_units, a.half ? 2 * a.nblk : a.nblk, A, slot,
+                                        a.half ? 128 : 256);
   const int u = bs.u;
-  if (u < 0) return;
-  const int p = blockIdx.x - bs.first, splits_u = bs.n;
-  if (p == 0 && tid == 0) {
-    a.ws.uinfo[2 * u] = bs.first;
-    a.ws.uinfo[2 * u + 1] = bs.n;
-  }
-  const mog_unit U = uni_unit(a.L.units + u);
-  const int C = U.C, S = U.S;
-  u32x4* buf = kvbuf[wave];
+  // (a share with no unit leaves; a half block's idle half still meets the
+  // other half at the epilogue's barriers)
+  if (u < 0 && !a.half) return;
   Engine acc;
-  // tile counts of the chosen clusters (in list order) -> exclusive prefix.
-  // Lists of up to 256 clusters (the usual case): each wave loads the four
-  // entries of each lane without waiting for the list length (issued before
-  // the query's loads, so one wait covers both) and scans them itself into
-  // its own LDS rows, with no barrier.  Longer lists: a block scan, E entries
-  // per thread.
-  const int64_t cw = (int64_t)u * a.cstride;
-  const int n_ch_raw = a.ws.n_chosen[u];
-  // (a whole-cluster step: rows | head mask << 24 and first rows)
-  const int32_t* la = a.whole ? reinterpret_cast<const int32_t*>(a.ws.ch_nm) : a.ws.ch_ntiles;
-  const int32_t* lb = a.whole ? a.ws.ch_row0 : a.ws.ch_tbase;
-  int wl[4], wt[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int x = min(4 * lane + k, a.cstride - 1);
-    wl[k] = la[cw + x];
-    wt[k] = lb[cw + x];
-  }
-  // (unit u is sequence u / Hkv, KV head u % Hkv: the query's address does
-  // not wait for the unit record)
-  acc.init(a.q + ((int64_t)(u / a.Hkv) * a.Hq + (int64_t)(u % a.Hkv) * G) * D, a.scale_l2, buf);
-  // (a whole-cluster step has at most kWaveListMax chosen clusters; the
-  // clamp only keeps every list access in range)
-  const int n_ch = a.whole ? min(uni(n_ch_raw), kWaveListMax) : uni(n_ch_raw);
-  const int* tp = lists;  // the prefix the listing searches, and the slot bases (or first rows)
-  const int* tb = lists + kMaxC + 1;
-  const int* tn = nullptr;  // a whole-cluster step's rows | head masks
-  if (n_ch <= kWaveListMax) {
-    int* wp = lists + wave * kWaveList;
-    int* wb = wp + kWaveListMax + 1;
-    int* wn = wb + kWaveListMax;
-    int cnt[4], sum = 0;
-#pragma unroll
+  if (u >= 0) {
+    const int p = slot - bs.first, splits_u = bs.n;
+    if (p == 0 && ws_wave == 0 && lane == 0) {
+      a.ws.uinfo[2 * u] = bs.first;
+      a.ws.uinfo[2 * u + 1] = bs.n;
+    }
+    const mog_unit U = uni_unit(a.L.units + u);
+    const int C = U.C, S = U.S;
+    u32x4* buf = kvbuf[wave];
+    // tile counts of the chosen clusters (in list order) -> exclusive prefix.
+    // Lists of up to 256 clusters (the usual case): each wave loads the four
+    // entries of each lane without waiting for the list length (issued before
+    // the query's loads, so one wait covers both) and scans them itself into
+    // its own LDS rows, with no barrier.  Longer lists: a block scan, E entries
+    // per thread.
+    const int64_t cw = (int64_t)u * a.cstride;
+    const int n_ch_raw = a.ws.n_chosen[u];
+    // (a whole-cluster step: rows | head mask << 24 and first rows)
+    const int32_t* la = a.whole ? reinterpret_cast<const int32_t*>(a.ws.ch_nm) : a.ws.ch_ntiles;
+    const int32_t* lb = a.whole ? a.ws.ch_row0 : a.ws.ch_tbase;
+    int wl[4], wt[4];
+  #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const bool in = 4 * lane + k < n_ch;
-      cnt[k] = !in ? 0 : a.whole ? (int)((((uint32_t)wl[k] & 0xffffffu) + 31u) >> 5) : wl[k];
-      sum += cnt[k];
+      const int x = min(4 * lane + k, a.cstride - 1);
+      wl[k] = la[cw + x];
+      wt[k] = lb[cw + x];
     }
-    const int incl = wave_incl_scan(sum);
-    int base = incl - sum;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (4 * lane + k < n_ch) {
-        wp[4 * lane + k] = base;
-        wb[4 * lane + k] = wt[k];
-        if (a.whole) wn[4 * lane + k] = wl[k];
+    // (unit u is sequence u / Hkv, KV head u % Hkv: the query's address does
+    // not wait for the unit record)
+    acc.init(a.q + ((int64_t)(u / a.Hkv) * a.Hq + (int64_t)(u % a.Hkv) * G) * D, a.scale_l2, buf);
+    // (a whole-cluster step has at most kWaveListMax chosen clusters; the
+    // clamp only keeps every list access in range)
+    const int n_ch = a.whole ? min(uni(n_ch_raw), kWaveListMax) : uni(n_ch_raw);
+    const int* tp = lists;  // the prefix the listing searches, and the slot bases (or first rows)
+    const int* tb = lists + kMaxC + 1;
+    const int* tn = nullptr;  // a whole-cluster step's rows | head masks
+    if (n_ch <= kWaveListMax) {
+      int* wp = lists + wave * kWaveList;
+      int* wb = wp + kWaveListMax + 1;
+      int* wn = wb + kWaveListMax;
+      int cnt[4], sum = 0;
+  #pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const bool in = 4 * lane + k < n_ch;
+        cnt[k] = !in ? 0 : a.whole ? (int)((((uint32_t)wl[k] & 0xffffffu) + 31u) >> 5) : wl[k];
+        sum += cnt[k];
       }
-      base += cnt[k];
-    }
-    if (lane == 63) wp[n_ch] = incl;
-    __asm__ volatile("" ::: "memory");  // (a wave's LDS operations run in order)
-    tp = wp;
-    tb = wb;
-    tn = wn;
-  } else {
-    int* tpre = lists;
-    int* tbs = lists + kMaxC + 1;
-    constexpr int EM = kMaxC / 256;
-    const int E = (n_ch + 255) / 256;
-    int loc[EM], tbl[EM];
-#pragma unroll
-    for (int k = 0; k < EM; ++k) {
-      const int x = min(tid * E + k, a.cstride - 1);
-      loc[k] = a.ws.ch_ntiles[cw + x];
-      tbl[k] = a.ws.ch_tbase[cw + x];
-    }
-    int sum = 0;
-#pragma unroll
-    for (int k = 0; k < EM; ++k) {
-      loc[k] = (k < E && tid * E + k < n_ch) ? loc[k] : 0;
-      sum += loc[k];
-    }
-    int total;
-    int base = block_excl_scan<256>(sum, sh, total);
-#pragma unroll
-    for (int k = 0; k < EM; ++k) {
-      const int x = tid * E + k;
-      if (k < E && x < n_ch) {
-        tpre[x] = base;
-        tbs[x] = tbl[k];
+      const int incl = wave_incl_scan(sum);
+      int base = incl - sum;
+  #pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (4 * lane + k < n_ch) {
+          wp[4 * lane + k] = base;
+          wb[4 * lane + k] = wt[k];
+          if (a.whole) wn[4 * lane + k] = wl[k];
+        }
+        base += cnt[k];
       }
-      base += loc[k];
-    }
-    if (tid == 0) tpre[n_ch] = total;
-    __syncthreads();
-  }
-  // virtual tiles of the unit: [sink tiles | recent tiles | chosen clusters'
-  // tiles in list order]; wave w of the unit takes [w NT / NW, (w+1) NT / NW)
-  const int n_st = (a.n_sink + 31) / 32, n_rt = (a.n_recent + 31) / 32, n_at = n_st + n_rt;
-  const int NT = n_at + uni(tp[n_ch]);
-  const int NW = splits_u * 4;
-  const int w = p * 4 + wave;
-  int k0 = (int)((int64_t)w * NT / NW);
-  const int k1 = (int)((int64_t)(w + 1) * NT / NW);
-  const T* kc = static_cast<const T*>(a.kv.k);
-  const T* vc = static_cast<const T*>(a.kv.v);
-  const uint32_t all = (1u << G) - 1u;
-  const KVRef kv = a.kv;
-  // first token and row count of anchor tile k (< n_at)
-  auto anchor_tile = [&](int k, int& tok, int& nr) {
-    if (k < n_st) {
-      tok = 32 * k;
-      nr = min(32, a.n_sink - 32 * k);
+      if (lane == 63) wp[n_ch] = incl;
+      __asm__ volatile("" ::: "memory");  // (a wave's LDS operations run in order)
+      tp = wp;
+      tb = wb;
+      tn = wn;
     } else {
-      const int j = k - n_st;
-      tok = U.N - a.n_recent + 32 * j;
-      nr = min(32, a.n_recent - 32 * j);
-    }
-  };
-  if (kv.paged) {
-    // anchors of a paged cache: rows gathered through the block table
-    for (; k0 < k1 && k0 < n_at; ++k0) {
-      int tok, nr;
-      anchor_tile(k0, tok, nr);
-      acc.tile_gather(buf, kc, vc, nr, all, [&](int i) { return kv_row_offset(kv, U.seq, U.kv_head, tok + i, D); });
-    }
-  }
-  if (k0 < k1) {
-    const T* km = static_cast<const T*>(a.L.k_mid);
-    const T* vm = static_cast<const T*>(a.L.v_mid);
-    const TileRec* utiles = a.ws.tiles + tile_unit_base(U.row_base, U.cl_base, u, a.L.fold_cap);
-    TileRec* tl = tiles[wave];
-    const int64_t anc_base = kv.paged ? 0 : kv_row_offset(kv, U.seq, U.kv_head, 0, D);
-    while (k0 < k1) {
-      // (1) list the next batch in LDS, one tile per lane: an anchor tile
-      //     of a contiguous cache, or the chosen cluster's slot (binary
-      //     search of the prefix, then one 16-byte load)
-      const int nt = min(kTileBatch, k1 - k0);
-      if (lane < nt) {
-        const int k = k0 + lane;
-        TileRec r;
-        if (k < n_at) {
-          int tok, nr;
-          anchor_tile(k, tok, nr);
-          r = TileRec{anc_base + (int64_t)tok * D, nr | (int)0x80000000, 0xffffffffu};
-        } else {
-          const int kv_ = k - n_at;
-          int lo = 0, hi = n_ch;  // last x with tp[x] <= kv_
-          while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (tp[mid] <= kv_) lo = mid; else hi = mid;
-          }
-          const int jt = kv_ - tp[lo];
-          if (a.whole) {
-            // tile jt of a whole cluster: its rows from the first, 32 at a time
-            const uint32_t nm = (uint32_t)tn[lo];
-            r = TileRec{(U.row_base + tb[lo] + 32 * jt) * (int64_t)D, min(32, (int)(nm & 0xffffffu) - 32 * jt),
-                        nm >> 24};
-          } else {
-            r = utiles[tb[lo] + jt];
-          }
-        }
-        tl[lane] = r;
+      // (a whole block: half-block shares are used only when every unit's
+      // list fits a wave's own list, so this branch has no idle half)
+      int* tpre = lists;
+      int* tbs = lists + kMaxC + 1;
+      constexpr int EM = kMaxC / 256;
+      const int E = (n_ch + 255) / 256;
+      int loc[EM], tbl[EM];
+  #pragma unroll
+      for (int k = 0; k < EM; ++k) {
+        const int x = min(tid * E + k, a.cstride - 1);
+        loc[k] = a.ws.ch_ntiles[cw + x];
+        tbl[k] = a.ws.ch_tbase[cw + x];
       }
-      k0 += nt;
-      // (2) stream the batch: the next tile's loads are in flight while the
-      //     current one is computed.  rd(i) is tile i of the batch, or past
-      //     the end an empty tile (0 rows: its loads read nothing), so every
-      //     load is issued unconditionally and the wait for a tile's
-      //     registers never has to cover the next tile's loads.
-      auto rd = [&](int i) {
-        const TileRec r = tl[i < nt ? i : nt - 1];
-        TileDesc t;
-        t.off = uni(r.off);
-        const int ns = uni(r.nrows_src);
-        t.nrows = i < nt ? (ns & 0x7fffffff) : 0;
-        t.src = (int)((uint32_t)ns >> 31);
-        t.mask = (uint32_t)uni((int)r.mask);
-        return t;
-      };
-      auto kp = [&](const TileDesc& t) { return (t.src ? kc : km) + t.off; };
-      auto vp = [&](const TileDesc& t) { return (t.src ? vc : vm) + t.off; };
-      if constexpr (Engine::PIPELINED) {
-        typename Engine::Regs ra, rb;
-        TileDesc ta = rd(0), tb;
-        Engine::load(kp(ta), vp(ta), ta.nrows, ra.k, ra.v);
-        // the scheduling barriers keep each tile's loads ahead of the
-        // previous tile's arithmetic (the scheduler would otherwise sink them
-        // to save registers and serialise load and compute)
-        for (int i = 0; i < nt; i += 2) {
-          tb = rd(i + 1);
-          Engine::load(kp(tb), vp(tb), tb.nrows, rb.k, rb.v);
-          __builtin_amdgcn_sched_barrier(0);
-          acc.compute(buf, ra.k, ra.v, ta.nrows, ta.mask);
-          if (i + 1 >= nt) break;
-          ta = rd(i + 2);
-          Engine::load(kp(ta), vp(ta), ta.nrows, ra.k, ra.v);
-          __builtin_amdgcn_sched_barrier(0);
-          acc.compute(buf, rb.k, rb.v, tb.nrows, tb.mask);
+      int sum = 0;
+  #pragma unroll
+      for (int k = 0; k < EM; ++k) {
+        loc[k] = (k < E && tid * E + k < n_ch) ? loc[k] : 0;
+        sum += loc[k];
+      }
+      int total;
+      int base = block_excl_scan<256>(sum, sh, total);
+  #pragma unroll
+      for (int k = 0; k < EM; ++k) {
+        const int x = tid * E + k;
+        if (k < E && x < n_ch) {
+          tpre[x] = base;
+          tbs[x] = tbl[k];
         }
+        base += loc[k];
+      }
+      if (tid == 0) tpre[n_ch] = total;
+      __syncthreads();
+    }
+    // virtual tiles of the unit: [sink tiles | recent tiles | chosen clusters'
+    // tiles in list order]; wave w of the unit takes [w NT / NW, (w+1) NT / NW)
+    const int n_st = (a.n_sink + 31) / 32, n_rt = (a.n_recent + 31) / 32, n_at = n_st + n_rt;
+    const int NT = n_at + uni(tp[n_ch]);
+    const int NW = splits_u * WPS;
+    const int w = p * WPS + ws_wave;
+    int k0 = (int)((int64_t)w * NT / NW);
+    const int k1 = (int)((int64_t)(w + 1) * NT / NW);
+    const T* kc = static_cast<const T*>(a.kv.k);
+    const T* vc = static_cast<const T*>(a.kv.v);
+    const uint32_t all = (1u << G) - 1u;
+    const KVRef kv = a.kv;
+    // first token and row count of anchor tile k (< n_at)
+    auto anchor_tile = [&](int k, int& tok, int& nr) {
+      if (k < n_st) {
+        tok = 32 * k;
+        nr = min(32, a.n_sink - 32 * k);
       } else {
-        for (int i = 0; i < nt; ++i) {
-          const TileDesc t = rd(i);
-          acc.tile(buf, kp(t), vp(t), t.nrows, t.mask);
+        const int j = k - n_st;
+        tok = U.N - a.n_recent + 32 * j;
+        nr = min(32, a.n_recent - 32 * j);
+      }
+    };
+    if (kv.paged) {
+      // anchors of a paged cache: rows gathered through the block table
+      for (; k0 < k1 && k0 < n_at; ++k0) {
+        int tok, nr;
+        anchor_tile(k0, tok, nr);
+        acc.tile_gather(buf, kc, vc, nr, all, [&](int i) { return kv_row_offset(kv, U.seq, U.kv_head, tok + i, D); });
+      }
+    }
+    if (k0 < k1) {
+      const T* km = static_cast<const T*>(a.L.k_mid);
+      const T* vm = static_cast<const T*>(a.L.v_mid);
+      const TileRec* utiles = a.ws.tiles + tile_unit_base(U.row_base, U.cl_base, u, a.L.fold_cap);
+      TileRec* tl = tiles[wave];
+      const int64_t anc_base = kv.paged ? 0 : kv_row_offset(kv, U.seq, U.kv_head, 0, D);
+      while (k0 < k1) {
+        // (1) list the next batch in LDS, one tile per lane: an anchor tile
+        //     of a contiguous cache, or the chosen cluster's slot (binary
+        //     search of the prefix, then one 16-byte load)
+        const int nt = min(kTileBatch, k1 - k0);
+        if (lane < nt) {
+          const int k = k0 + lane;
+          TileRec r;
+          if (k < n_at) {
+            int tok, nr;
+            anchor_tile(k, tok, nr);
+            r = TileRec{anc_base + (int64_t)tok * D, nr | (int)0x80000000, 0xffffffffu};
+          } else {
+            const int kv_ = k - n_at;
+            int lo = 0, hi = n_ch;  // last x with tp[x] <= kv_
+            while (hi - lo > 1) {
+              const int mid = (lo + hi) >> 1;
+              if (tp[mid] <= kv_) lo = mid; else hi = mid;
+            }
+            const int jt = kv_ - tp[lo];
+            if (a.whole) {
+              // tile jt of a whole cluster: its rows from the first, 32 at a time
+              const uint32_t nm = (uint32_t)tn[lo];
+              r = TileRec{(U.row_base + tb[lo] + 32 * jt) * (int64_t)D, min(32, (int)(nm & 0xffffffu) - 32 * jt),
+                          nm >> 24};
+            } else {
+              r = utiles[tb[lo] + jt];
+            }
+          }
+          tl[lane] = r;
+        }
+        k0 += nt;
+        // (2) stream the batch: the next tile's loads are in flight while the
+        //     current one is computed.  rd(i) is tile i of the batch, or past
+        //     the end an empty tile (0 rows: its loads read nothing), so every
+        //     load is issued unconditionally and the wait for a tile's
+        //     registers never has to cover the next tile's loads.
+        auto rd = [&](int i) {
+          const TileRec r = tl[i < nt ? i : nt - 1];
+          TileDesc t;
+          t.off = uni(r.off);
+          const int ns = uni(r.nrows_src);
+          t.nrows = i < nt ? (ns & 0x7fffffff) : 0;
+          t.src = (int)((uint32_t)ns >> 31);
+          t.mask = (uint32_t)uni((int)r.mask);
+          return t;
+        };
+        auto kp = [&](const TileDesc& t) { return (t.src ? kc : km) + t.off; };
+        auto vp = [&](const TileDesc& t) { return (t.src ? vc : vm) + t.off; };
+        if constexpr (Engine::PIPELINED) {
+          typename Engine::Regs ra, rb;
+          TileDesc ta = rd(0), tb;
+          Engine::load(kp(ta), vp(ta), ta.nrows, ra.k, ra.v);
+          // the scheduling barriers keep each tile's loads ahead of the
+          // previous tile's arithmetic (the scheduler would otherwise sink them
+          // to save registers and serialise load and compute)
+          for (int i = 0; i < nt; i += 2) {
+            tb = rd(i + 1);
+            Engine::load(kp(tb), vp(tb), tb.nrows, rb.k, rb.v);
+            __builtin_amdgcn_sched_barrier(0);
+            acc.compute(buf, ra.k, ra.v, ta.nrows, ta.mask);
+            if (i + 1 >= nt) break;
+            ta = rd(i + 2);
+            Engine::load(kp(ta), vp(ta), ta.nrows, ra.k, ra.v);
+            __builtin_amdgcn_sched_barrier(0);
+            acc.compute(buf, rb.k, rb.v, tb.nrows, tb.mask);
+          }
+        } else {
+          for (int i = 0; i < nt; ++i) {
+            const TileDesc t = rd(i);
+            acc.tile(buf, kp(t), vp(t), t.nrows, t.mask);
+          }
         }
       }
     }
@@ -1716,7 +1732,10 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
   __syncthreads();  // every wave is done with its tile buffer
   acc.to_lds(st);
   __syncthreads();
-  write_block_record<D, G>(st, a.ws.ex_part + (int64_t)blockIdx.x * G * RS);
+  if (!a.half)
+    write_record<D, G, 4>(st, 0, a.ws.ex_part + (int64_t)slot * G * RS, tid, 256);
+  else if (u >= 0)
+    write_record<D, G, 2>(st, 2 * hf, a.ws.ex_part + (int64_t)slot * G * RS, tid & 127, 128);
 }
 
 // ---------------------------------------------------------------------------
@@ -2004,6 +2023,7 @@ hipError_t launch_decode(const DecodeLaunch& x, hipStream_t s) {
   a.half_s2_l2 = 0.5f * x.scale * x.scale * kLog2e;
   a.L_head_dim = x.D;
   a.whole = x.whole;
+  a.half = x.half;
   {
     // equal units: every sequence with the first one's length and fold count
     bool eq = true;

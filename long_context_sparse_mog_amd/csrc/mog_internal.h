@@ -155,6 +155,7 @@ struct DecodeLaunch {
   int32_t nblk;         // exact blocks launched: splits + n_units
   int32_t nb_res;       // residual record slots per unit: nb_chosen + ceil(max_C / kRestClustersSmall)
   int32_t nb_chosen;    // chosen-cluster blocks per unit (max G * top_c)
+  int32_t half;         // exact blocks in halves of 2 waves, each with a unit share of its own
   int32_t whole;        // whole-cluster step: every sequence's top_s reaches its S, no folded
                         // rows, Gaussian residual or none, no subcluster output, at most
                         // kWaveListMax chosen clusters per unit.  The top-c kernel writes each
