@@ -126,6 +126,15 @@ def test_bf16_d64():
                                  n_components=32))
 
 
+@pytest.mark.parametrize("lens", [[3000] * 5, [2000, 2600, 3100, 1500, 2900]])
+def test_many_units_half_block_shares(lens):
+    # more than 16 units: the exact blocks take unit shares per half block
+    # (the last block's second half is idle when the share count is odd)
+    wl = synth.config(1, seq_lens=lens, n_kv_heads=4, n_q_heads=8, n_components=32)
+    run_decode_case(wl)
+    run_decode_case(wl, sel="c")
+
+
 @pytest.mark.parametrize("residual", [True, False])
 def test_subcluster_budgets_mixed(residual):
     # per-sequence subcluster budgets below S, zero and above S in one batch;
