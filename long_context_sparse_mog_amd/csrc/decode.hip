@@ -670,8 +670,11 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. Subclusters and residual.  Grid (units, n_rest + nb_chosen); blocks
-//    are numbered x (record slot order) as below, but the rest blocks come
+// 3. Subclusters and residual, one block per chosen cluster: the steps
+//    with shared selection, the feature-map residual or folded rows (the
+//    others run the one-wave-per-cluster kernel of 3b).  Grid (units,
+//    n_rest + nb_chosen); blocks are numbered x (record slot order) as
+//    below, but the rest blocks come
 //    first in the grid, so the dispatcher starts them together with the
 //    chosen-cluster blocks instead of after every chosen slot (most of which
 //    find no cluster and leave):
@@ -1333,27 +1336,29 @@ __global__ __launch_bounds__(256) void k_sub_wave(DArgs a, BudgetArgs b, int nb_
 // ---------------------------------------------------------------------------
 // ---------------------------------------------------------------------------
 // 4a. Shares of the exact blocks.  Unit u reads T_u = anchors + rows of its
-//     chosen subclusters exactly; it gets n_u(r) = 1 + floor(T_u * r) blocks,
-//     numbered unit by unit, for the largest scale r found by bisection with
-//     sum_u n_u(r) <= B, B = min(nblk, n_units + ceil(total / 256)) (so no
-//     block gets much under 256 rows).  This bounds the heaviest block by
-//     the smallest load the block count allows, up to rounding: with many
-//     units of a few blocks each, a fixed scale (r = (B - n_units) / total)
-//     leaves up to one block per unit unused and its siblings a third more
-//     work.  With many blocks per unit the fixed scale is kept.  Every wave of every exact block recomputes the shares from the
-//     per-unit row counts (a few KB): no table, no launch, no barrier.
+//     chosen subclusters exactly; it gets n_u(r) = 1 + floor(T_u * r) slots
+//     (blocks, or half blocks when many units split them), numbered unit by
+//     unit, for the largest scale r a 4-ary search finds with
+//     sum_u n_u(r) <= B, B = min(slots, n_units + ceil(total / min_rows)) (so
+//     no slot gets much under min_rows rows).  This bounds the heaviest slot
+//     by the smallest load the slot count allows, up to rounding: with many
+//     units of a few slots each, a fixed scale (r = (B - n_units) / total)
+//     leaves up to one slot per unit unused and its siblings a third more
+//     work.  With many slots per unit the fixed scale is kept.  Every wave of
+//     every exact block recomputes the shares from the per-unit row counts
+//     (a few KB): no table, no launch, no barrier.
 // ---------------------------------------------------------------------------
 struct BlockShare {
-  int u;      // unit (-1: the block has no work)
-  int first;  // first block of the unit
-  int n;      // blocks of the unit
+  int u;      // unit (-1: the slot has no work)
+  int first;  // first slot of the unit
+  int n;      // slots of the unit
 };
 
-// The share holding block want_block, found by one wave on its own (every
-// wave of a block computes the same, so no barrier is needed): lane l holds
-// the totals of units l + 64 k (k < kShareRegs) in registers, the counts
-// are wave sums, the block numbers a lane scan.  Past 64 kShareRegs units
-// the scale is the fixed one, the units read 64 at a time.
+// The share holding slot want_block of nblk, found by one wave on its own
+// (every wave of a slot computes the same, so no barrier is needed): lane l
+// holds the totals of units l + 64 k (k < kShareRegs) in registers, the
+// counts are wave sums, the slot numbers a lane scan.  Past 64 kShareRegs
+// units the scale is the fixed one, the units read 64 at a time.
 constexpr int kShareRegs = 4;
 constexpr int kShareRounds = 3;
 
@@ -1730,7 +1735,7 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
     }
   }
   __syncthreads();  // every wave is done with its tile buffer
-  acc.to_lds(st);
+  if (u >= 0) acc.to_lds(st);  // (an idle half's engine holds no state)
   __syncthreads();
   if (!a.half)
     write_record<D, G, 4>(st, 0, a.ws.ex_part + (int64_t)slot * G * RS, tid, 256);
