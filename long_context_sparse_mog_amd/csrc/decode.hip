@@ -1361,6 +1361,11 @@ struct BlockShare {
 // units the scale is the fixed one, the units read 64 at a time.
 constexpr int kShareRegs = 4;
 constexpr int kShareRounds = 3;
+// Rows a block gets at least (half of it for a half block): small steps
+// (32K: about 25K rows over 8 units) then spread over more blocks, whose
+// waves stream 2-3 tiles after their set-up instead of 7 (64 measured best
+// against 256, 128, 32 and 16: 32K 24.6 -> 23.3 us per step).
+constexpr int kShareMinRows = 64;
 
 __device__ BlockShare wave_find_share(const int32_t* unit_rows, int n_units, int nblk, int A, int want_block,
                                       int min_rows) {
@@ -1518,7 +1523,7 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
   const int ws_wave = a.half ? wave & 1 : wave;     // the wave's index in its share
   const int slot = a.half ? 2 * (int)blockIdx.x + hf : (int)blockIdx.x;
   const BlockShare bs = wave_find_share(a.ws.unit_rows, a.n_units, a.half ? 2 * a.nblk : a.nblk, A, slot,
-                                        a.half ? 128 : 256);
+                                        a.half ? kShareMinRows / 2 : kShareMinRows);
   const int u = bs.u;
   // (a share with no unit leaves; a half block's idle half still meets the
   // other half at the epilogue's barriers)
