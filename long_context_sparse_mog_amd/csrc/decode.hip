@@ -239,6 +239,8 @@ __global__ __launch_bounds__(256) void k_score_clusters(DArgs a) {
   }
   const mog_unit U = unit_record(a, u);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // (a subcluster step's kernels add the unit's exact rows to this count)
+  if (blockIdx.x == 0 && threadIdx.x == 0 && !a.whole) a.ws.unit_rows[u] = 0;
   const int g0 = blockIdx.x * (4 * kScoreRowsPerWave) + wave * kScoreRowsPerWave;
   if (g0 >= U.C) return;
   const float* qb = a.q + ((int64_t)U.seq * a.Hq + (int64_t)U.kv_head * G) * D;
@@ -315,6 +317,171 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // bits 0..b set (b in [-1, 31])
 __device__ inline uint32_t mask_upto(int b) { return b >= 31 ? ~0u : ((1u << (b + 1)) - 1u); }
 
+// The selection of one wave: its keys sit in KPL slots (slot j of lane l:
+// item 64 j + l; key 0: not valid), c_eff of the nvalid valid ones are to be
+// taken, hb is the wave's LDS bins (256 + 64 ints).  On return the chosen
+// are the keys above prefix on the bits of hi_mask, then the first kk (by
+// index) of the cand keys equal to prefix there (hi_mask: decided bits,
+// prefix: their values).  No barrier: a wave's LDS operations run in order.
+template <int KPL>
+__device__ inline void wave_select(const float (&scv)[KPL], const uint32_t (&key)[KPL], int c_eff, int nvalid, int* hb,
+                                   int& kk, int& cand, uint32_t& prefix, uint32_t& hi_mask) {
+  const int lane = threadIdx.x & 63;
+  kk = c_eff;
+  cand = nvalid;
+  prefix = 0u;
+  hi_mask = 0u;
+  bool resolved = false;
+  if (kk > 0 && kk < nvalid) {
+    // One 256-bin histogram of the valid values over [lo, hi]: value x goes
+    // to bin floor((hi - x) * 256 / (hi - lo)) (at most 255).  Rounded
+    // subtraction and scaling are monotone, so a value in a lower bin is
+    // strictly larger than every value in a higher bin: the chosen keys are
+    // those of the bins before the one where the count reaches c, plus the
+    // best of that boundary bin, ranked exactly by key and index when it
+    // holds at most 64 keys.  A more crowded boundary bin falls back to the
+    // radix select below.
+    float vhi = -INFINITY, vlo = INFINITY;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      if (key[j] != 0u) {
+        vhi = fmaxf(vhi, scv[j]);
+        vlo = fminf(vlo, scv[j]);
+      }
+    }
+    vhi = __uint_as_float(wave_reduce_uniform(
+        __float_as_uint(vhi), [](uint32_t x, uint32_t y) { return __float_as_uint(fmaxf(__uint_as_float(x), __uint_as_float(y))); },
+        __float_as_uint(-INFINITY)));
+    vlo = __uint_as_float(wave_reduce_uniform(
+        __float_as_uint(vlo), [](uint32_t x, uint32_t y) { return __float_as_uint(fminf(__uint_as_float(x), __uint_as_float(y))); },
+        __float_as_uint(INFINITY)));
+    const float inv = vhi > vlo ? 256.f / (vhi - vlo) : 0.f;
+    int bin[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) bin[j] = key[j] != 0u ? (int)fminf(255.f, (vhi - scv[j]) * inv) : 256 + lane;
+    int* hh = hb;
+    *reinterpret_cast<int4*>(&hh[4 * lane]) = make_int4(0, 0, 0, 0);
+    __asm__ volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) atomicAdd(&hh[bin[j]], 1);
+    __asm__ volatile("" ::: "memory");
+    // lane l holds bins 4l .. 4l+3 (bins in increasing order = values in
+    // decreasing order); the keys before its bins come from the lanes before
+    const int4 cv = *reinterpret_cast<const int4*>(&hh[4 * lane]);
+    const int part = cv.x + cv.y + cv.z + cv.w;
+    const int b0 = wave_incl_scan(part) - part, b1 = b0 + cv.x, b2 = b1 + cv.y, b3 = b2 + cv.z;
+    int dsel = -1, dbef = 0, dcnt = 0;
+    if (b0 < kk && kk <= b1) { dsel = 4 * lane; dbef = b0; dcnt = cv.x; }
+    else if (b1 < kk && kk <= b2) { dsel = 4 * lane + 1; dbef = b1; dcnt = cv.y; }
+    else if (b2 < kk && kk <= b3) { dsel = 4 * lane + 2; dbef = b2; dcnt = cv.z; }
+    else if (b3 < kk && kk <= b3 + cv.w) { dsel = 4 * lane + 3; dbef = b3; dcnt = cv.w; }
+    const unsigned long long fb = __ballot(dsel >= 0);
+    const int src = fb ? __ffsll((long long)fb) - 1 : 0;
+    const int bsel = __builtin_amdgcn_readlane(dsel, src);
+    const int nbef = __builtin_amdgcn_readlane(dbef, src);
+    const int nbin = __builtin_amdgcn_readlane(dcnt, src);
+    if (fb != 0ull && nbin <= 64) {
+      // the boundary bin's keys, one per lane, in the wave's LDS bins
+      // (every lane has read its bins above; a wave's LDS operations run
+      // in order)
+      int nmine = 0;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) nmine += bin[j] == bsel;
+      int pos = wave_incl_scan(nmine) - nmine;
+      uint32_t* lk = reinterpret_cast<uint32_t*>(hh);
+      int* li = hh + 64;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) {
+        if (bin[j] == bsel) {
+          lk[pos] = key[j];
+          li[pos] = 64 * j + lane;
+          ++pos;
+        }
+      }
+      __asm__ volatile("" ::: "memory");
+      const uint32_t myk = lane < nbin ? lk[lane] : 0u;
+      const int myi = lane < nbin ? li[lane] : 0;
+      int rk = 0;
+      for (int t = 0; t < nbin; ++t) {
+        const uint32_t kt = lk[t];
+        const int it = li[t];
+        rk += (int)((kt > myk) | ((kt == myk) & (it < myi)));
+      }
+      const int need = kk - nbef;  // keys still to be taken from the bin (>= 1)
+      const unsigned long long cb = __ballot(lane < nbin && rk == need - 1);
+      const uint32_t kcut = (uint32_t)__builtin_amdgcn_readlane((int)myk, __ffsll((long long)cb) - 1);
+      const int n_gt = __popcll(__ballot(lane < nbin && myk > kcut));
+      const int n_eq = __popcll(__ballot(lane < nbin && myk == kcut));
+      prefix = kcut;
+      hi_mask = ~0u;
+      kk = need - n_gt;
+      cand = n_eq;
+      resolved = true;
+    }
+  }
+  if (kk > 0 && !resolved) {
+    uint32_t kor = 0u, kand = ~0u;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      kor |= key[j];
+      kand &= key[j] != 0u ? key[j] : ~0u;
+    }
+    kor = wave_reduce_uniform(kor, [](uint32_t x, uint32_t y) { return x | y; }, 0u);
+    kand = wave_reduce_uniform(kand, [](uint32_t x, uint32_t y) { return x & y; }, ~0u);
+    const uint32_t varying = kor ^ kand;
+    int* hh = hb;
+    int top = 31;  // highest undecided bit
+    while (cand > kk && top >= 0) {
+      const uint32_t low = mask_upto(top);
+      const uint32_t rem = varying & low;
+      if (rem == 0u) {  // the candidates are all equal
+        prefix |= kand & low;
+        hi_mask |= low;
+        break;
+      }
+      const int nb = 31 - __clz(rem);  // next varying bit; bits (nb, top] shared
+      const uint32_t shared_bits = low & ~mask_upto(nb);
+      prefix |= kand & shared_bits;
+      hi_mask |= shared_bits;
+      const int w = nb + 1 < 8 ? nb + 1 : 8;
+      const int shift = nb - w + 1;
+      const uint32_t dmask = (1u << w) - 1u;
+      // histogram of the candidates' next digit; keys that are not
+      // candidates go to the lane's spare bin, so there is no branch (a wave
+      // executes its LDS operations in order)
+      *reinterpret_cast<int4*>(&hh[4 * lane]) = make_int4(0, 0, 0, 0);
+      __asm__ volatile("" ::: "memory");
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) {
+        const uint32_t kv = key[j];
+        const bool m = kv != 0u && (kv & hi_mask) == prefix;
+        atomicAdd(&hh[m ? (int)((kv >> shift) & dmask) : 256 + lane], 1);
+      }
+      __asm__ volatile("" ::: "memory");
+      // lane l holds digits 252-4l .. 255-4l; candidates above its digits
+      // come from the lanes before it
+      const int4 cv = *reinterpret_cast<const int4*>(&hh[4 * (63 - lane)]);
+      const int c0 = cv.x, c1 = cv.y, c2 = cv.z, c3 = cv.w;
+      const int part = c0 + c1 + c2 + c3;
+      const int a3 = wave_incl_scan(part) - part, a2 = a3 + c3, a1 = a2 + c2, a0 = a1 + c1;
+      const int dbase = 4 * (63 - lane);
+      int dsel = -1, dab = 0, dcnt = 0;
+      if (a3 < kk && kk <= a2) { dsel = dbase + 3; dab = a3; dcnt = c3; }
+      else if (a2 < kk && kk <= a1) { dsel = dbase + 2; dab = a2; dcnt = c2; }
+      else if (a1 < kk && kk <= a0) { dsel = dbase + 1; dab = a1; dcnt = c1; }
+      else if (a0 < kk && kk <= a0 + c0) { dsel = dbase; dab = a0; dcnt = c0; }
+      const unsigned long long fb = __ballot(dsel >= 0);
+      const int src = fb ? __ffsll((long long)fb) - 1 : 0;
+      const int d = __builtin_amdgcn_readlane(dsel, src);
+      prefix |= (uint32_t)d << shift;
+      hi_mask |= dmask << shift;
+      kk -= __builtin_amdgcn_readlane(dab, src);
+      cand = __builtin_amdgcn_readlane(dcnt, src);
+      top = shift - 1;
+    }
+  }
+}
+
 template <int G, int KPL>
 __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
   constexpr int NSW = (KPL + G - 1) / G;  // tail slots per wave
@@ -389,157 +556,9 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
   const int c_eff = want < nvalid ? want : nvalid;
   // hi_mask: decided bits, prefix: their values; cand: keys matching the
   // prefix there; kk: how many of those are still to be taken
-  int kk = c_eff, cand = nvalid;
-  uint32_t prefix = 0u, hi_mask = 0u;
-  bool resolved = false;
-  if (kk > 0 && kk < nvalid) {
-    // One 256-bin histogram of the valid values over [lo, hi]: value x goes
-    // to bin floor((hi - x) * 256 / (hi - lo)) (at most 255).  Rounded
-    // subtraction and scaling are monotone, so a value in a lower bin is
-    // strictly larger than every value in a higher bin: the chosen keys are
-    // those of the bins before the one where the count reaches c, plus the
-    // best of that boundary bin, ranked exactly by key and index when it
-    // holds at most 64 keys.  A more crowded boundary bin falls back to the
-    // radix select below.
-    float vhi = -INFINITY, vlo = INFINITY;
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) {
-      if (key[j] != 0u) {
-        vhi = fmaxf(vhi, scv[j]);
-        vlo = fminf(vlo, scv[j]);
-      }
-    }
-    vhi = __uint_as_float(wave_reduce_uniform(
-        __float_as_uint(vhi), [](uint32_t x, uint32_t y) { return __float_as_uint(fmaxf(__uint_as_float(x), __uint_as_float(y))); },
-        __float_as_uint(-INFINITY)));
-    vlo = __uint_as_float(wave_reduce_uniform(
-        __float_as_uint(vlo), [](uint32_t x, uint32_t y) { return __float_as_uint(fminf(__uint_as_float(x), __uint_as_float(y))); },
-        __float_as_uint(INFINITY)));
-    const float inv = vhi > vlo ? 256.f / (vhi - vlo) : 0.f;
-    int bin[KPL];
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) bin[j] = key[j] != 0u ? (int)fminf(255.f, (vhi - scv[j]) * inv) : 256 + lane;
-    int* hh = hist[h];
-    *reinterpret_cast<int4*>(&hh[4 * lane]) = make_int4(0, 0, 0, 0);
-    __asm__ volatile("" ::: "memory");
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) atomicAdd(&hh[bin[j]], 1);
-    __asm__ volatile("" ::: "memory");
-    // lane l holds bins 4l .. 4l+3 (bins in increasing order = values in
-    // decreasing order); the keys before its bins come from the lanes before
-    const int4 cv = *reinterpret_cast<const int4*>(&hh[4 * lane]);
-    const int part = cv.x + cv.y + cv.z + cv.w;
-    const int b0 = wave_incl_scan(part) - part, b1 = b0 + cv.x, b2 = b1 + cv.y, b3 = b2 + cv.z;
-    int dsel = -1, dbef = 0, dcnt = 0;
-    if (b0 < kk && kk <= b1) { dsel = 4 * lane; dbef = b0; dcnt = cv.x; }
-    else if (b1 < kk && kk <= b2) { dsel = 4 * lane + 1; dbef = b1; dcnt = cv.y; }
-    else if (b2 < kk && kk <= b3) { dsel = 4 * lane + 2; dbef = b2; dcnt = cv.z; }
-    else if (b3 < kk && kk <= b3 + cv.w) { dsel = 4 * lane + 3; dbef = b3; dcnt = cv.w; }
-    const unsigned long long fb = __ballot(dsel >= 0);
-    const int src = fb ? __ffsll((long long)fb) - 1 : 0;
-    const int bsel = __builtin_amdgcn_readlane(dsel, src);
-    const int nbef = __builtin_amdgcn_readlane(dbef, src);
-    const int nbin = __builtin_amdgcn_readlane(dcnt, src);
-    if (fb != 0ull && nbin <= 64) {
-      // the boundary bin's keys, one per lane, in the wave's LDS bins
-      // (every lane has read its bins above; a wave's LDS operations run
-      // in order)
-      int nmine = 0;
-#pragma unroll
-      for (int j = 0; j < KPL; ++j) nmine += bin[j] == bsel;
-      int pos = wave_incl_scan(nmine) - nmine;
-      uint32_t* lk = reinterpret_cast<uint32_t*>(hh);
-      int* li = hh + 64;
-#pragma unroll
-      for (int j = 0; j < KPL; ++j) {
-        if (bin[j] == bsel) {
-          lk[pos] = key[j];
-          li[pos] = 64 * j + lane;
-          ++pos;
-        }
-      }
-      __asm__ volatile("" ::: "memory");
-      const uint32_t myk = lane < nbin ? lk[lane] : 0u;
-      const int myi = lane < nbin ? li[lane] : 0;
-      int rk = 0;
-      for (int t = 0; t < nbin; ++t) {
-        const uint32_t kt = lk[t];
-        const int it = li[t];
-        rk += (int)((kt > myk) | ((kt == myk) & (it < myi)));
-      }
-      const int need = kk - nbef;  // keys still to be taken from the bin (>= 1)
-      const unsigned long long cb = __ballot(lane < nbin && rk == need - 1);
-      const uint32_t kcut = (uint32_t)__builtin_amdgcn_readlane((int)myk, __ffsll((long long)cb) - 1);
-      const int n_gt = __popcll(__ballot(lane < nbin && myk > kcut));
-      const int n_eq = __popcll(__ballot(lane < nbin && myk == kcut));
-      prefix = kcut;
-      hi_mask = ~0u;
-      kk = need - n_gt;
-      cand = n_eq;
-      resolved = true;
-    }
-  }
-  if (kk > 0 && !resolved) {
-    uint32_t kor = 0u, kand = ~0u;
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) {
-      kor |= key[j];
-      kand &= key[j] != 0u ? key[j] : ~0u;
-    }
-    kor = wave_reduce_uniform(kor, [](uint32_t x, uint32_t y) { return x | y; }, 0u);
-    kand = wave_reduce_uniform(kand, [](uint32_t x, uint32_t y) { return x & y; }, ~0u);
-    const uint32_t varying = kor ^ kand;
-    int* hh = hist[h];
-    int top = 31;  // highest undecided bit
-    while (cand > kk && top >= 0) {
-      const uint32_t low = mask_upto(top);
-      const uint32_t rem = varying & low;
-      if (rem == 0u) {  // the candidates are all equal
-        prefix |= kand & low;
-        hi_mask |= low;
-        break;
-      }
-      const int nb = 31 - __clz(rem);  // next varying bit; bits (nb, top] shared
-      const uint32_t shared_bits = low & ~mask_upto(nb);
-      prefix |= kand & shared_bits;
-      hi_mask |= shared_bits;
-      const int w = nb + 1 < 8 ? nb + 1 : 8;
-      const int shift = nb - w + 1;
-      const uint32_t dmask = (1u << w) - 1u;
-      // histogram of the candidates' next digit; keys that are not
-      // candidates go to the lane's spare bin, so there is no branch (a wave
-      // executes its LDS operations in order)
-      *reinterpret_cast<int4*>(&hh[4 * lane]) = make_int4(0, 0, 0, 0);
-      __asm__ volatile("" ::: "memory");
-#pragma unroll
-      for (int j = 0; j < KPL; ++j) {
-        const uint32_t kv = key[j];
-        const bool m = kv != 0u && (kv & hi_mask) == prefix;
-        atomicAdd(&hh[m ? (int)((kv >> shift) & dmask) : 256 + lane], 1);
-      }
-      __asm__ volatile("" ::: "memory");
-      // lane l holds digits 252-4l .. 255-4l; candidates above its digits
-      // come from the lanes before it
-      const int4 cv = *reinterpret_cast<const int4*>(&hh[4 * (63 - lane)]);
-      const int c0 = cv.x, c1 = cv.y, c2 = cv.z, c3 = cv.w;
-      const int part = c0 + c1 + c2 + c3;
-      const int a3 = wave_incl_scan(part) - part, a2 = a3 + c3, a1 = a2 + c2, a0 = a1 + c1;
-      const int dbase = 4 * (63 - lane);
-      int dsel = -1, dab = 0, dcnt = 0;
-      if (a3 < kk && kk <= a2) { dsel = dbase + 3; dab = a3; dcnt = c3; }
-      else if (a2 < kk && kk <= a1) { dsel = dbase + 2; dab = a2; dcnt = c2; }
-      else if (a1 < kk && kk <= a0) { dsel = dbase + 1; dab = a1; dcnt = c1; }
-      else if (a0 < kk && kk <= a0 + c0) { dsel = dbase; dab = a0; dcnt = c0; }
-      const unsigned long long fb = __ballot(dsel >= 0);
-      const int src = fb ? __ffsll((long long)fb) - 1 : 0;
-      const int d = __builtin_amdgcn_readlane(dsel, src);
-      prefix |= (uint32_t)d << shift;
-      hi_mask |= dmask << shift;
-      kk -= __builtin_amdgcn_readlane(dab, src);
-      cand = __builtin_amdgcn_readlane(dcnt, src);
-      top = shift - 1;
-    }
-  }
+  int kk, cand;
+  uint32_t prefix, hi_mask;
+  wave_select<KPL>(scv, key, c_eff, nvalid, hist[h], kk, cand, prefix, hi_mask);
   // chosen: keys above the prefix on the decided bits, then the first kk
   // (by index) of the keys that match it there.  When every key matching
   // the prefix is taken (cand == kk) no tie ranks are needed.
@@ -1179,8 +1198,12 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
 // ---------------------------------------------------------------------------
 constexpr int kSubChunk = 8;
 
+// The work of one wave on the x-th chosen cluster g of unit u (slot base
+// tbx, head mask `mask`): what 3b describes after the cluster is known.
+// lsc is the wave's LDS row of scores.
 template <int D, int G>
-__global__ __launch_bounds__(256) void k_sub_wave(DArgs a, BudgetArgs b, int nb_chosen) {
+__device__ inline void sub_wave_cluster(const DArgs& a, int u, int x, const mog_unit& U, int g, int tbx,
+                                        uint32_t mask, int s_keep_raw, float4 (&lsc)[G][kDecodeSubRows / 4]) {
   constexpr int EPL = D / 32;
   constexpr int VPL = D / 64;
   constexpr int RS = D + kPartPad;
@@ -1189,30 +1212,18 @@ __global__ __launch_bounds__(256) void k_sub_wave(DArgs a, BudgetArgs b, int nb_
   constexpr int NCH = SR / RC;
   static_assert(SR % RC == 0 && SR % 4 == 0, "whole chunks, float4 rows");
   static_assert(RC * G <= 64, "one lane per (row, head) sum of a chunk");
-  __shared__ float4 lsc4[4][G][SR / 4];  // each wave's scores [head][subcluster]
-  const int u = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int x = (int)blockIdx.y * 4 + wave;
+  const int lane = threadIdx.x & 63;
   const int64_t cw = (int64_t)u * a.cstride;
-  const int s_keep_raw = b.top_s[u / a.Hkv];
-  const int n_ch_raw = a.ws.n_chosen[u];
-  // (entries below nb_chosen <= the largest C are in range; they are used
-  // only for x < n_chosen)
-  const int xs = min(x, nb_chosen - 1);
-  const int g_raw = a.ws.cl_list[cw + xs];
-  const int tb_raw = a.ws.ch_tbase[cw + xs];
-  const mog_unit U = uni_unit(a.L.units + u);
-  if (x >= uni(n_ch_raw)) return;
-  const int g = uni(g_raw), S = U.S;
+  const int S = U.S;
   const int64_t cg = cw + g;
   const int64_t sg0 = U.sub_base + (int64_t)g * S;
-  const uint32_t mask = (uint32_t)uni((int)a.ws.cl_mask[cg]);
   // subcluster bounds: lane i <= S holds offset i
   const int32_t* off = a.L.sub_off + U.off_base + (int64_t)g * S;
   const int o_i = off[min(lane, S)];
   const int o_n = __shfl_down(o_i, 1, 64);
   const int cnt = lane < S ? o_n - o_i : 0;
   const int s_keep = s_keep_raw < 0 ? 0 : s_keep_raw;
-  float* sc = reinterpret_cast<float*>(&lsc4[wave][0][0]);  // sc[h * SR + i]
+  float* sc = reinterpret_cast<float*>(&lsc[0][0]);  // sc[h * SR + i]
   uint32_t sm = 0u;  // lane i: the heads that chose subcluster i
   if (s_keep >= S) {
     // a budget of S or more reads every nonempty subcluster of the cluster
@@ -1256,7 +1267,7 @@ __global__ __launch_bounds__(256) void k_sub_wave(DArgs a, BudgetArgs b, int nb_
       int rank = 0;
 #pragma unroll
       for (int j4 = 0; j4 < SR / 4; ++j4) {
-        const float4 o4 = lsc4[wave][h][j4];
+        const float4 o4 = lsc[h][j4];
         const float ov[4] = {o4.x, o4.y, o4.z, o4.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1276,7 +1287,9 @@ __global__ __launch_bounds__(256) void k_sub_wave(DArgs a, BudgetArgs b, int nb_
       if (!((mask >> h) & 1u)) continue;
       const bool mine = (sm >> h) & 1u;
       const unsigned long long bits = __ballot(mine);
-      const int rch = a.ws.cl_rank[cg * G + h];
+      // (one head: the cluster's rank is its list position, which the fused
+      // launch knows before the unit's ranks are written)
+      const int rch = G == 1 ? x : a.ws.cl_rank[cg * G + h];
       const int64_t base = (((int64_t)U.seq * a.Hq + U.kv_head * G + h) * a.c_stride + rch) * a.s_stride;
       if (mine) a.sel_s[base + __popcll(bits & below)] = lane;
       for (int j = __popcll(bits) + lane; j < a.s_stride; j += 64) a.sel_s[base + j] = -1;
@@ -1287,7 +1300,7 @@ __global__ __launch_bounds__(256) void k_sub_wave(DArgs a, BudgetArgs b, int nb_
     const int rsum = (int)wave_reduce_uniform(rows, [](uint32_t p, uint32_t q) { return p + q; }, 0u);
     if (lane == 0) atomicAdd(&a.ws.unit_rows[u], rsum);
   }
-  TileRec* ctiles = a.ws.tiles + tile_unit_base(U.row_base, U.cl_base, u, a.L.fold_cap) + uni(tb_raw);
+  TileRec* ctiles = a.ws.tiles + tile_unit_base(U.row_base, U.cl_base, u, a.L.fold_cap) + tbx;
   const int n_tiles =
       write_run_tiles(ctiles, U.row_base, a.L_head_dim, lane < S ? o_i : 0, lane < S ? o_n : 0, lane < S ? sm : 0u);
   if (lane == 0) a.ws.ch_ntiles[cw + x] = n_tiles;
@@ -1324,6 +1337,137 @@ __global__ __launch_bounds__(256) void k_sub_wave(DArgs a, BudgetArgs b, int nb_
     for (int e = 0; e < VPL; ++e) dst[h * RS + lane * VPL + e] = ro[h][e];
     if (lane == 0) *reinterpret_cast<float2*>(dst + h * RS + D) = float2{rm[h], rl[h]};
   }
+}
+
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_sub_wave(DArgs a, BudgetArgs b, int nb_chosen) {
+  __shared__ float4 lsc4[4][G][kDecodeSubRows / 4];  // each wave's scores [head][subcluster]
+  const int u = blockIdx.x, wave = threadIdx.x >> 6;
+  const int x = (int)blockIdx.y * 4 + wave;
+  const int64_t cw = (int64_t)u * a.cstride;
+  const int s_keep_raw = b.top_s[u / a.Hkv];
+  const int n_ch_raw = a.ws.n_chosen[u];
+  // (entries below nb_chosen <= the largest C are in range; they are used
+  // only for x < n_chosen)
+  const int xs = min(x, nb_chosen - 1);
+  const int g_raw = a.ws.cl_list[cw + xs];
+  const int tb_raw = a.ws.ch_tbase[cw + xs];
+  const mog_unit U = uni_unit(a.L.units + u);
+  if (x >= uni(n_ch_raw)) return;
+  const int g = uni(g_raw);
+  const uint32_t mask = (uint32_t)uni((int)a.ws.cl_mask[cw + g]);
+  sub_wave_cluster<D, G>(a, u, x, U, g, uni(tb_raw), mask, s_keep_raw, lsc4[wave]);
+}
+
+// ---------------------------------------------------------------------------
+// 3c. Top-c and subclusters in one launch, for one query head per KV head
+//     (the steps of 3b): every wave of block (u, y) selects its unit's top-c
+//     itself (the selection of 2, on the unit's scores and tile bounds, which
+//     the L2 serves to all of the unit's waves), takes the unit's x-th
+//     chosen cluster, x = 4 y + w, with its slot base, and does 3b's work on
+//     it.  Wave 0 of block (u, 0) also writes the unit's selection (head
+//     masks, list, slot bases, count and the selection output) for the exact
+//     and merge kernels.  The top-c launch and every wave's list loads drop
+//     out of the step; the unit's exact row count is cleared by the score
+//     kernel.
+// ---------------------------------------------------------------------------
+template <int D, int KPL>
+__global__ __launch_bounds__(256) void k_select_sub1(DArgs a, BudgetArgs b) {
+  __shared__ int hist[4][256 + 64];
+  __shared__ float4 lsc4[4][1][kDecodeSubRows / 4];
+  const int u = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int x = (int)blockIdx.y * 4 + wave;
+  const int64_t cw = (int64_t)u * a.cstride;
+  const int want_raw = b.top_c[u / a.Hkv];
+  const int s_keep_raw = b.top_s[u / a.Hkv];
+  // scores and tile bounds of the unit's clusters (slot j of lane l: cluster
+  // 64 j + l; one head, so the head's scores start at u * cstride)
+  float scv[KPL];
+  int bound[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int i = min(64 * j + lane, a.cstride - 1);
+    scv[j] = a.ws.cl_score[cw + i];
+    bound[j] = a.ws.cl_tiles[cw + i];
+  }
+  const mog_unit U = uni_unit(a.L.units + u);
+  const int C = U.C;
+  uint32_t key[KPL];
+  int nvalid = 0;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const bool in = 64 * j + lane < C && scv[j] != -INFINITY;
+    key[j] = in ? float_key(scv[j]) : 0u;
+    nvalid += in;
+  }
+  nvalid = (int)wave_reduce_uniform((uint32_t)nvalid, [](uint32_t p, uint32_t q) { return p + q; }, 0u);
+  const int want = want_raw < 0 ? 0 : want_raw;
+  const int c_eff = want < nvalid ? want : nvalid;
+  int kk, cand;
+  uint32_t prefix, hi_mask;
+  wave_select<KPL>(scv, key, c_eff, nvalid, hist[wave], kk, cand, prefix, hi_mask);
+  // the chosen clusters (the rule of 2), their positions in the ascending
+  // list and their tile-slot bases; the wave's own cluster x
+  const unsigned long long below = (1ull << lane) - 1ull;
+  const bool all_ties = cand == kk;
+  int ties = 0, n_before = 0, t_before = 0, g = 0, tbx = 0;
+  bool sel[KPL];
+  int pos[KPL], tbs[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const uint32_t kd = key[j] & hi_mask;
+    const bool valid = c_eff > 0 && key[j] != 0u;
+    bool sj;
+    if (all_ties) {
+      sj = valid && kd >= prefix;
+    } else {
+      const bool tie = valid && kd == prefix;
+      const unsigned long long tb = __ballot(tie);
+      sj = valid && (kd > prefix || (tie && ties + __popcll(tb & below) < kk));
+      ties += __popcll(tb);
+    }
+    sel[j] = sj;
+    const unsigned long long sb = __ballot(sj);
+    pos[j] = n_before + __popcll(sb & below);
+    const int bnd = sj ? bound[j] : 0;
+    const int incl = wave_incl_scan(bnd);
+    tbs[j] = t_before + incl - bnd;
+    const unsigned long long hit = __ballot(sj && pos[j] == x);
+    if (hit) {
+      const int src = __ffsll((long long)hit) - 1;
+      g = 64 * j + src;
+      tbx = __builtin_amdgcn_readlane(tbs[j], src);
+    }
+    n_before += __popcll(sb);
+    t_before += __builtin_amdgcn_readlane(incl, 63);
+  }
+  const int n_ch = n_before;
+  if (blockIdx.y == 0 && wave == 0) {
+    const int64_t row = (int64_t)U.seq * a.Hq + U.kv_head;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const int i = 64 * j + lane;
+      if (i < C) {
+        a.ws.cl_mask[cw + i] = sel[j] ? 1u : 0u;
+        if (a.sel_s) a.ws.cl_rank[cw + i] = sel[j] ? pos[j] : -1;  // read back only for sel_s
+      }
+      if (sel[j]) {
+        a.ws.cl_list[cw + pos[j]] = i;
+        a.ws.ch_tbase[cw + pos[j]] = tbs[j];
+        if (a.sel_c) a.sel_c[row * a.c_stride + pos[j]] = i;
+      }
+    }
+    if (a.sel_c)
+      for (int j = n_ch + lane; j < a.c_stride; j += 64) a.sel_c[row * a.c_stride + j] = -1;
+    if (a.sel_s) {
+      const int64_t base = row * a.c_stride * a.s_stride;
+      for (int j = n_ch * a.s_stride + lane; j < a.c_stride * a.s_stride; j += 64) a.sel_s[base + j] = -1;
+    }
+    if (lane == 0) a.ws.n_chosen[u] = n_ch;
+  }
+  if (x >= n_ch) return;
+  sub_wave_cluster<D, 1>(a, u, x, U, g, tbx, 1u, s_keep_raw, lsc4[wave]);
 }
 
 // ---------------------------------------------------------------------------
@@ -1930,7 +2074,19 @@ static hipError_t decode_impl(const DecodeLaunch& x, const DArgs& a, const Budge
   const int nu = x.L.n_units;
   const int fblocks = x.residual == 2 ? (G * x.L.fm_dim + 255) / 256 : 0;
   hipLaunchKernelGGL((k_score_clusters<D, G>), dim3(a.score_blocks + fblocks, nu), dim3(256), 0, s, a);
-  if (x.L.max_C <= 256)
+  // one query head per KV head and a subcluster step of 3b: top-c and the
+  // subclusters in one launch (3c)
+  const bool fused = G == 1 && !x.whole && x.residual != 2 && !x.shared && x.L.fold_capacity == 0 &&
+                     x.nb_chosen > 0 && x.L.max_C <= 1024;
+  if (fused) {
+    const dim3 grid(nu, (x.nb_chosen + 3) / 4);
+    if (x.L.max_C <= 256)
+      hipLaunchKernelGGL((k_select_sub1<D, 4>), grid, dim3(256), 0, s, a, b);
+    else if (x.L.max_C <= 512)
+      hipLaunchKernelGGL((k_select_sub1<D, 8>), grid, dim3(256), 0, s, a, b);
+    else
+      hipLaunchKernelGGL((k_select_sub1<D, 16>), grid, dim3(256), 0, s, a, b);
+  } else if (x.L.max_C <= 256)
     hipLaunchKernelGGL((k_select_topc<G, 4>), dim3(nu), dim3(64 * G), 0, s, a, b);
   else if (x.L.max_C <= 512)
     hipLaunchKernelGGL((k_select_topc<G, 8>), dim3(nu), dim3(64 * G), 0, s, a, b);
@@ -1941,7 +2097,7 @@ static hipError_t decode_impl(const DecodeLaunch& x, const DArgs& a, const Budge
   // the Gaussian residual of the clusters left out runs in blocks after the
   // exact ones, in the spread of their end times; the feature-map residual's
   // in the subcluster kernel; none without a residual
-  if (!x.whole) {
+  if (!x.whole && !fused) {
     if (x.residual != 2 && !x.shared && x.L.fold_capacity == 0) {
       // one wave per chosen cluster
       if (x.nb_chosen > 0)
