@@ -60,8 +60,8 @@ def meta(tmp_path_factory):
     return _kernel_metadata(capi.LIB_PATH, str(tmp_path_factory.mktemp("co")))
 
 
-DECODE_KERNELS = ("k_score_clusters", "k_select_topc", "k_sub_wave", "k_subclusters", "k_exact", "k_merge",
-                  "k_dense")
+DECODE_KERNELS = ("k_score_clusters", "k_select_topc", "k_select_sub1", "k_sub_wave", "k_subclusters", "k_exact",
+                  "k_merge", "k_dense")
 
 
 def test_metadata_lists_the_decode_kernels(meta):
