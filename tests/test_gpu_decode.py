@@ -171,15 +171,17 @@ def test_budget_larger_than_partition():
     assert rel_l2(out[0], o) < 2e-3
 
 
+@pytest.mark.parametrize("hq", [2, 1])
 @pytest.mark.parametrize("c", [3, 17, 40, 64, 65, 120])
-def test_exact_ties_go_to_lower_index(c):
+def test_exact_ties_go_to_lower_index(c, hq):
     """A zero query makes every group's score its log count, so groups of
     equal size tie exactly in any precision: the chosen clusters and
     subclusters must be exactly the oracle's (ties to the lower index), for
     budgets from a few clusters to most of them."""
-    wl = synth.config(1, seq_lens=[20000], n_kv_heads=1, n_q_heads=2, n_components=64, top_c=[c],
+    # (hq = 1: one query head per KV head, top-c inside the subcluster launch)
+    wl = synth.config(1, seq_lens=[20000], n_kv_heads=1, n_q_heads=hq, n_components=64, top_c=[c],
                       top_s=[3])
-    say(f"[case] zero query, {wl.seq_lens} keys, c={c}")
+    say(f"[case] zero query, {wl.seq_lens} keys, c={c}, G={hq}")
     b = synth.generate(wl, device="cuda", n_qsets=1)
     kv = ops.KVCache.from_batch(b)
     lays = build_oracle_layouts(b)

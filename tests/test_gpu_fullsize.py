@@ -85,6 +85,15 @@ def test_fullsize_mha_128k_sampled():
     run_fullsize(synth.config(2), [0, 45, 127], check_build=(45,))
 
 
+def test_fullsize_one_head_many_clusters():
+    """One query head per KV head and more than 512 clusters (N = 600K, C =
+    775, s = 2): top-c and the subclusters in one launch, with 16 cluster
+    slots per lane."""
+    wl = synth.config(2, n_q_heads=2, n_kv_heads=2, seq_lens=[600000], name="mha-2h-d128-600K-bf16")
+    assert wl.top_s[0] < 20
+    run_fullsize(wl, [0, 1])
+
+
 def test_fullsize_gqa_1m_sampled():
     run_fullsize(synth.config(3), [0, 3, 7], check_build=(3,))
 
