@@ -135,6 +135,16 @@ def test_many_units_half_block_shares(lens):
     run_decode_case(wl, sel="c")
 
 
+def test_more_than_256_units():
+    # 272 units: the exact shares take the fixed scale (the units' row counts
+    # are read 64 at a time instead of held in registers), per half block;
+    # one query head per KV head, with and without the subcluster output
+    wl = synth.config(1, seq_lens=[1000 + 37 * i for i in range(34)], n_kv_heads=8, n_q_heads=8,
+                      n_components=16)
+    run_decode_case(wl, top_c=[2] * 34, top_s=[3] * 34)
+    run_decode_case(wl, sel="c")
+
+
 @pytest.mark.parametrize("residual", [True, False])
 def test_subcluster_budgets_mixed(residual):
     # per-sequence subcluster budgets below S, zero and above S in one batch;
