@@ -622,8 +622,7 @@ static mog_status decode_with_ws(const mog_layout* layout, const mog_kv* kv, con
   x.nb_chosen = d.nb_chosen;
   // whole-cluster step: every chosen cluster is read entirely, so there are
   // no subclusters to score or rank
-  x.whole = params->residual != 2 && layout->fold_capacity == 0 && sel_s == nullptr &&
-            d.nb_chosen <= kWaveListMax;
+  x.whole = layout->fold_capacity == 0 && sel_s == nullptr && d.nb_chosen <= kWaveListMax;
   for (int s = 0; s < kv->n_seq && x.whole; ++s) {
     const UnitSizes z = unit_sizes(layout->seq_lens[s] - layout->fold_count[s], layout->n_sink, layout->n_recent);
     x.whole = x.seq.top_s[s] >= z.S;

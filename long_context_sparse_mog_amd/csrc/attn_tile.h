@@ -173,6 +173,18 @@ __device__ inline bool rs_owner(int l) {
   return (l & undecided) == 0 && rs_index<V>(l) < V;
 }
 
+// the lane that reports value j of wave_reduce_scatter<V> (the inverse of
+// rs_index over the rs_owner lanes: the bit each exchange decided, undecided
+// bits clear)
+template <int V>
+__host__ __device__ constexpr int rs_lane(int j) {
+  constexpr int H = RsSteps<V>::H;
+  constexpr int order[6] = {3, 2, 1, 0, 4, 5};
+  int l = 0;
+  for (int s = 0; s < H; ++s) l |= ((j >> (H - 1 - s)) & 1) << order[s];
+  return l;
+}
+
 // ---------------------------------------------------------------------------
 // MFMA tile engine (bf16)
 // ---------------------------------------------------------------------------

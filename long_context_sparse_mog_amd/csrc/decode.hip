@@ -205,28 +205,57 @@ __device__ inline void score_coefs(const DArgs& a, const float* qb, float (&coef
 // ---------------------------------------------------------------------------
 constexpr int kScoreRowsPerWave = 4;  // clusters scored per wave (16 per block)
 
-// Feature-map residual: log2 of the features of every query head,
+// Feature-map residual: log2 of the features of every query head of unit u,
 // fq[u][h][i] = log2(e) (sqrt(s) w_i.q_h - s |q_h|^2 / 2) (the 1/sqrt(m) factor
-// is applied where the features are used).  One thread per (head, feature).
+// is applied where the features are used).  Block f of the unit takes
+// features [64 f, 64 f + 64): their rows of W and the unit's queries pass
+// through LDS (`lds`, dynamic; the rows padded to D + 1 floats, so that the
+// 64 lanes reading 64 rows hit 64 banks), lane i takes feature 64 f + i and
+// wave w heads w, w + 4.
 template <int D, int G>
-__device__ inline void query_features(const DArgs& a, int u, int blk) {
+__host__ __device__ constexpr int query_features_lds() {
+  return (64 * (D + 1) + G * D) * (int)sizeof(float);
+}
+
+template <int D, int G>
+__device__ inline void query_features(const DArgs& a, int u, int f, float* lds) {
+  constexpr int P = D + 1, R4 = D / 4;  // (LDS row pitch; float4s per row)
+  float* wr = lds;           // [64][P]
+  float* qs = lds + 64 * P;  // [G][D]
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int m = a.L.fm_dim;
-  const int pi = blk * 256 + threadIdx.x;
-  if (pi >= G * m) return;
-  const int h = pi / m, i = pi % m;
   const int seq = u / a.Hkv, kvh = u % a.Hkv;
-  const float* q = a.q + ((int64_t)seq * a.Hq + (int64_t)kvh * G + h) * D;
-  const float* w = a.L.fm_w + (int64_t)i * D;
-  float dot = 0.f, qq = 0.f;
-#pragma unroll 8
-  for (int e = 0; e < D; e += 4) {
-    const float4 qv = *reinterpret_cast<const float4*>(q + e);
-    const float4 wv = *reinterpret_cast<const float4*>(w + e);
-    dot += wv.x * qv.x + wv.y * qv.y + wv.z * qv.z + wv.w * qv.w;
-    qq += qv.x * qv.x + qv.y * qv.y + qv.z * qv.z + qv.w * qv.w;
+  const float* qb = a.q + ((int64_t)seq * a.Hq + (int64_t)kvh * G) * D;
+  const float* wb = a.L.fm_w + (int64_t)64 * f * D;
+  constexpr int NL = 64 * R4 / 256;  // float4s of the block's rows per thread
+  float4 w[NL];
+#pragma unroll
+  for (int k = 0; k < NL; ++k) w[k] = *reinterpret_cast<const float4*>(wb + 4 * (t + 256 * k));
+  for (int k = t; k < G * D; k += 256) qs[k] = qb[k];
+#pragma unroll
+  for (int k = 0; k < NL; ++k) {
+    const int r = (t + 256 * k) / R4, c = (t + 256 * k) % R4;
+    float* d = wr + r * P + 4 * c;
+    d[0] = w[k].x;
+    d[1] = w[k].y;
+    d[2] = w[k].z;
+    d[3] = w[k].w;
   }
+  __syncthreads();
   const float s = a.sqrt_scale;
-  a.ws.fq[((int64_t)u * G + h) * m + i] = kLog2e * (s * dot - 0.5f * s * s * qq);
+  const float* wi = wr + lane * P;
+#pragma unroll
+  for (int h = wave; h < G; h += 4) {
+    const float* qh = qs + h * D;
+    float dot = 0.f, qq = 0.f;
+#pragma unroll 16
+    for (int e = 0; e < D; ++e) {
+      const float qv = qh[e];
+      dot += wi[e] * qv;
+      qq += qv * qv;
+    }
+    a.ws.fq[((int64_t)u * G + h) * m + 64 * f + lane] = kLog2e * (s * dot - 0.5f * s * s * qq);
+  }
 }
 
 template <int D, int G>
@@ -234,7 +263,8 @@ __global__ __launch_bounds__(256) void k_score_clusters(DArgs a) {
   constexpr int EPL = D / 32;
   const int u = blockIdx.y;
   if ((int)blockIdx.x >= a.score_blocks) {
-    query_features<D, G>(a, u, blockIdx.x - a.score_blocks);
+    extern __shared__ float fq_lds[];  // (sized only when these blocks exist)
+    query_features<D, G>(a, u, blockIdx.x - a.score_blocks, fq_lds);
     return;
   }
   const mog_unit U = unit_record(a, u);
@@ -789,6 +819,95 @@ __device__ inline void store_wave_states(float* st, const float (&rm)[G], const 
   }
 }
 
+// The feature table of unit u's G heads, for the feature-map residual:
+// fe[256 h + i] = 2^(fq[h][i] - max_h) and fbase[h] = max_h - log2(m) / 2
+// (waves h, h + 4, ... of the block; visible after the caller's barrier).
+template <int G>
+__device__ inline void fm_table(const DArgs& a, int u, float* fe, float* fbase) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int FM = a.L.fm_dim;
+  for (int h = wave; h < G; h += 4) {
+    const float* fqh = a.ws.fq + ((int64_t)u * G + h) * FM;
+    float v[4], mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[k] = 64 * k < FM ? fqh[lane + 64 * k] : -INFINITY;
+      mx = fmaxf(mx, v[k]);
+    }
+    mx = wave_max(mx);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (64 * k < FM) fe[256 * h + lane + 64 * k] = exp2f(v[k] - mx);
+    if (lane == 0) fbase[h] = mx - 0.5f * log2f((float)FM);
+  }
+}
+
+// Feature-map residual of clusters [R y, R y + R) of unit u (R =
+// kRestClustersPerBlock, R / 4 per wave): every head that left a cluster out
+// adds its term with the cluster's feature-map mass estimate.  A wave takes
+// NB clusters at a time, their loads issued before any is used (clusters past
+// C re-read the last one and are skipped); the NB G dot products of feature
+// sums with the heads' feature exponentials (held in registers) are summed
+// over the lanes by one reduce-scatter, each lane takes the log of its sum,
+// and every weight is then read from the lane that holds it.
+template <int D, int G, int NB>
+__device__ inline void rest_clusters_fm(const DArgs& a, int u, const mog_unit& U, int y, const float* fe,
+                                        const float* fbase, float (&rm)[G], float (&rl)[G],
+                                        float (&ro)[G][D / 64]) {
+  constexpr int VPL = D / 64;
+  constexpr int RCW = kRestClustersPerBlock / 4;
+  constexpr int V = NB * G;
+  static_assert(RCW % NB == 0 && V <= 64, "batches of whole clusters, one reduce-scatter each");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int C = U.C, S = U.S, FM = a.L.fm_dim;
+  const int64_t cw = (int64_t)u * a.cstride;
+  const int32_t* off = a.L.sub_off + U.off_base;
+  const uint32_t all = (1u << G) - 1u;
+  float e[G][4];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) e[h][k] = 64 * k < FM ? fe[256 * h + lane + 64 * k] : 0.f;
+  const float base = fbase[rs_index<V>(lane) % G];  // (of the head whose sum the lane receives)
+  const int g0 = y * kRestClustersPerBlock + wave * RCW;
+#pragma unroll 1
+  for (int k0 = 0; k0 < RCW; k0 += NB) {
+    uint32_t mask[NB];
+    int n_g[NB];
+    float vb[NB][VPL], z[NB][4];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int g = min(g0 + k0 + k, C - 1);
+      mask[k] = a.ws.cl_mask[cw + g];
+      n_g[k] = off[(g + 1) * S] - off[g * S] + (a.L.fold_cap ? a.L.cl_fold[U.cl_base + g] : 0);
+      load_floats<VPL>(a.L.cl_vbar + (U.cl_base + g) * D + lane * VPL, vb[k]);
+      load_fz(a.L.cl_fz + (U.cl_base + g) * FM, FM, z[k]);
+    }
+    float part[V];
+#pragma unroll
+    for (int k = 0; k < NB; ++k)
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float t = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t += e[h][j] * z[k][j];
+        part[k * G + h] = t;
+      }
+    const float t = wave_reduce_scatter<V>(part);
+    const float wl = t > 0.f ? base + log2f(t) : -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const uint32_t unchosen = (g0 + k0 + k < C && n_g[k] > 0) ? (all & ~mask[k]) : 0u;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        if (!((unchosen >> h) & 1u)) continue;
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), rs_lane<V>(k * G + h)));
+        if (w != -INFINITY) add_group<VPL>(rm[h], rl[h], ro[h], w, vb[k]);
+      }
+    }
+  }
+}
+
 // Exact tiles of a chosen cluster (lane i: subcluster i, rows [st, en) of
 // the unit's middle rows, head mask m; m = 0 for a subcluster no head
 // chose): a run is a maximal sequence of chosen nonempty subclusters with
@@ -879,24 +998,7 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
   const uint32_t all = (1u << G) - 1u;
   const bool fmr = a.residual == 2;
   const int FM = a.L.fm_dim;
-  if (fmr) {
-    // every head's features, scaled by their maximum (read after the next
-    // barrier)
-    for (int h = wave; h < G; h += 4) {
-      const float* fqh = a.ws.fq + ((int64_t)u * G + h) * FM;
-      float v[4], mx = -INFINITY;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        v[k] = 64 * k < FM ? fqh[lane + 64 * k] : -INFINITY;
-        mx = fmaxf(mx, v[k]);
-      }
-      mx = wave_max(mx);
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (64 * k < FM) lds_fe[h][lane + 64 * k] = exp2f(v[k] - mx);
-      if (lane == 0) lds_fbase[h] = mx - 0.5f * log2f((float)FM);
-    }
-  }
+  if (fmr) fm_table<G>(a, u, &lds_fe[0][0], lds_fbase);  // (read after the next barrier)
   const int32_t* off = a.L.sub_off + U.off_base;
   float rm[G], rl[G], ro[G][VPL];
 #pragma unroll
@@ -1133,43 +1235,11 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
       }
     }
   } else {
-    // -------- residual of clusters left out, RCW clusters per wave -----------
-    // every load of the wave's clusters is issued before any is used
-    // (clusters past C re-read the last one and are skipped)
-    constexpr int RCW = kRestClustersPerBlock / 4;
+    // -------- residual of clusters left out (feature-map residual) -----------
     const int y = x - nb_chosen;
     if (fmr && a.residual) {
-      // the feature-map estimate of each left-out cluster's mass, HALF
-      // clusters' loads at a time (this mode keeps the Gaussian path's
-      // registers)
-      constexpr int HALF = 2;
       __syncthreads();  // the feature table
-#pragma unroll 1
-      for (int k0 = 0; k0 < RCW; k0 += HALF) {
-        uint32_t mask[HALF];
-        int n_g[HALF];
-        float vb[HALF][VPL], z[HALF][4];
-#pragma unroll
-        for (int k = 0; k < HALF; ++k) {
-          const int g = min(y * kRestClustersPerBlock + wave * RCW + k0 + k, C - 1);
-          mask[k] = a.ws.cl_mask[cw + g];
-          n_g[k] = off[(g + 1) * S] - off[g * S] + (a.L.fold_cap ? a.L.cl_fold[U.cl_base + g] : 0);
-          load_floats<VPL>(a.L.cl_vbar + (U.cl_base + g) * D + lane * VPL, vb[k]);
-          load_fz(a.L.cl_fz + (U.cl_base + g) * FM, FM, z[k]);
-        }
-#pragma unroll
-        for (int k = 0; k < HALF; ++k) {
-          const int g = y * kRestClustersPerBlock + wave * RCW + k0 + k;
-          if (g >= C) break;
-          const uint32_t unchosen = n_g[k] > 0 ? (all & ~mask[k]) : 0u;
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            if (!((unchosen >> h) & 1u)) continue;
-            const float w = fm_weight(z[k], lds_fe[h], lds_fbase[h], FM);
-            if (w != -INFINITY) add_group<VPL>(rm[h], rl[h], ro[h], w, vb[k]);
-          }
-        }
-      }
+      rest_clusters_fm<D, G, 2>(a, u, U, y, &lds_fe[0][0], lds_fbase, rm, rl, ro);  // (this kernel's registers)
     }
   }
 
@@ -1630,11 +1700,11 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   if ((int)blockIdx.x >= a.nblk) {
-    // the Gaussian residual of the clusters some head left out, in blocks
-    // after the exact ones (dispatched as exact blocks retire); record y of
-    // unit u covers clusters [R y, R y + R) (R = rest_cl),
-    // after the unit's chosen-
-    // cluster records (none for a whole-cluster step)
+    // the residual of the clusters some head left out, in blocks after the
+    // exact ones (dispatched as exact blocks retire): the Gaussian one, or a
+    // whole-cluster step's feature-map one; record y of unit u covers
+    // clusters [R y, R y + R) (R = rest_cl), after the unit's chosen-cluster
+    // records (none for a whole-cluster step)
     const int r = (int)blockIdx.x - a.nblk;
     const int u = r / a.rest_per_unit, y = r % a.rest_per_unit;
     const int n_ch_raw = a.whole ? 0 : a.ws.n_chosen[u];
@@ -1649,10 +1719,18 @@ __global__ __launch_bounds__(256, 2) void k_exact(DArgs a) {
 #pragma unroll
       for (int e = 0; e < VPL; ++e) ro[h][e] = 0.f;
     }
-    if (a.rest_cl == kRestClustersSmall)
+    if (a.residual == 2) {
+      // (the unit's feature table in the list LDS, which this path does not
+      // otherwise use)
+      float* fe = reinterpret_cast<float*>(lists);
+      fm_table<G>(a, u, fe, fe + 256 * G);
+      __syncthreads();
+      rest_clusters_fm<D, G, (G <= 6 ? 8 : 4)>(a, u, U, y, fe, fe + 256 * G, rm, rl, ro);
+    } else if (a.rest_cl == kRestClustersSmall) {
       rest_clusters<D, G, kRestClustersSmall / 4>(a, u, U.C, U.cl_base, y, rm, rl, ro);
-    else
+    } else {
       rest_clusters<D, G, kRestClustersPerBlock / 4>(a, u, U.C, U.cl_base, y, rm, rl, ro);
+    }
     store_wave_states<D, G>(st, rm, rl, ro);
     __syncthreads();
     write_block_record<D, G>(st, a.ws.res_part + ((int64_t)u * a.nb_res + uni(n_ch_raw) + y) * G * RS);
@@ -2072,8 +2150,9 @@ __global__ __launch_bounds__(256, 2) void k_dense(KVRef kv, const float* q, int 
 template <int D, int G>
 static hipError_t decode_impl(const DecodeLaunch& x, const DArgs& a, const BudgetArgs& b, hipStream_t s) {
   const int nu = x.L.n_units;
-  const int fblocks = x.residual == 2 ? (G * x.L.fm_dim + 255) / 256 : 0;
-  hipLaunchKernelGGL((k_score_clusters<D, G>), dim3(a.score_blocks + fblocks, nu), dim3(256), 0, s, a);
+  const int fblocks = x.residual == 2 ? x.L.fm_dim / 64 : 0;
+  const unsigned fq_lds = fblocks ? (unsigned)query_features_lds<D, G>() : 0u;
+  hipLaunchKernelGGL((k_score_clusters<D, G>), dim3(a.score_blocks + fblocks, nu), dim3(256), fq_lds, s, a);
   // one query head per KV head and a subcluster step of 3b: top-c and the
   // subclusters in one launch (3c)
   const bool fused = G == 1 && !x.whole && x.residual != 2 && !x.shared && x.L.fold_capacity == 0 &&
@@ -2110,7 +2189,9 @@ static hipError_t decode_impl(const DecodeLaunch& x, const DArgs& a, const Budge
                            x.nb_chosen, nrest_sub);
     }
   }
-  const int nrest = x.residual == 1 ? nu * a.rest_per_unit : 0;
+  // (the feature-map residual's blocks run in the subcluster kernel unless
+  // the step is whole-cluster)
+  const int nrest = (x.residual == 1 || (x.residual == 2 && x.whole)) ? nu * a.rest_per_unit : 0;
   // the timing events (if any) are taken by the dispatches themselves: the
   // start of the first exact launch and the end of the last
   for (int r = 0; r < x.repeat; ++r) {

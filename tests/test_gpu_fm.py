@@ -58,11 +58,15 @@ def run_fm_build_case(wl, m=128, units=None):
     return b, kv, lay
 
 
-def run_fm_decode_case(wl, m=128, shared=False, top=None):
+def run_fm_decode_case(wl, m=128, shared=False, top=None, sel=True):
+    # sel: True asks for the chosen clusters and subclusters (the subcluster
+    # kernel runs), "c" for the clusters only (a whole-cluster budget then
+    # skips it: the exact kernel's residual blocks take the feature-map
+    # residual)
     tc = list(top[0]) if top else list(wl.top_c)
     ts = list(top[1]) if top else list(wl.top_s)
     say(f"[fm decode] {wl.name} lens={wl.seq_lens} Hq={wl.n_q_heads} Hkv={wl.n_kv_heads} D={wl.head_dim} "
-        f"{wl.dtype} m={m} c={tc} s={ts} shared={shared}")
+        f"{wl.dtype} m={m} c={tc} s={ts} shared={shared} sel={sel}")
     b = synth.generate(wl, device="cuda")
     kv = ops.KVCache.from_batch(b)
     W = synth.feature_map_w(m, wl.head_dim).numpy()
@@ -74,10 +78,11 @@ def run_fm_decode_case(wl, m=128, shared=False, top=None):
     lay = ops.import_layout(kv, wl.n_sink, wl.n_recent, [unit_layout_arrays(lays[u]) for u in range(len(lays))])
     params = ops.decode_params(wl.n_q_heads, tc, ts, residual="fm", shared=shared)
     q = b.Q[0].contiguous()
-    out, lse, sel_c, sel_s = ops.mog_decode(lay, kv, q, params, want_sel=True)
+    out, lse, sel_c, sel_s = ops.mog_decode(lay, kv, q, params, want_sel=sel)
     torch.cuda.synchronize()
     out, lse = out.cpu().numpy(), lse.cpu().numpy()
-    sel_c, sel_s = sel_c.cpu().numpy(), sel_s.cpu().numpy()
+    sel_c = sel_c.cpu().numpy()
+    sel_s = sel_s.cpu().numpy() if sel_s is not None else None
     tol = 1e-5 if wl.dtype == "fp32" else 2e-3
     G = wl.group
     worst = 0.0
@@ -86,8 +91,8 @@ def run_fm_decode_case(wl, m=128, shared=False, top=None):
         K, V = b.unit_kv(s, h)
         Q = q[s, h * G:(h + 1) * G].cpu().numpy().astype(np.float64)
         hs = slice(h * G, (h + 1) * G)
-        r = compare_unit(lays[u], K, V, Q, tc[s], ts[s], out[s, hs], lse[s, hs], sel_c[s, hs], sel_s[s, hs], tol,
-                         residual="fm", shared=shared)
+        r = compare_unit(lays[u], K, V, Q, tc[s], ts[s], out[s, hs], lse[s, hs], sel_c[s, hs],
+                         None if sel_s is None else sel_s[s, hs], tol, residual="fm", shared=shared)
         assert r["lse_err"] < (1e-5 if wl.dtype == "fp32" else 1e-3) * max(1.0, float(np.abs(lse[s, hs]).max()))
         worst = max(worst, r["max_rel"])
     say(f"  worst per-head rel L2 = {worst:.3e}")
@@ -128,6 +133,56 @@ def test_fm_decode_no_clusters_chosen():
     # every middle token estimated from the feature sums
     wl = synth.config(0, seq_lens=[3000])
     run_fm_decode_case(wl, m=256, top=([0], [0]))
+
+
+# whole-cluster budgets (top_s >= S) without the subcluster output: no
+# subcluster kernel runs and the exact kernel's residual blocks estimate the
+# clusters left out from their feature sums
+@pytest.mark.parametrize("name", ["gqa", "ragged-paged", "fp32-g8", "d64-g1"])
+def test_fm_decode_whole_cluster(name):
+    wl = {
+        "gqa": lambda: synth.config(1, seq_lens=[8192], n_kv_heads=2, n_q_heads=8, n_components=64, top_c=[6],
+                                    top_s=[13]),
+        "ragged-paged": lambda: synth.config(4, seq_lens=[3000, 9000, 1000], n_kv_heads=2, n_q_heads=8,
+                                             high_entropy_heads=(1,), n_components=64, top_c=[3, 5, 2],
+                                             top_s=[12, 14, 10]),
+        "fp32-g8": lambda: synth.config(1, seq_lens=[5000], n_kv_heads=1, n_q_heads=8, n_components=32,
+                                        dtype="fp32"),
+        "d64-g1": lambda: synth.config(1, seq_lens=[4000], n_kv_heads=2, n_q_heads=2, head_dim=64, n_components=32),
+    }[name]()
+    run_fm_decode_case(wl, m=128 if name != "ragged-paged" else 256, sel="c")
+
+
+def test_fm_decode_whole_cluster_edges():
+    # no cluster chosen (every middle token estimated), shared selection, and
+    # more clusters than one residual block holds (C = 300)
+    run_fm_decode_case(synth.config(0, seq_lens=[3000]), m=64, top=([0], [12]), sel="c")
+    run_fm_decode_case(synth.config(3, seq_lens=[6000], n_components=64), shared=True, sel="c")
+    wl = synth.config(1, seq_lens=[20000], n_kv_heads=1, n_q_heads=4, n_components=300, top_c=[40], top_s=[16])
+    run_fm_decode_case(wl, m=128, sel="c")
+
+
+def test_fm_whole_and_subcluster_paths_agree():
+    """On one built layout with feature summaries, the whole-cluster step and
+    the subcluster path read the same exact tiles in the same order and sum
+    the same feature-map residual terms in another order."""
+    wl = synth.config(4, seq_lens=[3000, 9000, 1000], n_kv_heads=2, n_q_heads=8, high_entropy_heads=(1,),
+                      n_components=64, top_c=[3, 5, 2], top_s=[12, 14, 10])
+    say(f"[fm paths] {wl.name} lens={wl.seq_lens}")
+    b = synth.generate(wl, device="cuda")
+    kv = ops.KVCache.from_batch(b)
+    W = synth.feature_map_w(128, wl.head_dim, device="cuda")
+    lay = ops.mog_build(kv, wl.n_sink, wl.n_recent, kmeans_iters=wl.kmeans_iters, seed=1, fm_w=W)
+    params = ops.decode_params(wl.n_q_heads, list(wl.top_c), list(wl.top_s), residual="fm")
+    q = b.Q[0].contiguous()
+    ow, lw, cw, _ = ops.mog_decode(lay, kv, q, params, want_sel="c")
+    os_, ls_, cs, _ = ops.mog_decode(lay, kv, q, params, want_sel=True)
+    torch.cuda.synchronize()
+    assert torch.equal(cw, cs)
+    d = ((ow - os_).norm(dim=-1) / os_.norm(dim=-1)).max().item()
+    say(f"  max per-head rel difference {d:.2e}, lse {(lw - ls_).abs().max().item():.2e}")
+    assert d < 1e-5
+    assert torch.allclose(lw, ls_, rtol=0, atol=1e-5 * max(1.0, ls_.abs().max().item()))
 
 
 def test_fm_incremental():
