@@ -111,11 +111,13 @@ def selection_volume(wl, lay, sel_c, sel_s, offs):
             rows_u = sum(off[g + 1] - off[g] for g in subs_union) + wl.n_sink + wl.n_recent
             rows_union += rows_u
             rows_head += G * (wl.n_sink + wl.n_recent)
-            stat_bytes += C * (2 * d + 1) * 4              # cluster mean, variance, count
-            stat_bytes += (C - len(inter_c)) * d * 4       # cluster mean values left out
-            rest_bytes += (C - len(inter_c)) * d * 4 + C * (G + 1) * 4
-            stat_bytes += len(union_c) * S * (2 * d + 1) * 4
-            stat_bytes += len(sub_vbar_needed) * d * 4
+            # group statistics are read in bf16 (2 bytes an element), counts
+            # as int32 offsets
+            stat_bytes += C * (2 * d * 2 + 4)              # cluster mean, variance, count
+            stat_bytes += (C - len(inter_c)) * d * 2       # cluster mean values left out
+            rest_bytes += (C - len(inter_c)) * d * 2 + C * (G + 1) * 4
+            stat_bytes += len(union_c) * S * (2 * d * 2 + 4)
+            stat_bytes += len(sub_vbar_needed) * d * 2
             stat_bytes += G * d * 4 * 2                    # queries in, outputs out
     kv_rows_bytes = rows_union * d * 2 * e
     return dict(rows_union=rows_union, rows_per_head=rows_head / G, n_tokens=n_tokens,

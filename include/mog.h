@@ -142,6 +142,12 @@ typedef struct {
  *                entries) then diagonal population variance of the keys.
  *  cl_vbar, sub_vbar [groups][head_dim] float32: mean value.
  *                Group statistics cover the folded tokens too.
+ *  cl_ms16, cl_vbar16, sub_ms16, sub_vbar16  the same four arrays in bf16
+ *                (bits as uint16, rounded to nearest, ties to even): the
+ *                statistics the decode reads.  mog_build and mog_append
+ *                keep them in step with the float32 arrays; a caller that
+ *                writes the float32 arrays itself calls
+ *                mog_layout_sync_stats before decoding.
  *  fold_sub      [n_units][fold_capacity] int32: subcluster (j*S+i, within
  *                the unit) of every folded token, in fold order.
  *  fold_pos      [n_units][fold_capacity] int32: its token position.
@@ -175,6 +181,10 @@ typedef struct {
   float* cl_vbar;
   float* sub_ms;
   float* sub_vbar;
+  uint16_t* cl_ms16;
+  uint16_t* cl_vbar16;
+  uint16_t* sub_ms16;
+  uint16_t* sub_vbar16;
   int32_t* fold_sub;
   int32_t* fold_pos;
   int32_t* cl_fold;
@@ -272,6 +282,16 @@ mog_status mog_layout_rows(const mog_dims* dims, int64_t* rows);
  * With dims->rows_external the caller also sets out->k_mid / out->v_mid. */
 mog_status mog_layout_init(const mog_dims* dims, void* layout_mem, size_t layout_bytes,
                            mog_layout* out, hipStream_t stream);
+
+/* Enqueue the rewrite of a layout's bf16 statistics (cl_ms16, cl_vbar16,
+ * sub_ms16, sub_vbar16) from its float32 ones, every group of every unit,
+ * for a caller that wrote cl_ms, cl_vbar, sub_ms or sub_vbar itself (an
+ * imported layout).  The decode reads group statistics in bf16 (the storage
+ * precision of the group means and variances is left open by the Iceberg
+ * and MoG write-ups; bf16 halves the bytes the latency-bound kernels move).
+ * Allocates nothing.  Errors: MOG_ERR_INVALID_ARG for a NULL or incomplete
+ * layout, MOG_ERR_HIP if the launch fails. */
+mog_status mog_layout_sync_stats(const mog_layout* layout, hipStream_t stream);
 
 /* Host copy of the geometry of unit `unit` of a layout. */
 mog_status mog_layout_unit(const mog_layout* layout, int32_t unit, mog_unit* out);

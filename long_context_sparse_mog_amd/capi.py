@@ -54,7 +54,8 @@ class mog_layout(C.Structure):
                 ("fold_count", i32 * MOG_MAX_SEQ), ("total_mid", i64),
                 ("total_cl", i64), ("total_sub", i64), ("total_off", i64), ("units", vp),
                 ("k_mid", vp), ("v_mid", vp), ("perm", vp), ("sub_off", vp), ("cl_ms", vp),
-                ("cl_vbar", vp), ("sub_ms", vp), ("sub_vbar", vp), ("fold_sub", vp),
+                ("cl_vbar", vp), ("sub_ms", vp), ("sub_vbar", vp), ("cl_ms16", vp), ("cl_vbar16", vp),
+                ("sub_ms16", vp), ("sub_vbar16", vp), ("fold_sub", vp),
                 ("fold_pos", vp), ("cl_fold", vp), ("sub_fold", vp),
                 ("append_scratch", vp), ("fm_w", vp), ("cl_fz", vp), ("sub_fz", vp),
                 ("rows_external", i32)]
@@ -80,6 +81,7 @@ SIGNATURES = {
     "mog_layout_rows": (i32, [C.POINTER(mog_dims), C.POINTER(i64)]),
     "mog_layout_init": (i32, [C.POINTER(mog_dims), vp, C.c_size_t, C.POINTER(mog_layout), vp]),
     "mog_layout_unit": (i32, [C.POINTER(mog_layout), i32, C.POINTER(mog_unit)]),
+    "mog_layout_sync_stats": (i32, [C.POINTER(mog_layout), vp]),
     "mog_workspace_size": (i32, [i32, C.POINTER(mog_kv), C.POINTER(mog_layout),
                                  C.POINTER(mog_build_params), C.POINTER(mog_decode_params),
                                  C.POINTER(C.c_size_t)]),

@@ -52,6 +52,7 @@ struct Totals {
 struct LayoutPlan {
   Totals t;
   size_t o_units, o_kmid, o_vmid, o_perm, o_suboff, o_clms, o_clvb, o_subms, o_subvb;
+  size_t o_clms16, o_clvb16, o_subms16, o_subvb16;
   size_t o_foldsub, o_foldpos, o_clfold, o_subfold, o_appws, o_fmw, o_clfz, o_subfz, bytes;
 };
 
@@ -108,6 +109,10 @@ LayoutPlan plan_layout(const mog_dims* d) {
   p.o_clvb = o; o = align_up(o + (size_t)p.t.cl * D * 4);
   p.o_subms = o; o = align_up(o + (size_t)p.t.sub * 2 * D * 4);
   p.o_subvb = o; o = align_up(o + (size_t)p.t.sub * D * 4);
+  p.o_clms16 = o; o = align_up(o + (size_t)p.t.cl * 2 * D * 2);
+  p.o_clvb16 = o; o = align_up(o + (size_t)p.t.cl * D * 2);
+  p.o_subms16 = o; o = align_up(o + (size_t)p.t.sub * 2 * D * 2);
+  p.o_subvb16 = o; o = align_up(o + (size_t)p.t.sub * D * 2);
   p.o_foldsub = o; o = align_up(o + (size_t)nu * d->fold_capacity * 4);
   p.o_foldpos = o; o = align_up(o + (size_t)nu * d->fold_capacity * 4);
   p.o_clfold = o; o = align_up(o + (size_t)p.t.cl * 4);
@@ -303,7 +308,8 @@ DensePlan plan_dense(const mog_kv* kv, const mog_decode_params* p) {
 
 mog_status check_layout_arrays(const mog_layout* L) {
   if (!L->units || !L->k_mid || !L->v_mid || !L->sub_off || !L->cl_ms || !L->cl_vbar || !L->sub_ms ||
-      !L->sub_vbar || !L->cl_fold || !L->sub_fold || !L->append_scratch)
+      !L->sub_vbar || !L->cl_ms16 || !L->cl_vbar16 || !L->sub_ms16 || !L->sub_vbar16 || !L->cl_fold ||
+      !L->sub_fold || !L->append_scratch)
     return fail(MOG_ERR_INVALID_ARG, "layout has NULL arrays (not initialised?)");
   if (L->fold_capacity < 0 || L->fold_capacity > MOG_MAX_FOLD)
     return fail(MOG_ERR_INVALID_ARG, "layout fold_capacity=%d outside [0, %d]", L->fold_capacity, MOG_MAX_FOLD);
@@ -473,6 +479,10 @@ static mog_status layout_carve(const mog_dims* dims, void* mem, size_t mem_bytes
   L.cl_vbar = reinterpret_cast<float*>(b + p.o_clvb);
   L.sub_ms = reinterpret_cast<float*>(b + p.o_subms);
   L.sub_vbar = reinterpret_cast<float*>(b + p.o_subvb);
+  L.cl_ms16 = reinterpret_cast<uint16_t*>(b + p.o_clms16);
+  L.cl_vbar16 = reinterpret_cast<uint16_t*>(b + p.o_clvb16);
+  L.sub_ms16 = reinterpret_cast<uint16_t*>(b + p.o_subms16);
+  L.sub_vbar16 = reinterpret_cast<uint16_t*>(b + p.o_subvb16);
   L.fold_sub = dims->fold_capacity ? reinterpret_cast<int32_t*>(b + p.o_foldsub) : nullptr;
   L.fold_pos = dims->fold_capacity ? reinterpret_cast<int32_t*>(b + p.o_foldpos) : nullptr;
   L.cl_fold = reinterpret_cast<int32_t*>(b + p.o_clfold);
@@ -499,6 +509,17 @@ mog_status mog_layout_init(const mog_dims* dims, void* layout_mem, size_t layout
   hipError_t e = launch_layout_table(L, sa, stream);
   if (e != hipSuccess) return fail(MOG_ERR_HIP, "layout table launch: %s", hipGetErrorString(e));
   *out = L;
+  return ok();
+}
+
+mog_status mog_layout_sync_stats(const mog_layout* L, hipStream_t stream) {
+  if (!L) return fail(MOG_ERR_INVALID_ARG, "layout is NULL");
+  mog_status st = check_layout_arrays(L);
+  if (st != MOG_OK) return st;
+  if (L->head_dim != 64 && L->head_dim != 128) return fail(MOG_ERR_INVALID_ARG, "layout head_dim=%d", L->head_dim);
+  if (L->total_cl < 0 || L->total_sub < 0) return fail(MOG_ERR_INVALID_ARG, "layout has negative group counts");
+  hipError_t e = launch_stats16(*L, stream);
+  if (e != hipSuccess) return fail(MOG_ERR_HIP, "statistics copy launch: %s", hipGetErrorString(e));
   return ok();
 }
 

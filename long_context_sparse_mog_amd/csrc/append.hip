@@ -28,6 +28,10 @@ struct AArgs {
   float* cl_vbar;
   float* sub_ms;
   float* sub_vbar;
+  uint16_t* cl_ms16;  // bf16 copies, updated beside them
+  uint16_t* cl_vbar16;
+  uint16_t* sub_ms16;
+  uint16_t* sub_vbar16;
   int32_t* cl_fold;
   int32_t* sub_fold;
   int32_t* fold_sub;
@@ -53,7 +57,7 @@ __device__ inline float to_f(uint16_t x) { return __uint_as_float((uint32_t)x <<
 // var and mean value vbar of one dimension (the stored float32 values),
 // updated by Welford's formulas in float64 and stored as float32.
 __device__ inline void welford_add(float mu_f, float var_f, float vbar_f, int n, double k, double v, float* mu_o,
-                                   float* var_o, float* vbar_o) {
+                                   float* var_o, float* vbar_o, uint16_t* mu_b, uint16_t* var_b, uint16_t* vbar_b) {
 #pragma clang fp contract(off)
   const double n1 = (double)(n + 1);
   const double mu = mu_f, var = var_f, vbar = vbar_f;
@@ -64,6 +68,10 @@ __device__ inline void welford_add(float mu_f, float var_f, float vbar_f, int n,
   *mu_o = (float)mu1;
   *var_o = (float)var1;
   *vbar_o = (float)vbar1;
+  // (the decode's bf16 copies, rounded from the stored float32 values)
+  *mu_b = bf16_bits((float)mu1);
+  *var_b = bf16_bits((float)var1);
+  *vbar_b = bf16_bits((float)vbar1);
 }
 
 // (d2, id) lexicographic minimum over the lanes l of the wave that differ
@@ -360,9 +368,11 @@ __global__ __launch_bounds__(256) void k_append_apply(AArgs a, int it) {
     vf[tid] = vx_t;
     const double k = (double)to_f(kx_t), v = (double)to_f(vx_t);
     welford_add(c_mu, c_var, c_vb, cn, k, v, a.cl_ms + cg * (2 * D) + tid, a.cl_ms + cg * (2 * D) + D + tid,
-                a.cl_vbar + cg * D + tid);
+                a.cl_vbar + cg * D + tid, a.cl_ms16 + cg * (2 * D) + tid, a.cl_ms16 + cg * (2 * D) + D + tid,
+                a.cl_vbar16 + cg * D + tid);
     welford_add(a.sub_ms[sg * (2 * D) + tid], a.sub_ms[sg * (2 * D) + D + tid], a.sub_vbar[sg * D + tid], sel[2], k,
-                v, a.sub_ms + sg * (2 * D) + tid, a.sub_ms + sg * (2 * D) + D + tid, a.sub_vbar + sg * D + tid);
+                v, a.sub_ms + sg * (2 * D) + tid, a.sub_ms + sg * (2 * D) + D + tid, a.sub_vbar + sg * D + tid,
+                a.sub_ms16 + sg * (2 * D) + tid, a.sub_ms16 + sg * (2 * D) + D + tid, a.sub_vbar16 + sg * D + tid);
   }
   if (a.fm_dim) {
     // the token's features join both groups' feature sums
@@ -415,6 +425,10 @@ hipError_t launch_append(const AppendLaunch& x, hipStream_t s) {
   a.cl_vbar = x.L.cl_vbar;
   a.sub_ms = x.L.sub_ms;
   a.sub_vbar = x.L.sub_vbar;
+  a.cl_ms16 = x.L.cl_ms16;
+  a.cl_vbar16 = x.L.cl_vbar16;
+  a.sub_ms16 = x.L.sub_ms16;
+  a.sub_vbar16 = x.L.sub_vbar16;
   a.cl_fold = x.L.cl_fold;
   a.sub_fold = x.L.sub_fold;
   a.fold_sub = x.L.fold_sub;

@@ -57,6 +57,10 @@ struct BArgs {
   float* cl_vbar;
   float* sub_ms;
   float* sub_vbar;
+  uint16_t* cl_ms16;  // bf16 copies of the four, written beside them
+  uint16_t* cl_vbar16;
+  uint16_t* sub_ms16;
+  uint16_t* sub_vbar16;
   unsigned long long seed;
   // feature-map summaries
   const float* fm_w_in;
@@ -738,8 +742,9 @@ __global__ __launch_bounds__(256) void k_gather_rows(BArgs a) {
 
 // 5b. Statistics of one cluster and its subclusters: two passes over the
 //     reordered keys (means, then centred squares), one over the values,
-//     accumulated in float64, stored in float32.  Thread (d, phase) owns
-//     dimension d of every NPH-th row.
+//     accumulated in float64, stored in float32 and, rounded from that, in
+//     bf16 for the decode.  Thread (d, phase) owns dimension d of every
+//     NPH-th row.
 template <int D, typename T>
 __global__ __launch_bounds__(256) void k_group_stats(BArgs a) {
   constexpr int NPH = 256 / D;
@@ -759,13 +764,17 @@ __global__ __launch_bounds__(256) void k_group_stats(BArgs a) {
     const int r0 = g < 0 ? off[j * S] : off[j * S + g];
     const int r1 = g < 0 ? off[(j + 1) * S] : off[j * S + g + 1];
     const int n = r1 - r0;
-    float* ms = g < 0 ? a.cl_ms + cg * 2 * D : a.sub_ms + (U.sub_base + (int64_t)j * S + g) * 2 * D;
-    float* vb = g < 0 ? a.cl_vbar + cg * D : a.sub_vbar + (U.sub_base + (int64_t)j * S + g) * D;
+    const int64_t gi = g < 0 ? cg : U.sub_base + (int64_t)j * S + g;
+    float* ms = (g < 0 ? a.cl_ms : a.sub_ms) + gi * 2 * D;
+    float* vb = (g < 0 ? a.cl_vbar : a.sub_vbar) + gi * D;
+    uint16_t* ms16 = (g < 0 ? a.cl_ms16 : a.sub_ms16) + gi * 2 * D;
+    uint16_t* vb16 = (g < 0 ? a.cl_vbar16 : a.sub_vbar16) + gi * D;
     if (n == 0) {
       if (ph == 0) {
         ms[d] = 0.f;
         ms[D + d] = 0.f;
         vb[d] = 0.f;
+        ms16[d] = ms16[D + d] = vb16[d] = 0;
       }
       continue;
     }
@@ -799,6 +808,9 @@ __global__ __launch_bounds__(256) void k_group_stats(BArgs a) {
       ms[d] = (float)mean;
       ms[D + d] = (float)(t / n);
       vb[d] = (float)vmean;
+      ms16[d] = bf16_bits((float)mean);
+      ms16[D + d] = bf16_bits((float)(t / n));
+      vb16[d] = bf16_bits((float)vmean);
     }
     __syncthreads();
   }
@@ -909,6 +921,34 @@ __global__ void k_layout_table(mog_unit* units, SeqArgs seq, int Hkv, int n_sink
   units[u] = U;
 }
 
+// The bf16 copies of the group statistics: element i of each float32
+// array, rounded (grid-stride over the four arrays one after another).
+__global__ __launch_bounds__(256) void k_stats16(const float* a0, uint16_t* b0, int64_t n0, const float* a1,
+                                                 uint16_t* b1, int64_t n1, const float* a2, uint16_t* b2,
+                                                 int64_t n2, const float* a3, uint16_t* b3, int64_t n3) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n0 + n1 + n2 + n3; i += stride) {
+    int64_t j = i;
+    if (j < n0) { b0[j] = bf16_bits(a0[j]); continue; }
+    j -= n0;
+    if (j < n1) { b1[j] = bf16_bits(a1[j]); continue; }
+    j -= n1;
+    if (j < n2) { b2[j] = bf16_bits(a2[j]); continue; }
+    j -= n2;
+    b3[j] = bf16_bits(a3[j]);
+  }
+}
+
+hipError_t launch_stats16(const mog_layout& L, hipStream_t s) {
+  const int64_t D = L.head_dim;
+  const int64_t n0 = L.total_cl * 2 * D, n1 = L.total_cl * D, n2 = L.total_sub * 2 * D, n3 = L.total_sub * D;
+  const int64_t nt = n0 + n1 + n2 + n3;
+  const int64_t nb = nt <= 0 ? 1 : (nt + 255) / 256 < 4096 ? (nt + 255) / 256 : 4096;
+  hipLaunchKernelGGL(k_stats16, dim3((unsigned)nb), dim3(256), 0, s, L.cl_ms, L.cl_ms16, n0, L.cl_vbar,
+                     L.cl_vbar16, n1, L.sub_ms, L.sub_ms16, n2, L.sub_vbar, L.sub_vbar16, n3);
+  return hipGetLastError();
+}
+
 hipError_t launch_layout_table(const mog_layout& L, const SeqArgs& seq, hipStream_t s) {
   const int n = L.n_units;
   const int64_t n_cnt = L.total_cl + L.total_sub;
@@ -944,6 +984,10 @@ static hipError_t build_impl(const BuildLaunch& x, hipStream_t s) {
   a.cl_vbar = x.L.cl_vbar;
   a.sub_ms = x.L.sub_ms;
   a.sub_vbar = x.L.sub_vbar;
+  a.cl_ms16 = x.L.cl_ms16;
+  a.cl_vbar16 = x.L.cl_vbar16;
+  a.sub_ms16 = x.L.sub_ms16;
+  a.sub_vbar16 = x.L.sub_vbar16;
   a.seed = x.seed;
   const int nu = x.L.n_units;
   int max_mid = 0;

@@ -25,10 +25,12 @@ struct LayoutRef {
   const void* k_mid;
   const void* v_mid;
   const int32_t* sub_off;
-  const float* cl_ms;
-  const float* cl_vbar;
-  const float* sub_ms;
-  const float* sub_vbar;
+  // group statistics in bf16 (the layout's copies of its float32 ones):
+  // [groups][2 D] key mean | variance, [groups][D] value mean
+  const uint16_t* cl_ms;
+  const uint16_t* cl_vbar;
+  const uint16_t* sub_ms;
+  const uint16_t* sub_vbar;
   // folded tokens (incremental decode): per-group counts, and per unit the
   // subcluster of every fold row; unit u's fold rows start at layout row
   // fold_row0 + u * fold_cap
@@ -176,6 +178,46 @@ __device__ inline void load_floats(const float* p, float (&x)[N]) {
 #pragma unroll
     for (int i = 0; i < N; ++i) x[i] = __builtin_nontemporal_load(p + i);
   }
+}
+
+// N consecutive bf16 statistics as float32 (exact), one load; non-temporal
+// like the float32 rows above.
+template <int N>
+__device__ inline void load_floats(const uint16_t* p, float (&x)[N]) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  if constexpr (N == 4) {
+    const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    x[0] = bf16_lo(t.x); x[1] = bf16_hi(t.x); x[2] = bf16_lo(t.y); x[3] = bf16_hi(t.y);
+  } else if constexpr (N == 2) {
+    const uint32_t t = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+    x[0] = bf16_lo(t); x[1] = bf16_hi(t);
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = __uint_as_float((uint32_t)__builtin_nontemporal_load(p + i) << 16);
+  }
+}
+
+// N consecutive bf16 statistics (N even) as N / 2 packed pairs, one
+// non-temporal load.
+template <int N>
+__device__ inline void load_bf16_pairs(const uint16_t* p, uint32_t (&r)[N / 2]) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  if constexpr (N == 4) {
+    const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    r[0] = t.x; r[1] = t.y;
+  } else {
+    static_assert(N == 2, "rows of 2 or 4 statistics a lane");
+    r[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+  }
+}
+
+// N (1 or 2) consecutive bf16 statistics as the bits of one 32-bit word
+// (the first in the low half), one non-temporal load.
+template <int N>
+__device__ inline uint32_t load_bf16_bits(const uint16_t* p) {
+  static_assert(N == 1 || N == 2, "one or two statistics a lane");
+  if constexpr (N == 2) return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+  else return (uint32_t)__builtin_nontemporal_load(p);
 }
 
 // Per-lane coefficients of the score: lanes 0-31 hold scale*log2e*q_i for the
@@ -1295,30 +1337,37 @@ __device__ inline void sub_wave_cluster(const DArgs& a, int u, int x, const mog_
   const int s_keep = s_keep_raw < 0 ? 0 : s_keep_raw;
   float* sc = reinterpret_cast<float*>(&lsc[0][0]);  // sc[h * SR + i]
   uint32_t sm = 0u;  // lane i: the heads that chose subcluster i
+  // every subcluster's value mean (the lane's VPL bf16 elements, packed),
+  // for the residual: loaded with the score rows, unpacked where used (a
+  // load whose result is used inside a branch waits there)
+  uint32_t vraw[SR];
   if (s_keep >= S) {
     // a budget of S or more reads every nonempty subcluster of the cluster
     sm = (lane < S && cnt > 0) ? mask : 0u;
   } else {
+    // every row of the cluster in one round trip: the bf16 pairs stay packed
+    // (EPL / 2 registers a row) until their chunk is scored
+    uint32_t raw[SR][EPL / 2];
+#pragma unroll
+    for (int k = 0; k < SR; ++k) load_bf16_pairs<EPL>(a.L.sub_ms + (sg0 + min(k, S - 1)) * (2 * D) + lane * EPL, raw[k]);
     float coef[G][EPL];
     score_coefs<D, G>(a, a.q + ((int64_t)U.seq * a.Hq + (int64_t)U.kv_head * G) * D, coef);
-    float xr[2][RC][EPL];
-    auto load_chunk = [&](int c, float (&dst)[RC][EPL]) {
-#pragma unroll
-      for (int k = 0; k < RC; ++k)
-        load_floats<EPL>(a.L.sub_ms + (sg0 + min(c * RC + k, S - 1)) * (2 * D) + lane * EPL, dst[k]);
-    };
-    load_chunk(0, xr[0]);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      if (c + 1 < NCH) load_chunk(c + 1, xr[(c + 1) & 1]);
       float part[RC * G];
 #pragma unroll
       for (int k = 0; k < RC; ++k) {
+        float xk[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL / 2; ++e) {
+          xk[2 * e] = bf16_lo(raw[c * RC + k][e]);
+          xk[2 * e + 1] = bf16_hi(raw[c * RC + k][e]);
+        }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           float t = 0.f;
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) t += coef[h][e] * xr[c & 1][k][e];
+          for (int e = 0; e < EPL; ++e) t += coef[h][e] * xk[e];
           part[k * G + h] = t;
         }
       }
@@ -1327,6 +1376,12 @@ __device__ inline void sub_wave_cluster(const DArgs& a, int u, int x, const mog_
       const int ci = __shfl(cnt, i & 63, 64);
       // (rows past S score -inf, so every row of the LDS row is written)
       if (rs_owner<RC * G>(lane)) sc[h * SR + i] = (i < S && ci > 0) ? t + log2f((float)ci) : -INFINITY;
+    }
+    // (issued once the rows' registers are free: the launch then keeps
+    // five waves a SIMD resident at one head per KV head)
+    if (a.residual) {
+#pragma unroll
+      for (int k = 0; k < SR; ++k) vraw[k] = load_bf16_bits<VPL>(a.L.sub_vbar + (sg0 + min(k, S - 1)) * D + lane * VPL);
     }
     __asm__ volatile("" ::: "memory");  // (a wave's LDS operations run in order)
 #pragma unroll
@@ -1365,6 +1420,43 @@ __device__ inline void sub_wave_cluster(const DArgs& a, int u, int x, const mog_
       for (int j = __popcll(bits) + lane; j < a.s_stride; j += 64) a.sel_s[base + j] = -1;
     }
   }
+  // the residual first: its value-mean loads are then the wave's only
+  // outstanding memory operations (the vector memory counter also counts
+  // stores, so a wait issued after the tile stores and the row-count atomic
+  // below would wait for them too)
+  if (a.residual) {
+    // residual of the subclusters a choosing head left out: every lane holds
+    // VPL elements of each such subcluster's value mean
+    const uint32_t need = (lane < S && cnt > 0) ? (mask & ~sm) : 0u;
+    const unsigned long long any_need = __ballot(need != 0u);
+    float rm[G], rl[G], ro[G][VPL];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      rm[h] = -INFINITY;
+      rl[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) ro[h][e] = 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < SR; ++k) {
+      if (!((any_need >> k) & 1ull)) continue;
+      const uint32_t nk = (uint32_t)__builtin_amdgcn_readlane((int)need, k);
+      float vb[VPL];
+      vb[0] = bf16_lo(vraw[k]);
+      if constexpr (VPL == 2) vb[1] = bf16_hi(vraw[k]);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        if ((nk >> h) & 1u) add_group<VPL>(rm[h], rl[h], ro[h], sc[h * SR + k], vb);
+    }
+    // the wave's record: one (o, m, l) row per head
+    float* dst = a.ws.res_part + ((int64_t)u * a.nb_res + x) * G * RS;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) dst[h * RS + lane * VPL + e] = ro[h][e];
+      if (lane == 0) *reinterpret_cast<float2*>(dst + h * RS + D) = float2{rm[h], rl[h]};
+    }
+  }
   {
     const uint32_t rows = (lane < S && sm != 0u) ? (uint32_t)cnt : 0u;
     const int rsum = (int)wave_reduce_uniform(rows, [](uint32_t p, uint32_t q) { return p + q; }, 0u);
@@ -1374,39 +1466,6 @@ __device__ inline void sub_wave_cluster(const DArgs& a, int u, int x, const mog_
   const int n_tiles =
       write_run_tiles(ctiles, U.row_base, a.L_head_dim, lane < S ? o_i : 0, lane < S ? o_n : 0, lane < S ? sm : 0u);
   if (lane == 0) a.ws.ch_ntiles[cw + x] = n_tiles;
-  if (!a.residual) return;
-  // residual of the subclusters a choosing head left out: every lane holds
-  // VPL elements of each such subcluster's value mean
-  const uint32_t need = (lane < S && cnt > 0) ? (mask & ~sm) : 0u;
-  const unsigned long long any_need = __ballot(need != 0u);
-  float vb[SR][VPL];
-#pragma unroll
-  for (int k = 0; k < SR; ++k)
-    if ((any_need >> k) & 1ull) load_floats<VPL>(a.L.sub_vbar + (sg0 + k) * D + lane * VPL, vb[k]);
-  float rm[G], rl[G], ro[G][VPL];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    rm[h] = -INFINITY;
-    rl[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < VPL; ++e) ro[h][e] = 0.f;
-  }
-#pragma unroll
-  for (int k = 0; k < SR; ++k) {
-    if (!((any_need >> k) & 1ull)) continue;
-    const uint32_t nk = (uint32_t)__builtin_amdgcn_readlane((int)need, k);
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-      if ((nk >> h) & 1u) add_group<VPL>(rm[h], rl[h], ro[h], sc[h * SR + k], vb[k]);
-  }
-  // the wave's record: one (o, m, l) row per head
-  float* dst = a.ws.res_part + ((int64_t)u * a.nb_res + x) * G * RS;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-#pragma unroll
-    for (int e = 0; e < VPL; ++e) dst[h * RS + lane * VPL + e] = ro[h][e];
-    if (lane == 0) *reinterpret_cast<float2*>(dst + h * RS + D) = float2{rm[h], rl[h]};
-  }
 }
 
 
@@ -2232,10 +2291,10 @@ hipError_t launch_decode(const DecodeLaunch& x, hipStream_t s) {
   a.L.k_mid = x.L.k_mid;
   a.L.v_mid = x.L.v_mid;
   a.L.sub_off = x.L.sub_off;
-  a.L.cl_ms = x.L.cl_ms;
-  a.L.cl_vbar = x.L.cl_vbar;
-  a.L.sub_ms = x.L.sub_ms;
-  a.L.sub_vbar = x.L.sub_vbar;
+  a.L.cl_ms = x.L.cl_ms16;
+  a.L.cl_vbar = x.L.cl_vbar16;
+  a.L.sub_ms = x.L.sub_ms16;
+  a.L.sub_vbar = x.L.sub_vbar16;
   a.L.cl_fold = x.L.cl_fold;
   a.L.sub_fold = x.L.sub_fold;
   a.L.fold_sub = x.L.fold_sub;

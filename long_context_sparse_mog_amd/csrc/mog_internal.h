@@ -201,6 +201,8 @@ constexpr int kPartPad = 4;
 constexpr int kExactResidentBlocks = 512;   // partial record = o[D], m, l, pad
 
 hipError_t launch_layout_table(const mog_layout& L, const SeqArgs& seq, hipStream_t s);
+// the bf16 copies of every group statistic, rewritten from the float32 ones
+hipError_t launch_stats16(const mog_layout& L, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Append (incremental decode) launch block.
@@ -293,6 +295,12 @@ __device__ inline mog_unit uni_unit(const mog_unit* p) {
 }
 
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+// float32 -> bf16 bits, rounded to nearest, ties to even (NaN stays NaN)
+__device__ inline uint16_t bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // 8 consecutive elements starting at element offset `off` as float32.

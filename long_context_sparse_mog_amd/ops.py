@@ -160,6 +160,11 @@ class Layout:
             cl_vbar=self._view(c.cl_vbar, c.total_cl * D, torch.float32).view(-1, D),
             sub_ms=self._view(c.sub_ms, c.total_sub * 2 * D, torch.float32).view(-1, 2 * D),
             sub_vbar=self._view(c.sub_vbar, c.total_sub * D, torch.float32).view(-1, D),
+            # the decode's bf16 copies of the four above (the bits, as int16)
+            cl_ms16=self._view(c.cl_ms16, c.total_cl * 2 * D, torch.int16).view(-1, 2 * D),
+            cl_vbar16=self._view(c.cl_vbar16, c.total_cl * D, torch.int16).view(-1, D),
+            sub_ms16=self._view(c.sub_ms16, c.total_sub * 2 * D, torch.int16).view(-1, 2 * D),
+            sub_vbar16=self._view(c.sub_vbar16, c.total_sub * D, torch.int16).view(-1, D),
         )
 
     def export_unit(self, u: int) -> dict:
@@ -387,7 +392,9 @@ def import_layout(kv: KVCache, n_sink, n_recent, units, k_rows=None, v_rows=None
     ``units[u]`` is a dict with ``perm`` (token position of every reordered
     row), ``sub_off`` (C*S+1 row offsets) and float32 ``cl_mu``, ``cl_var``,
     ``cl_vbar``, ``sub_mu``, ``sub_var``, ``sub_vbar``.  The reordered K/V
-    rows are gathered from ``kv`` on the device.
+    rows are gathered from ``kv`` on the device; the decode's bf16 copies of
+    the statistics are then rewritten by the library
+    (``mog_layout_sync_stats``).
     """
     fm = units[0].get("cl_z") if units else None
     fm_dim = 0 if fm is None else int(np.asarray(fm).shape[1])
@@ -428,6 +435,8 @@ def import_layout(kv: KVCache, n_sink, n_recent, units, k_rows=None, v_rows=None
         if fm_dim:
             a["cl_fz"][cl] = f32(src["cl_z"])
             a["sub_fz"][sb] = f32(src["sub_z"])
+    # the decode's bf16 copies of the statistics just written
+    check(lib().mog_layout_sync_stats(C.byref(lay.c), _stream(stream)), "mog_layout_sync_stats")
     if fm_dim:
         a["fm_w"][:] = torch.as_tensor(np.asarray(units[0]["fm_w"], np.float32), device=dev)
         sc = float(units[0]["fm_scale"])

@@ -24,6 +24,8 @@ from .mog import (  # noqa: F401
     lloyd,
     group_stats,
     group_log_mass,
+    bf16_round,
+    decode_statistics,
     top_by_score,
     UnitLayout,
     build_unit,

@@ -88,12 +88,22 @@ in the design notes of the repository):
       numerator models; the library implements the mean-value one (a value
       summary holds m*d floats per group, more than the group's rows at the
       workloads' group sizes).
+  R18 Storage precision of the group statistics at decode time (not fixed
+      by the pages): the decode reads every group's mean key, variance and
+      mean value rounded to bfloat16 (``decode_statistics``: float32, then
+      round to nearest, ties to even, at 8 significant bits), the precision
+      the cache's own keys and values are stored in.  Selections and
+      residual terms are computed from those values; the build and the
+      incremental updates (R15) keep the statistics at full precision.
+      ``decode_unit`` itself takes whatever statistics the layout holds, so
+      every property of the method is checked on exact statistics; the GPU
+      parity tests hand it ``decode_statistics(L)``.
 """
 
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 
 import numpy as np
 
@@ -566,6 +576,30 @@ def fm_log_mass(q, Z, W, scale):
 # ---------------------------------------------------------------------------
 # Decode (readings R6-R8; merge rule from page 4's abstract)
 # ---------------------------------------------------------------------------
+
+
+def bf16_round(x) -> np.ndarray:
+    """x rounded to bfloat16, returned as float64 (reading R18).  bfloat16
+    keeps float32's sign and 8 exponent bits and the top 7 of its 23
+    fraction bits, so the value is first stored as float32 and the float32
+    bit pattern is then rounded at bit 16: add half of that unit minus one,
+    plus the kept lowest bit (round half to even), and clear the low 16
+    bits.  A carry out of the fraction steps the exponent, which also sends
+    values past the largest bfloat16 to infinity; NaN stays NaN."""
+    f = np.atleast_1d(np.asarray(x, dtype=np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    r = (((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16).astype(np.uint32)
+    out = r.view(np.float32).astype(np.float64)
+    out[np.isnan(f)] = np.nan
+    return out.reshape(np.shape(x))
+
+
+def decode_statistics(L: UnitLayout) -> UnitLayout:
+    """The layout as the decode reads it (reading R18): cluster and
+    subcluster mean keys, variances and mean values rounded to bfloat16.
+    Counts, offsets, folded-token bookkeeping and feature sums are kept."""
+    return replace(L, cl_mu=bf16_round(L.cl_mu), cl_var=bf16_round(L.cl_var), cl_vbar=bf16_round(L.cl_vbar),
+                   sub_mu=bf16_round(L.sub_mu), sub_var=bf16_round(L.sub_var), sub_vbar=bf16_round(L.sub_vbar))
 
 
 def group_log_mass(q, count, mu, var, scale):

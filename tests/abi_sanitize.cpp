@@ -71,6 +71,7 @@ static mog_layout host_layout(const std::vector<int32_t>& lens, int cap, const s
   L.k_mid = L.v_mid = p;
   L.perm = L.sub_off = L.fold_sub = L.fold_pos = L.cl_fold = L.sub_fold = static_cast<int32_t*>(p);
   L.cl_ms = L.cl_vbar = L.sub_ms = L.sub_vbar = static_cast<float*>(p);
+  L.cl_ms16 = L.cl_vbar16 = L.sub_ms16 = L.sub_vbar16 = static_cast<uint16_t*>(p);
   L.append_scratch = p;
   return L;
 }
@@ -150,6 +151,11 @@ int main() {
   mog_unit U;
   EXPECT(mog_layout_unit(&g, 6, &U) == MOG_ERR_INVALID_ARG);
   EXPECT(mog_layout_unit(&g, -1, &U) == MOG_ERR_INVALID_ARG);
+  // the statistics copy: rejected before any launch
+  EXPECT(mog_layout_sync_stats(nullptr, nullptr) == MOG_ERR_INVALID_ARG);
+  mog_layout bad = g;
+  bad.head_dim = 96;
+  EXPECT(mog_layout_sync_stats(&bad, nullptr) == MOG_ERR_INVALID_ARG);
 
   // workspace sizes and parameter rejections
   mog_kv kv = kv_of(ok_len);

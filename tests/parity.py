@@ -98,6 +98,8 @@ def compare_unit(L, K, V, Q, c, s, gpu_out, gpu_lse, gpu_sel_c, gpu_sel_s, tol, 
     ``gpu_sel_s`` None: a budget of whole clusters (s >= S), whose chosen
     subclusters are every nonempty one of each chosen cluster."""
     G, d = Q.shape
+    # the statistics as the library's decode reads them (reading R18)
+    L = O.decode_statistics(L)
     if gpu_sel_s is None:
         assert s >= L.S, (s, L.S)
         gpu_sel_s = [[np.flatnonzero(L.sub_count[int(j) * L.S:(int(j) + 1) * L.S] > 0) if j >= 0 else []

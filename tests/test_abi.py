@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     out = subprocess.run(["nm", "-D", "--defined-only", capi.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (mog_\w+)", out))
     assert set(names) == exported, (set(names) ^ exported)
@@ -76,10 +76,11 @@ def test_layout_size_matches_geometry(L):
     out = C.c_size_t()
     assert L.mog_layout_size(C.byref(d), C.byref(out)) == capi.MOG_OK
     n_mid, Cc, S, D = 1048576 - 320, 1024, 20, 128
-    # rows, perm, offsets, group statistics, per-group fold counts
-    expect = 8 * (2 * n_mid * D * 2 + n_mid * 4 + (Cc * S + 1) * 4 + Cc * 3 * D * 4 + Cc * S * 3 * D * 4
+    # rows, perm, offsets, group statistics (float32, and the decode's bf16
+    # copies), per-group fold counts
+    expect = 8 * (2 * n_mid * D * 2 + n_mid * 4 + (Cc * S + 1) * 4 + (Cc + Cc * S) * 3 * D * (4 + 2)
                   + (Cc + Cc * S) * 4)
-    assert expect <= out.value <= expect + 16 * 256
+    assert expect <= out.value <= expect + 20 * 256
     # a fold area: K/V rows, their subcluster and position, per unit
     cap = 1000
     d2, keep2 = _dims([1048576], fold_capacity=cap)
@@ -278,7 +279,8 @@ def _host_layout(lens, cap, folded):
         lay.seq_lens[i] = x
         lay.fold_count[i] = f
     for name in ("units", "k_mid", "v_mid", "perm", "sub_off", "cl_ms", "cl_vbar", "sub_ms", "sub_vbar",
-                 "fold_sub", "fold_pos", "cl_fold", "sub_fold", "append_scratch"):
+                 "cl_ms16", "cl_vbar16", "sub_ms16", "sub_vbar16", "fold_sub", "fold_pos", "cl_fold", "sub_fold",
+                 "append_scratch"):
         setattr(lay, name, 0x10000)
     return lay
 
@@ -313,3 +315,16 @@ def test_status_strings(L):
     for s in range(6):
         assert L.mog_status_string(s).decode()
     assert L.mog_status_string(99).decode() == "unknown status"
+
+
+def test_sync_stats_validation(L):
+    # rejected before anything is enqueued: no layout, a layout with NULL
+    # arrays, and a complete descriptor with an unsupported head dimension
+    assert L.mog_layout_sync_stats(None, None) == capi.MOG_ERR_INVALID_ARG
+    empty = capi.mog_layout()
+    assert L.mog_layout_sync_stats(C.byref(empty), None) == capi.MOG_ERR_INVALID_ARG
+    assert b"NULL arrays" in L.mog_last_error()
+    lay = _host_layout([5000], cap=0, folded=[0])
+    lay.head_dim = 96
+    assert L.mog_layout_sync_stats(C.byref(lay), None) == capi.MOG_ERR_INVALID_ARG
+    assert b"head_dim" in L.mog_last_error()

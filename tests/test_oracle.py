@@ -955,3 +955,56 @@ def test_feature_value_sums_follow_the_folds():
     R = O.with_feature_summaries(F, K, W, V=V)
     np.testing.assert_allclose(F.cl_zv, R.cl_zv, rtol=1e-5, atol=1e-6)
     np.testing.assert_allclose(F.sub_zv, R.sub_zv, rtol=1e-5, atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# Reading R18: the decode's statistics in bfloat16
+# ---------------------------------------------------------------------------
+def test_bf16_round_matches_torch_conversion():
+    # torch's float32 -> bfloat16 conversion rounds to nearest, ties to even
+    import torch
+    rng = np.random.default_rng(18)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000),
+                        rng.standard_normal(2000), np.array([0.0, -0.0, 1e-40, -1e-40, 3.4e38, -3.4e38])])
+    x32 = x.astype(np.float32)
+    ref = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    got = O.bf16_round(x32)
+    assert np.array_equal(got, ref, equal_nan=True)
+
+
+def test_bf16_round_worked_values():
+    # 1 + 2^-8 lies halfway between 1 and 1 + 2^-7: the even neighbour (1)
+    # wins; 1 + 3 * 2^-8 lies halfway between 1 + 2^-7 (odd last bit) and
+    # 1 + 2^-6: the latter wins; anything past halfway rounds up
+    cases = {1.0: 1.0, 1 + 2 ** -8: 1.0, 1 + 3 * 2 ** -8: 1 + 2 ** -6, 1 + 2 ** -8 + 2 ** -20: 1 + 2 ** -7,
+             -(1 + 2 ** -8 + 2 ** -20): -(1 + 2 ** -7), 1 + 2 ** -9: 1.0, 3.0: 3.0, 0.1: 0.10009765625,
+             -0.0: -0.0, 2.0 ** -130: 2.0 ** -130}
+    for x, want in cases.items():
+        assert O.bf16_round(x) == want, (x, float(O.bf16_round(x)), want)
+    big = float(np.finfo(np.float32).max)
+    assert O.bf16_round(big) == np.inf and O.bf16_round(-big) == -np.inf
+    assert np.isnan(O.bf16_round(np.nan)) and O.bf16_round(np.inf) == np.inf
+    # 8 significant bits: every value is within half a unit in the 8th bit
+    x = np.random.default_rng(3).uniform(-1e3, 1e3, 10000)
+    r = O.bf16_round(x)
+    assert np.all(np.abs(r - x.astype(np.float32)) <= np.abs(x) * 2.0 ** -8)
+    # and rounding is idempotent
+    assert np.array_equal(O.bf16_round(r), r)
+
+
+def test_decode_statistics_rounds_only_the_statistics():
+    rng = np.random.default_rng(5)
+    K = rng.standard_normal((700, 16))
+    V = rng.standard_normal((700, 16))
+    L = O.build_unit(K, V, 4, 16, 3, O.unit_state(1, 0, 0, 1))
+    R = O.decode_statistics(L)
+    for name in ("cl_mu", "cl_var", "cl_vbar", "sub_mu", "sub_var", "sub_vbar"):
+        assert np.array_equal(getattr(R, name), O.bf16_round(getattr(L, name))), name
+        assert not np.array_equal(getattr(R, name), getattr(L, name)), name
+    assert np.array_equal(R.perm, L.perm) and np.array_equal(R.sub_off, L.sub_off)
+    assert np.array_equal(R.cl_count, L.cl_count) and np.array_equal(R.sub_count, L.sub_count)
+    # every group chosen whole: no statistic is used, the decode is dense
+    Q = rng.standard_normal((2, 16))
+    a = O.decode_unit(R, K, V, Q, R.C, R.S)
+    o, _ = O.dense_attention(K, V, Q)
+    assert np.max(np.abs(a["out"] - o)) < 1e-12
