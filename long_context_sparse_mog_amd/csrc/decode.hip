@@ -74,6 +74,37 @@ struct DArgs {
 // Unit u's record: computed from the index for a layout of equal units (the
 // unit table's own rule: units in order, C clusters, C*S subclusters, C*S+1
 // offsets and n_mid rows each), else loaded.
+// A block-uniform value by a scalar load (through the scalar cache, whose
+// round trip is shorter than a vector load's); only for memory no launch of
+// the step writes while the reading kernel runs.
+template <typename T>
+__device__ inline T scalar_load(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
+// A unit record by scalar loads: the table is read-only while a decode runs
+// (the layout's own launches write it before), and every lane of the wave
+// reads the same address, so the record can come through the scalar cache,
+// whose round trip is shorter than a vector load's.
+__device__ inline mog_unit unit_scalar(const mog_unit* p) {
+  typedef const __attribute__((address_space(4))) mog_unit* const_unit_ptr;
+  const const_unit_ptr c = (const_unit_ptr)p;
+  mog_unit U;
+  U.seq = c->seq;
+  U.kv_head = c->kv_head;
+  U.N = c->N;
+  U.n_mid = c->n_mid;
+  U.C = c->C;
+  U.S = c->S;
+  U.n_fold = c->n_fold;
+  U.reserved1 = 0;
+  U.row_base = c->row_base;
+  U.cl_base = c->cl_base;
+  U.sub_base = c->sub_base;
+  U.off_base = c->off_base;
+  return U;
+}
+
 __device__ inline mog_unit unit_record(const DArgs& a, int u) {
   if (a.uni_C > 0) {
     mog_unit U;
@@ -91,7 +122,7 @@ __device__ inline mog_unit unit_record(const DArgs& a, int u) {
     U.off_base = (int64_t)u * (a.uni_C * a.uni_S + 1);
     return U;
   }
-  return uni_unit(a.L.units + u);
+  return unit_scalar(a.L.units + u);
 }
 
 struct BudgetArgs {
@@ -579,7 +610,7 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
     bound[t] = a.ws.cl_tiles[cg];
     row0[t] = a.whole ? a.ws.cl_row0[cg] : 0;
   }
-  const mog_unit U = uni_unit(a.L.units + u);
+  const mog_unit U = unit_scalar(a.L.units + u);
   const int C = U.C;
   if (tid == 0 && !a.whole) a.ws.unit_rows[u] = 0;  // the subcluster kernel adds to it
   // (cleared while the score loads are in flight; the heads OR their bits in
@@ -1032,7 +1063,7 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
     g_x = a.ws.cl_list[cw + x];
     tb_x = a.ws.ch_tbase[cw + x];
   }
-  const mog_unit U = uni_unit(a.L.units + u);
+  const mog_unit U = unit_scalar(a.L.units + u);
   const int S = U.S, C = U.C, n_ch = uni(n_ch_raw);
   // the unit's records: one per chosen cluster, then one per rest block;
   // slots past them (no such cluster in this unit) leave at once
@@ -1482,7 +1513,7 @@ __global__ __launch_bounds__(256) void k_sub_wave(DArgs a, BudgetArgs b, int nb_
   const int xs = min(x, nb_chosen - 1);
   const int g_raw = a.ws.cl_list[cw + xs];
   const int tb_raw = a.ws.ch_tbase[cw + xs];
-  const mog_unit U = uni_unit(a.L.units + u);
+  const mog_unit U = unit_scalar(a.L.units + u);
   if (x >= uni(n_ch_raw)) return;
   const int g = uni(g_raw);
   const uint32_t mask = (uint32_t)uni((int)a.ws.cl_mask[cw + g]);
@@ -1520,7 +1551,7 @@ __global__ __launch_bounds__(256) void k_select_sub1(DArgs a, BudgetArgs b) {
     scv[j] = a.ws.cl_score[cw + i];
     bound[j] = a.ws.cl_tiles[cw + i];
   }
-  const mog_unit U = uni_unit(a.L.units + u);
+  const mog_unit U = unit_scalar(a.L.units + u);
   const int C = U.C;
   uint32_t key[KPL];
   int nvalid = 0;
@@ -2056,8 +2087,8 @@ __global__ __launch_bounds__(1024) void k_merge(const float* part, int n_part, c
   const int u = seq * Hkv + kvh;
   int64_t first = (int64_t)u * n_part;
   if (uinfo) {
-    first = uinfo[2 * u];
-    n_part = uinfo[2 * u + 1];
+    first = scalar_load(uinfo + 2 * u);
+    n_part = scalar_load(uinfo + 2 * u + 1);
   }
   const int64_t stride = (int64_t)G * RS;
   const float* eb = part + (first * G + h) * RS;
@@ -2065,7 +2096,7 @@ __global__ __launch_bounds__(1024) void k_merge(const float* part, int n_part, c
   // n_chosen: a whole-cluster step leaves nothing out of a chosen cluster),
   // then one per rest_cl clusters
   int n_res = 0;
-  if (res) n_res = (n_chosen ? n_chosen[u] : 0) + (units[u].C + rest_cl - 1) / rest_cl;
+  if (res) n_res = (n_chosen ? scalar_load(n_chosen + u) : 0) + (scalar_load(&units[u].C) + rest_cl - 1) / rest_cl;
   const float* rb = res ? res + ((int64_t)u * res_stride * G + h) * RS : nullptr;
   const int total = n_part + (res ? n_res : 0);
   const int q = tid % QL, grp = tid / QL;
