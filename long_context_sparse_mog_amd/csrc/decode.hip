@@ -654,6 +654,15 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
     key[j] = in ? float_key(scv[j]) : 0u;
     nvalid += in;
   }
+  if (a.shared) {
+    // the selection's histogram bins on log2 of the summed fractions (a
+    // monotone map, clamped away from 0): the sums crowd near 0, where bins
+    // over their linear range would put the c-th key among hundreds of tiny
+    // ones.  The keys, which rank the boundary bin, stay the sums themselves.
+#pragma unroll
+    for (int j = 0; j < KPL; ++j)
+      if (key[j] != 0u) scv[j] = log2f(fmaxf(scv[j], 1e-30f));
+  }
   nvalid = (int)wave_reduce_uniform((uint32_t)nvalid, [](uint32_t x, uint32_t y) { return x + y; }, 0u);
   const int want = want_raw < 0 ? 0 : want_raw;
   const int c_eff = want < nvalid ? want : nvalid;
