@@ -592,7 +592,7 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
   __shared__ uint32_t lmask[64 * KPL];     // per cluster: the heads that chose it
   __shared__ int slot_cnt[KPL], slot_tiles[KPL];
   __shared__ int wave_rows[G];  // whole-cluster step: rows of each wave's chosen clusters
-  __shared__ float gsum[64 * KPL];  // shared selection: summed mass fractions
+  __shared__ float gfr[G][64 * KPL];  // shared selection: each head's mass fractions
   const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63, h = tid >> 6;
   const int want_raw = b.top_c[u / a.Hkv];
   // the scores need only the unit index: their loads go out with the unit
@@ -620,8 +620,9 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
   if (a.shared) {
     // one selection per KV head: the key of a cluster is the sum over the
     // heads of the head's estimated mass fraction 2^(score - L_h), L_h the
-    // log2 of the head's total over its nonempty clusters; summed in head
-    // order through LDS, so every wave then holds the same keys
+    // log2 of the head's total over its nonempty clusters; each head's
+    // fractions go to its own LDS row, and after one barrier every wave adds
+    // the rows in head order, so every wave holds the same keys
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < KPL; ++j)
@@ -632,19 +633,18 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
     for (int j = 0; j < KPL; ++j) sm += (64 * j + lane < C && scv[j] != -INFINITY) ? exp2f(scv[j] - mx) : 0.f;
     const float lh = mx + log2f(wave_sum_uniform(sm));
     if (lane == 0) a.ws.cl_lse[(int64_t)u * G + h] = lh;
-    for (int hh = 0; hh < G; ++hh) {
-      if (h == hh) {
-#pragma unroll
-        for (int j = 0; j < KPL; ++j) {
-          const float f = (64 * j + lane < C && scv[j] != -INFINITY) ? exp2f(scv[j] - lh) : 0.f;
-          gsum[64 * j + lane] = hh == 0 ? f : gsum[64 * j + lane] + f;
-        }
-      }
-      __syncthreads();
-    }
 #pragma unroll
     for (int j = 0; j < KPL; ++j)
-      if (scv[j] != -INFINITY) scv[j] = gsum[64 * j + lane];
+      gfr[h][64 * j + lane] = (64 * j + lane < C && scv[j] != -INFINITY) ? exp2f(scv[j] - lh) : 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      if (scv[j] != -INFINITY) {
+        float t = gfr[0][64 * j + lane];
+        for (int hh = 1; hh < G; ++hh) t += gfr[hh][64 * j + lane];
+        scv[j] = t;
+      }
+    }
   }
   uint32_t key[KPL];
   int nvalid = 0;
