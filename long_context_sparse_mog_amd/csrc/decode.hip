@@ -802,8 +802,8 @@ __global__ __launch_bounds__(64 * G) void k_select_topc(DArgs a, BudgetArgs b) {
 
 // ---------------------------------------------------------------------------
 // 3. Subclusters and residual, one block per chosen cluster: the steps
-//    with shared selection, the feature-map residual or folded rows (the
-//    others run the one-wave-per-cluster kernel of 3b).  Grid (units,
+//    with shared selection or the feature-map residual (the others run the
+//    one-wave-per-cluster kernel of 3b).  Grid (units,
 //    n_rest + nb_chosen); blocks are numbered x (record slot order) as
 //    below, but the rest blocks come
 //    first in the grid, so the dispatcher starts them together with the
@@ -1332,7 +1332,8 @@ __global__ __launch_bounds__(256) void k_subclusters(DArgs a, BudgetArgs b, int 
 
 // ---------------------------------------------------------------------------
 // 3b. Subclusters, one wave per chosen cluster (selection per query head,
-//     Gaussian residual or none, no folded rows): wave w of block (u, y)
+//     Gaussian residual or none; folded rows count in their subcluster's
+//     size and are read as tiles after the cluster's runs): wave w of block (u, y)
 //     takes the unit's chosen cluster x = 4 y + w and does alone, with no
 //     barrier, what a block of the kernel above does for it:
 //     * the S subcluster scores (count term included) in chunks of
@@ -1374,6 +1375,10 @@ __device__ inline void sub_wave_cluster(const DArgs& a, int u, int x, const mog_
   const int o_i = off[min(lane, S)];
   const int o_n = __shfl_down(o_i, 1, 64);
   const int cnt = lane < S ? o_n - o_i : 0;
+  // folded rows of each subcluster (incremental decode): they count in the
+  // group's size and are read as tiles of their own
+  const int fcnt = (a.L.fold_cap && lane < S) ? a.L.sub_fold[sg0 + lane] : 0;
+  const int ncnt = cnt + fcnt;
   const int s_keep = s_keep_raw < 0 ? 0 : s_keep_raw;
   float* sc = reinterpret_cast<float*>(&lsc[0][0]);  // sc[h * SR + i]
   uint32_t sm = 0u;  // lane i: the heads that chose subcluster i
@@ -1383,7 +1388,7 @@ __device__ inline void sub_wave_cluster(const DArgs& a, int u, int x, const mog_
   uint32_t vraw[SR];
   if (s_keep >= S) {
     // a budget of S or more reads every nonempty subcluster of the cluster
-    sm = (lane < S && cnt > 0) ? mask : 0u;
+    sm = (lane < S && ncnt > 0) ? mask : 0u;
   } else {
     // every row of the cluster in one round trip: the bf16 pairs stay packed
     // (EPL / 2 registers a row) until their chunk is scored
@@ -1413,7 +1418,7 @@ __device__ inline void sub_wave_cluster(const DArgs& a, int u, int x, const mog_
       }
       const float t = wave_reduce_scatter<RC * G>(part);
       const int j = rs_index<RC * G>(lane), i = c * RC + j / G, h = j % G;
-      const int ci = __shfl(cnt, i & 63, 64);
+      const int ci = __shfl(ncnt, i & 63, 64);
       // (rows past S score -inf, so every row of the LDS row is written)
       if (rs_owner<RC * G>(lane)) sc[h * SR + i] = (i < S && ci > 0) ? t + log2f((float)ci) : -INFINITY;
     }
@@ -1467,7 +1472,7 @@ __device__ inline void sub_wave_cluster(const DArgs& a, int u, int x, const mog_
   if (a.residual) {
     // residual of the subclusters a choosing head left out: every lane holds
     // VPL elements of each such subcluster's value mean
-    const uint32_t need = (lane < S && cnt > 0) ? (mask & ~sm) : 0u;
+    const uint32_t need = (lane < S && ncnt > 0) ? (mask & ~sm) : 0u;
     const unsigned long long any_need = __ballot(need != 0u);
     float rm[G], rl[G], ro[G][VPL];
 #pragma unroll
@@ -1498,14 +1503,42 @@ __device__ inline void sub_wave_cluster(const DArgs& a, int u, int x, const mog_
     }
   }
   {
-    const uint32_t rows = (lane < S && sm != 0u) ? (uint32_t)cnt : 0u;
+    const uint32_t rows = (lane < S && sm != 0u) ? (uint32_t)ncnt : 0u;
     const int rsum = (int)wave_reduce_uniform(rows, [](uint32_t p, uint32_t q) { return p + q; }, 0u);
     if (lane == 0) atomicAdd(&a.ws.unit_rows[u], rsum);
   }
   TileRec* ctiles = a.ws.tiles + tile_unit_base(U.row_base, U.cl_base, u, a.L.fold_cap) + tbx;
   const int n_tiles =
       write_run_tiles(ctiles, U.row_base, a.L_head_dim, lane < S ? o_i : 0, lane < S ? o_n : 0, lane < S ? sm : 0u);
-  if (lane == 0) a.ws.ch_ntiles[cw + x] = n_tiles;
+  int n_all = n_tiles;
+  if (__ballot(lane < S && sm != 0u && fcnt > 0)) {
+    // folded rows of the chosen subclusters, after the reordered ones: the
+    // unit's fold rows are scanned 64 at a time (lane l: row f0 + l); a tile
+    // is a run of consecutive fold rows with one head mask, cut at every
+    // 32nd row
+    const int nf = U.n_fold;
+    const int32_t* fs = a.L.fold_sub + (int64_t)u * a.L.fold_cap;
+    const int64_t frow = a.L.fold_row0 + (int64_t)u * a.L.fold_cap;
+    TileRec* ft = ctiles + n_tiles;
+    int nt = 0;
+    for (int f0 = 0; f0 < nf; f0 += 64) {
+      const int f = f0 + lane;
+      const int li = (f < nf ? fs[f] : -1) - g * S;
+      const bool mine = li >= 0 && li < S;
+      const uint32_t smi = (uint32_t)__shfl((int)sm, mine ? li : 0, 64);
+      const uint32_t fm = mine ? smi : 0u;
+      const uint32_t fm_prv = (uint32_t)__shfl_up((int)fm, 1, 64);
+      const bool cont = fm != 0u && (lane & 31) != 0 && fm_prv == fm;
+      const bool fhead = fm != 0u && !cont;
+      const unsigned long long fhb = __ballot(fhead);
+      const unsigned long long after = __ballot(!cont) & ~((2ull << lane) - 1ull);
+      const int fend = after ? __ffsll((long long)after) - 1 : 64;
+      if (fhead) ft[nt + __popcll(fhb & below)] = TileRec{(frow + f) * (int64_t)a.L_head_dim, fend - lane, fm};
+      nt += __popcll(fhb);
+    }
+    n_all += nt;
+  }
+  if (lane == 0) a.ws.ch_ntiles[cw + x] = n_all;
 }
 
 
@@ -2254,7 +2287,7 @@ static hipError_t decode_impl(const DecodeLaunch& x, const DArgs& a, const Budge
   hipLaunchKernelGGL((k_score_clusters<D, G>), dim3(a.score_blocks + fblocks, nu), dim3(256), fq_lds, s, a);
   // one query head per KV head and a subcluster step of 3b: top-c and the
   // subclusters in one launch (3c)
-  const bool fused = G == 1 && !x.whole && x.residual != 2 && !x.shared && x.L.fold_capacity == 0 &&
+  const bool fused = G == 1 && !x.whole && x.residual != 2 && !x.shared &&
                      x.nb_chosen > 0 && x.L.max_C <= 1024;
   if (fused) {
     const dim3 grid(nu, (x.nb_chosen + 3) / 4);
@@ -2276,7 +2309,7 @@ static hipError_t decode_impl(const DecodeLaunch& x, const DArgs& a, const Budge
   // exact ones, in the spread of their end times; the feature-map residual's
   // in the subcluster kernel; none without a residual
   if (!x.whole && !fused) {
-    if (x.residual != 2 && !x.shared && x.L.fold_capacity == 0) {
+    if (x.residual != 2 && !x.shared) {
       // one wave per chosen cluster
       if (x.nb_chosen > 0)
         hipLaunchKernelGGL((k_sub_wave<D, G>), dim3(nu, (x.nb_chosen + 3) / 4), dim3(256), 0, s, a, b, x.nb_chosen);

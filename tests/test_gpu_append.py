@@ -124,6 +124,15 @@ def test_append_gqa_bf16_reduced():
     run_append_case(wl, [200])
 
 
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (2, 2)])
+def test_append_partial_subclusters(hq, hkv):
+    """Folded rows under a budget of some subclusters per chosen cluster:
+    their subclusters' sizes count them, and the one-wave subcluster kernel
+    (the fused one at one query head per KV head) lists them as tiles."""
+    wl = synth.config(1, seq_lens=[7000, 4000], n_kv_heads=hkv, n_q_heads=hq, n_components=48)
+    run_append_case(wl, [150, 33], chunks=[[1, 0], [149, 33]], top=([6, 4], [4, 3]))
+
+
 def test_append_gqa_bf16_shared_selection():
     wl = synth.config(3, seq_lens=[6000], n_components=64)
     run_append_case(wl, [150], shared=True)
