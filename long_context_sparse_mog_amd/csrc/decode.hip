@@ -1356,7 +1356,8 @@ constexpr int kSubChunk = 8;
 // lsc is the wave's LDS row of scores.
 template <int D, int G>
 __device__ inline void sub_wave_cluster(const DArgs& a, int u, int x, const mog_unit& U, int g, int tbx,
-                                        uint32_t mask, int s_keep_raw, float4 (&lsc)[G][kDecodeSubRows / 4]) {
+                                        uint32_t mask, int s_keep_raw, float4 (&lsc)[G][kDecodeSubRows / 4],
+                                        const float* fe, const float* fbase) {
   constexpr int EPL = D / 32;
   constexpr int VPL = D / 64;
   constexpr int RS = D + kPartPad;
@@ -1482,16 +1483,47 @@ __device__ inline void sub_wave_cluster(const DArgs& a, int u, int x, const mog_
 #pragma unroll
       for (int e = 0; e < VPL; ++e) ro[h][e] = 0.f;
     }
+    if (a.residual == 2) {
+      // the feature-map estimate of each left-out subcluster's mass (the
+      // unit's feature table fe / fbase in LDS): ZB subclusters' feature sums
+      // loaded at a time, unconditionally, then one wave sum per
+      // (subcluster, head)
+      constexpr int ZB = 8;
+      static_assert(SR % ZB == 0, "whole batches");
+      const int FM = a.L.fm_dim;
 #pragma unroll
-    for (int k = 0; k < SR; ++k) {
-      if (!((any_need >> k) & 1ull)) continue;
-      const uint32_t nk = (uint32_t)__builtin_amdgcn_readlane((int)need, k);
-      float vb[VPL];
-      vb[0] = bf16_lo(vraw[k]);
-      if constexpr (VPL == 2) vb[1] = bf16_hi(vraw[k]);
+      for (int k0 = 0; k0 < SR; k0 += ZB) {
+        if (!((any_need >> k0) & ((1ull << ZB) - 1ull))) continue;
+        float z[ZB][4];
 #pragma unroll
-      for (int h = 0; h < G; ++h)
-        if ((nk >> h) & 1u) add_group<VPL>(rm[h], rl[h], ro[h], sc[h * SR + k], vb);
+        for (int k = 0; k < ZB; ++k) load_fz(a.L.sub_fz + (sg0 + min(k0 + k, S - 1)) * FM, FM, z[k]);
+#pragma unroll
+        for (int k = 0; k < ZB; ++k) {
+          if (!((any_need >> (k0 + k)) & 1ull)) continue;
+          const uint32_t nk = (uint32_t)__builtin_amdgcn_readlane((int)need, k0 + k);
+          float vb[VPL];
+          vb[0] = bf16_lo(vraw[k0 + k]);
+          if constexpr (VPL == 2) vb[1] = bf16_hi(vraw[k0 + k]);
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            if (!((nk >> h) & 1u)) continue;
+            const float w = fm_weight(z[k], fe + 256 * h, fbase[h], FM);
+            if (w != -INFINITY) add_group<VPL>(rm[h], rl[h], ro[h], w, vb);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < SR; ++k) {
+        if (!((any_need >> k) & 1ull)) continue;
+        const uint32_t nk = (uint32_t)__builtin_amdgcn_readlane((int)need, k);
+        float vb[VPL];
+        vb[0] = bf16_lo(vraw[k]);
+        if constexpr (VPL == 2) vb[1] = bf16_hi(vraw[k]);
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+          if ((nk >> h) & 1u) add_group<VPL>(rm[h], rl[h], ro[h], sc[h * SR + k], vb);
+      }
     }
     // the wave's record: one (o, m, l) row per head
     float* dst = a.ws.res_part + ((int64_t)u * a.nb_res + x) * G * RS;
@@ -1545,6 +1577,8 @@ __device__ inline void sub_wave_cluster(const DArgs& a, int u, int x, const mog_
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_sub_wave(DArgs a, BudgetArgs b, int nb_chosen) {
   __shared__ float4 lsc4[4][G][kDecodeSubRows / 4];  // each wave's scores [head][subcluster]
+  __shared__ float lds_fe[G][256];  // feature-map residual: 2^(fq - max) per head
+  __shared__ float lds_fbase[G];    // and max - log2(m) / 2
   const int u = blockIdx.x, wave = threadIdx.x >> 6;
   const int x = (int)blockIdx.y * 4 + wave;
   const int64_t cw = (int64_t)u * a.cstride;
@@ -1556,10 +1590,15 @@ __global__ __launch_bounds__(256) void k_sub_wave(DArgs a, BudgetArgs b, int nb_
   const int g_raw = a.ws.cl_list[cw + xs];
   const int tb_raw = a.ws.ch_tbase[cw + xs];
   const mog_unit U = unit_scalar(a.L.units + u);
+  if (a.residual == 2) {
+    // (before any wave leaves: the table's barrier)
+    fm_table<G>(a, u, &lds_fe[0][0], lds_fbase);
+    __syncthreads();
+  }
   if (x >= uni(n_ch_raw)) return;
   const int g = uni(g_raw);
   const uint32_t mask = (uint32_t)uni((int)a.ws.cl_mask[cw + g]);
-  sub_wave_cluster<D, G>(a, u, x, U, g, uni(tb_raw), mask, s_keep_raw, lsc4[wave]);
+  sub_wave_cluster<D, G>(a, u, x, U, g, uni(tb_raw), mask, s_keep_raw, lsc4[wave], &lds_fe[0][0], lds_fbase);
 }
 
 // ---------------------------------------------------------------------------
@@ -1578,7 +1617,13 @@ template <int D, int KPL>
 __global__ __launch_bounds__(256) void k_select_sub1(DArgs a, BudgetArgs b) {
   __shared__ int hist[4][256 + 64];
   __shared__ float4 lsc4[4][1][kDecodeSubRows / 4];
+  __shared__ float lds_fe[256];  // feature-map residual: the head's 2^(fq - max)
+  __shared__ float lds_fbase[1];
   const int u = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (a.residual == 2) {
+    fm_table<1>(a, u, lds_fe, lds_fbase);
+    __syncthreads();
+  }
   const int x = (int)blockIdx.y * 4 + wave;
   const int64_t cw = (int64_t)u * a.cstride;
   const int want_raw = b.top_c[u / a.Hkv];
@@ -1669,7 +1714,7 @@ __global__ __launch_bounds__(256) void k_select_sub1(DArgs a, BudgetArgs b) {
     if (lane == 0) a.ws.n_chosen[u] = n_ch;
   }
   if (x >= n_ch) return;
-  sub_wave_cluster<D, 1>(a, u, x, U, g, tbx, 1u, s_keep_raw, lsc4[wave]);
+  sub_wave_cluster<D, 1>(a, u, x, U, g, tbx, 1u, s_keep_raw, lsc4[wave], lds_fe, lds_fbase);
 }
 
 // ---------------------------------------------------------------------------
@@ -2287,7 +2332,7 @@ static hipError_t decode_impl(const DecodeLaunch& x, const DArgs& a, const Budge
   hipLaunchKernelGGL((k_score_clusters<D, G>), dim3(a.score_blocks + fblocks, nu), dim3(256), fq_lds, s, a);
   // one query head per KV head and a subcluster step of 3b: top-c and the
   // subclusters in one launch (3c)
-  const bool fused = G == 1 && !x.whole && x.residual != 2 && !x.shared &&
+  const bool fused = G == 1 && !x.whole && !x.shared &&
                      x.nb_chosen > 0 && x.L.max_C <= 1024;
   if (fused) {
     const dim3 grid(nu, (x.nb_chosen + 3) / 4);
@@ -2305,11 +2350,13 @@ static hipError_t decode_impl(const DecodeLaunch& x, const DArgs& a, const Budge
     hipLaunchKernelGGL((k_select_topc<G, 16>), dim3(nu), dim3(64 * G), 0, s, a, b);
   else
     hipLaunchKernelGGL((k_select_topc<G, kMaxC / 64>), dim3(nu), dim3(64 * G), 0, s, a, b);
-  // the Gaussian residual of the clusters left out runs in blocks after the
-  // exact ones, in the spread of their end times; the feature-map residual's
-  // in the subcluster kernel; none without a residual
+  // the residual of the clusters left out runs in blocks after the exact
+  // ones, in the spread of their end times (with shared selection, the
+  // feature-map residual's in the subcluster block kernel); none without a
+  // residual
+  const bool sub_blocks = !x.whole && !fused && x.shared;
   if (!x.whole && !fused) {
-    if (x.residual != 2 && !x.shared) {
+    if (!x.shared) {
       // one wave per chosen cluster
       if (x.nb_chosen > 0)
         hipLaunchKernelGGL((k_sub_wave<D, G>), dim3(nu, (x.nb_chosen + 3) / 4), dim3(256), 0, s, a, b, x.nb_chosen);
@@ -2321,9 +2368,7 @@ static hipError_t decode_impl(const DecodeLaunch& x, const DArgs& a, const Budge
                            x.nb_chosen, nrest_sub);
     }
   }
-  // (the feature-map residual's blocks run in the subcluster kernel unless
-  // the step is whole-cluster)
-  const int nrest = (x.residual == 1 || (x.residual == 2 && x.whole)) ? nu * a.rest_per_unit : 0;
+  const int nrest = (x.residual == 1 || (x.residual == 2 && !sub_blocks)) ? nu * a.rest_per_unit : 0;
   // the timing events (if any) are taken by the dispatches themselves: the
   // start of the first exact launch and the end of the last
   for (int r = 0; r < x.repeat; ++r) {
