@@ -1486,17 +1486,38 @@ __device__ inline void sub_wave_cluster(const DArgs& a, int u, int x, const mog_
     if (a.residual == 2) {
       // the feature-map estimate of each left-out subcluster's mass (the
       // unit's feature table fe / fbase in LDS): ZB subclusters' feature sums
-      // loaded at a time, unconditionally, then one wave sum per
-      // (subcluster, head)
-      constexpr int ZB = 8;
-      static_assert(SR % ZB == 0, "whole batches");
+      // loaded at a time, unconditionally; their ZB G dot products with the
+      // heads' features (held in registers) summed over the lanes by one
+      // reduce-scatter, each lane taking the log of the sum it receives, and
+      // every weight read from the lane that holds it
+      constexpr int ZB = G <= 2 ? 8 : 4;
+      constexpr int V = ZB * G;
+      static_assert(SR % ZB == 0 && V <= 64, "whole batches, one reduce-scatter each");
       const int FM = a.L.fm_dim;
+      float e[G][4];
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) e[h][j] = 64 * j < FM ? fe[256 * h + lane + 64 * j] : 0.f;
+      const float base = fbase[rs_index<V>(lane) % G];  // (of the head whose sum the lane receives)
 #pragma unroll
       for (int k0 = 0; k0 < SR; k0 += ZB) {
         if (!((any_need >> k0) & ((1ull << ZB) - 1ull))) continue;
         float z[ZB][4];
 #pragma unroll
         for (int k = 0; k < ZB; ++k) load_fz(a.L.sub_fz + (sg0 + min(k0 + k, S - 1)) * FM, FM, z[k]);
+        float part[V];
+#pragma unroll
+        for (int k = 0; k < ZB; ++k)
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            float t = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) t += e[h][j] * z[k][j];
+            part[k * G + h] = t;
+          }
+        const float t = wave_reduce_scatter<V>(part);
+        const float wl = t > 0.f ? base + log2f(t) : -INFINITY;
 #pragma unroll
         for (int k = 0; k < ZB; ++k) {
           if (!((any_need >> (k0 + k)) & 1ull)) continue;
@@ -1507,7 +1528,7 @@ __device__ inline void sub_wave_cluster(const DArgs& a, int u, int x, const mog_
 #pragma unroll
           for (int h = 0; h < G; ++h) {
             if (!((nk >> h) & 1u)) continue;
-            const float w = fm_weight(z[k], fe + 256 * h, fbase[h], FM);
+            const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), rs_lane<V>(k * G + h)));
             if (w != -INFINITY) add_group<VPL>(rm[h], rl[h], ro[h], w, vb);
           }
         }
