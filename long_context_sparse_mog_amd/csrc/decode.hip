@@ -1566,28 +1566,41 @@ __device__ inline void sub_wave_cluster(const DArgs& a, int u, int x, const mog_
   int n_all = n_tiles;
   if (__ballot(lane < S && sm != 0u && fcnt > 0)) {
     // folded rows of the chosen subclusters, after the reordered ones: the
-    // unit's fold rows are scanned 64 at a time (lane l: row f0 + l); a tile
-    // is a run of consecutive fold rows with one head mask, cut at every
-    // 32nd row
+    // unit's fold rows are scanned 64 at a time (lane l: row f0 + l), the
+    // subclusters of FB such chunks loaded before any is used; a tile is a
+    // run of consecutive fold rows with one head mask, cut at every 32nd row
+    constexpr int FB = 8;
     const int nf = U.n_fold;
     const int32_t* fs = a.L.fold_sub + (int64_t)u * a.L.fold_cap;
     const int64_t frow = a.L.fold_row0 + (int64_t)u * a.L.fold_cap;
     TileRec* ft = ctiles + n_tiles;
     int nt = 0;
-    for (int f0 = 0; f0 < nf; f0 += 64) {
-      const int f = f0 + lane;
-      const int li = (f < nf ? fs[f] : -1) - g * S;
-      const bool mine = li >= 0 && li < S;
-      const uint32_t smi = (uint32_t)__shfl((int)sm, mine ? li : 0, 64);
-      const uint32_t fm = mine ? smi : 0u;
-      const uint32_t fm_prv = (uint32_t)__shfl_up((int)fm, 1, 64);
-      const bool cont = fm != 0u && (lane & 31) != 0 && fm_prv == fm;
-      const bool fhead = fm != 0u && !cont;
-      const unsigned long long fhb = __ballot(fhead);
-      const unsigned long long after = __ballot(!cont) & ~((2ull << lane) - 1ull);
-      const int fend = after ? __ffsll((long long)after) - 1 : 64;
-      if (fhead) ft[nt + __popcll(fhb & below)] = TileRec{(frow + f) * (int64_t)a.L_head_dim, fend - lane, fm};
-      nt += __popcll(fhb);
+    for (int fb0 = 0; fb0 < nf; fb0 += 64 * FB) {
+      int fsv[FB];
+#pragma unroll
+      for (int c = 0; c < FB; ++c) {
+        const int f = fb0 + 64 * c + lane;
+        fsv[c] = f < nf ? fs[f] : -1;
+      }
+#pragma unroll
+      for (int c = 0; c < FB; ++c) {
+        const int f0 = fb0 + 64 * c;
+        if (f0 < nf) {
+          const int f = f0 + lane;
+          const int li = fsv[c] - g * S;
+          const bool mine = li >= 0 && li < S;
+          const uint32_t smi = (uint32_t)__shfl((int)sm, mine ? li : 0, 64);
+          const uint32_t fm = mine ? smi : 0u;
+          const uint32_t fm_prv = (uint32_t)__shfl_up((int)fm, 1, 64);
+          const bool cont = fm != 0u && (lane & 31) != 0 && fm_prv == fm;
+          const bool fhead = fm != 0u && !cont;
+          const unsigned long long fhb = __ballot(fhead);
+          const unsigned long long after = __ballot(!cont) & ~((2ull << lane) - 1ull);
+          const int fend = after ? __ffsll((long long)after) - 1 : 64;
+          if (fhead) ft[nt + __popcll(fhb & below)] = TileRec{(frow + f) * (int64_t)a.L_head_dim, fend - lane, fm};
+          nt += __popcll(fhb);
+        }
+      }
     }
     n_all += nt;
   }
