@@ -185,9 +185,14 @@ def test_fm_whole_and_subcluster_paths_agree():
     assert torch.allclose(lw, ls_, rtol=0, atol=1e-5 * max(1.0, ls_.abs().max().item()))
 
 
-def test_fm_incremental():
+@pytest.mark.parametrize("hq,budget", [(8, None), (2, ([4], [3]))])
+def test_fm_incremental(hq, budget):
+    # (2, c = 4, s = 3): one query head per KV head and some subclusters of
+    # each chosen cluster, so the fused top-c and subcluster kernel weights
+    # left-out subclusters, folded rows among them, from their feature sums
     from test_gpu_append import run_append_case  # noqa: F401 (fold checks without summaries)
-    wl = synth.config(1, seq_lens=[6000], n_kv_heads=2, n_q_heads=8, n_components=32)
+    extra = {} if budget is None else dict(top_c=budget[0], top_s=budget[1])
+    wl = synth.config(1, seq_lens=[6000], n_kv_heads=2, n_q_heads=hq, n_components=32, **extra)
     grow, m = 120, 128
     wg = replace(wl, seq_lens=[6000 + grow])
     b = synth.generate(wg, device="cuda")
